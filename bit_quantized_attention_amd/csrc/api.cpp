@@ -1,0 +1,253 @@
+// api.cpp — the C ABI declared in include/bqa.h: argument validation (host
+// only, before anything touches the device), the once-per-device gfx950
+// check, workspace sizing and dispatch to the kernels' launchers.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "bqa.h"
+#include "internal.hpp"
+
+using namespace bqa;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+bqa_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return BQA_E_DEVICE;
+    if (dev >= kMaxDevices) return BQA_E_DEVICE;
+    int st = g_dev_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BQA_E_DEVICE;
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? BQA_OK : BQA_E_DEVICE;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// dense [B, H, N, d] half-precision tensor
+bqa_status check_dense(const bqa_tensor* t, bool allow_f16, bool allow_bf16) {
+    if (!t || !t->data) return BQA_E_NULL;
+    if (!((t->dtype == BQA_BF16 && allow_bf16) || (t->dtype == BQA_FP16 && allow_f16))) return BQA_E_UNSUPPORTED;
+    if (t->stride[3] != 1) return BQA_E_ALIGN;
+    if (!aligned16(t->data)) return BQA_E_ALIGN;
+    for (int i = 0; i < 3; ++i)
+        if (t->stride[i] < 0 || (t->stride[i] * 2) % 16 != 0) return BQA_E_ALIGN;
+    return BQA_OK;
+}
+
+Dense as_dense(const bqa_tensor* t) { return Dense{t->data, t->stride[0], t->stride[1], t->stride[2]}; }
+
+bqa_status check_problem(const bqa_problem* p) {
+    if (!p) return BQA_E_NULL;
+    if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->Nq < 1 || p->Nk < 1) return BQA_E_SHAPE;
+    if (p->Hq % p->Hkv != 0) return BQA_E_SHAPE;
+    if (p->d != 64 && p->d != 128) return BQA_E_UNSUPPORTED;
+    if (p->mode < BQA_SAGE_I8_F16PV || p->mode > BQA_THRIFT) return BQA_E_UNSUPPORTED;
+    if (p->causal && p->Nq > p->Nk) return BQA_E_SHAPE;
+    if ((int64_t)p->B * p->Hq * p->Nq * p->d > ((int64_t)1 << 40)) return BQA_E_SHAPE;
+    return BQA_OK;
+}
+
+bool is_sage(int mode) { return mode == BQA_SAGE_I8_F16PV || mode == BQA_SAGE_I8_F8PV || mode == BQA_SAGE_I8_I8PV; }
+
+bqa_status check_sage_blocks(const bqa_problem* p) {
+    if (p->q_block != 64 && p->q_block != 128) return BQA_E_UNSUPPORTED;
+    if (p->k_block != 64) return BQA_E_UNSUPPORTED;
+    if (p->Nq % p->q_block != 0 || p->Nk % p->k_block != 0) return BQA_E_UNSUPPORTED;
+    return BQA_OK;
+}
+
+bqa_status check_q(const bqa_qtensor* q, int fmt, int axis) {
+    if (!q || !q->codes || !q->scales) return BQA_E_NULL;
+    if (q->fmt != fmt || q->axis != axis) return BQA_E_UNSUPPORTED;
+    if (!aligned16(q->codes)) return BQA_E_ALIGN;
+    if (fmt != BQA_MXFP4 && ((uintptr_t)q->scales & 3u)) return BQA_E_ALIGN;
+    return BQA_OK;
+}
+
+float tau_of(const bqa_problem* p) { return p->sm_scale > 0.0f ? p->sm_scale : 1.0f / std::sqrt((float)p->d); }
+
+bqa_status launched(hipError_t e) { return e == hipSuccess ? BQA_OK : BQA_E_LAUNCH; }
+
+#define TRY(x)                           \
+    do {                                 \
+        bqa_status _s = (x);             \
+        if (_s != BQA_OK) return _s;     \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t bqa_abi_version(void) { return BQA_ABI_VERSION; }
+
+const char* bqa_status_string(bqa_status s) {
+    switch (s) {
+        case BQA_OK: return "ok";
+        case BQA_E_NULL: return "a required pointer is NULL";
+        case BQA_E_SHAPE: return "inconsistent or out-of-range sizes";
+        case BQA_E_UNSUPPORTED: return "unsupported combination of mode, format or sizes";
+        case BQA_E_ALIGN: return "misaligned pointer or stride, or inner stride != 1";
+        case BQA_E_WORKSPACE: return "workspace missing or too small";
+        case BQA_E_DEVICE: return "current device is not gfx950 (MI355X) or no device";
+        case BQA_E_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t bqa_workspace_size(const bqa_problem* p, int32_t op) {
+    if (check_problem(p) != BQA_OK) return 0;
+    switch (op) {
+        case BQA_OP_QUANTIZE_K:
+            if (is_sage(p->mode) && p->smooth_k)
+                return ws_kmean_bytes(p->B * p->Hkv, p->Nk, p->d) + (size_t)p->B * p->Hkv * p->d * sizeof(float);
+            return 0;
+        case BQA_OP_QUANTIZE_V:
+            if (p->mode == BQA_SAGE_I8_F8PV || p->mode == BQA_SAGE_I8_I8PV) return ws_chan_bytes(p->B * p->Hkv, p->Nk, p->d);
+            return 0;
+        default:
+            return 0;
+    }
+}
+
+bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_tensor* x, bqa_qtensor* out,
+                               float* k_mean, float* block_means, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_problem(p));
+    if (role < BQA_ROLE_Q || role > BQA_ROLE_DO) return BQA_E_UNSUPPORTED;
+    if (!out) return BQA_E_NULL;
+    const bool kv = role == BQA_ROLE_K || role == BQA_ROLE_V;
+    const int H = kv ? p->Hkv : p->Hq, N = kv ? p->Nk : p->Nq, d = p->d;
+    TRY(check_dense(x, true, true));
+    const bool f16 = x->dtype == BQA_FP16;
+    hipStream_t st = (hipStream_t)stream;
+    if (out->fmt == BQA_MXFP4) {
+        if (role == BQA_ROLE_DO) return BQA_E_UNSUPPORTED;
+        const int axis = role == BQA_ROLE_V ? 1 : 0;
+        TRY(check_q(out, BQA_MXFP4, axis));
+        if (out->block != 32) return BQA_E_UNSUPPORTED;
+        if (axis == 1 && N % 128 != 0) return BQA_E_UNSUPPORTED;
+        if (block_means && (role == BQA_ROLE_V || p->sel_block != 128)) return BQA_E_UNSUPPORTED;
+        if (block_means && N > 1 && N % 128 != 0) return BQA_E_UNSUPPORTED;
+        TRY(check_device());
+        return launched(launch_quant_mx(as_dense(x), f16, p->B, H, N, d, axis, (uint8_t*)out->codes,
+                                        (uint8_t*)out->scales, block_means, st));
+    }
+    if (role == BQA_ROLE_V) {
+        if (out->fmt != BQA_INT8 && out->fmt != BQA_FP8E4M3) return BQA_E_UNSUPPORTED;
+        TRY(check_q(out, out->fmt, 1));
+        if (out->block != N || N % 64 != 0) return BQA_E_UNSUPPORTED;
+        const size_t need = ws_chan_bytes(p->B * H, N, d);
+        if (!ws || ws_bytes < need) return BQA_E_WORKSPACE;
+        TRY(check_device());
+        return launched(launch_quant_chan(as_dense(x), f16, p->B, H, N, d, out->fmt == BQA_INT8 ? 0 : 1,
+                                          (uint8_t*)out->codes, (float*)out->scales, ws, st));
+    }
+    // INT8 token blocks: Q, K, dO
+    TRY(check_q(out, BQA_INT8, 0));
+    const int blk = out->block;
+    if (blk != 64 && blk != 128) return BQA_E_UNSUPPORTED;
+    if (N % blk != 0) return BQA_E_UNSUPPORTED;
+    const bool smooth = role == BQA_ROLE_K && p->smooth_k;
+    if (smooth) {
+        const size_t need = ws_kmean_bytes(p->B * H, N, d) + (size_t)p->B * H * d * sizeof(float);
+        if (!ws || ws_bytes < need) return BQA_E_WORKSPACE;
+        if (!std::isfinite(p->smooth_eps)) return BQA_E_SHAPE;
+    }
+    TRY(check_device());
+    float* mu = nullptr;
+    if (smooth) {
+        mu = k_mean ? k_mean : (float*)((char*)ws + ws_kmean_bytes(p->B * H, N, d));
+        hipError_t e = launch_kmean(as_dense(x), f16, p->B, H, N, d, (double)p->smooth_eps, mu, ws, st);
+        if (e != hipSuccess) return BQA_E_LAUNCH;
+    }
+    return launched(launch_quant_i8_tokblock(as_dense(x), f16, p->B, H, N, d, blk, mu, (int8_t*)out->codes,
+                                             (float*)out->scales, st));
+}
+
+bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const float* k_means, int32_t* sel_idx,
+                             int32_t* sel_cnt, void* ws, size_t ws_bytes, void* stream) {
+    (void)q_means; (void)k_means; (void)sel_idx; (void)sel_cnt; (void)ws; (void)ws_bytes; (void)stream;
+    TRY(check_problem(p));
+    return BQA_E_UNSUPPORTED;
+}
+
+bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k, const bqa_qtensor* v,
+                        const bqa_tensor* q_hi, const bqa_tensor* k_hi, const bqa_tensor* v_hi,
+                        const int32_t* sel_idx, const int32_t* sel_cnt, bqa_tensor* o, bqa_tensor* o_aux,
+                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+    (void)q_hi; (void)k_hi; (void)sel_idx; (void)sel_cnt; (void)o_aux; (void)ws; (void)ws_bytes;
+    TRY(check_problem(p));
+    hipStream_t st = (hipStream_t)stream;
+    if (is_sage(p->mode)) {
+        TRY(check_sage_blocks(p));
+        TRY(check_q(q, BQA_INT8, 0));
+        TRY(check_q(k, BQA_INT8, 0));
+        if (q->block != p->q_block || k->block != p->k_block) return BQA_E_UNSUPPORTED;
+        SageFwdArgs a{};
+        int pv;
+        if (p->mode == BQA_SAGE_I8_F16PV) {
+            TRY(check_dense(v_hi, true, false));
+            pv = PV_F16;
+            a.v16 = as_dense(v_hi);
+        } else {
+            const int fmt = p->mode == BQA_SAGE_I8_F8PV ? BQA_FP8E4M3 : BQA_INT8;
+            TRY(check_q(v, fmt, 1));
+            if (v->block != p->Nk) return BQA_E_UNSUPPORTED;
+            pv = p->mode == BQA_SAGE_I8_F8PV ? PV_F8 : PV_I8;
+            a.vc = (const uint8_t*)v->codes;
+            a.vs = (const float*)v->scales;
+        }
+        TRY(check_dense(o, pv == PV_F16, pv != PV_F16));
+        a.qc = (const int8_t*)q->codes; a.qs = (const float*)q->scales; a.q_blk = p->q_block;
+        a.kc = (const int8_t*)k->codes; a.ks = (const float*)k->scales;
+        a.o = as_dense(o); a.lse = lse;
+        a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk; a.causal = p->causal;
+        a.c_log2 = tau_of(p) * 1.4426950408889634f;
+        TRY(check_device());
+        return launched(launch_sage_fwd(a, pv, p->d, st));
+    }
+    return BQA_E_UNSUPPORTED;
+}
+
+bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k, const bqa_qtensor* v,
+                        const bqa_tensor* v_hi, const bqa_tensor* o_for_delta, const float* lse,
+                        const bqa_tensor* d_o, bqa_tensor* dq, bqa_tensor* dk, bqa_tensor* dv, void* ws,
+                        size_t ws_bytes, void* stream) {
+    (void)q; (void)k; (void)v; (void)v_hi; (void)o_for_delta; (void)lse; (void)d_o; (void)dq; (void)dk; (void)dv;
+    (void)ws; (void)ws_bytes; (void)stream;
+    TRY(check_problem(p));
+    return BQA_E_UNSUPPORTED;
+}
+
+bqa_status bqa_debug_qk_scores(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k, int32_t b,
+                               int32_t h, int32_t q_tile, int32_t k_tile, void* out, void* stream) {
+    TRY(check_problem(p));
+    if (!out) return BQA_E_NULL;
+    if (b < 0 || b >= p->B || h < 0 || h >= p->Hq) return BQA_E_SHAPE;
+    if (q_tile < 0 || (int64_t)(q_tile + 1) * 32 > p->Nq || k_tile < 0 || (int64_t)(k_tile + 1) * 32 > p->Nk)
+        return BQA_E_SHAPE;
+    if (!q || !k) return BQA_E_NULL;
+    if (q->fmt == BQA_INT8) {
+        TRY(check_q(q, BQA_INT8, 0));
+        TRY(check_q(k, BQA_INT8, 0));
+        TRY(check_device());
+        const int hk = h / (p->Hq / p->Hkv);
+        const int64_t qrow = ((int64_t)b * p->Hq + h) * p->Nq + (int64_t)q_tile * 32;
+        const int64_t krow = ((int64_t)b * p->Hkv + hk) * p->Nk + (int64_t)k_tile * 32;
+        return launched(launch_debug_scores_i8((const int8_t*)q->codes, (const int8_t*)k->codes, p->d, qrow, krow,
+                                               (int32_t*)out, (hipStream_t)stream));
+    }
+    return BQA_E_UNSUPPORTED;
+}
+
+}  // extern "C"

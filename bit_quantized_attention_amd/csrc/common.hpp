@@ -1,0 +1,131 @@
+// common.hpp — types and device helpers shared by the gfx950 kernels of libbqa.
+//
+// Everything here is written for CDNA4 (gfx950) only: 64-lane wavefronts,
+// the gfx950 matrix instructions (i8 32x32x32, scaled f8f6f4 32x32x64 /
+// 16x16x128, bf16/f16 32x32x16) and permlane32_swap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bqa {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------------ tensors
+// Dense [B, H, N, d] view with element strides (innermost stride 1).
+struct Dense {
+    void* p;
+    int64_t sB, sH, sN;
+};
+
+// ------------------------------------------------------------------ lanes
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Value of x held by the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ int partner32(int x) {
+    v2i r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ float partner32f(float x) {
+    return __builtin_bit_cast(float, partner32(__builtin_bit_cast(int, x)));
+}
+
+// ------------------------------------------------------------------ MFMA
+__device__ __forceinline__ v16i mfma_i8_32x32x32(v4i a, v4i b, v16i c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+// fp8 e4m3 x fp8 e4m3 with unit scales (E8M0 127 = 2^0)
+__device__ __forceinline__ v16f mfma_f8_32x32x64(v8i a, v8i b, v16f c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+// MXFP4 x MXFP4: 16 bytes (32 e2m1) per lane, one E8M0 scale byte per lane
+__device__ __forceinline__ v16f mfma_f4_32x32x64(v4i a, int sa, v4i b, int sb, v16f c) {
+    v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+    v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
+}
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(v8bf a, v8bf b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16f mfma_f16_32x32x16(v8h a, v8h b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ formats
+// fp32 <-> bf16 / fp16 with round-to-nearest-even.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+template <bool IS_F16>
+__device__ __forceinline__ float load_half(const uint16_t* p) {
+    return IS_F16 ? f16_bits_to_f32(*p) : bf16_bits_to_f32(*p);
+}
+
+// Symmetric INT8: nearest-even integer of the fp32 product, clamped to +-127.
+__device__ __forceinline__ int enc_i8(float x, float inv) {
+    float r = __builtin_rintf(x * inv);
+    r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// OCP e4m3 ("fn"): exponent bias 7, 3 mantissa bits, largest finite 448;
+// nearest-even, saturating (anything at or above 448 encodes as 448).
+__device__ __forceinline__ uint32_t enc_e4m3(float x) {
+    uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
+    float a = __builtin_fabsf(x);
+    if (!(a < 448.0f)) return sign | 0x7Eu;                 // saturate (+inf too)
+    if (a < 0.015625f) {                                   // below 2^-6: steps of 2^-9
+        return sign | (uint32_t)__builtin_rintf(a * 512.0f);   // 8 rounds up to the first normal
+    }
+    int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFF) - 127;
+    float m = __builtin_rintf((__builtin_ldexpf(a, -e) - 1.0f) * 8.0f);
+    uint32_t mi = (uint32_t)m;
+    if (mi == 8u) { mi = 0u; e += 1; }
+    return sign | ((uint32_t)(e + 7) << 3) | mi;
+}
+
+// OCP e2m1: values 0, 0.5, 1, 1.5, 2, 3, 4, 6; nearest-even, saturating.
+__device__ __forceinline__ uint32_t enc_e2m1(float x) {
+    uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 28) & 0x8u;
+    float a = __builtin_fabsf(x);
+    if (!(a < 6.0f)) return sign | 0x7u;
+    if (a < 1.0f) return sign | (uint32_t)__builtin_rintf(a * 2.0f);   // 0, 0.5, or 1.0 (code 2)
+    int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFF) - 127;   // 0, 1 or 2
+    uint32_t m = (uint32_t)__builtin_rintf((__builtin_ldexpf(a, -e) - 1.0f) * 2.0f);
+    if (m == 2u) { m = 0u; e += 1; }
+    return sign | ((uint32_t)(e + 1) << 1) | m;
+}
+
+// OCP MX shared exponent of a block with absolute maximum amax:
+// floor(log2 amax) - 2, clamped to [-127, 127]; -127 for 0 and subnormals.
+__device__ __forceinline__ int mx_exponent(float amax) {
+    uint32_t E = (__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFF;
+    if (E == 0) return -127;
+    int e = (int)E - 127 - 2;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// ------------------------------------------------------------------ reductions
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+}  // namespace bqa

@@ -1,0 +1,41 @@
+// internal.hpp — host-side declarations shared by the library's translation
+// units (launchers and argument blocks).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace bqa {
+
+// ---- quantisation (quant.hip)
+size_t ws_kmean_bytes(int BH, int N, int d);
+size_t ws_chan_bytes(int BH, int N, int d);
+hipError_t launch_kmean(const Dense& x, bool f16, int B, int H, int N, int d, double eps, float* mu, void* ws,
+                        hipStream_t st);
+hipError_t launch_quant_i8_tokblock(const Dense& x, bool f16, int B, int H, int N, int d, int blk, const float* mu,
+                                    int8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_quant_chan(const Dense& x, bool f16, int B, int H, int N, int d, int fmt, uint8_t* codes_t,
+                             float* scales, void* ws, hipStream_t st);
+hipError_t launch_quant_mx(const Dense& x, bool f16, int B, int H, int N, int d, int axis, uint8_t* codes,
+                           uint8_t* scales, float* means, hipStream_t st);
+
+// ---- SageAttention INT8 forward (attn_sage_fwd.hip)
+enum { PV_F16 = 0, PV_F8 = 1, PV_I8 = 2 };
+struct SageFwdArgs {
+    const int8_t* qc;  const float* qs;  int q_blk;     // Q codes [B,Hq,Nq,d], scales [B,Hq,Nq/q_blk]
+    const int8_t* kc;  const float* ks;                  // K codes [B,Hkv,Nk,d], scales [B,Hkv,Nk/64]
+    const uint8_t* vc; const float* vs;                  // V codes [B,Hkv,d,Nk], scales [B,Hkv,d]
+    Dense v16;                                           // V fp16 (PV_F16)
+    Dense o;                                             // O [B,Hq,Nq,d] bf16 (fp16 for PV_F16)
+    float* lse;                                          // [B,Hq,Nq] or null
+    int B, Hq, Hkv, Nq, Nk;
+    int causal;
+    float c_log2;                                        // tau * log2(e)
+};
+hipError_t launch_sage_fwd(const SageFwdArgs& a, int pv, int d, hipStream_t st);
+hipError_t launch_debug_scores_i8(const int8_t* qc, const int8_t* kc, int d, int64_t q_row0, int64_t k_row0,
+                                  int32_t* out, hipStream_t st);
+
+}  // namespace bqa

@@ -1,0 +1,80 @@
+"""Buffer set-up and call sequences for whole passes of the hot path.
+
+Each class allocates the quantised operands, outputs and workspace of one
+problem once (torch device memory), builds the ABI descriptors once, and then
+issues the C-ABI calls of one pass in order on the current stream.  Nothing
+here computes: all arithmetic happens inside libbqa's kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (BQA_FP8E4M3, BQA_INT8, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_V, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V,
+               BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV, bqa_attn_fwd, bqa_quantize_blocks, bqa_workspace_size, dense,
+               problem, qtensor)
+
+
+def sage_problem(B, Hq, Hkv, Nq, Nk, d, causal, mode, q_block=128, k_block=64, smooth_k=True, smooth_eps=0.0,
+                 sm_scale=0.0):
+    return problem(B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d, causal=int(causal), sm_scale=sm_scale, mode=mode,
+                   q_block=q_block, k_block=k_block, smooth_k=int(smooth_k), smooth_eps=smooth_eps)
+
+
+class SagePath:
+    """SageAttention INT8 forward: quantise Q, K (smoothed), V, then attend."""
+
+    def __init__(self, p, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+        dev = q.device
+        self.p = p
+        B, Hq, Hkv, Nq, Nk, d = p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d
+        self.q, self.k, self.v = q, k, v
+        self.qc = torch.empty((B, Hq, Nq, d), dtype=torch.int8, device=dev)
+        self.qs = torch.empty((B, Hq, Nq // p.q_block), dtype=torch.float32, device=dev)
+        self.kc = torch.empty((B, Hkv, Nk, d), dtype=torch.int8, device=dev)
+        self.ks = torch.empty((B, Hkv, Nk // p.k_block), dtype=torch.float32, device=dev)
+        self.mu = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev)
+        self.qq = qtensor(BQA_INT8, 0, p.q_block, self.qc, self.qs)
+        self.kq = qtensor(BQA_INT8, 0, p.k_block, self.kc, self.ks)
+        self.vq = None
+        if p.mode != BQA_SAGE_I8_F16PV:
+            self.vc = torch.empty((B, Hkv, d, Nk), dtype=torch.uint8, device=dev)
+            self.vs = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev)
+            fmt = BQA_FP8E4M3 if p.mode == BQA_SAGE_I8_F8PV else BQA_INT8
+            self.vq = qtensor(fmt, 1, Nk, self.vc, self.vs)
+        ws = max(bqa_workspace_size(p, BQA_OP_QUANTIZE_K), bqa_workspace_size(p, BQA_OP_QUANTIZE_V), 16)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        odt = torch.float16 if p.mode == BQA_SAGE_I8_F16PV else torch.bfloat16
+        self.o = torch.empty((B, Hq, Nq, d), dtype=odt, device=dev)
+        self.lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+        self._qd, self._kd, self._vd, self._od = dense(q), dense(k), dense(v), dense(self.o)
+
+    def quantize(self):
+        bqa_quantize_blocks(self.p, BQA_ROLE_Q, self._qd, self.qq, workspace=self.ws)
+        bqa_quantize_blocks(self.p, BQA_ROLE_K, self._kd, self.kq, k_mean=self.mu, workspace=self.ws)
+        if self.vq is not None:
+            bqa_quantize_blocks(self.p, BQA_ROLE_V, self._vd, self.vq, workspace=self.ws)
+
+    def forward(self):
+        if self.p.mode == BQA_SAGE_I8_F16PV:
+            bqa_attn_fwd(self.p, q=self.qq, k=self.kq, v_hi=self._vd, o=self._od, lse=self.lse)
+        else:
+            bqa_attn_fwd(self.p, q=self.qq, k=self.kq, v=self.vq, o=self._od, lse=self.lse)
+
+    def step(self):
+        self.quantize()
+        self.forward()
+        return self.o
+
+
+def attention_ops(p) -> float:
+    """Effective operation count of one forward: 4 B Hq Nq Nk d, halved when causal."""
+    ops = 4.0 * p.B * p.Hq * p.Nq * p.Nk * p.d
+    return ops / 2 if p.causal else ops
+
+
+def to_device(x, dtype: str, device="cuda") -> torch.Tensor:
+    """fp32 NumPy array of bf16/fp16-exact values -> torch tensor of that dtype on the device."""
+    t = torch.from_numpy(x)
+    t = t.to(torch.bfloat16 if dtype == "bf16" else torch.float16)
+    return t.to(device)
+

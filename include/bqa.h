@@ -1,0 +1,253 @@
+/*
+ * bqa.h — C ABI of the block-quantized attention library (libbqa.so, gfx950).
+ *
+ * The library implements fused, tiled FlashAttention-style attention whose
+ * matrix products run on block-quantized operands, in the three variants
+ * described by the source pages:
+ *
+ *  - SageAttention / SageBwd ("SageBwd: A Trainable Low-bit Attention",
+ *    Methodology items 1, 2 and 4): K-smoothing, per-block INT8 Q and K with
+ *    exact int32 Q K^T, online softmax, low-bit P.V, and an INT8 backward
+ *    that keeps the softmax-gradient product dP = dO V^T in 16-bit.
+ *  - Attn-QAT ("Attn-QAT: 4-Bit Attention With Quantization-Aware Training",
+ *    technical summary §2, Principles 1 and 2): FP4 forward that also emits a
+ *    high-precision auxiliary output O', and a backward that recomputes P at
+ *    the forward's FP4 precision and uses delta = rowsum(dO o O').
+ *  - ThriftAttention ("ThriftAttention" technical summary, Method steps 1 and
+ *    2): block-mean importance scores, top-k query/key block pairs computed in
+ *    bf16 and the rest in FP4, merged by online softmax; prefill and decode.
+ *
+ * FP4 here is OCP MXFP4 (e2m1 values with one E8M0 power-of-two scale per 32
+ * elements), which the gfx950 scaled matrix instructions consume; it stands
+ * in for the pages' NVFP4.  The bf16 path stands in for the pages' FP16.
+ *
+ * Conventions
+ *  - Every tensor pointer is a device pointer on the current HIP device.
+ *    The caller allocates and owns every buffer, including the workspace
+ *    sized by bqa_workspace_size(); the library never allocates memory and
+ *    keeps no state between calls.
+ *  - Every call validates all of its arguments on the host before anything is
+ *    enqueued and returns a negative bqa_status on the first violation; then
+ *    nothing has been launched and no output has been written.  On success the
+ *    work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without waiting for it.
+ *  - Dense tensors are [B, H, N, d] with element strides given per dimension;
+ *    the innermost stride must be 1, rows must start on 16-byte boundaries.
+ *    Quantized tensors are contiguous in the layouts listed at bqa_qtensor.
+ *  - Outputs are overwritten, never accumulated into.
+ *  - Calls that overlap on one stream are ordered by the stream; the library
+ *    itself holds no locks and is safe to call from several host threads.
+ */
+#ifndef BQA_H
+#define BQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BQA_ABI_VERSION 1
+
+typedef int32_t bqa_status;
+enum {
+    BQA_OK = 0,
+    BQA_E_NULL = -1,          /* a required pointer is NULL */
+    BQA_E_SHAPE = -2,         /* inconsistent or out-of-range sizes */
+    BQA_E_UNSUPPORTED = -3,   /* a valid request this build does not implement */
+    BQA_E_ALIGN = -4,         /* misaligned pointer or stride, or inner stride != 1 */
+    BQA_E_WORKSPACE = -5,     /* workspace pointer NULL or smaller than bqa_workspace_size() */
+    BQA_E_DEVICE = -6,        /* the current device is not gfx950, or no device */
+    BQA_E_LAUNCH = -7         /* a kernel launch reported an error */
+};
+
+typedef enum {
+    BQA_BF16 = 0,
+    BQA_FP16 = 1,
+    BQA_INT8 = 2,             /* symmetric int8 codes, fp32 scales */
+    BQA_FP8E4M3 = 3,          /* OCP e4m3 ("fn") codes, fp32 scales */
+    BQA_MXFP4 = 4             /* packed e2m1 codes (even element in the low nibble), E8M0 scales */
+} bqa_dtype;
+
+typedef enum {
+    BQA_SAGE_I8_F16PV = 0,    /* INT8 Q K^T, P and V in fp16 for P.V (V given as fp16) */
+    BQA_SAGE_I8_F8PV = 1,     /* INT8 Q K^T, P = e4m3(448 P) and per-channel e4m3 V */
+    BQA_SAGE_I8_I8PV = 2,     /* INT8 Q K^T, P int8 per (row, key tile), per-channel int8 V; trainable */
+    BQA_QAT_MXFP4 = 3,        /* Attn-QAT: MXFP4 Q, K, P, V; optional bf16 auxiliary output O' */
+    BQA_THRIFT = 4            /* ThriftAttention: selected block pairs in bf16, the rest MXFP4 */
+} bqa_mode;
+
+typedef enum {
+    BQA_ROLE_Q = 0,
+    BQA_ROLE_K = 1,
+    BQA_ROLE_V = 2,
+    BQA_ROLE_DO = 3
+} bqa_role;
+
+/* The attention problem.  Fields that a mode does not use are ignored. */
+typedef struct bqa_problem {
+    int32_t B, Hq, Hkv;       /* batch, query heads, key/value heads (Hq % Hkv == 0) */
+    int32_t Nq, Nk;           /* query and key lengths */
+    int32_t d;                /* head dimension: 64 or 128 */
+    int32_t causal;           /* 1: key j is visible to query i iff j <= i + (Nk - Nq) */
+    float sm_scale;           /* softmax scale tau; <= 0 selects 1/sqrt(d) */
+    int32_t mode;             /* bqa_mode */
+    int32_t q_block;          /* INT8 token block of Q and dO (64 or 128; Sage modes) */
+    int32_t k_block;          /* INT8 token block of K (64; Sage modes); also the key tile */
+    int32_t smooth_k;         /* Sage: subtract the per-channel token-mean of K ... */
+    float smooth_eps;         /* ... and add this constant back (K-smoothing) */
+    int32_t hp_budget_ppm;    /* Thrift: share of valid block pairs kept in bf16, parts per million */
+    int32_t sel_block;        /* Thrift: selection block (128) */
+    int32_t num_splits;       /* Thrift decode: key-range splits merged at the end; 0 = automatic */
+} bqa_problem;
+
+/* A dense [B, H, N, d] tensor; stride[] in elements, stride[3] must be 1. */
+typedef struct bqa_tensor {
+    void* data;
+    int32_t dtype;            /* bqa_dtype: BQA_BF16 or BQA_FP16 */
+    int64_t stride[4];
+} bqa_tensor;
+
+/*
+ * A quantized tensor, contiguous, in one of these layouts (H = Hq for Q and
+ * dO, Hkv for K and V):
+ *   INT8 / FP8E4M3, token blocks (Q, K, dO): codes int8 [B, H, N, d],
+ *       scales fp32 [B, H, N / block]                         (axis 0)
+ *   INT8 / FP8E4M3, per channel (V):         codes [B, H, d, N] (channel-major),
+ *       scales fp32 [B, H, d]                                  (axis 1)
+ *   MXFP4 along d (Q, K):      codes u8 [B, H, N, d / 2], scales u8 [B, H, N, d / 32]  (axis 0)
+ *   MXFP4 along tokens (V):    codes u8 [B, H, d, N / 2], scales u8 [B, H, d, N / 32]  (axis 1)
+ * E8M0 scale bytes hold e + 127 for the power of two 2^e.
+ */
+typedef struct bqa_qtensor {
+    int32_t fmt;              /* bqa_dtype: BQA_INT8, BQA_FP8E4M3 or BQA_MXFP4 */
+    int32_t axis;             /* 0: blocks along tokens of rows / along d; 1: per channel / along tokens */
+    int32_t block;            /* token block for INT8 axis 0; 32 for MXFP4; N for per-channel */
+    void* codes;
+    void* scales;
+} bqa_qtensor;
+
+/* Operations, for bqa_workspace_size(). */
+enum {
+    BQA_OP_QUANTIZE_Q = 0, BQA_OP_QUANTIZE_K = 1, BQA_OP_QUANTIZE_V = 2, BQA_OP_QUANTIZE_DO = 3,
+    BQA_OP_SELECT = 4, BQA_OP_FWD = 5, BQA_OP_BWD = 6
+};
+
+/* ABI version of the loaded library (BQA_ABI_VERSION it was built with). */
+int32_t bqa_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* bqa_status_string(bqa_status status);
+
+/* Bytes of workspace the operation `op` needs for problem `p`; 0 when it needs
+ * none or the problem is invalid. */
+size_t bqa_workspace_size(const bqa_problem* p, int32_t op);
+
+/*
+ * Quantize one operand into `out` (whose fmt/axis/block select the format;
+ * codes and scales must be allocated by the caller in the layout above).
+ *
+ *  - Q, dO, INT8 axis 0: per token block of out->block tokens, scale =
+ *    amax/127 and code = round-half-even(x * (127/amax)) clamped to +-127,
+ *    both divisions correctly rounded in fp32 ("SageBwd", Methodology 1:
+ *    per-block INT8).
+ *  - K, INT8 axis 0 with p->smooth_k: K-smoothing ("SageBwd", Methodology 4
+ *    and Results): mu = fp32(sum_t K / N - eps) per (b, h, channel), summed
+ *    in fp64, written to k_mean [B, Hkv, d] when k_mean is not NULL; the codes
+ *    are those of fp32(K - mu).
+ *  - V, INT8 or FP8E4M3 axis 1: one scale per (b, h, channel) over all tokens,
+ *    amax/127 or amax/448; e4m3 codes round to nearest even and saturate.
+ *  - Q, K, MXFP4 axis 0; V, MXFP4 axis 1: OCP MX blocks of 32 along d (Q, K)
+ *    or along tokens (V) ("Attn-QAT", §1 Problem: FP4 has 15 values;
+ *    "ThriftAttention", Method step 2: micro-scaled FP4): X = 2^e with
+ *    e = floor(log2 amax) - 2 clamped to [-127, 127], codes e2m1(x / X),
+ *    nearest-even, saturating at 6.  With block_means != NULL and role Q or K
+ *    the means over each p->sel_block tokens are written as fp32
+ *    [B, H, N / sel_block, d] ("ThriftAttention", Method step 1).
+ *  A block whose amax is 0 (or whose inverse scale overflows fp32) gets
+ *  scale 0 and all-zero codes.
+ * `x` is [B, H, N, d] bf16 (fp16 for Q, K, V allowed in BQA_SAGE_I8_F16PV).
+ */
+bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_tensor* x,
+                               bqa_qtensor* out, float* k_mean, float* block_means,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ThriftAttention block selection ("ThriftAttention", Method step 1): for
+ * every (b, query head h, query block i) the importance of key block j is
+ * qbar_i . kbar_j (kbar of KV head h / (Hq/Hkv)) over the valid key blocks
+ * (causal: j <= i + nkb - nqb); the k_i = max(1, ceil(n_valid * budget))
+ * highest-scoring blocks (equal scores: smaller j first) are written to
+ * sel_idx [B, Hq, nqb, max_sel] in ascending order, unused slots -1, and k_i
+ * to sel_cnt [B, Hq, nqb].  q_means [B, Hq, nqb, d], k_means [B, Hkv, nkb, d]
+ * are fp32 block means; nqb = ceil(Nq / sel_block) (a decode query is its own
+ * block), nkb = Nk / sel_block; max_sel = max(1, ceil(nkb * budget)).
+ */
+bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const float* k_means,
+                             int32_t* sel_idx, int32_t* sel_cnt,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Attention forward.  Output o [B, Hq, Nq, d] (bf16; fp16 in
+ * BQA_SAGE_I8_F16PV) and, when lse is not NULL, the natural-log
+ * log-sum-exp of every row, fp32 [B, Hq, Nq].
+ *
+ *  - Sage modes ("SageBwd", Methodology 1): q, k are the INT8 token-block
+ *    codes (k of the smoothed K); v is per-channel e4m3 (F8PV) or int8
+ *    (I8PV) codes, or for F16PV v_hi holds V in fp16 and v is unused.
+ *    Keys are visited in tiles of k_block, ascending; per tile the running max
+ *    is updated, P = exp(s - m) is rounded for P.V as the mode says, and the
+ *    row sum accumulates the unrounded P.
+ *  - BQA_QAT_MXFP4 ("Attn-QAT", §2): q, k MXFP4 along d, v MXFP4 along tokens;
+ *    key tiles of 128; P is MXFP4 per 32 keys of the row for O; when o_aux is
+ *    not NULL, O' = sum bf16(P) V / l is written too (Principle 2).
+ *    Non-causal only.
+ *  - BQA_THRIFT ("ThriftAttention", Method step 2 and kernel paragraph): per
+ *    query block, the unselected valid key blocks go through the FP4 path
+ *    (MXFP4 q, k, v; P quantised in two levels: scaled so its row max is 6,
+ *    then MXFP4 per 32 keys), then the selected blocks (sel_idx, sel_cnt from
+ *    bqa_select_blocks) through the bf16 path (q_hi, k_hi, v_hi), all merged
+ *    by one online softmax.  Nq == 1 is decode: the key range is cut into
+ *    p->num_splits parts whose partial results are merged at the end.
+ */
+bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
+                        const bqa_qtensor* v, const bqa_tensor* q_hi, const bqa_tensor* k_hi,
+                        const bqa_tensor* v_hi, const int32_t* sel_idx, const int32_t* sel_cnt,
+                        bqa_tensor* o, bqa_tensor* o_aux, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Attention backward: dq, dk, dv [B, H, N, d] bf16 from the forward's codes,
+ * its lse and d_o.
+ *  - BQA_SAGE_I8_I8PV ("SageBwd", Methodology 2, Limitations): delta =
+ *    rowsum(dO o O) with o_for_delta = the forward's O; dO is quantized to
+ *    INT8 per q_block tokens; tiles of 128 queries x 64 keys; P and dS are
+ *    INT8 with one scale per tile; dV = P^T dO, dQ = tau dS K and
+ *    dK = tau dS^T Q run as INT8 products, dP = dO V^T in bf16 from v_hi.
+ *  - BQA_QAT_MXFP4 ("Attn-QAT", §2 Principles 1 and 2): o_for_delta = O';
+ *    P is recomputed from the same FP4 scores and fake-quantised to MXFP4
+ *    with the forward's blocking for dV; dP, dQ, dK run in bf16 against the
+ *    FP4 operands; delta = rowsum(dO o O').
+ */
+bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
+                        const bqa_qtensor* v, const bqa_tensor* v_hi,
+                        const bqa_tensor* o_for_delta, const float* lse, const bqa_tensor* d_o,
+                        bqa_tensor* dq, bqa_tensor* dk, bqa_tensor* dv,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Test hook: the raw Q K^T accumulator of one tile as the forward kernel's
+ * matrix-instruction code computes it — int32 [32 x 32] for INT8 codes
+ * (exact integer dot products) or fp32 [32 x 32] for MXFP4 codes (the
+ * instruction's fp32 result, before tau) — for query rows q_tile*32 .. +31
+ * and key rows k_tile*32 .. +31 of (b, h), written row-major to out.
+ */
+bqa_status bqa_debug_qk_scores(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
+                               int32_t b, int32_t h, int32_t q_tile, int32_t k_tile, void* out,
+                               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BQA_H */

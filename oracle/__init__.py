@@ -63,6 +63,7 @@ def _declare(L):
         "orc_bf16_value": (d, [d]),
         "orc_f16_value": (d, [d]),
         "orc_i8_encode": (C.c_int8, [f, f]),
+        "orc_round_array": (None, [vp, C.c_int64, i, vp]),
         "orc_i8_scale": (None, [f, vp, vp]),
         "orc_smooth_mean": (i, [vp, i, i, i, d, vp]),
         "orc_quant_i8_tokblock": (None, [vp, vp, i, i, i, i, vp, vp]),
@@ -140,10 +141,12 @@ def f16_value(x: float) -> float:
     return float(lib().orc_f16_value(float(x)))
 
 
-def round_bf16(a: np.ndarray) -> np.ndarray:
-    """Round an array to bf16 values (nearest-even), via the oracle's encoder."""
-    f = np.frompyfunc(lambda v: lib().orc_bf16_value(float(v)), 1, 1)
-    return f(np.asarray(a, dtype=np.float64)).astype(np.float64)
+def round_to(a: np.ndarray, fmt: str) -> np.ndarray:
+    """Round an array to bf16 or fp16 values (nearest-even) with the oracle's encoder."""
+    x = np.ascontiguousarray(a, dtype=np.float64)
+    out = np.empty_like(x)
+    lib().orc_round_array(_p(x), x.size, 0 if fmt == "bf16" else 1, _p(out))
+    return out
 
 
 # ---------------------------------------------------------------- quantisers

@@ -129,6 +129,11 @@ uint16_t orc_f16_bits(double x) {
 double orc_bf16_value(double x) { return orc_round_grid(x, 7, -126, 0x1.FEp127, 0); }
 double orc_f16_value(double x) { return orc_round_grid(x, 10, -14, 65504.0, 0); }
 
+/* Round n values to bf16 (fmt 0) or fp16 (fmt 1), nearest-even, as values. */
+void orc_round_array(const double* x, int64_t n, int fmt, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = fmt == 0 ? orc_bf16_value(x[i]) : orc_f16_value(x[i]);
+}
+
 /* Symmetric INT8 with a per-block absmax scale: scale = amax/127 and
  * inv = 127/amax, both correctly-rounded fp32 divisions; the code is the
  * nearest-even integer of the fp32 product x*inv, clamped to [-127, 127].

@@ -30,6 +30,7 @@ uint16_t orc_bf16_bits(double x);
 uint16_t orc_f16_bits(double x);
 double  orc_bf16_value(double x);           /* x rounded to bf16, as a value */
 double  orc_f16_value(double x);
+void    orc_round_array(const double* x, int64_t n, int fmt, double* out);
 int8_t  orc_i8_encode(float x, float inv);  /* clamp(rint(fp32(x*inv)), -127, 127) */
 void    orc_i8_scale(float amax, float* scale, float* inv);
 

@@ -1,0 +1,147 @@
+"""The C-ABI library loads, exports every symbol bqa.h declares, and rejects
+bad arguments on the host before touching a device (CPU only; with valid
+arguments and no GPU the calls return BQA_E_DEVICE)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import bit_quantized_attention_amd as bqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bqa.LIB_PATH):
+        pytest.fail("libbqa.so is not built (run __graft_entry__.build())")
+    return bqa.lib()
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "bqa.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(bqa_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == set(bqa.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", bqa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (bqa_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(L, n) is not None
+
+
+def test_version_and_strings(L):
+    assert bqa.bqa_abi_version() == 1
+    for s in range(-7, 1):
+        assert isinstance(bqa.bqa_status_string(s), str) and bqa.bqa_status_string(s)
+    assert bqa.bqa_status_string(-99) == "unknown status"
+
+
+class FakeTensor:
+    """A host object posing as a device tensor (only pointer and strides are read)."""
+
+    def __init__(self, ptr, shape, strides, dtype):
+        self._p, self.shape, self._s, self.dtype = ptr, shape, strides, dtype
+
+    def data_ptr(self):
+        return self._p
+
+    def dim(self):
+        return 4
+
+    def stride(self, i):
+        return self._s[i]
+
+
+def _dense(ptr=0x10000, strides=(4096 * 128 * 16, 4096 * 128, 128, 1), dtype=bqa.BQA_BF16):
+    t = bqa.bqa_tensor()
+    t.data, t.dtype = ptr, dtype
+    for i, s in enumerate(strides):
+        t.stride[i] = s
+    return t
+
+
+def _p(**kw):
+    base = dict(B=2, Hq=16, Hkv=16, Nq=4096, Nk=4096, d=128, causal=1, mode=bqa.BQA_SAGE_I8_F8PV, q_block=128,
+                k_block=64, smooth_k=1, smooth_eps=0.0)
+    base.update(kw)
+    return bqa.problem(**base)
+
+
+def _q(fmt=bqa.BQA_INT8, axis=0, block=128, codes=0x20000, scales=0x30000):
+    return bqa.qtensor(fmt, axis, block, codes, scales)
+
+
+def _quant(p, role, x, out, ws=0x40000, wsb=1 << 30):
+    return bqa.lib().bqa_quantize_blocks(C.byref(p), role, None if x is None else C.byref(x), C.byref(out), None,
+                                         None, ws, wsb, None)
+
+
+def test_quantize_validation(L):
+    x = _dense()
+    assert _quant(None if False else _p(d=96), bqa.BQA_ROLE_Q, x, _q()) == bqa.BQA_E_UNSUPPORTED
+    assert _quant(_p(Hq=16, Hkv=3), bqa.BQA_ROLE_Q, x, _q()) == bqa.BQA_E_SHAPE
+    assert _quant(_p(B=0), bqa.BQA_ROLE_Q, x, _q()) == bqa.BQA_E_SHAPE
+    assert _quant(_p(), bqa.BQA_ROLE_Q, None, _q()) == bqa.BQA_E_NULL
+    assert _quant(_p(), bqa.BQA_ROLE_Q, _dense(ptr=0x10008), _q()) == bqa.BQA_E_ALIGN
+    assert _quant(_p(), bqa.BQA_ROLE_Q, _dense(strides=(1 << 20, 1 << 16, 130, 1)), _q()) == bqa.BQA_E_ALIGN
+    assert _quant(_p(), bqa.BQA_ROLE_Q, _dense(strides=(1 << 20, 1 << 16, 128, 2)), _q()) == bqa.BQA_E_ALIGN
+    assert _quant(_p(), bqa.BQA_ROLE_Q, x, _q(codes=0x20004)) == bqa.BQA_E_ALIGN
+    assert _quant(_p(), bqa.BQA_ROLE_Q, x, _q(codes=0)) == bqa.BQA_E_NULL
+    assert _quant(_p(), bqa.BQA_ROLE_Q, x, _q(block=96)) == bqa.BQA_E_UNSUPPORTED
+    assert _quant(_p(Nq=4032), bqa.BQA_ROLE_Q, x, _q(block=128)) == bqa.BQA_E_UNSUPPORTED
+    assert _quant(_p(), 7, x, _q()) == bqa.BQA_E_UNSUPPORTED
+    # smoothing needs a workspace
+    assert _quant(_p(), bqa.BQA_ROLE_K, x, _q(block=64), ws=0, wsb=0) == bqa.BQA_E_WORKSPACE
+    need = bqa.bqa_workspace_size(_p(), bqa.BQA_OP_QUANTIZE_K)
+    assert need > 0
+    assert _quant(_p(), bqa.BQA_ROLE_K, x, _q(block=64), wsb=need - 1) == bqa.BQA_E_WORKSPACE
+    assert bqa.bqa_workspace_size(_p(d=96), bqa.BQA_OP_QUANTIZE_K) == 0
+    # per-channel V: block must be N
+    assert _quant(_p(), bqa.BQA_ROLE_V, x, _q(fmt=bqa.BQA_FP8E4M3, axis=1, block=64)) == bqa.BQA_E_UNSUPPORTED
+    # valid arguments: no GPU here, so the device check answers
+    import torch
+    if not torch.cuda.is_available():
+        assert _quant(_p(), bqa.BQA_ROLE_Q, x, _q()) == bqa.BQA_E_DEVICE
+        assert _quant(_p(), bqa.BQA_ROLE_V, x, _q(fmt=bqa.BQA_FP8E4M3, axis=1, block=4096)) == bqa.BQA_E_DEVICE
+
+
+def test_fwd_validation(L):
+    o = _dense()
+    q, k = _q(), _q(block=64)
+    v = _q(fmt=bqa.BQA_FP8E4M3, axis=1, block=4096)
+
+    def fwd(p, q=q, k=k, v=v, o=o, v_hi=None):
+        return bqa.lib().bqa_attn_fwd(C.byref(p), C.byref(q), C.byref(k), None if v is None else C.byref(v), None,
+                                      None, None if v_hi is None else C.byref(v_hi), None, None,
+                                      None if o is None else C.byref(o), None, None, None, 0, None)
+    assert fwd(_p(k_block=32)) == bqa.BQA_E_UNSUPPORTED
+    assert fwd(_p(q_block=32)) == bqa.BQA_E_UNSUPPORTED
+    assert fwd(_p(causal=1, Nq=8192)) == bqa.BQA_E_SHAPE
+    assert fwd(_p(), q=_q(block=64)) == bqa.BQA_E_UNSUPPORTED          # block differs from q_block
+    assert fwd(_p(), v=_q(fmt=bqa.BQA_INT8, axis=1, block=4096)) == bqa.BQA_E_UNSUPPORTED
+    assert fwd(_p(), o=None) == bqa.BQA_E_NULL
+    assert fwd(_p(), o=_dense(dtype=bqa.BQA_FP16)) == bqa.BQA_E_UNSUPPORTED
+    assert fwd(_p(mode=bqa.BQA_SAGE_I8_F16PV), v=None) == bqa.BQA_E_NULL
+    assert fwd(_p(mode=9)) == bqa.BQA_E_UNSUPPORTED
+    import torch
+    if not torch.cuda.is_available():
+        assert fwd(_p()) == bqa.BQA_E_DEVICE
+        assert fwd(_p(mode=bqa.BQA_SAGE_I8_F16PV), v=None, v_hi=_dense(dtype=bqa.BQA_FP16),
+                   o=_dense(dtype=bqa.BQA_FP16)) == bqa.BQA_E_DEVICE
+
+
+def test_debug_scores_validation(L):
+    q, k = _q(), _q(block=64)
+    f = bqa.lib().bqa_debug_qk_scores
+    assert f(C.byref(_p()), C.byref(q), C.byref(k), 0, 0, 0, 0, None, None) == bqa.BQA_E_NULL
+    assert f(C.byref(_p()), C.byref(q), C.byref(k), 2, 0, 0, 0, 0x1000, None) == bqa.BQA_E_SHAPE
+    assert f(C.byref(_p()), C.byref(q), C.byref(k), 0, 0, 128, 0, 0x1000, None) == bqa.BQA_E_SHAPE
+    assert f(C.byref(_p()), C.byref(q), C.byref(k), 0, 0, 0, -1, 0x1000, None) == bqa.BQA_E_SHAPE

@@ -1,0 +1,152 @@
+"""GPU parity of the SageAttention INT8 path (quantisers + forward) against the
+oracle, through the C ABI.  Codes, scales, smoothing means and integer scores
+must match bit for bit; outputs within max-abs 2e-2 and mean-rel 1e-3 of the
+oracle rounded to the output format."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from tests.helpers import SageOracle, assert_same, compare_outputs, tau_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import bit_quantized_attention_amd as bqa
+    bqa.lib()
+
+
+def _run(w, mode_name, q_block, eps, Nq=None):
+    """Generate the workload, run the GPU path, and build the oracle."""
+    import bit_quantized_attention_amd as bqa
+    from bit_quantized_attention_amd.runner import SagePath, sage_problem, to_device
+    Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
+    if Nq is not None:
+        Q = np.ascontiguousarray(Q[:, :, -Nq:])
+    mode = {"f16": bqa.BQA_SAGE_I8_F16PV, "f8": bqa.BQA_SAGE_I8_F8PV, "i8": bqa.BQA_SAGE_I8_I8PV}[mode_name]
+    p = sage_problem(w.B, w.Hq, w.Hkv, Q.shape[2], K.shape[2], w.d, w.causal, mode, q_block=q_block,
+                     smooth_k=True, smooth_eps=eps)
+    vdt = "fp16" if mode_name == "f16" else w.dtype
+    path = SagePath(p, to_device(Q, w.dtype), to_device(K, w.dtype), to_device(V, vdt))
+    path.step()
+    torch.cuda.synchronize()
+    orc = SageOracle(Q, K, V, q_block=q_block, eps=eps, pv=mode_name)
+    return p, path, orc
+
+
+def _check_codes(p, path, orc):
+    assert orc.uncertified == 0
+    B, Hq, Hkv, d = p.B, p.Hq, p.Hkv, p.d
+    assert_same(path.mu.cpu().numpy().reshape(-1, d), orc.mu, "K token-mean")
+    assert_same(path.qc.cpu().numpy().reshape(orc.qc.shape), orc.qc, "Q codes")
+    assert_same(path.qs.cpu().numpy().reshape(orc.qs.shape), orc.qs, "Q scales")
+    assert_same(path.kc.cpu().numpy().reshape(orc.kc.shape), orc.kc, "K codes")
+    assert_same(path.ks.cpu().numpy().reshape(orc.ks.shape), orc.ks, "K scales")
+    if orc.vc is not None:
+        assert_same(path.vc.cpu().numpy().reshape(orc.vc.shape), orc.vc, "V codes")
+        assert_same(path.vs.cpu().numpy().reshape(orc.vs.shape), orc.vs, "V scales")
+
+
+def _check_heads(p, path, orc, heads, rows=None):
+    tau = tau_for(p.d)
+    O = path.o.float().cpu().numpy()
+    L = path.lse.cpu().numpy()
+    fmt = "fp16" if path.o.dtype == torch.float16 else "bf16"
+    for (b, h) in heads:
+        r = rows or (0, p.Nq)
+        ref, lse = orc.forward(b, h, bool(p.causal), tau, rows=r)
+        compare_outputs(O[b, h, r[0]:r[1]], ref, fmt, what=f"O[b={b},h={h},rows={r}]")
+        assert np.abs(L[b, h, r[0]:r[1]] - lse).max() < 2e-3
+
+
+def test_c1_tiny_fp16_pv():
+    """Tiny INT8 forward (B=H=1, N=128, d=64, non-causal, fp16 P.V)."""
+    w = wl.WORKLOADS["c1"]
+    p, path, orc = _run(w, "f16", q_block=64, eps=0.0)
+    _check_codes(p, path, orc)
+    _check_heads(p, path, orc, [(0, 0)])
+
+
+@pytest.mark.parametrize("N", [512, 1024])
+def test_c2_recipe_small_causal(N):
+    """c2 recipe (outlier channels, K bias, fp8 P.V) at sizes spanning many tiles."""
+    w = wl.with_len(wl.WORKLOADS["c2"], N, b=1, hq=3, hkv=3)
+    p, path, orc = _run(w, "f8", q_block=128, eps=0.0)
+    _check_codes(p, path, orc)
+    _check_heads(p, path, orc, [(0, 0), (0, 2)])
+
+
+def test_c2_ragged_query_tail():
+    """Nq not a multiple of the 128-row workgroup tile (q_block 64): last tile half full."""
+    w = wl.with_len(wl.WORKLOADS["c2"], 320, b=1, hq=2, hkv=2)
+    p, path, orc = _run(w, "f8", q_block=64, eps=0.0)
+    _check_codes(p, path, orc)
+    _check_heads(p, path, orc, [(0, 0), (0, 1)])
+
+
+def test_c2_short_queries_bottom_right_causal():
+    """Nq < Nk with causal masking aligned to the bottom-right corner."""
+    w = wl.with_len(wl.WORKLOADS["c2"], 512, b=1, hq=2, hkv=2)
+    p, path, orc = _run(w, "f8", q_block=128, eps=0.0, Nq=256)
+    _check_heads(p, path, orc, [(0, 0), (0, 1)])
+
+
+def test_c3_recipe_int8_pv():
+    """SageBwd training forward (QK-norm inputs, eps=1e-3, int8 P.V)."""
+    w = wl.with_len(wl.WORKLOADS["c3"], 512, hq=2, hkv=2)
+    p, path, orc = _run(w, "i8", q_block=128, eps=1e-3)
+    _check_codes(p, path, orc)
+    _check_heads(p, path, orc, [(0, 0), (0, 1)])
+
+
+def test_c2_full_size_sampled():
+    """The full c2 workload (B=2, H=16, N=4096) in the launch configuration the
+    benchmark times; all codes compared, outputs on sampled query tiles."""
+    w = wl.WORKLOADS["c2"]
+    p, path, orc = _run(w, "f8", q_block=128, eps=0.0)
+    _check_codes(p, path, orc)
+    for (b, h, r) in [(0, 0, (0, 128)), (1, 15, (3968, 4096)), (0, 7, (2048, 2176)), (1, 3, (1920, 2048))]:
+        _check_heads(p, path, orc, [(b, h)], rows=r)
+
+
+def test_debug_scores_bit_exact():
+    """Integer Q K^T tiles through the forward kernel's tile code equal the
+    oracle codes' exact integer dot products."""
+    import bit_quantized_attention_amd as bqa
+    w = wl.with_len(wl.WORKLOADS["c2"], 512, b=2, hq=2, hkv=2)
+    p, path, orc = _run(w, "f8", q_block=128, eps=0.0)
+    out = torch.empty((32, 32), dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(0)
+    for _ in range(6):
+        b, h = int(rng.integers(2)), int(rng.integers(2))
+        qt, kt = int(rng.integers(16)), int(rng.integers(16))
+        bqa.bqa_debug_qk_scores(p, path.qq, path.kq, b, h, qt, kt, out)
+        torch.cuda.synchronize()
+        iq = b * 2 + h
+        ref = orc.qc[iq, qt * 32:(qt + 1) * 32].astype(np.int64) @ orc.kc[iq, kt * 32:(kt + 1) * 32].astype(np.int64).T
+        assert_same(out.cpu().numpy(), ref.astype(np.int32), f"S_int tile b={b} h={h} q={qt} k={kt}")
+
+
+def test_deterministic_and_zero_block():
+    """Two passes give identical bits; an all-zero Q block gets scale 0 and
+    zero codes and its rows attend uniformly."""
+    import bit_quantized_attention_amd as bqa
+    from bit_quantized_attention_amd.runner import SagePath, sage_problem, to_device
+    w = wl.with_len(wl.WORKLOADS["c2"], 512, b=1, hq=2, hkv=2)
+    Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
+    Q[0, 1, 128:256] = 0.0
+    p = sage_problem(1, 2, 2, 512, 512, 128, False, bqa.BQA_SAGE_I8_F8PV)
+    path = SagePath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
+    o1 = path.step().clone()
+    c1 = path.qc.clone()
+    o2 = path.step().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(c1, path.qc)
+    assert path.qs[0, 1, 1].item() == 0.0 and not path.qc[0, 1, 128:256].any()
+    orc = SageOracle(Q, K, V, q_block=128, pv="f8")
+    ref, _ = orc.forward(0, 1, False, tau_for(128), rows=(128, 256))
+    compare_outputs(o1[0, 1, 128:256].float().cpu().numpy(), ref)
