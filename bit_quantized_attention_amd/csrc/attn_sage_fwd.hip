@@ -4,7 +4,8 @@
 // per-block scales) and 4 (K-smoothing, which happens in the K quantiser):
 //   S_int = Qhat Khat^T exactly in int32 (i8 matrix instructions), scores
 //   s = S_int * s_q * s_k * tau; online softmax over key tiles of 64
-//   (FlashAttention-2 style); P rounded for the P.V product as fp16 (V fp16),
+//   (FlashAttention-2 style) whose reference point is the running max rounded
+//   up to a power of two; P rounded for the P.V product as fp16 (V fp16),
 //   e4m3(448 P) (V per-channel e4m3) or int8 per (row, tile) (V per-channel
 //   int8); the row sum accumulates the unrounded P.
 //
@@ -12,15 +13,17 @@
 // (batch, head); each wavefront owns 32 rows.  The score tile is computed
 // transposed, S^T = Khat Qhat^T (A = key rows from LDS, B = the wavefront's
 // query rows held in registers), so the 32x32 accumulator puts one query row
-// in each lane (32 keys per lane, the other 32 of the tile in lane l^32).
-// Row max and row sum are then in-lane reductions plus one permlane32 swap,
-// and the probabilities are already laid out as the B operand of
-// O^T = V^T P^T, which therefore needs no LDS round trip.  K tiles and the
-// channel-major V tiles are staged in LDS with XOR-swizzled 16-byte chunks
-// (conflict-free 128-bit reads for 16 consecutive lanes), double-buffered
-// through registers so the next tile's HBM/L2 loads overlap the current
-// tile's math.  Causal workgroups are issued heaviest-first; consecutive
-// workgroup ids take different heads, which keeps each head on one XCD.
+// in each lane.  The K rows are fed through a fixed permutation (sigma) so
+// that each lane half holds 16 consecutive keys: row max and row sum are
+// in-lane reductions plus one permlane32 swap, and the probabilities are
+// already the B operand of O^T = V^T P^T against contiguous V^T chunks, with
+// no LDS round trip.  K tiles and channel-major V tiles go global ->
+// registers -> LDS (XOR-swizzled 16-byte chunks, conflict-free for 16
+// consecutive lanes) three tiles deep; the loop is unrolled by the buffer
+// count so every LDS address is an immediate offset.  Causal workgroups are
+// issued heaviest-first; consecutive workgroup ids take different heads,
+// which keeps each head on one XCD.
+#include <type_traits>
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -30,40 +33,231 @@ namespace {
 
 constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile (= INT8 K block)
+constexpr int NBUF = 3;   // LDS tiles in flight: QK(j+1), PV(j), staging of j+2
 
-// LDS byte offset of logical 16-byte chunk `c` of row `r` in a tile whose rows
-// are `row_bytes` long; XOR swizzle so 16 consecutive rows read at one logical
-// chunk land in 16 distinct 16-byte bank groups.
+// XOR swizzle of the 16-byte chunks of a tile row (rows of ROW_BYTES).  For
+// the K tile (read through the row permutation below) and for the V^T tile
+// (read by consecutive rows) 16 consecutive lanes reading one logical chunk
+// hit 16 distinct 16-byte bank groups.
 template <int ROW_BYTES>
-__device__ __forceinline__ int swz(int r, int c) {
-    constexpr int rows_per_256 = 256 / ROW_BYTES;
-    constexpr int nch = ROW_BYTES / 16;
-    return r * ROW_BYTES + 16 * (c ^ ((r / rows_per_256) & (nch - 1)));
+__device__ __forceinline__ int swz_k(int r, int c) {
+    if constexpr (ROW_BYTES == 128) return r * 128 + 16 * (c ^ (((r >> 1) & 7) ^ (((r >> 4) & 1) << 2)));
+    else return r * 64 + 16 * (c ^ (((r >> 2) & 3) ^ (((r >> 4) & 1) << 1)));
+}
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz_v(int r, int c) {
+    if constexpr (ROW_BYTES == 128) return r * 128 + 16 * (c ^ ((r >> 1) & 7));
+    else return r * 64 + 16 * (c ^ ((r >> 2) & 3));
 }
 
-// S^T tile of 64 keys x 32 queries for one wavefront: acc0 keys 0..31,
-// acc1 keys 32..63 (of the tile in LDS); lane (q = l%32, half h) register i
-// holds key 8(i/4) + 4h + i%4 (+32 for acc1).
+// Row of the K tile that lane l feeds into matrix row l%32 of the S^T product.
+// With this permutation the accumulator register i of lane (q, half h) holds
+// key 16h + i (plus 32 for the second 32-key half): every lane half owns 16
+// consecutive keys, so the probabilities line up with contiguous V^T chunks.
+__device__ __forceinline__ int sigma(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+
+// S^T tile of 64 keys x 32 queries for one wavefront.  acc0: keys 16h + i,
+// acc1: keys 32 + 16h + i (i = register index).
 template <int D>
-__device__ __forceinline__ void qk_tile(const uint8_t* k_lds, const v4i* qb, int lq, int h, v16i& acc0, v16i& acc1) {
+__device__ __forceinline__ void qk_tile(const uint8_t* k_lds, const v4i* qb, int krow, int h, v16i& acc0, v16i& acc1) {
     acc0 = v16i{};
     acc1 = v16i{};
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-        v4i a0 = *(const v4i*)(k_lds + swz<D>(lq, 2 * kk + h));
-        v4i a1 = *(const v4i*)(k_lds + swz<D>(32 + lq, 2 * kk + h));
+        v4i a0 = *(const v4i*)(k_lds + swz_k<D>(krow, 2 * kk + h));
+        v4i a1 = *(const v4i*)(k_lds + swz_k<D>(32 + krow, 2 * kk + h));
         acc0 = mfma_i8_32x32x32(a0, qb[kk], acc0);
         acc1 = mfma_i8_32x32x32(a1, qb[kk], acc1);
     }
 }
 
+template <int PV, int D>
+struct Staging {
+    static constexpr int V_ROW = PV == PV_F16 ? BN * 2 : BN;   // bytes per V^T row in LDS
+    static constexpr int KPT = BN * D / 16 / 256;              // 16-byte K chunks per thread
+    static constexpr int VPT = D * V_ROW / 16 / 256;           // 16-byte V chunks per thread
+    v4i k[KPT];
+    v4i v[VPT];
+    float ks;   // the tile's K scale
+};
+
+template <int PV, int D>
+__device__ __forceinline__ void stage_load(Staging<PV, D>& st, const SageFwdArgs& a, const int8_t* kbase,
+                                           int b, int hk, int bhk, int t0, int tid) {
+    using S = Staging<PV, D>;
+    st.ks = a.ks[(int64_t)bhk * (a.Nk / BN) + t0 / BN];
+#pragma unroll
+    for (int u = 0; u < S::KPT; ++u) {
+        const int g = tid + 256 * u, r = g / (D / 16), c = g % (D / 16);
+        st.k[u] = *(const v4i*)(kbase + (int64_t)(t0 + r) * D + 16 * c);
+    }
+    if constexpr (PV == PV_F16) {
+        const uint16_t* vb = (const uint16_t*)a.v16.p + b * a.v16.sB + hk * a.v16.sH;
+#pragma unroll
+        for (int u = 0; u < S::VPT; ++u) {
+            const int g = tid + 256 * u, key = g / (D / 8), c8 = (g % (D / 8)) * 8;
+            st.v[u] = *(const v4i*)(vb + (int64_t)(t0 + key) * a.v16.sN + c8);
+        }
+    } else {
+        const uint8_t* vb = a.vc + (int64_t)bhk * D * a.Nk + t0;
+#pragma unroll
+        for (int u = 0; u < S::VPT; ++u) {
+            const int g = tid + 256 * u, r = g / 4, q = g % 4;
+            st.v[u] = *(const v4i*)(vb + (int64_t)r * a.Nk + 16 * q);
+        }
+    }
+}
+
+template <int PV, int D>
+__device__ __forceinline__ void stage_store(const Staging<PV, D>& st, uint8_t* k_lds, uint8_t* v_lds, float* ks_lds,
+                                            int tid) {
+    using S = Staging<PV, D>;
+    if (tid == 0) *ks_lds = st.ks;
+#pragma unroll
+    for (int u = 0; u < S::KPT; ++u) {
+        const int g = tid + 256 * u, r = g / (D / 16), c = g % (D / 16);
+        *(v4i*)(k_lds + swz_k<D>(r, c)) = st.k[u];
+    }
+    if constexpr (PV == PV_F16) {
+        // transpose fp16 V into V^T [channel][key] (128-byte rows)
+#pragma unroll
+        for (int u = 0; u < S::VPT; ++u) {
+            const int g = tid + 256 * u, key = g / (D / 8), c8 = (g % (D / 8)) * 8;
+            const uint16_t* e = (const uint16_t*)&st.v[u];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                *(uint16_t*)(v_lds + swz_v<128>(c8 + k, key / 8) + 2 * (key % 8)) = e[k];
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < S::VPT; ++u) {
+            const int g = tid + 256 * u, r = g / 4, q = g % 4;
+            *(v4i*)(v_lds + swz_v<BN>(r, q)) = st.v[u];
+        }
+    }
+}
+
+// Per-wavefront running state of the online softmax.
+template <int D>
+struct RowState {
+    v16f oacc[D / 32];      // O^T accumulator: lane (query lq, half h), channel 32cb + 8(i/4) + 4h + i%4
+    float m;                // running max of the scaled scores (log2 units)
+    float l;                // this lane half's share of the row sum
+};
+
+// Online-softmax update with one 64-key tile (scores s0/s1 from qk_tile) and
+// its P.V product.  `diag_lim` >= 64 means no key of the tile is masked for
+// this wavefront; otherwise register i (+32) is visible iff i (+32) <= diag_lim.
+template <int PV, int D>
+__device__ __forceinline__ void tile_update(RowState<D>& st, const v16i& s0, const v16i& s1, float c, bool diag,
+                                            int diag_lim, const uint8_t* vt, int lq, int h) {
+    constexpr float pbias = PV == PV_F8 ? 8.807354922057604f : 0.0f;    // log2(448): P scaled by 448
+    float f0[16], f1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { f0[i] = (float)s0[i]; f1[i] = (float)s1[i]; }
+    if (diag) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            f0[i] = i > diag_lim ? -__builtin_inff() : f0[i];
+            f1[i] = i + 32 > diag_lim ? -__builtin_inff() : f1[i];
+        }
+    }
+    float mx = __builtin_fmaxf(f0[0], f1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, f0[i]), f1[i]);
+    mx = __builtin_fmaxf(mx, partner32f(mx));
+    // reference point: the running max rounded up to an integer (log2 units),
+    // so rescaling factors are exact powers of two and rarely needed
+    const float m_new = __builtin_fmaxf(st.m, __builtin_ceilf(mx * c));
+    const float alpha = st.m == -__builtin_inff() ? 0.0f : __builtin_ldexpf(1.0f, (int)(st.m - m_new));
+    const float bias = m_new == -__builtin_inff() ? 0.0f : pbias - m_new;
+    float psum0 = 0.0f, psum1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        f0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(f0[i], c, bias));
+        f1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(f1[i], c, bias));
+        psum0 += f0[i];
+        psum1 += f1[i];
+    }
+    const bool moved = m_new != st.m;
+    st.l = st.l * alpha + (psum0 + psum1);
+    st.m = m_new;
+    if (__any(moved)) {
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st.oacc[cb][i] *= alpha;
+    }
+    if constexpr (PV == PV_F8) {
+        v8i pb;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f0[4 * k], f0[4 * k + 1], 0, false);
+            pb[k] = __builtin_amdgcn_cvt_pk_fp8_f32(f0[4 * k + 2], f0[4 * k + 3], w0, true);
+            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k], f1[4 * k + 1], 0, false);
+            pb[4 + k] = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k + 2], f1[4 * k + 3], w1, true);
+        }
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) {
+            const int r = 32 * cb + lq;
+            v4i lo = *(const v4i*)(vt + swz_v<BN>(r, h));
+            v4i hi = *(const v4i*)(vt + swz_v<BN>(r, 2 + h));
+            v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            st.oacc[cb] = mfma_f8_32x32x64(av, pb, st.oacc[cb]);
+        }
+    } else if constexpr (PV == PV_I8) {
+        // int8 P per (row, tile): r = the row's largest P in the tile
+        const float r = mx == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, bias));
+        float inv = r > 0.0f ? 127.0f / r : 0.0f;
+        if (__builtin_isinf(inv)) inv = 0.0f;
+        const float rs = r * (1.0f / 127.0f);
+        v4i pb0, pb1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                w0 |= (uint32_t)enc_i8(f0[4 * k + e], inv) << (8 * e);
+                w1 |= (uint32_t)enc_i8(f1[4 * k + e], inv) << (8 * e);
+            }
+            pb0[k] = (int)w0;
+            pb1[k] = (int)w1;
+        }
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) {
+            const int rr = 32 * cb + lq;
+            v4i v0 = *(const v4i*)(vt + swz_v<BN>(rr, h));
+            v4i v1 = *(const v4i*)(vt + swz_v<BN>(rr, 2 + h));
+            v16i pv = mfma_i8_32x32x32(v0, pb0, v16i{});
+            pv = mfma_i8_32x32x32(v1, pb1, pv);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st.oacc[cb][i] = __builtin_fmaf((float)pv[i], rs, st.oacc[cb][i]);
+        }
+    } else {
+        // fp16 P; four 16-key steps: keys 32(s/2) + 16h + 8(s%2) + e
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            v8h pb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[e] = (_Float16)(s < 2 ? f0[8 * (s % 2) + e] : f1[8 * (s % 2) + e]);
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb) {
+                const int ch = 32 * cb + lq;
+                v8h av = *(const v8h*)(vt + swz_v<128>(ch, 4 * (s / 2) + 2 * h + (s % 2)));
+                st.oacc[cb] = mfma_f16_32x32x16(av, pb, st.oacc[cb]);
+            }
+        }
+    }
+}
+
 template <int PV, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void sage_fwd_kernel(SageFwdArgs a) {
-    constexpr int V_ROW = PV == PV_F16 ? BN * 2 : BN;          // bytes per V^T row in LDS
-    __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][BN * D];
-    __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][D * V_ROW];
+    using S = Staging<PV, D>;
+    __shared__ __attribute__((aligned(16))) uint8_t k_lds[NBUF][BN * D];
+    __shared__ __attribute__((aligned(16))) uint8_t v_lds[NBUF][D * S::V_ROW];
+    __shared__ float ks_lds[NBUF];
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
     const int BHq = a.B * a.Hq;
     const int n_qt = (a.Nq + BM - 1) / BM;
     const int bid = blockIdx.x;
@@ -74,209 +268,65 @@ __global__ __launch_bounds__(256, 2) void sage_fwd_kernel(SageFwdArgs a) {
     const int qrow = q0 + 32 * w + lq;
     const bool row_ok = qrow < a.Nq;
     const int off = a.Nk - a.Nq;
+    const int krow = sigma(lq);
 
-    // ---- this lane's query codes: B operand, Q[qrow][16h + 32kk .. +16)
+    // this lane's query codes: B operand, Q[qrow][16h + 32kk .. +16)
     v4i qb[D / 32];
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
         qb[kk] = row_ok ? *(const v4i*)(a.qc + ((int64_t)bh * a.Nq + qrow) * D + 16 * h + 32 * kk) : v4i{};
     const float cq = row_ok ? a.qs[(int64_t)bh * (a.Nq / a.q_blk) + qrow / a.q_blk] * a.c_log2 : 0.0f;
+    __builtin_amdgcn_s_waitcnt(0);   // Q fragments and scales are in registers before the tile loop
+    const float* kscale = a.ks + (int64_t)bhk * (a.Nk / BN);
 
     const int last_row = min(q0 + BM, a.Nq) - 1;
     const int n_tiles = CAUSAL ? min(a.Nk / BN, (last_row + off) / BN + 1) : a.Nk / BN;
     const int wave_row0 = q0 + 32 * w;
-
-    // ---- staging: global -> registers -> LDS
+    // tiles this wavefront sees at all (causal: up to its last row's diagonal)
+    const int wave_tiles = CAUSAL ? min(n_tiles, (wave_row0 + 31 + off) / BN + 1) : n_tiles;
     const int8_t* kbase = a.kc + (int64_t)bhk * a.Nk * D;
-    constexpr int K_CHUNKS = BN * D / 16;                 // 16-byte chunks per K tile
-    constexpr int KPT = K_CHUNKS / 256;                    // per thread (1 or 2)
-    constexpr int V_CHUNKS = D * V_ROW / 16;
-    constexpr int VPT = V_CHUNKS / 256;
-    uint4 kreg[KPT], vreg[VPT];
 
-    auto gload = [&](int j) {
-        const int t0 = j * BN;
+    RowState<D> rs;
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int g = tid + 256 * u, r = g / (D / 16), c = g % (D / 16);
-            kreg[u] = *(const uint4*)(kbase + (int64_t)(t0 + r) * D + 16 * c);
-        }
-        if constexpr (PV == PV_F16) {
-            const uint16_t* vb = (const uint16_t*)a.v16.p + b * a.v16.sB + hk * a.v16.sH;
-#pragma unroll
-            for (int u = 0; u < VPT; ++u) {
-                const int g = tid + 256 * u, key = g / (D / 8), c8 = (g % (D / 8)) * 8;
-                vreg[u] = *(const uint4*)(vb + (int64_t)(t0 + key) * a.v16.sN + c8);
-            }
-        } else {
-            const uint8_t* vb = a.vc + (int64_t)bhk * D * a.Nk + t0;
-#pragma unroll
-            for (int u = 0; u < VPT; ++u) {
-                const int g = tid + 256 * u, r = g / 4, q = g % 4;
-                vreg[u] = *(const uint4*)(vb + (int64_t)r * a.Nk + 16 * q);
-            }
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int g = tid + 256 * u, r = g / (D / 16), c = g % (D / 16);
-            *(uint4*)(&k_lds[buf][swz<D>(r, c)]) = kreg[u];
-        }
-        if constexpr (PV == PV_F16) {
-            // transpose fp16 V into V^T [channel][key]
-            uint16_t* vt = (uint16_t*)v_lds[buf];
-#pragma unroll
-            for (int u = 0; u < VPT; ++u) {
-                const int g = tid + 256 * u, key = g / (D / 8), c8 = (g % (D / 8)) * 8;
-                const uint16_t* e = (const uint16_t*)&vreg[u];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) vt[(c8 + k) * BN + key] = e[k];
-            }
-        } else {
-            // even dwords of a 64-key row first, odd dwords second (see the B
-            // operand layout of the probabilities), then the 16-byte swizzle
-#pragma unroll
-            for (int u = 0; u < VPT; ++u) {
-                const int g = tid + 256 * u, r = g / 4, q = g % 4;
-                const uint32_t* dw = (const uint32_t*)&vreg[u];
-                const int lo = 8 * q, hi = 32 + 8 * q;
-                *(uint2*)(&v_lds[buf][swz<BN>(r, lo / 16) + lo % 16]) = make_uint2(dw[0], dw[2]);
-                *(uint2*)(&v_lds[buf][swz<BN>(r, hi / 16) + hi % 16]) = make_uint2(dw[1], dw[3]);
-            }
-        }
-    };
+    for (int cb = 0; cb < D / 32; ++cb) rs.oacc[cb] = v16f{};
+    rs.m = -__builtin_inff();
+    rs.l = 0.0f;
 
-    // ---- running state: O^T accumulator (lane: query lq, channels 32cb + 8(i/4) + 4h + i%4)
-    v16f oacc[D / 32];
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = v16f{};
-    float m_run = -__builtin_inff();
-    float l_run = 0.0f;                                   // this lane-half's share of the row sum
-    const float pbias = PV == PV_F8 ? 8.807354922057604f : 0.0f;     // log2(448): P scaled by 448
-
-    if (n_tiles > 0) {
-        gload(0);
-        lstore(0);
-    }
+    // prologue: tiles 0 and 1 in LDS, tile 2 in flight
+    S st;
+    if (n_tiles > 0) { stage_load<PV, D>(st, a, kbase, b, hk, bhk, 0, tid); stage_store<PV, D>(st, k_lds[0], v_lds[0], &ks_lds[0], tid); }
+    if (n_tiles > 1) { stage_load<PV, D>(st, a, kbase, b, hk, bhk, BN, tid); stage_store<PV, D>(st, k_lds[1], v_lds[1], &ks_lds[1], tid); }
     __syncthreads();
+    if (n_tiles > 2) stage_load<PV, D>(st, a, kbase, b, hk, bhk, 2 * BN, tid);
 
-    for (int j = 0; j < n_tiles; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < n_tiles) gload(j + 1);
-        const int t0 = j * BN;
-        // wavefront-uniform: does any of this wave's rows see any key of this tile?
-        const bool wave_live = !CAUSAL || (t0 <= wave_row0 + 31 + off);
-        if (wave_live) {
-            v16i s0, s1;
-            qk_tile<D>(k_lds[buf], qb, lq, h, s0, s1);
+    // One iteration: QK of tile j+1 into (n0, n1) is issued before the softmax
+    // and P.V of tile j (scores in (c0, c1)), so the matrix cores work on the
+    // next tile while the vector ALUs do this one.  Then tile j+2 goes from
+    // registers to LDS, a barrier, and tile j+3's loads are issued.
+    auto body = [&](int j, auto bufc) __attribute__((always_inline)) {
+        constexpr int B0 = decltype(bufc)::value;
+        if (j < wave_tiles) {
+            v16i x0, x1;
+            qk_tile<D>(k_lds[B0], qb, krow, h, x0, x1);
+            const int t0 = j * BN;
             const bool diag = CAUSAL && (t0 + BN - 1 > wave_row0 + off);
-            const int lim = qrow + off - t0;               // keys with tile index <= lim are visible
-            int mx = INT32_MIN;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int k0 = 8 * (i / 4) + 4 * h + (i % 4);
-                if (diag) {
-                    if (k0 > lim) s0[i] = INT32_MIN;
-                    if (k0 + 32 > lim) s1[i] = INT32_MIN;
-                }
-                mx = max(mx, max(s0[i], s1[i]));
-            }
-            mx = max(mx, partner32(mx));
-            const float c = cq * a.ks[(int64_t)bhk * (a.Nk / BN) + j];
-            const float tmax = mx == INT32_MIN ? -__builtin_inff() : (float)mx * c;
-            const float m_new = __builtin_fmaxf(m_run, tmax);
-            const float alpha = m_run == m_new ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-            const float bias = pbias - m_new;
-            float p0[16], p1[16];
-            float psum = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                p0[i] = s0[i] == INT32_MIN ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf((float)s0[i], c, bias));
-                p1[i] = s1[i] == INT32_MIN ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf((float)s1[i], c, bias));
-                psum += p0[i] + p1[i];
-            }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            if (__any(alpha != 1.0f)) {
-#pragma unroll
-                for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
-            }
-            if constexpr (PV == PV_F8) {
-                v8i pb;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(p0[4 * k], p0[4 * k + 1], 0, false);
-                    pb[k] = __builtin_amdgcn_cvt_pk_fp8_f32(p0[4 * k + 2], p0[4 * k + 3], w0, true);
-                    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(p1[4 * k], p1[4 * k + 1], 0, false);
-                    pb[4 + k] = __builtin_amdgcn_cvt_pk_fp8_f32(p1[4 * k + 2], p1[4 * k + 3], w1, true);
-                }
-#pragma unroll
-                for (int cb = 0; cb < D / 32; ++cb) {
-                    const uint8_t* vrow = v_lds[buf];
-                    const int r = 32 * cb + lq;
-                    v4i lo = *(const v4i*)(vrow + swz<BN>(r, 2 * h));
-                    v4i hi = *(const v4i*)(vrow + swz<BN>(r, 2 * h + 1));
-                    v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    oacc[cb] = mfma_f8_32x32x64(av, pb, oacc[cb]);
-                }
-            } else if constexpr (PV == PV_I8) {
-                // int8 P per (row, tile): r = the row's largest P in the tile
-                const float r = mx == INT32_MIN ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf((float)mx, c, bias));
-                float inv = r > 0.0f ? 127.0f / r : 0.0f;
-                if (__builtin_isinf(inv)) inv = 0.0f;
-                const float rs = r * (1.0f / 127.0f);
-                v4i pb0, pb1;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        w0 |= (uint32_t)enc_i8(p0[4 * k + e], inv) << (8 * e);
-                        w1 |= (uint32_t)enc_i8(p1[4 * k + e], inv) << (8 * e);
-                    }
-                    pb0[k] = (int)w0;
-                    pb1[k] = (int)w1;
-                }
-#pragma unroll
-                for (int cb = 0; cb < D / 32; ++cb) {
-                    const uint8_t* vrow = v_lds[buf];
-                    const int rr = 32 * cb + lq;
-                    v4i v0 = *(const v4i*)(vrow + swz<BN>(rr, 2 * h));
-                    v4i v1 = *(const v4i*)(vrow + swz<BN>(rr, 2 * h + 1));
-                    v16i pv = mfma_i8_32x32x32(v0, pb0, v16i{});
-                    pv = mfma_i8_32x32x32(v1, pb1, pv);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[cb][i] = __builtin_fmaf((float)pv[i], rs, oacc[cb][i]);
-                }
-            } else {
-                // fp16 P; the 64 keys go through four 16-deep steps
-                const uint16_t* vt = (const uint16_t*)v_lds[buf];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    v8h pb;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) pb[e] = (_Float16)((s < 2 ? p0 : p1)[8 * (s % 2) + e]);
-#pragma unroll
-                    for (int cb = 0; cb < D / 32; ++cb) {
-                        const int ch = 32 * cb + lq;
-                        const uint16_t* row = vt + ch * BN + 16 * s + 4 * h;
-                        uint2 x0 = *(const uint2*)row;
-                        uint2 x1 = *(const uint2*)(row + 8);
-                        v8h av = __builtin_bit_cast(v8h, make_uint4(x0.x, x0.y, x1.x, x1.y));
-                        oacc[cb] = mfma_f16_32x32x16(av, pb, oacc[cb]);
-                    }
-                }
-            }
+            const float c = __builtin_fmaxf(cq * ks_lds[B0], 1.17549435e-38f);
+            tile_update<PV, D>(rs, x0, x1, c, diag, qrow + off - t0 - 16 * h, v_lds[B0], lq, h);
         }
-        if (j + 1 < n_tiles) lstore(buf ^ 1);
+        if (j + 2 < n_tiles) stage_store<PV, D>(st, k_lds[(B0 + 2) % NBUF], v_lds[(B0 + 2) % NBUF], &ks_lds[(B0 + 2) % NBUF], tid);
         __syncthreads();
+        if (j + 3 < n_tiles) stage_load<PV, D>(st, a, kbase, b, hk, bhk, (j + 3) * BN, tid);
+    };
+    for (int j = 0; j < n_tiles; j += 3) {
+        body(j, std::integral_constant<int, 0>{});
+        if (j + 1 >= n_tiles) break;
+        body(j + 1, std::integral_constant<int, 1>{});
+        if (j + 2 >= n_tiles) break;
+        body(j + 2, std::integral_constant<int, 2>{});
     }
 
-    // ---- epilogue
-    const float l_tot = l_run + partner32f(l_run);
+    // ---- epilogue: O = O^T acc / l (times the V channel scale), LSE in natural log
+    const float l_tot = rs.l + partner32f(rs.l);
     if (!row_ok) return;
     const float inv_l = 1.0f / l_tot;
     uint16_t* orow = (uint16_t*)a.o.p + b * a.o.sB + hq * a.o.sH + (int64_t)qrow * a.o.sN;
@@ -288,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void sage_fwd_kernel(SageFwdArgs a) {
             uint16_t out[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float v = oacc[cb][4 * g + e] * inv_l;
+                float v = rs.oacc[cb][4 * g + e] * inv_l;
                 if constexpr (PV != PV_F16) v *= a.vs[(int64_t)bhk * D + ch0 + e];
                 out[e] = PV == PV_F16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
             }
@@ -298,8 +348,7 @@ __global__ __launch_bounds__(256, 2) void sage_fwd_kernel(SageFwdArgs a) {
     }
     if (a.lse && h == 0) {
         // natural-log LSE; with P scaled by 448 the sum carries that factor
-        const float ln2 = 0.6931471805599453f;
-        float lse = m_run * ln2 + __logf(l_tot);
+        float lse = rs.m * 0.6931471805599453f + __logf(l_tot);
         if (PV == PV_F8) lse -= 6.104793232414985f;   // ln(448)
         a.lse[(int64_t)bh * a.Nq + qrow] = lse;
     }
@@ -312,20 +361,20 @@ __global__ __launch_bounds__(64) void debug_scores_i8_kernel(const int8_t* qc, c
     const int l = threadIdx.x, h = l >> 5, lq = l & 31;
     for (int g = l; g < 32 * D / 16; g += 64) {
         const int r = g / (D / 16), c = g % (D / 16);
-        *(uint4*)(&k_lds[swz<D>(r, c)]) = *(const uint4*)(kc + (int64_t)r * D + 16 * c);
+        *(uint4*)(&k_lds[swz_k<D>(r, c)]) = *(const uint4*)(kc + (int64_t)r * D + 16 * c);
     }
     for (int g = l; g < 32 * D / 16; g += 64) {            // rows 32..63: zero
         const int r = 32 + g / (D / 16), c = g % (D / 16);
-        *(uint4*)(&k_lds[swz<D>(r, c)]) = make_uint4(0, 0, 0, 0);
+        *(uint4*)(&k_lds[swz_k<D>(r, c)]) = make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
     v4i qb[D / 32];
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) qb[kk] = *(const v4i*)(qc + (int64_t)lq * D + 16 * h + 32 * kk);
     v16i s0, s1;
-    qk_tile<D>(k_lds, qb, lq, h, s0, s1);
+    qk_tile<D>(k_lds, qb, sigma(lq), h, s0, s1);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) out[lq * 32 + 8 * (i / 4) + 4 * h + (i % 4)] = s0[i];
+    for (int i = 0; i < 16; ++i) out[lq * 32 + 16 * h + i] = s0[i];
 }
 
 template <int PV, int D>

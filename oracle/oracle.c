@@ -392,7 +392,19 @@ typedef struct {
     double* acc2;    /* d values: second output (Attn-QAT O'), may be NULL */
 } row_state;
 
-/* Move the row to a new running maximum: scale the sums by exp(m_old - m_new). */
+/* The reference point of the online softmax.  Any value at or above the row
+ * maximum gives the same attention in exact arithmetic; the one used here is
+ * the running maximum rounded up to a whole power of two of the probability
+ * scale, m = ln2 * ceil(max / ln2), so that every rescaling factor
+ * exp(m_old - m_new) is an exact power of two and the largest P of a row lies
+ * in (1/2, 1]. */
+static double ref_max(double running_max) {
+    if (running_max == -INFINITY) return running_max;
+    const double ln2 = 0.69314718055994530942;
+    return ln2 * ceil(running_max / ln2);
+}
+
+/* Move the row to a new reference maximum: scale the sums by exp(m_old - m_new). */
 static void row_rescale(row_state* st, double m_new, int d) {
     double alpha = (st->m == -INFINITY) ? 0.0 : exp(st->m - m_new);
     st->l *= alpha;
@@ -421,7 +433,8 @@ static double sage_score(int qk_mode, const int8_t* qc, const float* qs, int q_b
 
 /* Rows [r0, r1) of one head.  Keys are visited in tiles of kv_tile in
  * ascending order (causal: up to the row's diagonal).  Per tile:
- * m_new = max(m, tile max), P = exp(s - m_new), l accumulates the
+ * m_new = max(m, ref(tile max)) with ref() rounding up to a power of two
+ * (see ref_max), P = exp(s - m_new), l accumulates the
  * unquantised P, and P is rounded for the P.V product by pv_mode:
  *   ORC_PV_F16: fp16(P) times V given in fp16;
  *   ORC_PV_F8 : e4m3(448 P)/448 times e4m3 V codes times the channel scale;
@@ -450,7 +463,7 @@ void orc_sage_fwd(int qk_mode, const int8_t* qc, const float* qs, int q_blk,
                 s[u] = sage_score(qk_mode, qc, qs, q_blk, kc, ks, k_blk, Qf, Kf, d, i, t0 + u, tau);
                 if (s[u] > tmax) tmax = s[u];
             }
-            row_rescale(&st, st.m > tmax ? st.m : tmax, d);
+            row_rescale(&st, st.m > ref_max(tmax) ? st.m : ref_max(tmax), d);
             double r = 0.0;
             for (int u = 0; u < n; ++u) {
                 p[u] = exp(s[u] - st.m);
@@ -703,7 +716,7 @@ void orc_qat_fwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const 
                 s[u] *= tau;
                 if (s[u] > tmax) tmax = s[u];
             }
-            row_rescale(&st, st.m > tmax ? st.m : tmax, d);
+            row_rescale(&st, st.m > ref_max(tmax) ? st.m : ref_max(tmax), d);
             for (int u = 0; u < kv_tile; ++u) { p[u] = exp(s[u] - st.m); st.l += p[u]; pq[u] = p[u]; }
             if (quantize_p) for (int u = 0; u < kv_tile; u += 32) mx_fake32(pq + u, 32);
             for (int u = 0; u < kv_tile; ++u) {
@@ -879,7 +892,7 @@ static void thrift_block(const thrift_ctx* c, row_state* st, int i, int j0, int 
         }
         if (s[u] > tmax) tmax = s[u];
     }
-    row_rescale(st, st->m > tmax ? st->m : tmax, d);
+    row_rescale(st, st->m > ref_max(tmax) ? st->m : ref_max(tmax), d);
     double r = 0.0;
     for (int u = 0; u < n; ++u) { p[u] = exp(s[u] - st->m); st->l += p[u]; if (p[u] > r) r = p[u]; }
     if (!c->quantize) {

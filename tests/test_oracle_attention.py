@@ -147,15 +147,17 @@ def test_sage_int8_scores_are_exact(orc):
 
 
 def _single_tile_ref(orc, s, Vd, rounding):
-    m = s.max(axis=1, keepdims=True)
+    # reference point: the row max rounded up to a whole power of two of P
+    m = np.log(2.0) * np.ceil(s.max(axis=1, keepdims=True) / np.log(2.0))
     p = np.exp(s - m)
     l = p.sum(axis=1, keepdims=True)
     return rounding(p) @ Vd / l
 
 
 def test_sage_pv_rounding_single_tile(orc):
-    """With one key tile the running max is the row max, so each P.V mode is a
-    library rounding of exp(s - max): fp16, e4m3 at 448 P, int8 at 127 P."""
+    """With one key tile the reference point is the row max rounded up to a
+    power of two, so each P.V mode is a library rounding of exp(s - m): fp16,
+    e4m3 at 448 P, int8 per tile at 127 P / max P."""
     rng = np.random.default_rng(13)
     N, d = 32, 16
     Q, K, V, qc, qs, kc, ks = _sage_inputs(orc, rng, N, d, q_blk=32, k_blk=32)
@@ -175,7 +177,8 @@ def test_sage_pv_rounding_single_tile(orc):
     vc, vs = orc.quant_chan(V[None], "i8")
     deq = vc[0].T.view(np.int8).astype(np.float64) * vs[0][None]
     O, _ = orc.sage_fwd(pv_mode=orc.PV_I8, vc_t=vc[0], vs=vs[0], **kw)
-    ref = _single_tile_ref(orc, s, deq, lambda p: np.rint((p * np.float32(127.0)).astype(np.float32)).astype(np.float64) / 127)
+    ref = _single_tile_ref(orc, s, deq, lambda p: np.rint((p * (127.0 / p.max(axis=1, keepdims=True)).astype(np.float32)).astype(
+        np.float32)).astype(np.float64) * p.max(axis=1, keepdims=True) / 127)
     assert np.abs(O - ref).max() < 1e-12
 
 
@@ -310,8 +313,9 @@ def test_qat_quantised_close_and_aux_identity(orc):
 
 
 def test_qat_one_hot_row_is_exact(orc):
-    """A row whose scores put all the mass on one key: P^ is exactly one-hot,
-    so O equals that key's FP4 value row."""
+    """A row whose scores put all the mass on one key: P^ is one-hot, so O is
+    exactly proportional to that key's FP4 value row; the factor is
+    e2m1(P / 2^e) 2^e / P for the key's P in (1/2, 1], i.e. within [0.75, 1.2]."""
     d, N = 32, 64
     Q = np.zeros((N, d), np.float32); K = np.zeros((N, d), np.float32)
     Q[:, 0] = 6.0
@@ -323,4 +327,9 @@ def test_qat_one_hot_row_is_exact(orc):
     O, Oa, _ = orc.qat_fwd(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0],
                            Nq=N, Nk=N, d=d, tau=1.0, kv_tile=32)
     Vd = _mx_deq_rows(vc[0], vs[0]).T
-    assert np.abs(O - Vd[7][None]).max() < 1e-12
+    v = Vd[7]
+    nz = np.abs(v) > 0
+    kappa = O[:, nz] / v[None, nz]
+    assert np.abs(kappa - kappa[:, :1]).max() < 1e-12          # one factor per row
+    assert np.all((kappa[:, 0] >= 0.75 - 1e-12) & (kappa[:, 0] <= 1.2 + 1e-12))
+    assert np.abs(O[:, ~nz]).max() < 1e-20            # other keys: P of order e^-60 (own MX block)
