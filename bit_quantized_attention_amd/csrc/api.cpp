@@ -110,7 +110,7 @@ size_t bqa_workspace_size(const bqa_problem* p, int32_t op) {
     switch (op) {
         case BQA_OP_QUANTIZE_K:
             if (is_sage(p->mode) && p->smooth_k)
-                return ws_kmean_bytes(p->B * p->Hkv, p->Nk, p->d) + (size_t)p->B * p->Hkv * p->d * sizeof(float);
+                return ws_kmean_bytes(p->B * p->Hkv, p->Nk, p->d);
             return 0;
         case BQA_OP_QUANTIZE_V:
             if (p->mode == BQA_SAGE_I8_F8PV || p->mode == BQA_SAGE_I8_I8PV) return ws_chan_bytes(p->B * p->Hkv, p->Nk, p->d);
@@ -159,19 +159,13 @@ bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_ten
     if (N % blk != 0) return BQA_E_UNSUPPORTED;
     const bool smooth = role == BQA_ROLE_K && p->smooth_k;
     if (smooth) {
-        const size_t need = ws_kmean_bytes(p->B * H, N, d) + (size_t)p->B * H * d * sizeof(float);
+        const size_t need = ws_kmean_bytes(p->B * H, N, d);
         if (!ws || ws_bytes < need) return BQA_E_WORKSPACE;
         if (!std::isfinite(p->smooth_eps)) return BQA_E_SHAPE;
     }
     TRY(check_device());
-    float* mu = nullptr;
-    if (smooth) {
-        mu = k_mean ? k_mean : (float*)((char*)ws + ws_kmean_bytes(p->B * H, N, d));
-        hipError_t e = launch_kmean(as_dense(x), f16, p->B, H, N, d, (double)p->smooth_eps, mu, ws, st);
-        if (e != hipSuccess) return BQA_E_LAUNCH;
-    }
-    return launched(launch_quant_i8_tokblock(as_dense(x), f16, p->B, H, N, d, blk, mu, (int8_t*)out->codes,
-                                             (float*)out->scales, st));
+    return launched(launch_quant_i8_tokblock(as_dense(x), f16, p->B, H, N, d, blk, smooth, (double)p->smooth_eps,
+                                             k_mean, ws, (int8_t*)out->codes, (float*)out->scales, st));
 }
 
 bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const float* k_means, int32_t* sel_idx,

@@ -12,10 +12,9 @@ namespace bqa {
 // ---- quantisation (quant.hip)
 size_t ws_kmean_bytes(int BH, int N, int d);
 size_t ws_chan_bytes(int BH, int N, int d);
-hipError_t launch_kmean(const Dense& x, bool f16, int B, int H, int N, int d, double eps, float* mu, void* ws,
-                        hipStream_t st);
-hipError_t launch_quant_i8_tokblock(const Dense& x, bool f16, int B, int H, int N, int d, int blk, const float* mu,
-                                    int8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_quant_i8_tokblock(const Dense& x, bool f16, int B, int H, int N, int d, int blk, bool smooth,
+                                    double eps, float* mu, void* ws, int8_t* codes, float* scales,
+                                    hipStream_t st);
 hipError_t launch_quant_chan(const Dense& x, bool f16, int B, int H, int N, int d, int fmt, uint8_t* codes_t,
                              float* scales, void* ws, hipStream_t st);
 hipError_t launch_quant_mx(const Dense& x, bool f16, int B, int H, int N, int d, int axis, uint8_t* codes,

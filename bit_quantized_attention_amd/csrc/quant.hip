@@ -21,20 +21,33 @@
 namespace bqa {
 
 // ------------------------------------------------------------ K token sums
-// grid (BH, chunks); 256 threads = 16 rows x 16 column groups of 8 channels.
+// grid (BH, chunks); 256 threads = 16 rows x 16 column groups of 8 channels;
+// fp64 partial sums of each chunk of tokens.
 template <bool IS_F16>
 __global__ __launch_bounds__(256) void ksum_partial_kernel(Dense x, int H, int N, int d, int rows_per_chunk,
                                                             double* __restrict__ part) {
     const int bh = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y;
     const int b = bh / H, h = bh % H;
     const int cg = threadIdx.x % 16, r = threadIdx.x / 16;
-    const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH;
+    const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH + cg * 8;
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const int t0 = chunk * rows_per_chunk, t1 = min(N, t0 + rows_per_chunk);
     if (cg * 8 < d) {
-        for (int t = t0 + r; t < t1; t += 16) {
-            uint4 v = *(const uint4*)(base + (int64_t)t * x.sN + cg * 8);
-            const uint16_t* e = (const uint16_t*)&v;
+        int t = t0 + r;
+        for (; t + 48 < t1; t += 64) {                       // four rows in flight per thread
+            v4i raw[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) raw[u] = *(const v4i*)(base + (int64_t)(t + 16 * u) * x.sN);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint16_t* e = (const uint16_t*)&raw[u];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] += (double)load_half<IS_F16>(e + k);
+            }
+        }
+        for (; t < t1; t += 16) {
+            v4i raw = *(const v4i*)(base + (int64_t)t * x.sN);
+            const uint16_t* e = (const uint16_t*)&raw;
 #pragma unroll
             for (int k = 0; k < 8; ++k) acc[k] += (double)load_half<IS_F16>(e + k);
         }
@@ -45,56 +58,65 @@ __global__ __launch_bounds__(256) void ksum_partial_kernel(Dense x, int H, int N
         if (cg * 8 + k < d) red[r][cg * 8 + k] = acc[k];
     __syncthreads();
     if (threadIdx.x < d) {
-        double s = 0.0;
-        for (int rr = 0; rr < 16; ++rr) s += red[rr][threadIdx.x];
-        part[((int64_t)bh * nchunks + chunk) * d + threadIdx.x] = s;
+        double sum = 0.0;
+        for (int rr = 0; rr < 16; ++rr) sum += red[rr][threadIdx.x];
+        part[((int64_t)bh * nchunks + chunk) * d + threadIdx.x] = sum;
     }
 }
 
-// grid BH, d threads: mu = fp32(sum / N - eps)
-__global__ void kmean_finalize_kernel(const double* __restrict__ part, int nchunks, int N, int d, double eps,
-                                      float* __restrict__ mu) {
-    const int bh = blockIdx.x, c = threadIdx.x;
-    if (c >= d) return;
-    double s = 0.0;
-    for (int k = 0; k < nchunks; ++k) s += part[((int64_t)bh * nchunks + k) * d + c];
-    mu[(int64_t)bh * d + c] = (float)(s / (double)N - eps);
-}
-
 // ------------------------------------------------------------ INT8 token blocks
-// grid BH * (N / blk); 256 threads; the block (blk x d <= 128 x 128) is held in
-// registers: each thread owns blk*d/256/8 groups of 8 consecutive elements.
-template <bool IS_F16>
+// grid BH * (N / blk); 256 threads; the block (blk x d) is held in registers:
+// each thread owns NG groups of 8 consecutive elements (NG = blk*d/2048),
+// always at the same 8 channels.  With `part` the K-smoothing mean is
+// finalised here from the fp64 partial token sums, mu = fp32(S/N - eps), and
+// the first block of each head writes it to `mu_out`.
+template <bool IS_F16, int NG>
 __global__ __launch_bounds__(256) void quant_i8_tokblock_kernel(Dense x, int H, int N, int d, int blk,
-                                                                 const float* __restrict__ mu,
+                                                                 const double* __restrict__ part, int nchunks,
+                                                                 double eps, float* __restrict__ mu_out,
                                                                  int8_t* __restrict__ codes,
                                                                  float* __restrict__ scales) {
     const int nb = N / blk;
     const int bh = blockIdx.x / nb, ib = blockIdx.x % nb;
     const int b = bh / H, h = bh % H;
     const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH;
-    const int groups_per_row = d / 8;
-    const int ngroups = blk * groups_per_row;          // <= 2048
-    float v[8][8];
+    const int gpr = d / 8;                               // groups per token row
+    const int c0 = (threadIdx.x % gpr) * 8;              // this thread's channels (256 % gpr == 0)
+    __shared__ float mu_s[128];
+    __shared__ float wmax[4];
+    v4i raw[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+        const int g = threadIdx.x + k * 256;
+        raw[k] = *(const v4i*)(base + (int64_t)(ib * blk + g / gpr) * x.sN + c0);
+    }
+    float mu[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (part) {
+        if ((int)threadIdx.x < d) {
+            double sum = 0.0;
+            for (int k = 0; k < nchunks; ++k) sum += part[((int64_t)bh * nchunks + k) * d + threadIdx.x];
+            const float m = (float)(sum / (double)N - eps);
+            mu_s[threadIdx.x] = m;
+            if (ib == 0 && mu_out) mu_out[(int64_t)bh * d + threadIdx.x] = m;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mu[j] = mu_s[c0 + j];
+    }
+    float v[NG][8];
     float amax = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int g = threadIdx.x + k * 256;
-        if (g < ngroups) {
-            const int t = ib * blk + g / groups_per_row, c = (g % groups_per_row) * 8;
-            uint4 raw = *(const uint4*)(base + (int64_t)t * x.sN + c);
-            const uint16_t* e = (const uint16_t*)&raw;
+    for (int k = 0; k < NG; ++k) {
+        const uint16_t* e = (const uint16_t*)&raw[k];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float f = load_half<IS_F16>(e + j);
-                if (mu) f = f - mu[(int64_t)bh * d + c + j];
-                v[k][j] = f;
-                amax = __builtin_fmaxf(amax, __builtin_fabsf(f));
-            }
+        for (int j = 0; j < 8; ++j) {
+            float f = load_half<IS_F16>(e + j);
+            if (part) f = f - mu[j];
+            v[k][j] = f;
+            amax = __builtin_fmaxf(amax, __builtin_fabsf(f));
         }
     }
     amax = wave_max(amax);
-    __shared__ float wmax[4];
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
     __syncthreads();
     amax = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
@@ -104,16 +126,14 @@ __global__ __launch_bounds__(256) void quant_i8_tokblock_kernel(Dense x, int H, 
     if (threadIdx.x == 0) scales[(int64_t)bh * nb + ib] = scale;
     int8_t* out = codes + ((int64_t)bh * N + (int64_t)ib * blk) * d;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NG; ++k) {
         const int g = threadIdx.x + k * 256;
-        if (g < ngroups) {
-            uint32_t w0 = 0, w1 = 0;
+        uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w0 |= ((uint32_t)(enc_i8(v[k][j], inv) & 0xFF)) << (8 * j);
+        for (int j = 0; j < 4; ++j) w0 |= ((uint32_t)(enc_i8(v[k][j], inv) & 0xFF)) << (8 * j);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w1 |= ((uint32_t)(enc_i8(v[k][4 + j], inv) & 0xFF)) << (8 * j);
-            *(uint2*)(out + (int64_t)g * 8) = make_uint2(w0, w1);
-        }
+        for (int j = 0; j < 4; ++j) w1 |= ((uint32_t)(enc_i8(v[k][4 + j], inv) & 0xFF)) << (8 * j);
+        *(uint2*)(out + (int64_t)g * 8) = make_uint2(w0, w1);
     }
 }
 
@@ -125,13 +145,25 @@ __global__ __launch_bounds__(256) void chan_amax_partial_kernel(Dense x, int H, 
     const int bh = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y;
     const int b = bh / H, h = bh % H;
     const int cg = threadIdx.x % 16, r = threadIdx.x / 16;
-    const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH;
+    const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH + cg * 8;
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const int t0 = chunk * rows_per_chunk, t1 = min(N, t0 + rows_per_chunk);
     if (cg * 8 < d) {
-        for (int t = t0 + r; t < t1; t += 16) {
-            uint4 v = *(const uint4*)(base + (int64_t)t * x.sN + cg * 8);
-            const uint16_t* e = (const uint16_t*)&v;
+        int t = t0 + r;
+        for (; t + 48 < t1; t += 64) {
+            v4i raw[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) raw[u] = *(const v4i*)(base + (int64_t)(t + 16 * u) * x.sN);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint16_t* e = (const uint16_t*)&raw[u];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) m[k] = __builtin_fmaxf(m[k], __builtin_fabsf(load_half<IS_F16>(e + k)));
+            }
+        }
+        for (; t < t1; t += 16) {
+            v4i raw = *(const v4i*)(base + (int64_t)t * x.sN);
+            const uint16_t* e = (const uint16_t*)&raw;
 #pragma unroll
             for (int k = 0; k < 8; ++k) m[k] = __builtin_fmaxf(m[k], __builtin_fabsf(load_half<IS_F16>(e + k)));
         }
@@ -142,14 +174,17 @@ __global__ __launch_bounds__(256) void chan_amax_partial_kernel(Dense x, int H, 
         if (cg * 8 + k < d) red[r][cg * 8 + k] = m[k];
     __syncthreads();
     if (threadIdx.x < d) {
-        float s = 0.0f;
-        for (int rr = 0; rr < 16; ++rr) s = __builtin_fmaxf(s, red[rr][threadIdx.x]);
-        part[((int64_t)bh * nchunks + chunk) * d + threadIdx.x] = s;
+        float mm = 0.0f;
+        for (int rr = 0; rr < 16; ++rr) mm = __builtin_fmaxf(mm, red[rr][threadIdx.x]);
+        part[((int64_t)bh * nchunks + chunk) * d + threadIdx.x] = mm;
     }
 }
 
 // pass 2: grid (BH, N / 64): encode 64 tokens of every channel, channel-major
-// output; block (bh, 0) also writes the scales.  FMT 0: int8, 1: e4m3.
+// output; block (bh, 0) also writes the scales.  FMT 0: int8, 1: e4m3
+// (hardware nearest-even conversion after clamping to +-448, i.e. saturating).
+// Thread t owns 4 tokens x 8 channels; codes are transposed through LDS as
+// 32-bit words (4 tokens of one channel) and written as 16-byte row chunks.
 template <bool IS_F16, int FMT>
 __global__ __launch_bounds__(256) void chan_encode_kernel(Dense x, int H, int N, int d,
                                                           const float* __restrict__ part, int nchunks,
@@ -158,8 +193,8 @@ __global__ __launch_bounds__(256) void chan_encode_kernel(Dense x, int H, int N,
     const int bh = blockIdx.x, tb = blockIdx.y;
     const int b = bh / H, h = bh % H;
     __shared__ float inv_s[128];
-    __shared__ uint8_t tile[128][64 + 4];
-    if (threadIdx.x < d) {
+    __shared__ uint32_t tile[128][16 + 1];
+    if ((int)threadIdx.x < d) {
         float amax = 0.0f;
         for (int k = 0; k < nchunks; ++k)
             amax = __builtin_fmaxf(amax, part[((int64_t)bh * nchunks + k) * d + threadIdx.x]);
@@ -172,28 +207,34 @@ __global__ __launch_bounds__(256) void chan_encode_kernel(Dense x, int H, int N,
     }
     __syncthreads();
     const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH;
-    const int gpr = d / 8;                               // 8-element groups per token row
-    for (int g = threadIdx.x; g < 64 * gpr; g += 256) {
-        const int t = g / gpr, c = (g % gpr) * 8;
-        uint4 raw = *(const uint4*)(base + (int64_t)(tb * 64 + t) * x.sN + c);
-        const uint16_t* e = (const uint16_t*)&raw;
+    const int gpr = d / 8;                                 // channel groups
+    const int tpg = 256 / gpr;                             // threads per channel group
+    const int c0 = (threadIdx.x % gpr) * 8;
+    const int q = threadIdx.x / gpr;                       // token quad index (64/4 = 16 quads)
+    for (int tq = q; tq < 16; tq += tpg) {
+        v4i raw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) raw[u] = *(const v4i*)(base + (int64_t)(tb * 64 + 4 * tq + u) * x.sN + c0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float f = load_half<IS_F16>(e + j);
-            uint32_t code = FMT == 0 ? (uint32_t)(enc_i8(f, inv_s[c + j]) & 0xFF) : enc_e4m3(f * inv_s[c + j]);
-            tile[c + j][t] = (uint8_t)code;
+            uint32_t word = 0;
+            const float iv = inv_s[c0 + j];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float f = load_half<IS_F16>((const uint16_t*)&raw[u] + j) * iv;
+                uint32_t code;
+                if constexpr (FMT == 0) code = (uint32_t)(enc_i8(f, 1.0f) & 0xFF);
+                else code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(f, -448.0f, 448.0f), 0.0f, 0, false) & 0xFFu;
+                word |= code << (8 * u);
+            }
+            tile[c0 + j][tq] = word;
         }
     }
     __syncthreads();
-    // each thread writes 16 bytes of one channel row: d rows x 4 chunks
-    for (int q = threadIdx.x; q < d * 4; q += 256) {
-        const int c = q / 4, part16 = q % 4;
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            w[k] = (uint32_t)tile[c][part16 * 16 + 4 * k] | ((uint32_t)tile[c][part16 * 16 + 4 * k + 1] << 8) |
-                   ((uint32_t)tile[c][part16 * 16 + 4 * k + 2] << 16) | ((uint32_t)tile[c][part16 * 16 + 4 * k + 3] << 24);
-        *(uint4*)(codes_t + ((int64_t)bh * d + c) * N + tb * 64 + part16 * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int qq = threadIdx.x; qq < d * 4; qq += 256) {
+        const int c = qq / 4, p16 = qq % 4;
+        *(uint4*)(codes_t + ((int64_t)bh * d + c) * N + tb * 64 + p16 * 16) =
+            make_uint4(tile[c][4 * p16], tile[c][4 * p16 + 1], tile[c][4 * p16 + 2], tile[c][4 * p16 + 3]);
     }
 }
 
@@ -286,9 +327,9 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(Dense x, int H, int N, int
 
 // ------------------------------------------------------------ launchers
 static int chunks_for(int BH, int N) {
-    // enough blocks to cover the chip (~4 per CU) while keeping >= 64 rows per chunk
-    int want = (1024 + BH - 1) / BH;
-    int maxc = (N + 63) / 64;
+    // enough blocks to fill the chip (~2 per CU), at least 256 rows per chunk
+    int want = (512 + BH - 1) / BH;
+    int maxc = (N + 255) / 256;
     int c = want < maxc ? want : maxc;
     return c < 1 ? 1 : c;
 }
@@ -296,22 +337,33 @@ static int chunks_for(int BH, int N) {
 size_t ws_kmean_bytes(int BH, int N, int d) { return (size_t)BH * chunks_for(BH, N) * d * sizeof(double); }
 size_t ws_chan_bytes(int BH, int N, int d) { return (size_t)BH * chunks_for(BH, N) * d * sizeof(float); }
 
-hipError_t launch_kmean(const Dense& x, bool f16, int B, int H, int N, int d, double eps, float* mu, void* ws,
-                        hipStream_t st) {
-    const int BH = B * H, nch = chunks_for(BH, N), rpc = (N + nch - 1) / nch;
-    double* part = (double*)ws;
-    if (f16) ksum_partial_kernel<true><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
-    else ksum_partial_kernel<false><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
-    kmean_finalize_kernel<<<BH, 128, 0, st>>>(part, nch, N, d, eps, mu);
+template <bool F16>
+static hipError_t launch_tokblock_t(const Dense& x, int B, int H, int N, int d, int blk, const double* part,
+                                    int nch, double eps, float* mu, int8_t* codes, float* scales, hipStream_t st) {
+    const int grid = B * H * (N / blk);
+    const int ng = blk * d / 2048;
+    switch (ng) {
+        case 2: quant_i8_tokblock_kernel<F16, 2><<<grid, 256, 0, st>>>(x, H, N, d, blk, part, nch, eps, mu, codes, scales); break;
+        case 4: quant_i8_tokblock_kernel<F16, 4><<<grid, 256, 0, st>>>(x, H, N, d, blk, part, nch, eps, mu, codes, scales); break;
+        default: quant_i8_tokblock_kernel<F16, 8><<<grid, 256, 0, st>>>(x, H, N, d, blk, part, nch, eps, mu, codes, scales); break;
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_quant_i8_tokblock(const Dense& x, bool f16, int B, int H, int N, int d, int blk, const float* mu,
-                                    int8_t* codes, float* scales, hipStream_t st) {
-    const int grid = B * H * (N / blk);
-    if (f16) quant_i8_tokblock_kernel<true><<<grid, 256, 0, st>>>(x, H, N, d, blk, mu, codes, scales);
-    else quant_i8_tokblock_kernel<false><<<grid, 256, 0, st>>>(x, H, N, d, blk, mu, codes, scales);
-    return hipGetLastError();
+// INT8 token blocks; with smoothing (mu != null) the K token sums go to the
+// workspace first and the quantiser finalises the mean.
+hipError_t launch_quant_i8_tokblock(const Dense& x, bool f16, int B, int H, int N, int d, int blk, bool smooth,
+                                    double eps, float* mu, void* ws, int8_t* codes, float* scales,
+                                    hipStream_t st) {
+    const int BH = B * H, nch = chunks_for(BH, N), rpc = (N + nch - 1) / nch;
+    double* part = nullptr;
+    if (smooth) {
+        part = (double*)ws;
+        if (f16) ksum_partial_kernel<true><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
+        else ksum_partial_kernel<false><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
+    }
+    return f16 ? launch_tokblock_t<true>(x, B, H, N, d, blk, part, nch, eps, mu, codes, scales, st)
+               : launch_tokblock_t<false>(x, B, H, N, d, blk, part, nch, eps, mu, codes, scales, st);
 }
 
 hipError_t launch_quant_chan(const Dense& x, bool f16, int B, int H, int N, int d, int fmt, uint8_t* codes_t,
