@@ -115,6 +115,9 @@ size_t bqa_workspace_size(const bqa_problem* p, int32_t op) {
         case BQA_OP_QUANTIZE_V:
             if (p->mode == BQA_SAGE_I8_F8PV || p->mode == BQA_SAGE_I8_I8PV) return ws_chan_bytes(p->B * p->Hkv, p->Nk, p->d);
             return 0;
+        case BQA_OP_FWD:
+            if (p->mode == BQA_QAT_MXFP4) return ws_qat_fwd_bytes(p->B, p->Hkv, p->Nk, p->d);
+            return 0;
         default:
             return 0;
     }
@@ -179,9 +182,33 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
                         const bqa_tensor* q_hi, const bqa_tensor* k_hi, const bqa_tensor* v_hi,
                         const int32_t* sel_idx, const int32_t* sel_cnt, bqa_tensor* o, bqa_tensor* o_aux,
                         float* lse, void* ws, size_t ws_bytes, void* stream) {
-    (void)q_hi; (void)k_hi; (void)sel_idx; (void)sel_cnt; (void)o_aux; (void)ws; (void)ws_bytes;
+    (void)q_hi; (void)k_hi; (void)sel_idx; (void)sel_cnt;
     TRY(check_problem(p));
     hipStream_t st = (hipStream_t)stream;
+    if (p->mode == BQA_QAT_MXFP4) {
+        if (p->d != 128 || p->causal || p->Nk % 64 != 0) return BQA_E_UNSUPPORTED;
+        TRY(check_q(q, BQA_MXFP4, 0));
+        TRY(check_q(k, BQA_MXFP4, 0));
+        TRY(check_q(v, BQA_MXFP4, 1));
+        if (q->block != 32 || k->block != 32 || v->block != 32) return BQA_E_UNSUPPORTED;
+        TRY(check_dense(o, false, true));
+        QatFwdArgs a{};
+        if (o_aux) {
+            TRY(check_dense(o_aux, false, true));
+            if (!ws || ws_bytes < ws_qat_fwd_bytes(p->B, p->Hkv, p->Nk, p->d)) return BQA_E_WORKSPACE;
+            if (!aligned16(ws)) return BQA_E_ALIGN;
+            a.vdeq = (uint16_t*)ws;
+            a.oa = as_dense(o_aux);
+        }
+        a.qc = (const uint8_t*)q->codes; a.qs = (const uint8_t*)q->scales;
+        a.kc = (const uint8_t*)k->codes; a.ks = (const uint8_t*)k->scales;
+        a.vc = (const uint8_t*)v->codes; a.vs = (const uint8_t*)v->scales;
+        a.o = as_dense(o); a.lse = lse;
+        a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk;
+        a.c_log2 = tau_of(p) * 1.4426950408889634f;
+        TRY(check_device());
+        return launched(launch_qat_fwd(a, st));
+    }
     if (is_sage(p->mode)) {
         TRY(check_sage_blocks(p));
         TRY(check_q(q, BQA_INT8, 0));
@@ -240,6 +267,20 @@ bqa_status bqa_debug_qk_scores(const bqa_problem* p, const bqa_qtensor* q, const
         const int64_t krow = ((int64_t)b * p->Hkv + hk) * p->Nk + (int64_t)k_tile * 32;
         return launched(launch_debug_scores_i8((const int8_t*)q->codes, (const int8_t*)k->codes, p->d, qrow, krow,
                                                (int32_t*)out, (hipStream_t)stream));
+    }
+    if (q->fmt == BQA_MXFP4) {
+        if (p->d != 128) return BQA_E_UNSUPPORTED;
+        TRY(check_q(q, BQA_MXFP4, 0));
+        TRY(check_q(k, BQA_MXFP4, 0));
+        TRY(check_device());
+        const int hk = h / (p->Hq / p->Hkv);
+        const int64_t qrow = ((int64_t)b * p->Hq + h) * p->Nq + (int64_t)q_tile * 32;
+        const int64_t krow = ((int64_t)b * p->Hkv + hk) * p->Nk + (int64_t)k_tile * 32;
+        const uint8_t* qc = (const uint8_t*)q->codes + qrow * (p->d / 2);
+        const uint8_t* qs = (const uint8_t*)q->scales + qrow * (p->d / 32);
+        const uint8_t* kc = (const uint8_t*)k->codes + krow * (p->d / 2);
+        const uint8_t* ks = (const uint8_t*)k->scales + krow * (p->d / 32);
+        return launched(launch_debug_scores_mx(qc, qs, kc, ks, (float*)out, (hipStream_t)stream));
     }
     return BQA_E_UNSUPPORTED;
 }

@@ -1,0 +1,356 @@
+// attn_qat.hip — Attn-QAT FP4 attention forward for gfx950.
+//
+// "Attn-QAT: 4-Bit Attention With Quantization-Aware Training", technical
+// summary §2: the forward runs Q K^T and P.V as FP4 products (MXFP4 here:
+// e2m1 values with an E8M0 scale per 32 elements, on the scaled f8f6f4
+// matrix instructions), P quantised per 32 keys of a row with no smoothing or
+// two-level step (§2 Implementation), and — for training — emits the
+// high-precision auxiliary output O' = sum bf16(P) Vhat / l next to O
+// (Principle 2).  The row sum l accumulates the unrounded P.
+//
+// Layout and schedule follow the INT8 kernel: one workgroup of 4 wavefronts
+// per 128 query rows, 32 rows per wavefront, S^T = Khat Qhat^T so that each
+// lane owns one query row and (through the sigma row permutation) 16
+// consecutive keys per 32-key half of a 64-key tile.
+//
+// Scaled frame: MXFP4 codes and bf16 roundings commute with multiplication by
+// powers of two, so P is kept relative to a fixed per-row power-of-two
+// reference m_ref (the first tile's maximum rounded up) instead of the
+// running one: P_frame = 2^(m_int - m_ref) P, whose MXFP4 codes are those of
+// P (the E8M0 block scale absorbs the power of two) and whose bf16 rounding is
+// 2^k bf16(P).  O, O' and l all carry the same factor, which cancels in O/l,
+// so the accumulators are never rescaled; only if a row's scores climb more
+// than 64 (log2 units) above m_ref is the frame moved (exactly, by a power of
+// two).
+//
+// The P.V product: the 32 keys of an MX block of P sit in two lane halves;
+// one permlane32 swap per code word gives each half one complete block (in
+// key order) as the B operand, with its E8M0 scale as the operand scale.
+// O' uses deq(Vhat) in bf16, prepared once per call by vdeq_kernel into a
+// channel-major workspace tensor.
+#include <type_traits>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace bqa {
+
+namespace {
+
+constexpr int BM = 128;   // query rows per workgroup
+constexpr int BN = 64;    // keys per tile
+constexpr int D = 128;    // head dimension
+constexpr int NBUF = 2;
+
+__device__ __forceinline__ int sigma(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+
+// 64-byte rows (K codes): rows read through sigma hit distinct bank groups
+__device__ __forceinline__ int swz64(int r, int c) { return r * 64 + 16 * (c ^ (((r >> 2) & 3) ^ (((r >> 4) & 1) << 1))); }
+// 32-byte rows (Vhat^T codes, consecutive rows)
+__device__ __forceinline__ int swz32(int r, int c) { return r * 32 + 16 * (c ^ ((r >> 3) & 1)); }
+// 128-byte rows (deq(Vhat)^T bf16, consecutive rows)
+__device__ __forceinline__ int swz128(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
+
+struct Lds {
+    uint8_t kc[BN * D / 2];        // K codes, 64 rows x 64 B
+    uint8_t ks[BN * D / 32];       // K E8M0 scales, 64 rows x 4
+    uint8_t vc[D * BN / 2];        // Vhat^T codes, 128 rows x 32 B
+    uint8_t vs[D * BN / 32];       // Vhat^T scales, 128 rows x 2
+    uint8_t vb[D * BN * 2];        // deq(Vhat)^T bf16, 128 rows x 128 B
+};
+
+template <bool AUX>
+struct Stage {
+    v4i kc, vc;
+    v4i vb[AUX ? 4 : 1];
+    uint32_t ks, vs;
+};
+
+template <bool AUX>
+__device__ __forceinline__ void stage_load(Stage<AUX>& st, const QatFwdArgs& a, int bhk, int t0, int tid) {
+    // K codes: 64 rows x 4 chunks
+    {
+        const int r = tid >> 2, c = tid & 3;
+        st.kc = *(const v4i*)(a.kc + ((int64_t)bhk * a.Nk + t0 + r) * (D / 2) + 16 * c);
+    }
+    // Vhat^T codes: 128 rows x 2 chunks
+    {
+        const int r = tid >> 1, c = tid & 1;
+        st.vc = *(const v4i*)(a.vc + ((int64_t)bhk * D + r) * (a.Nk / 2) + t0 / 2 + 16 * c);
+    }
+    // K scales: 64 rows x 4 bytes = 64 words; Vhat scales: 128 rows x 2 bytes
+    st.ks = tid < 64 ? *(const uint32_t*)(a.ks + ((int64_t)bhk * a.Nk + t0 + tid) * (D / 32)) : 0u;
+    st.vs = tid < 128 ? (uint32_t)*(const uint16_t*)(a.vs + ((int64_t)bhk * D + tid) * (a.Nk / 32) + t0 / 32) : 0u;
+    if constexpr (AUX) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int g = tid + 256 * u, r = g >> 3, c = g & 7;
+            st.vb[u] = *(const v4i*)(a.vdeq + ((int64_t)bhk * D + r) * a.Nk + t0 + 8 * c);
+        }
+    }
+}
+
+template <bool AUX>
+__device__ __forceinline__ void stage_store(const Stage<AUX>& st, Lds& L, int tid) {
+    {
+        const int r = tid >> 2, c = tid & 3;
+        *(v4i*)(L.kc + swz64(r, c)) = st.kc;
+    }
+    {
+        const int r = tid >> 1, c = tid & 1;
+        *(v4i*)(L.vc + swz32(r, c)) = st.vc;
+    }
+    if (tid < 64) *(uint32_t*)(L.ks + 4 * tid) = st.ks;
+    if (tid < 128) *(uint16_t*)(L.vs + 2 * tid) = (uint16_t)st.vs;
+    if constexpr (AUX) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int g = tid + 256 * u, r = g >> 3, c = g & 7;
+            *(v4i*)(L.vb + swz128(r, c)) = st.vb[u];
+        }
+    }
+}
+
+// S^T tile (64 keys x 32 queries) from MXFP4 codes: acc0 keys 16h + i,
+// acc1 keys 32 + 16h + i; raw fp32 products (before tau).
+__device__ __forceinline__ void qk_tile_mx(const Lds& L, const v4i* qb, const int* qsb, int krow, int h, v16f& acc0,
+                                           v16f& acc1) {
+    acc0 = v16f{};
+    acc1 = v16f{};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const v4i a0 = *(const v4i*)(L.kc + swz64(krow, 2 * kk + h));
+        const v4i a1 = *(const v4i*)(L.kc + swz64(32 + krow, 2 * kk + h));
+        const int s0 = L.ks[4 * krow + 2 * kk + h], s1 = L.ks[4 * (32 + krow) + 2 * kk + h];
+        acc0 = mfma_f4_32x32x64(a0, s0, qb[kk], qsb[kk], acc0);
+        acc1 = mfma_f4_32x32x64(a1, s1, qb[kk], qsb[kk], acc1);
+    }
+}
+
+template <bool AUX>
+__global__ __launch_bounds__(256, AUX ? 1 : 2) void qat_fwd_kernel(QatFwdArgs a) {
+    __shared__ __attribute__((aligned(16))) Lds lds[NBUF];
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
+    // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
+    // contiguous range of (head, query block) so that the workgroups sharing
+    // an XCD's L2 also share a head's K and V.
+    const int nqt = (a.Nq + BM - 1) / BM;
+    const int grid = gridDim.x;
+    const int bid = (grid & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (grid >> 3) + (int)(blockIdx.x >> 3);
+    const int qt = bid % nqt;
+    const int bh = bid / nqt, b = bh / a.Hq, hq = bh % a.Hq;
+    const int bhk = b * a.Hkv + hq / (a.Hq / a.Hkv);
+    const int qrow = qt * BM + 32 * w + lq;
+    const bool row_ok = qrow < a.Nq;
+    const int krow = sigma(lq);
+
+    // this lane's query codes: B operand of S^T, Q[qrow][64kk + 32h .. +32) and its scale
+    v4i qb[2];
+    int qsb[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        qb[kk] = row_ok ? *(const v4i*)(a.qc + ((int64_t)bh * a.Nq + qrow) * (D / 2) + 32 * kk + 16 * h) : v4i{};
+        qsb[kk] = row_ok ? (int)a.qs[((int64_t)bh * a.Nq + qrow) * (D / 32) + 2 * kk + h] : 0;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+    v16f oacc[D / 32], xacc[AUX ? D / 32 : 1];
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = v16f{};
+#pragma unroll
+    for (int cb = 0; cb < (AUX ? D / 32 : 1); ++cb) xacc[cb] = v16f{};
+    float m_ref = -__builtin_inff();          // frame reference (log2 units, an integer)
+    float l_run = 0.0f;                        // this lane half's share of the row sum, in the frame
+    const float c = a.c_log2;
+    const int n_tiles = a.Nk / BN;
+
+    Stage<AUX> st;
+    stage_load<AUX>(st, a, bhk, 0, tid);
+    stage_store<AUX>(st, lds[0], tid);
+    __syncthreads();
+
+    auto body = [&](int j, auto bufc) __attribute__((always_inline)) {
+        constexpr int B0 = decltype(bufc)::value;
+        if (j + 1 < n_tiles) stage_load<AUX>(st, a, bhk, (j + 1) * BN, tid);
+        const Lds& L = lds[B0];
+        v16f s0, s1;
+        qk_tile_mx(L, qb, qsb, krow, h, s0, s1);
+        // ---- frame: fixed reference; moved (exactly) only when scores climb far above it
+        float mx = __builtin_fmaxf(s0[0], s1[0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s0[i]), s1[i]);
+        mx = __builtin_fmaxf(mx, partner32f(mx)) * c;
+        if (m_ref == -__builtin_inff() || __any(mx > m_ref + 64.0f)) {
+            const float m_new = __builtin_ceilf(__builtin_fmaxf(mx, m_ref));
+            if (m_ref != -__builtin_inff()) {
+                const float f = __builtin_ldexpf(1.0f, (int)(m_ref - m_new));
+                l_run *= f;
+#pragma unroll
+                for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[cb][i] *= f;
+                if constexpr (AUX) {
+#pragma unroll
+                    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) xacc[cb][i] *= f;
+                }
+            }
+            m_ref = m_new;
+        }
+        float psum = 0.0f, a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -m_ref));
+            s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -m_ref));
+            psum += s0[i] + s1[i];
+            a0 = __builtin_fmaxf(a0, s0[i]);
+            a1 = __builtin_fmaxf(a1, s1[i]);
+        }
+        l_run += psum;
+        // ---- MXFP4 P: block kb = keys 32kb .. 32kb+31 (16 in each lane half)
+        a0 = __builtin_fmaxf(a0, partner32f(a0));
+        a1 = __builtin_fmaxf(a1, partner32f(a1));
+        const int e0 = mx_exponent(a0), e1 = mx_exponent(a1);
+        const float sc0 = __builtin_bit_cast(float, (uint32_t)(e0 + 127) << 23);
+        const float sc1 = __builtin_bit_cast(float, (uint32_t)(e1 + 127) << 23);
+        uint32_t p0w[2], p1w[2];
+#pragma unroll
+        for (int wd = 0; wd < 2; ++wd) {
+            uint32_t x0 = 0, x1 = 0;
+            x0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x0, s0[8 * wd + 0], s0[8 * wd + 1], sc0, 0);
+            x0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x0, s0[8 * wd + 2], s0[8 * wd + 3], sc0, 1);
+            x0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x0, s0[8 * wd + 4], s0[8 * wd + 5], sc0, 2);
+            x0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x0, s0[8 * wd + 6], s0[8 * wd + 7], sc0, 3);
+            x1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x1, s1[8 * wd + 0], s1[8 * wd + 1], sc1, 0);
+            x1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x1, s1[8 * wd + 2], s1[8 * wd + 3], sc1, 1);
+            x1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x1, s1[8 * wd + 4], s1[8 * wd + 5], sc1, 2);
+            x1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x1, s1[8 * wd + 6], s1[8 * wd + 7], sc1, 3);
+            p0w[wd] = x0;
+            p1w[wd] = x1;
+        }
+        // half 0 takes block 0 (own keys 0..15, partner's 16..31), half 1 block 1
+        const v2i r0 = __builtin_amdgcn_permlane32_swap((int)p0w[0], (int)p1w[0], false, false);
+        const v2i r1 = __builtin_amdgcn_permlane32_swap((int)p0w[1], (int)p1w[1], false, false);
+        const v4i pb = {r0[0], r1[0], r0[1], r1[1]};
+        const int psc = (h ? e1 : e0) + 127;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) {
+            const int r = 32 * cb + lq;
+            const v4i av = *(const v4i*)(L.vc + swz32(r, h));
+            oacc[cb] = mfma_f4_32x32x64(av, (int)L.vs[2 * r + h], pb, psc, oacc[cb]);
+        }
+        if constexpr (AUX) {
+            // O' = bf16(P) . deq(Vhat): four 16-key steps, keys 32(s/2) + 16h + 8(s%2) + e
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                v8bf pbf;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pbf[e] = (__bf16)(s < 2 ? s0[8 * (s % 2) + e] : s1[8 * (s % 2) + e]);
+#pragma unroll
+                for (int cb = 0; cb < D / 32; ++cb) {
+                    const v8bf av = *(const v8bf*)(L.vb + swz128(32 * cb + lq, 4 * (s / 2) + 2 * h + (s % 2)));
+                    xacc[cb] = mfma_bf16_32x32x16(av, pbf, xacc[cb]);
+                }
+            }
+        }
+        if (j + 1 < n_tiles) stage_store<AUX>(st, lds[B0 ^ 1], tid);
+        __syncthreads();
+    };
+    for (int j = 0; j < n_tiles; j += 2) {
+        body(j, std::integral_constant<int, 0>{});
+        if (j + 1 >= n_tiles) break;
+        body(j + 1, std::integral_constant<int, 1>{});
+    }
+
+    const float l_tot = l_run + partner32f(l_run);
+    if (!row_ok) return;
+    const float inv_l = 1.0f / l_tot;
+    uint16_t* orow = (uint16_t*)a.o.p + b * a.o.sB + hq * a.o.sH + (int64_t)qrow * a.o.sN;
+    uint16_t* xrow = AUX ? (uint16_t*)a.oa.p + b * a.oa.sB + hq * a.oa.sH + (int64_t)qrow * a.oa.sN : nullptr;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int ch0 = 32 * cb + 8 * g + 4 * h;
+            uint16_t o4[4], x4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o4[e] = f32_to_bf16_bits(oacc[cb][4 * g + e] * inv_l);
+                if constexpr (AUX) x4[e] = f32_to_bf16_bits(xacc[cb][4 * g + e] * inv_l);
+            }
+            *(uint2*)(orow + ch0) = make_uint2((uint32_t)o4[0] | ((uint32_t)o4[1] << 16), (uint32_t)o4[2] | ((uint32_t)o4[3] << 16));
+            if constexpr (AUX)
+                *(uint2*)(xrow + ch0) = make_uint2((uint32_t)x4[0] | ((uint32_t)x4[1] << 16), (uint32_t)x4[2] | ((uint32_t)x4[3] << 16));
+        }
+    }
+    if (a.lse && h == 0) a.lse[(int64_t)bh * a.Nq + qrow] = m_ref * 0.6931471805599453f + __logf(l_tot);
+}
+
+// deq(Vhat) in bf16, channel-major [B, H, d, N]: every e2m1 value times its
+// power-of-two scale is exact in bf16.  One thread per 32-token block.
+__global__ __launch_bounds__(256) void vdeq_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                                   int64_t nblocks, uint16_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= nblocks) return;
+    const v4i raw = *(const v4i*)(codes + 16 * i);
+    const int e = (int)scales[i] - 127;
+    uint32_t w[16];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        const uint32_t nib = ((uint32_t)raw[k / 8] >> (4 * (k % 8))) & 0xF;
+        // e2m1 value times 2^e is exact in fp32 and in bf16
+        const uint32_t bits = f32_to_bf16_bits(__builtin_ldexpf(dec_e2m1(nib), e));
+        if (k & 1) w[k / 2] |= bits << 16; else w[k / 2] = bits;
+    }
+    v4i* o = (v4i*)(out + 32 * i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = v4i{(int)w[4 * q], (int)w[4 * q + 1], (int)w[4 * q + 2], (int)w[4 * q + 3]};
+}
+
+// Raw fp32 S tile (32 queries x 32 keys) of MXFP4 codes through the same tile code.
+__global__ __launch_bounds__(64) void debug_scores_mx_kernel(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
+                                                             const uint8_t* ks, float* out) {
+    __shared__ __attribute__((aligned(16))) Lds L;
+    const int l = threadIdx.x, h = l >> 5, lq = l & 31;
+    for (int g = l; g < 64 * 4; g += 64) {
+        const int r = g >> 2, c = g & 3;
+        *(v4i*)(L.kc + swz64(r, c)) = r < 32 ? *(const v4i*)(kc + (int64_t)r * (D / 2) + 16 * c) : v4i{};
+    }
+    for (int g = l; g < 64; g += 64) *(uint32_t*)(L.ks + 4 * g) = g < 32 ? *(const uint32_t*)(ks + 4 * g) : 0u;
+    __syncthreads();
+    v4i qb[2];
+    int qsb[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        qb[kk] = *(const v4i*)(qc + (int64_t)lq * (D / 2) + 32 * kk + 16 * h);
+        qsb[kk] = qs[lq * (D / 32) + 2 * kk + h];
+    }
+    v16f s0, s1;
+    qk_tile_mx(L, qb, qsb, sigma(lq), h, s0, s1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[lq * 32 + 16 * h + i] = s0[i];
+}
+
+}  // namespace
+
+hipError_t launch_qat_fwd(const QatFwdArgs& a, hipStream_t st) {
+    if (a.vdeq) {
+        const int64_t nblocks = (int64_t)a.B * a.Hkv * D * (a.Nk / 32);
+        vdeq_kernel<<<(unsigned)((nblocks + 255) / 256), 256, 0, st>>>(a.vc, a.vs, nblocks, a.vdeq);
+    }
+    const int grid = a.B * a.Hq * ((a.Nq + BM - 1) / BM);
+    if (a.vdeq) qat_fwd_kernel<true><<<grid, 256, 0, st>>>(a);
+    else qat_fwd_kernel<false><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+size_t ws_qat_fwd_bytes(int B, int Hkv, int Nk, int d) { return (size_t)B * Hkv * Nk * d * 2; }
+
+hipError_t launch_debug_scores_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                                  float* out, hipStream_t st) {
+    debug_scores_mx_kernel<<<1, 64, 0, st>>>(qc, qs, kc, ks, out);
+    return hipGetLastError();
+}
+
+}  // namespace bqa

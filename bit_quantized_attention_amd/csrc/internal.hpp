@@ -37,4 +37,20 @@ hipError_t launch_sage_fwd(const SageFwdArgs& a, int pv, int d, hipStream_t st);
 hipError_t launch_debug_scores_i8(const int8_t* qc, const int8_t* kc, int d, int64_t q_row0, int64_t k_row0,
                                   int32_t* out, hipStream_t st);
 
+// ---- Attn-QAT MXFP4 forward (attn_qat.hip); head dimension 128, non-causal
+struct QatFwdArgs {
+    const uint8_t* qc; const uint8_t* qs;                // Q codes [B,Hq,Nq,d/2], E8M0 [B,Hq,Nq,d/32]
+    const uint8_t* kc; const uint8_t* ks;                // K codes [B,Hkv,Nk,d/2], E8M0 [B,Hkv,Nk,d/32]
+    const uint8_t* vc; const uint8_t* vs;                // V codes [B,Hkv,d,Nk/2], E8M0 [B,Hkv,d,Nk/32]
+    uint16_t* vdeq;                                      // workspace [B,Hkv,d,Nk] bf16; null: no O'
+    Dense o, oa;                                         // O, O' [B,Hq,Nq,d] bf16
+    float* lse;                                          // [B,Hq,Nq] or null
+    int B, Hq, Hkv, Nq, Nk;
+    float c_log2;                                        // tau * log2(e)
+};
+size_t ws_qat_fwd_bytes(int B, int Hkv, int Nk, int d);
+hipError_t launch_qat_fwd(const QatFwdArgs& a, hipStream_t st);
+hipError_t launch_debug_scores_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                                  float* out, hipStream_t st);
+
 }  // namespace bqa

@@ -9,9 +9,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (BQA_FP8E4M3, BQA_INT8, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_V, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V,
-               BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV, bqa_attn_fwd, bqa_quantize_blocks, bqa_workspace_size, dense,
-               problem, qtensor)
+from . import (BQA_FP8E4M3, BQA_INT8, BQA_MXFP4, BQA_OP_FWD, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_V,
+               BQA_QAT_MXFP4, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V, BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV,
+               bqa_attn_fwd, bqa_quantize_blocks, bqa_workspace_size, dense, problem, qtensor)
 
 
 def sage_problem(B, Hq, Hkv, Nq, Nk, d, causal, mode, q_block=128, k_block=64, smooth_k=True, smooth_eps=0.0,
@@ -59,6 +59,52 @@ class SagePath:
             bqa_attn_fwd(self.p, q=self.qq, k=self.kq, v_hi=self._vd, o=self._od, lse=self.lse)
         else:
             bqa_attn_fwd(self.p, q=self.qq, k=self.kq, v=self.vq, o=self._od, lse=self.lse)
+
+    def step(self):
+        self.quantize()
+        self.forward()
+        return self.o
+
+
+def qat_problem(B, Hq, Hkv, Nq, Nk, d, sm_scale=0.0):
+    return problem(B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d, causal=0, sm_scale=sm_scale, mode=BQA_QAT_MXFP4)
+
+
+class QatPath:
+    """Attn-QAT FP4 forward: MXFP4 Q, K (along d) and V (along tokens), then
+    attend, emitting O and (with aux=True) the bf16 auxiliary output O'."""
+
+    def __init__(self, p, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, aux: bool = True):
+        dev = q.device
+        self.p = p
+        B, Hq, Hkv, Nq, Nk, d = p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d
+        self.q, self.k, self.v = q, k, v
+        u8 = torch.uint8
+        self.qc = torch.empty((B, Hq, Nq, d // 2), dtype=u8, device=dev)
+        self.qs = torch.empty((B, Hq, Nq, d // 32), dtype=u8, device=dev)
+        self.kc = torch.empty((B, Hkv, Nk, d // 2), dtype=u8, device=dev)
+        self.ks = torch.empty((B, Hkv, Nk, d // 32), dtype=u8, device=dev)
+        self.vc = torch.empty((B, Hkv, d, Nk // 2), dtype=u8, device=dev)
+        self.vs = torch.empty((B, Hkv, d, Nk // 32), dtype=u8, device=dev)
+        self.qq = qtensor(BQA_MXFP4, 0, 32, self.qc, self.qs)
+        self.kq = qtensor(BQA_MXFP4, 0, 32, self.kc, self.ks)
+        self.vq = qtensor(BQA_MXFP4, 1, 32, self.vc, self.vs)
+        self.o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=dev)
+        self.oa = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=dev) if aux else None
+        self.lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(max(bqa_workspace_size(p, BQA_OP_FWD), 16) if aux else 16, dtype=u8, device=dev)
+        self._qd, self._kd, self._vd = dense(q), dense(k), dense(v)
+        self._od = dense(self.o)
+        self._oad = dense(self.oa) if aux else None
+
+    def quantize(self):
+        bqa_quantize_blocks(self.p, BQA_ROLE_Q, self._qd, self.qq)
+        bqa_quantize_blocks(self.p, BQA_ROLE_K, self._kd, self.kq)
+        bqa_quantize_blocks(self.p, BQA_ROLE_V, self._vd, self.vq)
+
+    def forward(self):
+        bqa_attn_fwd(self.p, q=self.qq, k=self.kq, v=self.vq, o=self._od, o_aux=self._oad, lse=self.lse,
+                     workspace=self.ws)
 
     def step(self):
         self.quantize()

@@ -200,9 +200,13 @@ bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const f
  *    is updated, P = exp(s - m) is rounded for P.V as the mode says, and the
  *    row sum accumulates the unrounded P.
  *  - BQA_QAT_MXFP4 ("Attn-QAT", §2): q, k MXFP4 along d, v MXFP4 along tokens;
- *    key tiles of 128; P is MXFP4 per 32 keys of the row for O; when o_aux is
- *    not NULL, O' = sum bf16(P) V / l is written too (Principle 2).
- *    Non-causal only.
+ *    d = 128, non-causal, Nk a multiple of 64.  P is taken relative to a
+ *    power-of-two reference point and made MXFP4 per 32 keys of the row for
+ *    O (so its codes do not depend on how the keys are tiled); the row sum
+ *    uses the unrounded P.  When o_aux is not NULL, O' = sum bf16(P) V / l is
+ *    written too (Principle 2); this needs a workspace of
+ *    bqa_workspace_size(p, BQA_OP_FWD) bytes (a bf16 copy of the dequantised
+ *    V), else none.
  *  - BQA_THRIFT ("ThriftAttention", Method step 2 and kernel paragraph): per
  *    query block, the unselected valid key blocks go through the FP4 path
  *    (MXFP4 q, k, v; P quantised in two levels: scaled so its row max is 6,

@@ -1,0 +1,115 @@
+"""GPU parity of the Attn-QAT FP4 forward against the oracle, through the C ABI:
+the MXFP4 scores of one tile, then O, O' and the log-sum-exp on the
+heavy-tailed Student-t recipe (small, ragged, grouped heads, full size on
+sampled rows)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import workloads as wl
+from tests.helpers import assert_same, compare_outputs, tau_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import bit_quantized_attention_amd as bqa
+    bqa.lib()
+
+
+def _run(w, Nq=None, aux=True):
+    from bit_quantized_attention_amd.runner import QatPath, qat_problem, to_device
+    Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
+    if Nq is not None:
+        Q = np.ascontiguousarray(Q[:, :, :Nq])
+    p = qat_problem(w.B, w.Hq, w.Hkv, Q.shape[2], K.shape[2], w.d)
+    path = QatPath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"), aux=aux)
+    path.step()
+    torch.cuda.synchronize()
+    return p, path, (Q, K, V)
+
+
+class _Oracle:
+    def __init__(self, Q, K, V):
+        self.Hq, self.Hkv, self.Nq, self.Nk, self.d = Q.shape[1], K.shape[1], Q.shape[2], K.shape[2], Q.shape[3]
+        self.qc, self.qs = orc.quant_mx_rows(Q.reshape(-1, self.Nq, self.d))
+        self.kc, self.ks = orc.quant_mx_rows(K.reshape(-1, self.Nk, self.d))
+        self.vc, self.vs = orc.quant_mx_cols(V.reshape(-1, self.Nk, self.d))
+
+    def forward(self, b, h, rows=None):
+        iq, ik = b * self.Hq + h, b * self.Hkv + h // (self.Hq // self.Hkv)
+        return orc.qat_fwd(qc=self.qc[iq], qs=self.qs[iq], kc=self.kc[ik], ks=self.ks[ik], vc_t=self.vc[ik],
+                           vs_t=self.vs[ik], Nq=self.Nq, Nk=self.Nk, d=self.d, tau=tau_for(self.d), kv_tile=64,
+                           rows=rows)
+
+
+def _check(path, oc, heads, rows=None):
+    O = path.o.float().cpu().numpy()
+    Oa = path.oa.float().cpu().numpy() if path.oa is not None else None
+    L = path.lse.cpu().numpy()
+    for b, h in heads:
+        r = rows or (0, oc.Nq)
+        ref, ref_aux, lse = oc.forward(b, h, rows=r)
+        compare_outputs(O[b, h, r[0]:r[1]], ref, "bf16", what=f"O[b={b},h={h},rows={r}]")
+        if Oa is not None:
+            compare_outputs(Oa[b, h, r[0]:r[1]], ref_aux, "bf16", what=f"O'[b={b},h={h},rows={r}]")
+        assert np.abs(L[b, h, r[0]:r[1]] - lse).max() < 2e-3
+
+
+def test_mx_scores_tile():
+    """One 32 x 32 tile of raw MXFP4 scores from the forward's tile code: the
+    exact MX dot products (the oracle's are exact rationals) to fp32 accuracy."""
+    import bit_quantized_attention_amd as bqa
+    w = wl.with_len(wl.WORKLOADS["c4"], 256, hq=2, hkv=2)
+    p, path, (Q, K, V) = _run(w)
+    oc = _Oracle(Q, K, V)
+    assert_same(path.qc.cpu().numpy().reshape(oc.qc.shape), oc.qc, "Q MX codes")
+    assert_same(path.kc.cpu().numpy().reshape(oc.kc.shape), oc.kc, "K MX codes")
+    out = torch.empty((32, 32), dtype=torch.float32, device="cuda")
+    for (h, qt, kt) in ((0, 0, 0), (1, 3, 5), (1, 7, 2)):
+        bqa.bqa_debug_qk_scores(p, path.qq, path.kq, 0, h, qt, kt, out)
+        torch.cuda.synchronize()
+        g = out.cpu().numpy().astype(np.float64)
+        ref = np.empty((32, 32))
+        for i in range(32):
+            for j in range(32):
+                ref[i, j], _ = orc.mx_score(oc.qc[h], oc.qs[h], oc.kc[h], oc.ks[h], 128, 32 * qt + i, 32 * kt + j)
+        # fp32 accumulation of exact block sums: within a few ulps of the largest partial sum
+        bound = 4 * np.finfo(np.float32).eps * (np.abs(ref).max() + 1e-30)
+        assert np.abs(g - ref).max() <= bound, (h, qt, kt, np.abs(g - ref).max(), bound)
+
+
+@pytest.mark.parametrize("Nq,Nk,hq,hkv", [(512, 512, 2, 2), (1000, 1024, 4, 2), (64, 384, 1, 1)])
+def test_qat_forward_small(Nq, Nk, hq, hkv):
+    """c4 recipe at sizes spanning several tiles: ragged query count, grouped
+    heads, a single partial query tile."""
+    w = wl.with_len(wl.WORKLOADS["c4"], Nk, hq=hq, hkv=hkv)
+    p, path, (Q, K, V) = _run(w, Nq=Nq)
+    oc = _Oracle(Q, K, V)
+    assert_same(path.vc.cpu().numpy().reshape(oc.vc.shape), oc.vc, "V MX codes")
+    _check(path, oc, [(0, h) for h in range(hq)])
+
+
+def test_qat_forward_without_aux_matches():
+    """Without O' the kernel takes its other variant; O must be bit-identical."""
+    w = wl.with_len(wl.WORKLOADS["c4"], 1024, hq=2, hkv=2)
+    _, with_aux, _ = _run(w)
+    _, no_aux, _ = _run(w, aux=False)
+    assert torch.equal(with_aux.o, no_aux.o)
+    assert torch.equal(with_aux.lse, no_aux.lse)
+
+
+@pytest.mark.slow
+def test_qat_forward_full_size_sampled():
+    """Full c4 shape (B=1, H=32, N=16384, d=128, non-causal); the oracle checks
+    sampled rows of sampled heads."""
+    w = wl.WORKLOADS["c4"]
+    p, path, (Q, K, V) = _run(w)
+    oc = _Oracle(Q, K, V)
+    for h in (0, 13, 31):
+        for r0 in (0, 8191, 16384 - 16):
+            _check(path, oc, [(0, h)], rows=(r0, r0 + 16))
