@@ -1,20 +1,26 @@
 """Benchmark of the block-quantized attention hot path on one MI355X.
 
-Default workload: the SageAttention INT8 forward at B=2, H=16, N=4096,
-d=128, causal, bf16 inputs (outlier channels and a K channel bias), INT8
-Q/K with K-smoothing, e4m3 P.V.  One step = one pass of the whole path over
-the batch: K-smoothing means, INT8 quantisation of Q and K, per-channel e4m3
-V, and the fused attention kernel.  Inputs are generated on the host and are
-resident in HBM before timing starts.
+Workloads (``--workload``, default c2):
+
+  c2  SageAttention INT8 forward at B=2, H=16, N=4096, d=128, causal, bf16
+      inputs (outlier channels and a K channel bias): K-smoothing means, INT8
+      Q/K, per-channel e4m3 V, fused attention with e4m3 P.V.
+  c4  Attn-QAT FP4 forward at B=1, H=32, N=16384, d=128, non-causal,
+      Student-t inputs: MXFP4 Q, K, V, fused attention with MXFP4 P.V and
+      the bf16 auxiliary output O'.
+
+One step = one pass of the whole path over the batch (quantisers and
+attention).  Inputs are generated on the host and are resident in HBM
+before timing starts.
 
 Prints one JSON line.  `value` is effective attention TOPS of the whole step
 (4*B*H*N^2*d, halved for causal, over the step time).  `roofline` reports the
-attention kernel alone: its algorithmic ops per launch over its average
-launch time, measured with HIP events on the stream it runs on, against the
-i8/fp8 dense MFMA peak.  `cpu_baseline` times the CPU oracle on a bounded
-sample of the same workload.
+attention call alone: its algorithmic operations per launch over its average
+time, measured with HIP events on the stream it runs on, against the dense
+matrix-core peak of its operand types.  `cpu_baseline` times the CPU oracle
+on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--workload c2|c4] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -29,6 +35,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_I8_TOPS = 5033.2          # MI355X dense INT8 (and FP8) MFMA peak, 256 CU x 2.4 GHz x 8192 ops/clk
+PEAK_F4_TFLOPS = 10066.3       # dense MXFP4, twice the fp8 rate
+PEAK_BF16_TFLOPS = 2516.6      # dense bf16, half the fp8 rate
 METRIC = "attention TOPS (fwd, fwd+bwd) at d=128, N=4k-131k; % of i8/fp8/fp4 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -88,18 +96,89 @@ def cpu_baseline(w, budget_s: float = 20.0):
                       f"{dt:.1f} s"}
 
 
+def cpu_baseline_qat(w, budget_s: float = 20.0):
+    """The oracle on a bounded sample of the Attn-QAT forward: MXFP4
+    quantisation of one whole head, then its forward (O and O') over chunks of
+    query rows until the time budget is spent."""
+    import oracle
+    import workloads as wl
+    from tests.helpers import tau_for
+    oracle.lib()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    Q, K, V = (wl.chunk(w, t, 0, 0)[None] for t in ("q", "k", "v"))
+    qc, qs = oracle.quant_mx_rows(Q)
+    kc, ks = oracle.quant_mx_rows(K)
+    vc, vs = oracle.quant_mx_cols(V)
+    rows, r0, chunk = 0, 0, 16
+    while r0 < w.Nq and time.perf_counter() - t0 < budget_s:
+        oracle.qat_fwd(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0], Nq=w.Nq, Nk=w.Nk, d=w.d,
+                       tau=tau_for(w.d), kv_tile=64, rows=(r0, r0 + chunk))
+        rows += chunk
+        r0 += chunk
+    dt = time.perf_counter() - t0
+    ops = 4.0 * rows * w.Nk * w.d
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"head (0,0): MXFP4 quantisation of Q, K, V, then O and O' for {rows} of {w.Nq} query "
+                      f"rows against N={w.Nk} keys, {dt:.1f} s"}
+
+
+def _sage_case(w, bqa, torch):
+    from bit_quantized_attention_amd.runner import SagePath, attention_ops, sage_problem, to_device
+    import workloads as wl
+    Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
+    p = sage_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.causal, bqa.BQA_SAGE_I8_F8PV, q_block=128,
+                     smooth_k=True, smooth_eps=0.0)
+    path = SagePath(p, to_device(Q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype))
+    ops = attention_ops(p)
+    return dict(
+        path=path, ops=ops, dtype="i8+e4m3",
+        workload="SageAttention INT8 forward (c2): B=2 H=16 N=4096 d=128 causal, bf16 in, K-smoothing, "
+                 "INT8 Q/K, e4m3 P.V; step = quantise Q,K,V + attention",
+        roofline={"bound": "mfma", "kernel": "sage_fwd_kernel (i8 QK^T + fp8 P.V)", "peak": PEAK_I8_TOPS,
+                  "ops_per_launch": ops},
+        traffic_key="sage_fwd_kernel<F8,128,causal>", cpu=cpu_baseline)
+
+
+def _qat_case(w, bqa, torch):
+    from bit_quantized_attention_amd.runner import QatPath, attention_ops, qat_problem, to_device
+    import workloads as wl
+    Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
+    p = qat_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+    path = QatPath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"), aux=True)
+    ops = attention_ops(p)                       # the two MXFP4 products
+    aux = ops / 2                                # O' = bf16(P) V, one more product of the P.V size
+    # time at the two peaks: the fp4 products at the MXFP4 rate, O' at the bf16 rate
+    t_peak = ops / (PEAK_F4_TFLOPS * 1e12) + aux / (PEAK_BF16_TFLOPS * 1e12)
+    return dict(
+        path=path, ops=ops, dtype="mxfp4+bf16",
+        workload="Attn-QAT FP4 forward (c4): B=1 H=32 N=16384 d=128 non-causal, Student-t bf16 in, MXFP4 Q/K/V/P, "
+                 "bf16 auxiliary output O'; step = quantise Q,K,V + attention",
+        roofline={"bound": "mfma", "kernel": "attn_fwd QAT (vdeq_kernel + qat_fwd_kernel<aux>): MXFP4 QK^T and "
+                                             "P.V plus bf16 O'",
+                  "peak": round((ops + aux) / t_peak / 1e12, 1), "peak_note": "fp4 and bf16 dense peaks "
+                  "weighted by each product's share of the operations",
+                  "ops_per_launch": ops + aux},
+        traffic_key="qat_fwd_kernel<aux>", cpu=cpu_baseline_qat)
+
+
+CASES = {"c2": _sage_case, "c4": _qat_case}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=sorted(CASES), default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(every kernel is independent per (batch, head); sharding is described in DESIGN.md)",
+              f"(every kernel is independent per (batch, head), so the path shards by heads; "
+              f"this benchmark measures one GPU's share)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -107,7 +186,6 @@ def main():
 
     import bit_quantized_attention_amd as bqa
     import workloads as wl
-    from bit_quantized_attention_amd.runner import SagePath, attention_ops, sage_problem, to_device
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
@@ -119,12 +197,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": src.numel(), "launches": 5}))
         return
-    w = wl.WORKLOADS["c2"]
-    Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
-    p = sage_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.causal, bqa.BQA_SAGE_I8_F8PV, q_block=128,
-                     smooth_k=True, smooth_eps=0.0)
-    path = SagePath(p, to_device(Q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype))
-    del Q, K, V
+    w = wl.WORKLOADS[args.workload]
+    case = CASES[args.workload](w, bqa, torch)
+    path = case["path"]
     for _ in range(args.warmup):
         path.step()
     torch.cuda.synchronize()
@@ -142,11 +217,13 @@ def main():
     dt = time.perf_counter() - t0
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
 
-    ops = attention_ops(p)
+    ops = case["ops"]
     ms_per_step = dt * 1e3 / args.steps
     value = ops / (ms_per_step * 1e-3) / 1e12
-    achieved = ops / (kern_ms * 1e-3) / 1e12
-    traffic = _traffic_for("sage_fwd_kernel<F8,128,causal>")
+    rl = dict(case["roofline"])
+    achieved = rl["ops_per_launch"] / (kern_ms * 1e-3) / 1e12
+    rl.update({"achieved": round(achieved, 1), "unit": "TFLOP/s", "frac": round(achieved / rl["peak"], 4),
+               "traffic": _traffic_for(case["traffic_key"]), "kernel_ms": round(kern_ms, 5)})
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -158,19 +235,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8+e4m3",
+        "dtype": case["dtype"],
         "data": "synthetic",
-        "config": {"workload": "SageAttention INT8 forward (c2): B=2 H=16 N=4096 d=128 causal, bf16 in, "
-                               "K-smoothing, INT8 Q/K, e4m3 P.V; step = quantise Q,K,V + attention",
-                   "global_batch": w.B, "seq_len": w.Nk, "heads": w.Hq, "head_dim": w.d,
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "sage_fwd_kernel (i8 QK^T + fp8 P.V)",
-                     "achieved": round(achieved, 1), "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_I8_TOPS, 4), "traffic": traffic,
-                     "kernel_ms": round(kern_ms, 5), "ops_per_launch": ops},
+        "config": {"workload": case["workload"], "global_batch": w.B, "seq_len": w.Nk, "heads": w.Hq,
+                   "head_dim": w.d, "parallelism": "single GPU"},
+        "roofline": rl,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w)
+        line["cpu_baseline"] = case["cpu"](w)
     print(json.dumps(line), flush=True)
 
 

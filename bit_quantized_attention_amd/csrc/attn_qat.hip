@@ -59,56 +59,47 @@ struct Lds {
     uint8_t vb[D * BN * 2];        // deq(Vhat)^T bf16, 128 rows x 128 B
 };
 
-template <bool AUX>
-struct Stage {
-    v4i kc, vc;
-    v4i vb[AUX ? 4 : 1];
-    uint32_t ks, vs;
-};
-
-template <bool AUX>
-__device__ __forceinline__ void stage_load(Stage<AUX>& st, const QatFwdArgs& a, int bhk, int t0, int tid) {
-    // K codes: 64 rows x 4 chunks
-    {
-        const int r = tid >> 2, c = tid & 3;
-        st.kc = *(const v4i*)(a.kc + ((int64_t)bhk * a.Nk + t0 + r) * (D / 2) + 16 * c);
-    }
-    // Vhat^T codes: 128 rows x 2 chunks
-    {
-        const int r = tid >> 1, c = tid & 1;
-        st.vc = *(const v4i*)(a.vc + ((int64_t)bhk * D + r) * (a.Nk / 2) + t0 / 2 + 16 * c);
-    }
-    // K scales: 64 rows x 4 bytes = 64 words; Vhat scales: 128 rows x 2 bytes
-    st.ks = tid < 64 ? *(const uint32_t*)(a.ks + ((int64_t)bhk * a.Nk + t0 + tid) * (D / 32)) : 0u;
-    st.vs = tid < 128 ? (uint32_t)*(const uint16_t*)(a.vs + ((int64_t)bhk * D + tid) * (a.Nk / 32) + t0 / 32) : 0u;
-    if constexpr (AUX) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int g = tid + 256 * u, r = g >> 3, c = g & 7;
-            st.vb[u] = *(const v4i*)(a.vdeq + ((int64_t)bhk * D + r) * a.Nk + t0 + 8 * c);
-        }
-    }
+// Direct global -> LDS copies (global_load_lds): every lane names its global
+// source, the data lands at LDS base + 16 x lane (4 x lane for dwords), so
+// the swizzled layouts are produced by choosing which source each lane reads.
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
 }
 
+// Issue the copies of key tile t0 into L (K codes and scales, Vhat^T codes,
+// and for O' the bf16 deq(Vhat)^T); Vhat's scales come back in a register
+// (128 strided 2-byte values) and are stored by vs_store.
 template <bool AUX>
-__device__ __forceinline__ void stage_store(const Stage<AUX>& st, Lds& L, int tid) {
-    {
-        const int r = tid >> 2, c = tid & 3;
-        *(v4i*)(L.kc + swz64(r, c)) = st.kc;
+__device__ __forceinline__ uint32_t tile_issue(const QatFwdArgs& a, int bhk, int t0, Lds& L, int w, int l, int tid) {
+    {   // K codes: wave w fills rows 16w .. 16w + 15
+        const int r = 16 * w + (l >> 2);
+        const int c = (l & 3) ^ (((r >> 2) & 3) ^ (((r >> 4) & 1) << 1));
+        dma16(a.kc + ((int64_t)bhk * a.Nk + t0 + r) * (D / 2) + 16 * c, L.kc + 1024 * w);
     }
-    {
-        const int r = tid >> 1, c = tid & 1;
-        *(v4i*)(L.vc + swz32(r, c)) = st.vc;
+    {   // Vhat^T codes: wave w fills rows 32w .. 32w + 31
+        const int r = 32 * w + (l >> 1);
+        const int c = (l & 1) ^ ((r >> 3) & 1);
+        dma16(a.vc + ((int64_t)bhk * D + r) * (a.Nk / 2) + t0 / 2 + 16 * c, L.vc + 1024 * w);
     }
-    if (tid < 64) *(uint32_t*)(L.ks + 4 * tid) = st.ks;
-    if (tid < 128) *(uint16_t*)(L.vs + 2 * tid) = (uint16_t)st.vs;
+    if (w == 0) dma4(a.ks + ((int64_t)bhk * a.Nk + t0 + l) * (D / 32), L.ks);
     if constexpr (AUX) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int g = tid + 256 * u, r = g >> 3, c = g & 7;
-            *(v4i*)(L.vb + swz128(r, c)) = st.vb[u];
+        for (int u = 0; u < 4; ++u) {   // 1 KB segments 4w + u: rows 8 (4w + u) .. + 7
+            const int sgm = 4 * w + u, r = 8 * sgm + (l >> 3);
+            const int c = (l & 7) ^ ((r >> 1) & 7);
+            dma16(a.vdeq + ((int64_t)bhk * D + r) * a.Nk + t0 + 8 * c, L.vb + 1024 * sgm);
         }
     }
+    return tid < 128 ? (uint32_t)*(const uint16_t*)(a.vs + ((int64_t)bhk * D + tid) * (a.Nk / 32) + t0 / 32) : 0u;
+}
+
+__device__ __forceinline__ void vs_store(uint32_t vs, Lds& L, int tid) {
+    if (tid < 128) *(uint16_t*)(L.vs + 2 * tid) = (uint16_t)vs;
 }
 
 // S^T tile (64 keys x 32 queries) from MXFP4 codes: acc0 keys 16h + i,
@@ -128,7 +119,7 @@ __device__ __forceinline__ void qk_tile_mx(const Lds& L, const v4i* qb, const in
 }
 
 template <bool AUX>
-__global__ __launch_bounds__(256, AUX ? 1 : 2) void qat_fwd_kernel(QatFwdArgs a) {
+__global__ __launch_bounds__(256, 2) void qat_fwd_kernel(QatFwdArgs a) {
     __shared__ __attribute__((aligned(16))) Lds lds[NBUF];
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
     // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
@@ -164,22 +155,28 @@ __global__ __launch_bounds__(256, AUX ? 1 : 2) void qat_fwd_kernel(QatFwdArgs a)
     const float c = a.c_log2;
     const int n_tiles = a.Nk / BN;
 
-    Stage<AUX> st;
-    stage_load<AUX>(st, a, bhk, 0, tid);
-    stage_store<AUX>(st, lds[0], tid);
+    vs_store(tile_issue<AUX>(a, bhk, 0, lds[0], w, l, tid), lds[0], tid);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     auto body = [&](int j, auto bufc) __attribute__((always_inline)) {
         constexpr int B0 = decltype(bufc)::value;
-        if (j + 1 < n_tiles) stage_load<AUX>(st, a, bhk, (j + 1) * BN, tid);
+        uint32_t vs_next = 0;
+        if (j + 1 < n_tiles) vs_next = tile_issue<AUX>(a, bhk, (j + 1) * BN, lds[B0 ^ 1], w, l, tid);
         const Lds& L = lds[B0];
         v16f s0, s1;
         qk_tile_mx(L, qb, qsb, krow, h, s0, s1);
-        // ---- frame: fixed reference; moved (exactly) only when scores climb far above it
-        float mx = __builtin_fmaxf(s0[0], s1[0]);
+        // ---- block maxima of the raw scores: keys 0..31 (s0 of both halves), 32..63 (s1)
+        float b0 = __builtin_fmaxf(s0[0], s0[1]), b1 = __builtin_fmaxf(s1[0], s1[1]);
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s0[i]), s1[i]);
-        mx = __builtin_fmaxf(mx, partner32f(mx)) * c;
+        for (int i = 2; i < 16; i += 2) {
+            b0 = __builtin_fmaxf(__builtin_fmaxf(b0, s0[i]), s0[i + 1]);
+            b1 = __builtin_fmaxf(__builtin_fmaxf(b1, s1[i]), s1[i + 1]);
+        }
+        b0 = __builtin_fmaxf(b0, partner32f(b0));
+        b1 = __builtin_fmaxf(b1, partner32f(b1));
+        // ---- frame: fixed reference; moved (exactly) only when scores climb far above it
+        const float mx = __builtin_fmaxf(b0, b1) * c;
         if (m_ref == -__builtin_inff() || __any(mx > m_ref + 64.0f)) {
             const float m_new = __builtin_ceilf(__builtin_fmaxf(mx, m_ref));
             if (m_ref != -__builtin_inff()) {
@@ -198,20 +195,19 @@ __global__ __launch_bounds__(256, AUX ? 1 : 2) void qat_fwd_kernel(QatFwdArgs a)
             }
             m_ref = m_new;
         }
-        float psum = 0.0f, a0 = 0.0f, a1 = 0.0f;
+        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -m_ref));
             s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -m_ref));
-            psum += s0[i] + s1[i];
-            a0 = __builtin_fmaxf(a0, s0[i]);
-            a1 = __builtin_fmaxf(a1, s1[i]);
+            ps[i & 1] += s0[i];
+            ps[2 + (i & 1)] += s1[i];
         }
-        l_run += psum;
-        // ---- MXFP4 P: block kb = keys 32kb .. 32kb+31 (16 in each lane half)
-        a0 = __builtin_fmaxf(a0, partner32f(a0));
-        a1 = __builtin_fmaxf(a1, partner32f(a1));
-        const int e0 = mx_exponent(a0), e1 = mx_exponent(a1);
+        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        // ---- MXFP4 P per 32-key block: P is monotone in the score, so the
+        // block's largest P is the P of its largest score
+        const int e0 = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(b0, c, -m_ref)));
+        const int e1 = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(b1, c, -m_ref)));
         const float sc0 = __builtin_bit_cast(float, (uint32_t)(e0 + 127) << 23);
         const float sc1 = __builtin_bit_cast(float, (uint32_t)(e1 + 127) << 23);
         uint32_t p0w[2], p1w[2];
@@ -254,7 +250,8 @@ __global__ __launch_bounds__(256, AUX ? 1 : 2) void qat_fwd_kernel(QatFwdArgs a)
                 }
             }
         }
-        if (j + 1 < n_tiles) stage_store<AUX>(st, lds[B0 ^ 1], tid);
+        if (j + 1 < n_tiles) vs_store(vs_next, lds[B0 ^ 1], tid);
+        __builtin_amdgcn_s_waitcnt(0);   // the tile copies have landed
         __syncthreads();
     };
     for (int j = 0; j < n_tiles; j += 2) {
