@@ -103,6 +103,13 @@ def problem(**kw) -> bqa_problem:
     return p
 
 
+def max_sel(p: bqa_problem) -> int:
+    """Slots per query block of the selection output, as include/bqa.h sizes
+    it: max(1, ceil(nkb * budget)), at most nkb = Nk / sel_block."""
+    nkb = p.Nk // p.sel_block
+    return max(1, min(nkb, -(-nkb * p.hp_budget_ppm // 1_000_000)))
+
+
 def _ptr(t):
     if t is None:
         return None

@@ -75,6 +75,15 @@ bqa_status check_q(const bqa_qtensor* q, int fmt, int axis) {
     return BQA_OK;
 }
 
+// slots per query block in sel_idx: max(1, ceil(nkb * budget)), at most nkb
+int max_sel_of(const bqa_problem* p) {
+    const int nkb = p->Nk / p->sel_block;
+    int64_t k = ((int64_t)nkb * p->hp_budget_ppm + 999999) / 1000000;
+    if (k < 1) k = 1;
+    if (k > nkb) k = nkb;
+    return (int)k;
+}
+
 float tau_of(const bqa_problem* p) { return p->sm_scale > 0.0f ? p->sm_scale : 1.0f / std::sqrt((float)p->d); }
 
 bqa_status launched(hipError_t e) { return e == hipSuccess ? BQA_OK : BQA_E_LAUNCH; }
@@ -173,9 +182,19 @@ bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_ten
 
 bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const float* k_means, int32_t* sel_idx,
                              int32_t* sel_cnt, void* ws, size_t ws_bytes, void* stream) {
-    (void)q_means; (void)k_means; (void)sel_idx; (void)sel_cnt; (void)ws; (void)ws_bytes; (void)stream;
+    (void)ws; (void)ws_bytes;
     TRY(check_problem(p));
-    return BQA_E_UNSUPPORTED;
+    if (p->mode != BQA_THRIFT || p->sel_block != 128) return BQA_E_UNSUPPORTED;
+    if (!q_means || !k_means || !sel_idx || !sel_cnt) return BQA_E_NULL;
+    if (p->Nk % p->sel_block != 0) return BQA_E_UNSUPPORTED;
+    if (p->hp_budget_ppm < 0 || p->hp_budget_ppm > 1000000) return BQA_E_SHAPE;
+    const int nkb = p->Nk / p->sel_block, nqb = (p->Nq + p->sel_block - 1) / p->sel_block;
+    if (nkb > 4096) return BQA_E_UNSUPPORTED;
+    if (!aligned16(k_means) || ((uintptr_t)q_means & 3u) || ((uintptr_t)sel_idx & 3u) || ((uintptr_t)sel_cnt & 3u))
+        return BQA_E_ALIGN;
+    TRY(check_device());
+    return launched(launch_select(q_means, k_means, p->B, p->Hq, p->Hkv, nqb, nkb, p->d, p->causal,
+                                  p->hp_budget_ppm, max_sel_of(p), sel_idx, sel_cnt, (hipStream_t)stream));
 }
 
 bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k, const bqa_qtensor* v,

@@ -53,4 +53,10 @@ hipError_t launch_qat_fwd(const QatFwdArgs& a, hipStream_t st);
 hipError_t launch_debug_scores_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                                   float* out, hipStream_t st);
 
+// ---- ThriftAttention block selection (select.hip)
+int select_sort_len(int nkb);
+hipError_t launch_select(const float* qbar, const float* kbar, int B, int Hq, int Hkv, int nqb, int nkb, int d,
+                         int causal, int budget_ppm, int max_sel, int32_t* sel_idx, int32_t* sel_cnt,
+                         hipStream_t st);
+
 }  // namespace bqa

@@ -1,0 +1,115 @@
+"""GPU parity of the ThriftAttention path against the oracle, through the C
+ABI: block selection (bit-exact indices and counts)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import workloads as wl
+from tests.helpers import assert_same
+
+pytestmark = pytest.mark.gpu
+
+PPM_5 = 50_000          # the pages' 5 % budget, in parts per million
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import bit_quantized_attention_amd as bqa
+    bqa.lib()
+
+
+def _select_gpu(p, qbar, kbar):
+    import bit_quantized_attention_amd as bqa
+    B, Hq, nqb, d = qbar.shape
+    ms = bqa.max_sel(p)
+    idx = torch.full((B, Hq, nqb, ms), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, Hq, nqb), -7, dtype=torch.int32, device="cuda")
+    bqa.bqa_select_blocks(p, torch.from_numpy(qbar).cuda(), torch.from_numpy(kbar).cuda(), idx, cnt)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy(), ms
+
+
+def _select_oracle(qbar, kbar, causal, ppm, ms):
+    B, Hq, nqb, d = qbar.shape
+    Hkv = kbar.shape[1]
+    idx = np.empty((B, Hq, nqb, ms), np.int32)
+    cnt = np.empty((B, Hq, nqb), np.int32)
+    for b in range(B):
+        for h in range(Hq):
+            idx[b, h], cnt[b, h] = orc.select_blocks(qbar[b, h], kbar[b, h // (Hq // Hkv)], causal, ppm, ms)
+    return idx, cnt
+
+
+@pytest.mark.parametrize("ppm", [PPM_5, 250_000, 0, 1_000_000])
+def test_selection_from_block_means(ppm):
+    """c5 recipe (low-rank shared component, GQA 8/2) at N=4096: the GPU's
+    own block means feed the GPU selection; the oracle computes its means
+    from the same inputs."""
+    import bit_quantized_attention_amd as bqa
+    from bit_quantized_attention_amd.runner import to_device
+    w = wl.with_len(wl.WORKLOADS["c5"], 4096, hq=8, hkv=2)
+    p = bqa.problem(B=1, Hq=8, Hkv=2, Nq=4096, Nk=4096, d=128, causal=1, mode=bqa.BQA_THRIFT, sel_block=128,
+                    hp_budget_ppm=ppm)
+    means = {}
+    for name, role, H in (("q", bqa.BQA_ROLE_Q, 8), ("k", bqa.BQA_ROLE_K, 2)):
+        X = wl.build(w, name)
+        codes = torch.empty((1, H, 4096, 64), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((1, H, 4096, 4), dtype=torch.uint8, device="cuda")
+        bm = torch.empty((1, H, 32, 128), dtype=torch.float32, device="cuda")
+        bqa.bqa_quantize_blocks(p, role, to_device(X, "bf16"), bqa.qtensor(bqa.BQA_MXFP4, 0, 32, codes, scales),
+                                block_means=bm)
+        means[name] = (bm, orc.block_means(X.reshape(H, 4096, 128), 128).reshape(1, H, 32, 128))
+    torch.cuda.synchronize()
+    qg, kg = (means[n][0].cpu().numpy() for n in ("q", "k"))
+    assert_same(qg, means["q"][1], "q block means")
+    assert_same(kg, means["k"][1], "k block means")
+    ms = bqa.max_sel(p)
+    idx, cnt, _ = _select_gpu(p, means["q"][1], means["k"][1])
+    ridx, rcnt = _select_oracle(means["q"][1], means["k"][1], True, ppm, ms)
+    assert_same(cnt, rcnt, "selection counts")
+    assert_same(idx, ridx, "selected blocks")
+
+
+def _lowrank_means(rng, B, H, nb, d, rank=4):
+    """Block means shaped like the c5 recipe's: a shared low-rank part per
+    head plus the block-averaged noise of 128 tokens."""
+    W = rng.standard_normal((H, rank, d)) / np.sqrt(d)
+    a = rng.standard_normal((B, H, nb, rank)) * 0.5
+    m = np.sqrt(d) * np.einsum("bhnr,hrd->bhnd", a, W) + rng.standard_normal((B, H, nb, d)) / np.sqrt(128)
+    return m.astype(np.float32)
+
+
+def test_selection_full_size_prefill():
+    """Full c5 prefill shape: 32 query heads, 8 KV heads, 1024 x 1024 causal
+    block pairs, 5 % budget (26,728 pairs per head)."""
+    import bit_quantized_attention_amd as bqa
+    rng = np.random.default_rng(51)
+    qbar = _lowrank_means(rng, 1, 32, 1024, 128)
+    kbar = _lowrank_means(rng, 1, 8, 1024, 128)
+    kbar[0, 3, 10] = kbar[0, 3, 11]                       # an exact tie: the smaller index ranks first
+    p = bqa.problem(B=1, Hq=32, Hkv=8, Nq=131072, Nk=131072, d=128, causal=1, mode=bqa.BQA_THRIFT, sel_block=128,
+                    hp_budget_ppm=PPM_5)
+    idx, cnt, ms = _select_gpu(p, qbar, kbar)
+    assert ms == 52
+    ridx, rcnt = _select_oracle(qbar, kbar, True, PPM_5, ms)
+    assert_same(cnt, rcnt, "selection counts")
+    assert int(cnt[0, 0].sum()) == 26728
+    assert_same(idx, ridx, "selected blocks")
+
+
+def test_selection_decode():
+    """Decode: one query per (b, head) against 1024 key blocks, k = 52."""
+    import bit_quantized_attention_amd as bqa
+    rng = np.random.default_rng(52)
+    qbar = _lowrank_means(rng, 16, 32, 1, 128)
+    kbar = _lowrank_means(rng, 16, 8, 1024, 128)
+    p = bqa.problem(B=16, Hq=32, Hkv=8, Nq=1, Nk=131072, d=128, causal=1, mode=bqa.BQA_THRIFT, sel_block=128,
+                    hp_budget_ppm=PPM_5)
+    idx, cnt, ms = _select_gpu(p, qbar, kbar)
+    ridx, rcnt = _select_oracle(qbar, kbar, True, PPM_5, ms)
+    assert np.all(cnt == 52)
+    assert_same(cnt, rcnt, "selection counts")
+    assert_same(idx, ridx, "selected blocks")
