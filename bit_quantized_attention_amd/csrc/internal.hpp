@@ -53,6 +53,21 @@ hipError_t launch_qat_fwd(const QatFwdArgs& a, hipStream_t st);
 hipError_t launch_debug_scores_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                                   float* out, hipStream_t st);
 
+// ---- ThriftAttention mixed prefill (attn_thrift.hip); head dimension 128, 128-token blocks
+struct ThriftFwdArgs {
+    const uint8_t* qc; const uint8_t* qs;                // MXFP4 Q [B,Hq,Nq,d/2], E8M0 [B,Hq,Nq,d/32]
+    const uint8_t* kc; const uint8_t* ks;                // MXFP4 K [B,Hkv,Nk,d/2], E8M0 [B,Hkv,Nk,d/32]
+    const uint8_t* vc; const uint8_t* vs;                // MXFP4 V [B,Hkv,d,Nk/2], E8M0 [B,Hkv,d,Nk/32]
+    Dense q_hi, k_hi, v_hi;                              // bf16 Q, K, V [B,H,N,d]
+    const int32_t* sel_idx; const int32_t* sel_cnt;      // [B,Hq,nqb,max_sel], [B,Hq,nqb]
+    int max_sel;
+    Dense o;                                             // O [B,Hq,Nq,d] bf16
+    float* lse;                                          // [B,Hq,Nq] or null
+    int B, Hq, Hkv, Nq, Nk, causal;
+    float c_log2;                                        // tau * log2(e)
+};
+hipError_t launch_thrift_fwd(const ThriftFwdArgs& a, hipStream_t st);
+
 // ---- ThriftAttention block selection (select.hip)
 int select_sort_len(int nkb);
 hipError_t launch_select(const float* qbar, const float* kbar, int B, int Hq, int Hkv, int nqb, int nkb, int d,

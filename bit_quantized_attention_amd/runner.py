@@ -10,8 +10,9 @@ from __future__ import annotations
 import torch
 
 from . import (BQA_FP8E4M3, BQA_INT8, BQA_MXFP4, BQA_OP_FWD, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_V,
-               BQA_QAT_MXFP4, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V, BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV,
-               bqa_attn_fwd, bqa_quantize_blocks, bqa_workspace_size, dense, problem, qtensor)
+               BQA_QAT_MXFP4, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V, BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV, BQA_THRIFT,
+               bqa_attn_fwd, bqa_quantize_blocks, bqa_select_blocks, bqa_workspace_size, dense, max_sel, problem,
+               qtensor)
 
 
 def sage_problem(B, Hq, Hkv, Nq, Nk, d, causal, mode, q_block=128, k_block=64, smooth_k=True, smooth_eps=0.0,
@@ -108,6 +109,59 @@ class QatPath:
 
     def step(self):
         self.quantize()
+        self.forward()
+        return self.o
+
+
+def thrift_problem(B, Hq, Hkv, Nq, Nk, d, budget_ppm=50_000, causal=True, num_splits=0, sm_scale=0.0):
+    return problem(B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d, causal=int(causal), sm_scale=sm_scale, mode=BQA_THRIFT,
+                   sel_block=128, hp_budget_ppm=budget_ppm, num_splits=num_splits)
+
+
+class ThriftPath:
+    """ThriftAttention prefill: MXFP4 Q, K (with 128-token block means) and V,
+    block selection, then the mixed-precision attention (FP4 for the
+    unselected pairs, the bf16 inputs for the selected ones)."""
+
+    def __init__(self, p, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+        dev = q.device
+        self.p = p
+        B, Hq, Hkv, Nq, Nk, d = p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d
+        self.q, self.k, self.v = q, k, v
+        u8 = torch.uint8
+        nqb, nkb = -(-Nq // 128), Nk // 128
+        self.qc = torch.empty((B, Hq, Nq, d // 2), dtype=u8, device=dev)
+        self.qs = torch.empty((B, Hq, Nq, d // 32), dtype=u8, device=dev)
+        self.kc = torch.empty((B, Hkv, Nk, d // 2), dtype=u8, device=dev)
+        self.ks = torch.empty((B, Hkv, Nk, d // 32), dtype=u8, device=dev)
+        self.vc = torch.empty((B, Hkv, d, Nk // 2), dtype=u8, device=dev)
+        self.vs = torch.empty((B, Hkv, d, Nk // 32), dtype=u8, device=dev)
+        self.qm = torch.empty((B, Hq, nqb, d), dtype=torch.float32, device=dev)
+        self.km = torch.empty((B, Hkv, nkb, d), dtype=torch.float32, device=dev)
+        self.sel_idx = torch.empty((B, Hq, nqb, max_sel(p)), dtype=torch.int32, device=dev)
+        self.sel_cnt = torch.empty((B, Hq, nqb), dtype=torch.int32, device=dev)
+        self.qq = qtensor(BQA_MXFP4, 0, 32, self.qc, self.qs)
+        self.kq = qtensor(BQA_MXFP4, 0, 32, self.kc, self.ks)
+        self.vq = qtensor(BQA_MXFP4, 1, 32, self.vc, self.vs)
+        self.o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+        self._qd, self._kd, self._vd, self._od = dense(q), dense(k), dense(v), dense(self.o)
+
+    def quantize(self):
+        bqa_quantize_blocks(self.p, BQA_ROLE_Q, self._qd, self.qq, block_means=self.qm)
+        bqa_quantize_blocks(self.p, BQA_ROLE_K, self._kd, self.kq, block_means=self.km)
+        bqa_quantize_blocks(self.p, BQA_ROLE_V, self._vd, self.vq)
+
+    def select(self):
+        bqa_select_blocks(self.p, self.qm, self.km, self.sel_idx, self.sel_cnt)
+
+    def forward(self):
+        bqa_attn_fwd(self.p, q=self.qq, k=self.kq, v=self.vq, q_hi=self._qd, k_hi=self._kd, v_hi=self._vd,
+                     sel_idx=self.sel_idx, sel_cnt=self.sel_cnt, o=self._od, lse=self.lse)
+
+    def step(self):
+        self.quantize()
+        self.select()
         self.forward()
         return self.o
 

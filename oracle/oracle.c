@@ -908,6 +908,7 @@ static void thrift_block(const thrift_ctx* c, row_state* st, int i, int j0, int 
         return;
     }
     float rf = (float)r;
+    if (rf == 0.0f) return;        /* every P of the block underflows fp32: nothing to add */
     float six_over_r = 6.0f / rf;
     double pp[256];
     for (int u = 0; u < n; ++u) pp[u] = (double)((float)p[u] * six_over_r);

@@ -6,7 +6,7 @@ import torch
 
 import oracle as orc
 import workloads as wl
-from tests.helpers import assert_same
+from tests.helpers import assert_same, compare_outputs, tau_for
 
 pytestmark = pytest.mark.gpu
 
@@ -113,3 +113,60 @@ def test_selection_decode():
     assert np.all(cnt == 52)
     assert_same(cnt, rcnt, "selection counts")
     assert_same(idx, ridx, "selected blocks")
+
+
+class _ThriftOracle:
+    """The oracle's own quantisation, block means and selection of the
+    generated inputs (nothing from the GPU)."""
+
+    def __init__(self, Q, K, V, ppm, causal=True):
+        self.Hq, self.Hkv, self.Nq, self.Nk, self.d = Q.shape[1], K.shape[1], Q.shape[2], K.shape[2], Q.shape[3]
+        self.Q, self.K, self.V = (x.reshape(-1, x.shape[2], x.shape[3]) for x in (Q, K, V))
+        self.qc, self.qs = orc.quant_mx_rows(self.Q)
+        self.kc, self.ks = orc.quant_mx_rows(self.K)
+        self.vc, self.vs = orc.quant_mx_cols(self.V)
+        nkb = self.Nk // 128
+        self.ms = max(1, min(nkb, -(-nkb * ppm // 1_000_000)))
+        qm = orc.block_means(self.Q, 128) if self.Nq > 1 else self.Q.copy()
+        km = orc.block_means(self.K, 128)
+        self.sel = [orc.select_blocks(qm[iq], km[iq // (self.Hq // self.Hkv)], causal, ppm, self.ms)
+                    for iq in range(qm.shape[0])]
+        self.causal = causal
+
+    def forward(self, iq, qblocks=None):
+        ik = iq // (self.Hq // self.Hkv)
+        idx, cnt = self.sel[iq]
+        return orc.thrift_fwd(qc=self.qc[iq], qs=self.qs[iq], kc=self.kc[ik], ks=self.ks[ik], vc_t=self.vc[ik],
+                              vs_t=self.vs[ik], Qh=self.Q[iq], Kh=self.K[ik], Vh=self.V[ik], sel_idx=idx, sel_cnt=cnt,
+                              Nq=self.Nq, Nk=self.Nk, d=self.d, blk=128, causal=self.causal, tau=tau_for(self.d),
+                              qblocks=qblocks)
+
+
+def _thrift_run(w, ppm):
+    import bit_quantized_attention_amd as bqa  # noqa: F401
+    from bit_quantized_attention_amd.runner import ThriftPath, thrift_problem, to_device
+    Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
+    p = thrift_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, budget_ppm=ppm)
+    path = ThriftPath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
+    path.step()
+    torch.cuda.synchronize()
+    return p, path, (Q, K, V)
+
+
+@pytest.mark.parametrize("ppm", [PPM_5, 250_000, 1_000_000])
+def test_thrift_prefill_small(ppm):
+    """c5 recipe at N=1024 (8 x 8 causal blocks), GQA 4/2: FP4 blocks first,
+    then the selected bf16 blocks, one online softmax; budgets 5 % (one
+    bf16 block per query block), 25 % and 100 % (every pair in bf16)."""
+    w = wl.with_len(wl.WORKLOADS["c5"], 1024, hq=4, hkv=2)
+    p, path, (Q, K, V) = _thrift_run(w, ppm)
+    oc = _ThriftOracle(Q, K, V, ppm)
+    idx = path.sel_idx.cpu().numpy()
+    for iq in range(4):
+        assert_same(idx[0, iq], oc.sel[iq][0], f"selection of head {iq}")
+    O = path.o.float().cpu().numpy()
+    L = path.lse.cpu().numpy()
+    for iq in range(4):
+        ref, lse = oc.forward(iq)
+        compare_outputs(O[0, iq], ref, "bf16", what=f"O[h={iq}]")
+        assert np.abs(L[0, iq] - lse).max() < 2e-3
