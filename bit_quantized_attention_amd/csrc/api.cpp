@@ -126,6 +126,8 @@ size_t bqa_workspace_size(const bqa_problem* p, int32_t op) {
             return 0;
         case BQA_OP_FWD:
             if (p->mode == BQA_QAT_MXFP4) return ws_qat_fwd_bytes(p->B, p->Hkv, p->Nk, p->d);
+            if (p->mode == BQA_THRIFT && p->Nq == 1 && p->Nk % 128 == 0)
+                return ws_decode_bytes(p->B, p->Hq, p->Hkv, p->Nk, p->num_splits);
             return 0;
         default:
             return 0;
@@ -227,6 +229,35 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
         a.c_log2 = tau_of(p) * 1.4426950408889634f;
         TRY(check_device());
         return launched(launch_qat_fwd(a, st));
+    }
+    if (p->mode == BQA_THRIFT && p->Nq == 1) {
+        if (p->d != 128 || p->sel_block != 128 || p->Nk % 128 != 0) return BQA_E_UNSUPPORTED;
+        if (p->Hq / p->Hkv > 32) return BQA_E_UNSUPPORTED;
+        if (p->num_splits < 0) return BQA_E_SHAPE;
+        TRY(check_q(q, BQA_MXFP4, 0));
+        TRY(check_q(k, BQA_MXFP4, 0));
+        TRY(check_q(v, BQA_MXFP4, 1));
+        if (q->block != 32 || k->block != 32 || v->block != 32) return BQA_E_UNSUPPORTED;
+        TRY(check_dense(q_hi, false, true));
+        TRY(check_dense(k_hi, false, true));
+        TRY(check_dense(v_hi, false, true));
+        TRY(check_dense(o, false, true));
+        if (!sel_idx || !sel_cnt) return BQA_E_NULL;
+        if (p->hp_budget_ppm < 0 || p->hp_budget_ppm > 1000000) return BQA_E_SHAPE;
+        if (!ws || ws_bytes < ws_decode_bytes(p->B, p->Hq, p->Hkv, p->Nk, p->num_splits)) return BQA_E_WORKSPACE;
+        if (!aligned16(ws)) return BQA_E_ALIGN;
+        ThriftDecArgs a{};
+        a.qc = (const uint8_t*)q->codes; a.qs = (const uint8_t*)q->scales;
+        a.kc = (const uint8_t*)k->codes; a.ks = (const uint8_t*)k->scales;
+        a.vc = (const uint8_t*)v->codes; a.vs = (const uint8_t*)v->scales;
+        a.q_hi = as_dense(q_hi); a.k_hi = as_dense(k_hi); a.v_hi = as_dense(v_hi);
+        a.sel_idx = sel_idx; a.sel_cnt = sel_cnt; a.max_sel = max_sel_of(p);
+        a.part = (float*)ws;
+        a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nk = p->Nk;
+        a.splits = decode_splits(p->B, p->Hkv, p->Nk, p->num_splits);
+        a.c_log2 = tau_of(p) * 1.4426950408889634f;
+        TRY(check_device());
+        return launched(launch_thrift_decode(a, as_dense(o), lse, st));
     }
     if (p->mode == BQA_THRIFT && p->Nq > 1) {
         if (p->d != 128 || p->sel_block != 128 || p->Nk % 128 != 0) return BQA_E_UNSUPPORTED;

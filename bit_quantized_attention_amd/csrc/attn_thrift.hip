@@ -375,3 +375,358 @@ hipError_t launch_thrift_fwd(const ThriftFwdArgs& a, hipStream_t st) {
 }
 
 }  // namespace bqa
+
+// ============================================================================
+// ThriftAttention decode ("ThriftAttention" technical summary, Methodology
+// step 2 and the decode results): one query token per (batch, query head)
+// against the whole cache.  One wavefront per (batch, KV head, key-range
+// split): the G = Hq / Hkv query heads of the KV head are the columns of the
+// matrix tiles, so each K/V block is read once for all of them.  Inside a
+// split the key blocks that not every head selected run through the FP4
+// path (heads that selected the block are masked there), then the blocks
+// any head selected run through the bf16 path in quarters of 32 keys (heads
+// that did not select it are masked).  Each split leaves a partial
+// (frame m, l, O) per head; decode_combine merges them exactly (the frames
+// are powers of two).
+namespace bqa {
+namespace {
+
+constexpr int DQ = 32;     // bf16 keys per decode step
+constexpr int PART = D + 4; // partial record: frame m, row sum l, 2 pad, O[d]
+
+struct LdsDec {
+    union {
+        LdsF4 f;
+        struct {
+            uint8_t k[DQ * D * 2];    // 32 keys x 256 B
+            uint8_t vt[D * DQ * 2];   // 128 channels x 64 B (32 keys)
+        } b;
+    };
+};
+
+__device__ __forceinline__ void dec_issue_f4(const ThriftDecArgs& a, int bhk, int J, LdsF4& L, int l) {
+    const int t0 = J * KB;
+#pragma unroll
+    for (int sgm = 0; sgm < 8; ++sgm) {
+        const int r = 16 * sgm + (l >> 2);
+        dma16(a.kc + ((int64_t)bhk * a.Nk + t0 + r) * (D / 2) + 16 * ((l & 3) ^ fk64(r)), L.kc + 1024 * sgm);
+        dma16(a.vc + ((int64_t)bhk * D + r) * (a.Nk / 2) + t0 / 2 + 16 * ((l & 3) ^ fv64(r)), L.vc + 1024 * sgm);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        dma4(a.ks + ((int64_t)bhk * a.Nk + t0 + 64 * u + l) * (D / 32), L.ks + 256 * u);
+        dma4(a.vs + ((int64_t)bhk * D + 64 * u + l) * (a.Nk / 32) + t0 / 32, L.vs + 256 * u);
+    }
+}
+
+struct VQuarter {
+    v4i v[8];
+};
+// 32 keys from k0: K rows by direct copies; V (keys 4 kq + u and 16 + 4 kq + u,
+// channels 8 cg ..) into registers for the transposed store.
+__device__ __forceinline__ void dec_issue_bf(const ThriftDecArgs& a, int b, int hk, int k0, LdsDec& L, int l,
+                                             VQuarter& vq) {
+    const uint16_t* kb = (const uint16_t*)a.k_hi.p + b * a.k_hi.sB + hk * a.k_hi.sH;
+#pragma unroll
+    for (int sgm = 0; sgm < 8; ++sgm) {
+        const int r = 4 * sgm + (l >> 4);
+        dma16(kb + (int64_t)(k0 + r) * a.k_hi.sN + 8 * ((l & 15) ^ fk256(r)), L.b.k + 1024 * sgm);
+    }
+    const uint16_t* vb = (const uint16_t*)a.v_hi.p + b * a.v_hi.sB + hk * a.v_hi.sH;
+    const int cg = l & 15, kq = l >> 4;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int key = 16 * (u >> 2) + 4 * kq + (u & 3);
+        vq.v[u] = *(const v4i*)(vb + (int64_t)(k0 + key) * a.v_hi.sN + 8 * cg);
+    }
+}
+__device__ __forceinline__ void dec_store_bf(const VQuarter& vq, LdsDec& L, int l) {
+    const int cg = l & 15, kq = l >> 4;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const int kw = 4 * hf + kq;    // 4-key group: keys 4 kw .. 4 kw + 3
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t lo = __builtin_amdgcn_perm((uint32_t)vq.v[4 * hf + 1][e >> 1], (uint32_t)vq.v[4 * hf][e >> 1], sel);
+            const uint32_t hi = __builtin_amdgcn_perm((uint32_t)vq.v[4 * hf + 3][e >> 1], (uint32_t)vq.v[4 * hf + 2][e >> 1], sel);
+            const int r = 8 * cg + e;
+            *(v2i*)(L.b.vt + r * 64 + 16 * ((kw >> 1) ^ fv64(r)) + 8 * (kw & 1)) = v2i{(int)lo, (int)hi};
+        }
+    }
+}
+
+__global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
+    __shared__ __attribute__((aligned(16))) LdsDec lds[2];
+    extern __shared__ uint32_t hmask[];                 // per key block of the split: heads that selected it
+    const int l = threadIdx.x, h = l >> 5, lq = l & 31;
+    const int S = a.splits;
+    const int sp = blockIdx.x % S;
+    const int bhk = blockIdx.x / S, b = bhk / a.Hkv, hk = bhk % a.Hkv;
+    const int G = a.Hq / a.Hkv;
+    const int nb = a.Nk / KB;
+    const int b0 = (int)((int64_t)sp * nb / S), b1 = (int)((int64_t)(sp + 1) * nb / S);
+    const bool col_ok = lq < G;
+    const int hq = hk * G + (col_ok ? lq : 0);
+    const int bhq = b * a.Hq + hq;
+    const int krow = sigma(lq);
+    const float c = a.c_log2;
+    const uint32_t all = G >= 32 ? 0xFFFFFFFFu : ((1u << G) - 1u);
+
+    for (int j = l; j < b1 - b0; j += 64) hmask[j] = 0u;
+    __syncthreads();
+    for (int g = 0; g < G; ++g) {
+        const int32_t* sel = a.sel_idx + (int64_t)(b * a.Hq + hk * G + g) * a.max_sel;
+        const int cnt = a.sel_cnt[b * a.Hq + hk * G + g];
+        for (int u = l; u < cnt; u += 64) {
+            const int J = sel[u];
+            if (J >= b0 && J < b1) atomicOr(&hmask[J - b0], 1u << g);
+        }
+    }
+    __syncthreads();
+
+    v4i qb[2];
+    int qsb[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        qb[kk] = col_ok ? *(const v4i*)(a.qc + (int64_t)bhq * (D / 2) + 32 * kk + 16 * h) : v4i{};
+        qsb[kk] = col_ok ? (int)a.qs[(int64_t)bhq * (D / 32) + 2 * kk + h] : 0;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+    v16f oacc[D / 32];
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = v16f{};
+    float m_ref = -__builtin_inff(), l_run = 0.0f, gsc = 1.0f;
+    const uint32_t mybit = col_ok ? (1u << lq) : 0u;
+
+    // ------------------------------------------------------------ FP4 blocks
+    auto next_f4 = [&](int J) {
+        while (J < b1 && hmask[J - b0] == all) ++J;
+        return J;
+    };
+    int J = next_f4(b0), buf = 0;
+    if (J < b1) {
+        dec_issue_f4(a, bhk, J, lds[0].f, l);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    while (J < b1) {
+        const int Jn = next_f4(J + 1);
+        if (Jn < b1) dec_issue_f4(a, bhk, Jn, lds[buf ^ 1].f, l);
+        const LdsF4& L = lds[buf].f;
+        const bool skip = !col_ok || (hmask[J - b0] & mybit);
+        v16f s[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            s[t] = v16f{};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int r = 32 * t + krow;
+                const v4i av = *(const v4i*)(L.kc + r * 64 + 16 * ((2 * kk + h) ^ fk64(r)));
+                s[t] = mfma_f4_32x32x64(av, (int)L.ks[4 * r + 2 * kk + h], qb[kk], qsb[kk], s[t]);
+            }
+            if (skip) s[t] = v16f{} - __builtin_inff();
+        }
+        float bt[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float m = __builtin_fmaxf(s[t][0], s[t][1]);
+#pragma unroll
+            for (int i = 2; i < 16; i += 2) m = __builtin_fmaxf(__builtin_fmaxf(m, s[t][i]), s[t][i + 1]);
+            bt[t] = __builtin_fmaxf(m, partner32f(m));
+        }
+        const float smax = __builtin_fmaxf(__builtin_fmaxf(bt[0], bt[1]), __builtin_fmaxf(bt[2], bt[3]));
+        const float mx = smax * c;
+        if (__any(mx > m_ref + 64.0f)) {
+            if (mx > m_ref) move_frame(oacc, l_run, m_ref, __builtin_ceilf(mx));
+        }
+        const float mu = m_ref == -__builtin_inff() ? 0.0f : m_ref;
+        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c, -mu));
+                ps[t] += s[t][i];
+            }
+        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        const float r = __builtin_amdgcn_exp2f(__builtin_fmaf(smax, c, -mu));
+        const float six_r = r > 0.0f ? 6.0f / r : 0.0f;
+        int e[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) e[t] = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(bt[t], c, -mu)) * six_r);
+        uint32_t pw[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float sc = __builtin_bit_cast(float, (uint32_t)(e[t] + 127) << 23);
+#pragma unroll
+            for (int wd = 0; wd < 2; ++wd) {
+                uint32_t x = 0;
+                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 0] * six_r, s[t][8 * wd + 1] * six_r, sc, 0);
+                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 2] * six_r, s[t][8 * wd + 3] * six_r, sc, 1);
+                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 4] * six_r, s[t][8 * wd + 5] * six_r, sc, 2);
+                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 6] * six_r, s[t][8 * wd + 7] * six_r, sc, 3);
+                pw[t][wd] = x;
+            }
+        }
+        if (r > 0.0f) {
+            const float ratio = gsc * six_r;
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[cb][i] *= ratio;
+            gsc = r * (1.0f / 6.0f);
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const v2i r0 = __builtin_amdgcn_permlane32_swap((int)pw[2 * g][0], (int)pw[2 * g + 1][0], false, false);
+            const v2i r1 = __builtin_amdgcn_permlane32_swap((int)pw[2 * g][1], (int)pw[2 * g + 1][1], false, false);
+            const v4i pb = {r0[0], r1[0], r0[1], r1[1]};
+            const int psc = (h ? e[2 * g + 1] : e[2 * g]) + 127;
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb) {
+                const int rr = 32 * cb + lq;
+                const v4i av = *(const v4i*)(L.vc + rr * 64 + 16 * ((2 * g + h) ^ fv64(rr)));
+                oacc[cb] = mfma_f4_32x32x64(av, (int)L.vs[4 * rr + 2 * g + h], pb, psc, oacc[cb]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        J = Jn;
+        buf ^= 1;
+    }
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[cb][i] *= gsc;
+
+    // ------------------------------------------------------------ bf16 blocks, 32 keys at a time
+    auto next_bf = [&](int it) {        // item = 4 J + quarter
+        while ((it >> 2) < b1 - b0 && hmask[it >> 2] == 0u) it = (it | 3) + 1;
+        return it;
+    };
+    const int n_it = 4 * (b1 - b0);
+    int it = next_bf(0);
+    buf = 0;
+    if (it < n_it) {
+        VQuarter vq;
+        dec_issue_bf(a, b, hk, (b0 + (it >> 2)) * KB + DQ * (it & 3), lds[0], l, vq);
+        dec_store_bf(vq, lds[0], l);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    const uint16_t* qh = (const uint16_t*)a.q_hi.p + b * a.q_hi.sB + hq * a.q_hi.sH;
+    v8bf qv[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) qv[st] = *(const v8bf*)(qh + 16 * st + 8 * h);
+    while (it < n_it) {
+        const int itn = next_bf(it + 1);
+        VQuarter vq;
+        if (itn < n_it) dec_issue_bf(a, b, hk, (b0 + (itn >> 2)) * KB + DQ * (itn & 3), lds[buf ^ 1], l, vq);
+        const LdsDec& L = lds[buf];
+        const bool skip = !col_ok || !(hmask[it >> 2] & mybit);
+        v16f s0 = v16f{};
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const v8bf av = *(const v8bf*)(L.b.k + krow * 256 + 16 * ((2 * st + h) ^ fk256(krow)));
+            s0 = mfma_bf16_32x32x16(av, qv[st], s0);
+        }
+        if (skip) s0 = v16f{} - __builtin_inff();
+        float m = s0[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m = __builtin_fmaxf(m, s0[i]);
+        const float mx = __builtin_fmaxf(m, partner32f(m)) * c;
+        if (__any(mx > m_ref + 64.0f)) {
+            if (mx > m_ref) move_frame(oacc, l_run, m_ref, __builtin_ceilf(mx));
+        }
+        const float mu = m_ref == -__builtin_inff() ? 0.0f : m_ref;
+        float ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -mu));
+            ps += s0[i];
+        }
+        l_run += ps;
+        // keys 16 h + 8 st + e of the quarter
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            v8bf pbf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pbf[e] = (__bf16)s0[8 * st + e];
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb) {
+                const int rr = 32 * cb + lq;
+                const v8bf av = *(const v8bf*)(L.b.vt + rr * 64 + 16 * ((2 * h + st) ^ fv64(rr)));
+                oacc[cb] = mfma_bf16_32x32x16(av, pbf, oacc[cb]);
+            }
+        }
+        if (itn < n_it) dec_store_bf(vq, lds[buf ^ 1], l);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        it = itn;
+        buf ^= 1;
+    }
+
+    // partial of this split: frame m (log2 units), row sum, unnormalised O
+    const float l_tot = l_run + partner32f(l_run);
+    if (!col_ok) return;
+    float* part = a.part + ((int64_t)bhq * S + sp) * PART;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int ch0 = 32 * cb + 8 * g + 4 * h;
+            *(v4f*)(part + 4 + ch0) = v4f{oacc[cb][4 * g], oacc[cb][4 * g + 1], oacc[cb][4 * g + 2], oacc[cb][4 * g + 3]};
+        }
+    if (h == 0) {
+        part[0] = m_ref;
+        part[1] = l_tot;
+    }
+}
+
+// Merge the splits of one (batch, query head): m = max m_s,
+// l = sum 2^(m_s - m) l_s, O = sum 2^(m_s - m) O_s / l (powers of two: exact).
+__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ part, int S, Dense o,
+                                                             float* lse, int Hq) {
+    const int bhq = blockIdx.x, ch = threadIdx.x;
+    const float* p = part + (int64_t)bhq * S * PART;
+    float m = -__builtin_inff();
+    for (int s = 0; s < S; ++s) m = __builtin_fmaxf(m, p[(int64_t)s * PART]);
+    float lsum = 0.0f, acc = 0.0f;
+    for (int s = 0; s < S; ++s) {
+        const float ms = p[(int64_t)s * PART];
+        if (ms == -__builtin_inff()) continue;
+        const float wgt = __builtin_ldexpf(1.0f, (int)(ms - m));
+        lsum += wgt * p[(int64_t)s * PART + 1];
+        acc += wgt * p[(int64_t)s * PART + 4 + ch];
+    }
+    const int b = bhq / Hq, hq = bhq % Hq;
+    uint16_t* orow = (uint16_t*)o.p + b * o.sB + hq * o.sH;
+    orow[ch] = f32_to_bf16_bits(acc / lsum);
+    if (lse && ch == 0) lse[bhq] = m * 0.6931471805599453f + __logf(lsum);
+}
+
+}  // namespace
+
+int decode_splits(int B, int Hkv, int Nk, int requested) {
+    const int nb = Nk / KB;
+    int S = requested > 0 ? requested : (2048 + B * Hkv - 1) / (B * Hkv);
+    if (S > nb) S = nb;
+    if (S < 1) S = 1;
+    return S;
+}
+
+size_t ws_decode_bytes(int B, int Hq, int Hkv, int Nk, int requested) {
+    return (size_t)B * Hq * decode_splits(B, Hkv, Nk, requested) * PART * sizeof(float);
+}
+
+hipError_t launch_thrift_decode(const ThriftDecArgs& a, Dense o, float* lse, hipStream_t st) {
+    const int nb = a.Nk / KB;
+    const int max_blocks = (nb + a.splits - 1) / a.splits;
+    thrift_decode_kernel<<<a.B * a.Hkv * a.splits, 64, max_blocks * sizeof(uint32_t), st>>>(a);
+    decode_combine_kernel<<<a.B * a.Hq, D, 0, st>>>(a.part, a.splits, o, lse, a.Hq);
+    return hipGetLastError();
+}
+
+}  // namespace bqa

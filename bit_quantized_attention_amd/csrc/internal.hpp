@@ -68,6 +68,22 @@ struct ThriftFwdArgs {
 };
 hipError_t launch_thrift_fwd(const ThriftFwdArgs& a, hipStream_t st);
 
+// ---- ThriftAttention decode (attn_thrift.hip): one query per (batch, query head)
+struct ThriftDecArgs {
+    const uint8_t* qc; const uint8_t* qs;                // MXFP4 q [B,Hq,1,d/2], E8M0 [B,Hq,1,d/32]
+    const uint8_t* kc; const uint8_t* ks;                // MXFP4 K cache [B,Hkv,Nk,d/2], E8M0
+    const uint8_t* vc; const uint8_t* vs;                // MXFP4 V cache [B,Hkv,d,Nk/2], E8M0
+    Dense q_hi, k_hi, v_hi;                              // bf16 q [B,Hq,1,d]; caches [B,Hkv,Nk,d]
+    const int32_t* sel_idx; const int32_t* sel_cnt;      // [B,Hq,1,max_sel], [B,Hq,1]
+    int max_sel;
+    float* part;                                         // workspace: [B,Hq,splits,d+4] partials
+    int B, Hq, Hkv, Nk, splits;
+    float c_log2;
+};
+int decode_splits(int B, int Hkv, int Nk, int requested);
+size_t ws_decode_bytes(int B, int Hq, int Hkv, int Nk, int requested);
+hipError_t launch_thrift_decode(const ThriftDecArgs& a, Dense o, float* lse, hipStream_t st);
+
 // ---- ThriftAttention block selection (select.hip)
 int select_sort_len(int nkb);
 hipError_t launch_select(const float* qbar, const float* kbar, int B, int Hq, int Hkv, int nqb, int nkb, int d,

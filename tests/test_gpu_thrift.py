@@ -170,3 +170,62 @@ def test_thrift_prefill_small(ppm):
         ref, lse = oc.forward(iq)
         compare_outputs(O[0, iq], ref, "bf16", what=f"O[h={iq}]")
         assert np.abs(L[0, iq] - lse).max() < 2e-3
+
+
+def _decode_run(w, ppm, splits):
+    import bit_quantized_attention_amd as bqa
+    from bit_quantized_attention_amd.runner import to_device
+    q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
+    B, Hq, Hkv, Nk, d = w.B, w.Hq, w.Hkv, w.Nk, w.d
+    p = bqa.problem(B=B, Hq=Hq, Hkv=Hkv, Nq=1, Nk=Nk, d=d, causal=1, mode=bqa.BQA_THRIFT, sel_block=128,
+                    hp_budget_ppm=ppm, num_splits=splits)
+    u8, dev = torch.uint8, "cuda"
+    qt, kt, vt = to_device(q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
+    qc = torch.empty((B, Hq, 1, d // 2), dtype=u8, device=dev); qs = torch.empty((B, Hq, 1, d // 32), dtype=u8, device=dev)
+    kc = torch.empty((B, Hkv, Nk, d // 2), dtype=u8, device=dev); ks = torch.empty((B, Hkv, Nk, d // 32), dtype=u8, device=dev)
+    vc = torch.empty((B, Hkv, d, Nk // 2), dtype=u8, device=dev); vs = torch.empty((B, Hkv, d, Nk // 32), dtype=u8, device=dev)
+    qm = torch.empty((B, Hq, 1, d), dtype=torch.float32, device=dev)
+    km = torch.empty((B, Hkv, Nk // 128, d), dtype=torch.float32, device=dev)
+    qq, kq, vq = (bqa.qtensor(bqa.BQA_MXFP4, ax, 32, c, s) for ax, c, s in ((0, qc, qs), (0, kc, ks), (1, vc, vs)))
+    bqa.bqa_quantize_blocks(p, bqa.BQA_ROLE_Q, qt, qq, block_means=qm)
+    bqa.bqa_quantize_blocks(p, bqa.BQA_ROLE_K, kt, kq, block_means=km)
+    bqa.bqa_quantize_blocks(p, bqa.BQA_ROLE_V, vt, vq)
+    ms = bqa.max_sel(p)
+    idx = torch.empty((B, Hq, 1, ms), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Hq, 1), dtype=torch.int32, device=dev)
+    bqa.bqa_select_blocks(p, qm, km, idx, cnt)
+    o = torch.empty((B, Hq, 1, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=dev)
+    ws = torch.empty(bqa.bqa_workspace_size(p, bqa.BQA_OP_FWD), dtype=torch.uint8, device=dev)
+    bqa.bqa_attn_fwd(p, q=qq, k=kq, v=vq, q_hi=qt, k_hi=kt, v_hi=vt, sel_idx=idx, sel_cnt=cnt, o=o, lse=lse,
+                     workspace=ws)
+    torch.cuda.synchronize()
+    return p, (q, K, V), idx.cpu().numpy(), o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("ppm,splits", [(PPM_5, 1), (PPM_5, 3), (250_000, 0), (1_000_000, 2)])
+def test_thrift_decode_small(ppm, splits):
+    """Decode recipe (batch 2, GQA 8/2) against a 4096-token cache: per split
+    the FP4 blocks, then each head's selected blocks in bf16; partials merged."""
+    w = wl.with_len(wl.WORKLOADS["c5d"], 4096, b=2, hq=8, hkv=2)
+    p, (q, K, V), idx, O, L = _decode_run(w, ppm, splits)
+    import bit_quantized_attention_amd as bqa
+    ms = bqa.max_sel(p)
+    B, Hq, Hkv, d = w.B, w.Hq, w.Hkv, w.d
+    qf, Kf, Vf = q.reshape(B * Hq, d), K.reshape(B * Hkv, -1, d), V.reshape(B * Hkv, -1, d)
+    qc, qs = orc.quant_mx_rows(qf[:, None])
+    kc, ks = orc.quant_mx_rows(Kf)
+    vc, vs = orc.quant_mx_cols(Vf)
+    km = orc.block_means(Kf, 128)
+    nb = w.Nk // 128
+    S = splits if splits > 0 else min(nb, -(-2048 // (B * Hkv)))
+    for bq in range(B * Hq):
+        b, hq = divmod(bq, Hq)
+        ik = b * Hkv + hq // (Hq // Hkv)
+        ridx, rcnt = orc.select_blocks(qf[bq][None], km[ik], True, ppm, ms)
+        assert_same(idx[b, hq, 0], ridx[0], f"decode selection (b={b}, h={hq})")
+        ref, lse = orc.thrift_decode(qc=qc[bq], qs=qs[bq], kc=kc[ik], ks=ks[ik], vc_t=vc[ik], vs_t=vs[ik], q=qf[bq],
+                                     Kh=Kf[ik], Vh=Vf[ik], sel=ridx[0, :rcnt[0]], Nk=w.Nk, d=d, blk=128,
+                                     tau=tau_for(d), num_splits=S)
+        compare_outputs(O[b, hq, 0], ref, "bf16", what=f"decode o (b={b}, h={hq})")
+        assert abs(L[b, hq, 0] - lse) < 2e-3
