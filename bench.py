@@ -8,6 +8,11 @@ Workloads (``--workload``, default c2):
   c4  Attn-QAT FP4 forward at B=1, H=32, N=16384, d=128, non-causal,
       Student-t inputs: MXFP4 Q, K, V, fused attention with MXFP4 P.V and
       the bf16 auxiliary output O'.
+  c5  ThriftAttention prefill at B=1, Hq=32, Hkv=8, N=131072, d=128,
+      causal, low-rank inputs: MXFP4 Q, K, V with block means, block
+      selection (5 %), mixed FP4 / bf16 attention.
+  c5d ThriftAttention decode, B=16, one query against a 131072-token
+      cache: query quantisation, selection, split-K attention and merge.
 
 One step = one pass of the whole path over the batch (quantisers and
 attention).  Inputs are generated on the host and are resident in HBM
@@ -20,7 +25,7 @@ time, measured with HIP events on the stream it runs on, against the dense
 matrix-core peak of its operand types.  `cpu_baseline` times the CPU oracle
 on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--workload c2|c4] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--workload c2|c4|c5|c5d] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -162,7 +167,152 @@ def _qat_case(w, bqa, torch):
         traffic_key="qat_fwd_kernel<aux>", cpu=cpu_baseline_qat)
 
 
-CASES = {"c2": _sage_case, "c4": _qat_case}
+def _thrift_pairs(path, w):
+    """(fp4 pairs, bf16 pairs) of (query, key) scores the prefill computes,
+    from the selection the step made (diagonal blocks count their causal half)."""
+    import numpy as np
+    idx = path.sel_idx.cpu().numpy()
+    cnt = path.sel_cnt.cpu().numpy()
+    full, diag = 128 * 128, 128 * 129 // 2
+    bf16 = 0
+    for i in range(idx.shape[2]):
+        sel = idx[:, :, i, :]
+        n = cnt[:, :, i]
+        on_diag = ((sel == i) & (np.arange(sel.shape[-1])[None, None, :] < n[..., None])).sum()
+        bf16 += int(n.sum() - on_diag) * full + int(on_diag) * diag
+    total = w.B * w.Hq * w.Nq * (w.Nq + 1) // 2
+    return total - bf16, bf16
+
+
+def cpu_baseline_thrift(w, budget_s: float = 20.0):
+    """The oracle on a bounded sample of the Thrift prefill: MXFP4
+    quantisation, block means and selection of head (0,0), then the mixed
+    forward of its last query blocks (the longest rows) until the budget."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+    from tests.helpers import tau_for
+    oracle.lib()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    Q, K, V = (wl.chunk(w, t, 0, 0) for t in ("q", "k", "v"))
+    qc, qs = oracle.quant_mx_rows(Q[None]); kc, ks = oracle.quant_mx_rows(K[None]); vc, vs = oracle.quant_mx_cols(V[None])
+    nkb = w.Nk // 128
+    ms = max(1, min(nkb, -(-nkb * 50_000 // 1_000_000)))
+    idx, cnt = oracle.select_blocks(oracle.block_means(Q[None], 128)[0], oracle.block_means(K[None], 128)[0], True,
+                                    50_000, ms)
+    pairs, qb = 0, nkb
+    while qb > 0 and time.perf_counter() - t0 < budget_s:
+        qb -= 1
+        oracle.thrift_fwd(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0], Qh=Q, Kh=K, Vh=V,
+                          sel_idx=idx, sel_cnt=cnt, Nq=w.Nq, Nk=w.Nk, d=w.d, blk=128, causal=True, tau=tau_for(w.d),
+                          qblocks=(qb, qb + 1))
+        pairs += sum(128 * qb + a + 1 for a in range(128))
+    dt = time.perf_counter() - t0
+    _ = np
+    return {"value": 4.0 * pairs * w.d / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"head (0,0): MXFP4 quantisation, block means and selection, then the mixed forward of its "
+                      f"last {nkb - qb} of {nkb} query blocks (N={w.Nk}), {dt:.1f} s"}
+
+
+def _thrift_case(w, bqa, torch):
+    from bit_quantized_attention_amd.runner import ThriftPath, thrift_problem, to_device
+    import workloads as wl
+    nw = wl.default_workers()
+    Q, K, V = (wl.build(w, t, workers=nw) for t in ("q", "k", "v"))
+    p = thrift_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, budget_ppm=50_000)
+    path = ThriftPath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
+    del Q, K, V
+    path.step()
+    torch.cuda.synchronize()
+    f4, b16 = _thrift_pairs(path, w)
+    ops_f4, ops_b16 = 4.0 * w.d * f4, 4.0 * w.d * b16
+    t_peak = ops_f4 / (PEAK_F4_TFLOPS * 1e12) + ops_b16 / (PEAK_BF16_TFLOPS * 1e12)
+    ops = 4.0 * w.B * w.Hq * w.Nq * w.Nk * w.d / 2
+    return dict(
+        path=path, ops=ops, dtype="mxfp4+bf16",
+        workload="ThriftAttention prefill (c5): B=1 Hq=32 Hkv=8 N=131072 d=128 causal, low-rank bf16 in, 5 % of "
+                 "128x128 block pairs in bf16, the rest MXFP4; step = quantise Q,K,V + block means + selection + "
+                 "attention",
+        roofline={"bound": "mfma", "kernel": "thrift_fwd_kernel: MXFP4 QK^T/P.V on unselected pairs, bf16 on "
+                                             "selected pairs",
+                  "peak": round((ops_f4 + ops_b16) / t_peak / 1e12, 1),
+                  "peak_note": f"fp4 and bf16 dense peaks weighted by the pairs each path computed "
+                               f"({100.0 * b16 / (f4 + b16):.2f} % bf16)",
+                  "ops_per_launch": ops_f4 + ops_b16},
+        traffic_key="thrift_fwd_kernel", cpu=cpu_baseline_thrift)
+
+
+def cpu_baseline_decode(w, budget_s: float = 20.0):
+    """The oracle on a bounded sample of decode: per (b, KV head) the MXFP4
+    cache and key means, then each query head's selection and decode, until
+    the budget."""
+    import oracle
+    import workloads as wl
+    from tests.helpers import tau_for
+    oracle.lib()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    G = w.Hq // w.Hkv
+    nkb = w.Nk // 128
+    ms = max(1, min(nkb, -(-nkb * 50_000 // 1_000_000)))
+    heads = 0
+    for bk in range(w.B * w.Hkv):
+        b, hk = divmod(bk, w.Hkv)
+        K, V = wl.chunk(w, "k", b, hk), wl.chunk(w, "v", b, hk)
+        kc, ks = oracle.quant_mx_rows(K[None]); vc, vs = oracle.quant_mx_cols(V[None])
+        km = oracle.block_means(K[None], 128)[0]
+        for g in range(G):
+            q = wl.chunk(w, "q", b, hk * G + g)
+            qc, qs = oracle.quant_mx_rows(q[None])
+            idx, cnt = oracle.select_blocks(q, km, True, 50_000, ms)
+            oracle.thrift_decode(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0], q=q[0], Kh=K, Vh=V,
+                                 sel=idx[0, :cnt[0]], Nk=w.Nk, d=w.d, blk=128, tau=tau_for(w.d), num_splits=1)
+            heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": 4.0 * heads * w.Nk * w.d / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.Hq} (b, query head) decodes with their KV head's MXFP4 cache, key means "
+                      f"and selection, Nk={w.Nk}, {dt:.1f} s"}
+
+
+def _decode_case(w, bqa, torch):
+    from bit_quantized_attention_amd.runner import ThriftDecodePath, thrift_problem, to_device
+    import numpy as np
+    import workloads as wl
+    nw = wl.default_workers()
+    q, K, V = wl.build(w, "q"), wl.build(w, "k", workers=nw), wl.build(w, "v", workers=nw)
+    p = thrift_problem(w.B, w.Hq, w.Hkv, 1, w.Nk, w.d, budget_ppm=50_000)
+    path = ThriftDecodePath(p, to_device(q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
+    del K, V
+    path.build_cache()
+    path.step()
+    torch.cuda.synchronize()
+    # algorithmic bytes of one attention call: the whole MXFP4 cache, the bf16
+    # blocks that some head of the KV head selected, the queries and the output
+    idx = path.sel_idx.cpu().numpy().reshape(w.B, w.Hkv, -1)
+    union = sum(len(set(int(j) for j in idx[b, hk] if j >= 0)) for b in range(w.B) for hk in range(w.Hkv))
+    fp4 = w.B * w.Hkv * w.Nk * 2 * (w.d // 2 + w.d // 32)
+    b16 = union * 128 * w.d * 2 * 2
+    qo = w.B * w.Hq * w.d * (2 + 0.5 + 2) + w.B * w.Hq * 4 * (idx.shape[-1] // (w.Hq // w.Hkv) + 1)
+    nbytes = fp4 + b16 + qo
+    ops = 4.0 * w.B * w.Hq * w.Nk * w.d
+    _ = np
+    return dict(
+        path=path, ops=ops, dtype="mxfp4+bf16",
+        workload="ThriftAttention decode (c5d): B=16 Hq=32 Hkv=8, one query against a 131072-token cache, d=128, "
+                 "top 52 of 1024 blocks per head in bf16, the rest MXFP4; step = quantise q + block mean + "
+                 "selection + attention (the double cache is built once, outside the step)",
+        roofline={"bound": "hbm", "kernel": "thrift_decode_kernel + decode_combine_kernel", "peak": 8000.0,
+                  "unit": "GB/s", "bytes_per_launch": nbytes,
+                  "bytes_note": f"MXFP4 K/V cache {fp4 / 1e9:.3f} GB + bf16 blocks selected by some head of the KV "
+                                f"head ({union} blocks, {b16 / 1e9:.3f} GB) + queries, selections and outputs"},
+        traffic_key="thrift_decode_kernel", cpu=cpu_baseline_decode)
+
+
+CASES = {"c2": _sage_case, "c4": _qat_case, "c5": _thrift_case, "c5d": _decode_case}
 
 
 def main():
@@ -221,8 +371,12 @@ def main():
     ms_per_step = dt * 1e3 / args.steps
     value = ops / (ms_per_step * 1e-3) / 1e12
     rl = dict(case["roofline"])
-    achieved = rl["ops_per_launch"] / (kern_ms * 1e-3) / 1e12
-    rl.update({"achieved": round(achieved, 1), "unit": "TFLOP/s", "frac": round(achieved / rl["peak"], 4),
+    if rl["bound"] == "hbm":
+        achieved = rl["bytes_per_launch"] / (kern_ms * 1e-3) / 1e9
+    else:
+        achieved = rl["ops_per_launch"] / (kern_ms * 1e-3) / 1e12
+        rl["unit"] = "TFLOP/s"
+    rl.update({"achieved": round(achieved, 1), "frac": round(achieved / rl["peak"], 4),
                "traffic": _traffic_for(case["traffic_key"]), "kernel_ms": round(kern_ms, 5)})
     line = {
         "metric": METRIC,

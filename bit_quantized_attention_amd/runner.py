@@ -166,6 +166,53 @@ class ThriftPath:
         return self.o
 
 
+class ThriftDecodePath:
+    """ThriftAttention decode: the double KV cache (MXFP4 codes with 128-token
+    key means, next to the bf16 cache) is built once by `build_cache`; a
+    step quantises the new query, selects each head's blocks and attends."""
+
+    def __init__(self, p, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+        dev = q.device
+        self.p = p
+        B, Hq, Hkv, Nk, d = p.B, p.Hq, p.Hkv, p.Nk, p.d
+        self.q, self.k, self.v = q, k, v
+        u8 = torch.uint8
+        self.qc = torch.empty((B, Hq, 1, d // 2), dtype=u8, device=dev)
+        self.qs = torch.empty((B, Hq, 1, d // 32), dtype=u8, device=dev)
+        self.kc = torch.empty((B, Hkv, Nk, d // 2), dtype=u8, device=dev)
+        self.ks = torch.empty((B, Hkv, Nk, d // 32), dtype=u8, device=dev)
+        self.vc = torch.empty((B, Hkv, d, Nk // 2), dtype=u8, device=dev)
+        self.vs = torch.empty((B, Hkv, d, Nk // 32), dtype=u8, device=dev)
+        self.qm = torch.empty((B, Hq, 1, d), dtype=torch.float32, device=dev)
+        self.km = torch.empty((B, Hkv, Nk // 128, d), dtype=torch.float32, device=dev)
+        self.sel_idx = torch.empty((B, Hq, 1, max_sel(p)), dtype=torch.int32, device=dev)
+        self.sel_cnt = torch.empty((B, Hq, 1), dtype=torch.int32, device=dev)
+        self.qq = qtensor(BQA_MXFP4, 0, 32, self.qc, self.qs)
+        self.kq = qtensor(BQA_MXFP4, 0, 32, self.kc, self.ks)
+        self.vq = qtensor(BQA_MXFP4, 1, 32, self.vc, self.vs)
+        self.o = torch.empty((B, Hq, 1, d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(max(bqa_workspace_size(p, BQA_OP_FWD), 16), dtype=u8, device=dev)
+        self._qd, self._kd, self._vd, self._od = dense(q), dense(k), dense(v), dense(self.o)
+
+    def build_cache(self):
+        bqa_quantize_blocks(self.p, BQA_ROLE_K, self._kd, self.kq, block_means=self.km)
+        bqa_quantize_blocks(self.p, BQA_ROLE_V, self._vd, self.vq)
+
+    def quantize(self):
+        bqa_quantize_blocks(self.p, BQA_ROLE_Q, self._qd, self.qq, block_means=self.qm)
+        bqa_select_blocks(self.p, self.qm, self.km, self.sel_idx, self.sel_cnt)
+
+    def forward(self):
+        bqa_attn_fwd(self.p, q=self.qq, k=self.kq, v=self.vq, q_hi=self._qd, k_hi=self._kd, v_hi=self._vd,
+                     sel_idx=self.sel_idx, sel_cnt=self.sel_cnt, o=self._od, lse=self.lse, workspace=self.ws)
+
+    def step(self):
+        self.quantize()
+        self.forward()
+        return self.o
+
+
 def attention_ops(p) -> float:
     """Effective operation count of one forward: 4 B Hq Nq Nk d, halved when causal."""
     ops = 4.0 * p.B * p.Hq * p.Nq * p.Nk * p.d

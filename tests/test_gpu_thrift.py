@@ -229,3 +229,68 @@ def test_thrift_decode_small(ppm, splits):
                                      tau=tau_for(d), num_splits=S)
         compare_outputs(O[b, hq, 0], ref, "bf16", what=f"decode o (b={b}, h={hq})")
         assert abs(L[b, hq, 0] - lse) < 2e-3
+
+
+@pytest.mark.slow
+def test_thrift_prefill_full_size_sampled():
+    """Full c5 prefill shape (B=1, Hq=32, Hkv=8, N=131072, 5 %): the GPU runs
+    the whole problem; the oracle checks sampled query blocks of two heads
+    (first, middle and last block, the last against all 1024 key blocks)."""
+    from bit_quantized_attention_amd.runner import ThriftPath, thrift_problem, to_device
+    w = wl.WORKLOADS["c5"]
+    nw = wl.default_workers()
+    Q, K, V = (wl.build(w, t, workers=nw) for t in ("q", "k", "v"))
+    p = thrift_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, budget_ppm=PPM_5)
+    path = ThriftPath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
+    path.step()
+    torch.cuda.synchronize()
+    O = path.o[0].float().cpu().numpy()
+    L = path.lse[0].cpu().numpy()
+    cnt = path.sel_cnt[0].cpu().numpy()
+    assert int(cnt[0].sum()) == 26728
+    for h in (0, 29):
+        hk = h // 4
+        Qh, Kh, Vh = Q[0, h], K[0, hk], V[0, hk]
+        qc, qs = orc.quant_mx_rows(Qh[None]); kc, ks = orc.quant_mx_rows(Kh[None]); vc, vs = orc.quant_mx_cols(Vh[None])
+        idx, rc = orc.select_blocks(orc.block_means(Qh[None], 128)[0], orc.block_means(Kh[None], 128)[0], True, PPM_5, 52)
+        assert_same(path.sel_idx[0, h].cpu().numpy(), idx, f"selection of head {h}")
+        for qb in (0, 517, 1023):
+            ref, lse = orc.thrift_fwd(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0], Qh=Qh, Kh=Kh, Vh=Vh,
+                                      sel_idx=idx, sel_cnt=rc, Nq=w.Nq, Nk=w.Nk, d=w.d, blk=128, causal=True,
+                                      tau=tau_for(w.d), qblocks=(qb, qb + 1))
+            compare_outputs(O[h, 128 * qb:128 * qb + 128], ref, "bf16", what=f"O[h={h}, query block {qb}]")
+            assert np.abs(L[h, 128 * qb:128 * qb + 128] - lse).max() < 2e-3
+
+
+@pytest.mark.slow
+def test_thrift_decode_full_size_sampled():
+    """Full decode shape (B=16, Hq=32, Hkv=8, 131072-token cache, k = 52,
+    automatic splits); the oracle checks sampled (batch, head) pairs with the
+    same split count."""
+    import bit_quantized_attention_amd as bqa
+    from bit_quantized_attention_amd.runner import ThriftDecodePath, thrift_problem, to_device
+    w = wl.WORKLOADS["c5d"]
+    nw = wl.default_workers()
+    q, K, V = wl.build(w, "q"), wl.build(w, "k", workers=nw), wl.build(w, "v", workers=nw)
+    p = thrift_problem(w.B, w.Hq, w.Hkv, 1, w.Nk, w.d, budget_ppm=PPM_5)
+    path = ThriftDecodePath(p, to_device(q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
+    path.build_cache()
+    path.step()
+    torch.cuda.synchronize()
+    O = path.o.float().cpu().numpy()
+    L = path.lse.cpu().numpy()
+    idx = path.sel_idx.cpu().numpy()
+    S = min(1024, -(-2048 // (w.B * w.Hkv)))
+    assert bqa.max_sel(p) == 52
+    for b, hq in ((0, 0), (7, 13), (15, 31)):
+        hk = hq // 4
+        Kh, Vh, qh = K[b, hk], V[b, hk], q[b, hq]
+        kc, ks = orc.quant_mx_rows(Kh[None]); vc, vs = orc.quant_mx_cols(Vh[None])
+        qc, qs = orc.quant_mx_rows(qh[None])
+        ridx, rcnt = orc.select_blocks(qh, orc.block_means(Kh[None], 128)[0], True, PPM_5, 52)
+        assert_same(idx[b, hq], ridx, f"decode selection (b={b}, h={hq})")
+        ref, lse = orc.thrift_decode(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0], q=qh[0], Kh=Kh,
+                                     Vh=Vh, sel=ridx[0, :rcnt[0]], Nk=w.Nk, d=w.d, blk=128, tau=tau_for(w.d),
+                                     num_splits=S)
+        compare_outputs(O[b, hq, 0], ref, "bf16", what=f"decode o (b={b}, h={hq})")
+        assert abs(L[b, hq, 0] - lse) < 2e-3

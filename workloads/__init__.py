@@ -178,12 +178,38 @@ def heads_of(w: Workload, tensor: str) -> int:
     return w.Hkv if tensor in ("k", "v") else w.Hq
 
 
-def build(w: Workload, tensor: str) -> np.ndarray:
-    """Whole [B, H, N, d] tensor (fp32 values, exact in the workload dtype)."""
+def _chunk_job(args):
+    w, tensor, b, h = args
+    return b, h, chunk(w, tensor, b, h)
+
+
+def build(w: Workload, tensor: str, workers: int = 0) -> np.ndarray:
+    """Whole [B, H, N, d] tensor (fp32 values, exact in the workload dtype).
+
+    workers > 1 generates the (b, h) chunks in that many fresh interpreter
+    processes (each chunk has its own seed, so the result is the same)."""
     H = heads_of(w, tensor)
     N = w.Nk if tensor in ("k", "v") else w.Nq
     out = np.empty((w.B, H, N, w.d), dtype=np.float32)
-    for b in range(w.B):
-        for h in range(H):
-            out[b, h] = chunk(w, tensor, b, h)
+    jobs = [(w, tensor, b, h) for b in range(w.B) for h in range(H)]
+    if workers > 1 and len(jobs) > 1:
+        import concurrent.futures as cf
+        import multiprocessing as mp
+        with cf.ProcessPoolExecutor(max_workers=min(workers, len(jobs)), mp_context=mp.get_context("spawn")) as ex:
+            for b, h, x in ex.map(_chunk_job, jobs, chunksize=1):
+                out[b, h] = x
+        return out
+    for job in jobs:
+        b, h, x = _chunk_job(job)
+        out[b, h] = x
     return out
+
+
+def default_workers() -> int:
+    """Generator processes for full-size inputs: the CPUs this process may use, at most 16."""
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
