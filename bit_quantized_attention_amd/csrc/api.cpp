@@ -124,6 +124,9 @@ size_t bqa_workspace_size(const bqa_problem* p, int32_t op) {
         case BQA_OP_QUANTIZE_V:
             if (p->mode == BQA_SAGE_I8_F8PV || p->mode == BQA_SAGE_I8_I8PV) return ws_chan_bytes(p->B * p->Hkv, p->Nk, p->d);
             return 0;
+        case BQA_OP_BWD:
+            if (is_sage(p->mode) && p->Nq == p->Nk) return ws_sage_bwd_bytes(p->B, p->Hq, p->Nq, p->d);
+            return 0;
         case BQA_OP_FWD:
             if (p->mode == BQA_QAT_MXFP4) return ws_qat_fwd_bytes(p->B, p->Hkv, p->Nk, p->d);
             if (p->mode == BQA_THRIFT && p->Nq == 1 && p->Nk % 128 == 0)
@@ -318,9 +321,35 @@ bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
                         const bqa_tensor* v_hi, const bqa_tensor* o_for_delta, const float* lse,
                         const bqa_tensor* d_o, bqa_tensor* dq, bqa_tensor* dk, bqa_tensor* dv, void* ws,
                         size_t ws_bytes, void* stream) {
-    (void)q; (void)k; (void)v; (void)v_hi; (void)o_for_delta; (void)lse; (void)d_o; (void)dq; (void)dk; (void)dv;
-    (void)ws; (void)ws_bytes; (void)stream;
+    (void)v;
     TRY(check_problem(p));
+    hipStream_t st = (hipStream_t)stream;
+    if (p->mode == BQA_SAGE_I8_I8PV || p->mode == BQA_SAGE_I8_F8PV || p->mode == BQA_SAGE_I8_F16PV) {
+        if (p->d != 128 || p->Hq != p->Hkv || p->Nq != p->Nk || p->Nq % 128 != 0) return BQA_E_UNSUPPORTED;
+        if (p->q_block != 128 || p->k_block != 64) return BQA_E_UNSUPPORTED;
+        TRY(check_q(q, BQA_INT8, 0));
+        TRY(check_q(k, BQA_INT8, 0));
+        if (q->block != 128 || k->block != 64) return BQA_E_UNSUPPORTED;
+        TRY(check_dense(v_hi, false, true));
+        TRY(check_dense(o_for_delta, false, true));
+        TRY(check_dense(d_o, false, true));
+        TRY(check_dense(dq, false, true));
+        TRY(check_dense(dk, false, true));
+        TRY(check_dense(dv, false, true));
+        if (!lse) return BQA_E_NULL;
+        if (!ws || ws_bytes < ws_sage_bwd_bytes(p->B, p->Hq, p->Nq, p->d)) return BQA_E_WORKSPACE;
+        if (!aligned16(ws) || ((uintptr_t)lse & 15u)) return BQA_E_ALIGN;
+        SageBwdArgs a{};
+        a.qc = (const int8_t*)q->codes; a.qs = (const float*)q->scales;
+        a.kc = (const int8_t*)k->codes; a.ks = (const float*)k->scales;
+        a.v = as_dense(v_hi); a.d_o = as_dense(d_o); a.lse = lse;
+        a.dq = as_dense(dq); a.dk = as_dense(dk); a.dv = as_dense(dv);
+        a.B = p->B; a.H = p->Hq; a.N = p->Nq; a.causal = p->causal;
+        a.tau = tau_of(p);
+        a.c_log2 = a.tau * 1.4426950408889634f;
+        TRY(check_device());
+        return launched(launch_sage_bwd(a, as_dense(o_for_delta), ws, st));
+    }
     return BQA_E_UNSUPPORTED;
 }
 

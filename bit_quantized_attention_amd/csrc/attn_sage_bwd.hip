@@ -1,0 +1,464 @@
+// attn_sage_bwd.hip — SageBwd INT8 attention backward for gfx950.
+//
+// "SageBwd: A Trainable Low-bit Attention", Methodology 2 and Limitations
+// (and the Chinese duplicate page): the backward recomputes S from the
+// forward's INT8 codes and P = exp(s - L) from the saved log-sum-exp; of the
+// five backward products four are INT8 with per-block scales (P^T dO, the
+// recompute Q K^T, dS K and dS^T Q) and the softmax-gradient product
+// dP = dO V^T stays in 16-bit (bf16 operands, fp32 accumulation).
+// dS = P o (dP - delta), delta = rowsum(dO o O) with the forward's O.  P and
+// dS are rounded to INT8 with one scale per 128 x 64 backward tile; dO is
+// INT8 per 128-token block.
+//
+// Kernels:
+//   delta_rows_kernel     delta per query row (fp32)
+//   transpose_i8_kernel   channel-major copies of the Q, K and dO codes (the
+//                         second operand of the INT8 products reads tokens
+//                         contiguously per channel)
+//   sbwd_dkdv_kernel      one workgroup per 64-key block, over the query
+//                         tiles; the tile is computed with keys in lanes, so
+//                         P^T and dS^T are already the A operands of
+//                         dV = P^T dO and dK = dS^T Q in registers
+//   sbwd_dq_kernel        one workgroup per 128-query tile, over the key
+//                         tiles; queries in lanes, so dS is the A operand of
+//                         dQ = dS K in registers
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace bqa {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int TQ = 128;   // backward tile: queries
+constexpr int TK = 64;    // backward tile: keys
+
+__device__ __forceinline__ int sigma(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+// XOR patterns of the 16-byte chunks per row: rows read through sigma
+// (..s) or by consecutive rows (..c), for 64 / 128 / 256-byte rows.
+__device__ __forceinline__ int fs128(int r) { return ((r >> 1) & 7) ^ (((r >> 4) & 1) << 2); }
+__device__ __forceinline__ int fs256(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
+__device__ __forceinline__ int fc64(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int fc128(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
+// Symmetric INT8 code of x with the tile's inverse scale (nearest even, +-127).
+__device__ __forceinline__ int q8(float x, float inv) {
+    return (int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(x * inv), -127.0f), 127.0f);
+}
+// Four INT8 codes into one word, lowest first.
+__device__ __forceinline__ int pack4(int a, int b, int c, int d) {
+    return (a & 0xFF) | ((b & 0xFF) << 8) | ((c & 0xFF) << 16) | ((int)((uint32_t)d << 24));
+}
+// 16 values (one lane half's keys or queries of a 32-group) -> v4i of codes
+__device__ __forceinline__ v4i pack16(const float* x, float inv) {
+    return v4i{pack4(q8(x[0], inv), q8(x[1], inv), q8(x[2], inv), q8(x[3], inv)),
+               pack4(q8(x[4], inv), q8(x[5], inv), q8(x[6], inv), q8(x[7], inv)),
+               pack4(q8(x[8], inv), q8(x[9], inv), q8(x[10], inv), q8(x[11], inv)),
+               pack4(q8(x[12], inv), q8(x[13], inv), q8(x[14], inv), q8(x[15], inv))};
+}
+
+// Largest value over the workgroup: wavefront maxima through LDS.
+__device__ __forceinline__ float block_max(float v, float* red, int w, int l) {
+    v = wave_max(v);
+    if (l == 0) red[w] = v;
+    __syncthreads();
+    const float r = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    return r;
+}
+
+// ------------------------------------------------------------------ preprocess
+__global__ __launch_bounds__(256) void delta_rows_kernel(Dense dO, Dense O, int H, int N, int64_t rows,
+                                                         float* __restrict__ delta) {
+    // delta_i = sum_c dO[i, c] O[i, c]; one row per 16 lanes, 8 channels each
+    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+    const int part = threadIdx.x & 15;
+    float acc = 0.0f;
+    if (row < rows) {
+        const int64_t bh = row / N, i = row % N, b = bh / H, h = bh % H;
+        const uint16_t* g = (const uint16_t*)dO.p + b * dO.sB + h * dO.sH + i * dO.sN + 8 * part;
+        const uint16_t* o = (const uint16_t*)O.p + b * O.sB + h * O.sH + i * O.sN + 8 * part;
+        const v4i gv = *(const v4i*)g, ov = *(const v4i*)o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc = __builtin_fmaf(bf16_bits_to_f32((uint16_t)gv[k]), bf16_bits_to_f32((uint16_t)ov[k]), acc);
+            acc = __builtin_fmaf(bf16_bits_to_f32((uint16_t)((uint32_t)gv[k] >> 16)),
+                                 bf16_bits_to_f32((uint16_t)((uint32_t)ov[k] >> 16)), acc);
+        }
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 16);
+    if (row < rows && part == 0) delta[row] = acc;
+}
+
+// [BH][N][d] int8 -> [BH][d][N], 64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_i8_kernel(const int8_t* __restrict__ in, int N, int d,
+                                                           int8_t* __restrict__ out) {
+    __shared__ uint8_t t[64][65];
+    const int tilesN = N / 64, tilesD = d / 64;
+    int blk = blockIdx.x;
+    const int td = blk % tilesD; blk /= tilesD;
+    const int tn = blk % tilesN;
+    const int64_t bh = blk / tilesN;
+    const int8_t* src = in + (bh * N + (int64_t)tn * 64) * d + td * 64;
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int r = e >> 6, c = e & 63;
+        t[r][c] = (uint8_t)src[(int64_t)r * d + c];
+    }
+    __syncthreads();
+    int8_t* dst = out + (bh * d + (int64_t)td * 64) * N + (int64_t)tn * 64;
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int r = e >> 6, c = e & 63;
+        dst[(int64_t)r * N + c] = (int8_t)t[c][r];
+    }
+}
+
+// ------------------------------------------------------------------ dK, dV
+struct LdsKV {
+    uint8_t q[TQ * D];          // Q codes of the query tile, 128 x 128 B (sigma reads)
+    uint8_t dob[TQ * D * 2];    // dO bf16, 128 x 256 B (sigma reads)
+    uint8_t doT[D * TQ];        // dO codes channel-major, 128 ch x 128 B
+    uint8_t qT[D * TQ];         // Q codes channel-major, 128 ch x 128 B
+    float lse[TQ];
+    float dlt[TQ];
+    float red[8];
+};
+// the closing exchange of partial dV, dK reuses dob .. qT (64 KB)
+static_assert(sizeof(LdsKV) - __builtin_offsetof(LdsKV, dob) >= 2 * 2 * 32 * D * sizeof(float), "exchange area");
+
+__device__ __forceinline__ void kv_issue_phase1(const SageBwdArgs& a, int bh, int b, int hq, int I, LdsKV& L, int w,
+                                                int l) {
+    const int q0 = I * TQ;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {     // Q codes: 16 x 1 KB (8 rows each)
+        const int sgm = 4 * w + u, r = 8 * sgm + (l >> 3);
+        dma16(a.qc + ((int64_t)bh * a.N + q0 + r) * D + 16 * ((l & 7) ^ fs128(r)), L.q + 1024 * sgm);
+    }
+    const uint16_t* dob = (const uint16_t*)a.d_o.p + b * a.d_o.sB + hq * a.d_o.sH;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {     // dO bf16: 32 x 1 KB (4 rows each)
+        const int sgm = 8 * w + u, r = 4 * sgm + (l >> 4);
+        dma16(dob + (int64_t)(q0 + r) * a.d_o.sN + 8 * ((l & 15) ^ fs256(r)), L.dob + 1024 * sgm);
+    }
+    // log-sum-exp and delta of the tile: one 256-byte copy per wavefront
+    if (w < 2) dma4(a.lse + (int64_t)bh * a.N + q0 + 64 * w + l, L.lse + 64 * w);
+    else dma4(a.delta + (int64_t)bh * a.N + q0 + 64 * (w - 2) + l, L.dlt + 64 * (w - 2));
+}
+__device__ __forceinline__ void kv_issue_phase2(const SageBwdArgs& a, int bh, int I, LdsKV& L, int w, int l) {
+    const int q0 = I * TQ;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {     // channel-major dO and Q codes: 16 x 1 KB each (8 rows of 128 B)
+        const int sgm = 4 * w + u, r = 8 * sgm + (l >> 3);
+        const int c = (l & 7) ^ fc128(r);
+        dma16(a.doT + ((int64_t)bh * D + r) * a.N + q0 + 16 * c, L.doT + 1024 * sgm);
+        dma16(a.qT + ((int64_t)bh * D + r) * a.N + q0 + 16 * c, L.qT + 1024 * sgm);
+    }
+}
+
+__global__ __launch_bounds__(256, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
+    __shared__ __attribute__((aligned(16))) LdsKV L;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
+    const int nkt = a.N / TK, nqt = a.N / TQ;
+    const int J = blockIdx.x % nkt;                  // ascending J: the longest query ranges first
+    const int bh = blockIdx.x / nkt, b = bh / a.H, hq = bh % a.H;
+    const int kh = w & 1, qh = w >> 1;               // the wavefront's 32 keys and 64 queries of the tile
+    const int key = J * TK + 32 * kh + lq;
+    const int qrow_s = sigma(lq);
+    const float c = a.c_log2;
+    const float ks = a.ks[(int64_t)bh * nkt + J];
+
+    // this lane's key: K codes (B operand of S = Q K^T) and V in bf16 (B operand of dP = dO V^T)
+    v4i kb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kb[kk] = *(const v4i*)(a.kc + ((int64_t)bh * a.N + key) * D + 32 * kk + 16 * h);
+    v8bf vb[8];
+    const uint16_t* vrow = (const uint16_t*)a.v.p + b * a.v.sB + hq * a.v.sH + (int64_t)key * a.v.sN;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) vb[st] = *(const v8bf*)(vrow + 16 * st + 8 * h);
+
+    v16f dv[4], dk[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) { dv[cb] = v16f{}; dk[cb] = v16f{}; }
+
+    const int I0 = a.causal ? (J * TK) / TQ : 0;
+    for (int I = I0; I < nqt; ++I) {
+        __syncthreads();                              // the previous tile's reads are done
+        kv_issue_phase1(a, bh, b, hq, I, L, w, l);
+        kv_issue_phase2(a, bh, I, L, w, l);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const float qsc = a.qs[(int64_t)bh * nqt + I];
+        const float sc = qsc * ks * c;
+        // ---- S (int32), dP (fp32) for 2 groups of 32 queries x 32 keys; reg i of half h = query 16h + i
+        float P[2][16], dS[2][16];
+        float pmax = 0.0f, dmax = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int rq = 64 * qh + 32 * g + qrow_s;            // A row fed by this lane
+            v16i s = v16i{};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const v4i av = *(const v4i*)(L.q + rq * 128 + 16 * ((2 * kk + h) ^ fs128(rq)));
+                s = mfma_i8_32x32x32(av, kb[kk], s);
+            }
+            v16f dp = v16f{};
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+                const v8bf av = *(const v8bf*)(L.dob + rq * 256 + 16 * ((2 * st + h) ^ fs256(rq)));
+                dp = mfma_bf16_32x32x16(av, vb[st], dp);
+            }
+            const int qb0 = 64 * qh + 32 * g + 16 * h;           // tile-local query of register 0
+            v4f lse4[4], dl4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                lse4[u] = *(const v4f*)(L.lse + qb0 + 4 * u);
+                dl4[u] = *(const v4f*)(L.dlt + qb0 + 4 * u);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int qpos = I * TQ + qb0 + i;
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[i], sc, -lse4[i >> 2][i & 3] * 1.4426950408889634f));
+                if (a.causal && key > qpos) p = 0.0f;
+                const float ds = p * (dp[i] - dl4[i >> 2][i & 3]);
+                P[g][i] = p;
+                dS[g][i] = ds;
+                pmax = __builtin_fmaxf(pmax, p);
+                dmax = __builtin_fmaxf(dmax, __builtin_fabsf(ds));
+            }
+        }
+        // ---- one INT8 scale per tile for P and for dS
+        pmax = block_max(pmax, L.red, w, l);
+        dmax = block_max(dmax, L.red + 4, w, l);
+        const float inv_p = pmax > 0.0f ? 127.0f / pmax : 0.0f;
+        const float inv_d = dmax > 0.0f ? 127.0f / dmax : 0.0f;
+        const bool p_ok = inv_p != 0.0f && inv_p < __builtin_inff();
+        const bool d_ok = inv_d != 0.0f && inv_d < __builtin_inff();
+        v4i pa[2], da[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            pa[g] = p_ok ? pack16(P[g], inv_p) : v4i{};
+            da[g] = d_ok ? pack16(dS[g], inv_d) : v4i{};
+        }
+        // ---- dV += P^T dO, dK += tau dS^T Q (keys x channels), K-steps = the 2 query groups
+        const float sv = p_ok ? pmax * (1.0f / 127.0f) * a.dos[(int64_t)bh * nqt + I] : 0.0f;
+        const float sk = d_ok ? dmax * (1.0f / 127.0f) * qsc * a.tau : 0.0f;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int rr = 32 * cb + lq;
+            v16i tv = v16i{}, tk = v16i{};
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const int ch = 4 * qh + 2 * g + h;                   // 16-query chunk of the row
+                const v4i bo = *(const v4i*)(L.doT + rr * 128 + 16 * (ch ^ fc128(rr)));
+                const v4i bq = *(const v4i*)(L.qT + rr * 128 + 16 * (ch ^ fc128(rr)));
+                tv = mfma_i8_32x32x32(pa[g], bo, tv);
+                tk = mfma_i8_32x32x32(da[g], bq, tk);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                dv[cb][i] = __builtin_fmaf((float)tv[i], sv, dv[cb][i]);
+                dk[cb][i] = __builtin_fmaf((float)tk[i], sk, dk[cb][i]);
+            }
+        }
+    }
+    // ---- the two query halves of each key half: sum through LDS, write bf16
+    __syncthreads();
+    float* xch = (float*)L.dob;                      // 2 key halves x (dV, dK) x 32 keys x 128 channels
+    if (qh == 1) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kr = 8 * (i >> 2) + 4 * h + (i & 3), ch = 32 * cb + lq;
+                xch[((kh * 2 + 0) * 32 + kr) * D + ch] = dv[cb][i];
+                xch[((kh * 2 + 1) * 32 + kr) * D + ch] = dk[cb][i];
+            }
+    }
+    __syncthreads();
+    if (qh == 0) {
+        uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sB + hq * a.dv.sH;
+        uint16_t* dkp = (uint16_t*)a.dk.p + b * a.dk.sB + hq * a.dk.sH;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kr = 8 * (i >> 2) + 4 * h + (i & 3), ch = 32 * cb + lq;
+                const int64_t kpos = (int64_t)J * TK + 32 * kh + kr;
+                dvp[kpos * a.dv.sN + ch] = f32_to_bf16_bits(dv[cb][i] + xch[((kh * 2 + 0) * 32 + kr) * D + ch]);
+                dkp[kpos * a.dk.sN + ch] = f32_to_bf16_bits(dk[cb][i] + xch[((kh * 2 + 1) * 32 + kr) * D + ch]);
+            }
+    }
+}
+
+// ------------------------------------------------------------------ dQ
+struct LdsQ {
+    uint8_t k[TK * D];          // K codes of the key tile, 64 x 128 B (sigma reads)
+    uint8_t vb[TK * D * 2];     // V bf16, 64 x 256 B (sigma reads)
+    uint8_t kT[D * TK];         // K codes channel-major, 128 ch x 64 B
+};
+
+__device__ __forceinline__ void q_issue(const SageBwdArgs& a, int bh, int b, int hq, int J, LdsQ& L, int w, int l) {
+    const int k0 = J * TK;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {     // K codes: 8 x 1 KB (8 rows of 128 B)
+        const int sgm = 2 * w + u, r = 8 * sgm + (l >> 3);
+        dma16(a.kc + ((int64_t)bh * a.N + k0 + r) * D + 16 * ((l & 7) ^ fs128(r)), L.k + 1024 * sgm);
+    }
+    const uint16_t* vb = (const uint16_t*)a.v.p + b * a.v.sB + hq * a.v.sH;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {     // V bf16: 16 x 1 KB (4 rows of 256 B)
+        const int sgm = 4 * w + u, r = 4 * sgm + (l >> 4);
+        dma16(vb + (int64_t)(k0 + r) * a.v.sN + 8 * ((l & 15) ^ fs256(r)), L.vb + 1024 * sgm);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {     // channel-major K codes: 8 x 1 KB (16 rows of 64 B)
+        const int sgm = 2 * w + u, r = 16 * sgm + (l >> 2);
+        dma16(a.kT + ((int64_t)bh * D + r) * a.N + k0 + 16 * ((l & 3) ^ fc64(r)), L.kT + 1024 * sgm);
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void sbwd_dq_kernel(SageBwdArgs a) {
+    __shared__ __attribute__((aligned(16))) LdsQ L[2];
+    __shared__ float red[8];
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
+    const int nkt = a.N / TK, nqt = a.N / TQ;
+    const int I = nqt - 1 - (int)(blockIdx.x % nqt);   // heaviest tiles first
+    const int bh = blockIdx.x / nqt, b = bh / a.H, hq = bh % a.H;
+    const int qrow = I * TQ + 32 * w + lq;
+    const int krow = sigma(lq);
+    const float c = a.c_log2;
+    const float qsc = a.qs[(int64_t)bh * nqt + I];
+
+    // this lane's query: codes (B operand of S^T = K Q^T), dO bf16 (B operand of dP^T = V dO^T)
+    v4i qb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qb[kk] = *(const v4i*)(a.qc + ((int64_t)bh * a.N + qrow) * D + 32 * kk + 16 * h);
+    v8bf gb[8];
+    const uint16_t* grow = (const uint16_t*)a.d_o.p + b * a.d_o.sB + hq * a.d_o.sH + (int64_t)qrow * a.d_o.sN;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) gb[st] = *(const v8bf*)(grow + 16 * st + 8 * h);
+    const float lse2 = a.lse[(int64_t)bh * a.N + qrow] * 1.4426950408889634f;
+    const float dlt = a.delta[(int64_t)bh * a.N + qrow];
+
+    v16f dq[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) dq[cb] = v16f{};
+
+    const int nJ = a.causal ? (I * TQ + TQ - 1) / TK + 1 : nkt;
+    q_issue(a, bh, b, hq, 0, L[0], w, l);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int J = 0; J < nJ; ++J) {
+        const int cur = J & 1;
+        if (J + 1 < nJ) q_issue(a, bh, b, hq, J + 1, L[cur ^ 1], w, l);
+        const LdsQ& T = L[cur];
+        const float ks = a.ks[(int64_t)bh * nkt + J];
+        const float sc = qsc * ks * c;
+        float P[2][16], dS[2][16];
+        float dmax = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int rk = 32 * g + krow;
+            v16i s = v16i{};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const v4i av = *(const v4i*)(T.k + rk * 128 + 16 * ((2 * kk + h) ^ fs128(rk)));
+                s = mfma_i8_32x32x32(av, qb[kk], s);
+            }
+            v16f dp = v16f{};
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+                const v8bf av = *(const v8bf*)(T.vb + rk * 256 + 16 * ((2 * st + h) ^ fs256(rk)));
+                dp = mfma_bf16_32x32x16(av, gb[st], dp);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kpos = J * TK + 32 * g + 16 * h + i;
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[i], sc, -lse2));
+                if (a.causal && kpos > qrow) p = 0.0f;
+                const float ds = p * (dp[i] - dlt);
+                P[g][i] = p;
+                dS[g][i] = ds;
+                dmax = __builtin_fmaxf(dmax, __builtin_fabsf(ds));
+            }
+        }
+        (void)P;
+        dmax = block_max(dmax, red + 4 * (J & 1), w, l);
+        const float inv_d = dmax > 0.0f ? 127.0f / dmax : 0.0f;
+        const bool d_ok = inv_d != 0.0f && inv_d < __builtin_inff();
+        v4i da[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) da[g] = d_ok ? pack16(dS[g], inv_d) : v4i{};
+        const float sq = d_ok ? dmax * (1.0f / 127.0f) * ks * a.tau : 0.0f;
+        // dQ += tau dS K: A = dS (queries x keys) from registers, B = K codes channel-major
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int rr = 32 * cb + lq;
+            v16i t = v16i{};
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const v4i bk = *(const v4i*)(T.kT + rr * 64 + 16 * ((2 * g + h) ^ fc64(rr)));
+                t = mfma_i8_32x32x32(da[g], bk, t);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) dq[cb][i] = __builtin_fmaf((float)t[i], sq, dq[cb][i]);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    // dq[cb] reg i: query 32 w + 8 (i / 4) + 4 h + i % 4, channel 32 cb + lq
+    uint16_t* dqp = (uint16_t*)a.dq.p + b * a.dq.sB + hq * a.dq.sH;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t qr = (int64_t)I * TQ + 32 * w + 8 * (i >> 2) + 4 * h + (i & 3);
+            dqp[qr * a.dq.sN + 32 * cb + lq] = f32_to_bf16_bits(dq[cb][i]);
+        }
+}
+
+}  // namespace
+
+size_t ws_sage_bwd_bytes(int B, int H, int N, int d) {
+    const size_t bhn = (size_t)B * H * N;
+    return bhn * 4                 // delta
+           + bhn * d               // dO codes
+           + (bhn / 128) * 4       // dO scales
+           + 3 * bhn * d           // channel-major dO, Q, K codes
+           + 256;
+}
+
+hipError_t launch_sage_bwd(SageBwdArgs a, Dense o, void* ws, hipStream_t st) {
+    const int64_t bhn = (int64_t)a.B * a.H * a.N;
+    uint8_t* p = (uint8_t*)ws;
+    float* delta = (float*)p;                 p += bhn * 4;
+    int8_t* doc = (int8_t*)p;                 p += bhn * D;
+    float* dos = (float*)p;                   p += (bhn / 128) * 4;
+    int8_t* doT = (int8_t*)p;                 p += bhn * D;
+    int8_t* qT = (int8_t*)p;                  p += bhn * D;
+    int8_t* kT = (int8_t*)p;
+    a.delta = delta; a.dos = dos; a.doT = doT; a.qT = qT; a.kT = kT;
+
+    const int64_t rows = bhn;
+    delta_rows_kernel<<<(unsigned)((rows * 16 + 255) / 256), 256, 0, st>>>(a.d_o, o, a.H, a.N, rows, delta);
+    hipError_t e = launch_quant_i8_tokblock(a.d_o, false, a.B, a.H, a.N, D, 128, false, 0.0, nullptr, nullptr, doc,
+                                            dos, st);
+    if (e != hipSuccess) return e;
+    const unsigned tgrid = (unsigned)((int64_t)a.B * a.H * (a.N / 64) * (D / 64));
+    transpose_i8_kernel<<<tgrid, 256, 0, st>>>(doc, a.N, D, doT);
+    transpose_i8_kernel<<<tgrid, 256, 0, st>>>(a.qc, a.N, D, qT);
+    transpose_i8_kernel<<<tgrid, 256, 0, st>>>(a.kc, a.N, D, kT);
+    sbwd_dkdv_kernel<<<a.B * a.H * (a.N / TK), 256, 0, st>>>(a);
+    sbwd_dq_kernel<<<a.B * a.H * (a.N / TQ), 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace bqa

@@ -53,6 +53,21 @@ hipError_t launch_qat_fwd(const QatFwdArgs& a, hipStream_t st);
 hipError_t launch_debug_scores_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                                   float* out, hipStream_t st);
 
+// ---- SageBwd backward (attn_sage_bwd.hip); d = 128, Hq == Hkv, N a multiple of 128
+struct SageBwdArgs {
+    const int8_t* qc; const float* qs;                   // forward Q codes [B,H,N,d], scales per 128 tokens
+    const int8_t* kc; const float* ks;                   // forward K codes [B,H,N,d], scales per 64 tokens
+    Dense v, d_o;                                        // V, dO bf16 [B,H,N,d]
+    const float* lse;                                    // forward log-sum-exp [B,H,N]
+    float* delta; const float* dos;                      // workspace: delta [B,H,N], dO scales
+    const int8_t* doT; const int8_t* qT; const int8_t* kT;   // workspace: channel-major codes [B,H,d,N]
+    Dense dq, dk, dv;                                    // outputs bf16
+    int B, H, N, causal;
+    float c_log2, tau;
+};
+size_t ws_sage_bwd_bytes(int B, int H, int N, int d);
+hipError_t launch_sage_bwd(SageBwdArgs a, Dense o, void* ws, hipStream_t st);
+
 // ---- ThriftAttention mixed prefill (attn_thrift.hip); head dimension 128, 128-token blocks
 struct ThriftFwdArgs {
     const uint8_t* qc; const uint8_t* qs;                // MXFP4 Q [B,Hq,Nq,d/2], E8M0 [B,Hq,Nq,d/32]

@@ -10,9 +10,9 @@ from __future__ import annotations
 import torch
 
 from . import (BQA_FP8E4M3, BQA_INT8, BQA_MXFP4, BQA_OP_FWD, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_V,
-               BQA_QAT_MXFP4, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V, BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV, BQA_THRIFT,
-               bqa_attn_fwd, bqa_quantize_blocks, bqa_select_blocks, bqa_workspace_size, dense, max_sel, problem,
-               qtensor)
+               BQA_OP_BWD, BQA_QAT_MXFP4, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V, BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV,
+               BQA_THRIFT, bqa_attn_bwd, bqa_attn_fwd, bqa_quantize_blocks, bqa_select_blocks, bqa_workspace_size, dense,
+               max_sel, problem, qtensor)
 
 
 def sage_problem(B, Hq, Hkv, Nq, Nk, d, causal, mode, q_block=128, k_block=64, smooth_k=True, smooth_eps=0.0,
@@ -65,6 +65,32 @@ class SagePath:
         self.quantize()
         self.forward()
         return self.o
+
+
+class SageTrainStep(SagePath):
+    """SageBwd training step: the INT8 forward (per-channel INT8 V in P.V),
+    then the backward from dO (delta from the stored O, INT8 dO, four INT8
+    products and the bf16 dP = dO V^T)."""
+
+    def __init__(self, p, q, k, v, d_o):
+        super().__init__(p, q, k, v)
+        dev = q.device
+        self.d_o = d_o
+        self.dq = torch.empty_like(q)
+        self.dk = torch.empty_like(k)
+        self.dv = torch.empty_like(v)
+        self.ws_bwd = torch.empty(max(bqa_workspace_size(p, BQA_OP_BWD), 16), dtype=torch.uint8, device=dev)
+        self._dod = dense(d_o)
+
+    def backward(self):
+        bqa_attn_bwd(self.p, q=self.qq, k=self.kq, v_hi=self._vd, o_for_delta=self._od, lse=self.lse,
+                     d_o=self._dod, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws_bwd)
+
+    def step(self):
+        self.quantize()
+        self.forward()
+        self.backward()
+        return self.dq, self.dk, self.dv
 
 
 def qat_problem(B, Hq, Hkv, Nq, Nk, d, sm_scale=0.0):
