@@ -5,6 +5,10 @@ Workloads (``--workload``, default c2):
   c2  SageAttention INT8 forward at B=2, H=16, N=4096, d=128, causal, bf16
       inputs (outlier channels and a K channel bias): K-smoothing means, INT8
       Q/K, per-channel e4m3 V, fused attention with e4m3 P.V.
+  c3  SageBwd training step at B=1, H=16, N=8192, d=128, causal, QK-norm
+      inputs: K-smoothing (eps 1e-3), INT8 forward, INT8 backward with the
+      bf16 dP = dO V^T; `value` counts forward + backward (14 B H N^2 d / 2)
+      and the roofline covers the backward call.
   c4  Attn-QAT FP4 forward at B=1, H=32, N=16384, d=128, non-causal,
       Student-t inputs: MXFP4 Q, K, V, fused attention with MXFP4 P.V and
       the bf16 auxiliary output O'.
@@ -25,7 +29,7 @@ time, measured with HIP events on the stream it runs on, against the dense
 matrix-core peak of its operand types.  `cpu_baseline` times the CPU oracle
 on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--workload c2|c4|c5|c5d] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--workload c2|c3|c4|c5|c5d] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -312,7 +316,64 @@ def _decode_case(w, bqa, torch):
         traffic_key="thrift_decode_kernel", cpu=cpu_baseline_decode)
 
 
-CASES = {"c2": _sage_case, "c4": _qat_case, "c5": _thrift_case, "c5d": _decode_case}
+def cpu_baseline_sagebwd(w, budget_s: float = 25.0):
+    """The oracle on a bounded sample of the SageBwd step: quantisation and
+    the whole forward of head (0,0) (every row's O and log-sum-exp feed the
+    backward), then its backward on the last query tile (dQ) and the first
+    key tile (dK, dV), the two longest."""
+    import oracle
+    import workloads as wl
+    from tests.helpers import tau_for
+    oracle.lib()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    Q, K, V, dO = (wl.chunk(w, t, 0, 0) for t in ("q", "k", "v", "do"))
+    tau = tau_for(w.d)
+    mu, _ = oracle.smooth_mean(K[None], float(__import__("numpy").float32(1e-3)))
+    qc, qs = oracle.quant_i8_tokblock(Q[None], 128)
+    kc, ks = oracle.quant_i8_tokblock(K[None], 64, mu)
+    vc, vs = oracle.quant_chan(V[None], "i8")
+    O, lse = oracle.sage_fwd(qc=qc[0], qs=qs[0], q_blk=128, kc=kc[0], ks=ks[0], k_blk=64, pv_mode=oracle.PV_I8,
+                             vc_t=vc[0], vs=vs[0], Nq=w.Nq, Nk=w.Nk, d=w.d, causal=True, tau=tau, kv_tile=64)
+    nqt, nkt = w.Nq // 128, w.Nk // 64
+    oracle.sage_bwd(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], V=V, dO=dO, O=oracle.round_to(O, "bf16"),
+                    lse=lse.astype("float32"), causal=True, tau=tau, qtiles=(nqt - 1, nqt), ktiles=(0, 1))
+    dt = time.perf_counter() - t0
+    n = w.Nq
+    fwd_pairs = n * (n + 1) // 2
+    dq_pairs = sum(i + 1 for i in range(n - 128, n))             # last query tile, causal
+    dkv_pairs = sum(n - j for j in range(64))                    # first key tile, causal
+    ops = 4.0 * w.d * fwd_pairs + 6.0 * w.d * dq_pairs + 8.0 * w.d * dkv_pairs
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"head (0,0) at N={n}: quantisation and the full forward, then the backward of the last "
+                      f"query tile (dQ) and the first key tile (dK, dV), {dt:.1f} s"}
+
+
+def _sagebwd_case(w, bqa, torch):
+    from bit_quantized_attention_amd.runner import SageTrainStep, sage_problem, to_device
+    import workloads as wl
+    Q, K, V, dO = (wl.build(w, t) for t in ("q", "k", "v", "do"))
+    p = sage_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.causal, bqa.BQA_SAGE_I8_I8PV, q_block=128,
+                     smooth_k=True, smooth_eps=1e-3)
+    path = SageTrainStep(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"), to_device(dO, "bf16"))
+    n_pairs = w.B * w.Hq * w.Nq * (w.Nq + 1) / 2
+    bwd_ops = 10.0 * w.d * n_pairs          # S recompute, dP, dV, dQ, dK
+    ops = 14.0 * w.B * w.Hq * w.Nq * w.Nk * w.d / 2
+    # backward roofline: 4 of the 5 products at the i8 rate, dP at the bf16 rate
+    t_peak = 0.8 * bwd_ops / (PEAK_I8_TOPS * 1e12) + 0.2 * bwd_ops / (PEAK_BF16_TFLOPS * 1e12)
+    return dict(
+        path=path, ops=ops, dtype="i8+bf16", timed="backward",
+        workload="SageBwd training step (c3): B=1 H=16 N=8192 d=128 causal, QK-norm bf16 in, K-smoothing eps=1e-3, "
+                 "INT8 Q/K/V/P forward; backward with INT8 dO/P/dS and bf16 dP; step = quantise + forward + backward",
+        roofline={"bound": "mfma", "kernel": "attn_bwd (delta, dO quantiser, code transposes, sbwd_dkdv_kernel, "
+                                             "sbwd_dq_kernel)",
+                  "peak": round(bwd_ops / t_peak / 1e12, 1),
+                  "peak_note": "i8 peak for 4 of the 5 backward products, bf16 for dP = dO V^T",
+                  "ops_per_launch": bwd_ops},
+        traffic_key="sbwd_dkdv_kernel", cpu=cpu_baseline_sagebwd)
+
+
+CASES = {"c2": _sage_case, "c3": _sagebwd_case, "c4": _qat_case, "c5": _thrift_case, "c5d": _decode_case}
 
 
 def main():
@@ -358,10 +419,16 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    timed_bwd = case.get("timed") == "backward"
     for i in range(args.steps):
         path.quantize()
+        if timed_bwd:
+            path.forward()
         ev[i][0].record(stream)
-        path.forward()
+        if timed_bwd:
+            path.backward()
+        else:
+            path.forward()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0

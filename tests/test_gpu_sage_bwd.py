@@ -52,3 +52,35 @@ def test_sage_backward_small(N):
         ref = _oracle_grads(oc, Q, V, dO, h, True)
         for name, gi, ri in zip(("dQ", "dK", "dV"), g, ref):
             compare_outputs(gi[0, h], ri, "bf16", what=f"{name}[h={h}]")
+
+
+@pytest.mark.slow
+def test_sage_backward_full_size_sampled():
+    """Full c3 shape (B=1, H=16, N=8192, causal): the GPU runs the whole
+    training step; the oracle runs its forward of one head and the backward
+    of sampled tiles (dQ of the first and last query tiles, dK and dV of the
+    first and last key tiles)."""
+    w = wl.WORKLOADS["c3"]
+    p, step, (Q, K, V, dO) = _run(w)
+    h = 11
+    oc = SageOracle(Q[:, h:h + 1], K[:, h:h + 1], V[:, h:h + 1], q_block=128, eps=1e-3, pv="i8")
+    g = [t.float().cpu().numpy()[0, h] for t in (step.dq, step.dk, step.dv)]
+    nqt, nkt = w.Nq // 128, w.Nk // 64
+    for qt, kt in ((0, nkt - 1), (nqt - 1, 0)):
+        dQ, dK, dV = _oracle_grads(oc, Q[:, h:h + 1], V[:, h:h + 1], dO[:, h:h + 1], 0, True, qtiles=(qt, qt + 1),
+                                   ktiles=(kt, kt + 1))
+        compare_outputs(g[0][128 * qt:128 * qt + 128], dQ, "bf16", what=f"dQ tile {qt}")
+        compare_outputs(g[1][64 * kt:64 * kt + 64], dK, "bf16", what=f"dK tile {kt}")
+        compare_outputs(g[2][64 * kt:64 * kt + 64], dV, "bf16", what=f"dV tile {kt}")
+
+
+def test_sage_backward_n2048_two_heads():
+    """The c3 comparison length (B=1, H=16, N=2048), two heads checked whole."""
+    w = wl.with_len(wl.WORKLOADS["c3"], 2048)
+    p, step, (Q, K, V, dO) = _run(w)
+    g = [t.float().cpu().numpy() for t in (step.dq, step.dk, step.dv)]
+    for h in (0, 15):
+        oc = SageOracle(Q[:, h:h + 1], K[:, h:h + 1], V[:, h:h + 1], q_block=128, eps=1e-3, pv="i8")
+        ref = _oracle_grads(oc, Q[:, h:h + 1], V[:, h:h + 1], dO[:, h:h + 1], 0, True)
+        for name, gi, ri in zip(("dQ", "dK", "dV"), g, ref):
+            compare_outputs(gi[0, h], ri, "bf16", what=f"{name}[h={h}]")
