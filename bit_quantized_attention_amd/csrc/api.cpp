@@ -126,6 +126,7 @@ size_t bqa_workspace_size(const bqa_problem* p, int32_t op) {
             return 0;
         case BQA_OP_BWD:
             if (is_sage(p->mode) && p->Nq == p->Nk) return ws_sage_bwd_bytes(p->B, p->Hq, p->Nq, p->d);
+            if (p->mode == BQA_QAT_MXFP4 && p->Nq == p->Nk) return ws_qat_bwd_bytes(p->B, p->Hq, p->Nq, p->d);
             return 0;
         case BQA_OP_FWD:
             if (p->mode == BQA_QAT_MXFP4) return ws_qat_fwd_bytes(p->B, p->Hkv, p->Nk, p->d);
@@ -349,6 +350,33 @@ bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
         a.c_log2 = a.tau * 1.4426950408889634f;
         TRY(check_device());
         return launched(launch_sage_bwd(a, as_dense(o_for_delta), ws, st));
+    }
+    if (p->mode == BQA_QAT_MXFP4) {
+        if (p->d != 128 || p->Hq != p->Hkv || p->Nq != p->Nk || p->Nq % 128 != 0 || p->causal)
+            return BQA_E_UNSUPPORTED;
+        TRY(check_q(q, BQA_MXFP4, 0));
+        TRY(check_q(k, BQA_MXFP4, 0));
+        TRY(check_q(v, BQA_MXFP4, 1));
+        if (q->block != 32 || k->block != 32 || v->block != 32) return BQA_E_UNSUPPORTED;
+        TRY(check_dense(o_for_delta, false, true));
+        TRY(check_dense(d_o, false, true));
+        TRY(check_dense(dq, false, true));
+        TRY(check_dense(dk, false, true));
+        TRY(check_dense(dv, false, true));
+        if (!lse) return BQA_E_NULL;
+        if (!ws || ws_bytes < ws_qat_bwd_bytes(p->B, p->Hq, p->Nq, p->d)) return BQA_E_WORKSPACE;
+        if (!aligned16(ws)) return BQA_E_ALIGN;
+        QatBwdArgs a{};
+        a.qc = (const uint8_t*)q->codes; a.qs = (const uint8_t*)q->scales;
+        a.kc = (const uint8_t*)k->codes; a.ks = (const uint8_t*)k->scales;
+        a.vc = (const uint8_t*)v->codes; a.vs = (const uint8_t*)v->scales;
+        a.d_o = as_dense(d_o); a.lse = lse;
+        a.dq = as_dense(dq); a.dk = as_dense(dk); a.dv = as_dense(dv);
+        a.B = p->B; a.H = p->Hq; a.N = p->Nq;
+        a.tau = tau_of(p);
+        a.c_log2 = a.tau * 1.4426950408889634f;
+        TRY(check_device());
+        return launched(launch_qat_bwd(a, as_dense(o_for_delta), ws, st));
     }
     return BQA_E_UNSUPPORTED;
 }

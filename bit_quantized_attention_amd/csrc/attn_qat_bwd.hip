@@ -1,0 +1,389 @@
+// attn_qat_bwd.hip — Attn-QAT backward for gfx950.
+//
+// "Attn-QAT: 4-Bit Attention With Quantization-Aware Training", technical
+// summary §2 Principles 1 and 2: the backward recomputes P at the forward's
+// precision (the same MXFP4 scores, P = exp(s - L); for dV = P^T dO the
+// forward's own rounded P: rounded relative to a power-of-two reference,
+// whose MXFP4 codes are the forward's, then scaled to exp(s - L)), keeps
+// the straight-through
+// softmax Jacobian dS = P o (dP - delta') with the unquantised P, and takes
+// delta' = rowsum(dO o O') from the forward's high-precision auxiliary
+// output.  dP = dO V^T, dQ = tau dS K and dK = tau dS^T Q run as bf16
+// products against the FP4 operands (e2m1 times a power of two is exact in
+// bf16); dS is rounded to bf16 for them.  dV = P^T dO runs in fp16: the
+// rounded P times its row's exp(m - L) is not a bf16 value, and fp16 keeps
+// it to 2^-11 while holding dO exactly.
+//
+// Kernels:
+//   qat_delta_kernel   delta' per query row
+//   deq_t_kernel       bf16 copies in the layouts the products read:
+//                      deq(V) token-major, deq(Q)^T, deq(K)^T and dO^T
+//                      channel-major
+//   qbwd_dkdv_kernel   one workgroup per 64-key block over the 128-query
+//                      tiles: the tile is computed with queries in lanes
+//                      (P's MX blocks lie along a lane's registers), P^ and
+//                      dS go to LDS transposed for dV = P^T dO, dK = dS^T Q
+//   qbwd_dq_kernel     one workgroup per 128-query tile over the key tiles:
+//                      dS is the A operand of dQ = dS K from registers
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace bqa {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int TQ = 128;
+constexpr int TK = 64;
+
+__device__ __forceinline__ int sigma(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+__device__ __forceinline__ int fs64(int r) { return ((r >> 2) & 3) ^ (((r >> 4) & 1) << 1); }
+__device__ __forceinline__ int fs256(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
+__device__ __forceinline__ int fc128(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int fc256(int r) { return r & 15; }
+
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
+// ------------------------------------------------------------------ preprocess
+__global__ __launch_bounds__(256) void qat_delta_kernel(Dense dO, Dense Oa, int H, int N, int64_t rows,
+                                                        float* __restrict__ delta) {
+    // delta'_i = sum_c dO[i, c] O'[i, c]; one row per 16 lanes, 8 channels each
+    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+    const int part = threadIdx.x & 15;
+    float acc = 0.0f;
+    if (row < rows) {
+        const int64_t bh = row / N, i = row % N, b = bh / H, h = bh % H;
+        const v4i gv = *(const v4i*)((const uint16_t*)dO.p + b * dO.sB + h * dO.sH + i * dO.sN + 8 * part);
+        const v4i ov = *(const v4i*)((const uint16_t*)Oa.p + b * Oa.sB + h * Oa.sH + i * Oa.sN + 8 * part);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc = __builtin_fmaf(bf16_bits_to_f32((uint16_t)gv[k]), bf16_bits_to_f32((uint16_t)ov[k]), acc);
+            acc = __builtin_fmaf(bf16_bits_to_f32((uint16_t)((uint32_t)gv[k] >> 16)),
+                                 bf16_bits_to_f32((uint16_t)((uint32_t)ov[k] >> 16)), acc);
+        }
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 16);
+    if (row < rows && part == 0) delta[row] = acc;
+}
+
+// Element (r, c) of a [BH][R][C] grid, as bf16 bits, and the transpose
+// writer: out[bh][c][r].  SRC 0: MXFP4 codes along C (rows of C/2 bytes,
+// E8M0 per 32 of C), written as bf16 (exact); SRC 1: dense bf16
+// [B][H][R][C] view, written as fp16 (exact for the normal fp16 range).
+template <int SRC>
+__global__ __launch_bounds__(256) void deq_t_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sc,
+                                                    Dense dense, int H, int R, int C, uint16_t* __restrict__ out) {
+    __shared__ uint16_t t[64][66];
+    const int tilesR = R / 64, tilesC = C / 64;
+    int blk = blockIdx.x;
+    const int tc = blk % tilesC; blk /= tilesC;
+    const int tr = blk % tilesR;
+    const int64_t bh = blk / tilesR;
+    for (int e = threadIdx.x; e < 64 * 32; e += 256) {      // two elements per step
+        const int r = e >> 5, c2 = e & 31;
+        const int64_t rr = (int64_t)tr * 64 + r, cc = (int64_t)tc * 64 + 2 * c2;
+        uint16_t v0, v1;
+        if constexpr (SRC == 0) {
+            const uint8_t byte = codes[(bh * R + rr) * (C / 2) + cc / 2];
+            const int ex = (int)sc[(bh * R + rr) * (C / 32) + cc / 32] - 127;
+            v0 = f32_to_bf16_bits(__builtin_ldexpf(dec_e2m1(byte & 0xF), ex));
+            v1 = f32_to_bf16_bits(__builtin_ldexpf(dec_e2m1(byte >> 4), ex));
+        } else {
+            const int64_t b = bh / H, h = bh % H;
+            const uint32_t pr = *(const uint32_t*)((const uint16_t*)dense.p + b * dense.sB + h * dense.sH +
+                                                   rr * dense.sN + cc);
+            v0 = f32_to_f16_bits(bf16_bits_to_f32((uint16_t)pr));
+            v1 = f32_to_f16_bits(bf16_bits_to_f32((uint16_t)(pr >> 16)));
+        }
+        t[r][2 * c2] = v0;
+        t[r][2 * c2 + 1] = v1;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 32; e += 256) {
+        const int c = e >> 5, r2 = e & 31;
+        const uint32_t pr = (uint32_t)t[2 * r2][c] | ((uint32_t)t[2 * r2 + 1][c] << 16);
+        *(uint32_t*)(out + (bh * C + (int64_t)tc * 64 + c) * R + (int64_t)tr * 64 + 2 * r2) = pr;
+    }
+}
+
+// ------------------------------------------------------------------ the tile (queries in lanes)
+// For one wavefront: 32 queries (lanes) x 64 keys of block J.  Inputs: K codes
+// and scales of the block and deq(V) rows of the block in LDS (sigma reads);
+// the lane's query codes, dO row (bf16), L (log2 units) and delta'.
+// Outputs per lane: p[g][i], ds[g][i] for key 32 g + 16 h + i.
+struct KeyTile {
+    uint8_t kc[TK * D / 2];     // 64 keys x 64 B
+    uint8_t ks[TK * D / 32];    // 64 keys x 4
+    uint8_t vr[TK * D * 2];     // deq(V) rows, 64 keys x 256 B
+};
+
+__device__ __forceinline__ void key_tile_issue(const QatBwdArgs& a, int bh, int J, KeyTile& T, int w, int l) {
+    const int k0 = J * TK;
+    {   // K codes: 4 x 1 KB (16 rows of 64 B)
+        const int r = 16 * w + (l >> 2);
+        dma16(a.kc + ((int64_t)bh * a.N + k0 + r) * (D / 2) + 16 * ((l & 3) ^ fs64(r)), T.kc + 1024 * w);
+    }
+    if (w == 0) dma4(a.ks + ((int64_t)bh * a.N + k0 + l) * (D / 32), T.ks);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {   // deq(V) rows: 16 x 1 KB (4 rows of 256 B)
+        const int sgm = 4 * w + u, r = 4 * sgm + (l >> 4);
+        dma16(a.vdeq + ((int64_t)bh * a.N + k0 + r) * D + 8 * ((l & 15) ^ fs256(r)), T.vr + 1024 * sgm);
+    }
+}
+
+struct RowIn {
+    v4i qb[2];
+    int qsb[2];
+    v8bf gb[8];
+    float lse2, dlt;
+};
+
+__device__ __forceinline__ void row_load(const QatBwdArgs& a, int bh, int b, int hq, int qrow, int h, RowIn& r) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        r.qb[kk] = *(const v4i*)(a.qc + ((int64_t)bh * a.N + qrow) * (D / 2) + 32 * kk + 16 * h);
+        r.qsb[kk] = a.qs[((int64_t)bh * a.N + qrow) * (D / 32) + 2 * kk + h];
+    }
+    const uint16_t* g = (const uint16_t*)a.d_o.p + b * a.d_o.sB + hq * a.d_o.sH + (int64_t)qrow * a.d_o.sN;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) r.gb[st] = *(const v8bf*)(g + 16 * st + 8 * h);
+    r.lse2 = a.lse[(int64_t)bh * a.N + qrow] * 1.4426950408889634f;
+    r.dlt = a.delta[(int64_t)bh * a.N + qrow];
+}
+
+// P (unrounded), its MXFP4 fake quantisation (as float) and dS (bf16-rounded) for the tile
+__device__ __forceinline__ void tile_pds(const KeyTile& T, const RowIn& r, float c, int krow, int h, float (&p)[2][16],
+                                         float (&pq)[2][16], float (&ds)[2][16]) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int rk = 32 * g + krow;
+        v16f s = v16f{};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const v4i av = *(const v4i*)(T.kc + rk * 64 + 16 * ((2 * kk + h) ^ fs64(rk)));
+            s = mfma_f4_32x32x64(av, (int)T.ks[4 * rk + 2 * kk + h], r.qb[kk], r.qsb[kk], s);
+        }
+        v16f dp = v16f{};
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const v8bf av = *(const v8bf*)(T.vr + rk * 256 + 16 * ((2 * st + h) ^ fs256(rk)));
+            dp = mfma_bf16_32x32x16(av, r.gb[st], dp);
+        }
+        // P relative to m2 = ceil(L) (log2 units), a power of two: its MXFP4
+        // codes are the forward's; exp2(m2 - L) brings both to P = exp(s - L)
+        const float m2 = __builtin_ceilf(r.lse2);
+        const float back = __builtin_amdgcn_exp2f(m2 - r.lse2);
+        float pr[16];
+        float smax = s[0];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m2));
+            p[g][i] = pr[i] * back;
+            smax = __builtin_fmaxf(smax, s[i]);
+            ds[g][i] = (float)(__bf16)(p[g][i] * (dp[i] - r.dlt));
+        }
+        // MX block g of the row: 16 keys here, 16 in the partner lane
+        smax = __builtin_fmaxf(smax, partner32f(smax));
+        const int e = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(smax, c, -m2)));
+        const float sc = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pr[i], pr[i + 1], sc, 0);
+            const v2f dq = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, sc, 0);
+            pq[g][i] = dq[0] * back;
+            pq[g][i + 1] = dq[1] * back;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ dK, dV
+struct LdsKVq {
+    KeyTile kt;                  // fixed: the workgroup's key block
+    uint8_t pt[TK * TQ * 2];     // P^ transposed: 64 keys x 128 queries fp16 (chunks XOR key % 16)
+    uint8_t st[TK * TQ * 2];     // dS transposed
+    uint8_t gT[D * TQ * 2];      // dO^T: 128 channels x 128 queries fp16
+    uint8_t qT[D * TQ * 2];      // deq(Q)^T
+};
+
+__global__ __launch_bounds__(256, 1) void qbwd_dkdv_kernel(QatBwdArgs a) {
+    __shared__ __attribute__((aligned(16))) LdsKVq L;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
+    const int nkt = a.N / TK, nqt = a.N / TQ;
+    const int J = blockIdx.x % nkt;
+    const int bh = blockIdx.x / nkt, b = bh / a.H, hq = bh % a.H;
+    const int krow = sigma(lq);
+    const float c = a.c_log2;
+    // output tiles of this wavefront: keys 32 (w & 1) .., channels 64 (w >> 1) + 32 t ..
+    const int ko = 32 * (w & 1), co = 64 * (w >> 1);
+
+    key_tile_issue(a, bh, J, L.kt, w, l);
+    v16f dv[2], dk[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) { dv[t] = v16f{}; dk[t] = v16f{}; }
+
+    for (int I = 0; I < nqt; ++I) {
+        // channel-major dO and deq(Q) of the query tile: 32 + 32 KB, 8 + 8 copies per wavefront
+        const int q0 = I * TQ;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int sgm = 8 * w + u, r = 4 * sgm + (l >> 4);
+            const int cc = (l & 15) ^ fc256(r);
+            dma16(a.doT + ((int64_t)bh * D + r) * a.N + q0 + 8 * cc, L.gT + 1024 * sgm);
+            dma16(a.qT + ((int64_t)bh * D + r) * a.N + q0 + 8 * cc, L.qT + 1024 * sgm);
+        }
+        RowIn rin;
+        const int qrow = q0 + 32 * w + lq;
+        row_load(a, bh, b, hq, qrow, h, rin);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();                       // key tile (first pass) and this tile's copies have landed
+        float p[2][16], pq[2][16], ds[2][16];
+        tile_pds(L.kt, rin, c, krow, h, p, pq, ds);
+        // P^ and dS to LDS as [key][query] bf16
+        const int qc = 32 * w + lq;
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = 32 * g + 16 * h + i;
+                const int off = key * 256 + 16 * ((qc >> 3) ^ (key & 15)) + 2 * (qc & 7);
+                *(uint16_t*)(L.pt + off) = f32_to_f16_bits(pq[g][i]);
+                *(uint16_t*)(L.st + off) = f32_to_bf16_bits(ds[g][i]);
+            }
+        __syncthreads();
+        // dV += P^T dO, dK += dS^T deq(Q): K-steps of 16 queries
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ch = co + 32 * t + lq;
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+                const int key = ko + lq;
+                const int pc = 16 * ((2 * st + h) ^ (key & 15));
+                const v8h ap = *(const v8h*)(L.pt + key * 256 + pc);
+                const v8bf as = *(const v8bf*)(L.st + key * 256 + pc);
+                const int cq = 2 * st + h;                // 16-byte chunk of 8 queries
+                const v8h bg = *(const v8h*)(L.gT + ch * 256 + 16 * (cq ^ fc256(ch)));
+                const v8bf bq = *(const v8bf*)(L.qT + ch * 256 + 16 * (cq ^ fc256(ch)));
+                dv[t] = mfma_f16_32x32x16(ap, bg, dv[t]);
+                dk[t] = mfma_bf16_32x32x16(as, bq, dk[t]);
+            }
+        }
+        __syncthreads();                       // LDS tiles free for the next query tile
+    }
+    // dv[t] reg i: key ko + 8 (i / 4) + 4 h + i % 4, channel co + 32 t + lq
+    uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sB + hq * a.dv.sH;
+    uint16_t* dkp = (uint16_t*)a.dk.p + b * a.dk.sB + hq * a.dk.sH;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t kpos = (int64_t)J * TK + ko + 8 * (i >> 2) + 4 * h + (i & 3);
+            const int ch = co + 32 * t + lq;
+            dvp[kpos * a.dv.sN + ch] = f32_to_bf16_bits(dv[t][i]);
+            dkp[kpos * a.dk.sN + ch] = f32_to_bf16_bits(dk[t][i] * a.tau);
+        }
+}
+
+// ------------------------------------------------------------------ dQ
+struct LdsQq {
+    KeyTile kt;
+    uint8_t kT[D * TK * 2];      // deq(K)^T: 128 channels x 64 keys bf16
+};
+
+__device__ __forceinline__ void dq_issue(const QatBwdArgs& a, int bh, int J, LdsQq& T, int w, int l) {
+    key_tile_issue(a, bh, J, T.kt, w, l);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {   // deq(K)^T: 16 x 1 KB (8 rows of 128 B)
+        const int sgm = 4 * w + u, r = 8 * sgm + (l >> 3);
+        dma16(a.kT + ((int64_t)bh * D + r) * a.N + J * TK + 8 * ((l & 7) ^ fc128(r)), T.kT + 1024 * sgm);
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void qbwd_dq_kernel(QatBwdArgs a) {
+    __shared__ __attribute__((aligned(16))) LdsQq L[2];
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
+    const int nkt = a.N / TK, nqt = a.N / TQ;
+    const int I = blockIdx.x % nqt;
+    const int bh = blockIdx.x / nqt, b = bh / a.H, hq = bh % a.H;
+    const int qrow = I * TQ + 32 * w + lq;
+    const int krow = sigma(lq);
+    const float c = a.c_log2;
+    RowIn rin;
+    row_load(a, bh, b, hq, qrow, h, rin);
+    v16f dq[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) dq[cb] = v16f{};
+    dq_issue(a, bh, 0, L[0], w, l);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int J = 0; J < nkt; ++J) {
+        const int cur = J & 1;
+        if (J + 1 < nkt) dq_issue(a, bh, J + 1, L[cur ^ 1], w, l);
+        const LdsQq& T = L[cur];
+        float p[2][16], pq[2][16], ds[2][16];
+        tile_pds(T.kt, rin, c, krow, h, p, pq, ds);
+        // dQ += dS deq(K): step st takes keys 32 (st / 2) + 16 h + 8 (st % 2) + e
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            v8bf ab;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ab[e] = (__bf16)ds[st >> 1][8 * (st & 1) + e];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const int rr = 32 * cb + lq;
+                const int ck = 4 * (st >> 1) + 2 * h + (st & 1);
+                const v8bf bk = *(const v8bf*)(T.kT + rr * 128 + 16 * (ck ^ fc128(rr)));
+                dq[cb] = mfma_bf16_32x32x16(ab, bk, dq[cb]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    // dq[cb] reg i: query 32 w + 8 (i / 4) + 4 h + i % 4, channel 32 cb + lq
+    uint16_t* dqp = (uint16_t*)a.dq.p + b * a.dq.sB + hq * a.dq.sH;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t qr = (int64_t)I * TQ + 32 * w + 8 * (i >> 2) + 4 * h + (i & 3);
+            dqp[qr * a.dq.sN + 32 * cb + lq] = f32_to_bf16_bits(dq[cb][i] * a.tau);
+        }
+}
+
+}  // namespace
+
+size_t ws_qat_bwd_bytes(int B, int H, int N, int d) {
+    const size_t bhn = (size_t)B * H * N;
+    return bhn * 4 + 4 * bhn * d * 2 + 256;   // delta', deq(V), deq(Q)^T, deq(K)^T, dO^T
+}
+
+hipError_t launch_qat_bwd(QatBwdArgs a, Dense o_aux, void* ws, hipStream_t st) {
+    const int64_t bhn = (int64_t)a.B * a.H * a.N;
+    uint8_t* p = (uint8_t*)ws;
+    float* delta = (float*)p;          p += bhn * 4;
+    uint16_t* vdeq = (uint16_t*)p;     p += bhn * D * 2;
+    uint16_t* qT = (uint16_t*)p;       p += bhn * D * 2;
+    uint16_t* kT = (uint16_t*)p;       p += bhn * D * 2;
+    uint16_t* doT = (uint16_t*)p;
+    a.delta = delta; a.vdeq = vdeq; a.qT = qT; a.kT = kT; a.doT = doT;
+
+    qat_delta_kernel<<<(unsigned)((bhn * 16 + 255) / 256), 256, 0, st>>>(a.d_o, o_aux, a.H, a.N, bhn, delta);
+    const unsigned tg = (unsigned)((int64_t)a.B * a.H * (a.N / 64) * (D / 64));
+    // V codes are channel-major [d][N/2]: transposing the (channel, token) grid gives token-major rows
+    deq_t_kernel<0><<<tg, 256, 0, st>>>(a.vc, a.vs, Dense{}, a.H, D, a.N, vdeq);
+    deq_t_kernel<0><<<tg, 256, 0, st>>>(a.qc, a.qs, Dense{}, a.H, a.N, D, qT);
+    deq_t_kernel<0><<<tg, 256, 0, st>>>(a.kc, a.ks, Dense{}, a.H, a.N, D, kT);
+    deq_t_kernel<1><<<tg, 256, 0, st>>>(nullptr, nullptr, a.d_o, a.H, a.N, D, doT);
+    qbwd_dkdv_kernel<<<a.B * a.H * (a.N / TK), 256, 0, st>>>(a);
+    qbwd_dq_kernel<<<a.B * a.H * (a.N / TQ), 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace bqa

@@ -68,6 +68,22 @@ struct SageBwdArgs {
 size_t ws_sage_bwd_bytes(int B, int H, int N, int d);
 hipError_t launch_sage_bwd(SageBwdArgs a, Dense o, void* ws, hipStream_t st);
 
+// ---- Attn-QAT backward (attn_qat_bwd.hip); d = 128, Hq == Hkv, N a multiple of 128, non-causal
+struct QatBwdArgs {
+    const uint8_t* qc; const uint8_t* qs;                // MXFP4 Q [B,H,N,d/2], E8M0 [B,H,N,d/32]
+    const uint8_t* kc; const uint8_t* ks;                // MXFP4 K
+    const uint8_t* vc; const uint8_t* vs;                // MXFP4 V [B,H,d,N/2], E8M0 [B,H,d,N/32]
+    Dense d_o;                                           // dO bf16
+    const float* lse;                                    // forward log-sum-exp
+    float* delta;                                        // workspace: delta' [B,H,N]
+    uint16_t* vdeq; uint16_t* qT; uint16_t* kT; uint16_t* doT;   // workspace: bf16 copies
+    Dense dq, dk, dv;
+    int B, H, N;
+    float c_log2, tau;
+};
+size_t ws_qat_bwd_bytes(int B, int H, int N, int d);
+hipError_t launch_qat_bwd(QatBwdArgs a, Dense o_aux, void* ws, hipStream_t st);
+
 // ---- ThriftAttention mixed prefill (attn_thrift.hip); head dimension 128, 128-token blocks
 struct ThriftFwdArgs {
     const uint8_t* qc; const uint8_t* qs;                // MXFP4 Q [B,Hq,Nq,d/2], E8M0 [B,Hq,Nq,d/32]

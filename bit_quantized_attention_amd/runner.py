@@ -139,6 +139,32 @@ class QatPath:
         return self.o
 
 
+class QatTrainStep(QatPath):
+    """Attn-QAT training step: the FP4 forward with O', then the backward
+    (P recomputed from the same MXFP4 scores and fake-quantised for dV,
+    delta' = rowsum(dO o O'), bf16 products against the FP4 operands)."""
+
+    def __init__(self, p, q, k, v, d_o):
+        super().__init__(p, q, k, v, aux=True)
+        dev = q.device
+        self.d_o = d_o
+        self.dq = torch.empty_like(q)
+        self.dk = torch.empty_like(k)
+        self.dv = torch.empty_like(v)
+        self.ws_bwd = torch.empty(max(bqa_workspace_size(p, BQA_OP_BWD), 16), dtype=torch.uint8, device=dev)
+        self._dod = dense(d_o)
+
+    def backward(self):
+        bqa_attn_bwd(self.p, q=self.qq, k=self.kq, v=self.vq, o_for_delta=self._oad, lse=self.lse, d_o=self._dod,
+                     dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws_bwd)
+
+    def step(self):
+        self.quantize()
+        self.forward()
+        self.backward()
+        return self.dq, self.dk, self.dv
+
+
 def thrift_problem(B, Hq, Hkv, Nq, Nk, d, budget_ppm=50_000, causal=True, num_splits=0, sm_scale=0.0):
     return problem(B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d, causal=int(causal), sm_scale=sm_scale, mode=BQA_THRIFT,
                    sel_block=128, hp_budget_ppm=budget_ppm, num_splits=num_splits)

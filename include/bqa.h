@@ -224,15 +224,21 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
 /*
  * Attention backward: dq, dk, dv [B, H, N, d] bf16 from the forward's codes,
  * its lse and d_o.
- *  - BQA_SAGE_I8_I8PV ("SageBwd", Methodology 2, Limitations): delta =
+ *  - Sage modes ("SageBwd", Methodology 2, Limitations): d = 128,
+ *    Hq == Hkv, Nq == Nk a multiple of 128, q_block 128, k_block 64.  delta =
  *    rowsum(dO o O) with o_for_delta = the forward's O; dO is quantized to
- *    INT8 per q_block tokens; tiles of 128 queries x 64 keys; P and dS are
+ *    INT8 per 128 tokens; tiles of 128 queries x 64 keys; P and dS are
  *    INT8 with one scale per tile; dV = P^T dO, dQ = tau dS K and
- *    dK = tau dS^T Q run as INT8 products, dP = dO V^T in bf16 from v_hi.
+ *    dK = tau dS^T Q run as INT8 products, dP = dO V^T in bf16 from v_hi
+ *    (bf16).  Workspace: bqa_workspace_size(p, BQA_OP_BWD) bytes.
  *  - BQA_QAT_MXFP4 ("Attn-QAT", §2 Principles 1 and 2): o_for_delta = O';
- *    P is recomputed from the same FP4 scores and fake-quantised to MXFP4
- *    with the forward's blocking for dV; dP, dQ, dK run in bf16 against the
- *    FP4 operands; delta = rowsum(dO o O').
+ *    d = 128, Hq == Hkv, Nq == Nk a multiple of 128, non-causal.  P is
+ *    recomputed from the same FP4 scores; for dV it is rounded exactly as the
+ *    forward rounded it (MXFP4 per 32 keys relative to a power-of-two
+ *    reference, then scaled to exp(s - L)); dS = P o (dP - delta) uses the
+ *    unrounded P and is rounded to bf16; dP, dQ, dK run in bf16 against the
+ *    FP4 operands; delta = rowsum(dO o O').  Workspace:
+ *    bqa_workspace_size(p, BQA_OP_BWD) bytes.
  */
 bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
                         const bqa_qtensor* v, const bqa_tensor* v_hi,

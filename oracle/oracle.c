@@ -738,8 +738,12 @@ void orc_qat_fwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const 
 }
 
 /* Attn-QAT backward ([AQ] §2 Principles 1 and 2): P = exp(s - L) recomputed
- * from the same exact MX scores, fake-quantised to MXFP4 with the forward's
- * blocking for dV = P^T dO; dP = dO V^T against the FP4 V;
+ * from the same exact MX scores.  For dV = P^ dO the recomputation matches
+ * the forward's precision: the forward rounded P relative to a reference
+ * that is a power of two (MXFP4 codes do not change under such a factor), so
+ * the backward rounds exp(s - m*), m* = ln2 ceil(L / ln2), per 32 keys and
+ * scales the result by exp(m* - L) -- exactly the forward's P^ divided by its
+ * row sum.  dP = dO V^T against the FP4 V;
  * dS = P o (dP - delta') with delta' = rowsum(dO o O') (the straight-through
  * estimator keeps the unquantised P in the softmax Jacobian); dS is rounded
  * to bf16 where the products take bf16 operands; dQ = tau dS K, dK = tau
@@ -763,6 +767,7 @@ void orc_qat_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const 
     int ra = need_all ? 0 : q0, rb = need_all ? Nq : q1;
 #pragma omp parallel
     {
+        const double ln2 = 0.69314718055994530942;
         double* p = (double*)malloc(sizeof(double) * (size_t)Nk);
         double* pq = (double*)malloc(sizeof(double) * (size_t)Nk);
         double* ds = (double*)malloc(sizeof(double) * (size_t)Nk);
@@ -772,13 +777,18 @@ void orc_qat_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const 
         for (int i = ra; i < rb; ++i) {
             int want_q = (i >= q0 && i < q1);
             int ja = want_q ? 0 : (k0 / 32) * 32, jb = want_q ? Nk : ((k1 + 31) / 32) * 32;
+            const double mstar = ln2 * ceil((double)lse[i] / ln2);
             for (int j = ja; j < jb; ++j) {
                 double s;
                 orc_mx_scores(qc, qs, kc, ks, d, i, j, &s);
                 p[j] = exp(tau * s - (double)lse[i]);
-                pq[j] = p[j];
+                pq[j] = quantize_p ? exp(tau * s - mstar) : p[j];
             }
-            if (quantize_p) for (int j = ja; j < jb; j += 32) mx_fake32(pq + j, 32);
+            if (quantize_p) {
+                const double back = exp(mstar - (double)lse[i]);
+                for (int j = ja; j < jb; j += 32) mx_fake32(pq + j, 32);
+                for (int j = ja; j < jb; ++j) pq[j] *= back;
+            }
             for (int j = ja; j < jb; ++j) {
                 double dp = 0.0;
                 for (int c = 0; c < d; ++c) dp += (double)dO[(size_t)i * d + c] * vmx(vc_t, vs_t, Nk, j, c);

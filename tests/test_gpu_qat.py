@@ -113,3 +113,52 @@ def test_qat_forward_full_size_sampled():
     for h in (0, 13, 31):
         for r0 in (0, 8191, 16384 - 16):
             _check(path, oc, [(0, h)], rows=(r0, r0 + 16))
+
+
+def _train(w):
+    from bit_quantized_attention_amd.runner import QatTrainStep, qat_problem, to_device
+    Q, K, V, dO = (wl.build(w, t) for t in ("q", "k", "v", "do"))
+    p = qat_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+    step = QatTrainStep(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"), to_device(dO, "bf16"))
+    step.step()
+    torch.cuda.synchronize()
+    return p, step, (Q, K, V, dO)
+
+
+def _qat_grads(oc, dO, h, qrows=None, krows=None):
+    """The oracle's own forward (O', log-sum-exp, stored as the GPU stores
+    them: bf16 and fp32), then its backward."""
+    _, Oa, lse = oc.forward(0, h)
+    return orc.qat_bwd(qc=oc.qc[h], qs=oc.qs[h], kc=oc.kc[h], ks=oc.ks[h], vc_t=oc.vc[h], vs_t=oc.vs[h],
+                       dO=dO[0, h], O_aux=orc.round_to(Oa, "bf16"), lse=lse.astype(np.float32), Nq=oc.Nq, Nk=oc.Nk,
+                       d=oc.d, tau=tau_for(oc.d), qrows=qrows, krows=krows)
+
+
+@pytest.mark.parametrize("N", [256, 1024])
+def test_qat_backward_small(N):
+    """Attn-QAT backward on the Student-t recipe: dQ, dK, dV against the
+    oracle's forward + backward on its own quantisation of the inputs."""
+    w = wl.with_len(wl.WORKLOADS["c4"], N, hq=2, hkv=2)
+    p, step, (Q, K, V, dO) = _train(w)
+    oc = _Oracle(Q, K, V)
+    g = [t.float().cpu().numpy() for t in (step.dq, step.dk, step.dv)]
+    for h in range(2):
+        ref = _qat_grads(oc, dO, h)
+        for name, gi, ri in zip(("dQ", "dK", "dV"), g, ref):
+            compare_outputs(gi[0, h], ri, "bf16", what=f"{name}[h={h}]")
+
+
+@pytest.mark.slow
+def test_qat_backward_full_size_sampled():
+    """Full c4 training shape (B=1, H=32, N=16384): the oracle checks sampled
+    query rows (dQ) and key rows (dK, dV) of one head."""
+    w = wl.WORKLOADS["c4"]
+    p, step, (Q, K, V, dO) = _train(w)
+    h = 21
+    oc = _Oracle(Q[:, h:h + 1], K[:, h:h + 1], V[:, h:h + 1])
+    g = [t.float().cpu().numpy()[0, h] for t in (step.dq, step.dk, step.dv)]
+    for r0 in (0, 16384 - 32):
+        dQ, dK, dV = _qat_grads(oc, dO[:, h:h + 1], 0, qrows=(r0, r0 + 32), krows=(r0, r0 + 32))
+        compare_outputs(g[0][r0:r0 + 32], dQ, "bf16", what=f"dQ rows {r0}")
+        compare_outputs(g[1][r0:r0 + 32], dK, "bf16", what=f"dK rows {r0}")
+        compare_outputs(g[2][r0:r0 + 32], dV, "bf16", what=f"dV rows {r0}")

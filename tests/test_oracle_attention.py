@@ -312,6 +312,31 @@ def test_qat_quantised_close_and_aux_identity(orc):
     assert np.allclose(sub[2], dV[32:64], rtol=1e-12, atol=1e-15)
 
 
+def test_qat_backward_reuses_forward_p(orc):
+    """Attn-QAT §2 Principle 1: the backward's rounded P is the forward's.
+    With dO one-hot on (row i, channel k), dV[:, k] is row i of the
+    backward's P^, and P^ V must give back the forward's O row exactly --
+    including peaked rows whose largest P sits at the MXFP4 exponent step."""
+    rng = np.random.default_rng(23)
+    N, d, tau = 128, 64, 1 / 8
+    X = [rng.standard_t(3, (N, d)).astype(np.float32) for _ in range(3)]
+    X[0][5] = X[1][77] * 4.0                     # row 5: one key dominates (largest P ~ 1)
+    qc, qs = orc.quant_mx_rows(X[0][None]); kc, ks = orc.quant_mx_rows(X[1][None]); vc, vs = orc.quant_mx_cols(X[2][None])
+    t = dict(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0])
+    O, Oa, lse = orc.qat_fwd(Nq=N, Nk=N, d=d, tau=tau, kv_tile=32, **t)
+    Vd = _mx_deq_rows(vc[0], vs[0]).T                  # [N keys, d]
+    for i in (5, 40, 101):
+        k = 3
+        dO = np.zeros((N, d), np.float32)
+        dO[i, k] = 1.0
+        _, _, dV = orc.qat_bwd(dO=dO, O_aux=Oa.astype(np.float32), lse=lse.astype(np.float32), Nq=N, Nk=N, d=d,
+                               tau=tau, **t)
+        prow = dV[:, k]
+        # the forward normalises by its own row sum; the backward by exp(L): equal up to L's fp32 storage
+        assert np.abs(prow @ Vd - O[i]).max() <= 1e-5 * np.abs(O[i]).max()
+    assert np.exp(tau * orc.mx_score(qc[0], qs[0], kc[0], ks[0], d, 5, 77)[0] - lse[5]) > 0.5
+
+
 def test_qat_one_hot_row_is_exact(orc):
     """A row whose scores put all the mass on one key: P^ is one-hot, so O is
     exactly proportional to that key's FP4 value row; the factor is
