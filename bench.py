@@ -12,6 +12,9 @@ Workloads (``--workload``, default c2):
   c4  Attn-QAT FP4 forward at B=1, H=32, N=16384, d=128, non-causal,
       Student-t inputs: MXFP4 Q, K, V, fused attention with MXFP4 P.V and
       the bf16 auxiliary output O'.
+  c4t the Attn-QAT training step on the same inputs: forward with O', then
+      the backward; `value` counts forward + backward, the roofline the
+      backward call.
   c5  ThriftAttention prefill at B=1, Hq=32, Hkv=8, N=131072, d=128,
       causal, low-rank inputs: MXFP4 Q, K, V with block means, block
       selection (5 %), mixed FP4 / bf16 attention.
@@ -29,7 +32,7 @@ time, measured with HIP events on the stream it runs on, against the dense
 matrix-core peak of its operand types.  `cpu_baseline` times the CPU oracle
 on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--workload c2|c3|c4|c5|c5d] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--workload c2|c3|c4|c4t|c5|c5d] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -373,7 +376,60 @@ def _sagebwd_case(w, bqa, torch):
         traffic_key="sbwd_dkdv_kernel", cpu=cpu_baseline_sagebwd)
 
 
-CASES = {"c2": _sage_case, "c3": _sagebwd_case, "c4": _qat_case, "c5": _thrift_case, "c5d": _decode_case}
+def cpu_baseline_qat_train(w, budget_s: float = 25.0):
+    """The oracle on a bounded sample of the Attn-QAT training step:
+    quantisation and the whole forward (O, O', log-sum-exp) of head (0,0),
+    then the backward for chunks of query rows (dQ) and key rows (dK, dV)
+    until the budget."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+    from tests.helpers import tau_for
+    oracle.lib()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    Q, K, V, dO = (wl.chunk(w, t, 0, 0) for t in ("q", "k", "v", "do"))
+    qc, qs = oracle.quant_mx_rows(Q[None]); kc, ks = oracle.quant_mx_rows(K[None]); vc, vs = oracle.quant_mx_cols(V[None])
+    t = dict(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0])
+    tau = tau_for(w.d)
+    _, Oa, lse = oracle.qat_fwd(Nq=w.Nq, Nk=w.Nk, d=w.d, tau=tau, kv_tile=64, **t)
+    ops = 6.0 * w.Nq * w.Nk * w.d                    # forward: QK^T, P.V and O'
+    r0 = 0
+    while r0 < w.Nq and time.perf_counter() - t0 < budget_s:
+        oracle.qat_bwd(dO=dO, O_aux=oracle.round_to(Oa, "bf16").astype(np.float32), lse=lse.astype(np.float32),
+                       Nq=w.Nq, Nk=w.Nk, d=w.d, tau=tau, qrows=(r0, r0 + 32), krows=(r0, r0 + 32), **t)
+        ops += 2.0 * 32 * w.Nk * w.d * 3 + 2.0 * 32 * w.Nq * w.d * 4      # dQ rows; dK, dV key rows
+        r0 += 32
+    dt = time.perf_counter() - t0
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"head (0,0) at N={w.Nk}: MXFP4 quantisation and the full forward with O', then the backward "
+                      f"of {r0} query rows (dQ) and {r0} key rows (dK, dV), {dt:.1f} s"}
+
+
+def _qat_train_case(w, bqa, torch):
+    from bit_quantized_attention_amd.runner import QatTrainStep, qat_problem, to_device
+    import workloads as wl
+    Q, K, V, dO = (wl.build(w, t) for t in ("q", "k", "v", "do"))
+    p = qat_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+    path = QatTrainStep(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"), to_device(dO, "bf16"))
+    n = w.B * w.Hq * w.Nq * w.Nk * w.d
+    bwd_f4, bwd_b16 = 2.0 * n, 8.0 * n          # S recompute in MXFP4; dP, dV, dQ, dK in 16-bit
+    t_peak = bwd_f4 / (PEAK_F4_TFLOPS * 1e12) + bwd_b16 / (PEAK_BF16_TFLOPS * 1e12)
+    return dict(
+        path=path, ops=14.0 * n, dtype="mxfp4+bf16", timed="backward",
+        workload="Attn-QAT training step (c4): B=1 H=32 N=16384 d=128 non-causal, Student-t bf16 in; MXFP4 forward "
+                 "with O', backward with P recomputed at the forward's precision and delta' = rowsum(dO o O'); "
+                 "step = quantise + forward + backward",
+        roofline={"bound": "mfma", "kernel": "attn_bwd QAT (delta', bf16 copies, qbwd_dkdv_kernel, qbwd_dq_kernel)",
+                  "peak": round((bwd_f4 + bwd_b16) / t_peak / 1e12, 1),
+                  "peak_note": "MXFP4 peak for the score recompute, bf16 (fp16 for dV) peak for the other four",
+                  "ops_per_launch": bwd_f4 + bwd_b16},
+        traffic_key="qbwd_dkdv_kernel", cpu=cpu_baseline_qat_train)
+
+
+CASES = {"c2": _sage_case, "c3": _sagebwd_case, "c4": _qat_case, "c4t": _qat_train_case, "c5": _thrift_case,
+         "c5d": _decode_case}
 
 
 def main():
@@ -408,7 +464,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": src.numel(), "launches": 5}))
         return
-    w = wl.WORKLOADS[args.workload]
+    w = wl.WORKLOADS[args.workload.rstrip("t")]
     case = CASES[args.workload](w, bqa, torch)
     path = case["path"]
     for _ in range(args.warmup):
