@@ -206,8 +206,11 @@ def build(w: Workload, tensor: str, workers: int = 0) -> np.ndarray:
 
 
 def default_workers() -> int:
-    """Generator processes for full-size inputs: the CPUs this process may use, at most 16."""
+    """Generator processes for full-size inputs: the CPUs this process may use,
+    at most 16 (BQA_GEN_WORKERS overrides, e.g. 1 under a profiler)."""
     import os
+    if os.environ.get("BQA_GEN_WORKERS"):
+        return max(1, int(os.environ["BQA_GEN_WORKERS"]))
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
