@@ -33,7 +33,7 @@ namespace {
 
 constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile (= INT8 K block)
-constexpr int NBUF = 3;   // LDS tiles in flight: QK(j+1), PV(j), staging of j+2
+constexpr int NBUF = 4;   // LDS tiles: P.V(j-1), softmax(j), QK(j+1), staging of j+2
 
 // XOR swizzle of the 16-byte chunks of a tile row (rows of ROW_BYTES).  For
 // the K tile (read through the row permutation below) and for the V^T tile
@@ -137,22 +137,31 @@ __device__ __forceinline__ void stage_store(const Staging<PV, D>& st, uint8_t* k
     }
 }
 
-// Per-wavefront running state of the online softmax.
+// Per-wavefront running state of the online softmax.  m is the oracle's
+// reference point (running row max rounded up to an integer, log2 units);
+// the accumulators and the row sum are kept in a frame m0 <= m.  For the
+// fp8 and int8 P.V products the factor 2^(m - m0) rides on the product
+// itself (the E8M0 operand scale of P, or the fp32 scale of the int32 tile),
+// so the accumulators are only rescaled when the frame falls more than
+// FRAME_GAP binades behind; for fp16 P the frame follows m exactly.
 template <int D>
 struct RowState {
     v16f oacc[D / 32];      // O^T accumulator: lane (query lq, half h), channel 32cb + 8(i/4) + 4h + i%4
-    float m;                // running max of the scaled scores (log2 units)
-    float l;                // this lane half's share of the row sum
+    float m;                // reference point (log2 units)
+    float m0;               // frame of oacc and l
+    float l;                // this lane half's share of the row sum, in the frame
 };
+constexpr float FRAME_GAP = 96.0f;
 
-// Online-softmax update with one 64-key tile (scores s0/s1 from qk_tile) and
-// its P.V product.  `diag_lim` >= 64 means no key of the tile is masked for
-// this wavefront; otherwise register i (+32) is visible iff i (+32) <= diag_lim.
+// Softmax of one 64-key tile: scores (int32, converted in place) -> P in
+// registers (f0: keys 16h + i, f1: keys 32 + 16h + i), reference and frame
+// updates, row sum.  Returns the row's largest P (int8 P.V needs it).
+// `diag_lim` >= 64 means no key of the tile is masked for this lane;
+// otherwise register i (+32) is visible iff i (+32) <= diag_lim.
 template <int PV, int D>
-__device__ __forceinline__ void tile_update(RowState<D>& st, const v16i& s0, const v16i& s1, float c, bool diag,
-                                            int diag_lim, const uint8_t* vt, int lq, int h) {
+__device__ __forceinline__ float tile_softmax(RowState<D>& st, const v16i& s0, const v16i& s1, float c, bool diag,
+                                              int diag_lim, float (&f0)[16], float (&f1)[16]) {
     constexpr float pbias = PV == PV_F8 ? 8.807354922057604f : 0.0f;    // log2(448): P scaled by 448
-    float f0[16], f1[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) { f0[i] = (float)s0[i]; f1[i] = (float)s1[i]; }
     if (diag) {
@@ -166,28 +175,56 @@ __device__ __forceinline__ void tile_update(RowState<D>& st, const v16i& s0, con
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, f0[i]), f1[i]);
     mx = __builtin_fmaxf(mx, partner32f(mx));
-    // reference point: the running max rounded up to an integer (log2 units),
-    // so rescaling factors are exact powers of two and rarely needed
     const float m_new = __builtin_fmaxf(st.m, __builtin_ceilf(mx * c));
-    const float alpha = st.m == -__builtin_inff() ? 0.0f : __builtin_ldexpf(1.0f, (int)(st.m - m_new));
+    if constexpr (PV == PV_F16) {
+        // fp16 P cannot carry the frame: rescale whenever the reference moves
+        if (__any(m_new != st.m0)) {
+            if (st.m0 != -__builtin_inff() && m_new != st.m0) {
+                const float f = __builtin_ldexpf(1.0f, (int)(st.m0 - m_new));
+                st.l *= f;
+#pragma unroll
+                for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) st.oacc[cb][i] *= f;
+            }
+            st.m0 = m_new;
+        }
+    } else {
+        if (__any(m_new - st.m0 > FRAME_GAP)) {
+            if (m_new - st.m0 > FRAME_GAP) {
+                if (st.m0 != -__builtin_inff()) {
+                    const float f = __builtin_ldexpf(1.0f, (int)(st.m0 - m_new));
+                    st.l *= f;
+#pragma unroll
+                    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) st.oacc[cb][i] *= f;
+                }
+                st.m0 = m_new;
+            }
+        }
+    }
+    st.m = m_new;
     const float bias = m_new == -__builtin_inff() ? 0.0f : pbias - m_new;
-    float psum0 = 0.0f, psum1 = 0.0f;
+    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         f0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(f0[i], c, bias));
         f1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(f1[i], c, bias));
-        psum0 += f0[i];
-        psum1 += f1[i];
+        ps[i & 1] += f0[i];
+        ps[2 + (i & 1)] += f1[i];
     }
-    const bool moved = m_new != st.m;
-    st.l = st.l * alpha + (psum0 + psum1);
-    st.m = m_new;
-    if (__any(moved)) {
-#pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) st.oacc[cb][i] *= alpha;
-    }
+    const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    // the row sum lives in the frame: times 2^(m - m0) (an exact power of two)
+    st.l += PV == PV_F16 ? psum : __builtin_ldexpf(psum, st.m0 == -__builtin_inff() ? 0 : (int)(m_new - st.m0));
+    return mx == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, bias));
+}
+
+// P.V of one tile into the frame-m0 accumulators (V^T tile in LDS).
+template <int PV, int D>
+__device__ __forceinline__ void tile_pv(RowState<D>& st, const float (&f0)[16], const float (&f1)[16], float pmax,
+                                        const uint8_t* vt, int lq, int h) {
+    const int shift = st.m0 == -__builtin_inff() ? 0 : (int)(st.m - st.m0);   // 0 .. FRAME_GAP
     if constexpr (PV == PV_F8) {
         v8i pb;
 #pragma unroll
@@ -197,20 +234,21 @@ __device__ __forceinline__ void tile_update(RowState<D>& st, const v16i& s0, con
             int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k], f1[4 * k + 1], 0, false);
             pb[4 + k] = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k + 2], f1[4 * k + 3], w1, true);
         }
+        const int sb = 127 + shift;     // E8M0 scale of P: the frame factor, exact
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb) {
             const int r = 32 * cb + lq;
             v4i lo = *(const v4i*)(vt + swz_v<BN>(r, h));
             v4i hi = *(const v4i*)(vt + swz_v<BN>(r, 2 + h));
             v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            st.oacc[cb] = mfma_f8_32x32x64(av, pb, st.oacc[cb]);
+            st.oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, st.oacc[cb], 0, 0, 0, 127, 0, sb);
         }
     } else if constexpr (PV == PV_I8) {
         // int8 P per (row, tile): r = the row's largest P in the tile
-        const float r = mx == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, bias));
+        const float r = pmax;
         float inv = r > 0.0f ? 127.0f / r : 0.0f;
         if (__builtin_isinf(inv)) inv = 0.0f;
-        const float rs = r * (1.0f / 127.0f);
+        const float rs = __builtin_ldexpf(r * (1.0f / 127.0f), shift);
         v4i pb0, pb1;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -234,6 +272,7 @@ __device__ __forceinline__ void tile_update(RowState<D>& st, const v16i& s0, con
             for (int i = 0; i < 16; ++i) st.oacc[cb][i] = __builtin_fmaf((float)pv[i], rs, st.oacc[cb][i]);
         }
     } else {
+        (void)shift;
         // fp16 P; four 16-key steps: keys 32(s/2) + 16h + 8(s%2) + e
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -246,6 +285,74 @@ __device__ __forceinline__ void tile_update(RowState<D>& st, const v16i& s0, con
                 v8h av = *(const v8h*)(vt + swz_v<128>(ch, 4 * (s / 2) + 2 * h + (s % 2)));
                 st.oacc[cb] = mfma_f16_32x32x16(av, pb, st.oacc[cb]);
             }
+        }
+    }
+}
+
+// P.V deferred by one iteration (the pipelined kernels): P packed into the
+// product's operand format plus its scale, issued while the next tile's
+// softmax runs on the vector ALUs.
+struct PvPend {
+    v8i pb;     // fp8: 32 e4m3 codes; int8: codes of keys 16h+i (0..3) and 32+16h+i (4..7)
+    float rs;   // int8: dequantisation scale of the row's tile (with the frame factor)
+    int sb;     // fp8: E8M0 scale (the frame factor)
+};
+
+template <int PV, int D>
+__device__ __forceinline__ void pv_prep(const RowState<D>& st, const float (&f0)[16], const float (&f1)[16],
+                                        float pmax, PvPend& pp) {
+    const int shift = st.m0 == -__builtin_inff() ? 0 : (int)(st.m - st.m0);
+    if constexpr (PV == PV_F8) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f0[4 * k], f0[4 * k + 1], 0, false);
+            pp.pb[k] = __builtin_amdgcn_cvt_pk_fp8_f32(f0[4 * k + 2], f0[4 * k + 3], w0, true);
+            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k], f1[4 * k + 1], 0, false);
+            pp.pb[4 + k] = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k + 2], f1[4 * k + 3], w1, true);
+        }
+        pp.sb = 127 + shift;
+        pp.rs = 0.0f;
+    } else {
+        float inv = pmax > 0.0f ? 127.0f / pmax : 0.0f;
+        if (__builtin_isinf(inv)) inv = 0.0f;
+        pp.rs = __builtin_ldexpf(pmax * (1.0f / 127.0f), shift);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                w0 |= (uint32_t)enc_i8(f0[4 * k + e], inv) << (8 * e);
+                w1 |= (uint32_t)enc_i8(f1[4 * k + e], inv) << (8 * e);
+            }
+            pp.pb[k] = (int)w0;
+            pp.pb[4 + k] = (int)w1;
+        }
+        pp.sb = 127;
+    }
+}
+
+template <int PV, int D>
+__device__ __forceinline__ void pv_issue(RowState<D>& st, const PvPend& pp, const uint8_t* vt, int lq, int h) {
+    if constexpr (PV == PV_F8) {
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) {
+            const int r = 32 * cb + lq;
+            v4i lo = *(const v4i*)(vt + swz_v<BN>(r, h));
+            v4i hi = *(const v4i*)(vt + swz_v<BN>(r, 2 + h));
+            v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            st.oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pp.pb, st.oacc[cb], 0, 0, 0, 127, 0, pp.sb);
+        }
+    } else {
+        const v4i pb0 = {pp.pb[0], pp.pb[1], pp.pb[2], pp.pb[3]}, pb1 = {pp.pb[4], pp.pb[5], pp.pb[6], pp.pb[7]};
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) {
+            const int rr = 32 * cb + lq;
+            v4i v0 = *(const v4i*)(vt + swz_v<BN>(rr, h));
+            v4i v1 = *(const v4i*)(vt + swz_v<BN>(rr, 2 + h));
+            v16i pv = mfma_i8_32x32x32(v0, pb0, v16i{});
+            pv = mfma_i8_32x32x32(v1, pb1, pv);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st.oacc[cb][i] = __builtin_fmaf((float)pv[i], pp.rs, st.oacc[cb][i]);
         }
     }
 }
@@ -290,39 +397,81 @@ __global__ __launch_bounds__(256, 2) void sage_fwd_kernel(SageFwdArgs a) {
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) rs.oacc[cb] = v16f{};
     rs.m = -__builtin_inff();
+    rs.m0 = -__builtin_inff();
     rs.l = 0.0f;
 
-    // prologue: tiles 0 and 1 in LDS, tile 2 in flight
+    // prologue: tiles 0 and 1 in LDS, tile 2 in flight, the scores of tile 0
     S st;
     if (n_tiles > 0) { stage_load<PV, D>(st, a, kbase, b, hk, bhk, 0, tid); stage_store<PV, D>(st, k_lds[0], v_lds[0], &ks_lds[0], tid); }
     if (n_tiles > 1) { stage_load<PV, D>(st, a, kbase, b, hk, bhk, BN, tid); stage_store<PV, D>(st, k_lds[1], v_lds[1], &ks_lds[1], tid); }
     __syncthreads();
     if (n_tiles > 2) stage_load<PV, D>(st, a, kbase, b, hk, bhk, 2 * BN, tid);
+    // The software pipeline holds two score tiles; the register budget allows
+    // it for the causal fp8 / int8 kernels (the benchmarked shapes), the other
+    // variants compute each tile's scores just before its softmax.
+    constexpr bool PIPE = CAUSAL && PV != PV_F16;
+    v16i sc[2][2];
+    if (PIPE && wave_tiles > 0) qk_tile<D>(k_lds[0], qb, krow, h, sc[0][0], sc[0][1]);
 
-    // One iteration: QK of tile j+1 into (n0, n1) is issued before the softmax
-    // and P.V of tile j (scores in (c0, c1)), so the matrix cores work on the
-    // next tile while the vector ALUs do this one.  Then tile j+2 goes from
-    // registers to LDS, a barrier, and tile j+3's loads are issued.
-    auto body = [&](int j, auto bufc) __attribute__((always_inline)) {
+    // Iteration j issues, on the matrix cores, P.V of tile j-1 (its P packed
+    // in registers from the previous iteration) and QK of tile j+1, while the
+    // vector ALUs run the softmax of tile j (scores from the previous
+    // iteration).  Then tile j+2 goes from registers to LDS, a barrier, and
+    // tile j+3's loads are issued.  Four LDS buffers: V(j-1), scale(j),
+    // K(j+1), tile j+2.  Unrolled by 4 so that the buffer (j % 4) and the
+    // score slot (j % 2) are compile-time.  The variants without the
+    // pipeline (fp16 P, non-causal) compute each tile in place.
+    PvPend pend;
+    bool have_pend = false;
+    auto body = [&](int j, auto bufc, auto slotc) __attribute__((always_inline)) {
         constexpr int B0 = decltype(bufc)::value;
+        constexpr int SL = decltype(slotc)::value;
+        if constexpr (PIPE) {
+            if (have_pend) pv_issue<PV, D>(rs, pend, v_lds[(B0 + NBUF - 1) % NBUF], lq, h);
+            have_pend = false;
+            if (j + 1 < wave_tiles) qk_tile<D>(k_lds[(B0 + 1) % NBUF], qb, krow, h, sc[SL ^ 1][0], sc[SL ^ 1][1]);
+        } else {
+            if (j < wave_tiles) qk_tile<D>(k_lds[B0], qb, krow, h, sc[SL][0], sc[SL][1]);
+        }
         if (j < wave_tiles) {
-            v16i x0, x1;
-            qk_tile<D>(k_lds[B0], qb, krow, h, x0, x1);
             const int t0 = j * BN;
             const bool diag = CAUSAL && (t0 + BN - 1 > wave_row0 + off);
             const float c = __builtin_fmaxf(cq * ks_lds[B0], 1.17549435e-38f);
-            tile_update<PV, D>(rs, x0, x1, c, diag, qrow + off - t0 - 16 * h, v_lds[B0], lq, h);
+            float f0[16], f1[16];
+            const float pmax = tile_softmax<PV, D>(rs, sc[SL][0], sc[SL][1], c, diag, qrow + off - t0 - 16 * h, f0, f1);
+            if constexpr (PIPE) {
+                pv_prep<PV, D>(rs, f0, f1, pmax, pend);
+                have_pend = true;
+            } else {
+                tile_pv<PV, D>(rs, f0, f1, pmax, v_lds[B0], lq, h);
+            }
         }
         if (j + 2 < n_tiles) stage_store<PV, D>(st, k_lds[(B0 + 2) % NBUF], v_lds[(B0 + 2) % NBUF], &ks_lds[(B0 + 2) % NBUF], tid);
         __syncthreads();
         if (j + 3 < n_tiles) stage_load<PV, D>(st, a, kbase, b, hk, bhk, (j + 3) * BN, tid);
     };
-    for (int j = 0; j < n_tiles; j += 3) {
-        body(j, std::integral_constant<int, 0>{});
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    int jend = 0;
+    for (int j = 0; j < n_tiles; j += 4) {
+        jend = j;
+        body(j, I0{}, I0{});
         if (j + 1 >= n_tiles) break;
-        body(j + 1, std::integral_constant<int, 1>{});
+        jend = j + 1;
+        body(j + 1, I1{}, I1{});
         if (j + 2 >= n_tiles) break;
-        body(j + 2, std::integral_constant<int, 2>{});
+        jend = j + 2;
+        body(j + 2, I2{}, I0{});
+        if (j + 3 >= n_tiles) break;
+        jend = j + 3;
+        body(j + 3, I3{}, I1{});
+    }
+    // the last tile's P.V (its V tile is in buffer jend % 4 and was not overwritten:
+    // the final iterations store no new tiles)
+    if constexpr (PIPE) {
+        if (have_pend) pv_issue<PV, D>(rs, pend, v_lds[0] + (size_t)(jend % NBUF) * sizeof(v_lds[0]), lq, h);
     }
 
     // ---- epilogue: O = O^T acc / l (times the V channel scale), LSE in natural log
@@ -348,7 +497,7 @@ __global__ __launch_bounds__(256, 2) void sage_fwd_kernel(SageFwdArgs a) {
     }
     if (a.lse && h == 0) {
         // natural-log LSE; with P scaled by 448 the sum carries that factor
-        float lse = rs.m * 0.6931471805599453f + __logf(l_tot);
+        float lse = rs.m0 * 0.6931471805599453f + __logf(l_tot);
         if (PV == PV_F8) lse -= 6.104793232414985f;   // ln(448)
         a.lse[(int64_t)bh * a.Nq + qrow] = lse;
     }
