@@ -33,7 +33,7 @@ namespace {
 
 constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile (= INT8 K block)
-constexpr int NBUF = 4;   // LDS tiles: P.V(j-1), softmax(j), QK(j+1), staging of j+2
+constexpr int NBUF = 3;   // LDS tiles: the one being used, the next (landed), the one after (in flight)
 
 // XOR swizzle of the 16-byte chunks of a tile row (rows of ROW_BYTES).  For
 // the K tile (read through the row permutation below) and for the V^T tile
@@ -289,80 +289,44 @@ __device__ __forceinline__ void tile_pv(RowState<D>& st, const float (&f0)[16], 
     }
 }
 
-// P.V deferred by one iteration (the pipelined kernels): P packed into the
-// product's operand format plus its scale, issued while the next tile's
-// softmax runs on the vector ALUs.
-struct PvPend {
-    v8i pb;     // fp8: 32 e4m3 codes; int8: codes of keys 16h+i (0..3) and 32+16h+i (4..7)
-    float rs;   // int8: dequantisation scale of the row's tile (with the frame factor)
-    int sb;     // fp8: E8M0 scale (the frame factor)
-};
-
-template <int PV, int D>
-__device__ __forceinline__ void pv_prep(const RowState<D>& st, const float (&f0)[16], const float (&f1)[16],
-                                        float pmax, PvPend& pp) {
-    const int shift = st.m0 == -__builtin_inff() ? 0 : (int)(st.m - st.m0);
-    if constexpr (PV == PV_F8) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f0[4 * k], f0[4 * k + 1], 0, false);
-            pp.pb[k] = __builtin_amdgcn_cvt_pk_fp8_f32(f0[4 * k + 2], f0[4 * k + 3], w0, true);
-            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k], f1[4 * k + 1], 0, false);
-            pp.pb[4 + k] = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k + 2], f1[4 * k + 3], w1, true);
-        }
-        pp.sb = 127 + shift;
-        pp.rs = 0.0f;
-    } else {
-        float inv = pmax > 0.0f ? 127.0f / pmax : 0.0f;
-        if (__builtin_isinf(inv)) inv = 0.0f;
-        pp.rs = __builtin_ldexpf(pmax * (1.0f / 127.0f), shift);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                w0 |= (uint32_t)enc_i8(f0[4 * k + e], inv) << (8 * e);
-                w1 |= (uint32_t)enc_i8(f1[4 * k + e], inv) << (8 * e);
-            }
-            pp.pb[k] = (int)w0;
-            pp.pb[4 + k] = (int)w1;
-        }
-        pp.sb = 127;
-    }
+// Direct global -> LDS copies (fp8 / int8 V): every lane names its global
+// source and the data lands at LDS base + 16 x lane, so the swizzled layouts
+// come from the choice of source per lane.
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
-
-template <int PV, int D>
-__device__ __forceinline__ void pv_issue(RowState<D>& st, const PvPend& pp, const uint8_t* vt, int lq, int h) {
-    if constexpr (PV == PV_F8) {
+// One K tile (64 rows of D bytes) and one V^T tile (D rows of 64 bytes): each
+// wavefront issues a quarter of the 1 KB segments.
+template <int D>
+__device__ __forceinline__ void tile_dma(const int8_t* kbase, const uint8_t* vbase, int64_t Nk, int t0, uint8_t* kl,
+                                         uint8_t* vl, int w, int l) {
+    constexpr int KSEG = BN * D / 1024, RPS = 1024 / D, LPR = D / 16;   // segments, rows per segment, lanes per row
 #pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb) {
-            const int r = 32 * cb + lq;
-            v4i lo = *(const v4i*)(vt + swz_v<BN>(r, h));
-            v4i hi = *(const v4i*)(vt + swz_v<BN>(r, 2 + h));
-            v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            st.oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pp.pb, st.oacc[cb], 0, 0, 0, 127, 0, pp.sb);
-        }
-    } else {
-        const v4i pb0 = {pp.pb[0], pp.pb[1], pp.pb[2], pp.pb[3]}, pb1 = {pp.pb[4], pp.pb[5], pp.pb[6], pp.pb[7]};
+    for (int u = 0; u < KSEG / 4; ++u) {
+        const int sgm = (KSEG / 4) * w + u, r = RPS * sgm + l / LPR, pc = l % LPR;
+        int c;
+        if constexpr (D == 128) c = pc ^ (((r >> 1) & 7) ^ (((r >> 4) & 1) << 2));
+        else c = pc ^ (((r >> 2) & 3) ^ (((r >> 4) & 1) << 1));
+        dma16(kbase + (int64_t)(t0 + r) * D + 16 * c, kl + 1024 * sgm);
+    }
+    constexpr int VSEG = D * BN / 1024;
 #pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb) {
-            const int rr = 32 * cb + lq;
-            v4i v0 = *(const v4i*)(vt + swz_v<BN>(rr, h));
-            v4i v1 = *(const v4i*)(vt + swz_v<BN>(rr, 2 + h));
-            v16i pv = mfma_i8_32x32x32(v0, pb0, v16i{});
-            pv = mfma_i8_32x32x32(v1, pb1, pv);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) st.oacc[cb][i] = __builtin_fmaf((float)pv[i], pp.rs, st.oacc[cb][i]);
-        }
+    for (int u = 0; u < VSEG / 4; ++u) {
+        const int sgm = (VSEG / 4) * w + u, r = 16 * sgm + (l >> 2);
+        const int c = (l & 3) ^ ((r >> 2) & 3);
+        dma16(vbase + (int64_t)r * Nk + t0 + 16 * c, vl + 1024 * sgm);
     }
 }
 
 template <int PV, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void sage_fwd_kernel(SageFwdArgs a) {
+__global__ __launch_bounds__(256, (PV == PV_F16 || !CAUSAL) ? 2 : 3) void sage_fwd_kernel(SageFwdArgs a) {
     using S = Staging<PV, D>;
-    __shared__ __attribute__((aligned(16))) uint8_t k_lds[NBUF][BN * D];
-    __shared__ __attribute__((aligned(16))) uint8_t v_lds[NBUF][D * S::V_ROW];
+    __shared__ __attribute__((aligned(16))) uint8_t k_l0[BN * D], k_l1[BN * D], k_l2[BN * D];
+    __shared__ __attribute__((aligned(16))) uint8_t v_l0[D * S::V_ROW], v_l1[D * S::V_ROW], v_l2[D * S::V_ROW];
     __shared__ float ks_lds[NBUF];
+    uint8_t* const k_lds[NBUF] = {k_l0, k_l1, k_l2};
+    uint8_t* const v_lds[NBUF] = {v_l0, v_l1, v_l2};
 
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
     const int BHq = a.B * a.Hq;
@@ -384,7 +348,9 @@ __global__ __launch_bounds__(256, 2) void sage_fwd_kernel(SageFwdArgs a) {
         qb[kk] = row_ok ? *(const v4i*)(a.qc + ((int64_t)bh * a.Nq + qrow) * D + 16 * h + 32 * kk) : v4i{};
     const float cq = row_ok ? a.qs[(int64_t)bh * (a.Nq / a.q_blk) + qrow / a.q_blk] * a.c_log2 : 0.0f;
     __builtin_amdgcn_s_waitcnt(0);   // Q fragments and scales are in registers before the tile loop
-    const float* kscale = a.ks + (int64_t)bhk * (a.Nk / BN);
+    // K scales per tile through the scalar cache (uniform addresses)
+    const __attribute__((address_space(4))) float* kscale =
+        (const __attribute__((address_space(4))) float*)(a.ks + (int64_t)bhk * (a.Nk / BN));
 
     const int last_row = min(q0 + BM, a.Nq) - 1;
     const int n_tiles = CAUSAL ? min(a.Nk / BN, (last_row + off) / BN + 1) : a.Nk / BN;
@@ -400,78 +366,64 @@ __global__ __launch_bounds__(256, 2) void sage_fwd_kernel(SageFwdArgs a) {
     rs.m0 = -__builtin_inff();
     rs.l = 0.0f;
 
-    // prologue: tiles 0 and 1 in LDS, tile 2 in flight, the scores of tile 0
+    // Tiles go to LDS three deep.  fp8 / int8 V: direct copies; while tile j
+    // is in use, tile j+1 has landed or is landing and tile j+2 is in flight;
+    // the barrier waits only for the older copies.  fp16 V (transposed on the
+    // way in): global -> registers -> LDS, one tile ahead.
+    const uint8_t* vbase = a.vc + (int64_t)bhk * D * a.Nk;
     S st;
-    if (n_tiles > 0) { stage_load<PV, D>(st, a, kbase, b, hk, bhk, 0, tid); stage_store<PV, D>(st, k_lds[0], v_lds[0], &ks_lds[0], tid); }
-    if (n_tiles > 1) { stage_load<PV, D>(st, a, kbase, b, hk, bhk, BN, tid); stage_store<PV, D>(st, k_lds[1], v_lds[1], &ks_lds[1], tid); }
-    __syncthreads();
-    if (n_tiles > 2) stage_load<PV, D>(st, a, kbase, b, hk, bhk, 2 * BN, tid);
-    // The software pipeline holds two score tiles; the register budget allows
-    // it for the causal fp8 / int8 kernels (the benchmarked shapes), the other
-    // variants compute each tile's scores just before its softmax.
-    constexpr bool PIPE = CAUSAL && PV != PV_F16;
-    v16i sc[2][2];
-    if (PIPE && wave_tiles > 0) qk_tile<D>(k_lds[0], qb, krow, h, sc[0][0], sc[0][1]);
+    if constexpr (PV == PV_F16) {
+        if (n_tiles > 0) { stage_load<PV, D>(st, a, kbase, b, hk, bhk, 0, tid); stage_store<PV, D>(st, k_lds[0], v_lds[0], &ks_lds[0], tid); }
+        if (n_tiles > 1) { stage_load<PV, D>(st, a, kbase, b, hk, bhk, BN, tid); stage_store<PV, D>(st, k_lds[1], v_lds[1], &ks_lds[1], tid); }
+        __syncthreads();
+        if (n_tiles > 2) stage_load<PV, D>(st, a, kbase, b, hk, bhk, 2 * BN, tid);
+    } else {
+        (void)st;
+        if (n_tiles > 0) tile_dma<D>(kbase, vbase, a.Nk, 0, k_lds[0], v_lds[0], w, l);
+        if (n_tiles > 1) tile_dma<D>(kbase, vbase, a.Nk, BN, k_lds[1], v_lds[1], w, l);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (n_tiles > 2) tile_dma<D>(kbase, vbase, a.Nk, 2 * BN, k_lds[2], v_lds[2], w, l);
+    }
 
-    // Iteration j issues, on the matrix cores, P.V of tile j-1 (its P packed
-    // in registers from the previous iteration) and QK of tile j+1, while the
-    // vector ALUs run the softmax of tile j (scores from the previous
-    // iteration).  Then tile j+2 goes from registers to LDS, a barrier, and
-    // tile j+3's loads are issued.  Four LDS buffers: V(j-1), scale(j),
-    // K(j+1), tile j+2.  Unrolled by 4 so that the buffer (j % 4) and the
-    // score slot (j % 2) are compile-time.  The variants without the
-    // pipeline (fp16 P, non-causal) compute each tile in place.
-    PvPend pend;
-    bool have_pend = false;
-    auto body = [&](int j, auto bufc, auto slotc) __attribute__((always_inline)) {
+    auto body = [&](int j, auto bufc) __attribute__((always_inline)) {
         constexpr int B0 = decltype(bufc)::value;
-        constexpr int SL = decltype(slotc)::value;
-        if constexpr (PIPE) {
-            if (have_pend) pv_issue<PV, D>(rs, pend, v_lds[(B0 + NBUF - 1) % NBUF], lq, h);
-            have_pend = false;
-            if (j + 1 < wave_tiles) qk_tile<D>(k_lds[(B0 + 1) % NBUF], qb, krow, h, sc[SL ^ 1][0], sc[SL ^ 1][1]);
-        } else {
-            if (j < wave_tiles) qk_tile<D>(k_lds[B0], qb, krow, h, sc[SL][0], sc[SL][1]);
-        }
         if (j < wave_tiles) {
+            v16i x0, x1;
+            qk_tile<D>(k_lds[B0], qb, krow, h, x0, x1);
             const int t0 = j * BN;
             const bool diag = CAUSAL && (t0 + BN - 1 > wave_row0 + off);
-            const float c = __builtin_fmaxf(cq * ks_lds[B0], 1.17549435e-38f);
+            const float kscj = PV == PV_F16 ? ks_lds[B0] : kscale[j];
+            const float c = __builtin_fmaxf(cq * kscj, 1.17549435e-38f);
             float f0[16], f1[16];
-            const float pmax = tile_softmax<PV, D>(rs, sc[SL][0], sc[SL][1], c, diag, qrow + off - t0 - 16 * h, f0, f1);
-            if constexpr (PIPE) {
-                pv_prep<PV, D>(rs, f0, f1, pmax, pend);
-                have_pend = true;
-            } else {
-                tile_pv<PV, D>(rs, f0, f1, pmax, v_lds[B0], lq, h);
-            }
+            const float pmax = tile_softmax<PV, D>(rs, x0, x1, c, diag, qrow + off - t0 - 16 * h, f0, f1);
+            tile_pv<PV, D>(rs, f0, f1, pmax, v_lds[B0], lq, h);
         }
-        if (j + 2 < n_tiles) stage_store<PV, D>(st, k_lds[(B0 + 2) % NBUF], v_lds[(B0 + 2) % NBUF], &ks_lds[(B0 + 2) % NBUF], tid);
-        __syncthreads();
-        if (j + 3 < n_tiles) stage_load<PV, D>(st, a, kbase, b, hk, bhk, (j + 3) * BN, tid);
+        if constexpr (PV == PV_F16) {
+            if (j + 2 < n_tiles) stage_store<PV, D>(st, k_lds[(B0 + 2) % NBUF], v_lds[(B0 + 2) % NBUF], &ks_lds[(B0 + 2) % NBUF], tid);
+            __syncthreads();
+            if (j + 3 < n_tiles) stage_load<PV, D>(st, a, kbase, b, hk, bhk, (j + 3) * BN, tid);
+        } else {
+            // tile j+1 must have landed (this wavefront's copies, then the
+            // barrier for everyone's); tile j+2's copies may stay in flight
+            constexpr int per_tile = (BN * D / 1024) / 4 + (D * BN / 1024) / 4;   // copies per wavefront
+            if (j + 2 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | per_tile);   // vmcnt(per_tile), lgkmcnt(0)
+            else __builtin_amdgcn_s_waitcnt(0);
+            // a plain s_barrier: the workgroup fence of __syncthreads would also
+            // wait for the copies still in flight
+            asm volatile("s_barrier" ::: "memory");
+            if (j + 3 < n_tiles) tile_dma<D>(kbase, vbase, a.Nk, (j + 3) * BN, k_lds[B0], v_lds[B0], w, l);
+        }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    int jend = 0;
-    for (int j = 0; j < n_tiles; j += 4) {
-        jend = j;
-        body(j, I0{}, I0{});
+    for (int j = 0; j < n_tiles; j += 3) {
+        body(j, I0{});
         if (j + 1 >= n_tiles) break;
-        jend = j + 1;
-        body(j + 1, I1{}, I1{});
+        body(j + 1, I1{});
         if (j + 2 >= n_tiles) break;
-        jend = j + 2;
-        body(j + 2, I2{}, I0{});
-        if (j + 3 >= n_tiles) break;
-        jend = j + 3;
-        body(j + 3, I3{}, I1{});
-    }
-    // the last tile's P.V (its V tile is in buffer jend % 4 and was not overwritten:
-    // the final iterations store no new tiles)
-    if constexpr (PIPE) {
-        if (have_pend) pv_issue<PV, D>(rs, pend, v_lds[0] + (size_t)(jend % NBUF) * sizeof(v_lds[0]), lq, h);
+        body(j + 2, I2{});
     }
 
     // ---- epilogue: O = O^T acc / l (times the V channel scale), LSE in natural log
