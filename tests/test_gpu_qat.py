@@ -162,3 +162,28 @@ def test_qat_backward_full_size_sampled():
         compare_outputs(g[0][r0:r0 + 32], dQ, "bf16", what=f"dQ rows {r0}")
         compare_outputs(g[1][r0:r0 + 32], dK, "bf16", what=f"dK rows {r0}")
         compare_outputs(g[2][r0:r0 + 32], dV, "bf16", what=f"dV rows {r0}")
+
+
+def test_qat_score_jump_moves_the_frame():
+    """Keys after the first tile score more than 64 binades above it: the
+    kernel moves its fixed per-row frame (exact rescale) and still matches."""
+    from bit_quantized_attention_amd.runner import QatPath, qat_problem, to_device
+    rng = np.random.default_rng(42)
+    N, d = 256, 128
+    Q, K, V = (rng.standard_t(3, (1, 1, N, d)).astype(np.float32) for _ in range(3))
+    Q[..., 0] = 40.0
+    K[0, 0, :64, 0] = -40.0
+    K[0, 0, 64:, 0] = 40.0
+    Q, K, V = (wl.round_to(x, "bf16").reshape(x.shape) for x in (Q, K, V))
+    p = qat_problem(1, 1, 1, N, N, d)
+    path = QatPath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
+    path.step()
+    torch.cuda.synchronize()
+    oc = _Oracle(Q, K, V)
+    ref, ref_aux, lse = oc.forward(0, 0)
+    s0 = max(orc.mx_score(oc.qc[0], oc.qs[0], oc.kc[0], oc.ks[0], d, 10, j)[0] for j in range(64))
+    s1 = max(orc.mx_score(oc.qc[0], oc.qs[0], oc.kc[0], oc.ks[0], d, 10, j)[0] for j in range(64, 128))
+    assert (s1 - s0) * tau_for(d) / np.log(2) > 64
+    compare_outputs(path.o[0, 0].float().cpu().numpy(), ref, "bf16", what="O (score jump)")
+    compare_outputs(path.oa[0, 0].float().cpu().numpy(), ref_aux, "bf16", what="O' (score jump)")
+    assert np.abs(path.lse[0, 0].cpu().numpy() - lse).max() < 2e-3

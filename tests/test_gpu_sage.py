@@ -150,3 +150,34 @@ def test_deterministic_and_zero_block():
     orc = SageOracle(Q, K, V, q_block=128, pv="f8")
     ref, _ = orc.forward(0, 1, False, tau_for(128), rows=(128, 256))
     compare_outputs(o1[0, 1, 128:256].float().cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("pv", ["f8", "i8"])
+def test_score_jump_moves_the_frame(pv):
+    """Keys after the first tile score far above it (more than the 96-binade
+    frame gap, in log2 units): the kernels' rare exact rescale of the
+    accumulators runs and the result still matches the oracle."""
+    import bit_quantized_attention_amd as bqa
+    from bit_quantized_attention_amd.runner import SagePath, sage_problem, to_device
+    rng = np.random.default_rng(41)
+    N, d = 512, 128
+    Q = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    K = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    V = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    Q[..., 0] = 30.0
+    K[0, 0, :64, 0] = -30.0
+    K[0, 0, 64:, 0] = 30.0
+    Q, K, V = (wl.round_to(x, "bf16").reshape(x.shape) for x in (Q, K, V))
+    mode = bqa.BQA_SAGE_I8_F8PV if pv == "f8" else bqa.BQA_SAGE_I8_I8PV
+    p = sage_problem(1, 1, 1, N, N, d, True, mode, q_block=128, smooth_k=True, smooth_eps=0.0)
+    path = SagePath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
+    path.step()
+    torch.cuda.synchronize()
+    orc = SageOracle(Q, K, V, q_block=128, pv=pv)
+    ref, lse = orc.forward(0, 0, True, tau_for(d))
+    # the jump really exceeds the frame gap: log2-unit score difference across key tile 0 / 1
+    s = (orc.qc[0].astype(np.float64) @ orc.kc[0].astype(np.float64).T) * np.repeat(orc.qs[0], 128)[:, None] \
+        * np.repeat(orc.ks[0], 64)[None, :] * tau_for(d) / np.log(2)
+    assert s[200, 64:128].max() - s[200, :64].max() > 96
+    compare_outputs(path.o[0, 0].float().cpu().numpy(), ref, "bf16", what=f"O ({pv} P.V, score jump)")
+    assert np.abs(path.lse[0, 0].cpu().numpy() - lse).max() < 2e-3

@@ -294,3 +294,29 @@ def test_thrift_decode_full_size_sampled():
                                      num_splits=S)
         compare_outputs(O[b, hq, 0], ref, "bf16", what=f"decode o (b={b}, h={hq})")
         assert abs(L[b, hq, 0] - lse) < 2e-3
+
+
+def test_thrift_score_jump_moves_the_frame():
+    """The first key blocks score far below the later ones (more than the
+    64-binade frame gap): both the FP4 and the bf16 path move the frame."""
+    from bit_quantized_attention_amd.runner import ThriftPath, thrift_problem, to_device
+    rng = np.random.default_rng(43)
+    N, d = 1024, 128
+    Q, K, V = (rng.standard_normal((1, 2, N, d)).astype(np.float32) for _ in range(3))
+    K = K[:, :1].copy(); V = V[:, :1].copy()
+    Q[..., 0] = 30.0
+    K[0, 0, :256, 0] = -30.0
+    K[0, 0, 256:, 0] = 30.0
+    Q, K, V = (wl.round_to(x, "bf16").reshape(x.shape) for x in (Q, K, V))
+    for ppm in (PPM_5, 250_000):
+        p = thrift_problem(1, 2, 1, N, N, d, budget_ppm=ppm)
+        path = ThriftPath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
+        path.step()
+        torch.cuda.synchronize()
+        oc = _ThriftOracle(Q, K, V, ppm)
+        O = path.o.float().cpu().numpy()
+        for iq in range(2):
+            assert_same(path.sel_idx[0, iq].cpu().numpy(), oc.sel[iq][0], f"selection h={iq}")
+            ref, lse = oc.forward(iq)
+            compare_outputs(O[0, iq], ref, "bf16", what=f"O[h={iq}] budget {ppm}")
+            assert np.abs(path.lse[0, iq].cpu().numpy() - lse).max() < 2e-3
