@@ -17,12 +17,17 @@
 // that each lane half holds 16 consecutive keys: row max and row sum are
 // in-lane reductions plus one permlane32 swap, and the probabilities are
 // already the B operand of O^T = V^T P^T against contiguous V^T chunks, with
-// no LDS round trip.  K tiles and channel-major V tiles go global ->
-// registers -> LDS (XOR-swizzled 16-byte chunks, conflict-free for 16
-// consecutive lanes) three tiles deep; the loop is unrolled by the buffer
-// count so every LDS address is an immediate offset.  Causal workgroups are
-// issued heaviest-first; consecutive workgroup ids take different heads,
-// which keeps each head on one XCD.
+// no LDS round trip.  K tiles and channel-major V tiles sit in LDS as
+// XOR-swizzled 16-byte chunks (conflict-free for 16 consecutive lanes).
+//
+// Two kernels share these pieces.  The fp8 P.V path (the common one) is a
+// three-stage software pipeline with direct global->LDS copies in rings of
+// four tiles and, for causal masks, one workgroup per pair of query tiles
+// (heaviest with lightest); see the section that defines it.  The fp16 and
+// int8 P.V paths take one tile at a time, three tiles deep in LDS (fp16 V is
+// transposed on the way in through registers), with causal workgroups issued
+// heaviest-first.  Consecutive workgroup ids take different heads, which
+// keeps each head on one XCD.
 #include <type_traits>
 #include "common.hpp"
 #include "internal.hpp"
@@ -206,13 +211,18 @@ __device__ __forceinline__ float tile_softmax(RowState<D>& st, const v16i& s0, c
     }
     st.m = m_new;
     const float bias = m_new == -__builtin_inff() ? 0.0f : pbias - m_new;
-    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float ps[4];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         f0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(f0[i], c, bias));
         f1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(f1[i], c, bias));
-        ps[i & 1] += f0[i];
-        ps[2 + (i & 1)] += f1[i];
+        if (i < 2) {
+            ps[i] = f0[i];
+            ps[2 + i] = f1[i];
+        } else {
+            ps[i & 1] += f0[i];
+            ps[2 + (i & 1)] += f1[i];
+        }
     }
     const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
     // the row sum lives in the frame: times 2^(m - m0) (an exact power of two)
@@ -229,9 +239,11 @@ __device__ __forceinline__ void tile_pv(RowState<D>& st, const float (&f0)[16], 
         v8i pb;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f0[4 * k], f0[4 * k + 1], 0, false);
+            // the first conversion of a pair writes the low half-word; the
+            // other half comes from the second one, so the old value is moot
+            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f0[4 * k], f0[4 * k + 1], __builtin_bit_cast(int, f0[4 * k]), false);
             pb[k] = __builtin_amdgcn_cvt_pk_fp8_f32(f0[4 * k + 2], f0[4 * k + 3], w0, true);
-            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k], f1[4 * k + 1], 0, false);
+            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k], f1[4 * k + 1], __builtin_bit_cast(int, f1[4 * k]), false);
             pb[4 + k] = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k + 2], f1[4 * k + 3], w1, true);
         }
         const int sb = 127 + shift;     // E8M0 scale of P: the frame factor, exact
@@ -455,6 +467,351 @@ __global__ __launch_bounds__(256, (PV == PV_F16 || !CAUSAL) ? 2 : 3) void sage_f
     }
 }
 
+// ---- fp8 P.V: three-stage software pipeline -----------------------------------
+// A wavefront overlaps its own matrix and vector work across three tiles: in
+// step j it issues P.V of tile j-1 while it converts the scores of tile j, and
+// the scores of tile j+1 while it computes the exponentials of tile j.  The
+// matrix instructions are spread between the vector ones so that neither this
+// wavefront nor the other one on its SIMD waits behind a burst of them.  Two
+// score tiles in registers cost VGPRs, so two workgroups share a CU.  K tiles
+// sit in a ring of four LDS slots (tile t is read in step t-1 and copied at
+// the end of step t-4), V^T tiles in another ring of four (read in step t+1,
+// copied at the end of step t-3).  The copies are issued from inline assembly
+// with a scalar base: the compiler then leaves their completion to the
+// kernel's own counted waits instead of waiting for every copy in flight
+// before any LDS read.
+constexpr int PRING = 4;
+
+__device__ __forceinline__ void copy16(uint32_t voff, const void* sbase, uint32_t lds) {
+    // M0 holds the LDS destination; one wait state before the copy reads it.
+    // M0 is reserved to the compiler, which sets it right before each of its
+    // own users (none in this kernel), so it is not named as a clobber.
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// Per-lane source offsets of one wavefront's share of a K tile and a V^T tile
+// (1 KB segments; the LDS swizzle comes from the source each lane names).
+template <int D>
+struct CopyPlan {
+    static constexpr int KU = BN * D / 1024 / 4, VU = D * BN / 1024 / 4;   // segments per wavefront
+    uint32_t koff[KU], voff[VU];
+    __device__ __forceinline__ CopyPlan(int w, int l, int Nk) {
+        constexpr int RPS = 1024 / D, LPR = D / 16;
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int sgm = KU * w + u, r = RPS * sgm + l / LPR, pc = l % LPR;
+            int c;
+            if constexpr (D == 128) c = pc ^ (((r >> 1) & 7) ^ (((r >> 4) & 1) << 2));
+            else c = pc ^ (((r >> 2) & 3) ^ (((r >> 4) & 1) << 1));
+            koff[u] = (uint32_t)(r * D + 16 * c);
+        }
+#pragma unroll
+        for (int u = 0; u < VU; ++u) {
+            const int sgm = VU * w + u, r = 16 * sgm + (l >> 2);
+            const int c = (l & 3) ^ ((r >> 2) & 3);
+            voff[u] = (uint32_t)r * (uint32_t)Nk + (uint32_t)(16 * c);
+        }
+    }
+    __device__ __forceinline__ void k_tile(const int8_t* kbase, int t0, const uint8_t* kl, int w) const {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) copy16(koff[u], kbase + (int64_t)t0 * D, lds_addr(kl) + 1024 * (KU * w + u));
+    }
+    __device__ __forceinline__ void v_tile(const uint8_t* vbase, int t0, const uint8_t* vl, int w) const {
+#pragma unroll
+        for (int u = 0; u < VU; ++u) copy16(voff[u], vbase + t0, lds_addr(vl) + 1024 * (VU * w + u));
+    }
+};
+
+// P of a finished tile, packed as the B operand of its P.V product.
+struct PendF8 {
+    v8i pb;   // e4m3 codes of 448 P: lane (query, half h), keys 16h + 4k .. (and +32)
+    int sb;   // E8M0 scale of P: 127 + the frame shift when P was made
+};
+
+template <int D>
+__device__ __forceinline__ void pv_f8(v16f (&oacc)[D / 32], const PendF8& pp, const uint8_t* vt, int lq, int h, int cb) {
+    const int r = 32 * cb + lq;
+    v4i lo = *(const v4i*)(vt + swz_v<BN>(r, h));
+    v4i hi = *(const v4i*)(vt + swz_v<BN>(r, 2 + h));
+    v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pp.pb, oacc[cb], 0, 0, 0, 127, 0, pp.sb);
+}
+
+// One step of the pipeline (see above).  s0/s1: int32 scores of this tile on
+// entry, of the next tile on exit; pend: P of the previous tile on entry, of
+// this tile on exit.  The arithmetic is the one of tile_softmax + tile_pv
+// (fp8 P.V), with the rare frame move done after the exponentials (they do
+// not depend on the frame) and after P.V of the previous tile was issued (it
+// belongs to the old frame).
+template <int D, bool DIAG>
+__device__ __forceinline__ void f8_step(RowState<D>& st, PendF8& pend, v16i& s0, v16i& s1, const uint8_t* k_next,
+                                        const uint8_t* v_prev, const v4i* qb, int krow, int lq, int h, float c,
+                                        int diag_lim) {
+    constexpr float pbias = 8.807354922057604f;   // log2(448): P scaled by 448
+    float f0[16], f1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { f0[i] = (float)s0[i]; f1[i] = (float)s1[i]; }
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) pv_f8<D>(st.oacc, pend, v_prev, lq, h, cb);
+    if constexpr (DIAG) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            f0[i] = i > diag_lim ? -__builtin_inff() : f0[i];
+            f1[i] = i + 32 > diag_lim ? -__builtin_inff() : f1[i];
+        }
+    }
+    float mx = __builtin_fmaxf(f0[0], f1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, f0[i]), f1[i]);
+    mx = __builtin_fmaxf(mx, partner32f(mx));
+    const float m_new = __builtin_fmaxf(st.m, __builtin_ceilf(mx * c));
+    // the frame moves when the reference runs more than FRAME_GAP binades ahead
+    // (always at the first visible tile, where m0 = -inf)
+    const bool need = m_new - st.m0 > FRAME_GAP;
+    const float bias = m_new == -__builtin_inff() ? 0.0f : pbias - m_new;
+    // scores of the next tile, one 32-channel slice every four exponentials;
+    // each slice's K operands are read while the slice before is issued
+    constexpr int NS = D / 32;
+    v4i ka = *(const v4i*)(k_next + swz_k<D>(krow, h));
+    v4i kb = *(const v4i*)(k_next + swz_k<D>(32 + krow, h));
+    v16i n0 = v16i{}, n1 = v16i{};
+    float ps[4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (i % 4 == 0 && i / 4 < NS) {
+            const int kk = i / 4;
+            n0 = mfma_i8_32x32x32(ka, qb[kk], n0);
+            n1 = mfma_i8_32x32x32(kb, qb[kk], n1);
+            if (kk + 1 < NS) {
+                ka = *(const v4i*)(k_next + swz_k<D>(krow, 2 * (kk + 1) + h));
+                kb = *(const v4i*)(k_next + swz_k<D>(32 + krow, 2 * (kk + 1) + h));
+            }
+        }
+        f0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(f0[i], c, bias));
+        f1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(f1[i], c, bias));
+        if (i < 2) {
+            ps[i] = f0[i];
+            ps[2 + i] = f1[i];
+        } else {
+            ps[i & 1] += f0[i];
+            ps[2 + (i & 1)] += f1[i];
+        }
+    }
+    const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    const int shift = (need || st.m0 == -__builtin_inff()) ? 0 : (int)(m_new - st.m0);   // 0 .. FRAME_GAP
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        // the first conversion of a pair writes the low half-word, the second
+        // one the high half-word: the old value is moot
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f0[4 * k], f0[4 * k + 1], __builtin_bit_cast(int, f0[4 * k]), false);
+        pend.pb[k] = __builtin_amdgcn_cvt_pk_fp8_f32(f0[4 * k + 2], f0[4 * k + 3], w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k], f1[4 * k + 1], __builtin_bit_cast(int, f1[4 * k]), false);
+        pend.pb[4 + k] = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k + 2], f1[4 * k + 3], w1, true);
+    }
+    pend.sb = 127 + shift;
+    s0 = n0;
+    s1 = n1;
+    // instruction order: the LDS reads of P.V and of the first score slice
+    // first, the conversions over their latency, P.V of the previous tile
+    // under the rest of the conversions and the maximum, then one score
+    // instruction of the next tile every dozen vector instructions, each
+    // slice's reads issued a slice ahead (the rare diagonal tiles keep the
+    // compiler's own order)
+    if constexpr (!DIAG) {
+        __builtin_amdgcn_sched_group_barrier(0x0100, 2 * NS + 2, 0);      // V reads, K reads of slice 0
+        __builtin_amdgcn_sched_group_barrier(0x0002, 20, 0);              // conversions
+#pragma unroll
+        for (int cb = 0; cb < NS; ++cb) {
+            __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);           // P.V
+            __builtin_amdgcn_sched_group_barrier(0x0002, 6, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x0002, 30, 0);              // conversions, maximum, frame
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);           // scores
+            if (k + 1 < NS) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // next slice's reads
+            __builtin_amdgcn_sched_group_barrier(0x0002, 96 / NS / 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+            if (k + 1 < NS) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x0002, 96 / NS / 2, 0);
+        }
+    }
+    // keep this tile's vector work ahead of the rare branch below (the
+    // compiler would otherwise sink it into the next step, away from the
+    // matrix instructions it is meant to hide)
+    asm volatile("" ::"v"(pend.pb[0]), "v"(pend.pb[1]), "v"(pend.pb[2]), "v"(pend.pb[3]), "v"(pend.pb[4]),
+                 "v"(pend.pb[5]), "v"(pend.pb[6]), "v"(pend.pb[7]), "v"(psum));
+    if (__any(need)) {
+        if (need) {
+            if (st.m0 != -__builtin_inff()) {
+                const float f = __builtin_ldexpf(1.0f, (int)(st.m0 - m_new));
+                st.l *= f;
+#pragma unroll
+                for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) st.oacc[cb][i] *= f;
+            }
+            st.m0 = m_new;
+        }
+    }
+    st.l += __builtin_ldexpf(psum, shift);
+    st.m = m_new;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void sage_fwd_f8_kernel(SageFwdArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t k_lds[PRING][BN * D];
+    __shared__ __attribute__((aligned(16))) uint8_t v_lds[PRING][D * BN];
+    using CP = CopyPlan<D>;
+
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
+    const int BHq = a.B * a.Hq;
+    const int n_qt = (a.Nq + BM - 1) / BM;
+    const int bid = blockIdx.x;
+    // causal: this workgroup takes query tile n_qt-1-p and then tile p, which
+    // gives every workgroup the same number of key tiles (no tail of short
+    // workgroups); the middle tile of an odd count goes alone
+    const int p = bid / BHq;
+    const int bh = bid % BHq, b = bh / a.Hq, hq = bh % a.Hq;
+    const int hk = hq / (a.Hq / a.Hkv), bhk = b * a.Hkv + hk;
+    const int off = a.Nk - a.Nq;
+    const int krow = sigma(lq);
+    const CP cp(w, l, a.Nk);
+    const int8_t* kbase = a.kc + (int64_t)bhk * a.Nk * D;
+    const uint8_t* vbase = a.vc + (int64_t)bhk * D * a.Nk;
+    const __attribute__((address_space(4))) float* kscale =
+        (const __attribute__((address_space(4))) float*)(a.ks + (int64_t)bhk * (a.Nk / BN));
+
+    auto qtile = [&](const int qt) __attribute__((always_inline)) {
+        const int q0 = qt * BM;
+        const int qrow = q0 + 32 * w + lq;
+        const bool row_ok = qrow < a.Nq;
+        v4i qb[D / 32];
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+            qb[kk] = row_ok ? *(const v4i*)(a.qc + ((int64_t)bh * a.Nq + qrow) * D + 16 * h + 32 * kk) : v4i{};
+        const float cq = row_ok ? a.qs[(int64_t)bh * (a.Nq / a.q_blk) + qrow / a.q_blk] * a.c_log2 : 0.0f;
+        __builtin_amdgcn_s_waitcnt(0);
+
+        const int last_row = min(q0 + BM, a.Nq) - 1;
+        const int n_tiles = CAUSAL ? min(a.Nk / BN, (last_row + off) / BN + 1) : a.Nk / BN;
+        const int wave_row0 = q0 + 32 * w;
+        const int wave_tiles = CAUSAL ? min(n_tiles, (wave_row0 + 31 + off) / BN + 1) : n_tiles;
+
+        RowState<D> rs;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) rs.oacc[cb] = v16f{};
+        rs.m = -__builtin_inff();
+        rs.m0 = -__builtin_inff();
+        rs.l = 0.0f;
+        PendF8 pend;
+        pend.pb = v8i{};
+        pend.sb = 127;
+
+        // V slot 3 starts as zeros: the first step's P.V (of no tile, P = 0) reads it
+#pragma unroll
+        for (int u = 0; u < D * BN / 16 / 256; ++u) *(v4i*)(&v_lds[3][16 * (tid + 256 * u)]) = v4i{};
+        // copies in the order of the steady state: K0 K1 V0 K2 V1 K3 V2 (a
+        // short row repeats its last tile, which keeps the wait counts exact)
+        if (n_tiles > 0) {
+            const int tl = n_tiles - 1;
+            cp.k_tile(kbase, 0, k_lds[0], w);
+            cp.k_tile(kbase, min(1, tl) * BN, k_lds[1], w);
+            cp.v_tile(vbase, 0, v_lds[0], w);
+            cp.k_tile(kbase, min(2, tl) * BN, k_lds[2], w);
+            cp.v_tile(vbase, min(1, tl) * BN, v_lds[1], w);
+            cp.k_tile(kbase, min(3, tl) * BN, k_lds[3], w);
+            cp.v_tile(vbase, min(2, tl) * BN, v_lds[2], w);
+        }
+        static_assert(CP::KU == CP::VU && 5 * CP::KU < 16, "wait counts");
+        __builtin_amdgcn_s_waitcnt(0x0070 | (5 * CP::KU));   // K0 and K1 landed, zero fill done
+        asm volatile("s_barrier" ::: "memory");
+
+        v16i s0 = v16i{}, s1 = v16i{};   // scores of the tile about to be processed
+        if (wave_tiles > 0) qk_tile<D>(k_lds[0], qb, krow, h, s0, s1);
+
+        // end of step j: K(j+2) and V(j) must have landed; the copies issued
+        // after K(j+2) (V(j+1), K(j+3), V(j+2)) may stay in flight
+        auto sync = [&](int j, const uint8_t* k_free, const uint8_t* v_free) __attribute__((always_inline)) {
+            if (j + 3 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | (3 * CP::KU));
+            else __builtin_amdgcn_s_waitcnt(0);
+            asm volatile("s_barrier" ::: "memory");
+            if (j + 4 < n_tiles) cp.k_tile(kbase, (j + 4) * BN, k_free, w);
+            if (j + 3 < n_tiles) cp.v_tile(vbase, (j + 3) * BN, v_free, w);
+        };
+        // Steps before the first tile that reaches the diagonal of any row of
+        // the workgroup: no masking, every wavefront active, ring slots as
+        // immediates (unrolled by the ring size).
+        const int J1 = CAUSAL ? min(n_tiles, max(0, q0 + off + 1) / BN) : n_tiles;
+        auto body = [&](int j, auto slot) __attribute__((always_inline)) {
+            constexpr int KB = decltype(slot)::value, KN = (KB + 1) % PRING, VP = (KB + PRING - 1) % PRING;
+            const float c = __builtin_fmaxf(cq * kscale[j], 1.17549435e-38f);
+            f8_step<D, false>(rs, pend, s0, s1, k_lds[KN], v_lds[VP], qb, krow, lq, h, c, 0);
+            sync(j, k_lds[KB], v_lds[VP]);
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        for (int j = 0; j < J1; j += PRING) {
+            body(j, I0{});
+            if (j + 1 >= J1) break;
+            body(j + 1, I1{});
+            if (j + 2 >= J1) break;
+            body(j + 2, I2{});
+            if (j + 3 >= J1) break;
+            body(j + 3, I3{});
+        }
+        // The few remaining steps (causal): masked tiles, and at j ==
+        // wave_tiles a fully masked step that only adds the wave's last P.V.
+        for (int j = J1; j < n_tiles; ++j) {
+            const int kb = j & (PRING - 1), kn = (j + 1) & (PRING - 1), vp = (j + PRING - 1) & (PRING - 1);
+            if (j <= wave_tiles) {
+                const float c = __builtin_fmaxf(cq * kscale[j], 1.17549435e-38f);
+                const int lim = j == wave_tiles ? -1 : qrow + off - j * BN - 16 * h;
+                f8_step<D, true>(rs, pend, s0, s1, k_lds[kn], v_lds[vp], qb, krow, lq, h, c, lim);
+            }
+            sync(j, k_lds[kb], v_lds[vp]);
+        }
+        if (wave_tiles == n_tiles && n_tiles > 0) {
+            const uint8_t* vt = v_lds[(n_tiles - 1) & (PRING - 1)];
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb) pv_f8<D>(rs.oacc, pend, vt, lq, h, cb);
+        }
+        // every LDS read of this query tile is done before the slots are reused
+        __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("s_barrier" ::: "memory");
+
+        const float l_tot = rs.l + partner32f(rs.l);
+        if (!row_ok) return;
+        const float inv_l = 1.0f / l_tot;
+        uint16_t* orow = (uint16_t*)a.o.p + b * a.o.sB + hq * a.o.sH + (int64_t)qrow * a.o.sN;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int ch0 = 32 * cb + 8 * g + 4 * h;
+                uint16_t out[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    out[e] = f32_to_bf16_bits(rs.oacc[cb][4 * g + e] * inv_l * a.vs[(int64_t)bhk * D + ch0 + e]);
+                *(uint2*)(orow + ch0) = make_uint2((uint32_t)out[0] | ((uint32_t)out[1] << 16),
+                                                   (uint32_t)out[2] | ((uint32_t)out[3] << 16));
+            }
+        }
+        if (a.lse && h == 0) {
+            // natural-log LSE; with P scaled by 448 the sum carries that factor
+            a.lse[(int64_t)bh * a.Nq + qrow] = rs.m0 * 0.6931471805599453f + __logf(l_tot) - 6.104793232414985f;
+        }
+    };
+    const int n_pass = CAUSAL && p != n_qt - 1 - p ? 2 : 1;
+    for (int pass = 0; pass < n_pass; ++pass) qtile(CAUSAL && pass == 0 ? n_qt - 1 - p : p);
+}
+
 // Raw int32 S tile (32 queries x 32 keys) through the same tile code.
 template <int D>
 __global__ __launch_bounds__(64) void debug_scores_i8_kernel(const int8_t* qc, const int8_t* kc, int32_t* out) {
@@ -481,8 +838,20 @@ __global__ __launch_bounds__(64) void debug_scores_i8_kernel(const int8_t* qc, c
 template <int PV, int D>
 hipError_t launch_t(const SageFwdArgs& a, hipStream_t st) {
     const int grid = a.B * a.Hq * ((a.Nq + BM - 1) / BM);
-    if (a.causal) sage_fwd_kernel<PV, D, true><<<grid, 256, 0, st>>>(a);
-    else sage_fwd_kernel<PV, D, false><<<grid, 256, 0, st>>>(a);
+    if constexpr (PV == PV_F16) {
+        if (a.causal) sage_fwd_kernel<PV, D, true><<<grid, 256, 0, st>>>(a);
+        else sage_fwd_kernel<PV, D, false><<<grid, 256, 0, st>>>(a);
+    } else if constexpr (PV == PV_I8) {
+        if (a.causal) sage_fwd_kernel<PV, D, true><<<grid, 256, 0, st>>>(a);
+        else sage_fwd_kernel<PV, D, false><<<grid, 256, 0, st>>>(a);
+    } else {
+        // lane offsets of the copies are 32-bit
+        if ((int64_t)D * a.Nk >= (int64_t)1 << 31) return hipErrorInvalidValue;
+        // causal: one workgroup per pair of query tiles
+        const int n_qt = (a.Nq + BM - 1) / BM;
+        if (a.causal) sage_fwd_f8_kernel<D, true><<<a.B * a.Hq * ((n_qt + 1) / 2), 256, 0, st>>>(a);
+        else sage_fwd_f8_kernel<D, false><<<grid, 256, 0, st>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -181,3 +181,17 @@ def test_score_jump_moves_the_frame(pv):
     assert s[200, 64:128].max() - s[200, :64].max() > 96
     compare_outputs(path.o[0, 0].float().cpu().numpy(), ref, "bf16", what=f"O ({pv} P.V, score jump)")
     assert np.abs(path.lse[0, 0].cpu().numpy() - lse).max() < 2e-3
+
+
+@pytest.mark.parametrize("N,d,causal,hq,hkv", [(128, 64, False, 2, 1), (192, 128, True, 2, 2), (384, 64, True, 4, 2),
+                                               (512, 128, False, 4, 2), (640, 64, False, 1, 1)])
+def test_f8_shapes(N, d, causal, hq, hkv):
+    """fp8 P.V path over the shapes its kernel distinguishes: head dimension 64
+    and 128, causal and not, grouped heads, sequences of fewer tiles than its
+    LDS ring holds, odd and even query-tile counts (causal pairing), a half
+    query tile (q_block 64)."""
+    import dataclasses
+    w = dataclasses.replace(wl.with_len(wl.WORKLOADS["c2"], N, b=1, hq=hq, hkv=hkv), d=d, causal=causal)
+    p, path, orc = _run(w, "f8", q_block=64, eps=0.0)
+    _check_codes(p, path, orc)
+    _check_heads(p, path, orc, [(0, h) for h in range(hq)])
