@@ -147,9 +147,9 @@ def _sage_case(w, bqa, torch):
         path=path, ops=ops, dtype="i8+e4m3",
         workload="SageAttention INT8 forward (c2): B=2 H=16 N=4096 d=128 causal, bf16 in, K-smoothing, "
                  "INT8 Q/K, e4m3 P.V; step = quantise Q,K,V + attention",
-        roofline={"bound": "mfma", "kernel": "sage_fwd_kernel (i8 QK^T + fp8 P.V)", "peak": PEAK_I8_TOPS,
-                  "ops_per_launch": ops},
-        traffic_key="sage_fwd_kernel<F8,128,causal>", cpu=cpu_baseline)
+        roofline={"bound": "mfma", "kernel": "sage_fwd_f8_kernel (i8 QK^T + fp8 P.V, three-stage pipeline)",
+                  "peak": PEAK_I8_TOPS, "ops_per_launch": ops},
+        traffic_key="sage_fwd_f8_kernel<128,causal>", cpu=cpu_baseline)
 
 
 def _qat_case(w, bqa, torch):
@@ -436,7 +436,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", choices=sorted(CASES), default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
