@@ -41,38 +41,21 @@ __device__ __forceinline__ int fs256(int r) { return (r & 7) | (((r >> 4) & 1) <
 __device__ __forceinline__ int fc64(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int fc128(int r) { return (r >> 1) & 7; }
 
-__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+// 16 values (one lane half's keys or queries of a 32-group) -> v4i of INT8
+// codes, rint(fp32(x * inv)) with the tile's inverse scale.  inv comes from
+// the tile's largest magnitude, so |x * inv| <= 127 and no clamp is needed:
+// the code is the low byte of fp32(x * inv) + 1.5 * 2^23 (the addition rounds
+// to the nearest even integer).
+__device__ __forceinline__ int q8x4(float a, float b, float c, float d, float inv) {
+#pragma clang fp contract(off)
+    const float M = 12582912.0f;
+    const uint32_t wa = __builtin_bit_cast(uint32_t, a * inv + M), wb = __builtin_bit_cast(uint32_t, b * inv + M);
+    const uint32_t wc = __builtin_bit_cast(uint32_t, c * inv + M), wd = __builtin_bit_cast(uint32_t, d * inv + M);
+    return (int)(__builtin_amdgcn_perm(wb, wa, 0x0c0c0400u) | __builtin_amdgcn_perm(wd, wc, 0x04000c0cu));
 }
-__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
-}
-
-// Symmetric INT8 code of x with the tile's inverse scale (nearest even, +-127).
-__device__ __forceinline__ int q8(float x, float inv) {
-    return (int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(x * inv), -127.0f), 127.0f);
-}
-// Four INT8 codes into one word, lowest first.
-__device__ __forceinline__ int pack4(int a, int b, int c, int d) {
-    return (a & 0xFF) | ((b & 0xFF) << 8) | ((c & 0xFF) << 16) | ((int)((uint32_t)d << 24));
-}
-// 16 values (one lane half's keys or queries of a 32-group) -> v4i of codes
 __device__ __forceinline__ v4i pack16(const float* x, float inv) {
-    return v4i{pack4(q8(x[0], inv), q8(x[1], inv), q8(x[2], inv), q8(x[3], inv)),
-               pack4(q8(x[4], inv), q8(x[5], inv), q8(x[6], inv), q8(x[7], inv)),
-               pack4(q8(x[8], inv), q8(x[9], inv), q8(x[10], inv), q8(x[11], inv)),
-               pack4(q8(x[12], inv), q8(x[13], inv), q8(x[14], inv), q8(x[15], inv))};
-}
-
-// Largest value over the workgroup: wavefront maxima through LDS.
-__device__ __forceinline__ float block_max(float v, float* red, int w, int l) {
-    v = wave_max(v);
-    if (l == 0) red[w] = v;
-    __syncthreads();
-    const float r = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
-    return r;
+    return v4i{q8x4(x[0], x[1], x[2], x[3], inv), q8x4(x[4], x[5], x[6], x[7], inv),
+               q8x4(x[8], x[9], x[10], x[11], inv), q8x4(x[12], x[13], x[14], x[15], inv)};
 }
 
 // ------------------------------------------------------------------ preprocess
@@ -122,45 +105,79 @@ __global__ __launch_bounds__(256) void transpose_i8_kernel(const int8_t* __restr
 }
 
 // ------------------------------------------------------------------ dK, dV
+// Query-side tiles: "A" (Q codes, dO bf16, log-sum-exp, delta) in two slots,
+// "B" (channel-major dO and Q codes, read only by the last products of a
+// step) in one.  Step I: copy A(I+1) into the other slot, scores and
+// probabilities from A(I), wait for B(I), dV and dK from B(I), then copy
+// B(I+1) and wait for A(I+1): every copy has at least half a step to land.
 struct LdsKV {
-    uint8_t q[TQ * D];          // Q codes of the query tile, 128 x 128 B (sigma reads)
-    uint8_t dob[TQ * D * 2];    // dO bf16, 128 x 256 B (sigma reads)
+    uint8_t q[2][TQ * D];       // Q codes of the query tile, 128 x 128 B (sigma reads)
+    uint8_t dob[2][TQ * D * 2]; // dO bf16, 128 x 256 B (sigma reads)
+    float lse[2][TQ];
+    float dlt[2][TQ];
     uint8_t doT[D * TQ];        // dO codes channel-major, 128 ch x 128 B
     uint8_t qT[D * TQ];         // Q codes channel-major, 128 ch x 128 B
-    float lse[TQ];
-    float dlt[TQ];
     float red[8];
 };
-// the closing exchange of partial dV, dK reuses dob .. qT (64 KB)
-static_assert(sizeof(LdsKV) - __builtin_offsetof(LdsKV, dob) >= 2 * 2 * 32 * D * sizeof(float), "exchange area");
+// the closing exchange of partial dV, dK reuses dob (64 KB)
+static_assert(sizeof(((LdsKV*)0)->dob) >= 2 * 2 * 32 * D * sizeof(float), "exchange area");
 
-__device__ __forceinline__ void kv_issue_phase1(const SageBwdArgs& a, int bh, int b, int hq, int I, LdsKV& L, int w,
-                                                int l) {
+// One wavefront's share of the copies of a query tile, as per-lane offsets
+// from a tile base (the swizzles come from the source each lane names).
+struct KvPlan {
+    static constexpr int NA = 4 + 8 + 1, NB = 4 + 4;   // copies per wavefront: A tile, B tile
+    uint32_t q[4], g[8], t[4];
+    __device__ __forceinline__ KvPlan(int w, int l, int N, int64_t g_sN) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {      // Q codes: 16 x 1 KB (8 rows of 128 B)
+            const int r = 8 * (4 * w + u) + (l >> 3);
+            q[u] = (uint32_t)(r * D + 16 * ((l & 7) ^ fs128(r)));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {      // dO bf16: 32 x 1 KB (4 rows of 256 B)
+            const int r = 4 * (8 * w + u) + (l >> 4);
+            g[u] = (uint32_t)(2 * (r * g_sN + 8 * ((l & 15) ^ fs256(r))));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {      // channel-major codes: 16 x 1 KB (8 rows of 128 B)
+            const int r = 8 * (4 * w + u) + (l >> 3);
+            t[u] = (uint32_t)r * (uint32_t)N + (uint32_t)(16 * ((l & 7) ^ fc128(r)));
+        }
+    }
+};
+
+__device__ __forceinline__ void kv_copy_a(const SageBwdArgs& a, const KvPlan& cp, int bh, int b, int hq, int I, LdsKV& L,
+                                          int slot, int w, int l) {
     const int q0 = I * TQ;
+    const int8_t* qbase = a.qc + ((int64_t)bh * a.N + q0) * D;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {     // Q codes: 16 x 1 KB (8 rows each)
-        const int sgm = 4 * w + u, r = 8 * sgm + (l >> 3);
-        dma16(a.qc + ((int64_t)bh * a.N + q0 + r) * D + 16 * ((l & 7) ^ fs128(r)), L.q + 1024 * sgm);
-    }
-    const uint16_t* dob = (const uint16_t*)a.d_o.p + b * a.d_o.sB + hq * a.d_o.sH;
+    for (int u = 0; u < 4; ++u) lds_copy16(cp.q[u], qbase, lds_addr(L.q[slot] + 1024 * (4 * w + u)));
+    const uint16_t* gbase = (const uint16_t*)a.d_o.p + b * a.d_o.sB + hq * a.d_o.sH + (int64_t)q0 * a.d_o.sN;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {     // dO bf16: 32 x 1 KB (4 rows each)
-        const int sgm = 8 * w + u, r = 4 * sgm + (l >> 4);
-        dma16(dob + (int64_t)(q0 + r) * a.d_o.sN + 8 * ((l & 15) ^ fs256(r)), L.dob + 1024 * sgm);
-    }
+    for (int u = 0; u < 8; ++u) lds_copy16(cp.g[u], gbase, lds_addr(L.dob[slot] + 1024 * (8 * w + u)));
     // log-sum-exp and delta of the tile: one 256-byte copy per wavefront
-    if (w < 2) dma4(a.lse + (int64_t)bh * a.N + q0 + 64 * w + l, L.lse + 64 * w);
-    else dma4(a.delta + (int64_t)bh * a.N + q0 + 64 * (w - 2) + l, L.dlt + 64 * (w - 2));
+    if (w < 2) lds_copy4(4 * l, a.lse + (int64_t)bh * a.N + q0 + 64 * w, lds_addr(L.lse[slot] + 64 * w));
+    else lds_copy4(4 * l, a.delta + (int64_t)bh * a.N + q0 + 64 * (w - 2), lds_addr(L.dlt[slot] + 64 * (w - 2)));
 }
-__device__ __forceinline__ void kv_issue_phase2(const SageBwdArgs& a, int bh, int I, LdsKV& L, int w, int l) {
+__device__ __forceinline__ void kv_copy_b(const SageBwdArgs& a, const KvPlan& cp, int bh, int I, LdsKV& L, int w) {
     const int q0 = I * TQ;
+    const int8_t* gT = a.doT + (int64_t)bh * D * a.N + q0;
+    const int8_t* qT = a.qT + (int64_t)bh * D * a.N + q0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {     // channel-major dO and Q codes: 16 x 1 KB each (8 rows of 128 B)
-        const int sgm = 4 * w + u, r = 8 * sgm + (l >> 3);
-        const int c = (l & 7) ^ fc128(r);
-        dma16(a.doT + ((int64_t)bh * D + r) * a.N + q0 + 16 * c, L.doT + 1024 * sgm);
-        dma16(a.qT + ((int64_t)bh * D + r) * a.N + q0 + 16 * c, L.qT + 1024 * sgm);
+    for (int u = 0; u < 4; ++u) {
+        lds_copy16(cp.t[u], gT, lds_addr(L.doT + 1024 * (4 * w + u)));
+        lds_copy16(cp.t[u], qT, lds_addr(L.qT + 1024 * (4 * w + u)));
     }
+}
+
+// Largest value over the workgroup: wavefront maxima through LDS (a barrier
+// that leaves the copies in flight).
+__device__ __forceinline__ float block_max_nc(float v, float* red, int w, int l) {
+    v = wave_max(v);
+    if (l == 0) red[w] = v;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's LDS write is done
+    barrier_only();
+    return __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
 }
 
 __global__ __launch_bounds__(256, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
@@ -173,7 +190,10 @@ __global__ __launch_bounds__(256, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
     const int key = J * TK + 32 * kh + lq;
     const int qrow_s = sigma(lq);
     const float c = a.c_log2;
-    const float ks = a.ks[(int64_t)bh * nkt + J];
+    const auto qs_u = uniform_ptr(a.qs + (int64_t)bh * nqt);
+    const auto dos_u = uniform_ptr(a.dos + (int64_t)bh * nqt);
+    const float ks = uniform_ptr(a.ks)[(int64_t)bh * nkt + J];
+    const KvPlan cp(w, l, a.N, a.d_o.sN);
 
     // this lane's key: K codes (B operand of S = Q K^T) and V in bf16 (B operand of dP = dO V^T)
     v4i kb[4];
@@ -183,60 +203,67 @@ __global__ __launch_bounds__(256, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
     const uint16_t* vrow = (const uint16_t*)a.v.p + b * a.v.sB + hq * a.v.sH + (int64_t)key * a.v.sN;
 #pragma unroll
     for (int st = 0; st < 8; ++st) vb[st] = *(const v8bf*)(vrow + 16 * st + 8 * h);
+    __builtin_amdgcn_s_waitcnt(0);
 
     v16f dv[4], dk[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) { dv[cb] = v16f{}; dk[cb] = v16f{}; }
 
     const int I0 = a.causal ? (J * TK) / TQ : 0;
+    kv_copy_a(a, cp, bh, b, hq, I0, L, 0, w, l);
+    kv_copy_b(a, cp, bh, I0, L, w);
+    BQA_WAIT_VM(0);
+    barrier_only();
     for (int I = I0; I < nqt; ++I) {
-        __syncthreads();                              // the previous tile's reads are done
-        kv_issue_phase1(a, bh, b, hq, I, L, w, l);
-        kv_issue_phase2(a, bh, I, L, w, l);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        const float qsc = a.qs[(int64_t)bh * nqt + I];
+        const int s = (I - I0) & 1;
+        const bool more = I + 1 < nqt;
+        if (more) kv_copy_a(a, cp, bh, b, hq, I + 1, L, s ^ 1, w, l);   // that slot's reads ended a step ago
+        const float qsc = qs_u[I];
         const float sc = qsc * ks * c;
+        // causal: only the first query tile of the key block crosses the diagonal
+        const bool diag = a.causal && I == I0;
         // ---- S (int32), dP (fp32) for 2 groups of 32 queries x 32 keys; reg i of half h = query 16h + i
         float P[2][16], dS[2][16];
         float pmax = 0.0f, dmax = 0.0f;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             const int rq = 64 * qh + 32 * g + qrow_s;            // A row fed by this lane
-            v16i s = v16i{};
+            v16i sacc = v16i{};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const v4i av = *(const v4i*)(L.q + rq * 128 + 16 * ((2 * kk + h) ^ fs128(rq)));
-                s = mfma_i8_32x32x32(av, kb[kk], s);
+                const v4i av = *(const v4i*)(L.q[s] + rq * 128 + 16 * ((2 * kk + h) ^ fs128(rq)));
+                sacc = mfma_i8_32x32x32(av, kb[kk], sacc);
             }
             v16f dp = v16f{};
 #pragma unroll
             for (int st = 0; st < 8; ++st) {
-                const v8bf av = *(const v8bf*)(L.dob + rq * 256 + 16 * ((2 * st + h) ^ fs256(rq)));
+                const v8bf av = *(const v8bf*)(L.dob[s] + rq * 256 + 16 * ((2 * st + h) ^ fs256(rq)));
                 dp = mfma_bf16_32x32x16(av, vb[st], dp);
             }
             const int qb0 = 64 * qh + 32 * g + 16 * h;           // tile-local query of register 0
             v4f lse4[4], dl4[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                lse4[u] = *(const v4f*)(L.lse + qb0 + 4 * u);
-                dl4[u] = *(const v4f*)(L.dlt + qb0 + 4 * u);
+                lse4[u] = *(const v4f*)(L.lse[s] + qb0 + 4 * u);
+                dl4[u] = *(const v4f*)(L.dlt[s] + qb0 + 4 * u);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                P[g][i] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sacc[i], sc, -lse4[i >> 2][i & 3] * 1.4426950408889634f));
+            if (diag) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) P[g][i] = key > I * TQ + qb0 + i ? 0.0f : P[g][i];
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int qpos = I * TQ + qb0 + i;
-                float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[i], sc, -lse4[i >> 2][i & 3] * 1.4426950408889634f));
-                if (a.causal && key > qpos) p = 0.0f;
-                const float ds = p * (dp[i] - dl4[i >> 2][i & 3]);
-                P[g][i] = p;
-                dS[g][i] = ds;
-                pmax = __builtin_fmaxf(pmax, p);
-                dmax = __builtin_fmaxf(dmax, __builtin_fabsf(ds));
+                dS[g][i] = P[g][i] * (dp[i] - dl4[i >> 2][i & 3]);
+                pmax = __builtin_fmaxf(pmax, P[g][i]);
+                dmax = __builtin_fmaxf(dmax, __builtin_fabsf(dS[g][i]));
             }
         }
         // ---- one INT8 scale per tile for P and for dS
-        pmax = block_max(pmax, L.red, w, l);
-        dmax = block_max(dmax, L.red + 4, w, l);
+        pmax = block_max_nc(pmax, L.red, w, l);
+        dmax = block_max_nc(dmax, L.red + 4, w, l);
         const float inv_p = pmax > 0.0f ? 127.0f / pmax : 0.0f;
         const float inv_d = dmax > 0.0f ? 127.0f / dmax : 0.0f;
         const bool p_ok = inv_p != 0.0f && inv_p < __builtin_inff();
@@ -247,9 +274,13 @@ __global__ __launch_bounds__(256, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
             pa[g] = p_ok ? pack16(P[g], inv_p) : v4i{};
             da[g] = d_ok ? pack16(dS[g], inv_d) : v4i{};
         }
-        // ---- dV += P^T dO, dK += tau dS^T Q (keys x channels), K-steps = the 2 query groups
-        const float sv = p_ok ? pmax * (1.0f / 127.0f) * a.dos[(int64_t)bh * nqt + I] : 0.0f;
+        const float sv = p_ok ? pmax * (1.0f / 127.0f) * dos_u[I] : 0.0f;
         const float sk = d_ok ? dmax * (1.0f / 127.0f) * qsc * a.tau : 0.0f;
+        // ---- B(I) landed (the copies of A(I+1) may stay in flight)
+        if (more) BQA_WAIT_VM(KvPlan::NA);
+        else BQA_WAIT_VM(0);
+        barrier_only();
+        // ---- dV += P^T dO, dK += tau dS^T Q (keys x channels), K-steps = the 2 query groups
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             const int rr = 32 * cb + lq;
@@ -268,9 +299,18 @@ __global__ __launch_bounds__(256, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
                 dk[cb][i] = __builtin_fmaf((float)tk[i], sk, dk[cb][i]);
             }
         }
+        // ---- B is free: copy B(I+1); then A(I+1) must have landed
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's reads of B are done
+        barrier_only();
+        if (more) {
+            kv_copy_b(a, cp, bh, I + 1, L, w);
+            BQA_WAIT_VM(KvPlan::NB);
+        } else {
+            BQA_WAIT_VM(0);
+        }
+        barrier_only();
     }
     // ---- the two query halves of each key half: sum through LDS, write bf16
-    __syncthreads();
     float* xch = (float*)L.dob;                      // 2 key halves x (dV, dK) x 32 keys x 128 channels
     if (qh == 1) {
 #pragma unroll
@@ -305,24 +345,39 @@ struct LdsQ {
     uint8_t kT[D * TK];         // K codes channel-major, 128 ch x 64 B
 };
 
-__device__ __forceinline__ void q_issue(const SageBwdArgs& a, int bh, int b, int hq, int J, LdsQ& L, int w, int l) {
+struct QPlan {
+    uint32_t k[2], v[4], t[2];
+    __device__ __forceinline__ QPlan(int w, int l, int Ntok, int64_t v_sN) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {      // K codes: 8 x 1 KB (8 rows of 128 B)
+            const int r = 8 * (2 * w + u) + (l >> 3);
+            k[u] = (uint32_t)(r * D + 16 * ((l & 7) ^ fs128(r)));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {      // V bf16: 16 x 1 KB (4 rows of 256 B)
+            const int r = 4 * (4 * w + u) + (l >> 4);
+            v[u] = (uint32_t)(2 * (r * v_sN + 8 * ((l & 15) ^ fs256(r))));
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {      // channel-major K codes: 8 x 1 KB (16 rows of 64 B)
+            const int r = 16 * (2 * w + u) + (l >> 2);
+            t[u] = (uint32_t)r * (uint32_t)Ntok + (uint32_t)(16 * ((l & 3) ^ fc64(r)));
+        }
+    }
+};
+
+__device__ __forceinline__ void q_copy(const SageBwdArgs& a, const QPlan& cp, int bh, int b, int hq, int J, LdsQ& L,
+                                       int w) {
     const int k0 = J * TK;
+    const int8_t* kbase = a.kc + ((int64_t)bh * a.N + k0) * D;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {     // K codes: 8 x 1 KB (8 rows of 128 B)
-        const int sgm = 2 * w + u, r = 8 * sgm + (l >> 3);
-        dma16(a.kc + ((int64_t)bh * a.N + k0 + r) * D + 16 * ((l & 7) ^ fs128(r)), L.k + 1024 * sgm);
-    }
-    const uint16_t* vb = (const uint16_t*)a.v.p + b * a.v.sB + hq * a.v.sH;
+    for (int u = 0; u < 2; ++u) lds_copy16(cp.k[u], kbase, lds_addr(L.k + 1024 * (2 * w + u)));
+    const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.sB + hq * a.v.sH + (int64_t)k0 * a.v.sN;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {     // V bf16: 16 x 1 KB (4 rows of 256 B)
-        const int sgm = 4 * w + u, r = 4 * sgm + (l >> 4);
-        dma16(vb + (int64_t)(k0 + r) * a.v.sN + 8 * ((l & 15) ^ fs256(r)), L.vb + 1024 * sgm);
-    }
+    for (int u = 0; u < 4; ++u) lds_copy16(cp.v[u], vbase, lds_addr(L.vb + 1024 * (4 * w + u)));
+    const int8_t* tbase = a.kT + (int64_t)bh * D * a.N + k0;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {     // channel-major K codes: 8 x 1 KB (16 rows of 64 B)
-        const int sgm = 2 * w + u, r = 16 * sgm + (l >> 2);
-        dma16(a.kT + ((int64_t)bh * D + r) * a.N + k0 + 16 * ((l & 3) ^ fc64(r)), L.kT + 1024 * sgm);
-    }
+    for (int u = 0; u < 2; ++u) lds_copy16(cp.t[u], tbase, lds_addr(L.kT + 1024 * (2 * w + u)));
 }
 
 __global__ __launch_bounds__(256, 2) void sbwd_dq_kernel(SageBwdArgs a) {
@@ -335,7 +390,9 @@ __global__ __launch_bounds__(256, 2) void sbwd_dq_kernel(SageBwdArgs a) {
     const int qrow = I * TQ + 32 * w + lq;
     const int krow = sigma(lq);
     const float c = a.c_log2;
-    const float qsc = a.qs[(int64_t)bh * nqt + I];
+    const float qsc = uniform_ptr(a.qs)[(int64_t)bh * nqt + I];
+    const auto ks_u = uniform_ptr(a.ks + (int64_t)bh * nkt);
+    const QPlan cp(w, l, a.N, a.v.sN);
 
     // this lane's query: codes (B operand of S^T = K Q^T), dO bf16 (B operand of dP^T = V dO^T)
     v4i qb[4];
@@ -347,31 +404,35 @@ __global__ __launch_bounds__(256, 2) void sbwd_dq_kernel(SageBwdArgs a) {
     for (int st = 0; st < 8; ++st) gb[st] = *(const v8bf*)(grow + 16 * st + 8 * h);
     const float lse2 = a.lse[(int64_t)bh * a.N + qrow] * 1.4426950408889634f;
     const float dlt = a.delta[(int64_t)bh * a.N + qrow];
+    __builtin_amdgcn_s_waitcnt(0);
 
     v16f dq[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) dq[cb] = v16f{};
 
     const int nJ = a.causal ? (I * TQ + TQ - 1) / TK + 1 : nkt;
-    q_issue(a, bh, b, hq, 0, L[0], w, l);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    q_copy(a, cp, bh, b, hq, 0, L[0], w);
+    BQA_WAIT_VM(0);
+    barrier_only();
     for (int J = 0; J < nJ; ++J) {
         const int cur = J & 1;
-        if (J + 1 < nJ) q_issue(a, bh, b, hq, J + 1, L[cur ^ 1], w, l);
+        const bool more = J + 1 < nJ;
+        if (more) q_copy(a, cp, bh, b, hq, J + 1, L[cur ^ 1], w);   // that buffer's reads ended a step ago
         const LdsQ& T = L[cur];
-        const float ks = a.ks[(int64_t)bh * nkt + J];
+        const float ks = ks_u[J];
         const float sc = qsc * ks * c;
-        float P[2][16], dS[2][16];
+        // causal: key tiles past the first query of the tile cross the diagonal
+        const bool diag = a.causal && J * TK + TK - 1 > I * TQ;
+        float dS[2][16];
         float dmax = 0.0f;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             const int rk = 32 * g + krow;
-            v16i s = v16i{};
+            v16i sacc = v16i{};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const v4i av = *(const v4i*)(T.k + rk * 128 + 16 * ((2 * kk + h) ^ fs128(rk)));
-                s = mfma_i8_32x32x32(av, qb[kk], s);
+                sacc = mfma_i8_32x32x32(av, qb[kk], sacc);
             }
             v16f dp = v16f{};
 #pragma unroll
@@ -379,19 +440,20 @@ __global__ __launch_bounds__(256, 2) void sbwd_dq_kernel(SageBwdArgs a) {
                 const v8bf av = *(const v8bf*)(T.vb + rk * 256 + 16 * ((2 * st + h) ^ fs256(rk)));
                 dp = mfma_bf16_32x32x16(av, gb[st], dp);
             }
+            float p[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sacc[i], sc, -lse2));
+            if (diag) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) p[i] = J * TK + 32 * g + 16 * h + i > qrow ? 0.0f : p[i];
+            }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int kpos = J * TK + 32 * g + 16 * h + i;
-                float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[i], sc, -lse2));
-                if (a.causal && kpos > qrow) p = 0.0f;
-                const float ds = p * (dp[i] - dlt);
-                P[g][i] = p;
-                dS[g][i] = ds;
-                dmax = __builtin_fmaxf(dmax, __builtin_fabsf(ds));
+                dS[g][i] = p[i] * (dp[i] - dlt);
+                dmax = __builtin_fmaxf(dmax, __builtin_fabsf(dS[g][i]));
             }
         }
-        (void)P;
-        dmax = block_max(dmax, red + 4 * (J & 1), w, l);
+        dmax = block_max_nc(dmax, red + 4 * (J & 1), w, l);
         const float inv_d = dmax > 0.0f ? 127.0f / dmax : 0.0f;
         const bool d_ok = inv_d != 0.0f && inv_d < __builtin_inff();
         v4i da[2];
@@ -411,8 +473,9 @@ __global__ __launch_bounds__(256, 2) void sbwd_dq_kernel(SageBwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) dq[cb][i] = __builtin_fmaf((float)t[i], sq, dq[cb][i]);
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        // the next key tile landed, and every wavefront is done with this one
+        BQA_WAIT_VM(0);
+        barrier_only();
     }
     // dq[cb] reg i: query 32 w + 8 (i / 4) + 4 h + i % 4, channel 32 cb + lq
     uint16_t* dqp = (uint16_t*)a.dq.p + b * a.dq.sB + hq * a.dq.sH;

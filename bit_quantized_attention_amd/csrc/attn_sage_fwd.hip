@@ -481,18 +481,6 @@ __global__ __launch_bounds__(256, (PV == PV_F16 || !CAUSAL) ? 2 : 3) void sage_f
 // kernel's own counted waits instead of waiting for every copy in flight
 // before any LDS read.
 constexpr int PRING = 4;
-
-__device__ __forceinline__ void copy16(uint32_t voff, const void* sbase, uint32_t lds) {
-    // M0 holds the LDS destination; one wait state before the copy reads it.
-    // M0 is reserved to the compiler, which sets it right before each of its
-    // own users (none in this kernel), so it is not named as a clobber.
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
-                 : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
-}
-
 // Per-lane source offsets of one wavefront's share of a K tile and a V^T tile
 // (1 KB segments; the LDS swizzle comes from the source each lane names).
 template <int D>
@@ -518,11 +506,11 @@ struct CopyPlan {
     }
     __device__ __forceinline__ void k_tile(const int8_t* kbase, int t0, const uint8_t* kl, int w) const {
 #pragma unroll
-        for (int u = 0; u < KU; ++u) copy16(koff[u], kbase + (int64_t)t0 * D, lds_addr(kl) + 1024 * (KU * w + u));
+        for (int u = 0; u < KU; ++u) lds_copy16(koff[u], kbase + (int64_t)t0 * D, lds_addr(kl) + 1024 * (KU * w + u));
     }
     __device__ __forceinline__ void v_tile(const uint8_t* vbase, int t0, const uint8_t* vl, int w) const {
 #pragma unroll
-        for (int u = 0; u < VU; ++u) copy16(voff[u], vbase + t0, lds_addr(vl) + 1024 * (VU * w + u));
+        for (int u = 0; u < VU; ++u) lds_copy16(voff[u], vbase + t0, lds_addr(vl) + 1024 * (VU * w + u));
     }
 };
 

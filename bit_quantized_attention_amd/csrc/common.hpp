@@ -39,6 +39,38 @@ __device__ __forceinline__ float partner32f(float x) {
     return __builtin_bit_cast(float, partner32(__builtin_bit_cast(int, x)));
 }
 
+// ------------------------------------------------------------------ LDS copies
+// Direct global -> LDS copies (global_load_lds, scalar base + per-lane 32-bit
+// offset): lane i's 16 (4) bytes land at lds + 16 i (4 i).  They are issued
+// from inline assembly, so the compiler does not track them (it would
+// otherwise wait for every copy in flight before any LDS read): the caller
+// waits for them with s_waitcnt vmcnt and makes them visible to the other
+// wavefronts with a barrier.  M0 holds the LDS destination, one wait state
+// before the copy reads it; M0 is reserved to the compiler, which sets it
+// right before each of its own users, so it is not named as a clobber.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+__device__ __forceinline__ void lds_copy16(uint32_t voff, const void* sbase, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "memory");
+}
+__device__ __forceinline__ void lds_copy4(uint32_t voff, const void* sbase, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "memory");
+}
+// s_waitcnt with vmcnt(n) (n < 16) and lgkmcnt(0), expcnt not waited for
+#define BQA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0070 | (n))
+// A workgroup barrier that does not wait for the copies above (the barrier of
+// __syncthreads carries a fence that waits for every memory operation)
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+// Scalar-cache view of a uniform array (loads become s_load, counted by
+// lgkmcnt, so they never wait for the copies above)
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* uniform_ptr(const T* p) {
+    return (const __attribute__((address_space(4))) T*)p;
+}
+
 // ------------------------------------------------------------------ MFMA
 __device__ __forceinline__ v16i mfma_i8_32x32x32(v4i a, v4i b, v16i c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
