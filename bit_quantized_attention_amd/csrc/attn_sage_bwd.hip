@@ -105,11 +105,19 @@ __global__ __launch_bounds__(256) void transpose_i8_kernel(const int8_t* __restr
 }
 
 // ------------------------------------------------------------------ dK, dV
+// One workgroup of 8 wavefronts per 64-key block, over the query tiles.
+// Step I has two phases.  Scores: wavefront (kh, qg) computes S and dP for
+// its 32 keys x 32 queries with keys in lanes, then P and dS; after the
+// tile's maxima it writes their INT8 codes, key-major, to LDS.  Products:
+// wavefront (kh, cq) accumulates dV and dK for its 32 keys x 32 channels over
+// the tile's 128 queries (P^T and dS^T codes from LDS, channel-major dO and Q
+// codes).  Each wavefront thus holds 32 accumulator registers, which lets
+// two of them share a SIMD.
+//
 // Query-side tiles: "A" (Q codes, dO bf16, log-sum-exp, delta) in two slots,
-// "B" (channel-major dO and Q codes, read only by the last products of a
-// step) in one.  Step I: copy A(I+1) into the other slot, scores and
-// probabilities from A(I), wait for B(I), dV and dK from B(I), then copy
-// B(I+1) and wait for A(I+1): every copy has at least half a step to land.
+// "B" (channel-major dO and Q codes, read by the products only) in one.  The
+// copy of A(I+1) is issued at the start of step I, the copy of B(I+1) after
+// the products of step I: every copy has at least half a step to land.
 struct LdsKV {
     uint8_t q[2][TQ * D];       // Q codes of the query tile, 128 x 128 B (sigma reads)
     uint8_t dob[2][TQ * D * 2]; // dO bf16, 128 x 256 B (sigma reads)
@@ -117,30 +125,30 @@ struct LdsKV {
     float dlt[2][TQ];
     uint8_t doT[D * TQ];        // dO codes channel-major, 128 ch x 128 B
     uint8_t qT[D * TQ];         // Q codes channel-major, 128 ch x 128 B
-    float red[8];
+    uint8_t pc[TK * TQ];        // P^T codes, 64 keys x 128 B
+    uint8_t dc[TK * TQ];        // dS^T codes
+    float red[16];
 };
-// the closing exchange of partial dV, dK reuses dob (64 KB)
-static_assert(sizeof(((LdsKV*)0)->dob) >= 2 * 2 * 32 * D * sizeof(float), "exchange area");
 
 // One wavefront's share of the copies of a query tile, as per-lane offsets
 // from a tile base (the swizzles come from the source each lane names).
 struct KvPlan {
-    static constexpr int NA = 4 + 8 + 1, NB = 4 + 4;   // copies per wavefront: A tile, B tile
-    uint32_t q[4], g[8], t[4];
+    static constexpr int NA = 2 + 4 + 1, NB = 2 + 2;   // copies per wavefront: A tile, B tile
+    uint32_t q[2], g[4], t[2];
     __device__ __forceinline__ KvPlan(int w, int l, int N, int64_t g_sN) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {      // Q codes: 16 x 1 KB (8 rows of 128 B)
-            const int r = 8 * (4 * w + u) + (l >> 3);
+        for (int u = 0; u < 2; ++u) {      // Q codes: 16 x 1 KB (8 rows of 128 B)
+            const int r = 8 * (2 * w + u) + (l >> 3);
             q[u] = (uint32_t)(r * D + 16 * ((l & 7) ^ fs128(r)));
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {      // dO bf16: 32 x 1 KB (4 rows of 256 B)
-            const int r = 4 * (8 * w + u) + (l >> 4);
+        for (int u = 0; u < 4; ++u) {      // dO bf16: 32 x 1 KB (4 rows of 256 B)
+            const int r = 4 * (4 * w + u) + (l >> 4);
             g[u] = (uint32_t)(2 * (r * g_sN + 8 * ((l & 15) ^ fs256(r))));
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {      // channel-major codes: 16 x 1 KB (8 rows of 128 B)
-            const int r = 8 * (4 * w + u) + (l >> 3);
+        for (int u = 0; u < 2; ++u) {      // channel-major codes: 16 x 1 KB each (8 rows of 128 B)
+            const int r = 8 * (2 * w + u) + (l >> 3);
             t[u] = (uint32_t)r * (uint32_t)N + (uint32_t)(16 * ((l & 7) ^ fc128(r)));
         }
     }
@@ -151,42 +159,46 @@ __device__ __forceinline__ void kv_copy_a(const SageBwdArgs& a, const KvPlan& cp
     const int q0 = I * TQ;
     const int8_t* qbase = a.qc + ((int64_t)bh * a.N + q0) * D;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) lds_copy16(cp.q[u], qbase, lds_addr(L.q[slot] + 1024 * (4 * w + u)));
+    for (int u = 0; u < 2; ++u) lds_copy16(cp.q[u], qbase, lds_addr(L.q[slot] + 1024 * (2 * w + u)));
     const uint16_t* gbase = (const uint16_t*)a.d_o.p + b * a.d_o.sB + hq * a.d_o.sH + (int64_t)q0 * a.d_o.sN;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) lds_copy16(cp.g[u], gbase, lds_addr(L.dob[slot] + 1024 * (8 * w + u)));
-    // log-sum-exp and delta of the tile: one 256-byte copy per wavefront
-    if (w < 2) lds_copy4(4 * l, a.lse + (int64_t)bh * a.N + q0 + 64 * w, lds_addr(L.lse[slot] + 64 * w));
-    else lds_copy4(4 * l, a.delta + (int64_t)bh * a.N + q0 + 64 * (w - 2), lds_addr(L.dlt[slot] + 64 * (w - 2)));
+    for (int u = 0; u < 4; ++u) lds_copy16(cp.g[u], gbase, lds_addr(L.dob[slot] + 1024 * (4 * w + u)));
+    // log-sum-exp and delta of the tile: 256-byte copies by wavefronts 0-3,
+    // repeated by 4-7 (same bytes) so every wavefront counts the same copies
+    const int v = w & 3;
+    if (v < 2) lds_copy4(4 * l, a.lse + (int64_t)bh * a.N + q0 + 64 * v, lds_addr(L.lse[slot] + 64 * v));
+    else lds_copy4(4 * l, a.delta + (int64_t)bh * a.N + q0 + 64 * (v - 2), lds_addr(L.dlt[slot] + 64 * (v - 2)));
 }
 __device__ __forceinline__ void kv_copy_b(const SageBwdArgs& a, const KvPlan& cp, int bh, int I, LdsKV& L, int w) {
     const int q0 = I * TQ;
     const int8_t* gT = a.doT + (int64_t)bh * D * a.N + q0;
     const int8_t* qT = a.qT + (int64_t)bh * D * a.N + q0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        lds_copy16(cp.t[u], gT, lds_addr(L.doT + 1024 * (4 * w + u)));
-        lds_copy16(cp.t[u], qT, lds_addr(L.qT + 1024 * (4 * w + u)));
+    for (int u = 0; u < 2; ++u) {
+        lds_copy16(cp.t[u], gT, lds_addr(L.doT + 1024 * (2 * w + u)));
+        lds_copy16(cp.t[u], qT, lds_addr(L.qT + 1024 * (2 * w + u)));
     }
 }
 
-// Largest value over the workgroup: wavefront maxima through LDS (a barrier
-// that leaves the copies in flight).
-__device__ __forceinline__ float block_max_nc(float v, float* red, int w, int l) {
+// Largest value over the 8 wavefronts: wavefront maxima through LDS (a
+// barrier that leaves the copies in flight).
+__device__ __forceinline__ float block_max8(float v, float* red, int w, int l) {
     v = wave_max(v);
     if (l == 0) red[w] = v;
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's LDS write is done
     barrier_only();
-    return __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    const v4f r0 = *(const v4f*)red, r1 = *(const v4f*)(red + 4);
+    return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(r0[0], r0[1]), __builtin_fmaxf(r0[2], r0[3])),
+                           __builtin_fmaxf(__builtin_fmaxf(r1[0], r1[1]), __builtin_fmaxf(r1[2], r1[3])));
 }
 
-__global__ __launch_bounds__(256, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
+__global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
     __shared__ __attribute__((aligned(16))) LdsKV L;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
     const int nkt = a.N / TK, nqt = a.N / TQ;
     const int J = blockIdx.x % nkt;                  // ascending J: the longest query ranges first
     const int bh = blockIdx.x / nkt, b = bh / a.H, hq = bh % a.H;
-    const int kh = w & 1, qh = w >> 1;               // the wavefront's 32 keys and 64 queries of the tile
+    const int kh = w & 1, qg = w >> 1;               // scores: 32 keys x 32 queries; products: 32 keys x 32 channels
     const int key = J * TK + 32 * kh + lq;
     const int qrow_s = sigma(lq);
     const float c = a.c_log2;
@@ -205,9 +217,9 @@ __global__ __launch_bounds__(256, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
     for (int st = 0; st < 8; ++st) vb[st] = *(const v8bf*)(vrow + 16 * st + 8 * h);
     __builtin_amdgcn_s_waitcnt(0);
 
-    v16f dv[4], dk[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) { dv[cb] = v16f{}; dk[cb] = v16f{}; }
+    v16f dv = v16f{}, dk = v16f{};                   // keys 32 kh + 8 (i/4) + 4 h + i%4, channel 32 qg + lq
+    const int prow = 32 * kh + lq;                   // key row of the P^T / dS^T codes this lane writes and reads
+    const int crow = 32 * qg + lq;                   // channel row of doT / qT this lane reads
 
     const int I0 = a.causal ? (J * TK) / TQ : 0;
     kv_copy_a(a, cp, bh, b, hq, I0, L, 0, w, l);
@@ -220,87 +232,81 @@ __global__ __launch_bounds__(256, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
         if (more) kv_copy_a(a, cp, bh, b, hq, I + 1, L, s ^ 1, w, l);   // that slot's reads ended a step ago
         const float qsc = qs_u[I];
         const float sc = qsc * ks * c;
+        // ---- scores: S (int32), dP (fp32) of 32 queries x 32 keys; reg i of half h = query 16h + i
+        const int rq = 32 * qg + qrow_s;             // A row fed by this lane
+        v16i sacc = v16i{};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const v4i av = *(const v4i*)(L.q[s] + rq * 128 + 16 * ((2 * kk + h) ^ fs128(rq)));
+            sacc = mfma_i8_32x32x32(av, kb[kk], sacc);
+        }
+        v16f dp = v16f{};
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const v8bf av = *(const v8bf*)(L.dob[s] + rq * 256 + 16 * ((2 * st + h) ^ fs256(rq)));
+            dp = mfma_bf16_32x32x16(av, vb[st], dp);
+        }
+        const int qb0 = 32 * qg + 16 * h;            // tile-local query of register 0
+        float P[16], dS[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const v4f lse4 = *(const v4f*)(L.lse[s] + qb0 + 4 * u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                P[4 * u + e] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sacc[4 * u + e], sc, -lse4[e] * 1.4426950408889634f));
+        }
         // causal: only the first query tile of the key block crosses the diagonal
-        const bool diag = a.causal && I == I0;
-        // ---- S (int32), dP (fp32) for 2 groups of 32 queries x 32 keys; reg i of half h = query 16h + i
-        float P[2][16], dS[2][16];
+        if (a.causal && I == I0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) P[i] = key > I * TQ + qb0 + i ? 0.0f : P[i];
+        }
         float pmax = 0.0f, dmax = 0.0f;
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const int rq = 64 * qh + 32 * g + qrow_s;            // A row fed by this lane
-            v16i sacc = v16i{};
+        for (int u = 0; u < 4; ++u) {
+            const v4f dl4 = *(const v4f*)(L.dlt[s] + qb0 + 4 * u);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const v4i av = *(const v4i*)(L.q[s] + rq * 128 + 16 * ((2 * kk + h) ^ fs128(rq)));
-                sacc = mfma_i8_32x32x32(av, kb[kk], sacc);
-            }
-            v16f dp = v16f{};
-#pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                const v8bf av = *(const v8bf*)(L.dob[s] + rq * 256 + 16 * ((2 * st + h) ^ fs256(rq)));
-                dp = mfma_bf16_32x32x16(av, vb[st], dp);
-            }
-            const int qb0 = 64 * qh + 32 * g + 16 * h;           // tile-local query of register 0
-            v4f lse4[4], dl4[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                lse4[u] = *(const v4f*)(L.lse[s] + qb0 + 4 * u);
-                dl4[u] = *(const v4f*)(L.dlt[s] + qb0 + 4 * u);
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                P[g][i] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sacc[i], sc, -lse4[i >> 2][i & 3] * 1.4426950408889634f));
-            if (diag) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) P[g][i] = key > I * TQ + qb0 + i ? 0.0f : P[g][i];
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                dS[g][i] = P[g][i] * (dp[i] - dl4[i >> 2][i & 3]);
-                pmax = __builtin_fmaxf(pmax, P[g][i]);
-                dmax = __builtin_fmaxf(dmax, __builtin_fabsf(dS[g][i]));
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * u + e;
+                dS[i] = P[i] * (dp[i] - dl4[e]);
+                pmax = __builtin_fmaxf(pmax, P[i]);
+                dmax = __builtin_fmaxf(dmax, __builtin_fabsf(dS[i]));
             }
         }
-        // ---- one INT8 scale per tile for P and for dS
-        pmax = block_max_nc(pmax, L.red, w, l);
-        dmax = block_max_nc(dmax, L.red + 4, w, l);
+        // ---- one INT8 scale per tile for P and for dS; codes to LDS, key-major
+        pmax = block_max8(pmax, L.red, w, l);
+        dmax = block_max8(dmax, L.red + 8, w, l);
         const float inv_p = pmax > 0.0f ? 127.0f / pmax : 0.0f;
         const float inv_d = dmax > 0.0f ? 127.0f / dmax : 0.0f;
         const bool p_ok = inv_p != 0.0f && inv_p < __builtin_inff();
         const bool d_ok = inv_d != 0.0f && inv_d < __builtin_inff();
-        v4i pa[2], da[2];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            pa[g] = p_ok ? pack16(P[g], inv_p) : v4i{};
-            da[g] = d_ok ? pack16(dS[g], inv_d) : v4i{};
-        }
+        const int wch = (2 * qg + h) ^ fc128(prow);  // this lane's 16 queries: chunk 2 qg + h of its key row
+        *(v4i*)(L.pc + prow * 128 + 16 * wch) = p_ok ? pack16(P, inv_p) : v4i{};
+        *(v4i*)(L.dc + prow * 128 + 16 * wch) = d_ok ? pack16(dS, inv_d) : v4i{};
         const float sv = p_ok ? pmax * (1.0f / 127.0f) * dos_u[I] : 0.0f;
         const float sk = d_ok ? dmax * (1.0f / 127.0f) * qsc * a.tau : 0.0f;
-        // ---- B(I) landed (the copies of A(I+1) may stay in flight)
+        // ---- codes written, B(I) landed (the copies of A(I+1) may stay in flight)
         if (more) BQA_WAIT_VM(KvPlan::NA);
         else BQA_WAIT_VM(0);
         barrier_only();
-        // ---- dV += P^T dO, dK += tau dS^T Q (keys x channels), K-steps = the 2 query groups
+        // ---- products: dV += P^T dO, dK += tau dS^T Q over the 4 groups of 32 queries
+        v16i tv = v16i{}, tk = v16i{};
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            const int rr = 32 * cb + lq;
-            v16i tv = v16i{}, tk = v16i{};
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                const int ch = 4 * qh + 2 * g + h;                   // 16-query chunk of the row
-                const v4i bo = *(const v4i*)(L.doT + rr * 128 + 16 * (ch ^ fc128(rr)));
-                const v4i bq = *(const v4i*)(L.qT + rr * 128 + 16 * (ch ^ fc128(rr)));
-                tv = mfma_i8_32x32x32(pa[g], bo, tv);
-                tk = mfma_i8_32x32x32(da[g], bq, tk);
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                dv[cb][i] = __builtin_fmaf((float)tv[i], sv, dv[cb][i]);
-                dk[cb][i] = __builtin_fmaf((float)tk[i], sk, dk[cb][i]);
-            }
+        for (int kq = 0; kq < 4; ++kq) {
+            const int ch = 2 * kq + h;
+            const v4i ap = *(const v4i*)(L.pc + prow * 128 + 16 * (ch ^ fc128(prow)));
+            const v4i ad = *(const v4i*)(L.dc + prow * 128 + 16 * (ch ^ fc128(prow)));
+            const v4i bo = *(const v4i*)(L.doT + crow * 128 + 16 * (ch ^ fc128(crow)));
+            const v4i bq = *(const v4i*)(L.qT + crow * 128 + 16 * (ch ^ fc128(crow)));
+            tv = mfma_i8_32x32x32(ap, bo, tv);
+            tk = mfma_i8_32x32x32(ad, bq, tk);
         }
-        // ---- B is free: copy B(I+1); then A(I+1) must have landed
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's reads of B are done
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            dv[i] = __builtin_fmaf((float)tv[i], sv, dv[i]);
+            dk[i] = __builtin_fmaf((float)tk[i], sk, dk[i]);
+        }
+        // ---- B and the codes are free: copy B(I+1); then A(I+1) must have landed
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's LDS reads are done
         barrier_only();
         if (more) {
             kv_copy_b(a, cp, bh, I + 1, L, w);
@@ -310,31 +316,13 @@ __global__ __launch_bounds__(256, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
         }
         barrier_only();
     }
-    // ---- the two query halves of each key half: sum through LDS, write bf16
-    float* xch = (float*)L.dob;                      // 2 key halves x (dV, dK) x 32 keys x 128 channels
-    if (qh == 1) {
+    uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sB + hq * a.dv.sH;
+    uint16_t* dkp = (uint16_t*)a.dk.p + b * a.dk.sB + hq * a.dk.sH;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kr = 8 * (i >> 2) + 4 * h + (i & 3), ch = 32 * cb + lq;
-                xch[((kh * 2 + 0) * 32 + kr) * D + ch] = dv[cb][i];
-                xch[((kh * 2 + 1) * 32 + kr) * D + ch] = dk[cb][i];
-            }
-    }
-    __syncthreads();
-    if (qh == 0) {
-        uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sB + hq * a.dv.sH;
-        uint16_t* dkp = (uint16_t*)a.dk.p + b * a.dk.sB + hq * a.dk.sH;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kr = 8 * (i >> 2) + 4 * h + (i & 3), ch = 32 * cb + lq;
-                const int64_t kpos = (int64_t)J * TK + 32 * kh + kr;
-                dvp[kpos * a.dv.sN + ch] = f32_to_bf16_bits(dv[cb][i] + xch[((kh * 2 + 0) * 32 + kr) * D + ch]);
-                dkp[kpos * a.dk.sN + ch] = f32_to_bf16_bits(dk[cb][i] + xch[((kh * 2 + 1) * 32 + kr) * D + ch]);
-            }
+    for (int i = 0; i < 16; ++i) {
+        const int64_t kpos = (int64_t)J * TK + 32 * kh + 8 * (i >> 2) + 4 * h + (i & 3);
+        dvp[kpos * a.dv.sN + crow] = f32_to_bf16_bits(dv[i]);
+        dkp[kpos * a.dk.sN + crow] = f32_to_bf16_bits(dk[i]);
     }
 }
 
@@ -344,6 +332,15 @@ struct LdsQ {
     uint8_t vb[TK * D * 2];     // V bf16, 64 x 256 B (sigma reads)
     uint8_t kT[D * TK];         // K codes channel-major, 128 ch x 64 B
 };
+
+// Largest value over the 4 wavefronts (same scheme as block_max8).
+__device__ __forceinline__ float block_max_nc(float v, float* red, int w, int l) {
+    v = wave_max(v);
+    if (l == 0) red[w] = v;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's LDS write is done
+    barrier_only();
+    return __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+}
 
 struct QPlan {
     uint32_t k[2], v[4], t[2];
@@ -519,7 +516,7 @@ hipError_t launch_sage_bwd(SageBwdArgs a, Dense o, void* ws, hipStream_t st) {
     transpose_i8_kernel<<<tgrid, 256, 0, st>>>(doc, a.N, D, doT);
     transpose_i8_kernel<<<tgrid, 256, 0, st>>>(a.qc, a.N, D, qT);
     transpose_i8_kernel<<<tgrid, 256, 0, st>>>(a.kc, a.N, D, kT);
-    sbwd_dkdv_kernel<<<a.B * a.H * (a.N / TK), 256, 0, st>>>(a);
+    sbwd_dkdv_kernel<<<a.B * a.H * (a.N / TK), 512, 0, st>>>(a);
     sbwd_dq_kernel<<<a.B * a.H * (a.N / TQ), 256, 0, st>>>(a);
     return hipGetLastError();
 }
