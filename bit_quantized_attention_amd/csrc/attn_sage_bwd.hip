@@ -180,18 +180,6 @@ __device__ __forceinline__ void kv_copy_b(const SageBwdArgs& a, const KvPlan& cp
     }
 }
 
-// Largest value over the 8 wavefronts: wavefront maxima through LDS (a
-// barrier that leaves the copies in flight).
-__device__ __forceinline__ float block_max8(float v, float* red, int w, int l) {
-    v = wave_max(v);
-    if (l == 0) red[w] = v;
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's LDS write is done
-    barrier_only();
-    const v4f r0 = *(const v4f*)red, r1 = *(const v4f*)(red + 4);
-    return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(r0[0], r0[1]), __builtin_fmaxf(r0[2], r0[3])),
-                           __builtin_fmaxf(__builtin_fmaxf(r1[0], r1[1]), __builtin_fmaxf(r1[2], r1[3])));
-}
-
 __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
     __shared__ __attribute__((aligned(16))) LdsKV L;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
@@ -272,9 +260,23 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
                 dmax = __builtin_fmaxf(dmax, __builtin_fabsf(dS[i]));
             }
         }
-        // ---- one INT8 scale per tile for P and for dS; codes to LDS, key-major
-        pmax = block_max8(pmax, L.red, w, l);
-        dmax = block_max8(dmax, L.red + 8, w, l);
+        // ---- one INT8 scale per tile for P and for dS (one exchange for both); codes to LDS, key-major
+        pmax = wave_max(pmax);
+        dmax = wave_max(dmax);
+        if (l == 0) {
+            L.red[w] = pmax;
+            L.red[8 + w] = dmax;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's LDS writes are done
+        barrier_only();
+        {
+            const v4f p0 = *(const v4f*)L.red, p1 = *(const v4f*)(L.red + 4);
+            const v4f d0 = *(const v4f*)(L.red + 8), d1 = *(const v4f*)(L.red + 12);
+            pmax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(p0[0], p0[1]), __builtin_fmaxf(p0[2], p0[3])),
+                                   __builtin_fmaxf(__builtin_fmaxf(p1[0], p1[1]), __builtin_fmaxf(p1[2], p1[3])));
+            dmax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(d0[0], d0[1]), __builtin_fmaxf(d0[2], d0[3])),
+                                   __builtin_fmaxf(__builtin_fmaxf(d1[0], d1[1]), __builtin_fmaxf(d1[2], d1[3])));
+        }
         const float inv_p = pmax > 0.0f ? 127.0f / pmax : 0.0f;
         const float inv_d = dmax > 0.0f ? 127.0f / dmax : 0.0f;
         const bool p_ok = inv_p != 0.0f && inv_p < __builtin_inff();
@@ -305,16 +307,12 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
             dv[i] = __builtin_fmaf((float)tv[i], sv, dv[i]);
             dk[i] = __builtin_fmaf((float)tk[i], sk, dk[i]);
         }
-        // ---- B and the codes are free: copy B(I+1); then A(I+1) must have landed
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's LDS reads are done
+        // ---- end of step: A(I+1) landed (the only copy in flight) and every
+        // wavefront is done with B, the codes and the maxima; then copy B(I+1),
+        // which lands during the next step's scores
+        BQA_WAIT_VM(0);
         barrier_only();
-        if (more) {
-            kv_copy_b(a, cp, bh, I + 1, L, w);
-            BQA_WAIT_VM(KvPlan::NB);
-        } else {
-            BQA_WAIT_VM(0);
-        }
-        barrier_only();
+        if (more) kv_copy_b(a, cp, bh, I + 1, L, w);
     }
     uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sB + hq * a.dv.sH;
     uint16_t* dkp = (uint16_t*)a.dk.p + b * a.dk.sB + hq * a.dk.sH;
@@ -333,7 +331,8 @@ struct LdsQ {
     uint8_t kT[D * TK];         // K codes channel-major, 128 ch x 64 B
 };
 
-// Largest value over the 4 wavefronts (same scheme as block_max8).
+// Largest value over the 4 wavefronts: wavefront maxima through LDS (a
+// barrier that leaves the copies in flight).
 __device__ __forceinline__ float block_max_nc(float v, float* red, int w, int l) {
     v = wave_max(v);
     if (l == 0) red[w] = v;
