@@ -116,8 +116,9 @@ __global__ __launch_bounds__(256) void transpose_i8_kernel(const int8_t* __restr
 //
 // Query-side tiles: "A" (Q codes, dO bf16, log-sum-exp, delta) in two slots,
 // "B" (channel-major dO and Q codes, read by the products only) in one.  The
-// copy of A(I+1) is issued at the start of step I, the copy of B(I+1) after
-// the products of step I: every copy has at least half a step to land.
+// query tiles go in descending order; the copy of the next tile's A is
+// issued at the start of a step, the copy of its B after the step's
+// products: every copy has at least half a step to land.
 struct LdsKV {
     uint8_t q[2][TQ * D];       // Q codes of the query tile, 128 x 128 B (sigma reads)
     uint8_t dob[2][TQ * D * 2]; // dO bf16, 128 x 256 B (sigma reads)
@@ -184,8 +185,11 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
     __shared__ __attribute__((aligned(16))) LdsKV L;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
     const int nkt = a.N / TK, nqt = a.N / TQ;
-    const int J = blockIdx.x % nkt;                  // ascending J: the longest query ranges first
-    const int bh = blockIdx.x / nkt, b = bh / a.H, hq = bh % a.H;
+    // consecutive workgroups take different heads (a head stays on one XCD);
+    // ascending J: the longest query ranges first
+    const int BH = a.B * a.H;
+    const int J = blockIdx.x / BH;
+    const int bh = blockIdx.x % BH, b = bh / a.H, hq = bh % a.H;
     const int kh = w & 1, qg = w >> 1;               // scores: 32 keys x 32 queries; products: 32 keys x 32 channels
     const int key = J * TK + 32 * kh + lq;
     const int qrow_s = sigma(lq);
@@ -210,14 +214,16 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
     const int crow = 32 * qg + lq;                   // channel row of doT / qT this lane reads
 
     const int I0 = a.causal ? (J * TK) / TQ : 0;
-    kv_copy_a(a, cp, bh, b, hq, I0, L, 0, w, l);
-    kv_copy_b(a, cp, bh, I0, L, w);
+    // query tiles in descending order: the key blocks of a head that run at
+    // the same time read the same query tile, which then comes from L2
+    kv_copy_a(a, cp, bh, b, hq, nqt - 1, L, 0, w, l);
+    kv_copy_b(a, cp, bh, nqt - 1, L, w);
     BQA_WAIT_VM(0);
     barrier_only();
-    for (int I = I0; I < nqt; ++I) {
-        const int s = (I - I0) & 1;
-        const bool more = I + 1 < nqt;
-        if (more) kv_copy_a(a, cp, bh, b, hq, I + 1, L, s ^ 1, w, l);   // that slot's reads ended a step ago
+    for (int I = nqt - 1; I >= I0; --I) {
+        const int s = (nqt - 1 - I) & 1;
+        const bool more = I > I0;
+        if (more) kv_copy_a(a, cp, bh, b, hq, I - 1, L, s ^ 1, w, l);   // that slot's reads ended a step ago
         const float qsc = qs_u[I];
         const float sc = qsc * ks * c;
         // ---- scores: S (int32), dP (fp32) of 32 queries x 32 keys; reg i of half h = query 16h + i
@@ -286,7 +292,7 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
         *(v4i*)(L.dc + prow * 128 + 16 * wch) = d_ok ? pack16(dS, inv_d) : v4i{};
         const float sv = p_ok ? pmax * (1.0f / 127.0f) * dos_u[I] : 0.0f;
         const float sk = d_ok ? dmax * (1.0f / 127.0f) * qsc * a.tau : 0.0f;
-        // ---- codes written, B(I) landed (the copies of A(I+1) may stay in flight)
+        // ---- codes written, B(I) landed (the copies of A(I-1) may stay in flight)
         if (more) BQA_WAIT_VM(KvPlan::NA);
         else BQA_WAIT_VM(0);
         barrier_only();
@@ -307,12 +313,12 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
             dv[i] = __builtin_fmaf((float)tv[i], sv, dv[i]);
             dk[i] = __builtin_fmaf((float)tk[i], sk, dk[i]);
         }
-        // ---- end of step: A(I+1) landed (the only copy in flight) and every
-        // wavefront is done with B, the codes and the maxima; then copy B(I+1),
+        // ---- end of step: A(I-1) landed (the only copy in flight) and every
+        // wavefront is done with B, the codes and the maxima; then copy B(I-1),
         // which lands during the next step's scores
         BQA_WAIT_VM(0);
         barrier_only();
-        if (more) kv_copy_b(a, cp, bh, I + 1, L, w);
+        if (more) kv_copy_b(a, cp, bh, I - 1, L, w);
     }
     uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sB + hq * a.dv.sH;
     uint16_t* dkp = (uint16_t*)a.dk.p + b * a.dk.sB + hq * a.dk.sH;
@@ -381,8 +387,11 @@ __global__ __launch_bounds__(256, 2) void sbwd_dq_kernel(SageBwdArgs a) {
     __shared__ float red[8];
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
     const int nkt = a.N / TK, nqt = a.N / TQ;
-    const int I = nqt - 1 - (int)(blockIdx.x % nqt);   // heaviest tiles first
-    const int bh = blockIdx.x / nqt, b = bh / a.H, hq = bh % a.H;
+    // heaviest tiles first; consecutive workgroups take different heads (a
+    // head stays on one XCD, where its query tiles sweep the key tiles together)
+    const int BH = a.B * a.H;
+    const int I = nqt - 1 - (int)(blockIdx.x / BH);
+    const int bh = blockIdx.x % BH, b = bh / a.H, hq = bh % a.H;
     const int qrow = I * TQ + 32 * w + lq;
     const int krow = sigma(lq);
     const float c = a.c_log2;
