@@ -42,15 +42,6 @@ __device__ __forceinline__ int fs256(int r) { return (r & 7) | (((r >> 4) & 1) <
 __device__ __forceinline__ int fc128(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int fc256(int r) { return r & 15; }
 
-__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
-}
-
 // ------------------------------------------------------------------ preprocess
 __global__ __launch_bounds__(256) void qat_delta_kernel(Dense dO, Dense Oa, int H, int N, int64_t rows,
                                                         float* __restrict__ delta) {
@@ -129,13 +120,16 @@ __device__ __forceinline__ void key_tile_issue(const QatBwdArgs& a, int bh, int 
     const int k0 = J * TK;
     {   // K codes: 4 x 1 KB (16 rows of 64 B)
         const int r = 16 * w + (l >> 2);
-        dma16(a.kc + ((int64_t)bh * a.N + k0 + r) * (D / 2) + 16 * ((l & 3) ^ fs64(r)), T.kc + 1024 * w);
+        lds_copy16((uint32_t)(r * (D / 2) + 16 * ((l & 3) ^ fs64(r))), a.kc + ((int64_t)bh * a.N + k0) * (D / 2),
+                   lds_addr(T.kc + 1024 * w));
     }
-    if (w == 0) dma4(a.ks + ((int64_t)bh * a.N + k0 + l) * (D / 32), T.ks);
+    // K scales: 256 B, one copy (repeated by every wavefront so that all count the same copies)
+    lds_copy4((uint32_t)(4 * l), a.ks + ((int64_t)bh * a.N + k0) * (D / 32), lds_addr(T.ks));
 #pragma unroll
     for (int u = 0; u < 4; ++u) {   // deq(V) rows: 16 x 1 KB (4 rows of 256 B)
         const int sgm = 4 * w + u, r = 4 * sgm + (l >> 4);
-        dma16(a.vdeq + ((int64_t)bh * a.N + k0 + r) * D + 8 * ((l & 15) ^ fs256(r)), T.vr + 1024 * sgm);
+        lds_copy16((uint32_t)(2 * (r * D + 8 * ((l & 15) ^ fs256(r)))), a.vdeq + ((int64_t)bh * a.N + k0) * D,
+                   lds_addr(T.vr + 1024 * sgm));
     }
 }
 
@@ -205,14 +199,98 @@ __device__ __forceinline__ void tile_pds(const KeyTile& T, const RowIn& r, float
 }
 
 // ------------------------------------------------------------------ dK, dV
+// The query tile's per-row inputs (one slot): what the dQ kernel loads into
+// each lane's registers once, this kernel reads from LDS for every tile.
+struct RowTile {
+    uint8_t qc[TQ * D / 2];     // Q codes, 128 rows x 64 B (chunk XOR (row >> 1) & 3)
+    uint8_t qs[TQ * D / 32];    // Q scales, 128 rows x 4 B
+    uint8_t dob[TQ * D * 2];    // dO bf16, 128 rows x 256 B (chunk XOR row & 15)
+    float lse[TQ];
+    float dlt[TQ];
+};
 struct LdsKVq {
     KeyTile kt;                  // fixed: the workgroup's key block
+    RowTile rt;                  // per-row inputs of the query tile
     uint8_t pt[TK * TQ * 2];     // P^ transposed: 64 keys x 128 queries fp16 (chunks XOR key % 16)
     uint8_t st[TK * TQ * 2];     // dS transposed
     uint8_t gT[D * TQ * 2];      // dO^T: 128 channels x 128 queries fp16
     uint8_t qT[D * TQ * 2];      // deq(Q)^T
 };
 
+// One wavefront's share of the copies of a query tile, as per-lane offsets
+// from tile bases.  "Rows" (RowTile) and "columns" (dO^T, deq(Q)^T).
+struct KvqPlan {
+    static constexpr int NR = 2 + 8 + 2, NC = 8 + 8;   // copies per wavefront
+    static_assert(NR + NC < 64, "vmcnt range");
+    uint32_t qc[2], g[8], t[8];
+    __device__ __forceinline__ KvqPlan(int w, int l, int N, int64_t g_sN) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {      // Q codes: 8 x 1 KB (16 rows of 64 B)
+            const int r = 16 * (2 * w + u) + (l >> 2);
+            qc[u] = (uint32_t)(r * (D / 2) + 16 * ((l & 3) ^ ((r >> 1) & 3)));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {      // dO bf16: 32 x 1 KB (4 rows of 256 B)
+            const int r = 4 * (8 * w + u) + (l >> 4);
+            g[u] = (uint32_t)(2 * (r * g_sN + 8 * ((l & 15) ^ (r & 15))));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {      // channel-major bf16: 32 x 1 KB each (4 rows of 256 B)
+            const int r = 4 * (8 * w + u) + (l >> 4);
+            t[u] = (uint32_t)(2 * (r * N + 8 * ((l & 15) ^ fc256(r))));
+        }
+    }
+};
+__device__ __forceinline__ void rows_issue(const QatBwdArgs& a, const KvqPlan& cp, int bh, int b, int hq, int I,
+                                           RowTile& R, int w, int l) {
+    const int q0 = I * TQ;
+    const uint8_t* qcb = a.qc + ((int64_t)bh * a.N + q0) * (D / 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) lds_copy16(cp.qc[u], qcb, lds_addr(R.qc + 1024 * (2 * w + u)));
+    const uint16_t* gb = (const uint16_t*)a.d_o.p + b * a.d_o.sB + hq * a.d_o.sH + (int64_t)q0 * a.d_o.sN;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) lds_copy16(cp.g[u], gb, lds_addr(R.dob + 1024 * (8 * w + u)));
+    // scales, log-sum-exp, delta: 512 B each, two 256-byte copies per wavefront
+    // (wavefront 3 repeats wavefront 0's so that all count the same copies)
+    const uint32_t o = (uint32_t)(4 * l);
+    if (w == 1) {
+        lds_copy4(o, a.lse + (int64_t)bh * a.N + q0, lds_addr(R.lse));
+        lds_copy4(o, a.lse + (int64_t)bh * a.N + q0 + 64, lds_addr(R.lse + 64));
+    } else if (w == 2) {
+        lds_copy4(o, a.delta + (int64_t)bh * a.N + q0, lds_addr(R.dlt));
+        lds_copy4(o, a.delta + (int64_t)bh * a.N + q0 + 64, lds_addr(R.dlt + 64));
+    } else {
+        const uint8_t* qsb = a.qs + ((int64_t)bh * a.N + q0) * (D / 32);
+        lds_copy4(o, qsb, lds_addr(R.qs));
+        lds_copy4(o, qsb + 256, lds_addr(R.qs + 256));
+    }
+}
+__device__ __forceinline__ void cols_issue(const QatBwdArgs& a, const KvqPlan& cp, int bh, int I, LdsKVq& L, int w) {
+    const uint16_t* gT = a.doT + (int64_t)bh * D * a.N + I * TQ;
+    const uint16_t* qT = a.qT + (int64_t)bh * D * a.N + I * TQ;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        lds_copy16(cp.t[u], gT, lds_addr(L.gT + 1024 * (8 * w + u)));
+        lds_copy16(cp.t[u], qT, lds_addr(L.qT + 1024 * (8 * w + u)));
+    }
+}
+__device__ __forceinline__ void row_from_lds(const RowTile& R, int row, int h, RowIn& r) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        r.qb[kk] = *(const v4i*)(R.qc + row * 64 + 16 * ((2 * kk + h) ^ ((row >> 1) & 3)));
+        r.qsb[kk] = R.qs[row * 4 + 2 * kk + h];
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st) r.gb[st] = *(const v8bf*)(R.dob + row * 256 + 16 * ((2 * st + h) ^ (row & 15)));
+    r.lse2 = R.lse[row] * 1.4426950408889634f;
+    r.dlt = R.dlt[row];
+}
+
+// One workgroup per 64-key block over the 128-query tiles.  Step I: P, its
+// fake quantisation and dS from the rows of tile I, the transposed P^ and dS
+// to LDS, then dV and dK from them and the channel-major dO^T, deq(Q)^T of
+// tile I.  The rows of tile I+1 are copied during the products, the columns
+// of tile I+1 during the next step's P and dS.
 __global__ __launch_bounds__(256, 1) void qbwd_dkdv_kernel(QatBwdArgs a) {
     __shared__ __attribute__((aligned(16))) LdsKVq L;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
@@ -223,30 +301,24 @@ __global__ __launch_bounds__(256, 1) void qbwd_dkdv_kernel(QatBwdArgs a) {
     const float c = a.c_log2;
     // output tiles of this wavefront: keys 32 (w & 1) .., channels 64 (w >> 1) + 32 t ..
     const int ko = 32 * (w & 1), co = 64 * (w >> 1);
+    const KvqPlan cp(w, l, a.N, a.d_o.sN);
 
-    key_tile_issue(a, bh, J, L.kt, w, l);
     v16f dv[2], dk[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) { dv[t] = v16f{}; dk[t] = v16f{}; }
 
+    key_tile_issue(a, bh, J, L.kt, w, l);
+    rows_issue(a, cp, bh, b, hq, 0, L.rt, w, l);
+    cols_issue(a, cp, bh, 0, L, w);
+    BQA_WAIT_VM(0);
+    barrier_only();
     for (int I = 0; I < nqt; ++I) {
-        // channel-major dO and deq(Q) of the query tile: 32 + 32 KB, 8 + 8 copies per wavefront
-        const int q0 = I * TQ;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int sgm = 8 * w + u, r = 4 * sgm + (l >> 4);
-            const int cc = (l & 15) ^ fc256(r);
-            dma16(a.doT + ((int64_t)bh * D + r) * a.N + q0 + 8 * cc, L.gT + 1024 * sgm);
-            dma16(a.qT + ((int64_t)bh * D + r) * a.N + q0 + 8 * cc, L.qT + 1024 * sgm);
-        }
+        const bool more = I + 1 < nqt;
         RowIn rin;
-        const int qrow = q0 + 32 * w + lq;
-        row_load(a, bh, b, hq, qrow, h, rin);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();                       // key tile (first pass) and this tile's copies have landed
+        row_from_lds(L.rt, 32 * w + lq, h, rin);
         float p[2][16], pq[2][16], ds[2][16];
         tile_pds(L.kt, rin, c, krow, h, p, pq, ds);
-        // P^ and dS to LDS as [key][query] bf16
+        // P^ and dS to LDS as [key][query] fp16 / bf16
         const int qc = 32 * w + lq;
 #pragma unroll
         for (int g = 0; g < 2; ++g)
@@ -257,7 +329,10 @@ __global__ __launch_bounds__(256, 1) void qbwd_dkdv_kernel(QatBwdArgs a) {
                 *(uint16_t*)(L.pt + off) = f32_to_f16_bits(pq[g][i]);
                 *(uint16_t*)(L.st + off) = f32_to_bf16_bits(ds[g][i]);
             }
-        __syncthreads();
+        // the columns of tile I landed, P^ and dS are written, the rows are read
+        BQA_WAIT_VM(0);
+        barrier_only();
+        if (more) rows_issue(a, cp, bh, b, hq, I + 1, L.rt, w, l);
         // dV += P^T dO, dK += dS^T deq(Q): K-steps of 16 queries
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -275,7 +350,17 @@ __global__ __launch_bounds__(256, 1) void qbwd_dkdv_kernel(QatBwdArgs a) {
                 dk[t] = mfma_bf16_32x32x16(as, bq, dk[t]);
             }
         }
-        __syncthreads();                       // LDS tiles free for the next query tile
+        // every wavefront is done with P^, dS and the columns: copy the next
+        // columns; the next rows must have landed
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        barrier_only();
+        if (more) {
+            cols_issue(a, cp, bh, I + 1, L, w);
+            BQA_WAIT_VM(KvqPlan::NC);
+        } else {
+            BQA_WAIT_VM(0);
+        }
+        barrier_only();
     }
     // dv[t] reg i: key ko + 8 (i / 4) + 4 h + i % 4, channel co + 32 t + lq
     uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sB + hq * a.dv.sH;
@@ -302,7 +387,8 @@ __device__ __forceinline__ void dq_issue(const QatBwdArgs& a, int bh, int J, Lds
 #pragma unroll
     for (int u = 0; u < 4; ++u) {   // deq(K)^T: 16 x 1 KB (8 rows of 128 B)
         const int sgm = 4 * w + u, r = 8 * sgm + (l >> 3);
-        dma16(a.kT + ((int64_t)bh * D + r) * a.N + J * TK + 8 * ((l & 7) ^ fc128(r)), T.kT + 1024 * sgm);
+        lds_copy16((uint32_t)(2 * (r * a.N + 8 * ((l & 7) ^ fc128(r)))), a.kT + (int64_t)bh * D * a.N + J * TK,
+                   lds_addr(T.kT + 1024 * sgm));
     }
 }
 
@@ -321,8 +407,8 @@ __global__ __launch_bounds__(256, 2) void qbwd_dq_kernel(QatBwdArgs a) {
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) dq[cb] = v16f{};
     dq_issue(a, bh, 0, L[0], w, l);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    BQA_WAIT_VM(0);
+    barrier_only();
     for (int J = 0; J < nkt; ++J) {
         const int cur = J & 1;
         if (J + 1 < nkt) dq_issue(a, bh, J + 1, L[cur ^ 1], w, l);
@@ -343,8 +429,9 @@ __global__ __launch_bounds__(256, 2) void qbwd_dq_kernel(QatBwdArgs a) {
                 dq[cb] = mfma_bf16_32x32x16(ab, bk, dq[cb]);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        // the next key tile landed, and every wavefront is done with this one
+        BQA_WAIT_VM(0);
+        barrier_only();
     }
     // dq[cb] reg i: query 32 w + 8 (i / 4) + 4 h + i % 4, channel 32 cb + lq
     uint16_t* dqp = (uint16_t*)a.dq.p + b * a.dq.sB + hq * a.dq.sH;

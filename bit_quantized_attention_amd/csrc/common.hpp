@@ -59,8 +59,8 @@ __device__ __forceinline__ void lds_copy4(uint32_t voff, const void* sbase, uint
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                  : "memory");
 }
-// s_waitcnt with vmcnt(n) (n < 16) and lgkmcnt(0), expcnt not waited for
-#define BQA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0070 | (n))
+// s_waitcnt with vmcnt(n) (n < 64) and lgkmcnt(0), expcnt not waited for
+#define BQA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 15) | (((n) >> 4) << 14))
 // A workgroup barrier that does not wait for the copies above (the barrier of
 // __syncthreads carries a fence that waits for every memory operation)
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
