@@ -153,49 +153,53 @@ __device__ __forceinline__ void row_load(const QatBwdArgs& a, int bh, int b, int
     r.dlt = a.delta[(int64_t)bh * a.N + qrow];
 }
 
-// P (unrounded), its MXFP4 fake quantisation (as float) and dS (bf16-rounded) for the tile
+// P (unrounded), its MXFP4 fake quantisation (as float) and dS (bf16-rounded)
+// for keys 32 g .. 32 g + 31 of the tile (one MX block of P per query row)
+__device__ __forceinline__ void tile_pds_g(const KeyTile& T, const RowIn& r, float c, int krow, int h, int g,
+                                           float (&p)[16], float (&pq)[16], float (&ds)[16]) {
+    const int rk = 32 * g + krow;
+    v16f s = v16f{};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const v4i av = *(const v4i*)(T.kc + rk * 64 + 16 * ((2 * kk + h) ^ fs64(rk)));
+        s = mfma_f4_32x32x64(av, (int)T.ks[4 * rk + 2 * kk + h], r.qb[kk], r.qsb[kk], s);
+    }
+    v16f dp = v16f{};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+        const v8bf av = *(const v8bf*)(T.vr + rk * 256 + 16 * ((2 * st + h) ^ fs256(rk)));
+        dp = mfma_bf16_32x32x16(av, r.gb[st], dp);
+    }
+    // P relative to m2 = ceil(L) (log2 units), a power of two: its MXFP4
+    // codes are the forward's; exp2(m2 - L) brings both to P = exp(s - L)
+    const float m2 = __builtin_ceilf(r.lse2);
+    const float back = __builtin_amdgcn_exp2f(m2 - r.lse2);
+    float pr[16];
+    float smax = s[0];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m2));
+        p[i] = pr[i] * back;
+        smax = __builtin_fmaxf(smax, s[i]);
+        ds[i] = (float)(__bf16)(p[i] * (dp[i] - r.dlt));
+    }
+    // MX block g of the row: 16 keys here, 16 in the partner lane
+    smax = __builtin_fmaxf(smax, partner32f(smax));
+    const int e = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(smax, c, -m2)));
+    const float sc = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+        const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pr[i], pr[i + 1], sc, 0);
+        const v2f dq = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, sc, 0);
+        pq[i] = dq[0] * back;
+        pq[i + 1] = dq[1] * back;
+    }
+}
+// both key halves of the tile
 __device__ __forceinline__ void tile_pds(const KeyTile& T, const RowIn& r, float c, int krow, int h, float (&p)[2][16],
                                          float (&pq)[2][16], float (&ds)[2][16]) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-        const int rk = 32 * g + krow;
-        v16f s = v16f{};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const v4i av = *(const v4i*)(T.kc + rk * 64 + 16 * ((2 * kk + h) ^ fs64(rk)));
-            s = mfma_f4_32x32x64(av, (int)T.ks[4 * rk + 2 * kk + h], r.qb[kk], r.qsb[kk], s);
-        }
-        v16f dp = v16f{};
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            const v8bf av = *(const v8bf*)(T.vr + rk * 256 + 16 * ((2 * st + h) ^ fs256(rk)));
-            dp = mfma_bf16_32x32x16(av, r.gb[st], dp);
-        }
-        // P relative to m2 = ceil(L) (log2 units), a power of two: its MXFP4
-        // codes are the forward's; exp2(m2 - L) brings both to P = exp(s - L)
-        const float m2 = __builtin_ceilf(r.lse2);
-        const float back = __builtin_amdgcn_exp2f(m2 - r.lse2);
-        float pr[16];
-        float smax = s[0];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m2));
-            p[g][i] = pr[i] * back;
-            smax = __builtin_fmaxf(smax, s[i]);
-            ds[g][i] = (float)(__bf16)(p[g][i] * (dp[i] - r.dlt));
-        }
-        // MX block g of the row: 16 keys here, 16 in the partner lane
-        smax = __builtin_fmaxf(smax, partner32f(smax));
-        const int e = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(smax, c, -m2)));
-        const float sc = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-            const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pr[i], pr[i + 1], sc, 0);
-            const v2f dq = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, sc, 0);
-            pq[g][i] = dq[0] * back;
-            pq[g][i + 1] = dq[1] * back;
-        }
-    }
+    for (int g = 0; g < 2; ++g) tile_pds_g(T, r, c, krow, h, g, p[g], pq[g], ds[g]);
 }
 
 // ------------------------------------------------------------------ dK, dV
@@ -217,26 +221,25 @@ struct LdsKVq {
     uint8_t qT[D * TQ * 2];      // deq(Q)^T
 };
 
-// One wavefront's share of the copies of a query tile, as per-lane offsets
-// from tile bases.  "Rows" (RowTile) and "columns" (dO^T, deq(Q)^T).
+// One wavefront's share (of 8) of the copies of a query tile, as per-lane
+// offsets from tile bases.  "Rows" (RowTile) and "columns" (dO^T, deq(Q)^T).
 struct KvqPlan {
-    static constexpr int NR = 2 + 8 + 2, NC = 8 + 8;   // copies per wavefront
+    static constexpr int NR = 1 + 4 + 1, NC = 4 + 4;   // copies per wavefront
     static_assert(NR + NC < 64, "vmcnt range");
-    uint32_t qc[2], g[8], t[8];
+    uint32_t qc, g[4], t[4];
     __device__ __forceinline__ KvqPlan(int w, int l, int N, int64_t g_sN) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {      // Q codes: 8 x 1 KB (16 rows of 64 B)
-            const int r = 16 * (2 * w + u) + (l >> 2);
-            qc[u] = (uint32_t)(r * (D / 2) + 16 * ((l & 3) ^ ((r >> 1) & 3)));
+        {                                  // Q codes: 8 x 1 KB (16 rows of 64 B)
+            const int r = 16 * w + (l >> 2);
+            qc = (uint32_t)(r * (D / 2) + 16 * ((l & 3) ^ ((r >> 1) & 3)));
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {      // dO bf16: 32 x 1 KB (4 rows of 256 B)
-            const int r = 4 * (8 * w + u) + (l >> 4);
+        for (int u = 0; u < 4; ++u) {      // dO bf16: 32 x 1 KB (4 rows of 256 B)
+            const int r = 4 * (4 * w + u) + (l >> 4);
             g[u] = (uint32_t)(2 * (r * g_sN + 8 * ((l & 15) ^ (r & 15))));
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {      // channel-major bf16: 32 x 1 KB each (4 rows of 256 B)
-            const int r = 4 * (8 * w + u) + (l >> 4);
+        for (int u = 0; u < 4; ++u) {      // channel-major bf16: 32 x 1 KB each (4 rows of 256 B)
+            const int r = 4 * (4 * w + u) + (l >> 4);
             t[u] = (uint32_t)(2 * (r * N + 8 * ((l & 15) ^ fc256(r))));
         }
     }
@@ -244,34 +247,25 @@ struct KvqPlan {
 __device__ __forceinline__ void rows_issue(const QatBwdArgs& a, const KvqPlan& cp, int bh, int b, int hq, int I,
                                            RowTile& R, int w, int l) {
     const int q0 = I * TQ;
-    const uint8_t* qcb = a.qc + ((int64_t)bh * a.N + q0) * (D / 2);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) lds_copy16(cp.qc[u], qcb, lds_addr(R.qc + 1024 * (2 * w + u)));
+    lds_copy16(cp.qc, a.qc + ((int64_t)bh * a.N + q0) * (D / 2), lds_addr(R.qc + 1024 * w));
     const uint16_t* gb = (const uint16_t*)a.d_o.p + b * a.d_o.sB + hq * a.d_o.sH + (int64_t)q0 * a.d_o.sN;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) lds_copy16(cp.g[u], gb, lds_addr(R.dob + 1024 * (8 * w + u)));
-    // scales, log-sum-exp, delta: 512 B each, two 256-byte copies per wavefront
-    // (wavefront 3 repeats wavefront 0's so that all count the same copies)
+    for (int u = 0; u < 4; ++u) lds_copy16(cp.g[u], gb, lds_addr(R.dob + 1024 * (4 * w + u)));
+    // scales, log-sum-exp, delta: six 256-byte copies (wavefronts 6, 7 repeat
+    // 0, 1 so that all count the same copies)
     const uint32_t o = (uint32_t)(4 * l);
-    if (w == 1) {
-        lds_copy4(o, a.lse + (int64_t)bh * a.N + q0, lds_addr(R.lse));
-        lds_copy4(o, a.lse + (int64_t)bh * a.N + q0 + 64, lds_addr(R.lse + 64));
-    } else if (w == 2) {
-        lds_copy4(o, a.delta + (int64_t)bh * a.N + q0, lds_addr(R.dlt));
-        lds_copy4(o, a.delta + (int64_t)bh * a.N + q0 + 64, lds_addr(R.dlt + 64));
-    } else {
-        const uint8_t* qsb = a.qs + ((int64_t)bh * a.N + q0) * (D / 32);
-        lds_copy4(o, qsb, lds_addr(R.qs));
-        lds_copy4(o, qsb + 256, lds_addr(R.qs + 256));
-    }
+    const int job = w % 6, half = job & 1;
+    if (job < 2) lds_copy4(o, a.qs + ((int64_t)bh * a.N + q0) * (D / 32) + 256 * half, lds_addr(R.qs + 256 * half));
+    else if (job < 4) lds_copy4(o, a.lse + (int64_t)bh * a.N + q0 + 64 * half, lds_addr(R.lse + 64 * half));
+    else lds_copy4(o, a.delta + (int64_t)bh * a.N + q0 + 64 * half, lds_addr(R.dlt + 64 * half));
 }
 __device__ __forceinline__ void cols_issue(const QatBwdArgs& a, const KvqPlan& cp, int bh, int I, LdsKVq& L, int w) {
     const uint16_t* gT = a.doT + (int64_t)bh * D * a.N + I * TQ;
     const uint16_t* qT = a.qT + (int64_t)bh * D * a.N + I * TQ;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        lds_copy16(cp.t[u], gT, lds_addr(L.gT + 1024 * (8 * w + u)));
-        lds_copy16(cp.t[u], qT, lds_addr(L.qT + 1024 * (8 * w + u)));
+    for (int u = 0; u < 4; ++u) {
+        lds_copy16(cp.t[u], gT, lds_addr(L.gT + 1024 * (4 * w + u)));
+        lds_copy16(cp.t[u], qT, lds_addr(L.qT + 1024 * (4 * w + u)));
     }
 }
 __device__ __forceinline__ void row_from_lds(const RowTile& R, int row, int h, RowIn& r) {
@@ -286,12 +280,14 @@ __device__ __forceinline__ void row_from_lds(const RowTile& R, int row, int h, R
     r.dlt = R.dlt[row];
 }
 
-// One workgroup per 64-key block over the 128-query tiles.  Step I: P, its
-// fake quantisation and dS from the rows of tile I, the transposed P^ and dS
-// to LDS, then dV and dK from them and the channel-major dO^T, deq(Q)^T of
-// tile I.  The rows of tile I+1 are copied during the products, the columns
-// of tile I+1 during the next step's P and dS.
-__global__ __launch_bounds__(256, 1) void qbwd_dkdv_kernel(QatBwdArgs a) {
+// One workgroup of 8 wavefronts per 64-key block over the 128-query tiles.
+// Step I: wavefront (qg, kh) computes P, its fake quantisation and dS for
+// queries 32 qg .. (in lanes) and keys 32 kh .. from the rows of tile I and
+// writes P^ and dS transposed to LDS; then wavefront (ko, co) accumulates dV
+// and dK for 32 keys x 32 channels from them and the channel-major dO^T,
+// deq(Q)^T of tile I.  The rows of tile I+1 are copied during the products,
+// the columns of tile I+1 during the next step's P and dS.
+__global__ __launch_bounds__(512, 1) void qbwd_dkdv_kernel(QatBwdArgs a) {
     __shared__ __attribute__((aligned(16))) LdsKVq L;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
     const int nkt = a.N / TK, nqt = a.N / TQ;
@@ -299,55 +295,49 @@ __global__ __launch_bounds__(256, 1) void qbwd_dkdv_kernel(QatBwdArgs a) {
     const int bh = blockIdx.x / nkt, b = bh / a.H, hq = bh % a.H;
     const int krow = sigma(lq);
     const float c = a.c_log2;
-    // output tiles of this wavefront: keys 32 (w & 1) .., channels 64 (w >> 1) + 32 t ..
-    const int ko = 32 * (w & 1), co = 64 * (w >> 1);
+    const int qg = w & 3, kh = w >> 2;               // P, dS: queries 32 qg + lane, keys 32 kh ..
+    const int ko = 32 * (w & 1), co = 32 * (w >> 1); // dV, dK: keys ko .., channels co ..
     const KvqPlan cp(w, l, a.N, a.d_o.sN);
 
-    v16f dv[2], dk[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) { dv[t] = v16f{}; dk[t] = v16f{}; }
+    v16f dv = v16f{}, dk = v16f{};
 
-    key_tile_issue(a, bh, J, L.kt, w, l);
+    if (w < 4) key_tile_issue(a, bh, J, L.kt, w, l);
     rows_issue(a, cp, bh, b, hq, 0, L.rt, w, l);
     cols_issue(a, cp, bh, 0, L, w);
     BQA_WAIT_VM(0);
     barrier_only();
     for (int I = 0; I < nqt; ++I) {
         const bool more = I + 1 < nqt;
+        const int qc = 32 * qg + lq;
         RowIn rin;
-        row_from_lds(L.rt, 32 * w + lq, h, rin);
-        float p[2][16], pq[2][16], ds[2][16];
-        tile_pds(L.kt, rin, c, krow, h, p, pq, ds);
+        row_from_lds(L.rt, qc, h, rin);
+        float p[16], pq[16], ds[16];
+        tile_pds_g(L.kt, rin, c, krow, h, kh, p, pq, ds);
         // P^ and dS to LDS as [key][query] fp16 / bf16
-        const int qc = 32 * w + lq;
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = 32 * g + 16 * h + i;
-                const int off = key * 256 + 16 * ((qc >> 3) ^ (key & 15)) + 2 * (qc & 7);
-                *(uint16_t*)(L.pt + off) = f32_to_f16_bits(pq[g][i]);
-                *(uint16_t*)(L.st + off) = f32_to_bf16_bits(ds[g][i]);
-            }
+        for (int i = 0; i < 16; ++i) {
+            const int key = 32 * kh + 16 * h + i;
+            const int off = key * 256 + 16 * ((qc >> 3) ^ (key & 15)) + 2 * (qc & 7);
+            *(uint16_t*)(L.pt + off) = f32_to_f16_bits(pq[i]);
+            *(uint16_t*)(L.st + off) = f32_to_bf16_bits(ds[i]);
+        }
         // the columns of tile I landed, P^ and dS are written, the rows are read
         BQA_WAIT_VM(0);
         barrier_only();
         if (more) rows_issue(a, cp, bh, b, hq, I + 1, L.rt, w, l);
         // dV += P^T dO, dK += dS^T deq(Q): K-steps of 16 queries
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int ch = co + 32 * t + lq;
+        {
+            const int ch = co + lq, key = ko + lq;
 #pragma unroll
             for (int st = 0; st < 8; ++st) {
-                const int key = ko + lq;
                 const int pc = 16 * ((2 * st + h) ^ (key & 15));
                 const v8h ap = *(const v8h*)(L.pt + key * 256 + pc);
                 const v8bf as = *(const v8bf*)(L.st + key * 256 + pc);
                 const int cq = 2 * st + h;                // 16-byte chunk of 8 queries
                 const v8h bg = *(const v8h*)(L.gT + ch * 256 + 16 * (cq ^ fc256(ch)));
                 const v8bf bq = *(const v8bf*)(L.qT + ch * 256 + 16 * (cq ^ fc256(ch)));
-                dv[t] = mfma_f16_32x32x16(ap, bg, dv[t]);
-                dk[t] = mfma_bf16_32x32x16(as, bq, dk[t]);
+                dv = mfma_f16_32x32x16(ap, bg, dv);
+                dk = mfma_bf16_32x32x16(as, bq, dk);
             }
         }
         // every wavefront is done with P^, dS and the columns: copy the next
@@ -362,18 +352,15 @@ __global__ __launch_bounds__(256, 1) void qbwd_dkdv_kernel(QatBwdArgs a) {
         }
         barrier_only();
     }
-    // dv[t] reg i: key ko + 8 (i / 4) + 4 h + i % 4, channel co + 32 t + lq
+    // dv reg i: key ko + 8 (i / 4) + 4 h + i % 4, channel co + lq
     uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sB + hq * a.dv.sH;
     uint16_t* dkp = (uint16_t*)a.dk.p + b * a.dk.sB + hq * a.dk.sH;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int64_t kpos = (int64_t)J * TK + ko + 8 * (i >> 2) + 4 * h + (i & 3);
-            const int ch = co + 32 * t + lq;
-            dvp[kpos * a.dv.sN + ch] = f32_to_bf16_bits(dv[t][i]);
-            dkp[kpos * a.dk.sN + ch] = f32_to_bf16_bits(dk[t][i] * a.tau);
-        }
+    for (int i = 0; i < 16; ++i) {
+        const int64_t kpos = (int64_t)J * TK + ko + 8 * (i >> 2) + 4 * h + (i & 3);
+        dvp[kpos * a.dv.sN + co + lq] = f32_to_bf16_bits(dv[i]);
+        dkp[kpos * a.dk.sN + co + lq] = f32_to_bf16_bits(dk[i] * a.tau);
+    }
 }
 
 // ------------------------------------------------------------------ dQ
@@ -468,7 +455,7 @@ hipError_t launch_qat_bwd(QatBwdArgs a, Dense o_aux, void* ws, hipStream_t st) {
     deq_t_kernel<0><<<tg, 256, 0, st>>>(a.qc, a.qs, Dense{}, a.H, a.N, D, qT);
     deq_t_kernel<0><<<tg, 256, 0, st>>>(a.kc, a.ks, Dense{}, a.H, a.N, D, kT);
     deq_t_kernel<1><<<tg, 256, 0, st>>>(nullptr, nullptr, a.d_o, a.H, a.N, D, doT);
-    qbwd_dkdv_kernel<<<a.B * a.H * (a.N / TK), 256, 0, st>>>(a);
+    qbwd_dkdv_kernel<<<a.B * a.H * (a.N / TK), 512, 0, st>>>(a);
     qbwd_dq_kernel<<<a.B * a.H * (a.N / TQ), 256, 0, st>>>(a);
     return hipGetLastError();
 }
