@@ -54,26 +54,21 @@ union LdsBuf {
     LdsBf b;
 };
 
-__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
-}
-
 // FP4 key block J: codes and scales of K and V^T, all by direct copies.
 __device__ __forceinline__ void issue_f4(const ThriftFwdArgs& a, int bhk, int J, LdsF4& L, int w, int l) {
     const int t0 = J * KB;
+    const uint8_t* kbase = a.kc + ((int64_t)bhk * a.Nk + t0) * (D / 2);
+    const uint8_t* vbase = a.vc + (int64_t)bhk * D * (a.Nk / 2) + t0 / 2;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int sgm = 2 * w + u, r = 16 * sgm + (l >> 2);
-        dma16(a.kc + ((int64_t)bhk * a.Nk + t0 + r) * (D / 2) + 16 * ((l & 3) ^ fk64(r)), L.kc + 1024 * sgm);
-        dma16(a.vc + ((int64_t)bhk * D + r) * (a.Nk / 2) + t0 / 2 + 16 * ((l & 3) ^ fv64(r)), L.vc + 1024 * sgm);
+        lds_copy16((uint32_t)(r * (D / 2) + 16 * ((l & 3) ^ fk64(r))), kbase, lds_addr(L.kc + 1024 * sgm));
+        lds_copy16((uint32_t)r * (uint32_t)(a.Nk / 2) + (uint32_t)(16 * ((l & 3) ^ fv64(r))), vbase,
+                   lds_addr(L.vc + 1024 * sgm));
     }
-    if (w < 2) dma4(a.ks + ((int64_t)bhk * a.Nk + t0 + 64 * w + l) * (D / 32), L.ks + 256 * w);
-    else dma4(a.vs + ((int64_t)bhk * D + 64 * (w - 2) + l) * (a.Nk / 32) + t0 / 32, L.vs + 256 * (w - 2));
+    if (w < 2) lds_copy4((uint32_t)(4 * l), a.ks + ((int64_t)bhk * a.Nk + t0 + 64 * w) * (D / 32), lds_addr(L.ks + 256 * w));
+    else lds_copy4((uint32_t)l * (uint32_t)(a.Nk / 32), a.vs + ((int64_t)bhk * D + 64 * (w - 2)) * (a.Nk / 32) + t0 / 32,
+                   lds_addr(L.vs + 256 * (w - 2)));
 }
 
 // bf16 half block (keys k0 .. k0 + 63): K rows by direct copies; V comes back
@@ -83,11 +78,11 @@ struct VStage {
 };
 __device__ __forceinline__ void issue_bf(const ThriftFwdArgs& a, int b, int hk, int k0, LdsBf& L, int w, int l,
                                          int tid, VStage& vs) {
-    const uint16_t* kb = (const uint16_t*)a.k_hi.p + b * a.k_hi.sB + hk * a.k_hi.sH;
+    const uint16_t* kb = (const uint16_t*)a.k_hi.p + b * a.k_hi.sB + hk * a.k_hi.sH + (int64_t)k0 * a.k_hi.sN;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int sgm = 4 * w + u, r = 4 * sgm + (l >> 4);
-        dma16(kb + (int64_t)(k0 + r) * a.k_hi.sN + 8 * ((l & 15) ^ fk256(r)), L.k + 1024 * sgm);
+        lds_copy16((uint32_t)(2 * (r * a.k_hi.sN + 8 * ((l & 15) ^ fk256(r)))), kb, lds_addr(L.k + 1024 * sgm));
     }
     const uint16_t* vb = (const uint16_t*)a.v_hi.p + b * a.v_hi.sB + hk * a.v_hi.sH;
     const int cg = tid & 15, kq = tid >> 4;
@@ -170,8 +165,8 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
     int J = next_unsel(0);
     if (J < nJ) {
         issue_f4(a, bhk, J, lds[0].f, w, l);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        BQA_WAIT_VM(0);
+        barrier_only();
     }
     int buf = 0;
     while (J < nJ) {
@@ -211,21 +206,30 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
             if (mx > m_ref) move_frame(oacc, l_run, m_ref, __builtin_ceilf(mx));
         }
         const float mu = m_ref == -__builtin_inff() ? 0.0f : m_ref;
-        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                s[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c, -mu));
-                ps[t] += s[t][i];
-            }
-        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-        // two-level P: r = the row's largest P in the block -> 6
+        // two-level P: r = the row's largest P in the block, P' = P 6 / r =
+        // 6 exp2((s - smax) c), formed directly by the exponential; the row
+        // sum of P is r/6 times that of P'.  A block whose P all underflow
+        // (r = 0) adds nothing.
         const float r = __builtin_amdgcn_exp2f(__builtin_fmaf(smax, c, -mu));
+        const float bias2 = r > 0.0f ? 2.584962500721156f - smax * c : -__builtin_inff();   // log2(6) - smax c
+        float ps[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float q0 = 0.0f, q1 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                s[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c, bias2));
+                s[t][i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i + 1], c, bias2));
+                q0 += s[t][i];
+                q1 += s[t][i + 1];
+            }
+            ps[t] = q0 + q1;
+        }
+        if (r > 0.0f) l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) * (r * (1.0f / 6.0f));
         const float six_r = r > 0.0f ? 6.0f / r : 0.0f;
         int e[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) e[t] = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(bt[t], c, -mu)) * six_r);
+        for (int t = 0; t < 4; ++t) e[t] = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(bt[t], c, bias2)));
         uint32_t pw[4][2];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -233,10 +237,10 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
 #pragma unroll
             for (int wd = 0; wd < 2; ++wd) {
                 uint32_t x = 0;
-                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 0] * six_r, s[t][8 * wd + 1] * six_r, sc, 0);
-                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 2] * six_r, s[t][8 * wd + 3] * six_r, sc, 1);
-                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 4] * six_r, s[t][8 * wd + 5] * six_r, sc, 2);
-                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 6] * six_r, s[t][8 * wd + 7] * six_r, sc, 3);
+                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 0], s[t][8 * wd + 1], sc, 0);
+                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 2], s[t][8 * wd + 3], sc, 1);
+                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 4], s[t][8 * wd + 5], sc, 2);
+                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 6], s[t][8 * wd + 7], sc, 3);
                 pw[t][wd] = x;
             }
         }
@@ -263,8 +267,8 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
                 oacc[cb] = mfma_f4_32x32x64(av, (int)L.vs[4 * rr + 2 * g + h], pb, psc, oacc[cb]);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        BQA_WAIT_VM(0);
+        barrier_only();
         J = Jn;
         buf ^= 1;
     }
@@ -280,8 +284,8 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
         VStage vst;
         issue_bf(a, b, hk, sel[0] * KB, lds[0].b, w, l, tid, vst);
         store_bf(vst, lds[0].b, tid);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        BQA_WAIT_VM(0);
+        barrier_only();
     }
     buf = 0;
     const uint16_t* qh = (const uint16_t*)a.q_hi.p + b * a.q_hi.sB + hq * a.q_hi.sH + (int64_t)(row_ok ? qrow : 0) * a.q_hi.sN;
@@ -341,8 +345,8 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
             }
         }
         if (it + 1 < n_items) store_bf(vst, lds[buf ^ 1].b, tid);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        BQA_WAIT_VM(0);
+        barrier_only();
         buf ^= 1;
         (void)k0;
     }
@@ -406,16 +410,20 @@ struct LdsDec {
 
 __device__ __forceinline__ void dec_issue_f4(const ThriftDecArgs& a, int bhk, int J, LdsF4& L, int l) {
     const int t0 = J * KB;
+    const uint8_t* kbase = a.kc + ((int64_t)bhk * a.Nk + t0) * (D / 2);
+    const uint8_t* vbase = a.vc + (int64_t)bhk * D * (a.Nk / 2) + t0 / 2;
 #pragma unroll
     for (int sgm = 0; sgm < 8; ++sgm) {
         const int r = 16 * sgm + (l >> 2);
-        dma16(a.kc + ((int64_t)bhk * a.Nk + t0 + r) * (D / 2) + 16 * ((l & 3) ^ fk64(r)), L.kc + 1024 * sgm);
-        dma16(a.vc + ((int64_t)bhk * D + r) * (a.Nk / 2) + t0 / 2 + 16 * ((l & 3) ^ fv64(r)), L.vc + 1024 * sgm);
+        lds_copy16((uint32_t)(r * (D / 2) + 16 * ((l & 3) ^ fk64(r))), kbase, lds_addr(L.kc + 1024 * sgm));
+        lds_copy16((uint32_t)r * (uint32_t)(a.Nk / 2) + (uint32_t)(16 * ((l & 3) ^ fv64(r))), vbase,
+                   lds_addr(L.vc + 1024 * sgm));
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        dma4(a.ks + ((int64_t)bhk * a.Nk + t0 + 64 * u + l) * (D / 32), L.ks + 256 * u);
-        dma4(a.vs + ((int64_t)bhk * D + 64 * u + l) * (a.Nk / 32) + t0 / 32, L.vs + 256 * u);
+        lds_copy4((uint32_t)(4 * l), a.ks + ((int64_t)bhk * a.Nk + t0 + 64 * u) * (D / 32), lds_addr(L.ks + 256 * u));
+        lds_copy4((uint32_t)l * (uint32_t)(a.Nk / 32), a.vs + ((int64_t)bhk * D + 64 * u) * (a.Nk / 32) + t0 / 32,
+                  lds_addr(L.vs + 256 * u));
     }
 }
 
@@ -426,11 +434,11 @@ struct VQuarter {
 // channels 8 cg ..) into registers for the transposed store.
 __device__ __forceinline__ void dec_issue_bf(const ThriftDecArgs& a, int b, int hk, int k0, LdsDec& L, int l,
                                              VQuarter& vq) {
-    const uint16_t* kb = (const uint16_t*)a.k_hi.p + b * a.k_hi.sB + hk * a.k_hi.sH;
+    const uint16_t* kb = (const uint16_t*)a.k_hi.p + b * a.k_hi.sB + hk * a.k_hi.sH + (int64_t)k0 * a.k_hi.sN;
 #pragma unroll
     for (int sgm = 0; sgm < 8; ++sgm) {
         const int r = 4 * sgm + (l >> 4);
-        dma16(kb + (int64_t)(k0 + r) * a.k_hi.sN + 8 * ((l & 15) ^ fk256(r)), L.b.k + 1024 * sgm);
+        lds_copy16((uint32_t)(2 * (r * a.k_hi.sN + 8 * ((l & 15) ^ fk256(r)))), kb, lds_addr(L.b.k + 1024 * sgm));
     }
     const uint16_t* vb = (const uint16_t*)a.v_hi.p + b * a.v_hi.sB + hk * a.v_hi.sH;
     const int cg = l & 15, kq = l >> 4;
@@ -508,8 +516,8 @@ __global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
     int J = next_f4(b0), buf = 0;
     if (J < b1) {
         dec_issue_f4(a, bhk, J, lds[0].f, l);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        BQA_WAIT_VM(0);
+        barrier_only();
     }
     while (J < b1) {
         const int Jn = next_f4(J + 1);
@@ -542,20 +550,27 @@ __global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
             if (mx > m_ref) move_frame(oacc, l_run, m_ref, __builtin_ceilf(mx));
         }
         const float mu = m_ref == -__builtin_inff() ? 0.0f : m_ref;
-        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                s[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c, -mu));
-                ps[t] += s[t][i];
-            }
-        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        // two-level P formed directly as P' = 6 exp2((s - smax) c) (see the prefill)
         const float r = __builtin_amdgcn_exp2f(__builtin_fmaf(smax, c, -mu));
+        const float bias2 = r > 0.0f ? 2.584962500721156f - smax * c : -__builtin_inff();   // log2(6) - smax c
+        float ps[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float q0 = 0.0f, q1 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                s[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c, bias2));
+                s[t][i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i + 1], c, bias2));
+                q0 += s[t][i];
+                q1 += s[t][i + 1];
+            }
+            ps[t] = q0 + q1;
+        }
+        if (r > 0.0f) l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) * (r * (1.0f / 6.0f));
         const float six_r = r > 0.0f ? 6.0f / r : 0.0f;
         int e[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) e[t] = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(bt[t], c, -mu)) * six_r);
+        for (int t = 0; t < 4; ++t) e[t] = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(bt[t], c, bias2)));
         uint32_t pw[4][2];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -563,10 +578,10 @@ __global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
 #pragma unroll
             for (int wd = 0; wd < 2; ++wd) {
                 uint32_t x = 0;
-                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 0] * six_r, s[t][8 * wd + 1] * six_r, sc, 0);
-                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 2] * six_r, s[t][8 * wd + 3] * six_r, sc, 1);
-                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 4] * six_r, s[t][8 * wd + 5] * six_r, sc, 2);
-                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 6] * six_r, s[t][8 * wd + 7] * six_r, sc, 3);
+                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 0], s[t][8 * wd + 1], sc, 0);
+                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 2], s[t][8 * wd + 3], sc, 1);
+                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 4], s[t][8 * wd + 5], sc, 2);
+                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 6], s[t][8 * wd + 7], sc, 3);
                 pw[t][wd] = x;
             }
         }
@@ -591,8 +606,8 @@ __global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
                 oacc[cb] = mfma_f4_32x32x64(av, (int)L.vs[4 * rr + 2 * g + h], pb, psc, oacc[cb]);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        BQA_WAIT_VM(0);
+        barrier_only();
         J = Jn;
         buf ^= 1;
     }
@@ -613,8 +628,8 @@ __global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
         VQuarter vq;
         dec_issue_bf(a, b, hk, (b0 + (it >> 2)) * KB + DQ * (it & 3), lds[0], l, vq);
         dec_store_bf(vq, lds[0], l);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        BQA_WAIT_VM(0);
+        barrier_only();
     }
     const uint16_t* qh = (const uint16_t*)a.q_hi.p + b * a.q_hi.sB + hq * a.q_hi.sH;
     v8bf qv[8];
@@ -662,8 +677,8 @@ __global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
             }
         }
         if (itn < n_it) dec_store_bf(vq, lds[buf ^ 1], l);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        BQA_WAIT_VM(0);
+        barrier_only();
         it = itn;
         buf ^= 1;
     }

@@ -51,12 +51,23 @@ __device__ __forceinline__ float partner32f(float x) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
+// The base and the LDS address must be the same in every lane; readfirstlane
+// puts them in scalar registers where the compiler cannot prove it itself
+// (it folds away for values already known to be uniform).
+__device__ __forceinline__ const void* uniform_base(const void* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void lds_copy16(uint32_t voff, const void* sbase, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+                 "s"(uniform_base(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory");
 }
 __device__ __forceinline__ void lds_copy4(uint32_t voff, const void* sbase, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff),
+                 "s"(uniform_base(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory");
 }
 // s_waitcnt with vmcnt(n) (n < 64) and lgkmcnt(0), expcnt not waited for
