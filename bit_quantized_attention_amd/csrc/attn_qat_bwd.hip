@@ -35,6 +35,8 @@ namespace {
 constexpr int D = 128;
 constexpr int TQ = 128;
 constexpr int TK = 64;
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int sigma(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
 __device__ __forceinline__ int fs64(int r) { return ((r >> 2) & 3) ^ (((r >> 4) & 1) << 1); }
@@ -215,8 +217,8 @@ struct RowTile {
 struct LdsKVq {
     KeyTile kt;                  // fixed: the workgroup's key block
     RowTile rt;                  // per-row inputs of the query tile
-    uint8_t pt[TK * TQ * 2];     // P^ transposed: 64 keys x 128 queries fp16 (chunks XOR key % 16)
-    uint8_t st[TK * TQ * 2];     // dS transposed
+    uint8_t pt[TQ * TK * 2];     // P^: 128 queries x 64 keys fp16, 128-byte rows (chunks XOR query % 8)
+    uint8_t st[TQ * TK * 2];     // dS, bf16, same layout
     uint8_t gT[D * TQ * 2];      // dO^T: 128 channels x 128 queries fp16
     uint8_t qT[D * TQ * 2];      // deq(Q)^T
 };
@@ -313,26 +315,46 @@ __global__ __launch_bounds__(512, 1) void qbwd_dkdv_kernel(QatBwdArgs a) {
         row_from_lds(L.rt, qc, h, rin);
         float p[16], pq[16], ds[16];
         tile_pds_g(L.kt, rin, c, krow, h, kh, p, pq, ds);
-        // P^ and dS to LDS as [key][query] fp16 / bf16
+        // P^ (fp16) and dS (bf16) to LDS, query-major: this lane's 16 keys are
+        // two 16-byte chunks of its query's row
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = 32 * kh + 16 * h + i;
-            const int off = key * 256 + 16 * ((qc >> 3) ^ (key & 15)) + 2 * (qc & 7);
-            *(uint16_t*)(L.pt + off) = f32_to_f16_bits(pq[i]);
-            *(uint16_t*)(L.st + off) = f32_to_bf16_bits(ds[i]);
+        for (int hc = 0; hc < 2; ++hc) {
+            v8h ph;
+            v8bf sb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ph[e] = (_Float16)pq[8 * hc + e];
+                sb[e] = (__bf16)ds[8 * hc + e];
+            }
+            const int off = qc * 128 + 16 * ((4 * kh + 2 * h + hc) ^ (qc & 7));
+            *(v8h*)(L.pt + off) = ph;
+            *(v8bf*)(L.st + off) = sb;
         }
         // the columns of tile I landed, P^ and dS are written, the rows are read
         BQA_WAIT_VM(0);
         barrier_only();
         if (more) rows_issue(a, cp, bh, b, hq, I + 1, L.rt, w, l);
-        // dV += P^T dO, dK += dS^T deq(Q): K-steps of 16 queries
+        // dV += P^T dO, dK += dS^T deq(Q): K-steps of 16 queries.  The A
+        // operands (key = lane % 32, 8 queries) come from the query-major P^
+        // and dS by transposing reads: in each 16-lane group, lane j names 4
+        // keys (4 (j % 4) ..) of query j / 4, and lane i receives key i of
+        // the 4 queries.
         {
-            const int ch = co + lq, key = ko + lq;
+            const int ch = co + lq;
+            const int grp = l >> 4, li = l & 15;
+            const int kcol = ko + 16 * (grp & 1) + 4 * (li & 3);
 #pragma unroll
             for (int st = 0; st < 8; ++st) {
-                const int pc = 16 * ((2 * st + h) ^ (key & 15));
-                const v8h ap = *(const v8h*)(L.pt + key * 256 + pc);
-                const v8bf as = *(const v8bf*)(L.st + key * 256 + pc);
+                v4s tp[2], ts[2];
+#pragma unroll
+                for (int part = 0; part < 2; ++part) {
+                    const int row = 16 * st + 8 * (grp >> 1) + 4 * part + (li >> 2);
+                    const int off = row * 128 + 16 * ((kcol >> 3) ^ (row & 7)) + 2 * (kcol & 7);
+                    tp[part] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(L.pt + off));
+                    ts[part] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(L.st + off));
+                }
+                const v8h ap = __builtin_bit_cast(v8h, v8s{tp[0][0], tp[0][1], tp[0][2], tp[0][3], tp[1][0], tp[1][1], tp[1][2], tp[1][3]});
+                const v8bf as = __builtin_bit_cast(v8bf, v8s{ts[0][0], ts[0][1], ts[0][2], ts[0][3], ts[1][0], ts[1][1], ts[1][2], ts[1][3]});
                 const int cq = 2 * st + h;                // 16-byte chunk of 8 queries
                 const v8h bg = *(const v8h*)(L.gT + ch * 256 + 16 * (cq ^ fc256(ch)));
                 const v8bf bq = *(const v8bf*)(L.qT + ch * 256 + 16 * (cq ^ fc256(ch)));
