@@ -42,17 +42,7 @@ __device__ __forceinline__ int fc64(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int fc128(int r) { return (r >> 1) & 7; }
 
 // 16 values (one lane half's keys or queries of a 32-group) -> v4i of INT8
-// codes, rint(fp32(x * inv)) with the tile's inverse scale.  inv comes from
-// the tile's largest magnitude, so |x * inv| <= 127 and no clamp is needed:
-// the code is the low byte of fp32(x * inv) + 1.5 * 2^23 (the addition rounds
-// to the nearest even integer).
-__device__ __forceinline__ int q8x4(float a, float b, float c, float d, float inv) {
-#pragma clang fp contract(off)
-    const float M = 12582912.0f;
-    const uint32_t wa = __builtin_bit_cast(uint32_t, a * inv + M), wb = __builtin_bit_cast(uint32_t, b * inv + M);
-    const uint32_t wc = __builtin_bit_cast(uint32_t, c * inv + M), wd = __builtin_bit_cast(uint32_t, d * inv + M);
-    return (int)(__builtin_amdgcn_perm(wb, wa, 0x0c0c0400u) | __builtin_amdgcn_perm(wd, wc, 0x04000c0cu));
-}
+// codes with the tile's inverse scale (q8x4).
 __device__ __forceinline__ v4i pack16(const float* x, float inv) {
     return v4i{q8x4(x[0], x[1], x[2], x[3], inv), q8x4(x[4], x[5], x[6], x[7], inv),
                q8x4(x[8], x[9], x[10], x[11], inv), q8x4(x[12], x[13], x[14], x[15], inv)};

@@ -129,6 +129,19 @@ __device__ __forceinline__ int enc_i8(float x, float inv) {
     return (int)r;
 }
 
+// Four values -> four INT8 codes rint(fp32(x * inv)) packed little-endian in
+// one word.  The caller guarantees |x * inv| <= 127 (inv comes from the
+// largest magnitude), so no clamp is needed: the code is the low byte of
+// fp32(x * inv) + 1.5 * 2^23, whose addition rounds to the nearest even
+// integer.  inv = 0 gives zero codes.
+__device__ __forceinline__ int q8x4(float a, float b, float c, float d, float inv) {
+#pragma clang fp contract(off)
+    const float M = 12582912.0f;
+    const uint32_t wa = __builtin_bit_cast(uint32_t, a * inv + M), wb = __builtin_bit_cast(uint32_t, b * inv + M);
+    const uint32_t wc = __builtin_bit_cast(uint32_t, c * inv + M), wd = __builtin_bit_cast(uint32_t, d * inv + M);
+    return (int)(__builtin_amdgcn_perm(wb, wa, 0x0c0c0400u) | __builtin_amdgcn_perm(wd, wc, 0x04000c0cu));
+}
+
 // OCP e4m3 ("fn"): exponent bias 7, 3 mantissa bits, largest finite 448;
 // nearest-even, saturating (anything at or above 448 encodes as 448).
 __device__ __forceinline__ uint32_t enc_e4m3(float x) {

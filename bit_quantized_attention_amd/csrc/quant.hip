@@ -13,6 +13,8 @@
 //
 // All kernels are coalesced on the [.., N, d] input rows; each thread moves
 // 16 bytes per load.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -20,56 +22,96 @@
 
 namespace bqa {
 
-// ------------------------------------------------------------ K token sums
-// grid (BH, chunks); 256 threads = 16 rows x 16 column groups of 8 channels;
-// fp64 partial sums of each chunk of tokens.
-template <bool IS_F16>
-__global__ __launch_bounds__(256) void ksum_partial_kernel(Dense x, int H, int N, int d, int rows_per_chunk,
-                                                            double* __restrict__ part) {
+// ------------------------------------------------------------ column partials
+// grid (BH, chunks); 256 threads = 16 rows x 16 column groups of 8 channels.
+// Each chunk of tokens is reduced per channel into part[bh][chunk][c]: SUM
+// gives fp64 token sums (K smoothing), otherwise fp32 absolute maxima
+// (per-channel V scales).
+template <bool IS_F16, bool SUM>
+__global__ __launch_bounds__(256) void col_partial_kernel(Dense x, int H, int N, int d, int rows_per_chunk,
+                                                          void* __restrict__ part_out) {
+    using Acc = typename std::conditional<SUM, double, float>::type;
     const int bh = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y;
     const int b = bh / H, h = bh % H;
     const int cg = threadIdx.x % 16, r = threadIdx.x / 16;
     const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH + cg * 8;
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    Acc acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    auto take = [&](const v4i& raw) {
+        const uint16_t* e = (const uint16_t*)&raw;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float f = load_half<IS_F16>(e + k);
+            if constexpr (SUM) acc[k] += (double)f;
+            else acc[k] = __builtin_fmaxf(acc[k], __builtin_fabsf(f));
+        }
+    };
     const int t0 = chunk * rows_per_chunk, t1 = min(N, t0 + rows_per_chunk);
     if (cg * 8 < d) {
+        // four rows in flight per thread (measured: two are too few for
+        // 512-row chunks, eight or more slow the maxima down)
         int t = t0 + r;
-        for (; t + 48 < t1; t += 64) {                       // four rows in flight per thread
+        for (; t + 48 < t1; t += 64) {
             v4i raw[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) raw[u] = *(const v4i*)(base + (int64_t)(t + 16 * u) * x.sN);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint16_t* e = (const uint16_t*)&raw[u];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) acc[k] += (double)load_half<IS_F16>(e + k);
-            }
+            for (int u = 0; u < 4; ++u) take(raw[u]);
         }
-        for (; t < t1; t += 16) {
-            v4i raw = *(const v4i*)(base + (int64_t)t * x.sN);
-            const uint16_t* e = (const uint16_t*)&raw;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) acc[k] += (double)load_half<IS_F16>(e + k);
-        }
+        for (; t < t1; t += 16) take(*(const v4i*)(base + (int64_t)t * x.sN));
     }
-    __shared__ double red[16][128];
+    __shared__ Acc red[16][128];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
         if (cg * 8 + k < d) red[r][cg * 8 + k] = acc[k];
     __syncthreads();
-    if (threadIdx.x < d) {
-        double sum = 0.0;
-        for (int rr = 0; rr < 16; ++rr) sum += red[rr][threadIdx.x];
-        part[((int64_t)bh * nchunks + chunk) * d + threadIdx.x] = sum;
+    if ((int)threadIdx.x < d) {
+        Acc v = red[0][threadIdx.x];
+        for (int rr = 1; rr < 16; ++rr) {
+            if constexpr (SUM) v += red[rr][threadIdx.x];
+            else v = __builtin_fmaxf(v, red[rr][threadIdx.x]);
+        }
+        ((Acc*)part_out)[((int64_t)bh * nchunks + chunk) * d + threadIdx.x] = v;
     }
 }
 
+// Per-chunk partials of one channel (stride d between chunks), combined in
+// two steps so that the first eight loads can be issued ahead of the bulk
+// loads of the consumer and overlap them.  Sums are exact here (fp64 sums of
+// bf16/fp16 values) and maxima are order-free, so the grouping is free.
+template <class Acc>
+struct PartLoad {
+    Acc t[8];
+    __device__ __forceinline__ void issue(const Acc* p, int n, int d) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = u < n ? p[(int64_t)u * d] : Acc(0);
+    }
+    template <bool SUM>
+    __device__ __forceinline__ Acc combine(Acc v) const {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if constexpr (SUM) v += t[u];
+            else v = __builtin_fmaxf(v, t[u]);
+        }
+        return v;
+    }
+    template <bool SUM>
+    __device__ __forceinline__ Acc finish(const Acc* p, int n, int d) const {
+        Acc v = combine<SUM>(Acc(0));
+        for (int k = 8; k < n; k += 8) {                 // further chunks, eight loads at a time
+            PartLoad more;
+            more.issue(p + (int64_t)k * d, n - k, d);
+            v = more.combine<SUM>(v);
+        }
+        return v;
+    }
+};
+
 // ------------------------------------------------------------ INT8 token blocks
-// grid BH * (N / blk); 256 threads; the block (blk x d) is held in registers:
-// each thread owns NG groups of 8 consecutive elements (NG = blk*d/2048),
+// grid BH * (N / blk); 256 threads; the blk x d block is held in registers:
+// each thread owns NG groups of 8 consecutive elements (NG = blk d / 2048),
 // always at the same 8 channels.  With `part` the K-smoothing mean is
 // finalised here from the fp64 partial token sums, mu = fp32(S/N - eps), and
-// the first block of each head writes it to `mu_out`.
+// block 0 of each head writes it to `mu_out`.
 template <bool IS_F16, int NG>
 __global__ __launch_bounds__(256) void quant_i8_tokblock_kernel(Dense x, int H, int N, int d, int blk,
                                                                  const double* __restrict__ part, int nchunks,
@@ -79,27 +121,32 @@ __global__ __launch_bounds__(256) void quant_i8_tokblock_kernel(Dense x, int H, 
     const int nb = N / blk;
     const int bh = blockIdx.x / nb, ib = blockIdx.x % nb;
     const int b = bh / H, h = bh % H;
-    const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH;
+    const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH + (int64_t)ib * blk * x.sN;
     const int gpr = d / 8;                               // groups per token row
     const int c0 = (threadIdx.x % gpr) * 8;              // this thread's channels (256 % gpr == 0)
     __shared__ float mu_s[128];
     __shared__ float wmax[4];
+    const bool has_mu = part != nullptr;
+    const bool fin = has_mu && (int)threadIdx.x < d;
+    const double* pch = part + (int64_t)bh * nchunks * d + threadIdx.x;
+    PartLoad<double> pl;
+    if (fin) pl.issue(pch, nchunks, d);
     v4i raw[NG];
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
         const int g = threadIdx.x + k * 256;
-        raw[k] = *(const v4i*)(base + (int64_t)(ib * blk + g / gpr) * x.sN + c0);
+        raw[k] = *(const v4i*)(base + (int64_t)(g / gpr) * x.sN + c0);
     }
     float mu[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (part) {
-        if ((int)threadIdx.x < d) {
-            double sum = 0.0;
-            for (int k = 0; k < nchunks; ++k) sum += part[((int64_t)bh * nchunks + k) * d + threadIdx.x];
-            const float m = (float)(sum / (double)N - eps);
+    if (has_mu) {
+        if (fin) {
+            const float m = (float)(pl.finish<true>(pch, nchunks, d) / (double)N - eps);
             mu_s[threadIdx.x] = m;
             if (ib == 0 && mu_out) mu_out[(int64_t)bh * d + threadIdx.x] = m;
         }
-        __syncthreads();
+        // LDS writes done; the bulk loads above stay in flight across the barrier
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        barrier_only();
 #pragma unroll
         for (int j = 0; j < 8; ++j) mu[j] = mu_s[c0 + j];
     }
@@ -111,7 +158,7 @@ __global__ __launch_bounds__(256) void quant_i8_tokblock_kernel(Dense x, int H, 
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             float f = load_half<IS_F16>(e + j);
-            if (part) f = f - mu[j];
+            if (has_mu) f = f - mu[j];
             v[k][j] = f;
             amax = __builtin_fmaxf(amax, __builtin_fabsf(f));
         }
@@ -119,85 +166,60 @@ __global__ __launch_bounds__(256) void quant_i8_tokblock_kernel(Dense x, int H, 
     amax = wave_max(amax);
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
     __syncthreads();
-    amax = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
-    float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-    float scale = amax / 127.0f;
-    if (!(amax > 0.0f) || __builtin_isinf(inv)) { inv = 0.0f; scale = 0.0f; }
+    const float am = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+    float inv = am > 0.0f ? 127.0f / am : 0.0f;
+    float scale = am / 127.0f;
+    if (!(am > 0.0f) || __builtin_isinf(inv)) { inv = 0.0f; scale = 0.0f; }
     if (threadIdx.x == 0) scales[(int64_t)bh * nb + ib] = scale;
     int8_t* out = codes + ((int64_t)bh * N + (int64_t)ib * blk) * d;
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
         const int g = threadIdx.x + k * 256;
-        uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w0 |= ((uint32_t)(enc_i8(v[k][j], inv) & 0xFF)) << (8 * j);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w1 |= ((uint32_t)(enc_i8(v[k][4 + j], inv) & 0xFF)) << (8 * j);
+        // |v| <= am, so |v * inv| <= 127
+        const uint32_t w0 = (uint32_t)q8x4(v[k][0], v[k][1], v[k][2], v[k][3], inv);
+        const uint32_t w1 = (uint32_t)q8x4(v[k][4], v[k][5], v[k][6], v[k][7], inv);
         *(uint2*)(out + (int64_t)g * 8) = make_uint2(w0, w1);
     }
 }
 
 // ------------------------------------------------------------ per-channel V
-// pass 1: grid (BH, chunks): per-channel absmax of a token chunk.
-template <bool IS_F16>
-__global__ __launch_bounds__(256) void chan_amax_partial_kernel(Dense x, int H, int N, int d, int rows_per_chunk,
-                                                                 float* __restrict__ part) {
-    const int bh = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y;
-    const int b = bh / H, h = bh % H;
-    const int cg = threadIdx.x % 16, r = threadIdx.x / 16;
-    const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH + cg * 8;
-    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int t0 = chunk * rows_per_chunk, t1 = min(N, t0 + rows_per_chunk);
-    if (cg * 8 < d) {
-        int t = t0 + r;
-        for (; t + 48 < t1; t += 64) {
-            v4i raw[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) raw[u] = *(const v4i*)(base + (int64_t)(t + 16 * u) * x.sN);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint16_t* e = (const uint16_t*)&raw[u];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) m[k] = __builtin_fmaxf(m[k], __builtin_fabsf(load_half<IS_F16>(e + k)));
-            }
-        }
-        for (; t < t1; t += 16) {
-            v4i raw = *(const v4i*)(base + (int64_t)t * x.sN);
-            const uint16_t* e = (const uint16_t*)&raw;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) m[k] = __builtin_fmaxf(m[k], __builtin_fabsf(load_half<IS_F16>(e + k)));
-        }
-    }
-    __shared__ float red[16][128];
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-        if (cg * 8 + k < d) red[r][cg * 8 + k] = m[k];
-    __syncthreads();
-    if (threadIdx.x < d) {
-        float mm = 0.0f;
-        for (int rr = 0; rr < 16; ++rr) mm = __builtin_fmaxf(mm, red[rr][threadIdx.x]);
-        part[((int64_t)bh * nchunks + chunk) * d + threadIdx.x] = mm;
-    }
-}
-
-// pass 2: grid (BH, N / 64): encode 64 tokens of every channel, channel-major
-// output; block (bh, 0) also writes the scales.  FMT 0: int8, 1: e4m3
-// (hardware nearest-even conversion after clamping to +-448, i.e. saturating).
-// Thread t owns 4 tokens x 8 channels; codes are transposed through LDS as
-// 32-bit words (4 tokens of one channel) and written as 16-byte row chunks.
-template <bool IS_F16, int FMT>
+// pass 2: grid (BH, N / TT): encode TT tokens of every channel into
+// channel-major codes; block (bh, 0) also writes the scales.  FMT 0: int8,
+// 1: e4m3 (hardware nearest-even conversion after clamping to +-448, i.e.
+// saturating).  Thread t owns quads of 4 tokens x 8 channels; codes are
+// transposed through LDS as 32-bit words (4 tokens of one channel) and written
+// as 16-byte chunks, TT bytes contiguous per channel.
+template <bool IS_F16, int FMT, int TT>
 __global__ __launch_bounds__(256) void chan_encode_kernel(Dense x, int H, int N, int d,
                                                           const float* __restrict__ part, int nchunks,
                                                           uint8_t* __restrict__ codes_t,
                                                           float* __restrict__ scales) {
+    constexpr int NQ = TT / 4;                             // token quads per tile
     const int bh = blockIdx.x, tb = blockIdx.y;
     const int b = bh / H, h = bh % H;
     __shared__ float inv_s[128];
-    __shared__ uint32_t tile[128][16 + 1];
-    if ((int)threadIdx.x < d) {
-        float amax = 0.0f;
-        for (int k = 0; k < nchunks; ++k)
-            amax = __builtin_fmaxf(amax, part[((int64_t)bh * nchunks + k) * d + threadIdx.x]);
+    __shared__ uint32_t tile[128][NQ + 1];
+    const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH;
+    const int gpr = d / 8;                                 // channel groups
+    const int tpg = 256 / gpr;                             // threads per channel group
+    const int c0 = (threadIdx.x % gpr) * 8;
+    const int q = threadIdx.x / gpr;
+    constexpr int MAXQ = NQ * 16 / 256;                    // quads per thread at d = 128, the most (d <= 128)
+    const bool fin = (int)threadIdx.x < d;
+    const float* pch = part + (int64_t)bh * nchunks * d + threadIdx.x;
+    PartLoad<float> pl;
+    if (fin) pl.issue(pch, nchunks, d);
+    v4i raw[MAXQ][4];
+#pragma unroll
+    for (int i = 0; i < MAXQ; ++i) {
+        const int tq = q + i * tpg;
+        if (tq < NQ) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) raw[i][u] = *(const v4i*)(base + (int64_t)(tb * TT + 4 * tq + u) * x.sN + c0);
+        }
+    }
+    if (fin) {
+        const float amax = pl.finish<false>(pch, nchunks, d);
         const float top = FMT == 0 ? 127.0f : 448.0f;
         float inv = amax > 0.0f ? top / amax : 0.0f;
         float scale = amax / top;
@@ -205,35 +227,36 @@ __global__ __launch_bounds__(256) void chan_encode_kernel(Dense x, int H, int N,
         inv_s[threadIdx.x] = inv;
         if (tb == 0) scales[(int64_t)bh * d + threadIdx.x] = scale;
     }
-    __syncthreads();
-    const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH;
-    const int gpr = d / 8;                                 // channel groups
-    const int tpg = 256 / gpr;                             // threads per channel group
-    const int c0 = (threadIdx.x % gpr) * 8;
-    const int q = threadIdx.x / gpr;                       // token quad index (64/4 = 16 quads)
-    for (int tq = q; tq < 16; tq += tpg) {
-        v4i raw[4];
+    __builtin_amdgcn_s_waitcnt(0xC07F);                    // LDS writes done; bulk loads stay in flight
+    barrier_only();
 #pragma unroll
-        for (int u = 0; u < 4; ++u) raw[u] = *(const v4i*)(base + (int64_t)(tb * 64 + 4 * tq + u) * x.sN + c0);
+    for (int i = 0; i < MAXQ; ++i) {
+        const int tq = q + i * tpg;
+        if (tq < NQ) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t word = 0;
-            const float iv = inv_s[c0 + j];
+            for (int j = 0; j < 8; ++j) {
+                const float iv = inv_s[c0 + j];
+                float f[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float f = load_half<IS_F16>((const uint16_t*)&raw[u] + j) * iv;
-                uint32_t code;
-                if constexpr (FMT == 0) code = (uint32_t)(enc_i8(f, 1.0f) & 0xFF);
-                else code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(f, -448.0f, 448.0f), 0.0f, 0, false) & 0xFFu;
-                word |= code << (8 * u);
+                for (int u = 0; u < 4; ++u) f[u] = load_half<IS_F16>((const uint16_t*)&raw[i][u] + j) * iv;
+                uint32_t word;
+                if constexpr (FMT == 0) {
+                    // |x| <= the channel's absmax, so |f| <= 127
+                    word = (uint32_t)q8x4(f[0], f[1], f[2], f[3], 1.0f);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) f[u] = __builtin_amdgcn_fmed3f(f[u], -448.0f, 448.0f);
+                    word = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+                    word = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], (int)word, true);
+                }
+                tile[c0 + j][tq] = word;
             }
-            tile[c0 + j][tq] = word;
         }
     }
     __syncthreads();
-    for (int qq = threadIdx.x; qq < d * 4; qq += 256) {
-        const int c = qq / 4, p16 = qq % 4;
-        *(uint4*)(codes_t + ((int64_t)bh * d + c) * N + tb * 64 + p16 * 16) =
+    for (int qq = threadIdx.x; qq < d * (TT / 16); qq += 256) {
+        const int c = qq / (TT / 16), p16 = qq % (TT / 16);
+        *(uint4*)(codes_t + ((int64_t)bh * d + c) * N + tb * TT + p16 * 16) =
             make_uint4(tile[c][4 * p16], tile[c][4 * p16 + 1], tile[c][4 * p16 + 2], tile[c][4 * p16 + 3]);
     }
 }
@@ -327,9 +350,11 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(Dense x, int H, int N, int
 
 // ------------------------------------------------------------ launchers
 static int chunks_for(int BH, int N) {
-    // enough blocks to fill the chip (~2 per CU), at least 256 rows per chunk
-    int want = (512 + BH - 1) / BH;
-    int maxc = (N + 255) / 256;
+    // about one block per CU, at least 512 rows per chunk (measured: fewer,
+    // longer streams beat two blocks per CU, and the consumers combine fewer
+    // partials)
+    int want = (256 + BH - 1) / BH;
+    int maxc = (N + 511) / 512;
     int c = want < maxc ? want : maxc;
     return c < 1 ? 1 : c;
 }
@@ -341,8 +366,7 @@ template <bool F16>
 static hipError_t launch_tokblock_t(const Dense& x, int B, int H, int N, int d, int blk, const double* part,
                                     int nch, double eps, float* mu, int8_t* codes, float* scales, hipStream_t st) {
     const int grid = B * H * (N / blk);
-    const int ng = blk * d / 2048;
-    switch (ng) {
+    switch (blk * d / 2048) {
         case 2: quant_i8_tokblock_kernel<F16, 2><<<grid, 256, 0, st>>>(x, H, N, d, blk, part, nch, eps, mu, codes, scales); break;
         case 4: quant_i8_tokblock_kernel<F16, 4><<<grid, 256, 0, st>>>(x, H, N, d, blk, part, nch, eps, mu, codes, scales); break;
         default: quant_i8_tokblock_kernel<F16, 8><<<grid, 256, 0, st>>>(x, H, N, d, blk, part, nch, eps, mu, codes, scales); break;
@@ -359,8 +383,8 @@ hipError_t launch_quant_i8_tokblock(const Dense& x, bool f16, int B, int H, int 
     double* part = nullptr;
     if (smooth) {
         part = (double*)ws;
-        if (f16) ksum_partial_kernel<true><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
-        else ksum_partial_kernel<false><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
+        if (f16) col_partial_kernel<true, true><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
+        else col_partial_kernel<false, true><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
     }
     return f16 ? launch_tokblock_t<true>(x, B, H, N, d, blk, part, nch, eps, mu, codes, scales, st)
                : launch_tokblock_t<false>(x, B, H, N, d, blk, part, nch, eps, mu, codes, scales, st);
@@ -370,16 +394,22 @@ hipError_t launch_quant_chan(const Dense& x, bool f16, int B, int H, int N, int 
                              float* scales, void* ws, hipStream_t st) {
     const int BH = B * H, nch = chunks_for(BH, N), rpc = (N + nch - 1) / nch;
     float* part = (float*)ws;
-    if (f16) chan_amax_partial_kernel<true><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
-    else chan_amax_partial_kernel<false><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
-    dim3 g(BH, N / 64);
+    if (f16) col_partial_kernel<true, false><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
+    else col_partial_kernel<false, false><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
+    // 128-token tiles (128-byte code rows) where N allows, else 64
+    const bool wide = N % 128 == 0;
+    dim3 g(BH, N / (wide ? 128 : 64));
+#define BQA_CHAN(F16, FMT)                                                                                  \
+    (wide ? chan_encode_kernel<F16, FMT, 128><<<g, 256, 0, st>>>(x, H, N, d, part, nch, codes_t, scales)   \
+          : chan_encode_kernel<F16, FMT, 64><<<g, 256, 0, st>>>(x, H, N, d, part, nch, codes_t, scales))
     if (fmt == 0) {
-        if (f16) chan_encode_kernel<true, 0><<<g, 256, 0, st>>>(x, H, N, d, part, nch, codes_t, scales);
-        else chan_encode_kernel<false, 0><<<g, 256, 0, st>>>(x, H, N, d, part, nch, codes_t, scales);
+        if (f16) BQA_CHAN(true, 0);
+        else BQA_CHAN(false, 0);
     } else {
-        if (f16) chan_encode_kernel<true, 1><<<g, 256, 0, st>>>(x, H, N, d, part, nch, codes_t, scales);
-        else chan_encode_kernel<false, 1><<<g, 256, 0, st>>>(x, H, N, d, part, nch, codes_t, scales);
+        if (f16) BQA_CHAN(true, 1);
+        else BQA_CHAN(false, 1);
     }
+#undef BQA_CHAN
     return hipGetLastError();
 }
 
