@@ -141,12 +141,12 @@ def _sage_case(w, bqa, torch):
     Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
     p = sage_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.causal, bqa.BQA_SAGE_I8_F8PV, q_block=128,
                      smooth_k=True, smooth_eps=0.0)
-    path = SagePath(p, to_device(Q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype))
+    path = SagePath(p, to_device(Q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype), keep_q_codes=False)
     ops = attention_ops(p)
     return dict(
         path=path, ops=ops, dtype="i8+e4m3",
         workload="SageAttention INT8 forward (c2): B=2 H=16 N=4096 d=128 causal, bf16 in, K-smoothing, "
-                 "INT8 Q/K, e4m3 P.V; step = quantise Q,K,V + attention",
+                 "INT8 Q/K, e4m3 P.V; step = quantise K,V + attention (Q quantised inside the attention kernel)",
         roofline={"bound": "mfma", "kernel": "sage_fwd_f8_kernel (i8 QK^T + fp8 P.V, three-stage pipeline)",
                   "peak": PEAK_I8_TOPS, "ops_per_launch": ops},
         traffic_key="sage_fwd_f8_kernel<128,causal>", cpu=cpu_baseline)
@@ -435,8 +435,11 @@ CASES = {"c2": _sage_case, "c3": _sagebwd_case, "c4": _qat_case, "c4t": _qat_tra
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps; 0 (default): enough for about 0.1 s, at least 10")
+    ap.add_argument("--warmup", type=int, default=0,
+                    help="untimed warmup steps; 0 (default): at least 20 and until 0.5 s have passed, which "
+                         "brings the GPU clocks up from idle")
     ap.add_argument("--workload", choices=sorted(CASES), default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -467,9 +470,18 @@ def main():
     w = wl.WORKLOADS[args.workload.rstrip("t")]
     case = CASES[args.workload](w, bqa, torch)
     path = case["path"]
-    for _ in range(args.warmup):
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or (args.warmup == 0 and (n_warm < 20 or time.perf_counter() - t_w < 0.5)):
         path.step()
+        n_warm += 1
+        if args.warmup == 0 and n_warm % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    args.warmup = n_warm
+    if args.steps <= 0:
+        est = (time.perf_counter() - t_w) / n_warm
+        args.steps = int(min(1000, max(10, round(0.1 / est))))
 
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]

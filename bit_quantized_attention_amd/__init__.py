@@ -14,7 +14,7 @@ import os
 
 __all__ = [
     "BQA_OK", "BqaError", "bqa_problem", "bqa_tensor", "bqa_qtensor", "lib", "problem",
-    "bqa_abi_version", "bqa_status_string", "bqa_workspace_size", "bqa_quantize_blocks",
+    "bqa_abi_version", "bqa_status_string", "bqa_workspace_size", "bqa_quantize_blocks", "bqa_quantize_kv",
     "bqa_select_blocks", "bqa_attn_fwd", "bqa_attn_bwd", "bqa_debug_qk_scores",
 ]
 
@@ -27,9 +27,9 @@ BQA_BF16, BQA_FP16, BQA_INT8, BQA_FP8E4M3, BQA_MXFP4 = range(5)
 BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV, BQA_SAGE_I8_I8PV, BQA_QAT_MXFP4, BQA_THRIFT = range(5)
 BQA_ROLE_Q, BQA_ROLE_K, BQA_ROLE_V, BQA_ROLE_DO = range(4)
 BQA_OP_QUANTIZE_Q, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_V, BQA_OP_QUANTIZE_DO, BQA_OP_SELECT, BQA_OP_FWD, \
-    BQA_OP_BWD = range(7)
+    BQA_OP_BWD, BQA_OP_QUANTIZE_KV = range(8)
 
-EXPORTS = ["bqa_abi_version", "bqa_status_string", "bqa_workspace_size", "bqa_quantize_blocks",
+EXPORTS = ["bqa_abi_version", "bqa_status_string", "bqa_workspace_size", "bqa_quantize_blocks", "bqa_quantize_kv",
            "bqa_select_blocks", "bqa_attn_fwd", "bqa_attn_bwd", "bqa_debug_qk_scores"]
 
 
@@ -77,6 +77,9 @@ def lib():
         L.bqa_quantize_blocks.restype = C.c_int32
         L.bqa_quantize_blocks.argtypes = [P(bqa_problem), C.c_int32, P(bqa_tensor), P(bqa_qtensor), vp, vp, vp,
                                           C.c_size_t, vp]
+        L.bqa_quantize_kv.restype = C.c_int32
+        L.bqa_quantize_kv.argtypes = [P(bqa_problem), P(bqa_tensor), P(bqa_tensor), P(bqa_qtensor), P(bqa_qtensor),
+                                      vp, vp, C.c_size_t, vp]
         L.bqa_select_blocks.restype = C.c_int32
         L.bqa_select_blocks.argtypes = [P(bqa_problem), vp, vp, vp, vp, vp, C.c_size_t, vp]
         L.bqa_attn_fwd.restype = C.c_int32
@@ -184,6 +187,19 @@ def bqa_quantize_blocks(p, role, x, out: bqa_qtensor, k_mean=None, block_means=N
                                   _stream(stream))
     if check:
         _check(s, "bqa_quantize_blocks")
+    return s
+
+
+def bqa_quantize_kv(p, k, v, kq: bqa_qtensor, vq: bqa_qtensor, k_mean=None, workspace=None, workspace_bytes=None,
+                    stream=None, check=True) -> int:
+    kd = k if isinstance(k, bqa_tensor) else dense(k)
+    vd = v if isinstance(v, bqa_tensor) else dense(v)
+    wb = workspace_bytes if workspace_bytes is not None else (workspace.numel() * workspace.element_size()
+                                                              if workspace is not None else 0)
+    s = lib().bqa_quantize_kv(C.byref(p), _ref(kd), _ref(vd), C.byref(kq), C.byref(vq), _ptr(k_mean),
+                              _ptr(workspace), wb, _stream(stream))
+    if check:
+        _check(s, "bqa_quantize_kv")
     return s
 
 

@@ -124,6 +124,9 @@ size_t bqa_workspace_size(const bqa_problem* p, int32_t op) {
         case BQA_OP_QUANTIZE_V:
             if (p->mode == BQA_SAGE_I8_F8PV || p->mode == BQA_SAGE_I8_I8PV) return ws_chan_bytes(p->B * p->Hkv, p->Nk, p->d);
             return 0;
+        case BQA_OP_QUANTIZE_KV:
+            if (p->mode == BQA_SAGE_I8_F8PV || p->mode == BQA_SAGE_I8_I8PV) return ws_kv_bytes(p->B * p->Hkv, p->Nk, p->d);
+            return 0;
         case BQA_OP_BWD:
             if (is_sage(p->mode) && p->Nq == p->Nk) return ws_sage_bwd_bytes(p->B, p->Hq, p->Nq, p->d);
             if (p->mode == BQA_QAT_MXFP4 && p->Nq == p->Nk) return ws_qat_bwd_bytes(p->B, p->Hq, p->Nq, p->d);
@@ -184,6 +187,30 @@ bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_ten
     TRY(check_device());
     return launched(launch_quant_i8_tokblock(as_dense(x), f16, p->B, H, N, d, blk, smooth, (double)p->smooth_eps,
                                              k_mean, ws, (int8_t*)out->codes, (float*)out->scales, st));
+}
+
+bqa_status bqa_quantize_kv(const bqa_problem* p, const bqa_tensor* k, const bqa_tensor* v, bqa_qtensor* kq,
+                           bqa_qtensor* vq, float* k_mean, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_problem(p));
+    if (p->mode != BQA_SAGE_I8_F8PV && p->mode != BQA_SAGE_I8_I8PV) return BQA_E_UNSUPPORTED;
+    TRY(check_sage_blocks(p));
+    if (!kq || !vq) return BQA_E_NULL;
+    TRY(check_dense(k, true, true));
+    TRY(check_dense(v, true, true));
+    if (k->dtype != v->dtype) return BQA_E_UNSUPPORTED;
+    TRY(check_q(kq, BQA_INT8, 0));
+    const int vfmt = p->mode == BQA_SAGE_I8_F8PV ? BQA_FP8E4M3 : BQA_INT8;
+    TRY(check_q(vq, vfmt, 1));
+    if (kq->block != 64 || p->k_block != 64 || vq->block != p->Nk || p->Nk % 64 != 0) return BQA_E_UNSUPPORTED;
+    const int BH = p->B * p->Hkv;
+    if (!ws || ws_bytes < ws_kv_bytes(BH, p->Nk, p->d)) return BQA_E_WORKSPACE;
+    if (!aligned16(ws)) return BQA_E_ALIGN;
+    if (p->smooth_k && !std::isfinite(p->smooth_eps)) return BQA_E_SHAPE;
+    TRY(check_device());
+    return launched(launch_quant_kv(as_dense(k), as_dense(v), k->dtype == BQA_FP16, p->B, p->Hkv, p->Nk, p->d,
+                                    p->smooth_k != 0, (double)p->smooth_eps, k_mean, (int8_t*)kq->codes,
+                                    (float*)kq->scales, vfmt == BQA_INT8 ? 0 : 1, (uint8_t*)vq->codes,
+                                    (float*)vq->scales, ws, (hipStream_t)stream));
 }
 
 bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const float* k_means, int32_t* sel_idx,
@@ -289,9 +316,18 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
     }
     if (is_sage(p->mode)) {
         TRY(check_sage_blocks(p));
-        TRY(check_q(q, BQA_INT8, 0));
+        // q_hi given (fp8 P.V): the kernel quantises Q itself; q, when given, receives its codes
+        const bool q_in = q_hi != nullptr;
+        if (q_in) {
+            if (p->mode != BQA_SAGE_I8_F8PV) return BQA_E_UNSUPPORTED;
+            TRY(check_dense(q_hi, false, true));
+        }
+        if (!q_in || q) {
+            TRY(check_q(q, BQA_INT8, 0));
+            if (q->block != p->q_block) return BQA_E_UNSUPPORTED;
+        }
         TRY(check_q(k, BQA_INT8, 0));
-        if (q->block != p->q_block || k->block != p->k_block) return BQA_E_UNSUPPORTED;
+        if (k->block != p->k_block) return BQA_E_UNSUPPORTED;
         SageFwdArgs a{};
         int pv;
         if (p->mode == BQA_SAGE_I8_F16PV) {
@@ -307,7 +343,13 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
             a.vs = (const float*)v->scales;
         }
         TRY(check_dense(o, pv == PV_F16, pv != PV_F16));
-        a.qc = (const int8_t*)q->codes; a.qs = (const float*)q->scales; a.q_blk = p->q_block;
+        a.q_blk = p->q_block;
+        if (q_in) {
+            a.q16 = as_dense(q_hi);
+            if (q) { a.qc_out = (int8_t*)q->codes; a.qs_out = (float*)q->scales; }
+        } else {
+            a.qc = (const int8_t*)q->codes; a.qs = (const float*)q->scales;
+        }
         a.kc = (const int8_t*)k->codes; a.ks = (const float*)k->scales;
         a.o = as_dense(o); a.lse = lse;
         a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk; a.causal = p->causal;

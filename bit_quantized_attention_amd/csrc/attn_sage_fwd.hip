@@ -261,17 +261,12 @@ __device__ __forceinline__ void tile_pv(RowState<D>& st, const float (&f0)[16], 
         float inv = r > 0.0f ? 127.0f / r : 0.0f;
         if (__builtin_isinf(inv)) inv = 0.0f;
         const float rs = __builtin_ldexpf(r * (1.0f / 127.0f), shift);
+        // every P of the row is at most r, so |P * inv| <= 127 (no clamp)
         v4i pb0, pb1;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                w0 |= (uint32_t)enc_i8(f0[4 * k + e], inv) << (8 * e);
-                w1 |= (uint32_t)enc_i8(f1[4 * k + e], inv) << (8 * e);
-            }
-            pb0[k] = (int)w0;
-            pb1[k] = (int)w1;
+            pb0[k] = q8x4(f0[4 * k], f0[4 * k + 1], f0[4 * k + 2], f0[4 * k + 3], inv);
+            pb1[k] = q8x4(f1[4 * k], f1[4 * k + 1], f1[4 * k + 2], f1[4 * k + 3], inv);
         }
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb) {
@@ -674,16 +669,43 @@ __global__ __launch_bounds__(256, 2) void sage_fwd_f8_kernel(SageFwdArgs a) {
     const __attribute__((address_space(4))) float* kscale =
         (const __attribute__((address_space(4))) float*)(a.ks + (int64_t)bhk * (a.Nk / BN));
 
+    __shared__ float qmax_s[4];
+    const bool q_in = a.q16.p != nullptr;
+
     auto qtile = [&](const int qt) __attribute__((always_inline)) {
         const int q0 = qt * BM;
         const int qrow = q0 + 32 * w + lq;
         const bool row_ok = qrow < a.Nq;
         v4i qb[D / 32];
+        v4i qraw[D / 16];                // Q quantised here: this lane's D/2 bf16 values, 8 per vector
+        float cq = 0.0f;
+        if (q_in) {
+            // the lane's channels are those of its INT8 operand: 32 kk + 16 h + 0..15
+            const uint16_t* qsrc = (const uint16_t*)a.q16.p + b * a.q16.sB + hq * a.q16.sH + (int64_t)qrow * a.q16.sN + 16 * h;
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-            qb[kk] = row_ok ? *(const v4i*)(a.qc + ((int64_t)bh * a.Nq + qrow) * D + 16 * h + 32 * kk) : v4i{};
-        const float cq = row_ok ? a.qs[(int64_t)bh * (a.Nq / a.q_blk) + qrow / a.q_blk] * a.c_log2 : 0.0f;
+            for (int u = 0; u < D / 16; ++u) qraw[u] = row_ok ? *(const v4i*)(qsrc + 32 * (u >> 1) + 8 * (u & 1)) : v4i{};
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk)
+                qb[kk] = row_ok ? *(const v4i*)(a.qc + ((int64_t)bh * a.Nq + qrow) * D + 16 * h + 32 * kk) : v4i{};
+            cq = row_ok ? a.qs[(int64_t)bh * (a.Nq / a.q_blk) + qrow / a.q_blk] * a.c_log2 : 0.0f;
+        }
         __builtin_amdgcn_s_waitcnt(0);
+        if (q_in) {
+            // largest magnitude of the wavefront's 32 rows; the block's (q_blk rows,
+            // whole wavefronts) is taken after the prologue barrier
+            float am = 0.0f;
+#pragma unroll
+            for (int u = 0; u < D / 16; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t wd = (uint32_t)qraw[u][e];
+                    am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(__builtin_bit_cast(float, wd << 16)),
+                                                             __builtin_fabsf(__builtin_bit_cast(float, wd & 0xFFFF0000u))));
+                }
+            am = wave_max(am);
+            if (l == 0) qmax_s[w] = am;
+        }
 
         const int last_row = min(q0 + BM, a.Nq) - 1;
         const int n_tiles = CAUSAL ? min(a.Nk / BN, (last_row + off) / BN + 1) : a.Nk / BN;
@@ -716,8 +738,39 @@ __global__ __launch_bounds__(256, 2) void sage_fwd_f8_kernel(SageFwdArgs a) {
             cp.v_tile(vbase, min(2, tl) * BN, v_lds[2], w);
         }
         static_assert(CP::KU == CP::VU && 5 * CP::KU < 16, "wait counts");
-        __builtin_amdgcn_s_waitcnt(0x0070 | (5 * CP::KU));   // K0 and K1 landed, zero fill done
+        __builtin_amdgcn_s_waitcnt(0x0070 | (5 * CP::KU));   // K0 and K1 landed, zero fill and maxima written
         asm volatile("s_barrier" ::: "memory");
+        if (q_in) {
+            // per-block INT8 as the token-block quantiser: scale = amax / 127,
+            // code = rint(fp32(x * (127 / amax))); no clamp since |x| <= amax
+            const int nwb = a.q_blk / 32, w0 = w - w % nwb;
+            float am = qmax_s[w0];
+            for (int u = 1; u < nwb; ++u) am = __builtin_fmaxf(am, qmax_s[w0 + u]);
+            float inv = am > 0.0f ? 127.0f / am : 0.0f;
+            float scale = am / 127.0f;
+            if (!(am > 0.0f) || __builtin_isinf(inv)) { inv = 0.0f; scale = 0.0f; }
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                float x[16];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t wd = (uint32_t)qraw[2 * kk + (e >> 2)][e & 3];
+                    x[2 * e] = __builtin_bit_cast(float, wd << 16);
+                    x[2 * e + 1] = __builtin_bit_cast(float, wd & 0xFFFF0000u);
+                }
+#pragma unroll
+                for (int g = 0; g < 4; ++g) qb[kk][g] = q8x4(x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3], inv);
+            }
+            if (row_ok) {
+                cq = scale * a.c_log2;
+                if (a.qc_out) {
+#pragma unroll
+                    for (int kk = 0; kk < D / 32; ++kk)
+                        *(v4i*)(a.qc_out + ((int64_t)bh * a.Nq + qrow) * D + 16 * h + 32 * kk) = qb[kk];
+                }
+                if (a.qs_out && l == 0 && w == w0) a.qs_out[(int64_t)bh * (a.Nq / a.q_blk) + qrow / a.q_blk] = scale;
+            }
+        }
 
         v16i s0 = v16i{}, s1 = v16i{};   // scores of the tile about to be processed
         if (wave_tiles > 0) qk_tile<D>(k_lds[0], qb, krow, h, s0, s1);

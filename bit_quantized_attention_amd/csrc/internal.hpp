@@ -17,6 +17,10 @@ hipError_t launch_quant_i8_tokblock(const Dense& x, bool f16, int B, int H, int 
                                     hipStream_t st);
 hipError_t launch_quant_chan(const Dense& x, bool f16, int B, int H, int N, int d, int fmt, uint8_t* codes_t,
                              float* scales, void* ws, hipStream_t st);
+size_t ws_kv_bytes(int BH, int N, int d);
+hipError_t launch_quant_kv(const Dense& k, const Dense& v, bool f16, int B, int H, int N, int d, bool smooth,
+                           double eps, float* mu, int8_t* kc, float* ks, int vfmt, uint8_t* vc, float* vs, void* ws,
+                           hipStream_t st);
 hipError_t launch_quant_mx(const Dense& x, bool f16, int B, int H, int N, int d, int axis, uint8_t* codes,
                            uint8_t* scales, float* means, hipStream_t st);
 
@@ -24,6 +28,8 @@ hipError_t launch_quant_mx(const Dense& x, bool f16, int B, int H, int N, int d,
 enum { PV_F16 = 0, PV_F8 = 1, PV_I8 = 2 };
 struct SageFwdArgs {
     const int8_t* qc;  const float* qs;  int q_blk;     // Q codes [B,Hq,Nq,d], scales [B,Hq,Nq/q_blk]
+    Dense q16;                                           // bf16 Q quantised in the kernel (p null: use qc/qs)
+    int8_t* qc_out;    float* qs_out;                    // with q16: where its codes / scales go (or null)
     const int8_t* kc;  const float* ks;                  // K codes [B,Hkv,Nk,d], scales [B,Hkv,Nk/64]
     const uint8_t* vc; const float* vs;                  // V codes [B,Hkv,d,Nk], scales [B,Hkv,d]
     Dense v16;                                           // V fp16 (PV_F16)

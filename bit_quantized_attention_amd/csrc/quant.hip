@@ -28,10 +28,9 @@ namespace bqa {
 // gives fp64 token sums (K smoothing), otherwise fp32 absolute maxima
 // (per-channel V scales).
 template <bool IS_F16, bool SUM>
-__global__ __launch_bounds__(256) void col_partial_kernel(Dense x, int H, int N, int d, int rows_per_chunk,
-                                                          void* __restrict__ part_out) {
+__device__ __forceinline__ void col_partial_body(const Dense& x, int H, int N, int d, int rows_per_chunk,
+                                                 void* __restrict__ part_out, int bh, int chunk, int nchunks) {
     using Acc = typename std::conditional<SUM, double, float>::type;
-    const int bh = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y;
     const int b = bh / H, h = bh % H;
     const int cg = threadIdx.x % 16, r = threadIdx.x / 16;
     const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH + cg * 8;
@@ -74,6 +73,12 @@ __global__ __launch_bounds__(256) void col_partial_kernel(Dense x, int H, int N,
     }
 }
 
+template <bool IS_F16, bool SUM>
+__global__ __launch_bounds__(256) void col_partial_kernel(Dense x, int H, int N, int d, int rows_per_chunk,
+                                                          void* __restrict__ part_out) {
+    col_partial_body<IS_F16, SUM>(x, H, N, d, rows_per_chunk, part_out, blockIdx.x, blockIdx.y, gridDim.y);
+}
+
 // Per-chunk partials of one channel (stride d between chunks), combined in
 // two steps so that the first eight loads can be issued ahead of the bulk
 // loads of the consumer and overlap them.  Sums are exact here (fp64 sums of
@@ -113,13 +118,12 @@ struct PartLoad {
 // finalised here from the fp64 partial token sums, mu = fp32(S/N - eps), and
 // block 0 of each head writes it to `mu_out`.
 template <bool IS_F16, int NG>
-__global__ __launch_bounds__(256) void quant_i8_tokblock_kernel(Dense x, int H, int N, int d, int blk,
-                                                                 const double* __restrict__ part, int nchunks,
-                                                                 double eps, float* __restrict__ mu_out,
-                                                                 int8_t* __restrict__ codes,
-                                                                 float* __restrict__ scales) {
+__device__ __forceinline__ void tokblock_body(const Dense& x, int H, int N, int d, int blk,
+                                              const double* __restrict__ part, int nchunks, double eps,
+                                              float* __restrict__ mu_out, int8_t* __restrict__ codes,
+                                              float* __restrict__ scales, int block_id) {
     const int nb = N / blk;
-    const int bh = blockIdx.x / nb, ib = blockIdx.x % nb;
+    const int bh = block_id / nb, ib = block_id % nb;
     const int b = bh / H, h = bh % H;
     const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH + (int64_t)ib * blk * x.sN;
     const int gpr = d / 8;                               // groups per token row
@@ -182,6 +186,15 @@ __global__ __launch_bounds__(256) void quant_i8_tokblock_kernel(Dense x, int H, 
     }
 }
 
+template <bool IS_F16, int NG>
+__global__ __launch_bounds__(256) void quant_i8_tokblock_kernel(Dense x, int H, int N, int d, int blk,
+                                                                 const double* __restrict__ part, int nchunks,
+                                                                 double eps, float* __restrict__ mu_out,
+                                                                 int8_t* __restrict__ codes,
+                                                                 float* __restrict__ scales) {
+    tokblock_body<IS_F16, NG>(x, H, N, d, blk, part, nchunks, eps, mu_out, codes, scales, blockIdx.x);
+}
+
 // ------------------------------------------------------------ per-channel V
 // pass 2: grid (BH, N / TT): encode TT tokens of every channel into
 // channel-major codes; block (bh, 0) also writes the scales.  FMT 0: int8,
@@ -190,12 +203,10 @@ __global__ __launch_bounds__(256) void quant_i8_tokblock_kernel(Dense x, int H, 
 // transposed through LDS as 32-bit words (4 tokens of one channel) and written
 // as 16-byte chunks, TT bytes contiguous per channel.
 template <bool IS_F16, int FMT, int TT>
-__global__ __launch_bounds__(256) void chan_encode_kernel(Dense x, int H, int N, int d,
-                                                          const float* __restrict__ part, int nchunks,
-                                                          uint8_t* __restrict__ codes_t,
-                                                          float* __restrict__ scales) {
+__device__ __forceinline__ void chan_encode_body(const Dense& x, int H, int N, int d, const float* __restrict__ part,
+                                                 int nchunks, uint8_t* __restrict__ codes_t,
+                                                 float* __restrict__ scales, int bh, int tb) {
     constexpr int NQ = TT / 4;                             // token quads per tile
-    const int bh = blockIdx.x, tb = blockIdx.y;
     const int b = bh / H, h = bh % H;
     __shared__ float inv_s[128];
     __shared__ uint32_t tile[128][NQ + 1];
@@ -258,6 +269,46 @@ __global__ __launch_bounds__(256) void chan_encode_kernel(Dense x, int H, int N,
         const int c = qq / (TT / 16), p16 = qq % (TT / 16);
         *(uint4*)(codes_t + ((int64_t)bh * d + c) * N + tb * TT + p16 * 16) =
             make_uint4(tile[c][4 * p16], tile[c][4 * p16 + 1], tile[c][4 * p16 + 2], tile[c][4 * p16 + 3]);
+    }
+}
+
+template <bool IS_F16, int FMT, int TT>
+__global__ __launch_bounds__(256) void chan_encode_kernel(Dense x, int H, int N, int d,
+                                                          const float* __restrict__ part, int nchunks,
+                                                          uint8_t* __restrict__ codes_t,
+                                                          float* __restrict__ scales) {
+    chan_encode_body<IS_F16, FMT, TT>(x, H, N, d, part, nchunks, codes_t, scales, blockIdx.x, blockIdx.y);
+}
+
+// ------------------------------------------------------------ K and V together
+// The same work as the K and V kernels above in two launches instead of four:
+// the first takes the K token sums (with smoothing) and the V channel maxima,
+// the second the K token blocks and the V codes; each workgroup picks its job
+// from its index (K jobs first).
+struct KvJob {
+    Dense k, v;
+    int H, N, d, nch, rpc;
+    bool smooth;
+    double eps;
+    double* kpart; float* vpart;
+    float* mu; int8_t* kc; float* ks; uint8_t* vc; float* vs;
+};
+
+template <bool IS_F16>
+__global__ __launch_bounds__(256) void kv_partial_kernel(KvJob j, int nk) {
+    const int id = blockIdx.x;
+    if (id < nk) col_partial_body<IS_F16, true>(j.k, j.H, j.N, j.d, j.rpc, j.kpart, id / j.nch, id % j.nch, j.nch);
+    else col_partial_body<IS_F16, false>(j.v, j.H, j.N, j.d, j.rpc, j.vpart, (id - nk) / j.nch, (id - nk) % j.nch, j.nch);
+}
+
+template <bool IS_F16, int FMT, int TT, int NG>
+__global__ __launch_bounds__(256) void kv_encode_kernel(KvJob j, int nk) {
+    const int id = blockIdx.x;
+    if (id < nk) {
+        tokblock_body<IS_F16, NG>(j.k, j.H, j.N, j.d, 64, j.smooth ? j.kpart : nullptr, j.nch, j.eps, j.mu, j.kc, j.ks, id);
+    } else {
+        const int nt = j.N / TT;
+        chan_encode_body<IS_F16, FMT, TT>(j.v, j.H, j.N, j.d, j.vpart, j.nch, j.vc, j.vs, (id - nk) / nt, (id - nk) % nt);
     }
 }
 
@@ -410,6 +461,45 @@ hipError_t launch_quant_chan(const Dense& x, bool f16, int B, int H, int N, int 
         else BQA_CHAN(false, 1);
     }
 #undef BQA_CHAN
+    return hipGetLastError();
+}
+
+size_t ws_kv_bytes(int BH, int N, int d) {
+    return (ws_kmean_bytes(BH, N, d) + 255) / 256 * 256 + ws_chan_bytes(BH, N, d);
+}
+
+hipError_t launch_quant_kv(const Dense& k, const Dense& v, bool f16, int B, int H, int N, int d, bool smooth,
+                           double eps, float* mu, int8_t* kc, float* ks, int vfmt, uint8_t* vc, float* vs, void* ws,
+                           hipStream_t st) {
+    KvJob j;
+    j.k = k; j.v = v; j.H = H; j.N = N; j.d = d;
+    const int BH = B * H;
+    j.nch = chunks_for(BH, N);
+    j.rpc = (N + j.nch - 1) / j.nch;
+    j.smooth = smooth; j.eps = eps;
+    j.kpart = (double*)ws;
+    j.vpart = (float*)((char*)ws + (ws_kmean_bytes(BH, N, d) + 255) / 256 * 256);
+    j.mu = mu; j.kc = kc; j.ks = ks; j.vc = vc; j.vs = vs;
+    const int nkp = smooth ? BH * j.nch : 0;
+    if (f16) kv_partial_kernel<true><<<nkp + BH * j.nch, 256, 0, st>>>(j, nkp);
+    else kv_partial_kernel<false><<<nkp + BH * j.nch, 256, 0, st>>>(j, nkp);
+    // K token blocks of 64: 64 d / 2048 groups of 8 per thread (4 at d = 128, 2 at d = 64)
+    const int nke = BH * (N / 64);
+    const bool wide = N % 128 == 0;
+    const int nve = BH * (N / (wide ? 128 : 64));
+#define BQA_KV_T(F16, FMT, NG)                                                               \
+    (wide ? kv_encode_kernel<F16, FMT, 128, NG><<<nke + nve, 256, 0, st>>>(j, nke)           \
+          : kv_encode_kernel<F16, FMT, 64, NG><<<nke + nve, 256, 0, st>>>(j, nke))
+#define BQA_KV(F16, FMT) (d == 128 ? BQA_KV_T(F16, FMT, 4) : BQA_KV_T(F16, FMT, 2))
+    if (vfmt == 0) {
+        if (f16) BQA_KV(true, 0);
+        else BQA_KV(false, 0);
+    } else {
+        if (f16) BQA_KV(true, 1);
+        else BQA_KV(false, 1);
+    }
+#undef BQA_KV
+#undef BQA_KV_T
     return hipGetLastError();
 }
 

@@ -9,10 +9,10 @@ from __future__ import annotations
 
 import torch
 
-from . import (BQA_FP8E4M3, BQA_INT8, BQA_MXFP4, BQA_OP_FWD, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_V,
-               BQA_OP_BWD, BQA_QAT_MXFP4, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V, BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV,
-               BQA_THRIFT, bqa_attn_bwd, bqa_attn_fwd, bqa_quantize_blocks, bqa_select_blocks, bqa_workspace_size, dense,
-               max_sel, problem, qtensor)
+from . import (BQA_FP8E4M3, BQA_INT8, BQA_MXFP4, BQA_OP_FWD, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_KV,
+               BQA_OP_QUANTIZE_V, BQA_OP_BWD, BQA_QAT_MXFP4, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V, BQA_SAGE_I8_F16PV,
+               BQA_SAGE_I8_F8PV, BQA_SAGE_I8_I8PV, BQA_THRIFT, bqa_attn_bwd, bqa_attn_fwd, bqa_quantize_blocks,
+               bqa_quantize_kv, bqa_select_blocks, bqa_workspace_size, dense, max_sel, problem, qtensor)
 
 
 def sage_problem(B, Hq, Hkv, Nq, Nk, d, causal, mode, q_block=128, k_block=64, smooth_k=True, smooth_eps=0.0,
@@ -22,11 +22,17 @@ def sage_problem(B, Hq, Hkv, Nq, Nk, d, causal, mode, q_block=128, k_block=64, s
 
 
 class SagePath:
-    """SageAttention INT8 forward: quantise Q, K (smoothed), V, then attend."""
+    """SageAttention INT8 forward: quantise Q, K (smoothed), V, then attend.
 
-    def __init__(self, p, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    With fp8 P.V the attention kernel quantises Q itself (fuse_q, the
+    default there): quantize() then handles K and V, and forward() writes the
+    Q codes and scales to qc / qs only when keep_q_codes is set."""
+
+    def __init__(self, p, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fuse_q=None, keep_q_codes=True):
         dev = q.device
         self.p = p
+        self.fuse_q = (p.mode == BQA_SAGE_I8_F8PV) if fuse_q is None else bool(fuse_q)
+        self.keep_q_codes = keep_q_codes
         B, Hq, Hkv, Nq, Nk, d = p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d
         self.q, self.k, self.v = q, k, v
         self.qc = torch.empty((B, Hq, Nq, d), dtype=torch.int8, device=dev)
@@ -42,15 +48,25 @@ class SagePath:
             self.vs = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev)
             fmt = BQA_FP8E4M3 if p.mode == BQA_SAGE_I8_F8PV else BQA_INT8
             self.vq = qtensor(fmt, 1, Nk, self.vc, self.vs)
-        ws = max(bqa_workspace_size(p, BQA_OP_QUANTIZE_K), bqa_workspace_size(p, BQA_OP_QUANTIZE_V), 16)
+        # K and V go through one call (two launches) in the fp8 / int8 P.V modes
+        self.kv_joint = p.mode in (BQA_SAGE_I8_F8PV, BQA_SAGE_I8_I8PV)
+        ws = max(bqa_workspace_size(p, BQA_OP_QUANTIZE_K), bqa_workspace_size(p, BQA_OP_QUANTIZE_V),
+                 bqa_workspace_size(p, BQA_OP_QUANTIZE_KV), 16)
         self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
         odt = torch.float16 if p.mode == BQA_SAGE_I8_F16PV else torch.bfloat16
         self.o = torch.empty((B, Hq, Nq, d), dtype=odt, device=dev)
         self.lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
         self._qd, self._kd, self._vd, self._od = dense(q), dense(k), dense(v), dense(self.o)
 
-    def quantize(self):
+    def quantize_q(self):
         bqa_quantize_blocks(self.p, BQA_ROLE_Q, self._qd, self.qq, workspace=self.ws)
+
+    def quantize(self):
+        if not self.fuse_q:
+            self.quantize_q()
+        if self.kv_joint:
+            bqa_quantize_kv(self.p, self._kd, self._vd, self.kq, self.vq, k_mean=self.mu, workspace=self.ws)
+            return
         bqa_quantize_blocks(self.p, BQA_ROLE_K, self._kd, self.kq, k_mean=self.mu, workspace=self.ws)
         if self.vq is not None:
             bqa_quantize_blocks(self.p, BQA_ROLE_V, self._vd, self.vq, workspace=self.ws)
@@ -58,6 +74,9 @@ class SagePath:
     def forward(self):
         if self.p.mode == BQA_SAGE_I8_F16PV:
             bqa_attn_fwd(self.p, q=self.qq, k=self.kq, v_hi=self._vd, o=self._od, lse=self.lse)
+        elif self.fuse_q:
+            bqa_attn_fwd(self.p, q=self.qq if self.keep_q_codes else None, q_hi=self._qd, k=self.kq, v=self.vq,
+                         o=self._od, lse=self.lse)
         else:
             bqa_attn_fwd(self.p, q=self.qq, k=self.kq, v=self.vq, o=self._od, lse=self.lse)
 

@@ -131,7 +131,7 @@ typedef struct bqa_qtensor {
 /* Operations, for bqa_workspace_size(). */
 enum {
     BQA_OP_QUANTIZE_Q = 0, BQA_OP_QUANTIZE_K = 1, BQA_OP_QUANTIZE_V = 2, BQA_OP_QUANTIZE_DO = 3,
-    BQA_OP_SELECT = 4, BQA_OP_FWD = 5, BQA_OP_BWD = 6
+    BQA_OP_SELECT = 4, BQA_OP_FWD = 5, BQA_OP_BWD = 6, BQA_OP_QUANTIZE_KV = 7
 };
 
 /* ABI version of the loaded library (BQA_ABI_VERSION it was built with). */
@@ -174,6 +174,20 @@ bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_ten
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * K and V of the Sage fp8 / int8 P.V modes in one call: the same codes,
+ * scales and k_mean as bqa_quantize_blocks for role K (INT8 token blocks of
+ * 64 tokens, K-smoothing per p->smooth_k and p->smooth_eps) and role V
+ * (per-channel e4m3 for BQA_SAGE_I8_F8PV, int8 for BQA_SAGE_I8_I8PV), in two
+ * kernel launches instead of four: the K token sums and the V channel maxima
+ * first, then both encodings.  k and v are [B, Hkv, Nk, d] of one dtype (bf16
+ * or fp16); kq is INT8 axis 0 with block 64, vq the per-channel layout with
+ * block Nk; Nk a multiple of 64.  Workspace: bqa_workspace_size(p,
+ * BQA_OP_QUANTIZE_KV) bytes, 16-byte aligned.
+ */
+bqa_status bqa_quantize_kv(const bqa_problem* p, const bqa_tensor* k, const bqa_tensor* v, bqa_qtensor* kq,
+                           bqa_qtensor* vq, float* k_mean, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * ThriftAttention block selection ("ThriftAttention", Method step 1): for
  * every (b, query head h, query block i) the importance of key block j is
  * qbar_i . kbar_j (kbar of KV head h / (Hq/Hkv)) over the valid key blocks
@@ -195,7 +209,11 @@ bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const f
  *
  *  - Sage modes ("SageBwd", Methodology 1): q, k are the INT8 token-block
  *    codes (k of the smoothed K); v is per-channel e4m3 (F8PV) or int8
- *    (I8PV) codes, or for F16PV v_hi holds V in fp16 and v is unused.
+ *    (I8PV) codes, or for F16PV v_hi holds V in fp16 and v is unused.  In
+ *    F8PV, q_hi (bf16 [B, Hq, Nq, d]) may be given instead: the kernel then
+ *    quantises Q itself, with the codes and scales bqa_quantize_blocks gives
+ *    for role Q, and writes them to q's buffers when q is not NULL (q may be
+ *    NULL).
  *    Keys are visited in tiles of k_block, ascending; per tile the running max
  *    is updated, P = exp(s - m) is rounded for P.V as the mode says, and the
  *    row sum accumulates the unrounded P.

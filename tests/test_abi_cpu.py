@@ -113,6 +113,34 @@ def test_quantize_validation(L):
         assert _quant(_p(), bqa.BQA_ROLE_V, x, _q(fmt=bqa.BQA_FP8E4M3, axis=1, block=4096)) == bqa.BQA_E_DEVICE
 
 
+def test_quantize_kv_validation(L):
+    k, v = _dense(), _dense(ptr=0x50000)
+    kq, vq = _q(block=64), _q(fmt=bqa.BQA_FP8E4M3, axis=1, block=4096)
+
+    def qkv(p, k=k, v=v, kq=kq, vq=vq, ws=0x40000, wsb=1 << 30):
+        return bqa.lib().bqa_quantize_kv(C.byref(p), None if k is None else C.byref(k),
+                                         None if v is None else C.byref(v), None if kq is None else C.byref(kq),
+                                         None if vq is None else C.byref(vq), None, ws, wsb, None)
+    assert qkv(_p(mode=bqa.BQA_SAGE_I8_F16PV)) == bqa.BQA_E_UNSUPPORTED
+    assert qkv(_p(mode=bqa.BQA_QAT_MXFP4)) == bqa.BQA_E_UNSUPPORTED
+    assert qkv(_p(), kq=None) == bqa.BQA_E_NULL
+    assert qkv(_p(), v=None) == bqa.BQA_E_NULL
+    assert qkv(_p(), v=_dense(ptr=0x50000, dtype=bqa.BQA_FP16)) == bqa.BQA_E_UNSUPPORTED   # K and V differ
+    assert qkv(_p(), kq=_q(block=128)) == bqa.BQA_E_UNSUPPORTED
+    assert qkv(_p(), vq=_q(fmt=bqa.BQA_INT8, axis=1, block=4096)) == bqa.BQA_E_UNSUPPORTED  # F8PV needs e4m3
+    assert qkv(_p(mode=bqa.BQA_SAGE_I8_I8PV)) == bqa.BQA_E_UNSUPPORTED                      # I8PV needs int8
+    assert qkv(_p(), vq=_q(fmt=bqa.BQA_FP8E4M3, axis=1, block=64)) == bqa.BQA_E_UNSUPPORTED
+    need = bqa.bqa_workspace_size(_p(), bqa.BQA_OP_QUANTIZE_KV)
+    assert need >= bqa.bqa_workspace_size(_p(), bqa.BQA_OP_QUANTIZE_K) + bqa.bqa_workspace_size(_p(), bqa.BQA_OP_QUANTIZE_V)
+    assert qkv(_p(), wsb=need - 1) == bqa.BQA_E_WORKSPACE
+    assert qkv(_p(), ws=0, wsb=0) == bqa.BQA_E_WORKSPACE
+    assert qkv(_p(), ws=0x40008) == bqa.BQA_E_ALIGN
+    import torch
+    if not torch.cuda.is_available():
+        assert qkv(_p()) == bqa.BQA_E_DEVICE
+        assert qkv(_p(mode=bqa.BQA_SAGE_I8_I8PV), vq=_q(fmt=bqa.BQA_INT8, axis=1, block=4096)) == bqa.BQA_E_DEVICE
+
+
 def test_fwd_validation(L):
     o = _dense()
     q, k = _q(), _q(block=64)
@@ -131,8 +159,21 @@ def test_fwd_validation(L):
     assert fwd(_p(), o=_dense(dtype=bqa.BQA_FP16)) == bqa.BQA_E_UNSUPPORTED
     assert fwd(_p(mode=bqa.BQA_SAGE_I8_F16PV), v=None) == bqa.BQA_E_NULL
     assert fwd(_p(mode=9)) == bqa.BQA_E_UNSUPPORTED
+
+    def fwd_qhi(p, q=q, q_hi=_dense(ptr=0x60000)):
+        return bqa.lib().bqa_attn_fwd(C.byref(p), None if q is None else C.byref(q), C.byref(k), C.byref(v),
+                                      None if q_hi is None else C.byref(q_hi), None, None, None, None, C.byref(o),
+                                      None, None, None, 0, None)
+    # Q quantised inside the kernel: fp8 P.V and bf16 only; q optional, but checked when given
+    assert fwd_qhi(_p(mode=bqa.BQA_SAGE_I8_I8PV)) == bqa.BQA_E_UNSUPPORTED
+    assert fwd_qhi(_p(), q_hi=_dense(ptr=0x60000, dtype=bqa.BQA_FP16)) == bqa.BQA_E_UNSUPPORTED
+    assert fwd_qhi(_p(), q_hi=_dense(ptr=0x60008)) == bqa.BQA_E_ALIGN
+    assert fwd_qhi(_p(), q=_q(block=64)) == bqa.BQA_E_UNSUPPORTED
+    assert fwd_qhi(_p(), q=_q(codes=0)) == bqa.BQA_E_NULL
     import torch
     if not torch.cuda.is_available():
+        assert fwd_qhi(_p()) == bqa.BQA_E_DEVICE
+        assert fwd_qhi(_p(), q=None) == bqa.BQA_E_DEVICE
         assert fwd(_p()) == bqa.BQA_E_DEVICE
         assert fwd(_p(mode=bqa.BQA_SAGE_I8_F16PV), v=None, v_hi=_dense(dtype=bqa.BQA_FP16),
                    o=_dense(dtype=bqa.BQA_FP16)) == bqa.BQA_E_DEVICE

@@ -20,7 +20,7 @@ def _gpu():
     bqa.lib()
 
 
-def _run(w, mode_name, q_block, eps, Nq=None):
+def _run(w, mode_name, q_block, eps, Nq=None, **kw):
     """Generate the workload, run the GPU path, and build the oracle."""
     import bit_quantized_attention_amd as bqa
     from bit_quantized_attention_amd.runner import SagePath, sage_problem, to_device
@@ -31,7 +31,7 @@ def _run(w, mode_name, q_block, eps, Nq=None):
     p = sage_problem(w.B, w.Hq, w.Hkv, Q.shape[2], K.shape[2], w.d, w.causal, mode, q_block=q_block,
                      smooth_k=True, smooth_eps=eps)
     vdt = "fp16" if mode_name == "f16" else w.dtype
-    path = SagePath(p, to_device(Q, w.dtype), to_device(K, w.dtype), to_device(V, vdt))
+    path = SagePath(p, to_device(Q, w.dtype), to_device(K, w.dtype), to_device(V, vdt), **kw)
     path.step()
     torch.cuda.synchronize()
     orc = SageOracle(Q, K, V, q_block=q_block, eps=eps, pv=mode_name)
@@ -105,9 +105,13 @@ def test_c3_recipe_int8_pv():
 
 def test_c2_full_size_sampled():
     """The full c2 workload (B=2, H=16, N=4096) in the launch configuration the
-    benchmark times; all codes compared, outputs on sampled query tiles."""
+    benchmark times (Q quantised inside the attention kernel, its codes not
+    kept); outputs on sampled query tiles, then every code (Q through the
+    stand-alone quantiser)."""
     w = wl.WORKLOADS["c2"]
-    p, path, orc = _run(w, "f8", q_block=128, eps=0.0)
+    p, path, orc = _run(w, "f8", q_block=128, eps=0.0, keep_q_codes=False)
+    path.quantize_q()
+    torch.cuda.synchronize()
     _check_codes(p, path, orc)
     for (b, h, r) in [(0, 0, (0, 128)), (1, 15, (3968, 4096)), (0, 7, (2048, 2176)), (1, 3, (1920, 2048))]:
         _check_heads(p, path, orc, [(b, h)], rows=r)
@@ -195,3 +199,38 @@ def test_f8_shapes(N, d, causal, hq, hkv):
     p, path, orc = _run(w, "f8", q_block=64, eps=0.0)
     _check_codes(p, path, orc)
     _check_heads(p, path, orc, [(0, h) for h in range(hq)])
+
+
+@pytest.mark.parametrize("N,d,causal,q_block", [(512, 128, True, 128), (320, 128, False, 64), (384, 64, True, 64)])
+def test_q_quantised_in_kernel_matches_separate(N, d, causal, q_block):
+    """fp8 P.V: Q quantised by the attention kernel gives the same codes and
+    scales as the token-block quantiser and bit-identical O and LSE."""
+    import dataclasses
+    w = dataclasses.replace(wl.with_len(wl.WORKLOADS["c2"], N, b=1, hq=2, hkv=2), d=d, causal=causal)
+    _, fused, _ = _run(w, "f8", q_block=q_block, eps=0.0, fuse_q=True)
+    _, sep, _ = _run(w, "f8", q_block=q_block, eps=0.0, fuse_q=False)
+    assert torch.equal(fused.qc, sep.qc) and torch.equal(fused.qs, sep.qs)
+    assert torch.equal(fused.o, sep.o) and torch.equal(fused.lse, sep.lse)
+
+
+@pytest.mark.parametrize("N,d,pv,smooth", [(512, 128, "f8", True), (320, 128, "i8", True), (384, 64, "f8", False)])
+def test_kv_joint_matches_separate(N, d, pv, smooth):
+    """bqa_quantize_kv (two launches) gives the K codes, scales, mean and the
+    V codes and scales of the per-operand calls bit for bit."""
+    import bit_quantized_attention_amd as bqa
+    from bit_quantized_attention_amd.runner import SagePath, sage_problem, to_device
+    import dataclasses
+    w = dataclasses.replace(wl.with_len(wl.WORKLOADS["c2"], N, b=2, hq=2, hkv=2), d=d)
+    Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
+    mode = bqa.BQA_SAGE_I8_F8PV if pv == "f8" else bqa.BQA_SAGE_I8_I8PV
+    p = sage_problem(2, 2, 2, N, N, d, True, mode, q_block=64, smooth_k=smooth, smooth_eps=1e-3)
+    paths = [SagePath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")) for _ in range(2)]
+    paths[1].kv_joint = False
+    for pa in paths:
+        pa.mu.fill_(7.0)
+        pa.quantize()
+    torch.cuda.synchronize()
+    a, b = paths
+    assert paths[0].kv_joint
+    for name in ("kc", "ks", "vc", "vs") + (("mu",) if smooth else ()):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
