@@ -96,19 +96,21 @@ __global__ __launch_bounds__(256) void transpose_i8_kernel(const int8_t* __restr
 
 // ------------------------------------------------------------------ dK, dV
 // One workgroup of 8 wavefronts per 64-key block, over the query tiles.
-// Step I has two phases.  Scores: wavefront (kh, qg) computes S and dP for
-// its 32 keys x 32 queries with keys in lanes, then P and dS; after the
-// tile's maxima it writes their INT8 codes, key-major, to LDS.  Products:
-// wavefront (kh, cq) accumulates dV and dK for its 32 keys x 32 channels over
-// the tile's 128 queries (P^T and dS^T codes from LDS, channel-major dO and Q
+// Scores of tile I: wavefront (kh, qg) computes S and dP for its 32 keys x
+// 32 queries with keys in lanes, then P and dS; after the tile's maxima it
+// writes their INT8 codes, key-major, to LDS.  Products of a tile: wavefront
+// (kh, cq) accumulates dV and dK for its 32 keys x 32 channels over the
+// tile's 128 queries (P^T and dS^T codes from LDS, channel-major dO and Q
 // codes).  Each wavefront thus holds 32 accumulator registers, which lets
-// two of them share a SIMD.
+// two of them share a SIMD.  Step I runs the scores of tile I, then, between
+// its two barriers, the products of tile I+1 under the encoding of tile I's
+// codes, which are written after the second barrier.
 //
 // Query-side tiles: "A" (Q codes, dO bf16, log-sum-exp, delta) in two slots,
 // "B" (channel-major dO and Q codes, read by the products only) in one.  The
 // query tiles go in descending order; the copy of the next tile's A is
-// issued at the start of a step, the copy of its B after the step's
-// products: every copy has at least half a step to land.
+// issued at the start of a step, the copy of a tile's B after its codes are
+// written: every copy has most of a step to land.
 struct LdsKV {
     uint8_t q[2][TQ * D];       // Q codes of the query tile, 128 x 128 B (sigma reads)
     uint8_t dob[2][TQ * D * 2]; // dO bf16, 128 x 256 B (sigma reads)
@@ -124,7 +126,7 @@ struct LdsKV {
 // One wavefront's share of the copies of a query tile, as per-lane offsets
 // from a tile base (the swizzles come from the source each lane names).
 struct KvPlan {
-    static constexpr int NA = 2 + 4 + 1, NB = 2 + 2;   // copies per wavefront: A tile, B tile
+    static constexpr int NA = 2 + 4 + 1;   // copies per wavefront of an A tile (a B tile: 2 + 2)
     uint32_t q[2], g[4], t[2];
     __device__ __forceinline__ KvPlan(int w, int l, int N, int64_t g_sN) {
 #pragma unroll
@@ -207,12 +209,36 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
     // query tiles in descending order: the key blocks of a head that run at
     // the same time read the same query tile, which then comes from L2
     kv_copy_a(a, cp, bh, b, hq, nqt - 1, L, 0, w, l);
-    kv_copy_b(a, cp, bh, nqt - 1, L, w);
     BQA_WAIT_VM(0);
     barrier_only();
+    // The products of tile I+1 run in step I, between its two barriers, under
+    // the vector work of tile I's codes: their MFMA results are folded into
+    // dV, dK at the end of the step with the scales of tile I+1.
+    auto products = [&](v16i& tv, v16i& tk) __attribute__((always_inline)) {
+        tv = v16i{};
+        tk = v16i{};
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            const int ch = 2 * kq + h;
+            const v4i ap = *(const v4i*)(L.pc + prow * 128 + 16 * (ch ^ fc128(prow)));
+            const v4i ad = *(const v4i*)(L.dc + prow * 128 + 16 * (ch ^ fc128(prow)));
+            const v4i bo = *(const v4i*)(L.doT + crow * 128 + 16 * (ch ^ fc128(crow)));
+            const v4i bq = *(const v4i*)(L.qT + crow * 128 + 16 * (ch ^ fc128(crow)));
+            tv = mfma_i8_32x32x32(ap, bo, tv);
+            tk = mfma_i8_32x32x32(ad, bq, tk);
+        }
+    };
+    auto fold = [&](const v16i& tv, const v16i& tk, float sv, float sk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            dv[i] = __builtin_fmaf((float)tv[i], sv, dv[i]);
+            dk[i] = __builtin_fmaf((float)tk[i], sk, dk[i]);
+        }
+    };
+    float sv_prev = 0.0f, sk_prev = 0.0f;
     for (int I = nqt - 1; I >= I0; --I) {
         const int s = (nqt - 1 - I) & 1;
-        const bool more = I > I0;
+        const bool more = I > I0, prev = I < nqt - 1;
         if (more) kv_copy_a(a, cp, bh, b, hq, I - 1, L, s ^ 1, w, l);   // that slot's reads ended a step ago
         const float qsc = qs_u[I];
         const float sc = qsc * ks * c;
@@ -256,15 +282,20 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
                 dmax = __builtin_fmaxf(dmax, __builtin_fabsf(dS[i]));
             }
         }
-        // ---- one INT8 scale per tile for P and for dS (one exchange for both); codes to LDS, key-major
+        // ---- one INT8 scale per tile for P and for dS (one exchange for both)
         pmax = wave_max(pmax);
         dmax = wave_max(dmax);
         if (l == 0) {
             L.red[w] = pmax;
             L.red[8 + w] = dmax;
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's LDS writes are done
+        // maxima written; B(I+1) landed (the copies of A(I-1) may stay in flight)
+        if (more) BQA_WAIT_VM(KvPlan::NA);
+        else BQA_WAIT_VM(0);
         barrier_only();
+        // ---- products of tile I+1 (codes and B written / landed before the barrier)
+        v16i tv, tk;
+        if (prev) products(tv, tk);
         {
             const v4f p0 = *(const v4f*)L.red, p1 = *(const v4f*)(L.red + 4);
             const v4f d0 = *(const v4f*)(L.red + 8), d1 = *(const v4f*)(L.red + 12);
@@ -277,38 +308,29 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
         const float inv_d = dmax > 0.0f ? 127.0f / dmax : 0.0f;
         const bool p_ok = inv_p != 0.0f && inv_p < __builtin_inff();
         const bool d_ok = inv_d != 0.0f && inv_d < __builtin_inff();
-        const int wch = (2 * qg + h) ^ fc128(prow);  // this lane's 16 queries: chunk 2 qg + h of its key row
-        *(v4i*)(L.pc + prow * 128 + 16 * wch) = p_ok ? pack16(P, inv_p) : v4i{};
-        *(v4i*)(L.dc + prow * 128 + 16 * wch) = d_ok ? pack16(dS, inv_d) : v4i{};
+        const v4i pcode = p_ok ? pack16(P, inv_p) : v4i{};
+        const v4i dcode = d_ok ? pack16(dS, inv_d) : v4i{};
         const float sv = p_ok ? pmax * (1.0f / 127.0f) * dos_u[I] : 0.0f;
         const float sk = d_ok ? dmax * (1.0f / 127.0f) * qsc * a.tau : 0.0f;
-        // ---- codes written, B(I) landed (the copies of A(I-1) may stay in flight)
-        if (more) BQA_WAIT_VM(KvPlan::NA);
-        else BQA_WAIT_VM(0);
-        barrier_only();
-        // ---- products: dV += P^T dO, dK += tau dS^T Q over the 4 groups of 32 queries
-        v16i tv = v16i{}, tk = v16i{};
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-            const int ch = 2 * kq + h;
-            const v4i ap = *(const v4i*)(L.pc + prow * 128 + 16 * (ch ^ fc128(prow)));
-            const v4i ad = *(const v4i*)(L.dc + prow * 128 + 16 * (ch ^ fc128(prow)));
-            const v4i bo = *(const v4i*)(L.doT + crow * 128 + 16 * (ch ^ fc128(crow)));
-            const v4i bq = *(const v4i*)(L.qT + crow * 128 + 16 * (ch ^ fc128(crow)));
-            tv = mfma_i8_32x32x32(ap, bo, tv);
-            tk = mfma_i8_32x32x32(ad, bq, tk);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            dv[i] = __builtin_fmaf((float)tv[i], sv, dv[i]);
-            dk[i] = __builtin_fmaf((float)tk[i], sk, dk[i]);
-        }
-        // ---- end of step: A(I-1) landed (the only copy in flight) and every
-        // wavefront is done with B, the codes and the maxima; then copy B(I-1),
-        // which lands during the next step's scores
+        // ---- every wavefront is done with the codes and B of tile I+1 and with
+        // the maxima; A(I-1) landed
         BQA_WAIT_VM(0);
         barrier_only();
-        if (more) kv_copy_b(a, cp, bh, I - 1, L, w);
+        const int wch = (2 * qg + h) ^ fc128(prow);  // this lane's 16 queries: chunk 2 qg + h of its key row
+        *(v4i*)(L.pc + prow * 128 + 16 * wch) = pcode;
+        *(v4i*)(L.dc + prow * 128 + 16 * wch) = dcode;
+        kv_copy_b(a, cp, bh, I, L, w);               // lands during the next step's scores
+        if (prev) fold(tv, tk, sv_prev, sk_prev);
+        sv_prev = sv;
+        sk_prev = sk;
+    }
+    // products of the last tile
+    BQA_WAIT_VM(0);
+    barrier_only();
+    {
+        v16i tv, tk;
+        products(tv, tk);
+        fold(tv, tk, sv_prev, sk_prev);
     }
     uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sB + hq * a.dv.sH;
     uint16_t* dkp = (uint16_t*)a.dk.p + b * a.dk.sB + hq * a.dk.sH;

@@ -187,9 +187,28 @@ __device__ __forceinline__ int mx_exponent(float amax) {
 }
 
 // ------------------------------------------------------------------ reductions
+// Value of x in the lane of the same 32-half 16 positions away.
+__device__ __forceinline__ float partner16f(float x) {
+    const int b = __builtin_bit_cast(int, x);
+    v2i r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
+}
+// x of another lane of the same row of 16 by a DPP pattern (whole wave active)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    const int b = __builtin_bit_cast(int, x);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, CTRL, 0xF, 0xF, false));
+}
+// Largest value over the 64 lanes, in every lane: DPP within rows of 16
+// (lane xor 1, xor 2, mirror of 8, mirror of 16), then the row swaps of 16
+// and 32 lanes; vector instructions only (no LDS round trips).
 __device__ __forceinline__ float wave_max(float v) {
-    for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = __builtin_fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = __builtin_fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = __builtin_fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+    v = __builtin_fmaxf(v, dpp_f<0x140>(v));   // row_mirror
+    v = __builtin_fmaxf(v, partner16f(v));
+    return __builtin_fmaxf(v, partner32f(v));
 }
 
 }  // namespace bqa
