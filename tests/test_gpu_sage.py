@@ -213,10 +213,12 @@ def test_q_quantised_in_kernel_matches_separate(N, d, causal, q_block):
     assert torch.equal(fused.o, sep.o) and torch.equal(fused.lse, sep.lse)
 
 
-@pytest.mark.parametrize("N,d,pv,smooth", [(512, 128, "f8", True), (320, 128, "i8", True), (384, 64, "f8", False)])
-def test_kv_joint_matches_separate(N, d, pv, smooth):
+@pytest.mark.parametrize("N,d,pv,smooth,dt", [(512, 128, "f8", True, "bf16"), (320, 128, "i8", True, "bf16"),
+                                             (384, 64, "f8", False, "bf16"), (448, 128, "f8", True, "fp16")])
+def test_kv_joint_matches_separate(N, d, pv, smooth, dt):
     """bqa_quantize_kv (two launches) gives the K codes, scales, mean and the
-    V codes and scales of the per-operand calls bit for bit."""
+    V codes and scales of the per-operand calls bit for bit (bf16 and fp16
+    inputs, 64- and 128-token V tiles)."""
     import bit_quantized_attention_amd as bqa
     from bit_quantized_attention_amd.runner import SagePath, sage_problem, to_device
     import dataclasses
@@ -224,7 +226,7 @@ def test_kv_joint_matches_separate(N, d, pv, smooth):
     Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
     mode = bqa.BQA_SAGE_I8_F8PV if pv == "f8" else bqa.BQA_SAGE_I8_I8PV
     p = sage_problem(2, 2, 2, N, N, d, True, mode, q_block=64, smooth_k=smooth, smooth_eps=1e-3)
-    paths = [SagePath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")) for _ in range(2)]
+    paths = [SagePath(p, to_device(Q, "bf16"), to_device(K, dt), to_device(V, dt)) for _ in range(2)]
     paths[1].kv_joint = False
     for pa in paths:
         pa.mu.fill_(7.0)
