@@ -446,7 +446,7 @@ def main():
                     help="only run a plain 256 MiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(every kernel is independent per (batch, head), so the path shards by heads; "
               f"this benchmark measures one GPU's share)",
               file=sys.stderr)

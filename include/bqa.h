@@ -55,7 +55,7 @@ enum {
     BQA_OK = 0,
     BQA_E_NULL = -1,          /* a required pointer is NULL */
     BQA_E_SHAPE = -2,         /* inconsistent or out-of-range sizes */
-    BQA_E_UNSUPPORTED = -3,   /* a valid request this build does not implement */
+    BQA_E_UNSUPPORTED = -3,   /* a valid request the library does not implement */
     BQA_E_ALIGN = -4,         /* misaligned pointer or stride, or inner stride != 1 */
     BQA_E_WORKSPACE = -5,     /* workspace pointer NULL or smaller than bqa_workspace_size() */
     BQA_E_DEVICE = -6,        /* the current device is not gfx950, or no device */
