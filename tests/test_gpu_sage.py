@@ -236,3 +236,26 @@ def test_kv_joint_matches_separate(N, d, pv, smooth, dt):
     assert paths[0].kv_joint
     for name in ("kc", "ks", "vc", "vs") + (("mu",) if smooth else ()):
         assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+def test_token_major_layouts():
+    """Q, K, V stored token-major ([B, N, H, d] memory viewed as [B, H, N, d]):
+    the in-kernel Q quantisation, the joint K/V call and the attention follow
+    the strides and give the bits of contiguous inputs."""
+    import bit_quantized_attention_amd as bqa
+    from bit_quantized_attention_amd.runner import SagePath, sage_problem, to_device
+    w = wl.with_len(wl.WORKLOADS["c2"], 384, b=2, hq=4, hkv=2)
+    Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
+    p = sage_problem(2, 4, 2, 384, 384, 128, True, bqa.BQA_SAGE_I8_F8PV, q_block=128, smooth_k=True, smooth_eps=0.0)
+
+    def token_major(x):
+        t = to_device(np.ascontiguousarray(x.transpose(0, 2, 1, 3)), "bf16")   # memory [B, N, H, d]
+        return t.transpose(1, 2)                                                # view [B, H, N, d]
+    dense = SagePath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
+    strided = SagePath(p, token_major(Q), token_major(K), token_major(V))
+    assert not strided.q.is_contiguous()
+    for pa in (dense, strided):
+        pa.step()
+    torch.cuda.synchronize()
+    for name in ("qc", "qs", "kc", "ks", "vc", "vs", "mu", "o", "lse"):
+        assert torch.equal(getattr(dense, name), getattr(strided, name)), name
