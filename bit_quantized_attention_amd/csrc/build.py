@@ -25,11 +25,19 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", HERE,
 ]
+# Per-source additions.  The Thrift decode kernel runs vector work on its
+# matrix accumulators every key block; with accumulators in AGPRs (the
+# compiler's choice when one wavefront per SIMD leaves it 512 registers) each
+# of those instructions costs two extra register-file moves.  The VGPR form
+# keeps them in VGPRs (214 registers, no spills; the prefill kernel of the
+# same file compiles to the same code either way).
+EXTRA = {"attn_thrift.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip" if src.endswith(".hip") else "hip", "-c", os.path.join(HERE, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip" if src.endswith(".hip") else "hip", "-c",
+           os.path.join(HERE, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

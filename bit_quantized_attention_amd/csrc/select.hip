@@ -42,10 +42,24 @@ __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qb
     __shared__ float q[128];
 
     const int tid = threadIdx.x;
-    const int i = blockIdx.x % nqb;
-    const int bh = blockIdx.x / nqb;                  // b * Hq + h
-    const int b = bh / Hq, h = bh % Hq;
-    const int hk = h / (Hq / Hkv);
+    // The G = Hq / Hkv query heads of a KV head read the same key means: when
+    // the (b, KV head) groups come in multiples of the 8 XCDs, workgroup id
+    // 32-aligned blocks are arranged so that the G heads of a group share an
+    // XCD (ids that differ by multiples of 8), and its L2.
+    const int G = Hq / Hkv, nbk = (int)(gridDim.x / nqb) / G;   // (b, KV head) groups
+    int bh, i;
+    if (nbk % 8 == 0) {
+        const int id = blockIdx.x, x = id % 8, rest = id / 8;   // XCD, then (group block, head, query block)
+        i = rest % nqb;
+        const int hh = (rest / nqb) % G, a = rest / nqb / G;
+        const int grp = 8 * a + x;                              // b * Hkv + KV head
+        bh = (grp / Hkv) * Hq + (grp % Hkv) * G + hh;
+    } else {
+        i = blockIdx.x % nqb;
+        bh = blockIdx.x / nqb;
+    }
+    const int b = bh / Hq, h = bh % Hq;                 // bh = b * Hq + h
+    const int hk = h / G;
     const float* qrow = qbar + ((int64_t)bh * nqb + i) * d;
     const float* kb = kbar + ((int64_t)b * Hkv + hk) * nkb * d;
     for (int c = tid; c < d; c += NT) q[c] = qrow[c];
