@@ -358,10 +358,20 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(Dense x, int H, int N, int
         scales[((int64_t)bh * N + t) * nblk + g] = (uint8_t)s;
     }
     if (means) {
-        // one thread per channel sums the block's tokens in fp64 (exact for bf16 inputs)
+        // one thread per channel sums the block's tokens in fp64, in token
+        // order; sixteen tokens are loaded ahead of their additions
         for (int c = threadIdx.x; c < d; c += 256) {
+            const uint16_t* col = base + (int64_t)tb * 128 * x.sN + c;
             double s = 0.0;
-            for (int t = 0; t < rows; ++t) s += (double)load_half<IS_F16>(base + (int64_t)(tb * 128 + t) * x.sN + c);
+            int t = 0;
+            for (; t + 16 <= rows; t += 16) {
+                uint16_t e[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) e[u] = col[(int64_t)(t + u) * x.sN];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) s += (double)load_half<IS_F16>(&e[u]);
+            }
+            for (; t < rows; ++t) s += (double)load_half<IS_F16>(col + (int64_t)t * x.sN);
             means[((int64_t)bh * nt + tb) * d + c] = (float)(s / (double)rows);
         }
     }
