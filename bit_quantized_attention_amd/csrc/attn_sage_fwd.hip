@@ -770,6 +770,9 @@ __global__ __launch_bounds__(256, 2) void sage_fwd_f8_kernel(SageFwdArgs a) {
                 }
                 if (a.qs_out && l == 0 && w == w0) a.qs_out[(int64_t)bh * (a.Nq / a.q_blk) + qrow / a.q_blk] = scale;
             }
+            // stores count in vmcnt too: finish them so that the loop's copy
+            // counts hold
+            if (a.qc_out || a.qs_out) __builtin_amdgcn_s_waitcnt(0x0070);
         }
 
         v16i s0 = v16i{}, s1 = v16i{};   // scores of the tile about to be processed
