@@ -13,6 +13,9 @@
 //
 // All kernels are coalesced on the [.., N, d] input rows; each thread moves
 // 16 bytes per load.
+#include <atomic>
+#include <chrono>
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.hpp"
@@ -312,6 +315,285 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(KvJob j, int nk) {
     }
 }
 
+// ------------------------------------------------------------ K and V resident
+// One launch for the same work when every workgroup of the grid can be
+// resident at once (d = 128, N a multiple of 256): a workgroup loads 256
+// tokens of one head, K and V (64 KB each), into registers, publishes its
+// partials (K token sums in fp64, V channel maxima), waits until the other
+// workgroups of its head have published theirs, and encodes from registers,
+// so K and V cross HBM once instead of twice.  The outputs are bit for bit
+// those of the two launches above: the fp64 sums are exact and maxima are
+// order-free, so neither depends on how the tokens are grouped.
+//
+// Workgroups of a head meet through flags in the workspace: each publishes
+// its partials, then writes the call's tag (a 64-bit value the host draws
+// fresh for every call) into its own flag, and waits until every flag of its
+// head holds the tag.  Whatever an earlier call or another operation left in
+// the workspace differs from a fresh tag, so nothing needs clearing.  The
+// host launches this kernel only when the whole grid fits on the device at
+// once and the stream is not being captured (a captured tag would repeat on
+// every replay); should a wait still run past its limit (other work holding
+// compute units), the workgroup takes the statistics of its head from HBM
+// itself, which gives the same values.
+constexpr int RES_T = 256;
+
+template <bool IS_F16, int FMT>
+__global__ __launch_bounds__(256, 2) void kv_resident_kernel(KvJob j, uint64_t* __restrict__ flags,
+                                                             int flag_stride, uint64_t tag, uint32_t spin_limit) {
+    constexpr int D = 128;
+    const int nch = j.N / RES_T;
+    const int bh = blockIdx.x / nch, ch = blockIdx.x % nch;
+    const int b = bh / j.H, h = bh % j.H;
+    const int tid = threadIdx.x, r = tid >> 4, c0 = (tid & 15) * 8;
+    const int t0 = ch * RES_T;
+    const uint16_t* kbase = (const uint16_t*)j.k.p + b * j.k.sB + h * j.k.sH + c0;
+    const uint16_t* vbase = (const uint16_t*)j.v.p + b * j.v.sB + h * j.v.sH + c0;
+    // K: token block kb (64 tokens, the scale blocks), group g: token 64 kb + 16 g + r
+    // V: 128-token tile vt, quad i, token 4 (r + 16 i) + u of the tile
+    v4i kr[4][4], vr[2][2][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) kr[kb][g] = *(const v4i*)(kbase + (int64_t)(t0 + 64 * kb + 16 * g + r) * j.k.sN);
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                vr[vt][i][u] = *(const v4i*)(vbase + (int64_t)(t0 + 128 * vt + 4 * (r + 16 * i) + u) * j.v.sN);
+
+    __shared__ double red_k[16][D];
+    __shared__ float red_v[16][D];
+    __shared__ float mu_s[D], inv_s[D], wmax[4][4];
+    __shared__ uint32_t tile[2][D][33];
+    __shared__ int late;
+
+    // ---- partials of this workgroup's 256 tokens
+    {
+        double sk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        float mv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (j.smooth) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sk[e] += (double)load_half<IS_F16>((const uint16_t*)&kr[kb][g] + e);
+        }
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        mv[e] = __builtin_fmaxf(mv[e], __builtin_fabsf(load_half<IS_F16>((const uint16_t*)&vr[vt][i][u] + e)));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            red_k[r][c0 + e] = sk[e];
+            red_v[r][c0 + e] = mv[e];
+        }
+    }
+    // the conversions are made again when encoding: holding the 256 converted
+    // values across the wait would spill, the 128 packed ones fit
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) asm volatile("" : "+v"(kr[kb][g]));
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) asm volatile("" : "+v"(vr[vt][i][u]));
+    __syncthreads();
+    if (tid < D) {
+        double s = red_k[0][tid];
+        float m = red_v[0][tid];
+        for (int rr = 1; rr < 16; ++rr) {
+            s += red_k[rr][tid];
+            m = __builtin_fmaxf(m, red_v[rr][tid]);
+        }
+        // device-scope stores go through to where every XCD reads them; the
+        // wait completes them before the flag is written.  (Partials and
+        // flags use device-scope accesses only, so no cache-wide write-back
+        // or invalidation is needed.)
+        if (j.smooth)
+            __hip_atomic_store((uint64_t*)j.kpart + ((int64_t)bh * nch + ch) * D + tid, __builtin_bit_cast(uint64_t, s),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store((uint32_t*)j.vpart + ((int64_t)bh * nch + ch) * D + tid, __builtin_bit_cast(uint32_t, m),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    uint64_t* hflags = flags + (int64_t)bh * flag_stride;   // this head's flags, one per workgroup
+    if (tid == 0) __hip_atomic_store(hflags + ch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < 64) {
+        // wavefront 0 watches the head's flags (device-scope loads, so never
+        // a stale cached copy)
+        uint32_t n = 0;
+        int timed_out = 0;
+        for (;;) {
+            bool mine = true;
+            for (int c = tid; c < nch; c += 64)
+                mine = mine && __hip_atomic_load(hflags + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+            if (__all(mine)) break;
+            if (++n >= spin_limit) {
+                timed_out = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(32);
+        }
+        if (tid == 0) late = timed_out;
+    }
+    __syncthreads();
+    const bool own = late != 0;
+
+    // ---- the head's statistics: K mean and V channel scales
+    if (own) {
+        // the head's tokens read again from HBM by this workgroup alone
+        double sk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        float mv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int t = r; t < j.N; t += 16) {
+            const v4i kx = *(const v4i*)(kbase + (int64_t)t * j.k.sN);
+            const v4i vx = *(const v4i*)(vbase + (int64_t)t * j.v.sN);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (j.smooth) sk[e] += (double)load_half<IS_F16>((const uint16_t*)&kx + e);
+                mv[e] = __builtin_fmaxf(mv[e], __builtin_fabsf(load_half<IS_F16>((const uint16_t*)&vx + e)));
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            red_k[r][c0 + e] = sk[e];
+            red_v[r][c0 + e] = mv[e];
+        }
+        __syncthreads();
+    }
+    if (tid < D) {
+        double s = 0.0;
+        float amax = 0.0f;
+        if (own) {
+            s = red_k[0][tid];
+            amax = red_v[0][tid];
+            for (int rr = 1; rr < 16; ++rr) {
+                s += red_k[rr][tid];
+                amax = __builtin_fmaxf(amax, red_v[rr][tid]);
+            }
+        } else {
+            // device-scope loads: never a stale line of an earlier call
+            const uint64_t* pk = (const uint64_t*)j.kpart + (int64_t)bh * nch * D + tid;
+            const uint32_t* pv = (const uint32_t*)j.vpart + (int64_t)bh * nch * D + tid;
+            for (int c = 0; c < nch; c += 8) {
+                uint64_t tk[8];
+                uint32_t tv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const bool in = c + u < nch;
+                    tk[u] = j.smooth && in ? __hip_atomic_load((uint64_t*)pk + (int64_t)(c + u) * D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+                    tv[u] = in ? __hip_atomic_load((uint32_t*)pv + (int64_t)(c + u) * D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    s += __builtin_bit_cast(double, tk[u]);
+                    amax = __builtin_fmaxf(amax, __builtin_bit_cast(float, tv[u]));
+                }
+            }
+        }
+        if (j.smooth) {
+            const float m = (float)(s / (double)j.N - j.eps);
+            mu_s[tid] = m;
+            if (ch == 0 && j.mu) j.mu[(int64_t)bh * D + tid] = m;
+        }
+        const float top = FMT == 0 ? 127.0f : 448.0f;
+        float inv = amax > 0.0f ? top / amax : 0.0f;
+        float scale = amax / top;
+        if (!(amax > 0.0f) || __builtin_isinf(inv)) { inv = 0.0f; scale = 0.0f; }
+        inv_s[tid] = inv;
+        if (ch == 0) j.vs[(int64_t)bh * D + tid] = scale;
+    }
+    __syncthreads();
+
+    // ---- K: INT8 per 64-token block, as tokblock_body
+    float mu[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mu[e] = j.smooth ? mu_s[c0 + e] : 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        float am = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float f = load_half<IS_F16>((const uint16_t*)&kr[kb][g] + e);
+                if (j.smooth) f = f - mu[e];
+                am = __builtin_fmaxf(am, __builtin_fabsf(f));
+            }
+        am = wave_max(am);
+        if ((tid & 63) == 0) wmax[kb][tid >> 6] = am;
+    }
+    __syncthreads();
+    const int nb = j.N / 64;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const float am = __builtin_fmaxf(__builtin_fmaxf(wmax[kb][0], wmax[kb][1]), __builtin_fmaxf(wmax[kb][2], wmax[kb][3]));
+        float inv = am > 0.0f ? 127.0f / am : 0.0f;
+        float scale = am / 127.0f;
+        if (!(am > 0.0f) || __builtin_isinf(inv)) { inv = 0.0f; scale = 0.0f; }
+        const int ib = t0 / 64 + kb;
+        if (tid == 0) j.ks[(int64_t)bh * nb + ib] = scale;
+        int8_t* out = j.kc + ((int64_t)bh * j.N + (int64_t)ib * 64) * D;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                f[e] = load_half<IS_F16>((const uint16_t*)&kr[kb][g] + e);
+                if (j.smooth) f[e] = f[e] - mu[e];
+            }
+            // |f| <= am, so |f * inv| <= 127
+            const uint32_t w0 = (uint32_t)q8x4(f[0], f[1], f[2], f[3], inv);
+            const uint32_t w1 = (uint32_t)q8x4(f[4], f[5], f[6], f[7], inv);
+            *(uint2*)(out + (int64_t)(16 * g + r) * D + c0) = make_uint2(w0, w1);
+        }
+    }
+
+    // ---- V: per-channel codes, channel-major, as chan_encode_body (128-token tiles)
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int tq = r + 16 * i;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float iv = inv_s[c0 + e];
+                float f[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) f[u] = load_half<IS_F16>((const uint16_t*)&vr[vt][i][u] + e) * iv;
+                uint32_t word;
+                if constexpr (FMT == 0) {
+                    word = (uint32_t)q8x4(f[0], f[1], f[2], f[3], 1.0f);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) f[u] = __builtin_amdgcn_fmed3f(f[u], -448.0f, 448.0f);
+                    word = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+                    word = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], (int)word, true);
+                }
+                tile[vt][c0 + e][tq] = word;
+            }
+        }
+    __syncthreads();
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt)
+        for (int qq = tid; qq < D * 8; qq += 256) {
+            const int c = qq >> 3, p16 = qq & 7;
+            *(uint4*)(j.vc + ((int64_t)bh * D + c) * j.N + t0 + 128 * vt + p16 * 16) =
+                make_uint4(tile[vt][c][4 * p16], tile[vt][c][4 * p16 + 1], tile[vt][c][4 * p16 + 2], tile[vt][c][4 * p16 + 3]);
+        }
+}
+
 // ------------------------------------------------------------ MXFP4
 // Encode 32 values (already loaded) as one MX block; returns the E8M0 byte.
 __device__ __forceinline__ uint32_t mx_encode32(const float* v, uint32_t* packed /* 4 words */) {
@@ -474,8 +756,68 @@ hipError_t launch_quant_chan(const Dense& x, bool f16, int B, int H, int N, int 
     return hipGetLastError();
 }
 
-size_t ws_kv_bytes(int BH, int N, int d) {
+// Workspace of the joint call: K token sums (fp64) then V channel maxima, per
+// (head, chunk); the resident kernel puts its per-head counters in front.
+static size_t ws_kv_two_pass(int BH, int N, int d) {
     return (ws_kmean_bytes(BH, N, d) + 255) / 256 * 256 + ws_chan_bytes(BH, N, d);
+}
+// flags: one 64-bit word per workgroup, each head's on 256-byte lines of its own
+static int kv_flag_stride(int N) { return (N / RES_T * 8 + 255) / 256 * 32; }
+static size_t ws_kv_counters(int BH, int N) { return (size_t)BH * kv_flag_stride(N) * sizeof(uint64_t); }
+static size_t ws_kv_resident(int BH, int N, int d) {
+    const size_t nch = (size_t)(N / RES_T);
+    return ws_kv_counters(BH, N) + ((size_t)BH * nch * d * sizeof(double) + 255) / 256 * 256 + (size_t)BH * nch * d * sizeof(float);
+}
+static bool resident_shape(int N, int d) { return d == 128 && N % RES_T == 0; }
+
+size_t ws_kv_bytes(int BH, int N, int d) {
+    const size_t a = ws_kv_two_pass(BH, N, d);
+    if (!resident_shape(N, d)) return a;
+    const size_t b = ws_kv_resident(BH, N, d);
+    return a > b ? a : b;
+}
+
+// Tags of the resident kernel's flags: a process-wide 64-bit sequence from a
+// start drawn from the clock and an address (distinct across processes and
+// runs); zero is skipped.
+static uint64_t next_kv_tag() {
+    static std::atomic<uint64_t> seq{[] {
+        uint64_t x = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+        x ^= (uint64_t)(uintptr_t)&seq << 17;
+        x ^= x >> 31; x *= 0x9E3779B97F4A7C15ull; x ^= x >> 29;   // mix
+        return x;
+    }()};
+    uint64_t t;
+    do t = seq.fetch_add(1, std::memory_order_relaxed); while (t == 0);
+    return t;
+}
+
+// Polls of a workgroup waiting for the others of its head before it takes the
+// head's statistics itself: a few tenths of a second by default.  Tests
+// set BQA_KV_WAIT_LIMIT (read at each call) to a tiny value to run that path.
+static uint32_t resident_spin_limit() {
+    const char* e = std::getenv("BQA_KV_WAIT_LIMIT");
+    const long n = e ? std::strtol(e, nullptr, 10) : 0;
+    return n > 0 && n < (1L << 30) ? (uint32_t)n : (uint32_t)(1u << 17);
+}
+
+// Workgroups of kv_resident_kernel<F16, FMT> the current device holds at
+// once (occupancy x compute units), cached per device and instance.
+template <bool F16, int FMT>
+static int resident_capacity() {
+    static std::atomic<int> cache[64];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = cache[dev].load(std::memory_order_acquire);
+    if (v == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kv_resident_kernel<F16, FMT>, 256, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            per_cu = cus = 0;
+        v = per_cu * cus > 0 ? per_cu * cus : -1;
+        cache[dev].store(v, std::memory_order_release);
+    }
+    return v;
 }
 
 hipError_t launch_quant_kv(const Dense& k, const Dense& v, bool f16, int B, int H, int N, int d, bool smooth,
@@ -484,12 +826,37 @@ hipError_t launch_quant_kv(const Dense& k, const Dense& v, bool f16, int B, int 
     KvJob j;
     j.k = k; j.v = v; j.H = H; j.N = N; j.d = d;
     const int BH = B * H;
+    j.smooth = smooth; j.eps = eps;
+    j.mu = mu; j.kc = kc; j.ks = ks; j.vc = vc; j.vs = vs;
+    hipStreamCaptureStatus cap_st = hipStreamCaptureStatusNone;
+    const bool capturing = hipStreamIsCapturing(st, &cap_st) == hipSuccess && cap_st != hipStreamCaptureStatusNone;
+    if (resident_shape(N, d) && !capturing) {
+        const int grid = BH * (N / RES_T);
+        const int cap = f16 ? (vfmt == 0 ? resident_capacity<true, 0>() : resident_capacity<true, 1>())
+                            : (vfmt == 0 ? resident_capacity<false, 0>() : resident_capacity<false, 1>());
+        if (grid <= cap) {
+            j.nch = N / RES_T;
+            j.rpc = RES_T;
+            j.kpart = (double*)((char*)ws + ws_kv_counters(BH, N));
+            j.vpart = (float*)((char*)j.kpart + ((size_t)BH * j.nch * d * sizeof(double) + 255) / 256 * 256);
+            uint64_t* flags = (uint64_t*)ws;
+            const int fs = kv_flag_stride(N);
+            const uint64_t tag = next_kv_tag();
+            const uint32_t lim = resident_spin_limit();
+            if (f16) {
+                if (vfmt == 0) kv_resident_kernel<true, 0><<<grid, 256, 0, st>>>(j, flags, fs, tag, lim);
+                else kv_resident_kernel<true, 1><<<grid, 256, 0, st>>>(j, flags, fs, tag, lim);
+            } else {
+                if (vfmt == 0) kv_resident_kernel<false, 0><<<grid, 256, 0, st>>>(j, flags, fs, tag, lim);
+                else kv_resident_kernel<false, 1><<<grid, 256, 0, st>>>(j, flags, fs, tag, lim);
+            }
+            return hipGetLastError();
+        }
+    }
     j.nch = chunks_for(BH, N);
     j.rpc = (N + j.nch - 1) / j.nch;
-    j.smooth = smooth; j.eps = eps;
     j.kpart = (double*)ws;
     j.vpart = (float*)((char*)ws + (ws_kmean_bytes(BH, N, d) + 255) / 256 * 256);
-    j.mu = mu; j.kc = kc; j.ks = ks; j.vc = vc; j.vs = vs;
     const int nkp = smooth ? BH * j.nch : 0;
     if (f16) kv_partial_kernel<true><<<nkp + BH * j.nch, 256, 0, st>>>(j, nkp);
     else kv_partial_kernel<false><<<nkp + BH * j.nch, 256, 0, st>>>(j, nkp);

@@ -48,7 +48,7 @@ class SagePath:
             self.vs = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev)
             fmt = BQA_FP8E4M3 if p.mode == BQA_SAGE_I8_F8PV else BQA_INT8
             self.vq = qtensor(fmt, 1, Nk, self.vc, self.vs)
-        # K and V go through one call (two launches) in the fp8 / int8 P.V modes
+        # K and V go through one call in the fp8 / int8 P.V modes
         self.kv_joint = p.mode in (BQA_SAGE_I8_F8PV, BQA_SAGE_I8_I8PV)
         ws = max(bqa_workspace_size(p, BQA_OP_QUANTIZE_K), bqa_workspace_size(p, BQA_OP_QUANTIZE_V),
                  bqa_workspace_size(p, BQA_OP_QUANTIZE_KV), 16)

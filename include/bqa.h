@@ -177,12 +177,18 @@ bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_ten
  * K and V of the Sage fp8 / int8 P.V modes in one call: the same codes,
  * scales and k_mean as bqa_quantize_blocks for role K (INT8 token blocks of
  * 64 tokens, K-smoothing per p->smooth_k and p->smooth_eps) and role V
- * (per-channel e4m3 for BQA_SAGE_I8_F8PV, int8 for BQA_SAGE_I8_I8PV), in two
- * kernel launches instead of four: the K token sums and the V channel maxima
- * first, then both encodings.  k and v are [B, Hkv, Nk, d] of one dtype (bf16
- * or fp16); kq is INT8 axis 0 with block 64, vq the per-channel layout with
- * block Nk; Nk a multiple of 64.  Workspace: bqa_workspace_size(p,
- * BQA_OP_QUANTIZE_KV) bytes, 16-byte aligned.
+ * (per-channel e4m3 for BQA_SAGE_I8_F8PV, int8 for BQA_SAGE_I8_I8PV).  With
+ * d = 128, Nk a multiple of 256, a grid of B Hkv Nk / 256 workgroups that the
+ * device holds at once and a stream that is not being captured, this is one
+ * kernel launch that reads K and V once (the workgroups of a head exchange
+ * their partial sums and maxima through the workspace); otherwise two
+ * launches (the K token sums and the V channel maxima, then both encodings).
+ * Either way the bytes equal those of the per-operand calls.  k and v are
+ * [B, Hkv, Nk, d] of one dtype (bf16 or fp16); kq is INT8 axis 0 with block
+ * 64, vq the per-channel layout with block Nk; Nk a multiple of 64.
+ * Workspace: bqa_workspace_size(p, BQA_OP_QUANTIZE_KV) bytes, 16-byte
+ * aligned, contents on entry arbitrary; two calls that run at the same time
+ * must not share it.
  */
 bqa_status bqa_quantize_kv(const bqa_problem* p, const bqa_tensor* k, const bqa_tensor* v, bqa_qtensor* kq,
                            bqa_qtensor* vq, float* k_mean, void* workspace, size_t workspace_bytes, void* stream);

@@ -213,40 +213,107 @@ def test_q_quantised_in_kernel_matches_separate(N, d, causal, q_block):
     assert torch.equal(fused.o, sep.o) and torch.equal(fused.lse, sep.lse)
 
 
-@pytest.mark.parametrize("N,d,pv,smooth,dt", [(512, 128, "f8", True, "bf16"), (320, 128, "i8", True, "bf16"),
-                                             (384, 64, "f8", False, "bf16"), (448, 128, "f8", True, "fp16")])
-def test_kv_joint_matches_separate(N, d, pv, smooth, dt):
-    """bqa_quantize_kv (two launches) gives the K codes, scales, mean and the
-    V codes and scales of the per-operand calls bit for bit (bf16 and fp16
-    inputs, 64- and 128-token V tiles)."""
+# (N % 256 == 0 at d = 128 runs the one-launch resident kernel, the others the two launches)
+KV_JOINT_CASES = [(512, 128, "f8", True, "bf16"), (320, 128, "i8", True, "bf16"), (384, 64, "f8", False, "bf16"),
+                  (448, 128, "f8", True, "fp16"), (1024, 128, "i8", True, "fp16"), (768, 128, "f8", False, "bf16"),
+                  (256, 128, "f8", True, "bf16")]
+
+
+def _kv_joint_vs_separate(N, d, pv, smooth, dt, b=2, h=2):
     import bit_quantized_attention_amd as bqa
     from bit_quantized_attention_amd.runner import SagePath, sage_problem, to_device
     import dataclasses
-    w = dataclasses.replace(wl.with_len(wl.WORKLOADS["c2"], N, b=2, hq=2, hkv=2), d=d)
+    w = dataclasses.replace(wl.with_len(wl.WORKLOADS["c2"], N, b=b, hq=h, hkv=h), d=d)
     Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
     mode = bqa.BQA_SAGE_I8_F8PV if pv == "f8" else bqa.BQA_SAGE_I8_I8PV
-    p = sage_problem(2, 2, 2, N, N, d, True, mode, q_block=64, smooth_k=smooth, smooth_eps=1e-3)
+    p = sage_problem(b, h, h, N, N, d, True, mode, q_block=64, smooth_k=smooth, smooth_eps=1e-3)
     paths = [SagePath(p, to_device(Q, "bf16"), to_device(K, dt), to_device(V, dt)) for _ in range(2)]
     paths[1].kv_joint = False
     for pa in paths:
         pa.mu.fill_(7.0)
+        pa.ws.fill_(0xA5)          # the joint call must not rely on workspace contents
         pa.quantize()
     torch.cuda.synchronize()
-    a, b = paths
+    a, b_ = paths
     assert paths[0].kv_joint
-    for name in ("kc", "ks", "vc", "vs") + (("mu",) if smooth else ()):
-        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    names = ("kc", "ks", "vc", "vs") + (("mu",) if smooth else ())
+    for name in names:
+        assert torch.equal(getattr(a, name), getattr(b_, name)), name
+    # a second call on the same workspace with other inputs: nothing of the
+    # first call (flags, partials) may leak into it
+    for pa in paths:
+        pa.k.mul_(-2.0).add_(0.5)
+        pa.v.mul_(0.25)
+        pa.quantize()
+    torch.cuda.synchronize()
+    for name in names:
+        assert torch.equal(getattr(a, name), getattr(b_, name)), name + " (second call)"
 
 
-def test_token_major_layouts():
-    """Q, K, V stored token-major ([B, N, H, d] memory viewed as [B, H, N, d]):
-    the in-kernel Q quantisation, the joint K/V call and the attention follow
-    the strides and give the bits of contiguous inputs."""
+@pytest.mark.parametrize("N,d,pv,smooth,dt", KV_JOINT_CASES)
+def test_kv_joint_matches_separate(N, d, pv, smooth, dt):
+    """bqa_quantize_kv gives the K codes, scales, mean and the V codes and
+    scales of the per-operand calls bit for bit (bf16 and fp16 inputs, 64- and
+    128-token V tiles, both the resident one-launch kernel and the two-launch
+    path)."""
+    _kv_joint_vs_separate(N, d, pv, smooth, dt)
+
+
+@pytest.mark.parametrize("limit", ["1", "3"])
+def test_kv_resident_own_statistics(limit, monkeypatch):
+    """With the resident kernel's wait cut to a few polls, workgroups that do
+    not see the rest of their head in time take the head's statistics from HBM
+    themselves: the bits are the same.  16 heads x 4 chunks of 256 tokens."""
+    monkeypatch.setenv("BQA_KV_WAIT_LIMIT", limit)
+    _kv_joint_vs_separate(1024, 128, "f8", True, "bf16", b=2, h=8)
+
+
+def test_kv_joint_in_captured_graph():
+    """bqa_quantize_kv captured in a graph (where the call takes the two-launch
+    path) and replayed on new inputs matches the eager call on each of them,
+    with eager work and synchronisations between the replays."""
     import bit_quantized_attention_amd as bqa
     from bit_quantized_attention_amd.runner import SagePath, sage_problem, to_device
-    w = wl.with_len(wl.WORKLOADS["c2"], 384, b=2, hq=4, hkv=2)
+    w = wl.with_len(wl.WORKLOADS["c2"], 1024, b=2, hq=4, hkv=4)
     Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
-    p = sage_problem(2, 4, 2, 384, 384, 128, True, bqa.BQA_SAGE_I8_F8PV, q_block=128, smooth_k=True, smooth_eps=0.0)
+    p = sage_problem(2, 4, 4, 1024, 1024, 128, True, bqa.BQA_SAGE_I8_F8PV, q_block=128, smooth_k=True, smooth_eps=0.0)
+    g_path = SagePath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
+    e_path = SagePath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g_path.quantize()                      # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g_path.quantize()
+    torch.cuda.synchronize()
+    names = ("kc", "ks", "vc", "vs", "mu")
+    for rep in range(3):
+        scale = 1.0 + 0.5 * rep
+        for pa in (g_path, e_path):
+            pa.k.copy_(to_device(K * scale - rep, "bf16"))
+            pa.v.copy_(to_device(V / scale, "bf16"))
+        e_path.quantize()                      # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name in names:
+            assert torch.equal(getattr(g_path, name), getattr(e_path, name)), f"{name} (replay {rep})"
+
+
+@pytest.mark.parametrize("N", [384, 512])
+def test_token_major_layouts(N):
+    """Q, K, V stored token-major ([B, N, H, d] memory viewed as [B, H, N, d]):
+    the in-kernel Q quantisation, the joint K/V call (two-launch and resident
+    kernels) and the attention follow the strides and give the bits of
+    contiguous inputs."""
+    import bit_quantized_attention_amd as bqa
+    from bit_quantized_attention_amd.runner import SagePath, sage_problem, to_device
+    w = wl.with_len(wl.WORKLOADS["c2"], N, b=2, hq=4, hkv=2)
+    Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
+    p = sage_problem(2, 4, 2, N, N, 128, True, bqa.BQA_SAGE_I8_F8PV, q_block=128, smooth_k=True, smooth_eps=0.0)
 
     def token_major(x):
         t = to_device(np.ascontiguousarray(x.transpose(0, 2, 1, 3)), "bf16")   # memory [B, N, H, d]
