@@ -11,8 +11,10 @@
 // INT8 per 128-token block.
 //
 // Kernels:
-//   delta_rows_kernel     delta per query row (fp32)
-//   transpose_i8_kernel   channel-major copies of the Q, K and dO codes (the
+//   do_prep_kernel        delta per query row (fp32) and the channel-major
+//                         INT8 codes of dO with their scales, one pass over
+//                         dO and O
+//   transpose2_i8_kernel  channel-major copies of the Q and K codes (the
 //                         second operand of the INT8 products reads tokens
 //                         contiguously per channel)
 //   sbwd_dkdv_kernel      one workgroup per 64-key block, over the query
@@ -49,48 +51,114 @@ __device__ __forceinline__ v4i pack16(const float* x, float inv) {
 }
 
 // ------------------------------------------------------------------ preprocess
-__global__ __launch_bounds__(256) void delta_rows_kernel(Dense dO, Dense O, int H, int N, int64_t rows,
-                                                         float* __restrict__ delta) {
-    // delta_i = sum_c dO[i, c] O[i, c]; one row per 16 lanes, 8 channels each
-    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
-    const int part = threadIdx.x & 15;
-    float acc = 0.0f;
-    if (row < rows) {
-        const int64_t bh = row / N, i = row % N, b = bh / H, h = bh % H;
-        const uint16_t* g = (const uint16_t*)dO.p + b * dO.sB + h * dO.sH + i * dO.sN + 8 * part;
-        const uint16_t* o = (const uint16_t*)O.p + b * O.sB + h * O.sH + i * O.sN + 8 * part;
-        const v4i gv = *(const v4i*)g, ov = *(const v4i*)o;
+// dO in one pass per 128-row block: delta_i = sum_c dO[i, c] O[i, c] (one row
+// per 16 lanes, 8 channels each, fma in channel order, then a butterfly over
+// the 16 lanes), and the block's INT8 codes with one absmax scale per 128
+// tokens (the token-block quantiser's arithmetic), written channel-major only
+// ([BH][d][N], the layout the products read) through an LDS transpose.
+__global__ __launch_bounds__(256) void do_prep_kernel(Dense dO, Dense O, int H, int N, float* __restrict__ delta,
+                                                      float* __restrict__ dos, int8_t* __restrict__ doT) {
+    const int nb = N / 128;
+    const int bh = blockIdx.x / nb, ib = blockIdx.x % nb;
+    const int b = bh / H, h = bh % H;
+    // thread: rows 4 q + u + 64 i (u < 4, i < 2), channels 8 part .. 8 part + 7
+    const int tid = threadIdx.x, part = tid & 15, q = tid >> 4;
+    const uint16_t* gb = (const uint16_t*)dO.p + b * dO.sB + h * dO.sH + (int64_t)ib * 128 * dO.sN + 8 * part;
+    const uint16_t* ob = (const uint16_t*)O.p + b * O.sB + h * O.sH + (int64_t)ib * 128 * O.sN + 8 * part;
+    v4i gv[2][4], ov[2][4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            acc = __builtin_fmaf(bf16_bits_to_f32((uint16_t)gv[k]), bf16_bits_to_f32((uint16_t)ov[k]), acc);
-            acc = __builtin_fmaf(bf16_bits_to_f32((uint16_t)((uint32_t)gv[k] >> 16)),
-                                 bf16_bits_to_f32((uint16_t)((uint32_t)ov[k] >> 16)), acc);
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            gv[i][u] = *(const v4i*)(gb + (int64_t)(4 * q + u + 64 * i) * dO.sN);
+            ov[i][u] = *(const v4i*)(ob + (int64_t)(4 * q + u + 64 * i) * O.sN);
         }
-    }
+    __shared__ uint32_t tT[D][33];     // codes, channel-major: words of 4 rows (stride 33: two lanes per bank at most)
+    __shared__ float wmax[4];
+    float am = 0.0f;
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 16);
-    if (row < rows && part == 0) delta[row] = acc;
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t g2 = (uint32_t)gv[i][u][w], o2 = (uint32_t)ov[i][u][w];
+                const float g0 = bf16_bits_to_f32((uint16_t)g2), g1 = bf16_bits_to_f32((uint16_t)(g2 >> 16));
+                acc = __builtin_fmaf(g0, bf16_bits_to_f32((uint16_t)o2), acc);
+                acc = __builtin_fmaf(g1, bf16_bits_to_f32((uint16_t)(o2 >> 16)), acc);
+                am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(g0), __builtin_fabsf(g1)));
+            }
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 16);
+            if (part == 0) delta[(int64_t)bh * N + ib * 128 + 4 * q + u + 64 * i] = acc;
+        }
+    am = wave_max(am);
+    if ((tid & 63) == 0) wmax[tid >> 6] = am;
+    __syncthreads();
+    const float bm = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+    float inv = bm > 0.0f ? 127.0f / bm : 0.0f;
+    float scale = bm / 127.0f;
+    if (!(bm > 0.0f) || __builtin_isinf(inv)) { inv = 0.0f; scale = 0.0f; }
+    if (tid == 0) dos[(int64_t)bh * nb + ib] = scale;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float f[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t w2 = (uint32_t)gv[i][u][e >> 1];
+                f[u] = bf16_bits_to_f32((uint16_t)((e & 1) ? (w2 >> 16) : w2));
+            }
+            // one channel, four consecutive rows; |f| <= bm, so |f * inv| <= 127
+            tT[8 * part + e][q + 16 * i] = (uint32_t)q8x4(f[0], f[1], f[2], f[3], inv);
+        }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int it = tid + 256 * k, c = it >> 3, sg = it & 7;
+        const v4i y = {(int)tT[c][4 * sg], (int)tT[c][4 * sg + 1], (int)tT[c][4 * sg + 2], (int)tT[c][4 * sg + 3]};
+        *(v4i*)(doT + ((int64_t)bh * D + c) * N + ib * 128 + 16 * sg) = y;
+    }
 }
 
-// [BH][N][d] int8 -> [BH][d][N], 64 x 64 tiles through LDS.
-__global__ __launch_bounds__(256) void transpose_i8_kernel(const int8_t* __restrict__ in, int N, int d,
-                                                           int8_t* __restrict__ out) {
-    __shared__ uint8_t t[64][65];
-    const int tilesN = N / 64, tilesD = d / 64;
+// Channel-major copies of two [BH][N][d] int8 tensors (the Q and K codes) in
+// one launch, 64 tokens x d per workgroup: a thread reads 8 channels of 4
+// consecutive tokens, packs each channel's 4 bytes into one word (byte
+// permutes), and the words cross LDS (row stride 17 words: no more than two
+// lanes per bank) to 16-byte stores along the tokens.
+__global__ __launch_bounds__(256) void transpose2_i8_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b,
+                                                            int8_t* __restrict__ aT, int8_t* __restrict__ bT, int N,
+                                                            int tiles) {
+    __shared__ uint32_t t[D][17];
     int blk = blockIdx.x;
-    const int td = blk % tilesD; blk /= tilesD;
+    const bool second = blk >= tiles;
+    if (second) blk -= tiles;
+    const int8_t* in = second ? b : a;
+    int8_t* out = second ? bT : aT;
+    const int tilesN = N / 64;
     const int tn = blk % tilesN;
     const int64_t bh = blk / tilesN;
-    const int8_t* src = in + (bh * N + (int64_t)tn * 64) * d + td * 64;
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int r = e >> 6, c = e & 63;
-        t[r][c] = (uint8_t)src[(int64_t)r * d + c];
+    const int tid = threadIdx.x, part = tid & 15, q = tid >> 4;       // tokens 4 q + u, channels 8 part ..
+    const int8_t* src = in + (bh * N + (int64_t)tn * 64 + 4 * q) * D + 8 * part;
+    v2i x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = *(const v2i*)(src + (int64_t)u * D);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int w = e >> 2;
+        const uint32_t sel = 0x0c0c0400u | (uint32_t)(e & 3) * 0x0101u;     // byte e&3 of the low source, then of the high
+        const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)x[1][w], (uint32_t)x[0][w], sel);
+        const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)x[3][w], (uint32_t)x[2][w], sel);
+        t[8 * part + e][q] = p01 | (p23 << 16);
     }
     __syncthreads();
-    int8_t* dst = out + (bh * d + (int64_t)td * 64) * N + (int64_t)tn * 64;
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int r = e >> 6, c = e & 63;
-        dst[(int64_t)r * N + c] = (int8_t)t[c][r];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int it = tid + 256 * k, c = it >> 2, sg = it & 3;
+        const v4i y = {(int)t[c][4 * sg], (int)t[c][4 * sg + 1], (int)t[c][4 * sg + 2], (int)t[c][4 * sg + 3]};
+        *(v4i*)(out + (bh * D + c) * N + (int64_t)tn * 64 + 16 * sg) = y;
     }
 }
 
@@ -510,7 +578,6 @@ __global__ __launch_bounds__(256, 2) void sbwd_dq_kernel(SageBwdArgs a) {
 size_t ws_sage_bwd_bytes(int B, int H, int N, int d) {
     const size_t bhn = (size_t)B * H * N;
     return bhn * 4                 // delta
-           + bhn * d               // dO codes
            + (bhn / 128) * 4       // dO scales
            + 3 * bhn * d           // channel-major dO, Q, K codes
            + 256;
@@ -520,22 +587,16 @@ hipError_t launch_sage_bwd(SageBwdArgs a, Dense o, void* ws, hipStream_t st) {
     const int64_t bhn = (int64_t)a.B * a.H * a.N;
     uint8_t* p = (uint8_t*)ws;
     float* delta = (float*)p;                 p += bhn * 4;
-    int8_t* doc = (int8_t*)p;                 p += bhn * D;
     float* dos = (float*)p;                   p += (bhn / 128) * 4;
+    p = (uint8_t*)(((uintptr_t)p + 15) & ~(uintptr_t)15);
     int8_t* doT = (int8_t*)p;                 p += bhn * D;
     int8_t* qT = (int8_t*)p;                  p += bhn * D;
     int8_t* kT = (int8_t*)p;
     a.delta = delta; a.dos = dos; a.doT = doT; a.qT = qT; a.kT = kT;
 
-    const int64_t rows = bhn;
-    delta_rows_kernel<<<(unsigned)((rows * 16 + 255) / 256), 256, 0, st>>>(a.d_o, o, a.H, a.N, rows, delta);
-    hipError_t e = launch_quant_i8_tokblock(a.d_o, false, a.B, a.H, a.N, D, 128, false, 0.0, nullptr, nullptr, doc,
-                                            dos, st);
-    if (e != hipSuccess) return e;
-    const unsigned tgrid = (unsigned)((int64_t)a.B * a.H * (a.N / 64) * (D / 64));
-    transpose_i8_kernel<<<tgrid, 256, 0, st>>>(doc, a.N, D, doT);
-    transpose_i8_kernel<<<tgrid, 256, 0, st>>>(a.qc, a.N, D, qT);
-    transpose_i8_kernel<<<tgrid, 256, 0, st>>>(a.kc, a.N, D, kT);
+    do_prep_kernel<<<(unsigned)(bhn / 128), 256, 0, st>>>(a.d_o, o, a.H, a.N, delta, dos, doT);
+    const int tiles = (int)((int64_t)a.B * a.H * (a.N / 64));
+    transpose2_i8_kernel<<<2 * tiles, 256, 0, st>>>(a.qc, a.kc, qT, kT, a.N, tiles);
     sbwd_dkdv_kernel<<<a.B * a.H * (a.N / TK), 512, 0, st>>>(a);
     sbwd_dq_kernel<<<a.B * a.H * (a.N / TQ), 256, 0, st>>>(a);
     return hipGetLastError();
