@@ -259,6 +259,12 @@ def test_kv_joint_matches_separate(N, d, pv, smooth, dt):
     _kv_joint_vs_separate(N, d, pv, smooth, dt)
 
 
+def test_kv_resident_long_head():
+    """One head of 65536 tokens: 256 workgroups meet on one head's flags
+    (four per polling lane)."""
+    _kv_joint_vs_separate(65536, 128, "f8", True, "bf16", b=1, h=1)
+
+
 @pytest.mark.parametrize("limit", ["1", "3"])
 def test_kv_resident_own_statistics(limit, monkeypatch):
     """With the resident kernel's wait cut to a few polls, workgroups that do
