@@ -158,18 +158,6 @@ __device__ __forceinline__ uint32_t enc_e4m3(float x) {
     return sign | ((uint32_t)(e + 7) << 3) | mi;
 }
 
-// OCP e2m1: values 0, 0.5, 1, 1.5, 2, 3, 4, 6; nearest-even, saturating.
-__device__ __forceinline__ uint32_t enc_e2m1(float x) {
-    uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 28) & 0x8u;
-    float a = __builtin_fabsf(x);
-    if (!(a < 6.0f)) return sign | 0x7u;
-    if (a < 1.0f) return sign | (uint32_t)__builtin_rintf(a * 2.0f);   // 0, 0.5, or 1.0 (code 2)
-    int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFF) - 127;   // 0, 1 or 2
-    uint32_t m = (uint32_t)__builtin_rintf((__builtin_ldexpf(a, -e) - 1.0f) * 2.0f);
-    if (m == 2u) { m = 0u; e += 1; }
-    return sign | ((uint32_t)(e + 1) << 1) | m;
-}
-
 // e2m1 code (low 4 bits: sign, 2 exponent bits, 1 mantissa bit) to its value.
 __device__ __forceinline__ float dec_e2m1(uint32_t nib) {
     const uint32_t m = nib & 7u;

@@ -596,17 +596,24 @@ __global__ __launch_bounds__(256, 2) void kv_resident_kernel(KvJob j, uint64_t* 
 
 // ------------------------------------------------------------ MXFP4
 // Encode 32 values (already loaded) as one MX block; returns the E8M0 byte.
+// The conversion is the hardware's scaled e2m1 conversion (the scale's
+// exponent only, nearest-even, saturating at 6): the same bits as scaling by
+// 2^-e and rounding to the OCP e2m1 grid (tested bit for bit against the
+// oracle, ties, saturation and subnormal blocks included).
 __device__ __forceinline__ uint32_t mx_encode32(const float* v, uint32_t* packed /* 4 words */) {
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < 32; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[k]));
     const int e = mx_exponent(amax);
+    const float sc = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) word |= enc_e2m1(__builtin_ldexpf(v[w * 8 + k], -e)) << (4 * k);
-        packed[w] = word;
+        uint32_t x = 0;
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[w * 8 + 0], v[w * 8 + 1], sc, 0);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[w * 8 + 2], v[w * 8 + 3], sc, 1);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[w * 8 + 4], v[w * 8 + 5], sc, 2);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[w * 8 + 6], v[w * 8 + 7], sc, 3);
+        packed[w] = x;
     }
     return (uint32_t)(e + 127);
 }
