@@ -142,22 +142,6 @@ __device__ __forceinline__ int q8x4(float a, float b, float c, float d, float in
     return (int)(__builtin_amdgcn_perm(wb, wa, 0x0c0c0400u) | __builtin_amdgcn_perm(wd, wc, 0x04000c0cu));
 }
 
-// OCP e4m3 ("fn"): exponent bias 7, 3 mantissa bits, largest finite 448;
-// nearest-even, saturating (anything at or above 448 encodes as 448).
-__device__ __forceinline__ uint32_t enc_e4m3(float x) {
-    uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
-    float a = __builtin_fabsf(x);
-    if (!(a < 448.0f)) return sign | 0x7Eu;                 // saturate (+inf too)
-    if (a < 0.015625f) {                                   // below 2^-6: steps of 2^-9
-        return sign | (uint32_t)__builtin_rintf(a * 512.0f);   // 8 rounds up to the first normal
-    }
-    int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFF) - 127;
-    float m = __builtin_rintf((__builtin_ldexpf(a, -e) - 1.0f) * 8.0f);
-    uint32_t mi = (uint32_t)m;
-    if (mi == 8u) { mi = 0u; e += 1; }
-    return sign | ((uint32_t)(e + 7) << 3) | mi;
-}
-
 // e2m1 code (low 4 bits: sign, 2 exponent bits, 1 mantissa bit) to its value.
 __device__ __forceinline__ float dec_e2m1(uint32_t nib) {
     const uint32_t m = nib & 7u;
