@@ -291,14 +291,17 @@ __global__ __launch_bounds__(256) void vdeq_kernel(const uint8_t* __restrict__ c
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= nblocks) return;
     const v4i raw = *(const v4i*)(codes + 16 * i);
-    const int e = (int)scales[i] - 127;
+    // the hardware's scaled e2m1 -> bf16 conversion, two values per byte (low
+    // nibble first); an e2m1 value times 2^e is exact in bf16
+    const float sc = __builtin_bit_cast(float, (uint32_t)scales[i] << 23);
     uint32_t w[16];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-        const uint32_t nib = ((uint32_t)raw[k / 8] >> (4 * (k % 8))) & 0xF;
-        // e2m1 value times 2^e is exact in fp32 and in bf16
-        const uint32_t bits = f32_to_bf16_bits(__builtin_ldexpf(dec_e2m1(nib), e));
-        if (k & 1) w[k / 2] |= bits << 16; else w[k / 2] = bits;
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t x = (uint32_t)raw[q];
+        w[4 * q + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, sc, 0));
+        w[4 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, sc, 1));
+        w[4 * q + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, sc, 2));
+        w[4 * q + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, sc, 3));
     }
     v4i* o = (v4i*)(out + 32 * i);
 #pragma unroll
