@@ -16,9 +16,9 @@
 //
 // Kernels:
 //   qat_delta_kernel   delta' per query row
-//   deq_t_kernel       bf16 copies in the layouts the products read:
-//                      deq(V) token-major, deq(Q)^T, deq(K)^T and dO^T
-//                      channel-major
+//   deq_t_fp4_kernel   bf16 copies in the layouts the products read:
+//   deq_t_bf16_kernel  deq(V) token-major, deq(Q)^T, deq(K)^T (from the
+//                      MXFP4 codes) and dO^T (fp16) channel-major
 //   qbwd_dkdv_kernel   one workgroup per 64-key block over the 128-query
 //                      tiles: the tile is computed with queries in lanes
 //                      (P's MX blocks lie along a lane's registers), P^ and
@@ -67,44 +67,76 @@ __global__ __launch_bounds__(256) void qat_delta_kernel(Dense dO, Dense Oa, int 
     if (row < rows && part == 0) delta[row] = acc;
 }
 
-// Element (r, c) of a [BH][R][C] grid, as bf16 bits, and the transpose
-// writer: out[bh][c][r].  SRC 0: MXFP4 codes along C (rows of C/2 bytes,
-// E8M0 per 32 of C), written as bf16 (exact); SRC 1: dense bf16
-// [B][H][R][C] view, written as fp16 (exact for the normal fp16 range).
-template <int SRC>
-__global__ __launch_bounds__(256) void deq_t_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sc,
-                                                    Dense dense, int H, int R, int C, uint16_t* __restrict__ out) {
-    __shared__ uint16_t t[64][66];
+// MXFP4 codes along C of a [BH][R][C] grid (rows of C/2 bytes, E8M0 per 32
+// of C) to bf16, transposed: out[bh][c][r].  64 x 64 tiles; a thread reads 8
+// code bytes (16 values of one row) and converts them with the hardware's
+// scaled e2m1 -> bf16 conversion (exact: an e2m1 value times 2^e), the tile
+// crosses LDS and leaves in 16-byte stores along r.
+__global__ __launch_bounds__(256) void deq_t_fp4_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sc,
+                                                        int R, int C, uint16_t* __restrict__ out) {
+    __shared__ uint32_t t[64][33];     // [r][pair of c], stride 33 words
     const int tilesR = R / 64, tilesC = C / 64;
     int blk = blockIdx.x;
     const int tc = blk % tilesC; blk /= tilesC;
     const int tr = blk % tilesR;
     const int64_t bh = blk / tilesR;
-    for (int e = threadIdx.x; e < 64 * 32; e += 256) {      // two elements per step
-        const int r = e >> 5, c2 = e & 31;
-        const int64_t rr = (int64_t)tr * 64 + r, cc = (int64_t)tc * 64 + 2 * c2;
-        uint16_t v0, v1;
-        if constexpr (SRC == 0) {
-            const uint8_t byte = codes[(bh * R + rr) * (C / 2) + cc / 2];
-            const int ex = (int)sc[(bh * R + rr) * (C / 32) + cc / 32] - 127;
-            v0 = f32_to_bf16_bits(__builtin_ldexpf(dec_e2m1(byte & 0xF), ex));
-            v1 = f32_to_bf16_bits(__builtin_ldexpf(dec_e2m1(byte >> 4), ex));
-        } else {
-            const int64_t b = bh / H, h = bh % H;
-            const uint32_t pr = *(const uint32_t*)((const uint16_t*)dense.p + b * dense.sB + h * dense.sH +
-                                                   rr * dense.sN + cc);
-            v0 = f32_to_f16_bits(bf16_bits_to_f32((uint16_t)pr));
-            v1 = f32_to_f16_bits(bf16_bits_to_f32((uint16_t)(pr >> 16)));
-        }
-        t[r][2 * c2] = v0;
-        t[r][2 * c2 + 1] = v1;
+    const int tid = threadIdx.x, r = tid >> 2, q = tid & 3;         // row r, columns 16 q .. 16 q + 15
+    const int64_t row = bh * R + (int64_t)tr * 64 + r;
+    const v2i x = *(const v2i*)(codes + row * (C / 2) + tc * 32 + 8 * q);
+    const float s = __builtin_bit_cast(float, (uint32_t)sc[row * (C / 32) + 2 * tc + (q >> 1)] << 23);
+    const uint32_t x0 = (uint32_t)x[0], x1 = (uint32_t)x[1];
+    t[r][8 * q + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, s, 0));
+    t[r][8 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, s, 1));
+    t[r][8 * q + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, s, 2));
+    t[r][8 * q + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, s, 3));
+    t[r][8 * q + 4] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, s, 0));
+    t[r][8 * q + 5] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, s, 1));
+    t[r][8 * q + 6] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, s, 2));
+    t[r][8 * q + 7] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, s, 3));
+    __syncthreads();
+    // output row c (64 of the tile), r = 16 g .. 16 g + 15
+    const int c = tid >> 2, g = tid & 3;
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t a = t[16 * g + 2 * k][c >> 1], b = t[16 * g + 2 * k + 1][c >> 1];
+        w[k] = (c & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+    }
+    uint16_t* dst = out + (bh * C + (int64_t)tc * 64 + c) * R + (int64_t)tr * 64 + 16 * g;
+    *(v4i*)dst = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    *(v4i*)(dst + 8) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+}
+
+// Dense bf16 [B][H][R][C] view to fp16 (exact for the normal fp16 range),
+// transposed: out[bh][c][r]; the tiling of deq_t_fp4_kernel, a thread
+// reading 16 values (32 bytes) of one row.
+__global__ __launch_bounds__(256) void deq_t_bf16_kernel(Dense x, int H, int R, int C, uint16_t* __restrict__ out) {
+    __shared__ uint32_t t[64][33];
+    const int tilesR = R / 64, tilesC = C / 64;
+    int blk = blockIdx.x;
+    const int tc = blk % tilesC; blk /= tilesC;
+    const int tr = blk % tilesR;
+    const int64_t bh = blk / tilesR, b = bh / H, h = bh % H;
+    const int tid = threadIdx.x, r = tid >> 2, q = tid & 3;
+    const uint16_t* src = (const uint16_t*)x.p + b * x.sB + h * x.sH + ((int64_t)tr * 64 + r) * x.sN + tc * 64 + 16 * q;
+    const v4i a0 = *(const v4i*)src, a1 = *(const v4i*)(src + 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t pr = (uint32_t)(j < 4 ? a0[j] : a1[j - 4]);
+        t[r][8 * q + j] = (uint32_t)f32_to_f16_bits(bf16_bits_to_f32((uint16_t)pr)) |
+                          ((uint32_t)f32_to_f16_bits(bf16_bits_to_f32((uint16_t)(pr >> 16))) << 16);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < 64 * 32; e += 256) {
-        const int c = e >> 5, r2 = e & 31;
-        const uint32_t pr = (uint32_t)t[2 * r2][c] | ((uint32_t)t[2 * r2 + 1][c] << 16);
-        *(uint32_t*)(out + (bh * C + (int64_t)tc * 64 + c) * R + (int64_t)tr * 64 + 2 * r2) = pr;
+    const int c = tid >> 2, g = tid & 3;
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t lo = t[16 * g + 2 * k][c >> 1], hi = t[16 * g + 2 * k + 1][c >> 1];
+        w[k] = (c & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
     }
+    uint16_t* dst = out + (bh * C + (int64_t)tc * 64 + c) * R + (int64_t)tr * 64 + 16 * g;
+    *(v4i*)dst = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    *(v4i*)(dst + 8) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
 }
 
 // ------------------------------------------------------------------ the tile (queries in lanes)
@@ -473,10 +505,10 @@ hipError_t launch_qat_bwd(QatBwdArgs a, Dense o_aux, void* ws, hipStream_t st) {
     qat_delta_kernel<<<(unsigned)((bhn * 16 + 255) / 256), 256, 0, st>>>(a.d_o, o_aux, a.H, a.N, bhn, delta);
     const unsigned tg = (unsigned)((int64_t)a.B * a.H * (a.N / 64) * (D / 64));
     // V codes are channel-major [d][N/2]: transposing the (channel, token) grid gives token-major rows
-    deq_t_kernel<0><<<tg, 256, 0, st>>>(a.vc, a.vs, Dense{}, a.H, D, a.N, vdeq);
-    deq_t_kernel<0><<<tg, 256, 0, st>>>(a.qc, a.qs, Dense{}, a.H, a.N, D, qT);
-    deq_t_kernel<0><<<tg, 256, 0, st>>>(a.kc, a.ks, Dense{}, a.H, a.N, D, kT);
-    deq_t_kernel<1><<<tg, 256, 0, st>>>(nullptr, nullptr, a.d_o, a.H, a.N, D, doT);
+    deq_t_fp4_kernel<<<tg, 256, 0, st>>>(a.vc, a.vs, D, a.N, vdeq);
+    deq_t_fp4_kernel<<<tg, 256, 0, st>>>(a.qc, a.qs, a.N, D, qT);
+    deq_t_fp4_kernel<<<tg, 256, 0, st>>>(a.kc, a.ks, a.N, D, kT);
+    deq_t_bf16_kernel<<<tg, 256, 0, st>>>(a.d_o, a.H, a.N, D, doT);
     qbwd_dkdv_kernel<<<a.B * a.H * (a.N / TK), 512, 0, st>>>(a);
     qbwd_dq_kernel<<<a.B * a.H * (a.N / TQ), 256, 0, st>>>(a);
     return hipGetLastError();

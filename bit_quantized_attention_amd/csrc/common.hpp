@@ -142,13 +142,6 @@ __device__ __forceinline__ int q8x4(float a, float b, float c, float d, float in
     return (int)(__builtin_amdgcn_perm(wb, wa, 0x0c0c0400u) | __builtin_amdgcn_perm(wd, wc, 0x04000c0cu));
 }
 
-// e2m1 code (low 4 bits: sign, 2 exponent bits, 1 mantissa bit) to its value.
-__device__ __forceinline__ float dec_e2m1(uint32_t nib) {
-    const uint32_t m = nib & 7u;
-    const float mag = m < 2u ? 0.5f * (float)m : __builtin_ldexpf(1.0f + 0.5f * (float)(m & 1u), (int)(m >> 1) - 1);
-    return (nib & 8u) ? -mag : mag;
-}
-
 // OCP MX shared exponent of a block with absolute maximum amax:
 // floor(log2 amax) - 2, clamped to [-127, 127]; -127 for 0 and subnormals.
 __device__ __forceinline__ int mx_exponent(float amax) {
