@@ -675,21 +675,23 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(Dense x, int H, int N, int
     const int bh = blockIdx.x / nt, tb = blockIdx.x % nt;
     const int b = bh / H, h = bh % H;
     const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH;
-    __shared__ float tile[128][129];
+    // the raw 16-bit values (34 KB of LDS, so four workgroups fit a CU),
+    // widened when read; row stride 130 halves keeps column reads spread
+    // over the banks
+    __shared__ uint16_t tile[128][130];
     const int gpr = d / 8;
     for (int g = threadIdx.x; g < 128 * gpr; g += 256) {
         const int t = g / gpr, c = (g % gpr) * 8;
-        uint4 raw = *(const uint4*)(base + (int64_t)(tb * 128 + t) * x.sN + c);
-        const uint16_t* e = (const uint16_t*)&raw;
+        const v4i raw = *(const v4i*)(base + (int64_t)(tb * 128 + t) * x.sN + c);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) tile[t][c + j] = load_half<IS_F16>(e + j);
+        for (int j = 0; j < 4; ++j) *(uint32_t*)&tile[t][c + 2 * j] = (uint32_t)raw[j];
     }
     __syncthreads();
     for (int it = threadIdx.x; it < d * 4; it += 256) {
         const int c = it / 4, grp = it % 4;
         float v[32];
 #pragma unroll
-        for (int k = 0; k < 32; ++k) v[k] = tile[grp * 32 + k][c];
+        for (int k = 0; k < 32; ++k) v[k] = load_half<IS_F16>(&tile[grp * 32 + k][c]);
         uint32_t packed[4];
         uint32_t s = mx_encode32(v, packed);
         const int64_t tok = (int64_t)tb * 128 + grp * 32;
