@@ -78,8 +78,8 @@ def _declare(L):
         "orc_sage_bwd": (None, [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, d, i, i, i, i,
                                 i, i, i, i, vp, vp, vp]),
         "orc_mx_scores": (i, [vp, vp, vp, vp, i, i, i, vp]),
-        "orc_qat_fwd": (None, [vp, vp, vp, vp, vp, vp, i, i, i, d, i, i, i, i, vp, vp, vp]),
-        "orc_qat_bwd": (None, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, d, i,
+        "orc_qat_fwd": (None, [vp, vp, vp, vp, vp, vp, i, i, i, d, i, i, i, i, vp, vp, vp, vp]),
+        "orc_qat_bwd": (None, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, d, i,
                                i, i, i, i, vp, vp, vp]),
         "orc_budget_count": (i, [i, i]),
         "orc_select_blocks": (None, [vp, vp, i, i, i, i, i, i, vp, vp]),
@@ -263,22 +263,27 @@ def mx_score(qc, qs, kc, ks, d, i, j):
     return s.value, bool(ok)
 
 
-def qat_fwd(*, qc, qs, kc, ks, vc_t, vs_t, Nq, Nk, d, tau, kv_tile=128, quantize_p=True, rows=None):
+def qat_fwd(*, qc, qs, kc, ks, vc_t, vs_t, Nq, Nk, d, tau, kv_tile=128, quantize_p=True, rows=None,
+            return_rowmax=False):
+    """O, O', lse (and with return_rowmax the rows' final running maxima tau*s)."""
     r0, r1 = (0, Nq) if rows is None else rows
-    O = np.empty((r1 - r0, d)); Oa = np.empty((r1 - r0, d)); lse = np.empty(r1 - r0)
+    O = np.empty((r1 - r0, d)); Oa = np.empty((r1 - r0, d)); lse = np.empty(r1 - r0); mrow = np.empty(r1 - r0)
     a = [_c(x, np.uint8) for x in (qc, qs, kc, ks, vc_t, vs_t)]
     lib().orc_qat_fwd(*[_p(x) for x in a], Nq, Nk, d, float(tau), kv_tile, int(quantize_p), r0, r1,
-                      _p(O), _p(Oa), _p(lse))
-    return O, Oa, lse
+                      _p(O), _p(Oa), _p(lse), _p(mrow))
+    return (O, Oa, lse, mrow) if return_rowmax else (O, Oa, lse)
 
 
 def qat_bwd(*, qc, qs, kc, ks, vc_t, vs_t, dO, O_aux, lse, Nq, Nk, d, tau, quantize_p=True,
-            qrows=None, krows=None):
+            qrows=None, krows=None, rowmax=None):
+    """rowmax: the rows' final running maxima from the forward (fp64, all Nq
+    rows); None takes them here from the scores of every key."""
     q0, q1 = (0, Nq) if qrows is None else qrows
     k0, k1 = (0, Nk) if krows is None else krows
     dQ = np.empty((q1 - q0, d)); dK = np.empty((k1 - k0, d)); dV = np.empty((k1 - k0, d))
     a = [_c(x, np.uint8) for x in (qc, qs, kc, ks, vc_t, vs_t)] + [_f32(dO), _f32(O_aux), _f32(lse)]
-    lib().orc_qat_bwd(*[_p(x) for x in a], Nq, Nk, d, float(tau), int(quantize_p), q0, q1, k0, k1,
+    mr = None if rowmax is None else _c(rowmax, np.float64)
+    lib().orc_qat_bwd(*[_p(x) for x in a], _p(mr), Nq, Nk, d, float(tau), int(quantize_p), q0, q1, k0, k1,
                       _p(dQ), _p(dK), _p(dV))
     return dQ, dK, dV
 

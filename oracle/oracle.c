@@ -392,20 +392,13 @@ typedef struct {
     double* acc2;    /* d values: second output (Attn-QAT O'), may be NULL */
 } row_state;
 
-/* The reference point of the online softmax.  Any value at or above the row
- * maximum gives the same attention in exact arithmetic; the one used here is
- * the running maximum rounded up to a whole power of two of the probability
- * scale, m = ln2 * ceil(max / ln2), so that every rescaling factor
- * exp(m_old - m_new) is an exact power of two and the largest P of a row lies
- * in (1/2, 1]. */
-static double ref_max(double running_max) {
-    if (running_max == -INFINITY) return running_max;
-    const double ln2 = 0.69314718055994530942;
-    return ln2 * ceil(running_max / ln2);
-}
-
-/* Move the row to a new reference maximum: scale the sums by exp(m_old - m_new). */
-static void row_rescale(row_state* st, double m_new, int d) {
+/* FlashAttention-2's merge step ([TA] step 2): the running maximum becomes
+ * m_new = max(m, tile max), and the sums gathered so far are scaled by
+ * exp(m - m_new) so that every later P = exp(s - m_new) joins them in the
+ * same frame.  The largest P of the row so far is therefore exactly 1. */
+static void row_update_max(row_state* st, double tile_max, int d) {
+    double m_new = st->m > tile_max ? st->m : tile_max;
+    if (m_new == st->m) return;
     double alpha = (st->m == -INFINITY) ? 0.0 : exp(st->m - m_new);
     st->l *= alpha;
     for (int c = 0; c < d; ++c) st->acc[c] *= alpha;
@@ -433,9 +426,9 @@ static double sage_score(int qk_mode, const int8_t* qc, const float* qs, int q_b
 
 /* Rows [r0, r1) of one head.  Keys are visited in tiles of kv_tile in
  * ascending order (causal: up to the row's diagonal).  Per tile:
- * m_new = max(m, ref(tile max)) with ref() rounding up to a power of two
- * (see ref_max), P = exp(s - m_new), l accumulates the
- * unquantised P, and P is rounded for the P.V product by pv_mode:
+ * m_new = max(m, tile max) (FlashAttention-2's running maximum),
+ * P = exp(s - m_new), l accumulates the unquantised P, and P is rounded for
+ * the P.V product by pv_mode:
  *   ORC_PV_F16: fp16(P) times V given in fp16;
  *   ORC_PV_F8 : e4m3(448 P)/448 times e4m3 V codes times the channel scale;
  *   ORC_PV_I8 : int8 per (row, tile) with r = the row's tile max of P,
@@ -463,7 +456,7 @@ void orc_sage_fwd(int qk_mode, const int8_t* qc, const float* qs, int q_blk,
                 s[u] = sage_score(qk_mode, qc, qs, q_blk, kc, ks, k_blk, Qf, Kf, d, i, t0 + u, tau);
                 if (s[u] > tmax) tmax = s[u];
             }
-            row_rescale(&st, st.m > ref_max(tmax) ? st.m : ref_max(tmax), d);
+            row_update_max(&st, tmax, d);
             double r = 0.0;
             for (int u = 0; u < n; ++u) {
                 p[u] = exp(s[u] - st.m);
@@ -692,15 +685,17 @@ static double kmx(const uint8_t* kc, const uint8_t* ks, int d, int j, int c) {
 }
 
 /* Attn-QAT forward, rows [r0, r1) of one head, non-causal: s = tau * exact
- * MX dot product; key tiles of kv_tile ascending; P fake-quantised to MXFP4
- * per 32 keys of the row (no smoothing, no two-level step, [AQ] §2
- * Implementation) for O, and rounded to bf16 for O' ([AQ] §2 Principle 2),
- * both against the FP4 V; l sums the unquantised P.  quantize_p == 0 uses
- * P itself in both products. */
+ * MX dot product; key tiles of kv_tile ascending with FlashAttention-2's
+ * running maximum; P = exp(s - m) fake-quantised to MXFP4 per 32 keys of the
+ * row (no smoothing, no two-level step, [AQ] §2 Implementation) for O, and
+ * rounded to bf16 for O' ([AQ] §2 Principle 2), both against the FP4 V;
+ * l sums the unquantised P.  quantize_p == 0 uses P itself in both products.
+ * Outputs O, O', lse = m + ln l and, when rowmax != NULL, the row's final
+ * running maximum m (= the largest tau * s of the row). */
 void orc_qat_fwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                  const uint8_t* vc_t, const uint8_t* vs_t, int Nq, int Nk, int d,
                  double tau, int kv_tile, int quantize_p, int r0, int r1,
-                 double* O, double* O_aux, double* lse) {
+                 double* O, double* O_aux, double* lse, double* rowmax) {
     (void)Nq;
 #pragma omp parallel for schedule(dynamic)
     for (int i = r0; i < r1; ++i) {
@@ -716,7 +711,7 @@ void orc_qat_fwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const 
                 s[u] *= tau;
                 if (s[u] > tmax) tmax = s[u];
             }
-            row_rescale(&st, st.m > ref_max(tmax) ? st.m : ref_max(tmax), d);
+            row_update_max(&st, tmax, d);
             for (int u = 0; u < kv_tile; ++u) { p[u] = exp(s[u] - st.m); st.l += p[u]; pq[u] = p[u]; }
             if (quantize_p) for (int u = 0; u < kv_tile; u += 32) mx_fake32(pq + u, 32);
             for (int u = 0; u < kv_tile; ++u) {
@@ -733,25 +728,28 @@ void orc_qat_fwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const 
             O_aux[(size_t)(i - r0) * d + c] = st.acc2[c] / st.l;
         }
         lse[i - r0] = st.m + log(st.l);
+        if (rowmax) rowmax[i - r0] = st.m;
         free(st.acc); free(st.acc2); free(s); free(p); free(pq);
     }
 }
 
 /* Attn-QAT backward ([AQ] §2 Principles 1 and 2): P = exp(s - L) recomputed
- * from the same exact MX scores.  For dV = P^ dO the recomputation matches
- * the forward's precision: the forward rounded P relative to a reference
- * that is a power of two (MXFP4 codes do not change under such a factor), so
- * the backward rounds exp(s - m*), m* = ln2 ceil(L / ln2), per 32 keys and
- * scales the result by exp(m* - L) -- exactly the forward's P^ divided by its
- * row sum.  dP = dO V^T against the FP4 V;
- * dS = P o (dP - delta') with delta' = rowsum(dO o O') (the straight-through
- * estimator keeps the unquantised P in the softmax Jacobian); dS is rounded
- * to bf16 where the products take bf16 operands; dQ = tau dS K, dK = tau
- * dS^T Q with the FP4 Q, K.  Outputs: dQ rows [q0, q1), dK and dV rows
- * [k0, k1) of one head.  quantize_p == 0 skips the P and dS roundings. */
+ * from the same exact MX scores.  For dV = P^ dO, P is fake-quantised at the
+ * forward's precision: the forward made MXFP4 codes of exp(s - m) per 32
+ * keys, with m the running maximum, so the backward rounds exp(s - M) per 32
+ * keys, M = the row's final maximum (rowmax, from the forward; NULL: taken
+ * here over every key), and scales the result by exp(M - L) = 1/l.  The row's
+ * largest P is then exactly 1/l, as in the forward, and every tile that the
+ * forward visited once its maximum had reached M gets the forward's own
+ * codes.  dP = dO V^T against the FP4 V; dS = P o (dP - delta') with
+ * delta' = rowsum(dO o O') (the straight-through estimator keeps the
+ * unquantised P in the softmax Jacobian); dS is rounded to bf16 where the
+ * products take bf16 operands; dQ = tau dS K, dK = tau dS^T Q with the FP4
+ * Q, K.  Outputs: dQ rows [q0, q1), dK and dV rows [k0, k1) of one head.
+ * quantize_p == 0 skips the P and dS roundings. */
 void orc_qat_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                  const uint8_t* vc_t, const uint8_t* vs_t, const float* dO, const float* O_aux,
-                 const float* lse, int Nq, int Nk, int d, double tau, int quantize_p,
+                 const float* lse, const double* rowmax, int Nq, int Nk, int d, double tau, int quantize_p,
                  int q0, int q1, int k0, int k1, double* dQ, double* dK, double* dV) {
     double* delta = (double*)malloc(sizeof(double) * (size_t)Nq);
     for (int i = 0; i < Nq; ++i) {
@@ -767,7 +765,6 @@ void orc_qat_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const 
     int ra = need_all ? 0 : q0, rb = need_all ? Nq : q1;
 #pragma omp parallel
     {
-        const double ln2 = 0.69314718055994530942;
         double* p = (double*)malloc(sizeof(double) * (size_t)Nk);
         double* pq = (double*)malloc(sizeof(double) * (size_t)Nk);
         double* ds = (double*)malloc(sizeof(double) * (size_t)Nk);
@@ -777,15 +774,21 @@ void orc_qat_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const 
         for (int i = ra; i < rb; ++i) {
             int want_q = (i >= q0 && i < q1);
             int ja = want_q ? 0 : (k0 / 32) * 32, jb = want_q ? Nk : ((k1 + 31) / 32) * 32;
-            const double mstar = ln2 * ceil((double)lse[i] / ln2);
+            double mrow = rowmax ? rowmax[i] : -INFINITY;
+            if (!rowmax)
+                for (int j = 0; j < Nk; ++j) {
+                    double s;
+                    orc_mx_scores(qc, qs, kc, ks, d, i, j, &s);
+                    if (tau * s > mrow) mrow = tau * s;
+                }
             for (int j = ja; j < jb; ++j) {
                 double s;
                 orc_mx_scores(qc, qs, kc, ks, d, i, j, &s);
                 p[j] = exp(tau * s - (double)lse[i]);
-                pq[j] = quantize_p ? exp(tau * s - mstar) : p[j];
+                pq[j] = quantize_p ? exp(tau * s - mrow) : p[j];
             }
             if (quantize_p) {
-                const double back = exp(mstar - (double)lse[i]);
+                const double back = exp(mrow - (double)lse[i]);
                 for (int j = ja; j < jb; j += 32) mx_fake32(pq + j, 32);
                 for (int j = ja; j < jb; ++j) pq[j] *= back;
             }
@@ -902,7 +905,7 @@ static void thrift_block(const thrift_ctx* c, row_state* st, int i, int j0, int 
         }
         if (s[u] > tmax) tmax = s[u];
     }
-    row_rescale(st, st->m > ref_max(tmax) ? st->m : ref_max(tmax), d);
+    row_update_max(st, tmax, d);
     double r = 0.0;
     for (int u = 0; u < n; ++u) { p[u] = exp(s[u] - st->m); st->l += p[u]; if (p[u] > r) r = p[u]; }
     if (!c->quantize) {

@@ -71,10 +71,10 @@ int  orc_mx_scores(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, cons
 void orc_qat_fwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                  const uint8_t* vc_t, const uint8_t* vs_t, int Nq, int Nk, int d,
                  double tau, int kv_tile, int quantize_p, int r0, int r1,
-                 double* O, double* O_aux, double* lse);
+                 double* O, double* O_aux, double* lse, double* rowmax);
 void orc_qat_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                  const uint8_t* vc_t, const uint8_t* vs_t, const float* dO, const float* O_aux,
-                 const float* lse, int Nq, int Nk, int d, double tau, int quantize_p,
+                 const float* lse, const double* rowmax, int Nq, int Nk, int d, double tau, int quantize_p,
                  int q0, int q1, int k0, int k1, double* dQ, double* dK, double* dV);
 
 /* ---- ThriftAttention ---- */

@@ -147,17 +147,16 @@ def test_sage_int8_scores_are_exact(orc):
 
 
 def _single_tile_ref(orc, s, Vd, rounding):
-    # reference point: the row max rounded up to a whole power of two of P
-    m = np.log(2.0) * np.ceil(s.max(axis=1, keepdims=True) / np.log(2.0))
+    m = s.max(axis=1, keepdims=True)
     p = np.exp(s - m)
     l = p.sum(axis=1, keepdims=True)
     return rounding(p) @ Vd / l
 
 
 def test_sage_pv_rounding_single_tile(orc):
-    """With one key tile the reference point is the row max rounded up to a
-    power of two, so each P.V mode is a library rounding of exp(s - m): fp16,
-    e4m3 at 448 P, int8 per tile at 127 P / max P."""
+    """With one key tile the running max is the row max, so each P.V mode is a
+    library rounding of exp(s - max): fp16, e4m3 at 448 P, int8 per tile at
+    127 P / max P (max P = 1)."""
     rng = np.random.default_rng(13)
     N, d = 32, 16
     Q, K, V, qc, qs, kc, ks = _sage_inputs(orc, rng, N, d, q_blk=32, k_blk=32)
@@ -177,8 +176,7 @@ def test_sage_pv_rounding_single_tile(orc):
     vc, vs = orc.quant_chan(V[None], "i8")
     deq = vc[0].T.view(np.int8).astype(np.float64) * vs[0][None]
     O, _ = orc.sage_fwd(pv_mode=orc.PV_I8, vc_t=vc[0], vs=vs[0], **kw)
-    ref = _single_tile_ref(orc, s, deq, lambda p: np.rint((p * (127.0 / p.max(axis=1, keepdims=True)).astype(np.float32)).astype(
-        np.float32)).astype(np.float64) * p.max(axis=1, keepdims=True) / 127)
+    ref = _single_tile_ref(orc, s, deq, lambda p: np.rint((p * np.float32(127.0)).astype(np.float32)).astype(np.float64) / 127)
     assert np.abs(O - ref).max() < 1e-12
 
 
@@ -315,32 +313,41 @@ def test_qat_quantised_close_and_aux_identity(orc):
 def test_qat_backward_reuses_forward_p(orc):
     """Attn-QAT §2 Principle 1: the backward's rounded P is the forward's.
     With dO one-hot on (row i, channel k), dV[:, k] is row i of the
-    backward's P^, and P^ V must give back the forward's O row exactly --
-    including peaked rows whose largest P sits at the MXFP4 exponent step."""
+    backward's P^.  For a row whose maximum sits in the first key tile, the
+    forward's running maximum never moves, every tile's P^ is made against the
+    final maximum, and P^ V gives back the forward's O row exactly --
+    including peaked rows whose largest P is 1 (on an MXFP4 exponent step)."""
     rng = np.random.default_rng(23)
-    N, d, tau = 128, 64, 1 / 8
+    N, d, tau, tile = 128, 64, 1 / 8, 32
     X = [rng.standard_t(3, (N, d)).astype(np.float32) for _ in range(3)]
-    X[0][5] = X[1][77] * 4.0                     # row 5: one key dominates (largest P ~ 1)
+    X[0][5] = X[1][3] * 4.0                      # row 5: key 3 (first tile) dominates
     qc, qs = orc.quant_mx_rows(X[0][None]); kc, ks = orc.quant_mx_rows(X[1][None]); vc, vs = orc.quant_mx_cols(X[2][None])
     t = dict(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0])
-    O, Oa, lse = orc.qat_fwd(Nq=N, Nk=N, d=d, tau=tau, kv_tile=32, **t)
+    O, Oa, lse, mrow = orc.qat_fwd(Nq=N, Nk=N, d=d, tau=tau, kv_tile=tile, return_rowmax=True, **t)
+    S = np.array([[orc.mx_score(qc[0], qs[0], kc[0], ks[0], d, i, j)[0] for j in range(N)] for i in range(N)])
+    assert np.array_equal(mrow, tau * S.max(axis=1))                 # the final running max is the row max
+    first = [i for i in range(N) if S[i].argmax() < tile]
+    assert 5 in first and len(first) >= 10
     Vd = _mx_deq_rows(vc[0], vs[0]).T                  # [N keys, d]
-    for i in (5, 40, 101):
+    for i in first[:8]:
         k = 3
         dO = np.zeros((N, d), np.float32)
         dO[i, k] = 1.0
-        _, _, dV = orc.qat_bwd(dO=dO, O_aux=Oa.astype(np.float32), lse=lse.astype(np.float32), Nq=N, Nk=N, d=d,
-                               tau=tau, **t)
+        kw = dict(dO=dO, O_aux=Oa.astype(np.float32), lse=lse.astype(np.float32), Nq=N, Nk=N, d=d, tau=tau, **t)
+        _, _, dV = orc.qat_bwd(rowmax=mrow, **kw)
+        _, _, dV2 = orc.qat_bwd(**kw)                  # row max taken inside: the same
+        assert np.array_equal(dV, dV2)
         prow = dV[:, k]
+        assert prow[S[i].argmax()] == pytest.approx(np.exp(mrow[i] - np.float32(lse[i])), rel=1e-15)
         # the forward normalises by its own row sum; the backward by exp(L): equal up to L's fp32 storage
         assert np.abs(prow @ Vd - O[i]).max() <= 1e-5 * np.abs(O[i]).max()
-    assert np.exp(tau * orc.mx_score(qc[0], qs[0], kc[0], ks[0], d, 5, 77)[0] - lse[5]) > 0.5
+    assert np.exp(tau * S[5, 3] - lse[5]) > 0.5
 
 
 def test_qat_one_hot_row_is_exact(orc):
-    """A row whose scores put all the mass on one key: P^ is one-hot, so O is
-    exactly proportional to that key's FP4 value row; the factor is
-    e2m1(P / 2^e) 2^e / P for the key's P in (1/2, 1], i.e. within [0.75, 1.2]."""
+    """A row whose scores put all the mass on one key: that key's P is exactly
+    1 (the running max), its MXFP4 code is exact and every other P rounds to
+    zero, so O and O' equal that key's FP4 value row."""
     d, N = 32, 64
     Q = np.zeros((N, d), np.float32); K = np.zeros((N, d), np.float32)
     Q[:, 0] = 6.0
@@ -352,9 +359,5 @@ def test_qat_one_hot_row_is_exact(orc):
     O, Oa, _ = orc.qat_fwd(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0],
                            Nq=N, Nk=N, d=d, tau=1.0, kv_tile=32)
     Vd = _mx_deq_rows(vc[0], vs[0]).T
-    v = Vd[7]
-    nz = np.abs(v) > 0
-    kappa = O[:, nz] / v[None, nz]
-    assert np.abs(kappa - kappa[:, :1]).max() < 1e-12          # one factor per row
-    assert np.all((kappa[:, 0] >= 0.75 - 1e-12) & (kappa[:, 0] <= 1.2 + 1e-12))
-    assert np.abs(O[:, ~nz]).max() < 1e-20            # other keys: P of order e^-60 (own MX block)
+    assert np.abs(O - Vd[7][None]).max() < 1e-12
+    assert np.abs(Oa - Vd[7][None]).max() < 1e-12

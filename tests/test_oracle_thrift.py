@@ -111,8 +111,9 @@ def test_thrift_fp4_close_and_order(orc):
 
 
 def test_thrift_fp4_one_hot_exact(orc):
-    """All the mass on one key: two-level P puts it at 6 (r/6 * 6 = r), every
-    other P rounds to zero, so the FP4 path returns that key's FP4 V row."""
+    """All the mass on one key: its P is exactly 1 (the running max), two-level
+    P puts it at exactly 6 (r/6 * 6 = 1), every other P rounds to zero, so the
+    FP4 path returns that key's FP4 V row."""
     d, N, blk = 32, 64, 32
     Q = np.zeros((N, d), np.float32); K = np.zeros((N, d), np.float32)
     Q[:, 0] = 6.0; K[:, 0] = -6.0; K[3, 0] = 6.0
@@ -125,8 +126,7 @@ def test_thrift_fp4_one_hot_exact(orc):
     tab = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6])
     c = vc[0][:, 1]                                       # tokens 2, 3 of every channel
     v3 = tab[c >> 4] * 2.0 ** (vs[0][:, 0].astype(np.int64) - 127)
-    # exact up to the fp32 rounding of the key's P (the two-level scale maps it to 6)
-    assert np.abs(O[3:] - v3[None]).max() < 1e-6 * np.abs(v3).max()
+    assert np.abs(O[3:] - v3[None]).max() < 1e-12
 
 
 @pytest.mark.parametrize("splits", [1, 3, 8, 16])
