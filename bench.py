@@ -213,7 +213,8 @@ def cpu_baseline_thrift(w, budget_s: float = 20.0):
     while qb > 0 and time.perf_counter() - t0 < budget_s:
         qb -= 1
         oracle.thrift_fwd(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0], Qh=Q, Kh=K, Vh=V,
-                          sel_idx=idx, sel_cnt=cnt, Nq=w.Nq, Nk=w.Nk, d=w.d, blk=128, causal=True, tau=tau_for(w.d),
+                          sel_idx=idx, sel_cnt=cnt, Nq=w.Nq, Nk=w.Nk, d=w.d, blk=128, hp_tile=64, causal=True,
+                          tau=tau_for(w.d),
                           qblocks=(qb, qb + 1))
         pairs += sum(128 * qb + a + 1 for a in range(128))
     dt = time.perf_counter() - t0
@@ -275,7 +276,8 @@ def cpu_baseline_decode(w, budget_s: float = 20.0):
             qc, qs = oracle.quant_mx_rows(q[None])
             idx, cnt = oracle.select_blocks(q, km, True, 50_000, ms)
             oracle.thrift_decode(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0], q=q[0], Kh=K, Vh=V,
-                                 sel=idx[0, :cnt[0]], Nk=w.Nk, d=w.d, blk=128, tau=tau_for(w.d), num_splits=1)
+                                 sel=idx[0, :cnt[0]], Nk=w.Nk, d=w.d, blk=128, hp_tile=32, tau=tau_for(w.d),
+                                 num_splits=1)
             heads += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -393,12 +395,12 @@ def cpu_baseline_qat_train(w, budget_s: float = 25.0):
     qc, qs = oracle.quant_mx_rows(Q[None]); kc, ks = oracle.quant_mx_rows(K[None]); vc, vs = oracle.quant_mx_cols(V[None])
     t = dict(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0])
     tau = tau_for(w.d)
-    _, Oa, lse = oracle.qat_fwd(Nq=w.Nq, Nk=w.Nk, d=w.d, tau=tau, kv_tile=64, **t)
+    _, Oa, lse, mrow = oracle.qat_fwd(Nq=w.Nq, Nk=w.Nk, d=w.d, tau=tau, kv_tile=64, return_rowmax=True, **t)
     ops = 6.0 * w.Nq * w.Nk * w.d                    # forward: QK^T, P.V and O'
     r0 = 0
     while r0 < w.Nq and time.perf_counter() - t0 < budget_s:
         oracle.qat_bwd(dO=dO, O_aux=oracle.round_to(Oa, "bf16").astype(np.float32), lse=lse.astype(np.float32),
-                       Nq=w.Nq, Nk=w.Nk, d=w.d, tau=tau, qrows=(r0, r0 + 32), krows=(r0, r0 + 32), **t)
+                       rowmax=mrow, Nq=w.Nq, Nk=w.Nk, d=w.d, tau=tau, qrows=(r0, r0 + 32), krows=(r0, r0 + 32), **t)
         ops += 2.0 * 32 * w.Nk * w.d * 3 + 2.0 * 32 * w.Nq * w.d * 4      # dQ rows; dK, dV key rows
         r0 += 32
     dt = time.perf_counter() - t0
@@ -438,8 +440,11 @@ def main():
     ap.add_argument("--steps", type=int, default=0,
                     help="timed steps; 0 (default): enough for about 0.1 s, at least 10")
     ap.add_argument("--warmup", type=int, default=0,
-                    help="untimed warmup steps; 0 (default): at least 20 and until 0.5 s have passed, which "
-                         "brings the GPU clocks up from idle")
+                    help="untimed warmup steps; the warmup runs at least this many steps and at least 0.5 s "
+                         "(and 20 steps), which brings the GPU clocks up from idle; the JSON line reports "
+                         "the number actually run")
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="minimum warmup time (profiler runs pass 0 to keep the number of dispatches small)")
     ap.add_argument("--workload", choices=sorted(CASES), default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -472,10 +477,12 @@ def main():
     path = case["path"]
     t_w = time.perf_counter()
     n_warm = 0
-    while n_warm < args.warmup or (args.warmup == 0 and (n_warm < 20 or time.perf_counter() - t_w < 0.5)):
+    warm_req = args.warmup
+    min_steps = 20 if args.warmup_seconds > 0 else 1
+    while n_warm < warm_req or n_warm < min_steps or time.perf_counter() - t_w < args.warmup_seconds:
         path.step()
         n_warm += 1
-        if args.warmup == 0 and n_warm % 10 == 0:
+        if n_warm % 10 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     args.warmup = n_warm
@@ -529,6 +536,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_rule": f"at least {warm_req} steps (requested), {min_steps} steps and {args.warmup_seconds} s",
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

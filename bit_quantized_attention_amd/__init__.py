@@ -84,11 +84,11 @@ def lib():
         L.bqa_select_blocks.argtypes = [P(bqa_problem), vp, vp, vp, vp, vp, C.c_size_t, vp]
         L.bqa_attn_fwd.restype = C.c_int32
         L.bqa_attn_fwd.argtypes = [P(bqa_problem), P(bqa_qtensor), P(bqa_qtensor), P(bqa_qtensor), P(bqa_tensor),
-                                   P(bqa_tensor), P(bqa_tensor), vp, vp, P(bqa_tensor), P(bqa_tensor), vp, vp,
+                                   P(bqa_tensor), P(bqa_tensor), vp, vp, P(bqa_tensor), P(bqa_tensor), vp, vp, vp,
                                    C.c_size_t, vp]
         L.bqa_attn_bwd.restype = C.c_int32
         L.bqa_attn_bwd.argtypes = [P(bqa_problem), P(bqa_qtensor), P(bqa_qtensor), P(bqa_qtensor), P(bqa_tensor),
-                                   P(bqa_tensor), vp, P(bqa_tensor), P(bqa_tensor), P(bqa_tensor), P(bqa_tensor),
+                                   P(bqa_tensor), vp, vp, P(bqa_tensor), P(bqa_tensor), P(bqa_tensor), P(bqa_tensor),
                                    vp, C.c_size_t, vp]
         L.bqa_debug_qk_scores.restype = C.c_int32
         L.bqa_debug_qk_scores.argtypes = [P(bqa_problem), P(bqa_qtensor), P(bqa_qtensor), C.c_int32, C.c_int32,
@@ -215,27 +215,29 @@ def bqa_select_blocks(p, q_means, k_means, sel_idx, sel_cnt, workspace=None, wor
 
 
 def bqa_attn_fwd(p, q=None, k=None, v=None, q_hi=None, k_hi=None, v_hi=None, sel_idx=None, sel_cnt=None, o=None,
-                 o_aux=None, lse=None, workspace=None, workspace_bytes=None, stream=None, check=True) -> int:
+                 o_aux=None, lse=None, row_max=None, workspace=None, workspace_bytes=None, stream=None,
+                 check=True) -> int:
     def dd(t):
         return t if (t is None or isinstance(t, bqa_tensor)) else dense(t)
     wb = workspace_bytes if workspace_bytes is not None else (workspace.numel() * workspace.element_size()
                                                               if workspace is not None else 0)
     s = lib().bqa_attn_fwd(C.byref(p), _ref(q), _ref(k), _ref(v), _ref(dd(q_hi)), _ref(dd(k_hi)), _ref(dd(v_hi)),
-                           _ptr(sel_idx), _ptr(sel_cnt), _ref(dd(o)), _ref(dd(o_aux)), _ptr(lse), _ptr(workspace),
+                           _ptr(sel_idx), _ptr(sel_cnt), _ref(dd(o)), _ref(dd(o_aux)), _ptr(lse), _ptr(row_max),
+                           _ptr(workspace),
                            wb, _stream(stream))
     if check:
         _check(s, "bqa_attn_fwd")
     return s
 
 
-def bqa_attn_bwd(p, q=None, k=None, v=None, v_hi=None, o_for_delta=None, lse=None, d_o=None, dq=None, dk=None,
-                 dv=None, workspace=None, workspace_bytes=None, stream=None, check=True) -> int:
+def bqa_attn_bwd(p, q=None, k=None, v=None, v_hi=None, o_for_delta=None, lse=None, row_max=None, d_o=None, dq=None,
+                 dk=None, dv=None, workspace=None, workspace_bytes=None, stream=None, check=True) -> int:
     def dd(t):
         return t if (t is None or isinstance(t, bqa_tensor)) else dense(t)
     wb = workspace_bytes if workspace_bytes is not None else (workspace.numel() * workspace.element_size()
                                                               if workspace is not None else 0)
     s = lib().bqa_attn_bwd(C.byref(p), _ref(q), _ref(k), _ref(v), _ref(dd(v_hi)), _ref(dd(o_for_delta)), _ptr(lse),
-                           _ref(dd(d_o)), _ref(dd(dq)), _ref(dd(dk)), _ref(dd(dv)), _ptr(workspace), wb,
+                           _ptr(row_max), _ref(dd(d_o)), _ref(dd(dq)), _ref(dd(dk)), _ref(dd(dv)), _ptr(workspace), wb,
                            _stream(stream))
     if check:
         _check(s, "bqa_attn_bwd")

@@ -233,7 +233,7 @@ bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const f
 bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k, const bqa_qtensor* v,
                         const bqa_tensor* q_hi, const bqa_tensor* k_hi, const bqa_tensor* v_hi,
                         const int32_t* sel_idx, const int32_t* sel_cnt, bqa_tensor* o, bqa_tensor* o_aux,
-                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+                        float* lse, float* row_max, void* ws, size_t ws_bytes, void* stream) {
     (void)q_hi; (void)k_hi; (void)sel_idx; (void)sel_cnt;
     TRY(check_problem(p));
     hipStream_t st = (hipStream_t)stream;
@@ -255,7 +255,7 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
         a.qc = (const uint8_t*)q->codes; a.qs = (const uint8_t*)q->scales;
         a.kc = (const uint8_t*)k->codes; a.ks = (const uint8_t*)k->scales;
         a.vc = (const uint8_t*)v->codes; a.vs = (const uint8_t*)v->scales;
-        a.o = as_dense(o); a.lse = lse;
+        a.o = as_dense(o); a.lse = lse; a.row_max = row_max;
         a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk;
         a.c_log2 = tau_of(p) * 1.4426950408889634f;
         TRY(check_device());
@@ -362,7 +362,7 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
 
 bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k, const bqa_qtensor* v,
                         const bqa_tensor* v_hi, const bqa_tensor* o_for_delta, const float* lse,
-                        const bqa_tensor* d_o, bqa_tensor* dq, bqa_tensor* dk, bqa_tensor* dv, void* ws,
+                        const float* row_max, const bqa_tensor* d_o, bqa_tensor* dq, bqa_tensor* dk, bqa_tensor* dv, void* ws,
                         size_t ws_bytes, void* stream) {
     (void)v;
     TRY(check_problem(p));
@@ -405,14 +405,14 @@ bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
         TRY(check_dense(dq, false, true));
         TRY(check_dense(dk, false, true));
         TRY(check_dense(dv, false, true));
-        if (!lse) return BQA_E_NULL;
+        if (!lse || !row_max) return BQA_E_NULL;
         if (!ws || ws_bytes < ws_qat_bwd_bytes(p->B, p->Hq, p->Nq, p->d)) return BQA_E_WORKSPACE;
-        if (!aligned16(ws)) return BQA_E_ALIGN;
+        if (!aligned16(ws) || ((uintptr_t)lse & 15u) || ((uintptr_t)row_max & 15u)) return BQA_E_ALIGN;
         QatBwdArgs a{};
         a.qc = (const uint8_t*)q->codes; a.qs = (const uint8_t*)q->scales;
         a.kc = (const uint8_t*)k->codes; a.ks = (const uint8_t*)k->scales;
         a.vc = (const uint8_t*)v->codes; a.vs = (const uint8_t*)v->scales;
-        a.d_o = as_dense(d_o); a.lse = lse;
+        a.d_o = as_dense(d_o); a.lse = lse; a.row_max = row_max;
         a.dq = as_dense(dq); a.dk = as_dense(dk); a.dv = as_dense(dv);
         a.B = p->B; a.H = p->Hq; a.N = p->Nq;
         a.tau = tau_of(p);

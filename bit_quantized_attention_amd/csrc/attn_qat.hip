@@ -13,15 +13,14 @@
 // lane owns one query row and (through the sigma row permutation) 16
 // consecutive keys per 32-key half of a 64-key tile.
 //
-// Scaled frame: MXFP4 codes and bf16 roundings commute with multiplication by
-// powers of two, so P is kept relative to a fixed per-row power-of-two
-// reference m_ref (the first tile's maximum rounded up) instead of the
-// running one: P_frame = 2^(m_int - m_ref) P, whose MXFP4 codes are those of
-// P (the E8M0 block scale absorbs the power of two) and whose bf16 rounding is
-// 2^k bf16(P).  O, O' and l all carry the same factor, which cancels in O/l,
-// so the accumulators are never rescaled; only if a row's scores climb more
-// than 64 (log2 units) above m_ref is the frame moved (exactly, by a power of
-// two).
+// Online softmax: FlashAttention-2's running row maximum M of the raw scores,
+// P = exp2((s - M) c) with c = tau log2(e), and O, O' and l scaled by
+// exp2((M_old - M_new) c) whenever a tile raises M in any lane of the
+// wavefront.  The difference s - M is exact near the maximum (both are fp32
+// values within a factor of two), so the P of the score that set M is exactly
+// 1 and the P near it are as accurate as fp32 allows: their MXFP4 codes,
+// whose top steps are 33-50 %, then match the exact arithmetic's.  M of each
+// row is also reported (row_max), for the backward to round P the same way.
 //
 // The P.V product: the 32 keys of an MX block of P sit in two lane halves;
 // one permlane32 swap per code word gives each half one complete block (in
@@ -150,8 +149,8 @@ __global__ __launch_bounds__(256, 2) void qat_fwd_kernel(QatFwdArgs a) {
     for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = v16f{};
 #pragma unroll
     for (int cb = 0; cb < (AUX ? D / 32 : 1); ++cb) xacc[cb] = v16f{};
-    float m_ref = -__builtin_inff();          // frame reference (log2 units, an integer)
-    float l_run = 0.0f;                        // this lane half's share of the row sum, in the frame
+    float m_run = -__builtin_inff();          // running maximum of the raw scores
+    float l_run = 0.0f;                        // this lane half's share of the row sum
     const float c = a.c_log2;
     const int n_tiles = a.Nk / BN;
 
@@ -175,39 +174,36 @@ __global__ __launch_bounds__(256, 2) void qat_fwd_kernel(QatFwdArgs a) {
         }
         b0 = __builtin_fmaxf(b0, partner32f(b0));
         b1 = __builtin_fmaxf(b1, partner32f(b1));
-        // ---- frame: fixed reference; moved (exactly) only when scores climb far above it
-        const float mx = __builtin_fmaxf(b0, b1) * c;
-        if (m_ref == -__builtin_inff() || __any(mx > m_ref + 64.0f)) {
-            const float m_new = __builtin_ceilf(__builtin_fmaxf(mx, m_ref));
-            if (m_ref != -__builtin_inff()) {
-                const float f = __builtin_ldexpf(1.0f, (int)(m_ref - m_new));
-                l_run *= f;
+        // ---- running maximum; the accumulators follow it
+        const float m_new = __builtin_fmaxf(m_run, __builtin_fmaxf(b0, b1));
+        if (__any(m_new > m_run)) {
+            const float f = m_new > m_run ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
+            l_run *= f;
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[cb][i] *= f;
+            if constexpr (AUX) {
 #pragma unroll
                 for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[cb][i] *= f;
-                if constexpr (AUX) {
-#pragma unroll
-                    for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) xacc[cb][i] *= f;
-                }
+                    for (int i = 0; i < 16; ++i) xacc[cb][i] *= f;
             }
-            m_ref = m_new;
         }
+        m_run = m_new;
         float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -m_ref));
-            s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -m_ref));
+            s0[i] = __builtin_amdgcn_exp2f((s0[i] - m_run) * c);
+            s1[i] = __builtin_amdgcn_exp2f((s1[i] - m_run) * c);
             ps[i & 1] += s0[i];
             ps[2 + (i & 1)] += s1[i];
         }
         l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
         // ---- MXFP4 P per 32-key block: P is monotone in the score, so the
         // block's largest P is the P of its largest score
-        const int e0 = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(b0, c, -m_ref)));
-        const int e1 = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(b1, c, -m_ref)));
+        const int e0 = mx_exponent(__builtin_amdgcn_exp2f((b0 - m_run) * c));
+        const int e1 = mx_exponent(__builtin_amdgcn_exp2f((b1 - m_run) * c));
         const float sc0 = __builtin_bit_cast(float, (uint32_t)(e0 + 127) << 23);
         const float sc1 = __builtin_bit_cast(float, (uint32_t)(e1 + 127) << 23);
         uint32_t p0w[2], p1w[2];
@@ -281,7 +277,8 @@ __global__ __launch_bounds__(256, 2) void qat_fwd_kernel(QatFwdArgs a) {
                 *(uint2*)(xrow + ch0) = make_uint2((uint32_t)x4[0] | ((uint32_t)x4[1] << 16), (uint32_t)x4[2] | ((uint32_t)x4[3] << 16));
         }
     }
-    if (a.lse && h == 0) a.lse[(int64_t)bh * a.Nq + qrow] = m_ref * 0.6931471805599453f + __logf(l_tot);
+    if (a.lse && h == 0) a.lse[(int64_t)bh * a.Nq + qrow] = __builtin_fmaf(m_run, c, __log2f(l_tot)) * 0.6931471805599453f;
+    if (a.row_max && h == 0) a.row_max[(int64_t)bh * a.Nq + qrow] = m_run;
 }
 
 // deq(Vhat) in bf16, channel-major [B, H, d, N]: every e2m1 value times its

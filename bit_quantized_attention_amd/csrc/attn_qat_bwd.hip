@@ -3,19 +3,22 @@
 // "Attn-QAT: 4-Bit Attention With Quantization-Aware Training", technical
 // summary §2 Principles 1 and 2: the backward recomputes P at the forward's
 // precision (the same MXFP4 scores, P = exp(s - L); for dV = P^T dO the
-// forward's own rounded P: rounded relative to a power-of-two reference,
-// whose MXFP4 codes are the forward's, then scaled to exp(s - L)), keeps
-// the straight-through
-// softmax Jacobian dS = P o (dP - delta') with the unquantised P, and takes
-// delta' = rowsum(dO o O') from the forward's high-precision auxiliary
-// output.  dP = dO V^T, dQ = tau dS K and dK = tau dS^T Q run as bf16
-// products against the FP4 operands (e2m1 times a power of two is exact in
-// bf16); dS is rounded to bf16 for them.  dV = P^T dO runs in fp16: the
-// rounded P times its row's exp(m - L) is not a bf16 value, and fp16 keeps
-// it to 2^-11 while holding dO exactly.
+// forward's rounding: MXFP4 codes of exp2((s - M) c) per 32 keys, M the row's
+// largest raw score as the forward reports it, scaled by exp(tau M - L)),
+// keeps the straight-through softmax Jacobian dS = P o (dP - delta') with the
+// unquantised P, and takes delta' = rowsum(dO o O') from the forward's
+// high-precision auxiliary output.  dP = dO V^T, dQ = tau dS K and
+// dK = tau dS^T Q run as bf16 products against the FP4 operands (e2m1 times a
+// power of two is exact in bf16); dS is rounded to bf16 for them.
+// dV = P^T dO runs in fp16: the rounded P times its row's exp(M - L) is not a
+// bf16 value, and fp16 keeps it to 2^-11.  dO enters that product scaled by
+// a power of two per (batch, head), chosen so that the head's largest |dO|
+// lands in [2^14, 2^15): small gradients keep fp16's full precision instead
+// of going subnormal, large ones do not overflow; dV is scaled back at the
+// end.
 //
 // Kernels:
-//   qat_delta_kernel   delta' per query row
+//   qat_delta_kernel   delta' per query row, the largest |dO| per head
 //   deq_t_fp4_kernel   bf16 copies in the layouts the products read:
 //   deq_t_bf16_kernel  deq(V) token-major, deq(Q)^T, deq(K)^T (from the
 //                      MXFP4 codes) and dO^T (fp16) channel-major
@@ -46,25 +49,50 @@ __device__ __forceinline__ int fc256(int r) { return r & 15; }
 
 // ------------------------------------------------------------------ preprocess
 __global__ __launch_bounds__(256) void qat_delta_kernel(Dense dO, Dense Oa, int H, int N, int64_t rows,
-                                                        float* __restrict__ delta) {
-    // delta'_i = sum_c dO[i, c] O'[i, c]; one row per 16 lanes, 8 channels each
+                                                        float* __restrict__ delta, uint32_t* __restrict__ do_amax) {
+    // delta'_i = sum_c dO[i, c] O'[i, c]; one row per 16 lanes, 8 channels each.
+    // A workgroup's 16 rows lie in one head (N is a multiple of 128).
+    __shared__ float wmax[4];
     const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
     const int part = threadIdx.x & 15;
-    float acc = 0.0f;
+    float acc = 0.0f, am = 0.0f;
     if (row < rows) {
         const int64_t bh = row / N, i = row % N, b = bh / H, h = bh % H;
         const v4i gv = *(const v4i*)((const uint16_t*)dO.p + b * dO.sB + h * dO.sH + i * dO.sN + 8 * part);
         const v4i ov = *(const v4i*)((const uint16_t*)Oa.p + b * Oa.sB + h * Oa.sH + i * Oa.sN + 8 * part);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            acc = __builtin_fmaf(bf16_bits_to_f32((uint16_t)gv[k]), bf16_bits_to_f32((uint16_t)ov[k]), acc);
-            acc = __builtin_fmaf(bf16_bits_to_f32((uint16_t)((uint32_t)gv[k] >> 16)),
-                                 bf16_bits_to_f32((uint16_t)((uint32_t)ov[k] >> 16)), acc);
+            const float g0 = bf16_bits_to_f32((uint16_t)gv[k]), g1 = bf16_bits_to_f32((uint16_t)((uint32_t)gv[k] >> 16));
+            acc = __builtin_fmaf(g0, bf16_bits_to_f32((uint16_t)ov[k]), acc);
+            acc = __builtin_fmaf(g1, bf16_bits_to_f32((uint16_t)((uint32_t)ov[k] >> 16)), acc);
+            am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(g0), __builtin_fabsf(g1)));
         }
     }
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 16);
     if (row < rows && part == 0) delta[row] = acc;
+    am = wave_max(am);
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = am;
+    __syncthreads();
+    const int64_t row0 = (int64_t)blockIdx.x * 16;
+    if (threadIdx.x == 0 && row0 < rows) {
+        const float m = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+        atomicMax(do_amax + row0 / N, __builtin_bit_cast(uint32_t, m));   // non-negative floats order as integers
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// Power of two k for a head's dO whose largest magnitude is amax (fp32
+// bits): amax 2^k lies in [2^14, 2^15); 0 for an all-zero head.
+__device__ __forceinline__ int do_shift(uint32_t amax_bits) {
+    const int e = (int)((amax_bits >> 23) & 0xFF);
+    if (amax_bits == 0u) return 0;
+    const int k = 14 - ((e == 0 ? 1 : e) - 127);
+    return k < -126 ? -126 : (k > 127 ? 127 : k);
 }
 
 // MXFP4 codes along C of a [BH][R][C] grid (rows of C/2 bytes, E8M0 per 32
@@ -107,10 +135,12 @@ __global__ __launch_bounds__(256) void deq_t_fp4_kernel(const uint8_t* __restric
     *(v4i*)(dst + 8) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
 }
 
-// Dense bf16 [B][H][R][C] view to fp16 (exact for the normal fp16 range),
+// Dense bf16 [B][H][R][C] view times 2^k of its head (do_shift) to fp16,
 // transposed: out[bh][c][r]; the tiling of deq_t_fp4_kernel, a thread
-// reading 16 values (32 bytes) of one row.
-__global__ __launch_bounds__(256) void deq_t_bf16_kernel(Dense x, int H, int R, int C, uint16_t* __restrict__ out) {
+// reading 16 values (32 bytes) of one row.  The scaled values lie below 2^15,
+// and every bf16 value at or above 2^-14 after scaling is exact in fp16.
+__global__ __launch_bounds__(256) void deq_t_bf16_kernel(Dense x, int H, int R, int C, const uint32_t* __restrict__ amax,
+                                                         uint16_t* __restrict__ out) {
     __shared__ uint32_t t[64][33];
     const int tilesR = R / 64, tilesC = C / 64;
     int blk = blockIdx.x;
@@ -118,13 +148,14 @@ __global__ __launch_bounds__(256) void deq_t_bf16_kernel(Dense x, int H, int R, 
     const int tr = blk % tilesR;
     const int64_t bh = blk / tilesR, b = bh / H, h = bh % H;
     const int tid = threadIdx.x, r = tid >> 2, q = tid & 3;
+    const float sc = __builtin_ldexpf(1.0f, do_shift(amax[bh]));
     const uint16_t* src = (const uint16_t*)x.p + b * x.sB + h * x.sH + ((int64_t)tr * 64 + r) * x.sN + tc * 64 + 16 * q;
     const v4i a0 = *(const v4i*)src, a1 = *(const v4i*)(src + 8);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const uint32_t pr = (uint32_t)(j < 4 ? a0[j] : a1[j - 4]);
-        t[r][8 * q + j] = (uint32_t)f32_to_f16_bits(bf16_bits_to_f32((uint16_t)pr)) |
-                          ((uint32_t)f32_to_f16_bits(bf16_bits_to_f32((uint16_t)(pr >> 16))) << 16);
+        t[r][8 * q + j] = (uint32_t)f32_to_f16_bits(bf16_bits_to_f32((uint16_t)pr) * sc) |
+                          ((uint32_t)f32_to_f16_bits(bf16_bits_to_f32((uint16_t)(pr >> 16)) * sc) << 16);
     }
     __syncthreads();
     const int c = tid >> 2, g = tid & 3;
@@ -171,7 +202,7 @@ struct RowIn {
     v4i qb[2];
     int qsb[2];
     v8bf gb[8];
-    float lse2, dlt;
+    float lse2, dlt, mraw;  // L (log2 units), delta', the row's largest raw score M
 };
 
 __device__ __forceinline__ void row_load(const QatBwdArgs& a, int bh, int b, int hq, int qrow, int h, RowIn& r) {
@@ -185,6 +216,7 @@ __device__ __forceinline__ void row_load(const QatBwdArgs& a, int bh, int b, int
     for (int st = 0; st < 8; ++st) r.gb[st] = *(const v8bf*)(g + 16 * st + 8 * h);
     r.lse2 = a.lse[(int64_t)bh * a.N + qrow] * 1.4426950408889634f;
     r.dlt = a.delta[(int64_t)bh * a.N + qrow];
+    r.mraw = a.row_max[(int64_t)bh * a.N + qrow];
 }
 
 // P (unrounded), its MXFP4 fake quantisation (as float) and dS (bf16-rounded)
@@ -204,22 +236,21 @@ __device__ __forceinline__ void tile_pds_g(const KeyTile& T, const RowIn& r, flo
         const v8bf av = *(const v8bf*)(T.vr + rk * 256 + 16 * ((2 * st + h) ^ fs256(rk)));
         dp = mfma_bf16_32x32x16(av, r.gb[st], dp);
     }
-    // P relative to m2 = ceil(L) (log2 units), a power of two: its MXFP4
-    // codes are the forward's; exp2(m2 - L) brings both to P = exp(s - L)
-    const float m2 = __builtin_ceilf(r.lse2);
-    const float back = __builtin_amdgcn_exp2f(m2 - r.lse2);
+    // P relative to the row's maximum, formed as the forward forms it;
+    // exp2(M c - L) brings it to P = exp(s - L)
+    const float back = __builtin_amdgcn_exp2f(__builtin_fmaf(r.mraw, c, -r.lse2));
     float pr[16];
     float smax = s[0];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m2));
+        pr[i] = __builtin_amdgcn_exp2f((s[i] - r.mraw) * c);
         p[i] = pr[i] * back;
         smax = __builtin_fmaxf(smax, s[i]);
         ds[i] = (float)(__bf16)(p[i] * (dp[i] - r.dlt));
     }
     // MX block g of the row: 16 keys here, 16 in the partner lane
     smax = __builtin_fmaxf(smax, partner32f(smax));
-    const int e = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(smax, c, -m2)));
+    const int e = mx_exponent(__builtin_amdgcn_exp2f((smax - r.mraw) * c));
     const float sc = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
@@ -245,6 +276,7 @@ struct RowTile {
     uint8_t dob[TQ * D * 2];    // dO bf16, 128 rows x 256 B (chunk XOR row & 15)
     float lse[TQ];
     float dlt[TQ];
+    float rmax[TQ];
 };
 struct LdsKVq {
     KeyTile kt;                  // fixed: the workgroup's key block
@@ -285,13 +317,13 @@ __device__ __forceinline__ void rows_issue(const QatBwdArgs& a, const KvqPlan& c
     const uint16_t* gb = (const uint16_t*)a.d_o.p + b * a.d_o.sB + hq * a.d_o.sH + (int64_t)q0 * a.d_o.sN;
 #pragma unroll
     for (int u = 0; u < 4; ++u) lds_copy16(cp.g[u], gb, lds_addr(R.dob + 1024 * (4 * w + u)));
-    // scales, log-sum-exp, delta: six 256-byte copies (wavefronts 6, 7 repeat
-    // 0, 1 so that all count the same copies)
+    // scales, log-sum-exp, delta, maxima: eight 256-byte copies, one per wavefront
     const uint32_t o = (uint32_t)(4 * l);
-    const int job = w % 6, half = job & 1;
+    const int job = w, half = job & 1;
     if (job < 2) lds_copy4(o, a.qs + ((int64_t)bh * a.N + q0) * (D / 32) + 256 * half, lds_addr(R.qs + 256 * half));
     else if (job < 4) lds_copy4(o, a.lse + (int64_t)bh * a.N + q0 + 64 * half, lds_addr(R.lse + 64 * half));
-    else lds_copy4(o, a.delta + (int64_t)bh * a.N + q0 + 64 * half, lds_addr(R.dlt + 64 * half));
+    else if (job < 6) lds_copy4(o, a.delta + (int64_t)bh * a.N + q0 + 64 * half, lds_addr(R.dlt + 64 * half));
+    else lds_copy4(o, a.row_max + (int64_t)bh * a.N + q0 + 64 * half, lds_addr(R.rmax + 64 * half));
 }
 __device__ __forceinline__ void cols_issue(const QatBwdArgs& a, const KvqPlan& cp, int bh, int I, LdsKVq& L, int w) {
     const uint16_t* gT = a.doT + (int64_t)bh * D * a.N + I * TQ;
@@ -312,6 +344,7 @@ __device__ __forceinline__ void row_from_lds(const RowTile& R, int row, int h, R
     for (int st = 0; st < 8; ++st) r.gb[st] = *(const v8bf*)(R.dob + row * 256 + 16 * ((2 * st + h) ^ (row & 15)));
     r.lse2 = R.lse[row] * 1.4426950408889634f;
     r.dlt = R.dlt[row];
+    r.mraw = R.rmax[row];
 }
 
 // One workgroup of 8 wavefronts per 64-key block over the 128-query tiles.
@@ -406,13 +439,14 @@ __global__ __launch_bounds__(512, 1) void qbwd_dkdv_kernel(QatBwdArgs a) {
         }
         barrier_only();
     }
-    // dv reg i: key ko + 8 (i / 4) + 4 h + i % 4, channel co + lq
+    // dv reg i: key ko + 8 (i / 4) + 4 h + i % 4, channel co + lq; dO entered scaled by 2^k
     uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sB + hq * a.dv.sH;
     uint16_t* dkp = (uint16_t*)a.dk.p + b * a.dk.sB + hq * a.dk.sH;
+    const int kdo = do_shift(a.do_amax[bh]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int64_t kpos = (int64_t)J * TK + ko + 8 * (i >> 2) + 4 * h + (i & 3);
-        dvp[kpos * a.dv.sN + co + lq] = f32_to_bf16_bits(dv[i]);
+        dvp[kpos * a.dv.sN + co + lq] = f32_to_bf16_bits(__builtin_ldexpf(dv[i], -kdo));
         dkp[kpos * a.dk.sN + co + lq] = f32_to_bf16_bits(dk[i] * a.tau);
     }
 }
@@ -489,7 +523,8 @@ __global__ __launch_bounds__(256, 2) void qbwd_dq_kernel(QatBwdArgs a) {
 
 size_t ws_qat_bwd_bytes(int B, int H, int N, int d) {
     const size_t bhn = (size_t)B * H * N;
-    return bhn * 4 + 4 * bhn * d * 2 + 256;   // delta', deq(V), deq(Q)^T, deq(K)^T, dO^T
+    // delta', deq(V), deq(Q)^T, deq(K)^T, dO^T, |dO| maxima per head
+    return bhn * 4 + 4 * bhn * d * 2 + (((size_t)B * H * 4 + 255) & ~(size_t)255) + 256;
 }
 
 hipError_t launch_qat_bwd(QatBwdArgs a, Dense o_aux, void* ws, hipStream_t st) {
@@ -499,16 +534,19 @@ hipError_t launch_qat_bwd(QatBwdArgs a, Dense o_aux, void* ws, hipStream_t st) {
     uint16_t* vdeq = (uint16_t*)p;     p += bhn * D * 2;
     uint16_t* qT = (uint16_t*)p;       p += bhn * D * 2;
     uint16_t* kT = (uint16_t*)p;       p += bhn * D * 2;
-    uint16_t* doT = (uint16_t*)p;
-    a.delta = delta; a.vdeq = vdeq; a.qT = qT; a.kT = kT; a.doT = doT;
+    uint16_t* doT = (uint16_t*)p;      p += bhn * D * 2;
+    uint32_t* do_amax = (uint32_t*)p;
+    a.delta = delta; a.vdeq = vdeq; a.qT = qT; a.kT = kT; a.doT = doT; a.do_amax = do_amax;
 
-    qat_delta_kernel<<<(unsigned)((bhn * 16 + 255) / 256), 256, 0, st>>>(a.d_o, o_aux, a.H, a.N, bhn, delta);
+    const int nbh = a.B * a.H;
+    fill_zero_kernel<<<(nbh + 255) / 256, 256, 0, st>>>(do_amax, nbh);
+    qat_delta_kernel<<<(unsigned)((bhn * 16 + 255) / 256), 256, 0, st>>>(a.d_o, o_aux, a.H, a.N, bhn, delta, do_amax);
     const unsigned tg = (unsigned)((int64_t)a.B * a.H * (a.N / 64) * (D / 64));
     // V codes are channel-major [d][N/2]: transposing the (channel, token) grid gives token-major rows
     deq_t_fp4_kernel<<<tg, 256, 0, st>>>(a.vc, a.vs, D, a.N, vdeq);
     deq_t_fp4_kernel<<<tg, 256, 0, st>>>(a.qc, a.qs, a.N, D, qT);
     deq_t_fp4_kernel<<<tg, 256, 0, st>>>(a.kc, a.ks, a.N, D, kT);
-    deq_t_bf16_kernel<<<tg, 256, 0, st>>>(a.d_o, a.H, a.N, D, doT);
+    deq_t_bf16_kernel<<<tg, 256, 0, st>>>(a.d_o, a.H, a.N, D, do_amax, doT);
     qbwd_dkdv_kernel<<<a.B * a.H * (a.N / TK), 512, 0, st>>>(a);
     qbwd_dq_kernel<<<a.B * a.H * (a.N / TQ), 256, 0, st>>>(a);
     return hipGetLastError();

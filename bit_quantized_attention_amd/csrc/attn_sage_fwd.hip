@@ -3,11 +3,11 @@
 // "SageBwd: A Trainable Low-bit Attention", Methodology 1 (INT8 attention with
 // per-block scales) and 4 (K-smoothing, which happens in the K quantiser):
 //   S_int = Qhat Khat^T exactly in int32 (i8 matrix instructions), scores
-//   s = S_int * s_q * s_k * tau; online softmax over key tiles of 64
-//   (FlashAttention-2 style) whose reference point is the running max rounded
-//   up to a power of two; P rounded for the P.V product as fp16 (V fp16),
-//   e4m3(448 P) (V per-channel e4m3) or int8 per (row, tile) (V per-channel
-//   int8); the row sum accumulates the unrounded P.
+//   s = S_int * s_q * s_k * tau; online softmax over key tiles of 64 with
+//   FlashAttention-2's running row maximum m (P = exp(s - m), the sums so far
+//   scaled by exp(m_old - m_new) when m moves); P rounded for the P.V product
+//   as fp16 (V fp16), e4m3(448 P) (V per-channel e4m3) or int8 per
+//   (row, tile) (V per-channel int8); the row sum accumulates the unrounded P.
 //
 // Work decomposition: one workgroup of 4 wavefronts per 128 query rows of one
 // (batch, head); each wavefront owns 32 rows.  The score tile is computed
@@ -142,25 +142,33 @@ __device__ __forceinline__ void stage_store(const Staging<PV, D>& st, uint8_t* k
     }
 }
 
-// Per-wavefront running state of the online softmax.  m is the oracle's
-// reference point (running row max rounded up to an integer, log2 units);
-// the accumulators and the row sum are kept in a frame m0 <= m.  For the
-// fp8 and int8 P.V products the factor 2^(m - m0) rides on the product
-// itself (the E8M0 operand scale of P, or the fp32 scale of the int32 tile),
-// so the accumulators are only rescaled when the frame falls more than
-// FRAME_GAP binades behind; for fp16 P the frame follows m exactly.
+// Per-wavefront running state of the online softmax: m is the running row
+// maximum of the scaled scores (log2 units), and O and l are kept relative to
+// it (FlashAttention-2): when a tile raises m in any lane of the wavefront,
+// the wavefront scales its accumulators by exp2(m_old - m_new) (1 in the
+// lanes whose maximum did not move).
 template <int D>
 struct RowState {
     v16f oacc[D / 32];      // O^T accumulator: lane (query lq, half h), channel 32cb + 8(i/4) + 4h + i%4
-    float m;                // reference point (log2 units)
-    float m0;               // frame of oacc and l
-    float l;                // this lane half's share of the row sum, in the frame
+    float m;                // running maximum (log2 units)
+    float l;                // this lane half's share of the row sum
 };
-constexpr float FRAME_GAP = 96.0f;
+
+// Scale the accumulators and the row sum to a new running maximum.
+template <int D>
+__device__ __forceinline__ void rescale(RowState<D>& st, float m_new) {
+    // exp2(-inf) = 0 for a row's first visible tile; 1 where m did not move
+    const float f = m_new > st.m ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.0f;
+    st.l *= f;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.oacc[cb][i] *= f;
+}
 
 // Softmax of one 64-key tile: scores (int32, converted in place) -> P in
-// registers (f0: keys 16h + i, f1: keys 32 + 16h + i), reference and frame
-// updates, row sum.  Returns the row's largest P (int8 P.V needs it).
+// registers (f0: keys 16h + i, f1: keys 32 + 16h + i), running maximum and
+// rescale, row sum.  Returns the row's largest P (int8 P.V needs it).
 // `diag_lim` >= 64 means no key of the tile is masked for this lane;
 // otherwise register i (+32) is visible iff i (+32) <= diag_lim.
 template <int PV, int D>
@@ -180,35 +188,8 @@ __device__ __forceinline__ float tile_softmax(RowState<D>& st, const v16i& s0, c
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, f0[i]), f1[i]);
     mx = __builtin_fmaxf(mx, partner32f(mx));
-    const float m_new = __builtin_fmaxf(st.m, __builtin_ceilf(mx * c));
-    if constexpr (PV == PV_F16) {
-        // fp16 P cannot carry the frame: rescale whenever the reference moves
-        if (__any(m_new != st.m0)) {
-            if (st.m0 != -__builtin_inff() && m_new != st.m0) {
-                const float f = __builtin_ldexpf(1.0f, (int)(st.m0 - m_new));
-                st.l *= f;
-#pragma unroll
-                for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) st.oacc[cb][i] *= f;
-            }
-            st.m0 = m_new;
-        }
-    } else {
-        if (__any(m_new - st.m0 > FRAME_GAP)) {
-            if (m_new - st.m0 > FRAME_GAP) {
-                if (st.m0 != -__builtin_inff()) {
-                    const float f = __builtin_ldexpf(1.0f, (int)(st.m0 - m_new));
-                    st.l *= f;
-#pragma unroll
-                    for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) st.oacc[cb][i] *= f;
-                }
-                st.m0 = m_new;
-            }
-        }
-    }
+    const float m_new = __builtin_fmaxf(st.m, mx * c);
+    if (__any(m_new > st.m)) rescale<D>(st, m_new);
     st.m = m_new;
     const float bias = m_new == -__builtin_inff() ? 0.0f : pbias - m_new;
     float ps[4];
@@ -224,17 +205,14 @@ __device__ __forceinline__ float tile_softmax(RowState<D>& st, const v16i& s0, c
             ps[2 + (i & 1)] += f1[i];
         }
     }
-    const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    // the row sum lives in the frame: times 2^(m - m0) (an exact power of two)
-    st.l += PV == PV_F16 ? psum : __builtin_ldexpf(psum, st.m0 == -__builtin_inff() ? 0 : (int)(m_new - st.m0));
+    st.l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     return mx == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, bias));
 }
 
-// P.V of one tile into the frame-m0 accumulators (V^T tile in LDS).
+// P.V of one tile into the accumulators (V^T tile in LDS).
 template <int PV, int D>
 __device__ __forceinline__ void tile_pv(RowState<D>& st, const float (&f0)[16], const float (&f1)[16], float pmax,
                                         const uint8_t* vt, int lq, int h) {
-    const int shift = st.m0 == -__builtin_inff() ? 0 : (int)(st.m - st.m0);   // 0 .. FRAME_GAP
     if constexpr (PV == PV_F8) {
         v8i pb;
 #pragma unroll
@@ -246,21 +224,20 @@ __device__ __forceinline__ void tile_pv(RowState<D>& st, const float (&f0)[16], 
             int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k], f1[4 * k + 1], __builtin_bit_cast(int, f1[4 * k]), false);
             pb[4 + k] = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k + 2], f1[4 * k + 3], w1, true);
         }
-        const int sb = 127 + shift;     // E8M0 scale of P: the frame factor, exact
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb) {
             const int r = 32 * cb + lq;
             v4i lo = *(const v4i*)(vt + swz_v<BN>(r, h));
             v4i hi = *(const v4i*)(vt + swz_v<BN>(r, 2 + h));
             v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            st.oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, st.oacc[cb], 0, 0, 0, 127, 0, sb);
+            st.oacc[cb] = mfma_f8_32x32x64(av, pb, st.oacc[cb]);
         }
     } else if constexpr (PV == PV_I8) {
         // int8 P per (row, tile): r = the row's largest P in the tile
         const float r = pmax;
         float inv = r > 0.0f ? 127.0f / r : 0.0f;
         if (__builtin_isinf(inv)) inv = 0.0f;
-        const float rs = __builtin_ldexpf(r * (1.0f / 127.0f), shift);
+        const float rs = r * (1.0f / 127.0f);
         // every P of the row is at most r, so |P * inv| <= 127 (no clamp)
         v4i pb0, pb1;
 #pragma unroll
@@ -279,7 +256,6 @@ __device__ __forceinline__ void tile_pv(RowState<D>& st, const float (&f0)[16], 
             for (int i = 0; i < 16; ++i) st.oacc[cb][i] = __builtin_fmaf((float)pv[i], rs, st.oacc[cb][i]);
         }
     } else {
-        (void)shift;
         // fp16 P; four 16-key steps: keys 32(s/2) + 16h + 8(s%2) + e
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -370,7 +346,6 @@ __global__ __launch_bounds__(256, (PV == PV_F16 || !CAUSAL) ? 2 : 3) void sage_f
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) rs.oacc[cb] = v16f{};
     rs.m = -__builtin_inff();
-    rs.m0 = -__builtin_inff();
     rs.l = 0.0f;
 
     // Tiles go to LDS three deep.  fp8 / int8 V: direct copies; while tile j
@@ -456,7 +431,7 @@ __global__ __launch_bounds__(256, (PV == PV_F16 || !CAUSAL) ? 2 : 3) void sage_f
     }
     if (a.lse && h == 0) {
         // natural-log LSE; with P scaled by 448 the sum carries that factor
-        float lse = rs.m0 * 0.6931471805599453f + __logf(l_tot);
+        float lse = rs.m * 0.6931471805599453f + __logf(l_tot);
         if (PV == PV_F8) lse -= 6.104793232414985f;   // ln(448)
         a.lse[(int64_t)bh * a.Nq + qrow] = lse;
     }
@@ -512,7 +487,6 @@ struct CopyPlan {
 // P of a finished tile, packed as the B operand of its P.V product.
 struct PendF8 {
     v8i pb;   // e4m3 codes of 448 P: lane (query, half h), keys 16h + 4k .. (and +32)
-    int sb;   // E8M0 scale of P: 127 + the frame shift when P was made
 };
 
 template <int D>
@@ -521,15 +495,15 @@ __device__ __forceinline__ void pv_f8(v16f (&oacc)[D / 32], const PendF8& pp, co
     v4i lo = *(const v4i*)(vt + swz_v<BN>(r, h));
     v4i hi = *(const v4i*)(vt + swz_v<BN>(r, 2 + h));
     v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pp.pb, oacc[cb], 0, 0, 0, 127, 0, pp.sb);
+    oacc[cb] = mfma_f8_32x32x64(av, pp.pb, oacc[cb]);
 }
 
 // One step of the pipeline (see above).  s0/s1: int32 scores of this tile on
 // entry, of the next tile on exit; pend: P of the previous tile on entry, of
 // this tile on exit.  The arithmetic is the one of tile_softmax + tile_pv
-// (fp8 P.V), with the rare frame move done after the exponentials (they do
-// not depend on the frame) and after P.V of the previous tile was issued (it
-// belongs to the old frame).
+// (fp8 P.V), with the rescale of the accumulators done after P.V of the
+// previous tile was issued (that product belongs to the old maximum) and after
+// the exponentials (so that it does not delay them).
 template <int D, bool DIAG>
 __device__ __forceinline__ void f8_step(RowState<D>& st, PendF8& pend, v16i& s0, v16i& s1, const uint8_t* k_next,
                                         const uint8_t* v_prev, const v4i* qb, int krow, int lq, int h, float c,
@@ -551,10 +525,8 @@ __device__ __forceinline__ void f8_step(RowState<D>& st, PendF8& pend, v16i& s0,
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, f0[i]), f1[i]);
     mx = __builtin_fmaxf(mx, partner32f(mx));
-    const float m_new = __builtin_fmaxf(st.m, __builtin_ceilf(mx * c));
-    // the frame moves when the reference runs more than FRAME_GAP binades ahead
-    // (always at the first visible tile, where m0 = -inf)
-    const bool need = m_new - st.m0 > FRAME_GAP;
+    const float m_new = __builtin_fmaxf(st.m, mx * c);
+    const bool need = m_new > st.m;
     const float bias = m_new == -__builtin_inff() ? 0.0f : pbias - m_new;
     // scores of the next tile, one 32-channel slice every four exponentials;
     // each slice's K operands are read while the slice before is issued
@@ -585,7 +557,6 @@ __device__ __forceinline__ void f8_step(RowState<D>& st, PendF8& pend, v16i& s0,
         }
     }
     const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    const int shift = (need || st.m0 == -__builtin_inff()) ? 0 : (int)(m_new - st.m0);   // 0 .. FRAME_GAP
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         // the first conversion of a pair writes the low half-word, the second
@@ -595,7 +566,6 @@ __device__ __forceinline__ void f8_step(RowState<D>& st, PendF8& pend, v16i& s0,
         int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k], f1[4 * k + 1], __builtin_bit_cast(int, f1[4 * k]), false);
         pend.pb[4 + k] = __builtin_amdgcn_cvt_pk_fp8_f32(f1[4 * k + 2], f1[4 * k + 3], w1, true);
     }
-    pend.sb = 127 + shift;
     s0 = n0;
     s1 = n1;
     // instruction order: the LDS reads of P.V and of the first score slice
@@ -612,7 +582,7 @@ __device__ __forceinline__ void f8_step(RowState<D>& st, PendF8& pend, v16i& s0,
             __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);           // P.V
             __builtin_amdgcn_sched_group_barrier(0x0002, 6, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x0002, 30, 0);              // conversions, maximum, frame
+        __builtin_amdgcn_sched_group_barrier(0x0002, 30, 0);              // conversions, maximum
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);           // scores
@@ -623,25 +593,13 @@ __device__ __forceinline__ void f8_step(RowState<D>& st, PendF8& pend, v16i& s0,
             __builtin_amdgcn_sched_group_barrier(0x0002, 96 / NS / 2, 0);
         }
     }
-    // keep this tile's vector work ahead of the rare branch below (the
-    // compiler would otherwise sink it into the next step, away from the
-    // matrix instructions it is meant to hide)
+    // keep this tile's vector work ahead of the branch below (the compiler
+    // would otherwise sink it into the next step, away from the matrix
+    // instructions it is meant to hide)
     asm volatile("" ::"v"(pend.pb[0]), "v"(pend.pb[1]), "v"(pend.pb[2]), "v"(pend.pb[3]), "v"(pend.pb[4]),
                  "v"(pend.pb[5]), "v"(pend.pb[6]), "v"(pend.pb[7]), "v"(psum));
-    if (__any(need)) {
-        if (need) {
-            if (st.m0 != -__builtin_inff()) {
-                const float f = __builtin_ldexpf(1.0f, (int)(st.m0 - m_new));
-                st.l *= f;
-#pragma unroll
-                for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) st.oacc[cb][i] *= f;
-            }
-            st.m0 = m_new;
-        }
-    }
-    st.l += __builtin_ldexpf(psum, shift);
+    if (__any(need)) rescale<D>(st, m_new);
+    st.l += psum;
     st.m = m_new;
 }
 
@@ -716,11 +674,9 @@ __global__ __launch_bounds__(256, 2) void sage_fwd_f8_kernel(SageFwdArgs a) {
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb) rs.oacc[cb] = v16f{};
         rs.m = -__builtin_inff();
-        rs.m0 = -__builtin_inff();
         rs.l = 0.0f;
         PendF8 pend;
         pend.pb = v8i{};
-        pend.sb = 127;
 
         // V slot 3 starts as zeros: the first step's P.V (of no tile, P = 0) reads it
 #pragma unroll
@@ -849,7 +805,7 @@ __global__ __launch_bounds__(256, 2) void sage_fwd_f8_kernel(SageFwdArgs a) {
         }
         if (a.lse && h == 0) {
             // natural-log LSE; with P scaled by 448 the sum carries that factor
-            a.lse[(int64_t)bh * a.Nq + qrow] = rs.m0 * 0.6931471805599453f + __logf(l_tot) - 6.104793232414985f;
+            a.lse[(int64_t)bh * a.Nq + qrow] = rs.m * 0.6931471805599453f + __logf(l_tot) - 6.104793232414985f;
         }
     };
     const int n_pass = CAUSAL && p != n_qt - 1 - p ? 2 : 1;

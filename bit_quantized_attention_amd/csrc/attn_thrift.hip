@@ -11,12 +11,15 @@
 //
 // Layout: one workgroup of 4 wavefronts per 128 query rows (32 rows per
 // wavefront, S^T = K Q^T so each lane owns one query row); FP4 key blocks of
-// 128 keys, bf16 key blocks in two halves of 64.  The softmax keeps P in a
-// fixed per-row power-of-two frame (MXFP4 codes, the two-level factor and
-// bf16 roundings are all invariant under it), moved exactly only when a
-// row's scores climb 64 binades above it.  The FP4 path's accumulator is
-// kept in units of the current block's r/6, rescaled when the next block
-// brings a new r.
+// 128 keys, bf16 key blocks in two halves of 64 (each half is one tile of
+// the online softmax).  The softmax is FlashAttention-2's: P = exp(s - m)
+// against the running row maximum m, the sums so far scaled by
+// exp(m_old - m_new) when m moves.  The FP4 path's accumulator is kept in
+// units of the current block's r/6 and rescaled when the next block brings a
+// new r; that rescale also carries the running maximum's factor.  A block
+// whose largest P is below 2^-64 adds nothing (as one whose P all underflow):
+// its share of O is below 2^-64 of the row's, and the unit change would leave
+// fp32's range.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -102,18 +105,21 @@ __device__ __forceinline__ void store_bf(const VStage& vs, LdsBf& L, int tid) {
     }
 }
 
-// Exact rescale of every accumulator and of the row sum by 2^(m_old - m_new).
-__device__ __forceinline__ void move_frame(v16f* oacc, float& l_run, float& m_ref, float m_new) {
-    if (m_ref != -__builtin_inff()) {
-        const float f = __builtin_ldexpf(1.0f, (int)(m_ref - m_new));
+// Running maximum of a bf16 tile: when it moves in any lane, scale the
+// accumulators and the row sum by exp2(m_old - m_new) (0 at a row's first
+// visible tile, 1 where the maximum did not move).
+__device__ __forceinline__ void follow_max(v16f* oacc, float& l_run, float& m_run, float m_new) {
+    if (__any(m_new > m_run)) {
+        const float f = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
         l_run *= f;
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[cb][i] *= f;
     }
-    m_ref = m_new;
+    m_run = m_new;
 }
+constexpr float R_FLOOR = 0x1p-64f;   // two-level factors below this add nothing
 
 __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
     __shared__ __attribute__((aligned(16))) LdsBuf lds[2];
@@ -151,8 +157,8 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
     v16f oacc[D / 32];
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = v16f{};
-    float m_ref = -__builtin_inff();   // frame (log2 units, an integer); -inf before the first finite score
-    float l_run = 0.0f;                // this lane half's share of the row sum, in the frame
+    float m_run = -__builtin_inff();   // running maximum (log2 units); -inf before the first finite score
+    float l_run = 0.0f;                // this lane half's share of the row sum
     float gsc = 1.0f;                  // FP4 path: oacc holds O / gsc, gsc = r / 6 of the last block
 
     // ------------------------------------------------------------ FP4 path
@@ -201,16 +207,15 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
             bt[t] = __builtin_fmaxf(m, partner32f(m));
         }
         const float smax = __builtin_fmaxf(__builtin_fmaxf(bt[0], bt[1]), __builtin_fmaxf(bt[2], bt[3]));
-        const float mx = smax * c;
-        if (__any(mx > m_ref + 64.0f)) {
-            if (mx > m_ref) move_frame(oacc, l_run, m_ref, __builtin_ceilf(mx));
-        }
-        const float mu = m_ref == -__builtin_inff() ? 0.0f : m_ref;
+        const float m_new = __builtin_fmaxf(m_run, smax * c);
+        const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        const float mu = m_new == -__builtin_inff() ? 0.0f : m_new;
         // two-level P: r = the row's largest P in the block, P' = P 6 / r =
         // 6 exp2((s - smax) c), formed directly by the exponential; the row
         // sum of P is r/6 times that of P'.  A block whose P all underflow
         // (r = 0) adds nothing.
-        const float r = __builtin_amdgcn_exp2f(__builtin_fmaf(smax, c, -mu));
+        float r = __builtin_amdgcn_exp2f(__builtin_fmaf(smax, c, -mu));
+        r = r >= R_FLOOR ? r : 0.0f;
         const float bias2 = r > 0.0f ? 2.584962500721156f - smax * c : -__builtin_inff();   // log2(6) - smax c
         float ps[4];
 #pragma unroll
@@ -225,7 +230,9 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
             }
             ps[t] = q0 + q1;
         }
+        l_run *= alpha;
         if (r > 0.0f) l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) * (r * (1.0f / 6.0f));
+        m_run = m_new;
         const float six_r = r > 0.0f ? 6.0f / r : 0.0f;
         int e[4];
 #pragma unroll
@@ -244,9 +251,11 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
                 pw[t][wd] = x;
             }
         }
-        // accumulator units: from the previous block's r/6 to this block's
+        // accumulator units: from the previous block's r/6 (at the old maximum)
+        // to this block's
+        // (when r = 0 the maximum did not move, alpha = 1)
         if (r > 0.0f) {
-            const float ratio = gsc * six_r;
+            const float ratio = gsc * six_r * alpha;
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -272,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
         J = Jn;
         buf ^= 1;
     }
-    // back to plain frame units
+    // back to plain units
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -317,11 +326,8 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
         float m = __builtin_fmaxf(s0[0], s1[0]);
 #pragma unroll
         for (int i = 1; i < 16; ++i) m = __builtin_fmaxf(__builtin_fmaxf(m, s0[i]), s1[i]);
-        const float mx = __builtin_fmaxf(m, partner32f(m)) * c;
-        if (__any(mx > m_ref + 64.0f)) {
-            if (mx > m_ref) move_frame(oacc, l_run, m_ref, __builtin_ceilf(mx));
-        }
-        const float mu = m_ref == -__builtin_inff() ? 0.0f : m_ref;
+        follow_max(oacc, l_run, m_run, __builtin_fmaxf(m_run, __builtin_fmaxf(m, partner32f(m)) * c));
+        const float mu = m_run == -__builtin_inff() ? 0.0f : m_run;
         float ps[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -367,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
                 make_uint2((uint32_t)o4[0] | ((uint32_t)o4[1] << 16), (uint32_t)o4[2] | ((uint32_t)o4[3] << 16));
         }
     }
-    if (a.lse && h == 0) a.lse[(int64_t)bh * a.Nq + qrow] = m_ref * 0.6931471805599453f + __logf(l_tot);
+    if (a.lse && h == 0) a.lse[(int64_t)bh * a.Nq + qrow] = m_run * 0.6931471805599453f + __logf(l_tot);
 }
 
 }  // namespace
@@ -389,14 +395,14 @@ hipError_t launch_thrift_fwd(const ThriftFwdArgs& a, hipStream_t st) {
 // split the key blocks that not every head selected run through the FP4
 // path (heads that selected the block are masked there), then the blocks
 // any head selected run through the bf16 path in quarters of 32 keys (heads
-// that did not select it are masked).  Each split leaves a partial
-// (frame m, l, O) per head; decode_combine merges them exactly (the frames
-// are powers of two).
+// that did not select it are masked; each quarter is one tile of the online
+// softmax).  Each split leaves a partial (running maximum m, l, O) per head;
+// decode_combine merges them.
 namespace bqa {
 namespace {
 
 constexpr int DQ = 32;     // bf16 keys per decode step
-constexpr int PART = D + 4; // partial record: frame m, row sum l, 2 pad, O[d]
+constexpr int PART = D + 4; // partial record: running maximum m, row sum l, 2 pad, O[d]
 
 struct LdsDec {
     union {
@@ -505,7 +511,7 @@ __global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
     v16f oacc[D / 32];
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = v16f{};
-    float m_ref = -__builtin_inff(), l_run = 0.0f, gsc = 1.0f;
+    float m_run = -__builtin_inff(), l_run = 0.0f, gsc = 1.0f;
     const uint32_t mybit = col_ok ? (1u << lq) : 0u;
 
     // ------------------------------------------------------------ FP4 blocks
@@ -545,13 +551,12 @@ __global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
             bt[t] = __builtin_fmaxf(m, partner32f(m));
         }
         const float smax = __builtin_fmaxf(__builtin_fmaxf(bt[0], bt[1]), __builtin_fmaxf(bt[2], bt[3]));
-        const float mx = smax * c;
-        if (__any(mx > m_ref + 64.0f)) {
-            if (mx > m_ref) move_frame(oacc, l_run, m_ref, __builtin_ceilf(mx));
-        }
-        const float mu = m_ref == -__builtin_inff() ? 0.0f : m_ref;
+        const float m_new = __builtin_fmaxf(m_run, smax * c);
+        const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        const float mu = m_new == -__builtin_inff() ? 0.0f : m_new;
         // two-level P formed directly as P' = 6 exp2((s - smax) c) (see the prefill)
-        const float r = __builtin_amdgcn_exp2f(__builtin_fmaf(smax, c, -mu));
+        float r = __builtin_amdgcn_exp2f(__builtin_fmaf(smax, c, -mu));
+        r = r >= R_FLOOR ? r : 0.0f;
         const float bias2 = r > 0.0f ? 2.584962500721156f - smax * c : -__builtin_inff();   // log2(6) - smax c
         float ps[4];
 #pragma unroll
@@ -566,7 +571,9 @@ __global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
             }
             ps[t] = q0 + q1;
         }
+        l_run *= alpha;
         if (r > 0.0f) l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) * (r * (1.0f / 6.0f));
+        m_run = m_new;
         const float six_r = r > 0.0f ? 6.0f / r : 0.0f;
         int e[4];
 #pragma unroll
@@ -585,8 +592,9 @@ __global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
                 pw[t][wd] = x;
             }
         }
+        // (when r = 0 the maximum did not move, alpha = 1)
         if (r > 0.0f) {
-            const float ratio = gsc * six_r;
+            const float ratio = gsc * six_r * alpha;
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -651,11 +659,8 @@ __global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
         float m = s0[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) m = __builtin_fmaxf(m, s0[i]);
-        const float mx = __builtin_fmaxf(m, partner32f(m)) * c;
-        if (__any(mx > m_ref + 64.0f)) {
-            if (mx > m_ref) move_frame(oacc, l_run, m_ref, __builtin_ceilf(mx));
-        }
-        const float mu = m_ref == -__builtin_inff() ? 0.0f : m_ref;
+        follow_max(oacc, l_run, m_run, __builtin_fmaxf(m_run, __builtin_fmaxf(m, partner32f(m)) * c));
+        const float mu = m_run == -__builtin_inff() ? 0.0f : m_run;
         float ps = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -683,7 +688,7 @@ __global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
         buf ^= 1;
     }
 
-    // partial of this split: frame m (log2 units), row sum, unnormalised O
+    // partial of this split: running maximum m (log2 units), row sum, unnormalised O
     const float l_tot = l_run + partner32f(l_run);
     if (!col_ok) return;
     float* part = a.part + ((int64_t)bhq * S + sp) * PART;
@@ -695,13 +700,13 @@ __global__ __launch_bounds__(64) void thrift_decode_kernel(ThriftDecArgs a) {
             *(v4f*)(part + 4 + ch0) = v4f{oacc[cb][4 * g], oacc[cb][4 * g + 1], oacc[cb][4 * g + 2], oacc[cb][4 * g + 3]};
         }
     if (h == 0) {
-        part[0] = m_ref;
+        part[0] = m_run;
         part[1] = l_tot;
     }
 }
 
 // Merge the splits of one (batch, query head): m = max m_s,
-// l = sum 2^(m_s - m) l_s, O = sum 2^(m_s - m) O_s / l (powers of two: exact).
+// l = sum 2^(m_s - m) l_s, O = sum 2^(m_s - m) O_s / l.
 __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ part, int S, Dense o,
                                                              float* lse, int Hq) {
     const int bhq = blockIdx.x, ch = threadIdx.x;
@@ -712,7 +717,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
     for (int s = 0; s < S; ++s) {
         const float ms = p[(int64_t)s * PART];
         if (ms == -__builtin_inff()) continue;
-        const float wgt = __builtin_ldexpf(1.0f, (int)(ms - m));
+        const float wgt = __builtin_amdgcn_exp2f(ms - m);
         lsum += wgt * p[(int64_t)s * PART + 1];
         acc += wgt * p[(int64_t)s * PART + 4 + ch];
     }

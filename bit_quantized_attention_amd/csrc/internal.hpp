@@ -51,6 +51,7 @@ struct QatFwdArgs {
     uint16_t* vdeq;                                      // workspace [B,Hkv,d,Nk] bf16; null: no O'
     Dense o, oa;                                         // O, O' [B,Hq,Nq,d] bf16
     float* lse;                                          // [B,Hq,Nq] or null
+    float* row_max;                                      // [B,Hq,Nq] largest raw score of each row, or null
     int B, Hq, Hkv, Nq, Nk;
     float c_log2;                                        // tau * log2(e)
 };
@@ -81,8 +82,10 @@ struct QatBwdArgs {
     const uint8_t* vc; const uint8_t* vs;                // MXFP4 V [B,H,d,N/2], E8M0 [B,H,d,N/32]
     Dense d_o;                                           // dO bf16
     const float* lse;                                    // forward log-sum-exp
+    const float* row_max;                                // forward: largest raw score of each row
     float* delta;                                        // workspace: delta' [B,H,N]
-    uint16_t* vdeq; uint16_t* qT; uint16_t* kT; uint16_t* doT;   // workspace: bf16 copies
+    uint32_t* do_amax;                                   // workspace: largest |dO| per (b, h), fp32 bits
+    uint16_t* vdeq; uint16_t* qT; uint16_t* kT; uint16_t* doT;   // workspace: bf16 copies (dO^T fp16, scaled)
     Dense dq, dk, dv;
     int B, H, N;
     float c_log2, tau;

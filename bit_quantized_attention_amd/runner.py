@@ -138,6 +138,7 @@ class QatPath:
         self.o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=dev)
         self.oa = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=dev) if aux else None
         self.lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+        self.row_max = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
         self.ws = torch.empty(max(bqa_workspace_size(p, BQA_OP_FWD), 16) if aux else 16, dtype=u8, device=dev)
         self._qd, self._kd, self._vd = dense(q), dense(k), dense(v)
         self._od = dense(self.o)
@@ -150,7 +151,7 @@ class QatPath:
 
     def forward(self):
         bqa_attn_fwd(self.p, q=self.qq, k=self.kq, v=self.vq, o=self._od, o_aux=self._oad, lse=self.lse,
-                     workspace=self.ws)
+                     row_max=self.row_max, workspace=self.ws)
 
     def step(self):
         self.quantize()
@@ -174,7 +175,8 @@ class QatTrainStep(QatPath):
         self._dod = dense(d_o)
 
     def backward(self):
-        bqa_attn_bwd(self.p, q=self.qq, k=self.kq, v=self.vq, o_for_delta=self._oad, lse=self.lse, d_o=self._dod,
+        bqa_attn_bwd(self.p, q=self.qq, k=self.kq, v=self.vq, o_for_delta=self._oad, lse=self.lse,
+                     row_max=self.row_max, d_o=self._dod,
                      dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws_bwd)
 
     def step(self):

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define BQA_ABI_VERSION 1
+#define BQA_ABI_VERSION 2
 
 typedef int32_t bqa_status;
 enum {
@@ -213,6 +213,13 @@ bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const f
  * BQA_SAGE_I8_F16PV) and, when lse is not NULL, the natural-log
  * log-sum-exp of every row, fp32 [B, Hq, Nq].
  *
+ * Every mode runs FlashAttention-2's online softmax ("ThriftAttention",
+ * Method step 2): keys are visited in tiles in a fixed order, the running
+ * row maximum m is updated per tile, P = exp(s - m) is rounded for P.V as the
+ * mode says (the row's largest P so far is 1, exactly representable in every
+ * P format), the sums gathered before are scaled by exp(m_old - m_new), and
+ * the row sum accumulates the unrounded P.
+ *
  *  - Sage modes ("SageBwd", Methodology 1): q, k are the INT8 token-block
  *    codes (k of the smoothed K); v is per-channel e4m3 (F8PV) or int8
  *    (I8PV) codes, or for F16PV v_hi holds V in fp16 and v is unused.  In
@@ -220,17 +227,16 @@ bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const f
  *    quantises Q itself, with the codes and scales bqa_quantize_blocks gives
  *    for role Q, and writes them to q's buffers when q is not NULL (q may be
  *    NULL).
- *    Keys are visited in tiles of k_block, ascending; per tile the running max
- *    is updated, P = exp(s - m) is rounded for P.V as the mode says, and the
- *    row sum accumulates the unrounded P.
+ *    Key tiles of k_block, ascending (causal: up to the row's diagonal).
  *  - BQA_QAT_MXFP4 ("Attn-QAT", §2): q, k MXFP4 along d, v MXFP4 along tokens;
- *    d = 128, non-causal, Nk a multiple of 64.  P is taken relative to a
- *    power-of-two reference point and made MXFP4 per 32 keys of the row for
- *    O (so its codes do not depend on how the keys are tiled); the row sum
- *    uses the unrounded P.  When o_aux is not NULL, O' = sum bf16(P) V / l is
- *    written too (Principle 2); this needs a workspace of
+ *    d = 128, non-causal, Nk a multiple of 64.  Key tiles of 64, ascending;
+ *    P is made MXFP4 per 32 keys of the row for O (no smoothing or two-level
+ *    step, §2 Implementation).  When o_aux is not NULL, O' = sum bf16(P) V / l
+ *    is written too (Principle 2); this needs a workspace of
  *    bqa_workspace_size(p, BQA_OP_FWD) bytes (a bf16 copy of the dequantised
- *    V), else none.
+ *    V), else none.  When row_max is not NULL it receives the largest raw
+ *    score q^.k^ (before the softmax scale) of every row, fp32 [B, Hq, Nq]:
+ *    the backward rounds P against it.
  *  - BQA_THRIFT ("ThriftAttention", Method step 2 and kernel paragraph): per
  *    query block, the unselected valid key blocks go through the FP4 path
  *    (MXFP4 q, k, v; P quantised in two levels: scaled so its row max is 6,
@@ -238,11 +244,12 @@ bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const f
  *    bqa_select_blocks) through the bf16 path (q_hi, k_hi, v_hi), all merged
  *    by one online softmax.  Nq == 1 is decode: the key range is cut into
  *    p->num_splits parts whose partial results are merged at the end.
+ * row_max is used by BQA_QAT_MXFP4 only (NULL elsewhere).
  */
 bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
                         const bqa_qtensor* v, const bqa_tensor* q_hi, const bqa_tensor* k_hi,
                         const bqa_tensor* v_hi, const int32_t* sel_idx, const int32_t* sel_cnt,
-                        bqa_tensor* o, bqa_tensor* o_aux, float* lse,
+                        bqa_tensor* o, bqa_tensor* o_aux, float* lse, float* row_max,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -257,16 +264,18 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
  *    (bf16).  Workspace: bqa_workspace_size(p, BQA_OP_BWD) bytes.
  *  - BQA_QAT_MXFP4 ("Attn-QAT", §2 Principles 1 and 2): o_for_delta = O';
  *    d = 128, Hq == Hkv, Nq == Nk a multiple of 128, non-causal.  P is
- *    recomputed from the same FP4 scores; for dV it is rounded exactly as the
- *    forward rounded it (MXFP4 per 32 keys relative to a power-of-two
- *    reference, then scaled to exp(s - L)); dS = P o (dP - delta) uses the
- *    unrounded P and is rounded to bf16; dP, dQ, dK run in bf16 against the
- *    FP4 operands; delta = rowsum(dO o O').  Workspace:
- *    bqa_workspace_size(p, BQA_OP_BWD) bytes.
+ *    recomputed from the same FP4 scores; for dV it is rounded at the
+ *    forward's precision: MXFP4 per 32 keys of exp(s - M), M the row's
+ *    maximum from the forward's row_max (required here), then scaled to
+ *    exp(s - L); dS = P o (dP - delta) uses the unrounded P and is rounded to
+ *    bf16; dP, dQ, dK run in bf16 against the FP4 operands; delta =
+ *    rowsum(dO o O').  Workspace: bqa_workspace_size(p, BQA_OP_BWD) bytes.
+ * row_max is used by BQA_QAT_MXFP4 only (NULL elsewhere).
  */
 bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
                         const bqa_qtensor* v, const bqa_tensor* v_hi,
-                        const bqa_tensor* o_for_delta, const float* lse, const bqa_tensor* d_o,
+                        const bqa_tensor* o_for_delta, const float* lse, const float* row_max,
+                        const bqa_tensor* d_o,
                         bqa_tensor* dq, bqa_tensor* dk, bqa_tensor* dv,
                         void* workspace, size_t workspace_bytes, void* stream);
 

@@ -84,8 +84,8 @@ def _declare(L):
         "orc_budget_count": (i, [i, i]),
         "orc_select_blocks": (None, [vp, vp, i, i, i, i, i, i, vp, vp]),
         "orc_thrift_fwd": (None, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i,
-                                  i, i, i, i, i, d, i, i, i, vp, vp]),
-        "orc_thrift_decode": (None, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, d,
+                                  i, i, i, i, i, i, d, i, i, i, vp, vp]),
+        "orc_thrift_decode": (None, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d,
                                      i, i, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -303,25 +303,27 @@ def select_blocks(qbar, kbar, causal: bool, budget_ppm: int, max_sel: int):
     return idx, cnt
 
 
-def thrift_fwd(*, qc, qs, kc, ks, vc_t, vs_t, Qh, Kh, Vh, sel_idx, sel_cnt, Nq, Nk, d, blk=128,
+def thrift_fwd(*, qc, qs, kc, ks, vc_t, vs_t, Qh, Kh, Vh, sel_idx, sel_cnt, Nq, Nk, d, blk=128, hp_tile=None,
                causal=True, tau, quantize=True, qblocks=None):
+    """hp_tile: keys per online-softmax tile of the bf16 path (default: the whole block)."""
     qb0, qb1 = (0, Nq // blk) if qblocks is None else qblocks
     O = np.empty(((qb1 - qb0) * blk, d)); lse = np.empty((qb1 - qb0) * blk)
     sel_idx = _c(sel_idx, np.int32)
     a = [_c(x, np.uint8) if x is not None else None for x in (qc, qs, kc, ks, vc_t, vs_t)]
     lib().orc_thrift_fwd(*[_p(x) for x in a], _p(_f32(Qh)), _p(_f32(Kh)), _p(_f32(Vh)),
                          _p(sel_idx), _p(_c(sel_cnt, np.int32)), sel_idx.shape[1], Nq, Nk, d, blk,
-                         int(causal), float(tau), int(quantize), qb0, qb1, _p(O), _p(lse))
+                         blk if hp_tile is None else hp_tile, int(causal), float(tau), int(quantize), qb0, qb1, _p(O), _p(lse))
     return O, lse
 
 
-def thrift_decode(*, qc, qs, kc, ks, vc_t, vs_t, q, Kh, Vh, sel, Nk, d, blk=128, tau, num_splits,
+def thrift_decode(*, qc, qs, kc, ks, vc_t, vs_t, q, Kh, Vh, sel, Nk, d, blk=128, hp_tile=None, tau, num_splits,
                   quantize=True):
     o = np.empty(d)
     lse = C.c_double()
     sel = _c(sel, np.int32)
     a = [_c(x, np.uint8) if x is not None else None for x in (qc, qs, kc, ks, vc_t, vs_t)]
     lib().orc_thrift_decode(*[_p(x) for x in a], _p(_f32(q)), _p(_f32(Kh)), _p(_f32(Vh)), _p(sel),
-                            len(sel), Nk, d, blk, float(tau), int(num_splits), int(quantize),
+                            len(sel), Nk, d, blk, blk if hp_tile is None else hp_tile, float(tau), int(num_splits),
+                            int(quantize),
                             _p(o), C.byref(lse))
     return o, lse.value

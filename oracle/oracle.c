@@ -937,12 +937,14 @@ static void thrift_block(const thrift_ctx* c, row_state* st, int i, int j0, int 
  * the kernel paragraph): per query block, the unselected valid key blocks
  * go through the FP4 path in ascending order, then the selected blocks
  * through the bf16 path in ascending order, all merged in one online
- * softmax.  The diagonal block is masked in whichever path takes it. */
+ * softmax.  The diagonal block is masked in whichever path takes it.  An FP4
+ * block is one tile of the online softmax (its two-level factor is per row
+ * and block); a bf16 block is visited as tiles of hp_tile keys. */
 void orc_thrift_fwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                     const uint8_t* vc_t, const uint8_t* vs_t,
                     const float* Qh, const float* Kh, const float* Vh,
                     const int32_t* sel_idx, const int32_t* sel_cnt, int max_sel,
-                    int Nq, int Nk, int d, int blk, int causal, double tau, int quantize,
+                    int Nq, int Nk, int d, int blk, int hp_tile, int causal, double tau, int quantize,
                     int qb0, int qb1, double* O, double* lse) {
     thrift_ctx c = {qc, qs, kc, ks, vc_t, vs_t, Qh, Kh, Vh, Nk, d, quantize, tau};
     int nkb = Nk / blk;
@@ -959,9 +961,12 @@ void orc_thrift_fwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, con
                     int picked = 0;
                     for (int u = 0; u < ns; ++u) if (sel[u] == J) picked = 1;
                     if (picked != pass) continue;
-                    int n = blk;
-                    if (J * blk + n - 1 > last) n = last - J * blk + 1;
-                    thrift_block(&c, &st, i, J * blk, n, pass);
+                    int tile = pass ? hp_tile : blk;
+                    for (int t0 = J * blk; t0 < (J + 1) * blk && t0 <= last; t0 += tile) {
+                        int n = tile;
+                        if (t0 + n - 1 > last) n = last - t0 + 1;
+                        thrift_block(&c, &st, i, t0, n, pass);
+                    }
                 }
             for (int k = 0; k < d; ++k) O[((size_t)(I - qb0) * blk + a) * d + k] = st.acc[k] / st.l;
             lse[(size_t)(I - qb0) * blk + a] = st.m + log(st.l);
@@ -972,13 +977,13 @@ void orc_thrift_fwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, con
 /* Thrift decode for one (batch, query head): the single query sits after
  * the whole cache, so every key is visible.  The key blocks are cut into
  * num_splits contiguous ranges [s nb/S, (s+1) nb/S); each range runs its
- * FP4 blocks, then its selected bf16 blocks, in ascending order, giving a
- * partial (m_s, l_s, acc_s); the partials are merged by
- * m = max m_s, l = sum e^(m_s - m) l_s, o = sum e^(m_s - m) acc_s / l. */
+ * FP4 blocks, then its selected bf16 blocks (as tiles of hp_tile keys), in
+ * ascending order, giving a partial (m_s, l_s, acc_s); the partials are
+ * merged by m = max m_s, l = sum e^(m_s - m) l_s, o = sum e^(m_s - m) acc_s / l. */
 void orc_thrift_decode(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                        const uint8_t* vc_t, const uint8_t* vs_t,
                        const float* q, const float* Kh, const float* Vh,
-                       const int32_t* sel, int nsel, int Nk, int d, int blk, double tau,
+                       const int32_t* sel, int nsel, int Nk, int d, int blk, int hp_tile, double tau,
                        int num_splits, int quantize, double* o, double* lse) {
     thrift_ctx c = {qc, qs, kc, ks, vc_t, vs_t, q, Kh, Vh, Nk, d, quantize, tau};
     int nb = Nk / blk;
@@ -993,7 +998,8 @@ void orc_thrift_decode(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, 
                 int picked = 0;
                 for (int u = 0; u < nsel; ++u) if (sel[u] == J) picked = 1;
                 if (picked != pass) continue;
-                thrift_block(&c, &st, 0, J * blk, blk, pass);
+                int tile = pass ? hp_tile : blk;
+                for (int t0 = J * blk; t0 < (J + 1) * blk; t0 += tile) thrift_block(&c, &st, 0, t0, tile, pass);
             }
         ms[sp] = st.m;
         ls[sp] = st.l;

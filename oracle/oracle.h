@@ -85,12 +85,12 @@ void orc_thrift_fwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, con
                     const uint8_t* vc_t, const uint8_t* vs_t,
                     const float* Qh, const float* Kh, const float* Vh,
                     const int32_t* sel_idx, const int32_t* sel_cnt, int max_sel,
-                    int Nq, int Nk, int d, int blk, int causal, double tau, int quantize,
+                    int Nq, int Nk, int d, int blk, int hp_tile, int causal, double tau, int quantize,
                     int qb0, int qb1, double* O, double* lse);
 void orc_thrift_decode(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                        const uint8_t* vc_t, const uint8_t* vs_t,
                        const float* q, const float* Kh, const float* Vh,
-                       const int32_t* sel, int nsel, int Nk, int d, int blk, double tau,
+                       const int32_t* sel, int nsel, int Nk, int d, int blk, int hp_tile, double tau,
                        int num_splits, int quantize, double* o, double* lse);
 
 #ifdef __cplusplus

@@ -38,7 +38,9 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert bqa.bqa_abi_version() == 1
+    import re
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "bqa.h")).read()
+    assert bqa.bqa_abi_version() == int(re.search(r"#define BQA_ABI_VERSION (\d+)", hdr).group(1))
     for s in range(-7, 1):
         assert isinstance(bqa.bqa_status_string(s), str) and bqa.bqa_status_string(s)
     assert bqa.bqa_status_string(-99) == "unknown status"
@@ -149,7 +151,7 @@ def test_fwd_validation(L):
     def fwd(p, q=q, k=k, v=v, o=o, v_hi=None):
         return bqa.lib().bqa_attn_fwd(C.byref(p), C.byref(q), C.byref(k), None if v is None else C.byref(v), None,
                                       None, None if v_hi is None else C.byref(v_hi), None, None,
-                                      None if o is None else C.byref(o), None, None, None, 0, None)
+                                      None if o is None else C.byref(o), None, None, None, None, 0, None)
     assert fwd(_p(k_block=32)) == bqa.BQA_E_UNSUPPORTED
     assert fwd(_p(q_block=32)) == bqa.BQA_E_UNSUPPORTED
     assert fwd(_p(causal=1, Nq=8192)) == bqa.BQA_E_SHAPE
@@ -163,7 +165,7 @@ def test_fwd_validation(L):
     def fwd_qhi(p, q=q, q_hi=_dense(ptr=0x60000)):
         return bqa.lib().bqa_attn_fwd(C.byref(p), None if q is None else C.byref(q), C.byref(k), C.byref(v),
                                       None if q_hi is None else C.byref(q_hi), None, None, None, None, C.byref(o),
-                                      None, None, None, 0, None)
+                                      None, None, None, None, 0, None)
     # Q quantised inside the kernel: fp8 P.V and bf16 only; q optional, but checked when given
     assert fwd_qhi(_p(mode=bqa.BQA_SAGE_I8_I8PV)) == bqa.BQA_E_UNSUPPORTED
     assert fwd_qhi(_p(), q_hi=_dense(ptr=0x60000, dtype=bqa.BQA_FP16)) == bqa.BQA_E_UNSUPPORTED

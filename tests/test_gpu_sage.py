@@ -157,10 +157,10 @@ def test_deterministic_and_zero_block():
 
 
 @pytest.mark.parametrize("pv", ["f8", "i8"])
-def test_score_jump_moves_the_frame(pv):
-    """Keys after the first tile score far above it (more than the 96-binade
-    frame gap, in log2 units): the kernels' rare exact rescale of the
-    accumulators runs and the result still matches the oracle."""
+def test_score_jump_rescales(pv):
+    """Keys after the first tile score far above it (more than 96 binades, in
+    log2 units): the running maximum jumps, the rescale factor of the first
+    tile's sums underflows to zero, and the result still matches the oracle."""
     import bit_quantized_attention_amd as bqa
     from bit_quantized_attention_amd.runner import SagePath, sage_problem, to_device
     rng = np.random.default_rng(41)
@@ -179,7 +179,7 @@ def test_score_jump_moves_the_frame(pv):
     torch.cuda.synchronize()
     orc = SageOracle(Q, K, V, q_block=128, pv=pv)
     ref, lse = orc.forward(0, 0, True, tau_for(d))
-    # the jump really exceeds the frame gap: log2-unit score difference across key tile 0 / 1
+    # the jump really is that large: log2-unit score difference across key tile 0 / 1
     s = (orc.qc[0].astype(np.float64) @ orc.kc[0].astype(np.float64).T) * np.repeat(orc.qs[0], 128)[:, None] \
         * np.repeat(orc.ks[0], 64)[None, :] * tau_for(d) / np.log(2)
     assert s[200, 64:128].max() - s[200, :64].max() > 96

@@ -138,7 +138,8 @@ class _ThriftOracle:
         idx, cnt = self.sel[iq]
         return orc.thrift_fwd(qc=self.qc[iq], qs=self.qs[iq], kc=self.kc[ik], ks=self.ks[ik], vc_t=self.vc[ik],
                               vs_t=self.vs[ik], Qh=self.Q[iq], Kh=self.K[ik], Vh=self.V[ik], sel_idx=idx, sel_cnt=cnt,
-                              Nq=self.Nq, Nk=self.Nk, d=self.d, blk=128, causal=self.causal, tau=tau_for(self.d),
+                              Nq=self.Nq, Nk=self.Nk, d=self.d, blk=128, hp_tile=64, causal=self.causal,
+                              tau=tau_for(self.d),
                               qblocks=qblocks)
 
 
@@ -225,7 +226,7 @@ def test_thrift_decode_small(ppm, splits):
         ridx, rcnt = orc.select_blocks(qf[bq][None], km[ik], True, ppm, ms)
         assert_same(idx[b, hq, 0], ridx[0], f"decode selection (b={b}, h={hq})")
         ref, lse = orc.thrift_decode(qc=qc[bq], qs=qs[bq], kc=kc[ik], ks=ks[ik], vc_t=vc[ik], vs_t=vs[ik], q=qf[bq],
-                                     Kh=Kf[ik], Vh=Vf[ik], sel=ridx[0, :rcnt[0]], Nk=w.Nk, d=d, blk=128,
+                                     Kh=Kf[ik], Vh=Vf[ik], sel=ridx[0, :rcnt[0]], Nk=w.Nk, d=d, blk=128, hp_tile=32,
                                      tau=tau_for(d), num_splits=S)
         compare_outputs(O[b, hq, 0], ref, "bf16", what=f"decode o (b={b}, h={hq})")
         assert abs(L[b, hq, 0] - lse) < 2e-3
@@ -256,7 +257,8 @@ def test_thrift_prefill_full_size_sampled():
         assert_same(path.sel_idx[0, h].cpu().numpy(), idx, f"selection of head {h}")
         for qb in (0, 517, 1023):
             ref, lse = orc.thrift_fwd(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0], Qh=Qh, Kh=Kh, Vh=Vh,
-                                      sel_idx=idx, sel_cnt=rc, Nq=w.Nq, Nk=w.Nk, d=w.d, blk=128, causal=True,
+                                      sel_idx=idx, sel_cnt=rc, Nq=w.Nq, Nk=w.Nk, d=w.d, blk=128, hp_tile=64,
+                                      causal=True,
                                       tau=tau_for(w.d), qblocks=(qb, qb + 1))
             compare_outputs(O[h, 128 * qb:128 * qb + 128], ref, "bf16", what=f"O[h={h}, query block {qb}]")
             assert np.abs(L[h, 128 * qb:128 * qb + 128] - lse).max() < 2e-3
@@ -290,15 +292,15 @@ def test_thrift_decode_full_size_sampled():
         ridx, rcnt = orc.select_blocks(qh, orc.block_means(Kh[None], 128)[0], True, PPM_5, 52)
         assert_same(idx[b, hq], ridx, f"decode selection (b={b}, h={hq})")
         ref, lse = orc.thrift_decode(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0], q=qh[0], Kh=Kh,
-                                     Vh=Vh, sel=ridx[0, :rcnt[0]], Nk=w.Nk, d=w.d, blk=128, tau=tau_for(w.d),
+                                     Vh=Vh, sel=ridx[0, :rcnt[0]], Nk=w.Nk, d=w.d, blk=128, hp_tile=32, tau=tau_for(w.d),
                                      num_splits=S)
         compare_outputs(O[b, hq, 0], ref, "bf16", what=f"decode o (b={b}, h={hq})")
         assert abs(L[b, hq, 0] - lse) < 2e-3
 
 
-def test_thrift_score_jump_moves_the_frame():
-    """The first key blocks score far below the later ones (more than the
-    64-binade frame gap): both the FP4 and the bf16 path move the frame."""
+def test_thrift_score_jump_rescales():
+    """The first key blocks score far below the later ones (more than 64
+    binades): the running maximum jumps in both the FP4 and the bf16 path."""
     from bit_quantized_attention_amd.runner import ThriftPath, thrift_problem, to_device
     rng = np.random.default_rng(43)
     N, d = 1024, 128
