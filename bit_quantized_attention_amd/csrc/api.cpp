@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 
 #include "bqa.h"
 #include "internal.hpp"
@@ -94,6 +95,51 @@ bqa_status launched(hipError_t e) { return e == hipSuccess ? BQA_OK : BQA_E_LAUN
         if (_s != BQA_OK) return _s;     \
     } while (0)
 
+// Validation and argument block of a ThriftAttention decode call (everything
+// but the partials buffer).
+bqa_status check_decode(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k, const bqa_qtensor* v,
+                        const bqa_tensor* q_hi, const bqa_tensor* k_hi, const bqa_tensor* v_hi,
+                        const int32_t* sel_idx, const int32_t* sel_cnt, const bqa_tensor* o, ThriftDecArgs& a) {
+    if (p->mode != BQA_THRIFT || p->Nq != 1) return BQA_E_UNSUPPORTED;
+    if (p->d != 128 || p->sel_block != 128 || p->Nk % 128 != 0) return BQA_E_UNSUPPORTED;
+    if (p->Hq / p->Hkv > 32) return BQA_E_UNSUPPORTED;
+    if (p->num_splits < 0) return BQA_E_SHAPE;
+    TRY(check_q(q, BQA_MXFP4, 0));
+    TRY(check_q(k, BQA_MXFP4, 0));
+    TRY(check_q(v, BQA_MXFP4, 1));
+    if (q->block != 32 || k->block != 32 || v->block != 32) return BQA_E_UNSUPPORTED;
+    TRY(check_dense(q_hi, false, true));
+    TRY(check_dense(k_hi, false, true));
+    TRY(check_dense(v_hi, false, true));
+    TRY(check_dense(o, false, true));
+    if (!sel_idx || !sel_cnt) return BQA_E_NULL;
+    if (p->hp_budget_ppm < 0 || p->hp_budget_ppm > 1000000) return BQA_E_SHAPE;
+    a.qc = (const uint8_t*)q->codes; a.qs = (const uint8_t*)q->scales;
+    a.kc = (const uint8_t*)k->codes; a.ks = (const uint8_t*)k->scales;
+    a.vc = (const uint8_t*)v->codes; a.vs = (const uint8_t*)v->scales;
+    a.q_hi = as_dense(q_hi); a.k_hi = as_dense(k_hi); a.v_hi = as_dense(v_hi);
+    a.sel_idx = sel_idx; a.sel_cnt = sel_cnt; a.max_sel = max_sel_of(p);
+    a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nk = p->Nk;
+    a.splits = decode_splits(p->B, p->Hkv, p->Nk, p->num_splits);
+    a.c_log2 = tau_of(p) * 1.4426950408889634f;
+    return BQA_OK;
+}
+
+// BQA_DEBUG=1: scan the call's floating-point inputs before it launches.
+DebugInput dbg16(const bqa_tensor* t, int B, int H, int N, int d) {
+    if (!t) return DebugInput{nullptr, DebugInput::BF16, 0, 0, 0, 0, 0, 0, 0, 0};
+    return DebugInput{t->data, t->dtype == BQA_FP16 ? DebugInput::F16 : DebugInput::BF16, t->stride[0], t->stride[1],
+                      t->stride[2], B, H, N, d, 0};
+}
+DebugInput dbg32(const float* p, int64_t n) { return DebugInput{p, DebugInput::F32, 0, 0, 0, 0, 0, 0, 0, n}; }
+
+bqa_status debug_check(void* stream, std::initializer_list<DebugInput> in) {
+    if (!debug_enabled()) return BQA_OK;
+    TRY(check_device());
+    const int r = debug_scan((hipStream_t)stream, in.begin(), (int)in.size());
+    return r < 0 ? BQA_E_LAUNCH : (r > 0 ? BQA_E_NONFINITE : BQA_OK);
+}
+
 }  // namespace
 
 extern "C" {
@@ -110,6 +156,7 @@ const char* bqa_status_string(bqa_status s) {
         case BQA_E_WORKSPACE: return "workspace missing or too small";
         case BQA_E_DEVICE: return "current device is not gfx950 (MI355X) or no device";
         case BQA_E_LAUNCH: return "kernel launch failed";
+        case BQA_E_NONFINITE: return "an input holds a NaN or an infinity (BQA_DEBUG=1 scan)";
         default: return "unknown status";
     }
 }
@@ -151,6 +198,7 @@ bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_ten
     TRY(check_dense(x, true, true));
     const bool f16 = x->dtype == BQA_FP16;
     hipStream_t st = (hipStream_t)stream;
+    if (out->fmt != BQA_MXFP4 && out->fmt != BQA_INT8 && out->fmt != BQA_FP8E4M3) return BQA_E_UNSUPPORTED;
     if (out->fmt == BQA_MXFP4) {
         if (role == BQA_ROLE_DO) return BQA_E_UNSUPPORTED;
         const int axis = role == BQA_ROLE_V ? 1 : 0;
@@ -160,6 +208,7 @@ bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_ten
         if (block_means && (role == BQA_ROLE_V || p->sel_block != 128)) return BQA_E_UNSUPPORTED;
         if (block_means && N > 1 && N % 128 != 0) return BQA_E_UNSUPPORTED;
         TRY(check_device());
+        TRY(debug_check(stream, {dbg16(x, p->B, H, N, d)}));
         return launched(launch_quant_mx(as_dense(x), f16, p->B, H, N, d, axis, (uint8_t*)out->codes,
                                         (uint8_t*)out->scales, block_means, st));
     }
@@ -170,6 +219,7 @@ bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_ten
         const size_t need = ws_chan_bytes(p->B * H, N, d);
         if (!ws || ws_bytes < need) return BQA_E_WORKSPACE;
         TRY(check_device());
+        TRY(debug_check(stream, {dbg16(x, p->B, H, N, d)}));
         return launched(launch_quant_chan(as_dense(x), f16, p->B, H, N, d, out->fmt == BQA_INT8 ? 0 : 1,
                                           (uint8_t*)out->codes, (float*)out->scales, ws, st));
     }
@@ -185,6 +235,7 @@ bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_ten
         if (!std::isfinite(p->smooth_eps)) return BQA_E_SHAPE;
     }
     TRY(check_device());
+    TRY(debug_check(stream, {dbg16(x, p->B, H, N, d)}));
     return launched(launch_quant_i8_tokblock(as_dense(x), f16, p->B, H, N, d, blk, smooth, (double)p->smooth_eps,
                                              k_mean, ws, (int8_t*)out->codes, (float*)out->scales, st));
 }
@@ -207,6 +258,7 @@ bqa_status bqa_quantize_kv(const bqa_problem* p, const bqa_tensor* k, const bqa_
     if (!aligned16(ws)) return BQA_E_ALIGN;
     if (p->smooth_k && !std::isfinite(p->smooth_eps)) return BQA_E_SHAPE;
     TRY(check_device());
+    TRY(debug_check(stream, {dbg16(k, p->B, p->Hkv, p->Nk, p->d), dbg16(v, p->B, p->Hkv, p->Nk, p->d)}));
     return launched(launch_quant_kv(as_dense(k), as_dense(v), k->dtype == BQA_FP16, p->B, p->Hkv, p->Nk, p->d,
                                     p->smooth_k != 0, (double)p->smooth_eps, k_mean, (int8_t*)kq->codes,
                                     (float*)kq->scales, vfmt == BQA_INT8 ? 0 : 1, (uint8_t*)vq->codes,
@@ -220,12 +272,16 @@ bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const f
     if (p->mode != BQA_THRIFT || p->sel_block != 128) return BQA_E_UNSUPPORTED;
     if (!q_means || !k_means || !sel_idx || !sel_cnt) return BQA_E_NULL;
     if (p->Nk % p->sel_block != 0) return BQA_E_UNSUPPORTED;
+    // causal prefill: the block-level mask assumes whole query blocks
+    if (p->causal && p->Nq > 1 && p->Nq % p->sel_block != 0) return BQA_E_UNSUPPORTED;
     if (p->hp_budget_ppm < 0 || p->hp_budget_ppm > 1000000) return BQA_E_SHAPE;
     const int nkb = p->Nk / p->sel_block, nqb = (p->Nq + p->sel_block - 1) / p->sel_block;
     if (nkb > 4096) return BQA_E_UNSUPPORTED;
     if (!aligned16(k_means) || ((uintptr_t)q_means & 3u) || ((uintptr_t)sel_idx & 3u) || ((uintptr_t)sel_cnt & 3u))
         return BQA_E_ALIGN;
     TRY(check_device());
+    TRY(debug_check(stream, {dbg32(q_means, (int64_t)p->B * p->Hq * nqb * p->d),
+                             dbg32(k_means, (int64_t)p->B * p->Hkv * nkb * p->d)}));
     return launched(launch_select(q_means, k_means, p->B, p->Hq, p->Hkv, nqb, nkb, p->d, p->causal,
                                   p->hp_budget_ppm, max_sel_of(p), sel_idx, sel_cnt, (hipStream_t)stream));
 }
@@ -237,6 +293,11 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
     (void)q_hi; (void)k_hi; (void)sel_idx; (void)sel_cnt;
     TRY(check_problem(p));
     hipStream_t st = (hipStream_t)stream;
+    // BQA_DEBUG=1 (after each mode's validation): the bf16 / fp16 inputs the mode reads
+    auto dbg_fwd = [&]() {
+        return debug_check(stream, {dbg16(q_hi, p->B, p->Hq, p->Nq, p->d), dbg16(k_hi, p->B, p->Hkv, p->Nk, p->d),
+                                    dbg16(v_hi, p->B, p->Hkv, p->Nk, p->d)});
+    };
     if (p->mode == BQA_QAT_MXFP4) {
         if (p->d != 128 || p->causal || p->Nk % 64 != 0) return BQA_E_UNSUPPORTED;
         TRY(check_q(q, BQA_MXFP4, 0));
@@ -259,39 +320,22 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
         a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk;
         a.c_log2 = tau_of(p) * 1.4426950408889634f;
         TRY(check_device());
+        TRY(dbg_fwd());
         return launched(launch_qat_fwd(a, st));
     }
     if (p->mode == BQA_THRIFT && p->Nq == 1) {
-        if (p->d != 128 || p->sel_block != 128 || p->Nk % 128 != 0) return BQA_E_UNSUPPORTED;
-        if (p->Hq / p->Hkv > 32) return BQA_E_UNSUPPORTED;
-        if (p->num_splits < 0) return BQA_E_SHAPE;
-        TRY(check_q(q, BQA_MXFP4, 0));
-        TRY(check_q(k, BQA_MXFP4, 0));
-        TRY(check_q(v, BQA_MXFP4, 1));
-        if (q->block != 32 || k->block != 32 || v->block != 32) return BQA_E_UNSUPPORTED;
-        TRY(check_dense(q_hi, false, true));
-        TRY(check_dense(k_hi, false, true));
-        TRY(check_dense(v_hi, false, true));
-        TRY(check_dense(o, false, true));
-        if (!sel_idx || !sel_cnt) return BQA_E_NULL;
-        if (p->hp_budget_ppm < 0 || p->hp_budget_ppm > 1000000) return BQA_E_SHAPE;
+        ThriftDecArgs a{};
+        TRY(check_decode(p, q, k, v, q_hi, k_hi, v_hi, sel_idx, sel_cnt, o, a));
         if (!ws || ws_bytes < ws_decode_bytes(p->B, p->Hq, p->Hkv, p->Nk, p->num_splits)) return BQA_E_WORKSPACE;
         if (!aligned16(ws)) return BQA_E_ALIGN;
-        ThriftDecArgs a{};
-        a.qc = (const uint8_t*)q->codes; a.qs = (const uint8_t*)q->scales;
-        a.kc = (const uint8_t*)k->codes; a.ks = (const uint8_t*)k->scales;
-        a.vc = (const uint8_t*)v->codes; a.vs = (const uint8_t*)v->scales;
-        a.q_hi = as_dense(q_hi); a.k_hi = as_dense(k_hi); a.v_hi = as_dense(v_hi);
-        a.sel_idx = sel_idx; a.sel_cnt = sel_cnt; a.max_sel = max_sel_of(p);
         a.part = (float*)ws;
-        a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nk = p->Nk;
-        a.splits = decode_splits(p->B, p->Hkv, p->Nk, p->num_splits);
-        a.c_log2 = tau_of(p) * 1.4426950408889634f;
         TRY(check_device());
+        TRY(dbg_fwd());
         return launched(launch_thrift_decode(a, as_dense(o), lse, st));
     }
     if (p->mode == BQA_THRIFT && p->Nq > 1) {
         if (p->d != 128 || p->sel_block != 128 || p->Nk % 128 != 0) return BQA_E_UNSUPPORTED;
+        if (p->causal && p->Nq % 128 != 0) return BQA_E_UNSUPPORTED;   // selection is per whole query block
         TRY(check_q(q, BQA_MXFP4, 0));
         TRY(check_q(k, BQA_MXFP4, 0));
         TRY(check_q(v, BQA_MXFP4, 1));
@@ -312,6 +356,7 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
         a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk; a.causal = p->causal;
         a.c_log2 = tau_of(p) * 1.4426950408889634f;
         TRY(check_device());
+        TRY(dbg_fwd());
         return launched(launch_thrift_fwd(a, st));
     }
     if (is_sage(p->mode)) {
@@ -355,6 +400,7 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
         a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk; a.causal = p->causal;
         a.c_log2 = tau_of(p) * 1.4426950408889634f;
         TRY(check_device());
+        TRY(dbg_fwd());
         return launched(launch_sage_fwd(a, pv, p->d, st));
     }
     return BQA_E_UNSUPPORTED;
@@ -391,6 +437,9 @@ bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
         a.tau = tau_of(p);
         a.c_log2 = a.tau * 1.4426950408889634f;
         TRY(check_device());
+        const int64_t bhn = (int64_t)p->B * p->Hq * p->Nq;
+        TRY(debug_check(stream, {dbg16(v_hi, p->B, p->Hq, p->Nq, p->d), dbg16(o_for_delta, p->B, p->Hq, p->Nq, p->d),
+                                 dbg16(d_o, p->B, p->Hq, p->Nq, p->d), dbg32(lse, bhn)}));
         return launched(launch_sage_bwd(a, as_dense(o_for_delta), ws, st));
     }
     if (p->mode == BQA_QAT_MXFP4) {
@@ -418,6 +467,9 @@ bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
         a.tau = tau_of(p);
         a.c_log2 = a.tau * 1.4426950408889634f;
         TRY(check_device());
+        const int64_t bhn = (int64_t)p->B * p->Hq * p->Nq;
+        TRY(debug_check(stream, {dbg16(o_for_delta, p->B, p->Hq, p->Nq, p->d), dbg16(d_o, p->B, p->Hq, p->Nq, p->d),
+                                 dbg32(lse, bhn), dbg32(row_max, bhn)}));
         return launched(launch_qat_bwd(a, as_dense(o_for_delta), ws, st));
     }
     return BQA_E_UNSUPPORTED;
@@ -459,3 +511,13 @@ bqa_status bqa_debug_qk_scores(const bqa_problem* p, const bqa_qtensor* q, const
 }
 
 }  // extern "C"
+
+extern "C" bqa_status bqa_debug_mx_dequant(const void* codes, const void* scales, int64_t nblocks, void* out,
+                                           void* stream) {
+    if (!codes || !scales || !out) return BQA_E_NULL;
+    if (nblocks < 0 || nblocks > ((int64_t)1 << 31)) return BQA_E_SHAPE;
+    if (!aligned16(codes) || !aligned16(out)) return BQA_E_ALIGN;
+    TRY(check_device());
+    return launched(launch_mx_dequant((const uint8_t*)codes, (const uint8_t*)scales, nblocks, (uint16_t*)out,
+                                      (hipStream_t)stream));
+}

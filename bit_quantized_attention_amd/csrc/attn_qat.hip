@@ -158,8 +158,9 @@ __global__ __launch_bounds__(256, 2) void qat_fwd_kernel(QatFwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    auto body = [&](int j, auto bufc) __attribute__((always_inline)) {
-        constexpr int B0 = decltype(bufc)::value;
+    // one copy of the tile code (the LDS buffer index is a run-time value): two
+    // copies, one per buffer, cost the allocator 60 registers and spilled
+    auto body = [&](int j, int B0) __attribute__((always_inline)) {
         uint32_t vs_next = 0;
         if (j + 1 < n_tiles) vs_next = tile_issue<AUX>(a, bhk, (j + 1) * BN, lds[B0 ^ 1], w, l, tid);
         const Lds& L = lds[B0];
@@ -250,11 +251,8 @@ __global__ __launch_bounds__(256, 2) void qat_fwd_kernel(QatFwdArgs a) {
         __builtin_amdgcn_s_waitcnt(0);   // the tile copies have landed
         __syncthreads();
     };
-    for (int j = 0; j < n_tiles; j += 2) {
-        body(j, std::integral_constant<int, 0>{});
-        if (j + 1 >= n_tiles) break;
-        body(j + 1, std::integral_constant<int, 1>{});
-    }
+#pragma unroll 1
+    for (int j = 0; j < n_tiles; ++j) body(j, j & 1);
 
     const float l_tot = l_run + partner32f(l_run);
     if (!row_ok) return;
@@ -343,6 +341,12 @@ hipError_t launch_qat_fwd(const QatFwdArgs& a, hipStream_t st) {
 }
 
 size_t ws_qat_fwd_bytes(int B, int Hkv, int Nk, int d) { return (size_t)B * Hkv * Nk * d * 2; }
+
+hipError_t launch_mx_dequant(const uint8_t* codes, const uint8_t* scales, int64_t nblocks, uint16_t* out,
+                             hipStream_t st) {
+    if (nblocks > 0) vdeq_kernel<<<(unsigned)((nblocks + 255) / 256), 256, 0, st>>>(codes, scales, nblocks, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_debug_scores_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                                   float* out, hipStream_t st) {

@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import sys
 
@@ -17,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libbqa.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "quant.hip", "attn_sage_fwd.hip", "attn_qat.hip", "select.hip", "attn_thrift.hip", "attn_sage_bwd.hip", "attn_qat_bwd.hip"]
+SOURCES = ["api.cpp", "quant.hip", "attn_sage_fwd.hip", "attn_qat.hip", "select.hip", "attn_thrift.hip", "attn_sage_bwd.hip", "attn_qat_bwd.hip", "debug.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -37,10 +38,22 @@ EXTRA = {"attn_thrift.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip" if src.endswith(".hip") else "hip", "-c",
-           os.path.join(HERE, src), "-o", obj]
+           os.path.join(HERE, src), "-o", obj, "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    # A kernel that spills registers to scratch memory runs several times
+    # slower; refuse to build one (BQA_ALLOW_SCRATCH=1 overrides).
+    spills, name = [], None
+    for line in r.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0 and name:
+            spills.append(f"{name}: {m.group(1)} bytes/lane")
+    if spills and os.environ.get("BQA_ALLOW_SCRATCH") != "1":
+        raise RuntimeError(f"{src}: kernels use scratch memory (register spills):\n  " + "\n  ".join(spills))
     return obj
 
 

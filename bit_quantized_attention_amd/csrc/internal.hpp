@@ -56,6 +56,9 @@ struct QatFwdArgs {
     float c_log2;                                        // tau * log2(e)
 };
 size_t ws_qat_fwd_bytes(int B, int Hkv, int Nk, int d);
+// MXFP4 blocks (16 code bytes + 1 E8M0 byte each) -> 32 bf16 values each (the conversion of deq(V))
+hipError_t launch_mx_dequant(const uint8_t* codes, const uint8_t* scales, int64_t nblocks, uint16_t* out,
+                             hipStream_t st);
 hipError_t launch_qat_fwd(const QatFwdArgs& a, hipStream_t st);
 hipError_t launch_debug_scores_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                                   float* out, hipStream_t st);
@@ -129,5 +132,17 @@ int select_sort_len(int nkb);
 hipError_t launch_select(const float* qbar, const float* kbar, int B, int Hq, int Hkv, int nqb, int nkb, int d,
                          int causal, int budget_ppm, int max_sel, int32_t* sel_idx, int32_t* sel_cnt,
                          hipStream_t st);
+
+// ---- BQA_DEBUG=1 input scan (debug.hip)
+struct DebugInput {
+    enum Kind { BF16 = 0, F16 = 1, F32 = 2 };
+    const void* p;        // null: skipped
+    int kind;
+    int64_t sB, sH, sN;   // 16-bit [B, H, N, d] views: element strides
+    int B, H, N, d;
+    int64_t n;            // fp32 arrays: element count
+};
+bool debug_enabled();
+int debug_scan(hipStream_t st, const DebugInput* in, int n_in);   // 1 found, 0 clean, -1 HIP error
 
 }  // namespace bqa

@@ -59,7 +59,8 @@ enum {
     BQA_E_ALIGN = -4,         /* misaligned pointer or stride, or inner stride != 1 */
     BQA_E_WORKSPACE = -5,     /* workspace pointer NULL or smaller than bqa_workspace_size() */
     BQA_E_DEVICE = -6,        /* the current device is not gfx950, or no device */
-    BQA_E_LAUNCH = -7         /* a kernel launch reported an error */
+    BQA_E_LAUNCH = -7,        /* a kernel launch reported an error */
+    BQA_E_NONFINITE = -8      /* BQA_DEBUG=1: an input holds a NaN or an infinity */
 };
 
 typedef enum {
@@ -202,7 +203,9 @@ bqa_status bqa_quantize_kv(const bqa_problem* p, const bqa_tensor* k, const bqa_
  * sel_idx [B, Hq, nqb, max_sel] in ascending order, unused slots -1, and k_i
  * to sel_cnt [B, Hq, nqb].  q_means [B, Hq, nqb, d], k_means [B, Hkv, nkb, d]
  * are fp32 block means; nqb = ceil(Nq / sel_block) (a decode query is its own
- * block), nkb = Nk / sel_block; max_sel = max(1, ceil(nkb * budget)).
+ * block), nkb = Nk / sel_block; max_sel = max(1, ceil(nkb * budget)).  A
+ * causal prefill needs Nq a multiple of sel_block (BQA_E_UNSUPPORTED
+ * otherwise): the block-level mask is defined for whole query blocks.
  */
 bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const float* k_means,
                              int32_t* sel_idx, int32_t* sel_cnt,
@@ -289,6 +292,16 @@ bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
 bqa_status bqa_debug_qk_scores(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
                                int32_t b, int32_t h, int32_t q_tile, int32_t k_tile, void* out,
                                void* stream);
+
+/*
+ * Test hook: the MXFP4 -> bf16 conversion that the Attn-QAT forward uses for
+ * the bf16 copy of deq(V) behind O' and the backward for its bf16 operands
+ * ("Attn-QAT", §2 Principle 2): nblocks blocks of 32 e2m1 values (16 code
+ * bytes each, low nibble first, 16-byte aligned) with one E8M0 byte each
+ * (scales[i]) to 32 bf16 values each (out, 16-byte aligned).  Every e2m1
+ * value times 2^e that is a finite bf16 value is exact.
+ */
+bqa_status bqa_debug_mx_dequant(const void* codes, const void* scales, int64_t nblocks, void* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -188,3 +188,53 @@ def test_debug_scores_validation(L):
     assert f(C.byref(_p()), C.byref(q), C.byref(k), 2, 0, 0, 0, 0x1000, None) == bqa.BQA_E_SHAPE
     assert f(C.byref(_p()), C.byref(q), C.byref(k), 0, 0, 128, 0, 0x1000, None) == bqa.BQA_E_SHAPE
     assert f(C.byref(_p()), C.byref(q), C.byref(k), 0, 0, 0, -1, 0x1000, None) == bqa.BQA_E_SHAPE
+
+
+def _nodev(st):
+    """A call with valid arguments stops at the device check without a GPU."""
+    import torch
+    return torch.cuda.is_available() or st == bqa.BQA_E_DEVICE
+
+
+def test_bwd_validation(L):
+    g = _dense()
+    q, k = _q(), _q(block=64)
+
+    def bwd(p, q=q, k=k, v=None, v_hi=g, o=g, lse=0x50000, row_max=None, d_o=g, dq=g, ws=0x40000, wsb=1 << 34):
+        return bqa.lib().bqa_attn_bwd(C.byref(p), None if q is None else C.byref(q), C.byref(k),
+                                      None if v is None else C.byref(v), None if v_hi is None else C.byref(v_hi),
+                                      C.byref(o), lse, row_max, C.byref(d_o), None if dq is None else C.byref(dq),
+                                      C.byref(g), C.byref(g), ws, wsb, None)
+    sage = dict(mode=bqa.BQA_SAGE_I8_I8PV, Nq=4096, Nk=4096)
+    assert bwd(_p(d=64, **sage)) == bqa.BQA_E_UNSUPPORTED
+    assert bwd(_p(Hkv=8, **sage)) == bqa.BQA_E_SHAPE or bwd(_p(Hkv=8, **sage)) == bqa.BQA_E_UNSUPPORTED
+    assert bwd(_p(mode=bqa.BQA_SAGE_I8_I8PV, Nq=2048, Nk=4096)) == bqa.BQA_E_UNSUPPORTED
+    assert bwd(_p(**sage), lse=None) == bqa.BQA_E_NULL
+    assert bwd(_p(**sage), dq=None) == bqa.BQA_E_NULL
+    assert bwd(_p(**sage), q=None) == bqa.BQA_E_NULL
+    assert bwd(_p(**sage), wsb=16) == bqa.BQA_E_WORKSPACE
+    assert bwd(_p(**sage), lse=0x50004) == bqa.BQA_E_ALIGN
+    assert _nodev(bwd(_p(**sage)))
+    mx = dict(mode=bqa.BQA_QAT_MXFP4, causal=0, Nq=4096, Nk=4096)
+    qm, km, vm = _q(fmt=bqa.BQA_MXFP4, block=32), _q(fmt=bqa.BQA_MXFP4, block=32), _q(fmt=bqa.BQA_MXFP4, axis=1, block=32)
+    assert bwd(_p(**mx), q=qm, k=km, v=vm, row_max=None) == bqa.BQA_E_NULL          # Attn-QAT needs row_max
+    assert bwd(_p(**dict(mx, causal=1)), q=qm, k=km, v=vm, row_max=0x60000) == bqa.BQA_E_UNSUPPORTED
+    assert bwd(_p(**mx), q=qm, k=km, v=vm, row_max=0x60008) == bqa.BQA_E_ALIGN
+    assert _nodev(bwd(_p(**mx), q=qm, k=km, v=vm, row_max=0x60000))
+
+
+def test_select_validation(L):
+    def sel(p, qm=0x10000, km=0x20000, idx=0x30000, cnt=0x40000):
+        return bqa.lib().bqa_select_blocks(C.byref(p), qm, km, idx, cnt, None, 0, None)
+    th = dict(mode=bqa.BQA_THRIFT, Hq=32, Hkv=8, Nq=131072, Nk=131072, hp_budget_ppm=50_000, sel_block=128)
+    assert sel(_p(**dict(th, mode=bqa.BQA_QAT_MXFP4))) == bqa.BQA_E_UNSUPPORTED
+    assert sel(_p(**dict(th, sel_block=64))) == bqa.BQA_E_UNSUPPORTED
+    assert sel(_p(**th), km=None) == bqa.BQA_E_NULL
+    assert sel(_p(**th), cnt=None) == bqa.BQA_E_NULL
+    assert sel(_p(**dict(th, hp_budget_ppm=1_000_001))) == bqa.BQA_E_SHAPE
+    assert sel(_p(**dict(th, Nk=131072 - 64, Nq=131072 - 64))) == bqa.BQA_E_UNSUPPORTED
+    assert sel(_p(**dict(th, Nq=200, Nk=1024))) == bqa.BQA_E_UNSUPPORTED         # ragged causal query blocks
+    assert sel(_p(**th), km=0x20004) == bqa.BQA_E_ALIGN
+    assert _nodev(sel(_p(**th)))
+    assert _nodev(sel(_p(**dict(th, Nq=1, Nk=1024))))                             # decode: one query, any length
+    assert _nodev(sel(_p(**dict(th, causal=0, Nq=200, Nk=1024))))
