@@ -15,7 +15,8 @@ import os
 __all__ = [
     "BQA_OK", "BqaError", "bqa_problem", "bqa_tensor", "bqa_qtensor", "lib", "problem",
     "bqa_abi_version", "bqa_status_string", "bqa_workspace_size", "bqa_quantize_blocks", "bqa_quantize_kv",
-    "bqa_select_blocks", "bqa_attn_fwd", "bqa_attn_bwd", "bqa_debug_qk_scores", "bqa_debug_mx_dequant",
+    "bqa_select_blocks", "bqa_attn_fwd", "bqa_attn_bwd", "bqa_debug_qk_scores", "bqa_attn_decode_static",
+    "bqa_debug_mx_dequant",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -23,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libbqa.so")
 
 BQA_OK, BQA_E_NULL, BQA_E_SHAPE, BQA_E_UNSUPPORTED, BQA_E_ALIGN, BQA_E_WORKSPACE, BQA_E_DEVICE, BQA_E_LAUNCH = \
     0, -1, -2, -3, -4, -5, -6, -7
-BQA_E_NONFINITE = -8
+BQA_E_NONFINITE, BQA_E_TOO_LARGE = -8, -9
 BQA_BF16, BQA_FP16, BQA_INT8, BQA_FP8E4M3, BQA_MXFP4 = range(5)
 BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV, BQA_SAGE_I8_I8PV, BQA_QAT_MXFP4, BQA_THRIFT = range(5)
 BQA_ROLE_Q, BQA_ROLE_K, BQA_ROLE_V, BQA_ROLE_DO = range(4)
@@ -31,7 +32,7 @@ BQA_OP_QUANTIZE_Q, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_V, BQA_OP_QUANTIZE_DO, BQA
     BQA_OP_BWD, BQA_OP_QUANTIZE_KV = range(8)
 
 EXPORTS = ["bqa_abi_version", "bqa_status_string", "bqa_workspace_size", "bqa_quantize_blocks", "bqa_quantize_kv",
-           "bqa_select_blocks", "bqa_attn_fwd", "bqa_attn_bwd", "bqa_debug_qk_scores",
+           "bqa_select_blocks", "bqa_attn_fwd", "bqa_attn_bwd", "bqa_debug_qk_scores", "bqa_attn_decode_static",
            "bqa_debug_mx_dequant"]
 
 
@@ -92,6 +93,10 @@ def lib():
         L.bqa_attn_bwd.argtypes = [P(bqa_problem), P(bqa_qtensor), P(bqa_qtensor), P(bqa_qtensor), P(bqa_tensor),
                                    P(bqa_tensor), vp, vp, P(bqa_tensor), P(bqa_tensor), P(bqa_tensor), P(bqa_tensor),
                                    vp, C.c_size_t, vp]
+        L.bqa_attn_decode_static.restype = C.c_int32
+        L.bqa_attn_decode_static.argtypes = [P(bqa_problem), P(bqa_qtensor), P(bqa_qtensor), P(bqa_qtensor),
+                                             P(bqa_tensor), P(bqa_tensor), P(bqa_tensor), vp, vp, P(bqa_tensor), vp,
+                                             vp]
         L.bqa_debug_mx_dequant.restype = C.c_int32
         L.bqa_debug_mx_dequant.argtypes = [vp, vp, C.c_int64, vp, vp]
         L.bqa_debug_qk_scores.restype = C.c_int32
@@ -245,6 +250,18 @@ def bqa_attn_bwd(p, q=None, k=None, v=None, v_hi=None, o_for_delta=None, lse=Non
                            _stream(stream))
     if check:
         _check(s, "bqa_attn_bwd")
+    return s
+
+
+def bqa_attn_decode_static(p, q=None, k=None, v=None, q_hi=None, k_hi=None, v_hi=None, sel_idx=None, sel_cnt=None,
+                           o=None, lse=None, stream=None, check=True) -> int:
+    def dd(t):
+        return t if (t is None or isinstance(t, bqa_tensor)) else dense(t)
+    s = lib().bqa_attn_decode_static(C.byref(p), _ref(q), _ref(k), _ref(v), _ref(dd(q_hi)), _ref(dd(k_hi)),
+                                     _ref(dd(v_hi)), _ptr(sel_idx), _ptr(sel_cnt), _ref(dd(o)), _ptr(lse),
+                                     _stream(stream))
+    if check:
+        _check(s, "bqa_attn_decode_static")
     return s
 
 

@@ -157,6 +157,7 @@ const char* bqa_status_string(bqa_status s) {
         case BQA_E_DEVICE: return "current device is not gfx950 (MI355X) or no device";
         case BQA_E_LAUNCH: return "kernel launch failed";
         case BQA_E_NONFINITE: return "an input holds a NaN or an infinity (BQA_DEBUG=1 scan)";
+        case BQA_E_TOO_LARGE: return "request exceeds the static scratch of the allocation-free entry point";
         default: return "unknown status";
     }
 }
@@ -404,6 +405,23 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
         return launched(launch_sage_fwd(a, pv, p->d, st));
     }
     return BQA_E_UNSUPPORTED;
+}
+
+bqa_status bqa_attn_decode_static(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
+                                  const bqa_qtensor* v, const bqa_tensor* q_hi, const bqa_tensor* k_hi,
+                                  const bqa_tensor* v_hi, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                  bqa_tensor* o, float* lse, void* stream) {
+    TRY(check_problem(p));
+    ThriftDecArgs a{};
+    TRY(check_decode(p, q, k, v, q_hi, k_hi, v_hi, sel_idx, sel_cnt, o, a));
+    if (ws_decode_bytes(p->B, p->Hq, p->Hkv, p->Nk, p->num_splits) > decode_scratch_bytes()) return BQA_E_TOO_LARGE;
+    TRY(check_device());
+    TRY(debug_check(stream, {dbg16(q_hi, p->B, p->Hq, 1, p->d), dbg16(k_hi, p->B, p->Hkv, p->Nk, p->d),
+                             dbg16(v_hi, p->B, p->Hkv, p->Nk, p->d)}));
+    float* part = nullptr;
+    if (decode_scratch(&part) != hipSuccess) return BQA_E_DEVICE;
+    a.part = part;
+    return launched(launch_thrift_decode(a, as_dense(o), lse, (hipStream_t)stream));
 }
 
 bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k, const bqa_qtensor* v,

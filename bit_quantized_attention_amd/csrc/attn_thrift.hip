@@ -20,6 +20,8 @@
 // whose largest P is below 2^-64 adds nothing (as one whose P all underflow):
 // its share of O is below 2^-64 of the row's, and the unit change would leave
 // fp32's range.
+#include <mutex>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -739,6 +741,39 @@ int decode_splits(int B, int Hkv, int Nk, int requested) {
 
 size_t ws_decode_bytes(int B, int Hq, int Hkv, int Nk, int requested) {
     return (size_t)B * Hq * decode_splits(B, Hkv, Nk, requested) * PART * sizeof(float);
+}
+
+// ---- allocation-free decode: the split partials in a static device array
+// Callers that cannot allocate (code under graph capture, serving loops)
+// get the partials from this array instead of a workspace.  Each device
+// holds its own copy for the life of the process; every call on a device
+// shares it, so calls that overlap on one device race.  Every split writes
+// its whole record before the merge reads it, so nothing needs clearing.
+namespace {
+constexpr size_t kScratchFloats = (size_t)4 << 20;    // 16 MiB
+__device__ __attribute__((aligned(256))) float scratch[kScratchFloats];
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+size_t decode_scratch_bytes() { return kScratchFloats * sizeof(float); }
+
+// Device address of this device's copy of `scratch` (looked up once per device).
+hipError_t decode_scratch(float** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = (float*)ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_thrift_decode(const ThriftDecArgs& a, Dense o, float* lse, hipStream_t st) {

@@ -126,6 +126,8 @@ struct ThriftDecArgs {
 int decode_splits(int B, int Hkv, int Nk, int requested);
 size_t ws_decode_bytes(int B, int Hq, int Hkv, int Nk, int requested);
 hipError_t launch_thrift_decode(const ThriftDecArgs& a, Dense o, float* lse, hipStream_t st);
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(float** out);    // this device's static partials array
 
 // ---- ThriftAttention block selection (select.hip)
 int select_sort_len(int nkb);

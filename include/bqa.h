@@ -60,7 +60,8 @@ enum {
     BQA_E_WORKSPACE = -5,     /* workspace pointer NULL or smaller than bqa_workspace_size() */
     BQA_E_DEVICE = -6,        /* the current device is not gfx950, or no device */
     BQA_E_LAUNCH = -7,        /* a kernel launch reported an error */
-    BQA_E_NONFINITE = -8      /* BQA_DEBUG=1: an input holds a NaN or an infinity */
+    BQA_E_NONFINITE = -8,     /* BQA_DEBUG=1: an input holds a NaN or an infinity */
+    BQA_E_TOO_LARGE = -9      /* bqa_attn_decode_static: the partials exceed its static scratch */
 };
 
 typedef enum {
@@ -254,6 +255,23 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
                         const bqa_tensor* v_hi, const int32_t* sel_idx, const int32_t* sel_cnt,
                         bqa_tensor* o, bqa_tensor* o_aux, float* lse, float* row_max,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ThriftAttention decode for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and arguments as bqa_attn_fwd in BQA_THRIFT mode with
+ * Nq == 1, without a workspace.  The per-split partial results live in a
+ * static 16 MiB device array of the library (one per device, held until the
+ * process ends); calls that would need more, B * Hq * splits * (d + 4) * 4
+ * bytes > 16 MiB, return BQA_E_TOO_LARGE and launch nothing.  Every call on
+ * a device shares that array: calls that overlap on one device (several
+ * streams or host threads) race and must be serialised by the caller.  No
+ * memory is allocated or freed by this call.
+ */
+bqa_status bqa_attn_decode_static(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
+                                  const bqa_qtensor* v, const bqa_tensor* q_hi, const bqa_tensor* k_hi,
+                                  const bqa_tensor* v_hi, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                  bqa_tensor* o, float* lse, void* stream);
 
 /*
  * Attention backward: dq, dk, dv [B, H, N, d] bf16 from the forward's codes,

@@ -238,3 +238,18 @@ def test_select_validation(L):
     assert _nodev(sel(_p(**th)))
     assert _nodev(sel(_p(**dict(th, Nq=1, Nk=1024))))                             # decode: one query, any length
     assert _nodev(sel(_p(**dict(th, causal=0, Nq=200, Nk=1024))))
+
+
+def test_decode_static_validation(L):
+    d = _dense()
+    qm, km, vm = _q(fmt=bqa.BQA_MXFP4, block=32), _q(fmt=bqa.BQA_MXFP4, block=32), _q(fmt=bqa.BQA_MXFP4, axis=1, block=32)
+
+    def dec(p, idx=0x30000):
+        return bqa.lib().bqa_attn_decode_static(C.byref(p), C.byref(qm), C.byref(km), C.byref(vm), C.byref(d),
+                                                C.byref(d), C.byref(d), idx, 0x40000, C.byref(d), None, None)
+    th = dict(mode=bqa.BQA_THRIFT, B=16, Hq=32, Hkv=8, Nq=1, Nk=131072, hp_budget_ppm=50_000, sel_block=128)
+    assert dec(_p(**dict(th, Nq=128, Nk=1024))) == bqa.BQA_E_UNSUPPORTED
+    assert dec(_p(**th), idx=None) == bqa.BQA_E_NULL
+    # 64 batches x 32 heads x 128 splits x 132 floats = 138 MB of partials > the 16 MiB static array
+    assert dec(_p(**dict(th, B=64, num_splits=128))) == bqa.BQA_E_TOO_LARGE
+    assert _nodev(dec(_p(**th)))                                                  # c5d: 4.3 MB of partials
