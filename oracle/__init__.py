@@ -87,6 +87,7 @@ def _declare(L):
                                   i, i, i, i, i, i, d, i, i, i, vp, vp]),
         "orc_thrift_decode": (None, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d,
                                      i, i, vp, vp]),
+        "orc_ptq_fwd": (None, [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -195,6 +196,35 @@ def quant_mx_cols(X: np.ndarray):
     scales = np.empty((BH, d, N // 32), np.uint8)
     lib().orc_quant_mx_cols(_p(X), BH, N, d, _p(codes), _p(scales))
     return codes, scales
+
+
+def smooth_q_blocks(Q: np.ndarray, blk: int = 128):
+    """Query smoothing of the post-training FP4 baseline ("Attn-QAT"
+    technical summary §1: the SageAttention3-style method smooths Q and K):
+    per block of `blk` rows (the last block may be short) the mean of its
+    rows, summed in fp64 and rounded to fp32 as the block means of
+    block_means are, then rounded to bf16: qbar [BH, nqb, d] (bf16 values
+    held as fp32).  Returns (qbar, Q_s) with Q_s = fp32(Q - qbar) row by row."""
+    Q = _f32(Q)
+    BH, N, d = Q.shape
+    nqb = (N + blk - 1) // blk
+    qbar = np.empty((BH, nqb, d), np.float32)
+    for I in range(nqb):
+        rows = Q[:, I * blk:(I + 1) * blk].astype(np.float64)
+        s = np.zeros((BH, d))
+        for t in range(rows.shape[1]):           # token order
+            s += rows[:, t]
+        qbar[:, I] = round_to((s / rows.shape[1]).astype(np.float32), "bf16")
+    Qs = (Q - np.repeat(qbar, blk, axis=1)[:, :N]).astype(np.float32)
+    return qbar, Qs
+
+
+def smooth_k(K: np.ndarray, eps: float = 0.0):
+    """Key smoothing as in the SageAttention path (token mean per channel,
+    mu = fp32(S/N - eps)); returns (mu [BH, d], K_s = fp32(K - mu))."""
+    K = _f32(K)
+    mu, _ = smooth_mean(K, eps)
+    return mu, (K - mu[:, None, :]).astype(np.float32)
 
 
 def block_means(X: np.ndarray, blk: int) -> np.ndarray:
@@ -327,3 +357,19 @@ def thrift_decode(*, qc, qs, kc, ks, vc_t, vs_t, q, Kh, Vh, sel, Nk, d, blk=128,
                             int(quantize),
                             _p(o), C.byref(lse))
     return o, lse.value
+
+
+def ptq_fwd(*, qc, qs, qbar, kc, ks, vc_t, vs_t, Nq, Nk, d, blk=128, causal=False, tau, qblocks=None):
+    """Post-training FP4 forward (query and key smoothing, two-level P) of one
+    head: qc/qs the MXFP4 codes of the smoothed Q, qbar [nqb, d] its bf16
+    block means, kc/ks those of the smoothed K.  Returns (O, lse) for the rows
+    of query blocks `qblocks` (default all)."""
+    nqb = (Nq + blk - 1) // blk
+    qb0, qb1 = (0, nqb) if qblocks is None else qblocks
+    rows = min(Nq, qb1 * blk) - qb0 * blk
+    O = np.empty((rows, d)); lse = np.empty(rows)
+    a = [_c(x, np.uint8) for x in (qc, qs)]
+    b = [_c(x, np.uint8) for x in (kc, ks, vc_t, vs_t)]
+    lib().orc_ptq_fwd(_p(a[0]), _p(a[1]), _p(_f32(qbar)), *[_p(x) for x in b], Nq, Nk, d, blk, int(causal),
+                      float(tau), qb0, qb1, _p(O), _p(lse))
+    return O, lse

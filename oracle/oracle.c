@@ -880,6 +880,7 @@ typedef struct {
     const float *Qh, *Kh, *Vh;
     int Nk, d, quantize;
     double tau;
+    const double* bias;   /* FP4 path: added to key j's raw score (query smoothing); NULL: none */
 } thrift_ctx;
 
 /* One key block (keys [j0, j0+n)) through one path, for query row i (row
@@ -897,6 +898,7 @@ static void thrift_block(const thrift_ctx* c, row_state* st, int i, int j0, int 
         int j = j0 + u;
         if (path == 0 && c->quantize) {
             orc_mx_scores(c->qc, c->qs, c->kc, c->ks, d, i, j, &s[u]);
+            if (c->bias) s[u] += c->bias[j];
             s[u] *= c->tau;
         } else {
             double acc = 0.0;
@@ -946,7 +948,7 @@ void orc_thrift_fwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, con
                     const int32_t* sel_idx, const int32_t* sel_cnt, int max_sel,
                     int Nq, int Nk, int d, int blk, int hp_tile, int causal, double tau, int quantize,
                     int qb0, int qb1, double* O, double* lse) {
-    thrift_ctx c = {qc, qs, kc, ks, vc_t, vs_t, Qh, Kh, Vh, Nk, d, quantize, tau};
+    thrift_ctx c = {qc, qs, kc, ks, vc_t, vs_t, Qh, Kh, Vh, Nk, d, quantize, tau, NULL};
     int nkb = Nk / blk;
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int I = qb0; I < qb1; ++I)
@@ -985,7 +987,7 @@ void orc_thrift_decode(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, 
                        const float* q, const float* Kh, const float* Vh,
                        const int32_t* sel, int nsel, int Nk, int d, int blk, int hp_tile, double tau,
                        int num_splits, int quantize, double* o, double* lse) {
-    thrift_ctx c = {qc, qs, kc, ks, vc_t, vs_t, q, Kh, Vh, Nk, d, quantize, tau};
+    thrift_ctx c = {qc, qs, kc, ks, vc_t, vs_t, q, Kh, Vh, Nk, d, quantize, tau, NULL};
     int nb = Nk / blk;
     double* ms = (double*)malloc(sizeof(double) * (size_t)num_splits);
     double* ls = (double*)malloc(sizeof(double) * (size_t)num_splits);
@@ -1017,4 +1019,56 @@ void orc_thrift_decode(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, 
     for (int k = 0; k < d; ++k) o[k] /= l;
     *lse = m + log(l);
     free(ms); free(ls); free(acc);
+}
+
+/* ========================================================================
+ * Post-training FP4 baseline in the SageAttention3 style
+ * ====================================================================== */
+
+/* [AQ] §1 and §2 Implementation describe the post-training FP4 method that
+ * Attn-QAT is measured against: FP4 attention with query and key smoothing
+ * and two-level quantisation of P ([TA] step 2 uses the same two-level
+ * scheme).  Reading: K is smoothed as in [SB] (its token mean is subtracted;
+ * the shift is the same for every key of a row, so the softmax is
+ * unchanged); Q is smoothed per block of blk rows: qbar_I, the block's mean
+ * rounded to bf16, is subtracted before quantisation and its product with
+ * the keys is added back, s_ij = tau (q^_s,i . k^_j + qbar_I . k^_j), both
+ * dot products exact in fp64 (k^ the dequantised MXFP4 key).  The softmax
+ * and P.V are those of the Thrift FP4 path with nothing selected: key
+ * blocks of blk keys in ascending order (causal: up to the row's last key),
+ * each one online-softmax tile with two-level P.  qc/qs hold the codes of
+ * the smoothed Q, kc/ks those of the smoothed K; qbar is [nqb][d] with
+ * nqb = ceil(Nq / blk); query blocks [qb0, qb1), the last one possibly
+ * short.  O and lse hold the rows of those blocks that exist. */
+void orc_ptq_fwd(const uint8_t* qc, const uint8_t* qs, const float* qbar, const uint8_t* kc, const uint8_t* ks,
+                 const uint8_t* vc_t, const uint8_t* vs_t, int Nq, int Nk, int d, int blk, int causal, double tau,
+                 int qb0, int qb1, double* O, double* lse) {
+    int nkb = Nk / blk;
+    double* bias = (double*)malloc(sizeof(double) * (size_t)Nk);
+    size_t out_row = 0;
+    for (int I = qb0; I < qb1; ++I) {
+        for (int j = 0; j < Nk; ++j) {
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c) acc += (double)qbar[(size_t)I * d + c] * kmx(kc, ks, d, j, c);
+            bias[j] = acc;
+        }
+        thrift_ctx ctx = {qc, qs, kc, ks, vc_t, vs_t, NULL, NULL, NULL, Nk, d, 1, tau, bias};
+        int rows = Nq - I * blk < blk ? Nq - I * blk : blk;
+#pragma omp parallel for schedule(dynamic)
+        for (int a = 0; a < rows; ++a) {
+            int i = I * blk + a;
+            int last = last_key(i, Nq, Nk, causal);
+            row_state st = {-INFINITY, 0.0, (double*)calloc((size_t)d, sizeof(double)), NULL};
+            for (int J = 0; J < nkb && J * blk <= last; ++J) {
+                int n = blk;
+                if (J * blk + n - 1 > last) n = last - J * blk + 1;
+                thrift_block(&ctx, &st, i, J * blk, n, 0);
+            }
+            for (int k = 0; k < d; ++k) O[(out_row + (size_t)a) * d + k] = st.acc[k] / st.l;
+            lse[out_row + (size_t)a] = st.m + log(st.l);
+            free(st.acc);
+        }
+        out_row += (size_t)rows;
+    }
+    free(bias);
 }

@@ -92,6 +92,9 @@ void orc_thrift_decode(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, 
                        const float* q, const float* Kh, const float* Vh,
                        const int32_t* sel, int nsel, int Nk, int d, int blk, int hp_tile, double tau,
                        int num_splits, int quantize, double* o, double* lse);
+void orc_ptq_fwd(const uint8_t* qc, const uint8_t* qs, const float* qbar, const uint8_t* kc, const uint8_t* ks,
+                 const uint8_t* vc_t, const uint8_t* vs_t, int Nq, int Nk, int d, int blk, int causal, double tau,
+                 int qb0, int qb1, double* O, double* lse);
 
 #ifdef __cplusplus
 }
