@@ -15,6 +15,10 @@ Workloads (``--workload``, default c2):
   c4t the Attn-QAT training step on the same inputs: forward with O', then
       the backward; `value` counts forward + backward, the roofline the
       backward call.
+  c4i the Attn-QAT inference forward on the same inputs: no O'.
+  c4p the post-training FP4 baseline that Attn-QAT is compared with, on
+      c4's inputs: Q smoothed by its bf16 128-row block means and K by its
+      token mean before MXFP4, the means' score shifts, two-level P.
   c5  ThriftAttention prefill at B=1, Hq=32, Hkv=8, N=131072, d=128,
       causal, low-rank inputs: MXFP4 Q, K, V with block means, block
       selection (5 %), mixed FP4 / bf16 attention.
@@ -32,7 +36,7 @@ time, measured with HIP events on the stream it runs on, against the dense
 matrix-core peak of its operand types.  `cpu_baseline` times the CPU oracle
 on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--workload c2|c3|c4|c4t|c5|c5d] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--workload c2|c3|c4|c4t|c4i|c4p|c5|c5d] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -174,6 +178,68 @@ def _qat_case(w, bqa, torch):
         traffic_key="qat_fwd_kernel<aux>", cpu=cpu_baseline_qat)
 
 
+def cpu_baseline_ptq(w, budget_s: float = 20.0):
+    """The oracle on a bounded sample of the post-training baseline: smoothing
+    and MXFP4 quantisation of one whole head, then its forward over query
+    blocks until the time budget is spent."""
+    import oracle
+    import workloads as wl
+    from tests.helpers import tau_for
+    oracle.lib()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    Q, K, V = (wl.chunk(w, t, 0, 0)[None] for t in ("q", "k", "v"))
+    qbar, Qs = oracle.smooth_q_blocks(Q)
+    _, Ks = oracle.smooth_k(K)
+    qc, qs = oracle.quant_mx_rows(Qs)
+    kc, ks = oracle.quant_mx_rows(Ks)
+    vc, vs = oracle.quant_mx_cols(V)
+    qb = 0
+    while qb * 128 < w.Nq and time.perf_counter() - t0 < budget_s:
+        oracle.ptq_fwd(qc=qc[0], qs=qs[0], qbar=qbar[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0], Nq=w.Nq,
+                       Nk=w.Nk, d=w.d, tau=tau_for(w.d), qblocks=(qb, qb + 1))
+        qb += 1
+    dt = time.perf_counter() - t0
+    rows = min(w.Nq, 128 * qb)
+    return {"value": 4.0 * rows * w.Nk * w.d / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"head (0,0): Q/K smoothing and MXFP4 quantisation, then the forward of {qb} of "
+                      f"{(w.Nq + 127) // 128} query blocks against N={w.Nk} keys, {dt:.1f} s"}
+
+
+def _ptq_case(w, bqa, torch):
+    from bit_quantized_attention_amd.runner import PtqPath, attention_ops, ptq_problem, to_device
+    import workloads as wl
+    Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
+    p = ptq_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, causal=w.causal)
+    path = PtqPath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
+    ops = attention_ops(p)                       # the two MXFP4 products
+    return dict(
+        path=path, ops=ops, dtype="mxfp4",
+        workload="post-training FP4 baseline on the Attn-QAT inputs (c4p): B=1 H=32 N=16384 d=128 non-causal, "
+                 "Student-t bf16 in; Q less its bf16 128-row block means and K less its token mean, MXFP4 Q/K/V, "
+                 "two-level MXFP4 P; step = smoothing quantisers + score shifts + attention",
+        roofline={"bound": "mfma", "kernel": "attn_fwd_ptq (ptq_bias_kernel + thrift_fwd_kernel<PTQ>): MXFP4 QK^T "
+                                             "and P.V; the bf16 score-shift product adds 0.02 % more operations",
+                  "peak": PEAK_F4_TFLOPS, "ops_per_launch": ops},
+        traffic_key="thrift_fwd_kernel<true>", cpu=cpu_baseline_ptq)
+
+
+def _qat_infer_case(w, bqa, torch):
+    from bit_quantized_attention_amd.runner import QatPath, attention_ops, qat_problem, to_device
+    import workloads as wl
+    Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
+    p = qat_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+    path = QatPath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"), aux=False)
+    ops = attention_ops(p)
+    return dict(
+        path=path, ops=ops, dtype="mxfp4",
+        workload="Attn-QAT FP4 inference forward (c4i): B=1 H=32 N=16384 d=128 non-causal, Student-t bf16 in, MXFP4 "
+                 "Q/K/V/P, no auxiliary output; step = quantise Q,K,V + attention",
+        roofline={"bound": "mfma", "kernel": "attn_fwd QAT without O' (qat_fwd_kernel<false>): MXFP4 QK^T and P.V",
+                  "peak": PEAK_F4_TFLOPS, "ops_per_launch": ops},
+        traffic_key="qat_fwd_kernel<false>", cpu=cpu_baseline_qat)
+
+
 def _thrift_pairs(path, w):
     """(fp4 pairs, bf16 pairs) of (query, key) scores the prefill computes,
     from the selection the step made (diagonal blocks count their causal half)."""
@@ -249,7 +315,7 @@ def _thrift_case(w, bqa, torch):
                   "peak_note": f"fp4 and bf16 dense peaks weighted by the pairs each path computed "
                                f"({100.0 * b16 / (f4 + b16):.2f} % bf16)",
                   "ops_per_launch": ops_f4 + ops_b16},
-        traffic_key="thrift_fwd_kernel", cpu=cpu_baseline_thrift)
+        traffic_key="thrift_fwd_kernel<false>", cpu=cpu_baseline_thrift)
 
 
 def cpu_baseline_decode(w, budget_s: float = 20.0):
@@ -430,8 +496,65 @@ def _qat_train_case(w, bqa, torch):
         traffic_key="qbwd_dkdv_kernel", cpu=cpu_baseline_qat_train)
 
 
-CASES = {"c2": _sage_case, "c3": _sagebwd_case, "c4": _qat_case, "c4t": _qat_train_case, "c5": _thrift_case,
-         "c5d": _decode_case}
+def probe_main(torch, bqa):
+    """Rate probes (bqa_debug_probe): the sustained dense matrix rate per
+    operand type, the v_exp_f32 rate and the HBM copy bandwidth, each beside
+    the published peak the roofline figures divide by.  Prints one JSON line."""
+    dev = torch.device("cuda")
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) * 1e-3
+            best = t if best is None or t < best else best
+        return best
+
+    res = {}
+    grid = 4 * n_cu                      # 16 wavefronts per compute unit
+    waves = grid * 4
+    mm = [("mfma_i8", bqa.BQA_PROBE_MFMA_I8, 65536, PEAK_I8_TOPS, "TOPS"),
+          ("mfma_fp8", bqa.BQA_PROBE_MFMA_F8, 131072, PEAK_I8_TOPS, "TFLOP/s"),
+          ("mfma_mxfp4", bqa.BQA_PROBE_MFMA_F4, 131072, PEAK_F4_TFLOPS, "TFLOP/s"),
+          ("mfma_bf16", bqa.BQA_PROBE_MFMA_BF16, 32768, PEAK_BF16_TFLOPS, "TFLOP/s")]
+    iters = 20000
+    for name, kind, per, peak, unit in mm:
+        t = timed(lambda: bqa.bqa_debug_probe(kind, grid, iters, None, out, out.numel()))
+        v = waves * iters * 8 * per / t / 1e12
+        res[name] = {"measured": round(v, 1), "peak": peak, "unit": unit, "frac": round(v / peak, 4),
+                     "time_ms": round(t * 1e3, 3)}
+    it_exp = 100000
+    t = timed(lambda: bqa.bqa_debug_probe(bqa.BQA_PROBE_EXP, grid, it_exp, None, out, out.numel()))
+    v = grid * 256 * it_exp * 8 / t / 1e12
+    # one transcendental per lane every 4 clocks on each SIMD (16 lanes / clock), 2.4 GHz
+    spec = n_cu * 4 * 16 * 2.4e9 / 1e12
+    res["v_exp_f32"] = {"measured": round(v, 3), "peak": round(spec, 3), "unit": "T exp/s",
+                        "frac": round(v / spec, 4), "time_ms": round(t * 1e3, 3),
+                        "peak_note": "16 lanes per clock per SIMD, 4 SIMDs per CU, 2.4 GHz (with one fp32 "
+                                     "subtraction per exponential in the loop)"}
+    nbytes = 1 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t = timed(lambda: bqa.bqa_debug_probe(bqa.BQA_PROBE_COPY, 8 * n_cu, 0, src, dst, nbytes))
+    v = 2 * nbytes / t / 1e9
+    res["hbm_copy"] = {"measured": round(v, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(v / 8000.0, 4),
+                       "time_ms": round(t * 1e3, 3), "note": "1 GiB read + 1 GiB written per launch"}
+    assert torch.equal(dst[:4096], src[:4096])
+    print(json.dumps({"probes": res, "compute_units": n_cu, "grid_matrix": grid, "iters_matrix": iters}), flush=True)
+
+
+CASES = {"c2": _sage_case, "c3": _sagebwd_case, "c4": _qat_case, "c4t": _qat_train_case, "c4i": _qat_infer_case,
+         "c4p": _ptq_case, "c5": _thrift_case, "c5d": _decode_case}
+INPUTS_OF = {"c4t": "c4", "c4i": "c4", "c4p": "c4"}        # workloads that reuse another's inputs
 
 
 def main():
@@ -447,6 +570,9 @@ def main():
                     help="minimum warmup time (profiler runs pass 0 to keep the number of dispatches small)")
     ap.add_argument("--workload", choices=sorted(CASES), default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe", action="store_true",
+                    help="only run the rate probes (matrix rate per type, v_exp_f32, HBM copy) and print them "
+                         "beside the published peaks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -464,6 +590,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
+    if args.probe:
+        probe_main(torch, bqa)
+        return
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -472,7 +601,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": src.numel(), "launches": 5}))
         return
-    w = wl.WORKLOADS[args.workload.rstrip("t")]
+    w = wl.WORKLOADS[INPUTS_OF.get(args.workload, args.workload)]
     case = CASES[args.workload](w, bqa, torch)
     path = case["path"]
     t_w = time.perf_counter()

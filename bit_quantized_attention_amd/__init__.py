@@ -26,14 +26,15 @@ BQA_OK, BQA_E_NULL, BQA_E_SHAPE, BQA_E_UNSUPPORTED, BQA_E_ALIGN, BQA_E_WORKSPACE
     0, -1, -2, -3, -4, -5, -6, -7
 BQA_E_NONFINITE, BQA_E_TOO_LARGE = -8, -9
 BQA_BF16, BQA_FP16, BQA_INT8, BQA_FP8E4M3, BQA_MXFP4 = range(5)
-BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV, BQA_SAGE_I8_I8PV, BQA_QAT_MXFP4, BQA_THRIFT = range(5)
+BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV, BQA_SAGE_I8_I8PV, BQA_QAT_MXFP4, BQA_THRIFT, BQA_PTQ_MXFP4 = range(6)
 BQA_ROLE_Q, BQA_ROLE_K, BQA_ROLE_V, BQA_ROLE_DO = range(4)
 BQA_OP_QUANTIZE_Q, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_V, BQA_OP_QUANTIZE_DO, BQA_OP_SELECT, BQA_OP_FWD, \
     BQA_OP_BWD, BQA_OP_QUANTIZE_KV = range(8)
 
 EXPORTS = ["bqa_abi_version", "bqa_status_string", "bqa_workspace_size", "bqa_quantize_blocks", "bqa_quantize_kv",
            "bqa_select_blocks", "bqa_attn_fwd", "bqa_attn_bwd", "bqa_debug_qk_scores", "bqa_attn_decode_static",
-           "bqa_debug_mx_dequant"]
+           "bqa_debug_mx_dequant", "bqa_attn_fwd_ptq", "bqa_debug_probe"]
+BQA_PROBE_MFMA_I8, BQA_PROBE_MFMA_F8, BQA_PROBE_MFMA_F4, BQA_PROBE_MFMA_BF16, BQA_PROBE_EXP, BQA_PROBE_COPY = range(6)
 
 
 class BqaError(RuntimeError):
@@ -97,6 +98,11 @@ def lib():
         L.bqa_attn_decode_static.argtypes = [P(bqa_problem), P(bqa_qtensor), P(bqa_qtensor), P(bqa_qtensor),
                                              P(bqa_tensor), P(bqa_tensor), P(bqa_tensor), vp, vp, P(bqa_tensor), vp,
                                              vp]
+        L.bqa_attn_fwd_ptq.restype = C.c_int32
+        L.bqa_attn_fwd_ptq.argtypes = [P(bqa_problem), P(bqa_qtensor), P(bqa_qtensor), P(bqa_qtensor), vp,
+                                       P(bqa_tensor), vp, vp, C.c_size_t, vp]
+        L.bqa_debug_probe.restype = C.c_int32
+        L.bqa_debug_probe.argtypes = [C.c_int32, C.c_int32, C.c_int64, vp, vp, C.c_size_t, vp]
         L.bqa_debug_mx_dequant.restype = C.c_int32
         L.bqa_debug_mx_dequant.argtypes = [vp, vp, C.c_int64, vp, vp]
         L.bqa_debug_qk_scores.restype = C.c_int32
@@ -253,6 +259,18 @@ def bqa_attn_bwd(p, q=None, k=None, v=None, v_hi=None, o_for_delta=None, lse=Non
     return s
 
 
+def bqa_attn_fwd_ptq(p, q=None, k=None, v=None, q_means=None, o=None, lse=None, workspace=None,
+                     workspace_bytes=None, stream=None, check=True) -> int:
+    od = o if (o is None or isinstance(o, bqa_tensor)) else dense(o)
+    wb = workspace_bytes if workspace_bytes is not None else (workspace.numel() * workspace.element_size()
+                                                              if workspace is not None else 0)
+    s = lib().bqa_attn_fwd_ptq(C.byref(p), _ref(q), _ref(k), _ref(v), _ptr(q_means), _ref(od), _ptr(lse),
+                               _ptr(workspace), wb, _stream(stream))
+    if check:
+        _check(s, "bqa_attn_fwd_ptq")
+    return s
+
+
 def bqa_attn_decode_static(p, q=None, k=None, v=None, q_hi=None, k_hi=None, v_hi=None, sel_idx=None, sel_cnt=None,
                            o=None, lse=None, stream=None, check=True) -> int:
     def dd(t):
@@ -262,6 +280,14 @@ def bqa_attn_decode_static(p, q=None, k=None, v=None, q_hi=None, k_hi=None, v_hi
                                      _stream(stream))
     if check:
         _check(s, "bqa_attn_decode_static")
+    return s
+
+
+def bqa_debug_probe(kind: int, grid: int, iters: int, src=None, dst=None, nbytes: int = 0, stream=None,
+                    check=True) -> int:
+    s = lib().bqa_debug_probe(int(kind), int(grid), int(iters), _ptr(src), _ptr(dst), int(nbytes), _stream(stream))
+    if check:
+        _check(s, "bqa_debug_probe")
     return s
 
 

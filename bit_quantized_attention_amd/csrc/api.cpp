@@ -53,7 +53,7 @@ bqa_status check_problem(const bqa_problem* p) {
     if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->Nq < 1 || p->Nk < 1) return BQA_E_SHAPE;
     if (p->Hq % p->Hkv != 0) return BQA_E_SHAPE;
     if (p->d != 64 && p->d != 128) return BQA_E_UNSUPPORTED;
-    if (p->mode < BQA_SAGE_I8_F16PV || p->mode > BQA_THRIFT) return BQA_E_UNSUPPORTED;
+    if (p->mode < BQA_SAGE_I8_F16PV || p->mode > BQA_PTQ_MXFP4) return BQA_E_UNSUPPORTED;
     if (p->causal && p->Nq > p->Nk) return BQA_E_SHAPE;
     if ((int64_t)p->B * p->Hq * p->Nq * p->d > ((int64_t)1 << 40)) return BQA_E_SHAPE;
     return BQA_OK;
@@ -166,7 +166,7 @@ size_t bqa_workspace_size(const bqa_problem* p, int32_t op) {
     if (check_problem(p) != BQA_OK) return 0;
     switch (op) {
         case BQA_OP_QUANTIZE_K:
-            if (is_sage(p->mode) && p->smooth_k)
+            if ((is_sage(p->mode) || p->mode == BQA_PTQ_MXFP4) && p->smooth_k)
                 return ws_kmean_bytes(p->B * p->Hkv, p->Nk, p->d);
             return 0;
         case BQA_OP_QUANTIZE_V:
@@ -183,6 +183,7 @@ size_t bqa_workspace_size(const bqa_problem* p, int32_t op) {
             if (p->mode == BQA_QAT_MXFP4) return ws_qat_fwd_bytes(p->B, p->Hkv, p->Nk, p->d);
             if (p->mode == BQA_THRIFT && p->Nq == 1 && p->Nk % 128 == 0)
                 return ws_decode_bytes(p->B, p->Hq, p->Hkv, p->Nk, p->num_splits);
+            if (p->mode == BQA_PTQ_MXFP4) return ws_ptq_fwd_bytes(p->B, p->Hq, p->Nq, p->Nk);
             return 0;
         default:
             return 0;
@@ -206,6 +207,26 @@ bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_ten
         TRY(check_q(out, BQA_MXFP4, axis));
         if (out->block != 32) return BQA_E_UNSUPPORTED;
         if (axis == 1 && N % 128 != 0) return BQA_E_UNSUPPORTED;
+        if (p->mode == BQA_PTQ_MXFP4 && role != BQA_ROLE_V) {
+            // the post-training baseline: Q less its bf16 block means (written to
+            // block_means, required), K less its token mean when p->smooth_k
+            if (d != 128) return BQA_E_UNSUPPORTED;
+            const bool key = role == BQA_ROLE_K;
+            if (key && block_means) return BQA_E_UNSUPPORTED;
+            if (!key && !block_means) return BQA_E_NULL;
+            if (!key || p->smooth_k) {
+                if (key) {
+                    if (!ws || ws_bytes < ws_kmean_bytes(p->B * H, N, d)) return BQA_E_WORKSPACE;
+                    if (!std::isfinite(p->smooth_eps)) return BQA_E_SHAPE;
+                }
+                if (((uintptr_t)block_means & 15u) || ((uintptr_t)k_mean & 3u)) return BQA_E_ALIGN;
+                TRY(check_device());
+                TRY(debug_check(stream, {dbg16(x, p->B, H, N, d)}));
+                return launched(launch_quant_mx_smooth(as_dense(x), f16, p->B, H, N, d, key, (double)p->smooth_eps,
+                                                       (uint8_t*)out->codes, (uint8_t*)out->scales,
+                                                       key ? k_mean : block_means, ws, st));
+            }
+        }
         if (block_means && (role == BQA_ROLE_V || p->sel_block != 128)) return BQA_E_UNSUPPORTED;
         if (block_means && N > 1 && N % 128 != 0) return BQA_E_UNSUPPORTED;
         TRY(check_device());
@@ -407,6 +428,32 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
     return BQA_E_UNSUPPORTED;
 }
 
+bqa_status bqa_attn_fwd_ptq(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k, const bqa_qtensor* v,
+                            const float* q_means, bqa_tensor* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_problem(p));
+    if (p->mode != BQA_PTQ_MXFP4) return BQA_E_UNSUPPORTED;
+    if (p->d != 128 || p->Nk % 128 != 0) return BQA_E_UNSUPPORTED;
+    TRY(check_q(q, BQA_MXFP4, 0));
+    TRY(check_q(k, BQA_MXFP4, 0));
+    TRY(check_q(v, BQA_MXFP4, 1));
+    if (q->block != 32 || k->block != 32 || v->block != 32) return BQA_E_UNSUPPORTED;
+    TRY(check_dense(o, false, true));
+    if (!q_means) return BQA_E_NULL;
+    if (!ws || ws_bytes < ws_ptq_fwd_bytes(p->B, p->Hq, p->Nq, p->Nk)) return BQA_E_WORKSPACE;
+    if (!aligned16(ws) || !aligned16(q_means) || ((uintptr_t)k->scales & 3u)) return BQA_E_ALIGN;
+    ThriftFwdArgs a{};
+    a.qc = (const uint8_t*)q->codes; a.qs = (const uint8_t*)q->scales;
+    a.kc = (const uint8_t*)k->codes; a.ks = (const uint8_t*)k->scales;
+    a.vc = (const uint8_t*)v->codes; a.vs = (const uint8_t*)v->scales;
+    a.o = as_dense(o); a.lse = lse;
+    a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk; a.causal = p->causal;
+    a.c_log2 = tau_of(p) * 1.4426950408889634f;
+    TRY(check_device());
+    const int nqb = (p->Nq + 127) / 128;
+    TRY(debug_check(stream, {dbg32(q_means, (int64_t)p->B * p->Hq * nqb * p->d)}));
+    return launched(launch_ptq_fwd(a, q_means, ws, (hipStream_t)stream));
+}
+
 bqa_status bqa_attn_decode_static(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
                                   const bqa_qtensor* v, const bqa_tensor* q_hi, const bqa_tensor* k_hi,
                                   const bqa_tensor* v_hi, const int32_t* sel_idx, const int32_t* sel_cnt,
@@ -538,4 +585,20 @@ extern "C" bqa_status bqa_debug_mx_dequant(const void* codes, const void* scales
     TRY(check_device());
     return launched(launch_mx_dequant((const uint8_t*)codes, (const uint8_t*)scales, nblocks, (uint16_t*)out,
                                       (hipStream_t)stream));
+}
+
+extern "C" bqa_status bqa_debug_probe(int32_t kind, int32_t grid, int64_t iters, const void* src, void* dst,
+                                      size_t bytes, void* stream) {
+    if (kind < BQA_PROBE_MFMA_I8 || kind > BQA_PROBE_COPY) return BQA_E_UNSUPPORTED;
+    if (grid < 1 || grid > (1 << 20) || iters < 0 || iters > ((int64_t)1 << 30)) return BQA_E_SHAPE;
+    if (!dst) return BQA_E_NULL;
+    if (kind == BQA_PROBE_COPY) {
+        if (!src) return BQA_E_NULL;
+        if (!aligned16(src) || !aligned16(dst) || bytes % 16 != 0) return BQA_E_ALIGN;
+    } else {
+        if ((uintptr_t)dst & 3u) return BQA_E_ALIGN;
+        if (bytes < (size_t)grid * 4) return BQA_E_SHAPE;
+    }
+    TRY(check_device());
+    return launched(launch_probe(kind, grid, iters, src, dst, bytes, (hipStream_t)stream));
 }

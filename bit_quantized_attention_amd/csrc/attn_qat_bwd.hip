@@ -48,33 +48,39 @@ __device__ __forceinline__ int fc128(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int fc256(int r) { return r & 15; }
 
 // ------------------------------------------------------------------ preprocess
+// delta'_i = sum_c dO[i, c] O'[i, c] for the 128 rows of one workgroup (16
+// rows at a time, 16 lanes per row, 8 channels each), and the largest |dO|
+// of those rows folded into its head's word with one atomic (N is a multiple
+// of 128, so a workgroup never spans two heads).
+constexpr int DELTA_ROWS = 128;
 __global__ __launch_bounds__(256) void qat_delta_kernel(Dense dO, Dense Oa, int H, int N, int64_t rows,
                                                         float* __restrict__ delta, uint32_t* __restrict__ do_amax) {
-    // delta'_i = sum_c dO[i, c] O'[i, c]; one row per 16 lanes, 8 channels each.
-    // A workgroup's 16 rows lie in one head (N is a multiple of 128).
     __shared__ float wmax[4];
-    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
     const int part = threadIdx.x & 15;
-    float acc = 0.0f, am = 0.0f;
-    if (row < rows) {
-        const int64_t bh = row / N, i = row % N, b = bh / H, h = bh % H;
-        const v4i gv = *(const v4i*)((const uint16_t*)dO.p + b * dO.sB + h * dO.sH + i * dO.sN + 8 * part);
-        const v4i ov = *(const v4i*)((const uint16_t*)Oa.p + b * Oa.sB + h * Oa.sH + i * Oa.sN + 8 * part);
+    const int64_t row0 = (int64_t)blockIdx.x * DELTA_ROWS;
+    float am = 0.0f;
+    for (int it = 0; it < DELTA_ROWS / 16; ++it) {
+        const int64_t row = row0 + 16 * it + (threadIdx.x >> 4);
+        float acc = 0.0f;
+        if (row < rows) {
+            const int64_t bh = row / N, i = row % N, b = bh / H, h = bh % H;
+            const v4i gv = *(const v4i*)((const uint16_t*)dO.p + b * dO.sB + h * dO.sH + i * dO.sN + 8 * part);
+            const v4i ov = *(const v4i*)((const uint16_t*)Oa.p + b * Oa.sB + h * Oa.sH + i * Oa.sN + 8 * part);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float g0 = bf16_bits_to_f32((uint16_t)gv[k]), g1 = bf16_bits_to_f32((uint16_t)((uint32_t)gv[k] >> 16));
-            acc = __builtin_fmaf(g0, bf16_bits_to_f32((uint16_t)ov[k]), acc);
-            acc = __builtin_fmaf(g1, bf16_bits_to_f32((uint16_t)((uint32_t)ov[k] >> 16)), acc);
-            am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(g0), __builtin_fabsf(g1)));
+            for (int k = 0; k < 4; ++k) {
+                const float g0 = bf16_bits_to_f32((uint16_t)gv[k]), g1 = bf16_bits_to_f32((uint16_t)((uint32_t)gv[k] >> 16));
+                acc = __builtin_fmaf(g0, bf16_bits_to_f32((uint16_t)ov[k]), acc);
+                acc = __builtin_fmaf(g1, bf16_bits_to_f32((uint16_t)((uint32_t)ov[k] >> 16)), acc);
+                am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(g0), __builtin_fabsf(g1)));
+            }
         }
-    }
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 16);
-    if (row < rows && part == 0) delta[row] = acc;
+        for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 16);
+        if (row < rows && part == 0) delta[row] = acc;
+    }
     am = wave_max(am);
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = am;
     __syncthreads();
-    const int64_t row0 = (int64_t)blockIdx.x * 16;
     if (threadIdx.x == 0 && row0 < rows) {
         const float m = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
         atomicMax(do_amax + row0 / N, __builtin_bit_cast(uint32_t, m));   // non-negative floats order as integers
@@ -540,7 +546,8 @@ hipError_t launch_qat_bwd(QatBwdArgs a, Dense o_aux, void* ws, hipStream_t st) {
 
     const int nbh = a.B * a.H;
     fill_zero_kernel<<<(nbh + 255) / 256, 256, 0, st>>>(do_amax, nbh);
-    qat_delta_kernel<<<(unsigned)((bhn * 16 + 255) / 256), 256, 0, st>>>(a.d_o, o_aux, a.H, a.N, bhn, delta, do_amax);
+    qat_delta_kernel<<<(unsigned)((bhn + DELTA_ROWS - 1) / DELTA_ROWS), 256, 0, st>>>(a.d_o, o_aux, a.H, a.N, bhn, delta,
+                                                                                    do_amax);
     const unsigned tg = (unsigned)((int64_t)a.B * a.H * (a.N / 64) * (D / 64));
     // V codes are channel-major [d][N/2]: transposing the (channel, token) grid gives token-major rows
     deq_t_fp4_kernel<<<tg, 256, 0, st>>>(a.vc, a.vs, D, a.N, vdeq);

@@ -54,9 +54,14 @@ struct LdsBf {
     uint8_t k[HB * D * 2];     // 64 keys x 256 B
     uint8_t vt[D * HB * 2];    // 128 channels x 128 B (64 keys)
 };
+struct LdsF4Bias {              // the post-training baseline: an FP4 block and its keys' score shifts
+    LdsF4 f;
+    float bias[KB];
+};
 union LdsBuf {
     LdsF4 f;
     LdsBf b;
+    LdsF4Bias p;
 };
 
 // FP4 key block J: codes and scales of K and V^T, all by direct copies.
@@ -123,6 +128,10 @@ __device__ __forceinline__ void follow_max(v16f* oacc, float& l_run, float& m_ru
 }
 constexpr float R_FLOOR = 0x1p-64f;   // two-level factors below this add nothing
 
+// PTQ: the post-training FP4 baseline (query and key smoothing, two-level
+// P): no selected blocks, and key j's shift qbar . k^_j of the workgroup's
+// query block (a.sbias) is added to its raw scores.
+template <bool PTQ>
 __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
     __shared__ __attribute__((aligned(16))) LdsBuf lds[2];
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
@@ -142,8 +151,13 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
     const int qpos_hi = off + (qt * BM + BM - 1 < a.Nq - 1 ? qt * BM + BM - 1 : a.Nq - 1);
     const int nkb = a.Nk / KB;
     const int nJ = a.causal ? (qpos_hi / KB + 1 < nkb ? qpos_hi / KB + 1 : nkb) : nkb;
-    const int32_t* sel = a.sel_idx + ((int64_t)bh * nqt + qt) * a.max_sel;
-    const int ns = a.sel_cnt[(int64_t)bh * nqt + qt];
+    const int32_t* sel = PTQ ? nullptr : a.sel_idx + ((int64_t)bh * nqt + qt) * a.max_sel;
+    const int ns = PTQ ? 0 : a.sel_cnt[(int64_t)bh * nqt + qt];
+    const float* brow = PTQ ? a.sbias + ((int64_t)bh * nqt + qt) * a.Nk : nullptr;
+    // waves 2 and 3 copy the 128 shifts of key block J next to its codes
+    auto issue_bias = [&](int J, LdsBuf& L) {
+        if (PTQ && w >= 2) lds_copy4((uint32_t)(4 * l), brow + J * KB + 64 * (w - 2), lds_addr(L.p.bias + 64 * (w - 2)));
+    };
     const float c = a.c_log2;
 
     // FP4 query codes: B operand of S^T (channels 64 kk + 32 h .. + 31)
@@ -173,13 +187,17 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
     int J = next_unsel(0);
     if (J < nJ) {
         issue_f4(a, bhk, J, lds[0].f, w, l);
+        issue_bias(J, lds[0]);
         BQA_WAIT_VM(0);
         barrier_only();
     }
     int buf = 0;
     while (J < nJ) {
         const int Jn = next_unsel(J + 1);
-        if (Jn < nJ) issue_f4(a, bhk, Jn, lds[buf ^ 1].f, w, l);
+        if (Jn < nJ) {
+            issue_f4(a, bhk, Jn, lds[buf ^ 1].f, w, l);
+            issue_bias(Jn, lds[buf ^ 1]);
+        }
         const LdsF4& L = lds[buf].f;
         // scores: s[t] reg i of half h is key 32 t + 16 h + i of the block
         v16f s[4];
@@ -192,6 +210,16 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
                 const v4i av = *(const v4i*)(L.kc + r * 64 + 16 * ((2 * kk + h) ^ fk64(r)));
                 s[t] = mfma_f4_32x32x64(av, (int)L.ks[4 * r + 2 * kk + h], qb[kk], qsb[kk], s[t]);
             }
+        }
+        if constexpr (PTQ) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const v4f bb = *(const v4f*)(lds[buf].p.bias + 32 * t + 16 * h + 4 * q4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[t][4 * q4 + e] += bb[e];
+                }
         }
         if (a.causal && J * KB + KB - 1 > qpos_lo) {
 #pragma unroll
@@ -378,11 +406,84 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
     if (a.lse && h == 0) a.lse[(int64_t)bh * a.Nq + qrow] = m_run * 0.6931471805599453f + __logf(l_tot);
 }
 
+// Score shifts of the post-training baseline: bias[b, hq, I, j] =
+// qbar_I . k^_j, the bf16 block mean of query block I against the
+// dequantised MXFP4 key j (exact in bf16), as one bf16 matrix product per
+// head with fp32 sums: A = qbar rows (32 query blocks), B = k^ (32 keys per
+// wavefront, 128 per workgroup).  grid B * Hq * (Nk / 128).
+__global__ __launch_bounds__(256) void ptq_bias_kernel(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks,
+                                                       const float* __restrict__ qbar, int Hq, int Hkv, int nqb,
+                                                       int Nk, float* __restrict__ bias) {
+    const int nkb = Nk / KB;
+    const int bhq = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+    const int b = bhq / Hq, hq = bhq % Hq, bhk = b * Hkv + hq / (Hq / Hkv);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, lq = l & 31, h = l >> 5;
+    const int key = kb * KB + 32 * w + lq;
+    // B operand: key `key`, channels 16 s + 8 h .. + 7 of step s
+    const uint8_t* krow = kc + ((int64_t)bhk * Nk + key) * (D / 2);
+    v4i raw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) raw[q] = *(const v4i*)(krow + 16 * q);
+    const uint32_t sc4 = *(const uint32_t*)(ks + ((int64_t)bhk * Nk + key) * (D / 32));
+    v8bf kb8[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+        const uint32_t word = (uint32_t)raw[st >> 1][2 * (st & 1) + h];
+        const float sc = __builtin_bit_cast(float, ((sc4 >> (8 * (st >> 1))) & 0xFFu) << 23);
+        const v4i pk = {__builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0)),
+                        __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1)),
+                        __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2)),
+                        __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3))};
+        kb8[st] = __builtin_bit_cast(v8bf, pk);
+    }
+    const float* qb0 = qbar + (int64_t)bhq * nqb * D;
+    float* out = bias + (int64_t)bhq * nqb * Nk + key;
+    for (int q0 = 0; q0 < nqb; q0 += 32) {
+        const int qb = q0 + lq;
+        v16f acc = v16f{};
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            v8bf av;
+            if (qb < nqb) {
+                const v4f x0 = *(const v4f*)(qb0 + (int64_t)qb * D + 16 * st + 8 * h);
+                const v4f x1 = *(const v4f*)(qb0 + (int64_t)qb * D + 16 * st + 8 * h + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    av[e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(x0[e]));
+                    av[4 + e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(x1[e]));
+                }
+            } else {
+                av = v8bf{};
+            }
+            acc = mfma_bf16_32x32x16(av, kb8[st], acc);
+        }
+        // register r of half h is query block q0 + 8 (r / 4) + 4 h + r % 4
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (row < nqb) out[(int64_t)row * Nk] = acc[r];
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_thrift_fwd(const ThriftFwdArgs& a, hipStream_t st) {
     const int grid = a.B * a.Hq * ((a.Nq + BM - 1) / BM);
-    thrift_fwd_kernel<<<grid, 256, 0, st>>>(a);
+    thrift_fwd_kernel<false><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+size_t ws_ptq_fwd_bytes(int B, int Hq, int Nq, int Nk) {
+    return (size_t)B * Hq * ((Nq + BM - 1) / BM) * Nk * sizeof(float);
+}
+
+hipError_t launch_ptq_fwd(ThriftFwdArgs a, const float* qbar, void* ws, hipStream_t st) {
+    const int nqb = (a.Nq + BM - 1) / BM;
+    float* bias = (float*)ws;
+    ptq_bias_kernel<<<a.B * a.Hq * (a.Nk / KB), 256, 0, st>>>(a.kc, a.ks, qbar, a.Hq, a.Hkv, nqb, a.Nk, bias);
+    a.sbias = bias;
+    thrift_fwd_kernel<true><<<a.B * a.Hq * nqb, 256, 0, st>>>(a);
     return hipGetLastError();
 }
 

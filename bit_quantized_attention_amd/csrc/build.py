@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libbqa.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "quant.hip", "attn_sage_fwd.hip", "attn_qat.hip", "select.hip", "attn_thrift.hip", "attn_sage_bwd.hip", "attn_qat_bwd.hip", "debug.hip"]
+SOURCES = ["api.cpp", "quant.hip", "attn_sage_fwd.hip", "attn_qat.hip", "select.hip", "attn_thrift.hip", "attn_sage_bwd.hip",
+           "attn_qat_bwd.hip", "debug.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

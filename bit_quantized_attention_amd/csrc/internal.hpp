@@ -23,6 +23,8 @@ hipError_t launch_quant_kv(const Dense& k, const Dense& v, bool f16, int B, int 
                            hipStream_t st);
 hipError_t launch_quant_mx(const Dense& x, bool f16, int B, int H, int N, int d, int axis, uint8_t* codes,
                            uint8_t* scales, float* means, hipStream_t st);
+hipError_t launch_quant_mx_smooth(const Dense& x, bool f16, int B, int H, int N, int d, bool key, double eps,
+                                  uint8_t* codes, uint8_t* scales, float* means, void* ws, hipStream_t st);
 
 // ---- SageAttention INT8 forward (attn_sage_fwd.hip)
 enum { PV_F16 = 0, PV_F8 = 1, PV_I8 = 2 };
@@ -108,8 +110,12 @@ struct ThriftFwdArgs {
     float* lse;                                          // [B,Hq,Nq] or null
     int B, Hq, Hkv, Nq, Nk, causal;
     float c_log2;                                        // tau * log2(e)
+    const float* sbias;                                  // post-training baseline: [B,Hq,nqb,Nk] score shifts
 };
 hipError_t launch_thrift_fwd(const ThriftFwdArgs& a, hipStream_t st);
+// post-training FP4 baseline: score shifts from qbar [B,Hq,nqb,d] into ws, then the FP4 path
+size_t ws_ptq_fwd_bytes(int B, int Hq, int Nq, int Nk);
+hipError_t launch_ptq_fwd(ThriftFwdArgs a, const float* qbar, void* ws, hipStream_t st);
 
 // ---- ThriftAttention decode (attn_thrift.hip): one query per (batch, query head)
 struct ThriftDecArgs {
@@ -146,5 +152,9 @@ struct DebugInput {
 };
 bool debug_enabled();
 int debug_scan(hipStream_t st, const DebugInput* in, int n_in);   // 1 found, 0 clean, -1 HIP error
+
+// ---- rate probes (probe.hip); the kinds are the BQA_PROBE_* values of bqa.h
+enum { PROBE_MFMA_I8 = 0, PROBE_MFMA_F8 = 1, PROBE_MFMA_F4 = 2, PROBE_MFMA_BF16 = 3, PROBE_EXP = 4, PROBE_COPY = 5 };
+hipError_t launch_probe(int kind, int grid, int64_t iters, const void* src, void* dst, size_t bytes, hipStream_t st);
 
 }  // namespace bqa

@@ -1,0 +1,125 @@
+// probe.hip — rate probes behind bqa_debug_probe: what the device sustains
+// for the operations the attention kernels are bound by, next to the
+// published peaks that the roofline figures divide by.
+//
+//  * matrix probes: every wavefront issues `iters` rounds of eight dense
+//    matrix instructions of one type on register operands, in four
+//    independent accumulator chains (enough to cover the instruction's
+//    latency at four wavefronts per SIMD);
+//  * exp probe: every lane runs `iters` rounds of eight independent
+//    v_exp_f32, each followed by one subtraction that keeps the values in
+//    [-1, 1];
+//  * copy probe: a grid-stride 16-byte copy of `bytes` from src to dst.
+// Each workgroup writes one checksum word to dst (matrix and exp probes) so
+// that nothing is optimised away.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace bqa {
+
+namespace {
+
+template <int KIND>
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int64_t iters, uint32_t* __restrict__ out) {
+    const int l = threadIdx.x & 63;
+    // operands: small values, different per lane (the rate does not depend on them)
+    const int seed = (int)(threadIdx.x * 2654435761u + blockIdx.x);
+    const v4i a4 = {seed & 0x07070707, (seed >> 1) & 0x07070707, 0x01020304, l};
+    const v8i a8 = {a4[0], a4[1], a4[2], a4[3], 0x01010101, 0x02020202, 0x03030303, 0x04040404};
+    uint32_t sum = 0;
+    if constexpr (KIND == PROBE_MFMA_I8) {
+        v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+        for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a4, a4, c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a4, a4, c1, 0, 0, 0);
+                c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a4, a4, c2, 0, 0, 0);
+                c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a4, a4, c3, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += (uint32_t)(c0[i] ^ c1[i] ^ c2[i] ^ c3[i]);
+    } else if constexpr (KIND == PROBE_MFMA_BF16) {
+        const v8bf b = __builtin_bit_cast(v8bf, a4);
+        v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+        for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c1, 0, 0, 0);
+                c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c2, 0, 0, 0);
+                c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += __builtin_bit_cast(uint32_t, c0[i] + c1[i] + c2[i] + c3[i]);
+    } else {
+        // f8f6f4 instructions: format 0 (e4m3) for the fp8 probe, 4 (e2m1, scaled) for fp4
+        constexpr int FMT = KIND == PROBE_MFMA_F8 ? 0 : 4;
+        v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+        for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, a8, c0, FMT, FMT, 0, 127, 0, 127);
+                c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, a8, c1, FMT, FMT, 0, 127, 0, 127);
+                c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, a8, c2, FMT, FMT, 0, 127, 0, 127);
+                c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, a8, c3, FMT, FMT, 0, 127, 0, 127);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += __builtin_bit_cast(uint32_t, c0[i] + c1[i] + c2[i] + c3[i]);
+    }
+    sum = (uint32_t)wave_max((float)(sum & 0xFFFF));
+    if (threadIdx.x == 0) out[blockIdx.x] = sum;
+}
+
+__global__ __launch_bounds__(256) void exp_probe_kernel(int64_t iters, uint32_t* __restrict__ out) {
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = (float)((threadIdx.x + 37 * k) & 63) * (1.0f / 64.0f) - 0.5f;
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = __builtin_amdgcn_exp2f(x[k]) - 1.5f;   // [-1, 1] -> [-1, 0.5]
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += x[k];
+    s = wave_max(s);
+    if (threadIdx.x == 0) out[blockIdx.x] = __builtin_bit_cast(uint32_t, s);
+}
+
+__global__ __launch_bounds__(256) void copy_probe_kernel(const v4i* __restrict__ src, v4i* __restrict__ dst,
+                                                         int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const v4i a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        dst[i] = a;
+        dst[i + stride] = b;
+        dst[i + 2 * stride] = c;
+        dst[i + 3 * stride] = d;
+    }
+    for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_probe(int kind, int grid, int64_t iters, const void* src, void* dst, size_t bytes,
+                        hipStream_t st) {
+    uint32_t* out = (uint32_t*)dst;
+    switch (kind) {
+        case PROBE_MFMA_I8: mfma_probe_kernel<PROBE_MFMA_I8><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_MFMA_F8: mfma_probe_kernel<PROBE_MFMA_F8><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_MFMA_F4: mfma_probe_kernel<PROBE_MFMA_F4><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_MFMA_BF16: mfma_probe_kernel<PROBE_MFMA_BF16><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_EXP: exp_probe_kernel<<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_COPY:
+            copy_probe_kernel<<<grid, 256, 0, st>>>((const v4i*)src, (v4i*)dst, (int64_t)(bytes / 16));
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace bqa

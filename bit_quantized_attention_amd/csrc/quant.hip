@@ -619,17 +619,61 @@ __device__ __forceinline__ uint32_t mx_encode32(const float* v, uint32_t* packed
 }
 
 // Rows (Q, K): grid BH * ceil(N / 128); thread handles (token, 32-channel
-// block) items; optional fp32 means over each 128-token block (over the
-// tokens present when the last block is short, e.g. a single decode query).
-template <bool IS_F16>
+// block) items.  SUB selects what is subtracted before encoding:
+//  MX_PLAIN  nothing; with `means` the fp32 means over each 128-token block
+//            are written too (over the tokens present when the last block is
+//            short, e.g. a single decode query);
+//  MX_QBLOCK query smoothing: the block's mean, fp32 as above, then rounded
+//            to bf16, is subtracted from its rows and written to `means`;
+//  MX_KMEAN  key smoothing: mu = fp32(S / N - eps) per channel from the fp64
+//            partial token sums `part` (nch chunks per head), subtracted from
+//            every row; block 0 of a head writes it to `means` if not null.
+// Every difference is one fp32 subtraction.
+enum { MX_PLAIN = 0, MX_QBLOCK = 1, MX_KMEAN = 2 };
+template <bool IS_F16, int SUB>
 __global__ __launch_bounds__(256) void mx_rows_kernel(Dense x, int H, int N, int d, uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales, float* __restrict__ means) {
+                                                       uint8_t* __restrict__ scales, float* __restrict__ means,
+                                                       const double* __restrict__ part, int nch, double eps) {
     const int nt = (N + 127) / 128;
     const int bh = blockIdx.x / nt, tb = blockIdx.x % nt;
     const int b = bh / H, h = bh % H;
     const int rows = min(128, N - tb * 128);
     const uint16_t* base = (const uint16_t*)x.p + b * x.sB + h * x.sH;
     const int nblk = d / 32;
+    __shared__ float shift[128];
+    // one thread per channel sums the block's tokens in fp64, in token order;
+    // sixteen tokens are loaded ahead of their additions
+    auto block_mean = [&](int c) {
+        const uint16_t* col = base + (int64_t)tb * 128 * x.sN + c;
+        double s = 0.0;
+        int t = 0;
+        for (; t + 16 <= rows; t += 16) {
+            uint16_t e[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) e[u] = col[(int64_t)(t + u) * x.sN];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) s += (double)load_half<IS_F16>(&e[u]);
+        }
+        for (; t < rows; ++t) s += (double)load_half<IS_F16>(col + (int64_t)t * x.sN);
+        return (float)(s / (double)rows);
+    };
+    if constexpr (SUB == MX_QBLOCK) {
+        for (int c = threadIdx.x; c < d; c += 256) {
+            const float m = bf16_bits_to_f32(f32_to_bf16_bits(block_mean(c)));
+            shift[c] = m;
+            means[((int64_t)bh * nt + tb) * d + c] = m;
+        }
+        __syncthreads();
+    } else if constexpr (SUB == MX_KMEAN) {
+        for (int c = threadIdx.x; c < d; c += 256) {
+            double S = 0.0;
+            for (int u = 0; u < nch; ++u) S += part[((int64_t)bh * nch + u) * d + c];
+            const float mu = (float)(S / (double)N - eps);
+            shift[c] = mu;
+            if (means && tb == 0) means[(int64_t)bh * d + c] = mu;
+        }
+        __syncthreads();
+    }
     for (int it = threadIdx.x; it < rows * nblk; it += 256) {
         const int t = tb * 128 + it / nblk, g = it % nblk;
         float v[32];
@@ -641,28 +685,18 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(Dense x, int H, int N, int
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[q * 8 + j] = load_half<IS_F16>(e + j);
         }
+        if constexpr (SUB != MX_PLAIN) {
+#pragma unroll
+            for (int k = 0; k < 32; ++k) v[k] = v[k] - shift[g * 32 + k];
+        }
         uint32_t packed[4];
         uint32_t s = mx_encode32(v, packed);
         *(uint4*)(codes + ((int64_t)bh * N + t) * (d / 2) + g * 16) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
         scales[((int64_t)bh * N + t) * nblk + g] = (uint8_t)s;
     }
-    if (means) {
-        // one thread per channel sums the block's tokens in fp64, in token
-        // order; sixteen tokens are loaded ahead of their additions
-        for (int c = threadIdx.x; c < d; c += 256) {
-            const uint16_t* col = base + (int64_t)tb * 128 * x.sN + c;
-            double s = 0.0;
-            int t = 0;
-            for (; t + 16 <= rows; t += 16) {
-                uint16_t e[16];
-#pragma unroll
-                for (int u = 0; u < 16; ++u) e[u] = col[(int64_t)(t + u) * x.sN];
-#pragma unroll
-                for (int u = 0; u < 16; ++u) s += (double)load_half<IS_F16>(&e[u]);
-            }
-            for (; t < rows; ++t) s += (double)load_half<IS_F16>(col + (int64_t)t * x.sN);
-            means[((int64_t)bh * nt + tb) * d + c] = (float)(s / (double)rows);
-        }
+    if constexpr (SUB == MX_PLAIN) {
+        if (means)
+            for (int c = threadIdx.x; c < d; c += 256) means[((int64_t)bh * nt + tb) * d + c] = block_mean(c);
     }
 }
 
@@ -893,11 +927,34 @@ hipError_t launch_quant_mx(const Dense& x, bool f16, int B, int H, int N, int d,
                            uint8_t* scales, float* means, hipStream_t st) {
     const int grid = B * H * ((N + 127) / 128);
     if (axis == 0) {
-        if (f16) mx_rows_kernel<true><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales, means);
-        else mx_rows_kernel<false><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales, means);
+        if (f16) mx_rows_kernel<true, MX_PLAIN><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales, means, nullptr, 0, 0.0);
+        else mx_rows_kernel<false, MX_PLAIN><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales, means, nullptr, 0, 0.0);
     } else {
         if (f16) mx_cols_kernel<true><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales);
         else mx_cols_kernel<false><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales);
+    }
+    return hipGetLastError();
+}
+
+// Smoothed MXFP4 rows of the post-training FP4 baseline: Q less its bf16
+// block means (written to `means`), or K less its token mean (the fp64 token
+// sums go to the workspace first; mu to `means` when not null).
+hipError_t launch_quant_mx_smooth(const Dense& x, bool f16, int B, int H, int N, int d, bool key, double eps,
+                                  uint8_t* codes, uint8_t* scales, float* means, void* ws, hipStream_t st) {
+    const int BH = B * H, grid = BH * ((N + 127) / 128);
+    if (!key) {
+        if (f16) mx_rows_kernel<true, MX_QBLOCK><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales, means, nullptr, 0, 0.0);
+        else mx_rows_kernel<false, MX_QBLOCK><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales, means, nullptr, 0, 0.0);
+        return hipGetLastError();
+    }
+    const int nch = chunks_for(BH, N), rpc = (N + nch - 1) / nch;
+    double* part = (double*)ws;
+    if (f16) {
+        col_partial_kernel<true, true><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
+        mx_rows_kernel<true, MX_KMEAN><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales, means, part, nch, eps);
+    } else {
+        col_partial_kernel<false, true><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
+        mx_rows_kernel<false, MX_KMEAN><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales, means, part, nch, eps);
     }
     return hipGetLastError();
 }

@@ -10,9 +10,10 @@ from __future__ import annotations
 import torch
 
 from . import (BQA_FP8E4M3, BQA_INT8, BQA_MXFP4, BQA_OP_FWD, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_KV,
-               BQA_OP_QUANTIZE_V, BQA_OP_BWD, BQA_QAT_MXFP4, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V, BQA_SAGE_I8_F16PV,
-               BQA_SAGE_I8_F8PV, BQA_SAGE_I8_I8PV, BQA_THRIFT, bqa_attn_bwd, bqa_attn_fwd, bqa_quantize_blocks,
-               bqa_quantize_kv, bqa_select_blocks, bqa_workspace_size, dense, max_sel, problem, qtensor)
+               BQA_OP_QUANTIZE_V, BQA_OP_BWD, BQA_PTQ_MXFP4, BQA_QAT_MXFP4, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V,
+               BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV, BQA_SAGE_I8_I8PV, BQA_THRIFT, bqa_attn_bwd, bqa_attn_fwd,
+               bqa_attn_fwd_ptq, bqa_quantize_blocks, bqa_quantize_kv, bqa_select_blocks, bqa_workspace_size, dense,
+               max_sel, problem, qtensor)
 
 
 def sage_problem(B, Hq, Hkv, Nq, Nk, d, causal, mode, q_block=128, k_block=64, smooth_k=True, smooth_eps=0.0,
@@ -184,6 +185,56 @@ class QatTrainStep(QatPath):
         self.forward()
         self.backward()
         return self.dq, self.dk, self.dv
+
+
+def ptq_problem(B, Hq, Hkv, Nq, Nk, d, causal=False, smooth_k=True, sm_scale=0.0):
+    return problem(B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d, causal=int(causal), sm_scale=sm_scale,
+                   mode=BQA_PTQ_MXFP4, smooth_k=int(smooth_k), smooth_eps=0.0)
+
+
+class PtqPath:
+    """The post-training FP4 baseline: Q smoothed by its bf16 128-row block
+    means and K by its token mean before MXFP4, V in MXFP4 along tokens, then
+    attention with the means' score shifts and two-level P."""
+
+    def __init__(self, p, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+        dev = q.device
+        self.p = p
+        B, Hq, Hkv, Nq, Nk, d = p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d
+        self.q, self.k, self.v = q, k, v
+        u8 = torch.uint8
+        self.qc = torch.empty((B, Hq, Nq, d // 2), dtype=u8, device=dev)
+        self.qs = torch.empty((B, Hq, Nq, d // 32), dtype=u8, device=dev)
+        self.kc = torch.empty((B, Hkv, Nk, d // 2), dtype=u8, device=dev)
+        self.ks = torch.empty((B, Hkv, Nk, d // 32), dtype=u8, device=dev)
+        self.vc = torch.empty((B, Hkv, d, Nk // 2), dtype=u8, device=dev)
+        self.vs = torch.empty((B, Hkv, d, Nk // 32), dtype=u8, device=dev)
+        self.qq = qtensor(BQA_MXFP4, 0, 32, self.qc, self.qs)
+        self.kq = qtensor(BQA_MXFP4, 0, 32, self.kc, self.ks)
+        self.vq = qtensor(BQA_MXFP4, 1, 32, self.vc, self.vs)
+        self.qbar = torch.empty((B, Hq, (Nq + 127) // 128, d), dtype=torch.float32, device=dev)
+        self.mu = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev)
+        self.o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+        self.ws_k = torch.empty(max(bqa_workspace_size(p, BQA_OP_QUANTIZE_K), 16), dtype=u8, device=dev)
+        self.ws = torch.empty(max(bqa_workspace_size(p, BQA_OP_FWD), 16), dtype=u8, device=dev)
+        self._qd, self._kd, self._vd = dense(q), dense(k), dense(v)
+        self._od = dense(self.o)
+
+    def quantize(self):
+        bqa_quantize_blocks(self.p, BQA_ROLE_Q, self._qd, self.qq, block_means=self.qbar)
+        bqa_quantize_blocks(self.p, BQA_ROLE_K, self._kd, self.kq, k_mean=self.mu if self.p.smooth_k else None,
+                            workspace=self.ws_k)
+        bqa_quantize_blocks(self.p, BQA_ROLE_V, self._vd, self.vq)
+
+    def forward(self):
+        bqa_attn_fwd_ptq(self.p, q=self.qq, k=self.kq, v=self.vq, q_means=self.qbar, o=self._od, lse=self.lse,
+                         workspace=self.ws)
+
+    def step(self):
+        self.quantize()
+        self.forward()
+        return self.o
 
 
 def thrift_problem(B, Hq, Hkv, Nq, Nk, d, budget_ppm=50_000, causal=True, num_splits=0, sm_scale=0.0):

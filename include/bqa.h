@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define BQA_ABI_VERSION 2
+#define BQA_ABI_VERSION 3
 
 typedef int32_t bqa_status;
 enum {
@@ -77,7 +77,8 @@ typedef enum {
     BQA_SAGE_I8_F8PV = 1,     /* INT8 Q K^T, P = e4m3(448 P) and per-channel e4m3 V */
     BQA_SAGE_I8_I8PV = 2,     /* INT8 Q K^T, P int8 per (row, key tile), per-channel int8 V; trainable */
     BQA_QAT_MXFP4 = 3,        /* Attn-QAT: MXFP4 Q, K, P, V; optional bf16 auxiliary output O' */
-    BQA_THRIFT = 4            /* ThriftAttention: selected block pairs in bf16, the rest MXFP4 */
+    BQA_THRIFT = 4,           /* ThriftAttention: selected block pairs in bf16, the rest MXFP4 */
+    BQA_PTQ_MXFP4 = 5         /* post-training FP4 baseline: smoothed MXFP4 Q, K; two-level P; MXFP4 V */
 } bqa_mode;
 
 typedef enum {
@@ -167,6 +168,16 @@ size_t bqa_workspace_size(const bqa_problem* p, int32_t op);
  *    nearest-even, saturating at 6.  With block_means != NULL and role Q or K
  *    the means over each p->sel_block tokens are written as fp32
  *    [B, H, N / sel_block, d] ("ThriftAttention", Method step 1).
+ *  - BQA_PTQ_MXFP4, Q and K (MXFP4 axis 0, d = 128): the smoothing of the
+ *    post-training FP4 method that Attn-QAT is compared with ("Attn-QAT",
+ *    technical summary §1 and §2 Implementation: SageAttention3-style Q/K
+ *    smoothing).  Q: per block of 128 rows (the last may be short) the mean
+ *    of its rows, summed in fp64, rounded to fp32 and then to bf16, is written
+ *    to block_means (required, fp32 [B, Hq, ceil(Nq / 128), d], 16-byte
+ *    aligned) and the codes are those of fp32(Q - mean).  K with
+ *    p->smooth_k: mu = fp32(sum_t K / N - eps) as for the Sage modes, to
+ *    k_mean when not NULL, codes of fp32(K - mu); workspace
+ *    bqa_workspace_size(p, BQA_OP_QUANTIZE_K) bytes.  V as for MXFP4 V.
  *  A block whose amax is 0 (or whose inverse scale overflows fp32) gets
  *  scale 0 and all-zero codes.
  * `x` is [B, H, N, d] bf16 (fp16 for Q, K, V allowed in BQA_SAGE_I8_F16PV).
@@ -257,6 +268,30 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Post-training FP4 attention in the SageAttention3 style, the baseline the
+ * Attn-QAT pages compare against ("Attn-QAT", technical summary §1: PTQ with
+ * Q/K smoothing and two-level quantisation; the two-level step as in
+ * "ThriftAttention", Method step 2).  p->mode must be BQA_PTQ_MXFP4; d = 128,
+ * Nk a multiple of 128; causal allowed (bottom-right); Hq a multiple of Hkv.
+ * q, k: the MXFP4 codes bqa_quantize_blocks writes for the smoothed Q and K;
+ * q_means: the bf16 block means it wrote for Q (fp32 [B, Hq, ceil(Nq/128), d],
+ * 16-byte aligned); v: MXFP4 along tokens.  The score of query row i in
+ * block I against key j is tau (q^_i . k^_j + qbar_I . k^_j): the smoothed
+ * product on the scaled FP4 matrix instructions plus the block mean's
+ * product with the dequantised key (bf16 products, fp32 sums, computed once
+ * per call into the workspace).  Keys are visited in blocks of 128 in
+ * ascending order; in each block P is quantised in two levels (scaled so the
+ * row's largest P in the block is 6, then MXFP4 per 32 keys, the factor
+ * undone in fp32) and merged by FlashAttention-2's online softmax.  Output
+ * o [B, Hq, Nq, d] bf16; lse (fp32 [B, Hq, Nq]) when not NULL.  Workspace:
+ * bqa_workspace_size(p, BQA_OP_FWD) = B Hq ceil(Nq/128) Nk 4 bytes, 16-byte
+ * aligned; two calls that run at the same time must not share it.
+ */
+bqa_status bqa_attn_fwd_ptq(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
+                            const bqa_qtensor* v, const float* q_means, bqa_tensor* o, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * ThriftAttention decode for callers that cannot allocate (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same computation and arguments as bqa_attn_fwd in BQA_THRIFT mode with
@@ -320,6 +355,26 @@ bqa_status bqa_debug_qk_scores(const bqa_problem* p, const bqa_qtensor* q, const
  * value times 2^e that is a finite bf16 value is exact.
  */
 bqa_status bqa_debug_mx_dequant(const void* codes, const void* scales, int64_t nblocks, void* out, void* stream);
+
+/*
+ * Measurement hook: rate probes for the roofline's denominators.  Each runs
+ * `grid` workgroups of 256 threads and is timed by the caller (events on
+ * `stream`).  Matrix probes: every wavefront issues iters x 8 dense matrix
+ * instructions of one type on register operands (4 independent accumulator
+ * chains): BQA_PROBE_MFMA_I8 (32x32x32 int8, 65536 ops each),
+ * BQA_PROBE_MFMA_F8 (32x32x64 e4m3, 131072), BQA_PROBE_MFMA_F4 (32x32x64
+ * scaled e2m1, 131072), BQA_PROBE_MFMA_BF16 (32x32x16 bf16, 32768).
+ * BQA_PROBE_EXP: every thread runs iters x 8 v_exp_f32.  These write one
+ * checksum word per workgroup to dst (bytes >= 4 grid, 4-byte aligned; src
+ * unused).  BQA_PROBE_COPY: copies `bytes` (a multiple of 16, both pointers
+ * 16-byte aligned) from src to dst with 16-byte accesses; iters unused.
+ */
+enum {
+    BQA_PROBE_MFMA_I8 = 0, BQA_PROBE_MFMA_F8 = 1, BQA_PROBE_MFMA_F4 = 2, BQA_PROBE_MFMA_BF16 = 3,
+    BQA_PROBE_EXP = 4, BQA_PROBE_COPY = 5
+};
+bqa_status bqa_debug_probe(int32_t kind, int32_t grid, int64_t iters, const void* src, void* dst, size_t bytes,
+                           void* stream);
 
 #ifdef __cplusplus
 }

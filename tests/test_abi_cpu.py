@@ -253,3 +253,56 @@ def test_decode_static_validation(L):
     # 64 batches x 32 heads x 128 splits x 132 floats = 138 MB of partials > the 16 MiB static array
     assert dec(_p(**dict(th, B=64, num_splits=128))) == bqa.BQA_E_TOO_LARGE
     assert _nodev(dec(_p(**th)))                                                  # c5d: 4.3 MB of partials
+
+
+def test_ptq_validation(L):
+    x = _dense()
+    pt = dict(mode=bqa.BQA_PTQ_MXFP4, B=1, Hq=4, Hkv=2, Nq=300, Nk=512, causal=0, smooth_k=1)
+    mq, mk, mv = _q(fmt=bqa.BQA_MXFP4, block=32), _q(fmt=bqa.BQA_MXFP4, block=32), \
+        _q(fmt=bqa.BQA_MXFP4, axis=1, block=32)
+
+    def quant(p, role, out, means=None, kmean=None, ws=0x40000, wsb=1 << 30):
+        return bqa.lib().bqa_quantize_blocks(C.byref(p), role, C.byref(x), C.byref(out), kmean, means, ws, wsb, None)
+
+    # Q smoothing writes its block means: required, 16-byte aligned
+    assert quant(_p(**pt), bqa.BQA_ROLE_Q, mq) == bqa.BQA_E_NULL
+    assert quant(_p(**pt), bqa.BQA_ROLE_Q, mq, means=0x50004) == bqa.BQA_E_ALIGN
+    assert quant(_p(**dict(pt, d=64)), bqa.BQA_ROLE_Q, mq, means=0x50000) == bqa.BQA_E_UNSUPPORTED
+    # K smoothing: token sums in the workspace; no block means for K
+    need = bqa.bqa_workspace_size(_p(**pt), bqa.BQA_OP_QUANTIZE_K)
+    assert need > 0 and bqa.bqa_workspace_size(_p(**dict(pt, smooth_k=0)), bqa.BQA_OP_QUANTIZE_K) == 0
+    assert quant(_p(**pt), bqa.BQA_ROLE_K, mk, wsb=need - 1) == bqa.BQA_E_WORKSPACE
+    assert quant(_p(**pt), bqa.BQA_ROLE_K, mk, means=0x50000) == bqa.BQA_E_UNSUPPORTED
+
+    def fwd(p, qm=0x60000, ws=0x70000, wsb=None):
+        wsb = bqa.bqa_workspace_size(p, bqa.BQA_OP_FWD) if wsb is None else wsb
+        return bqa.lib().bqa_attn_fwd_ptq(C.byref(p), C.byref(mq), C.byref(mk), C.byref(mv), qm, C.byref(x), None,
+                                          ws, wsb, None)
+    # score shifts: B Hq ceil(Nq / 128) Nk fp32
+    assert bqa.bqa_workspace_size(_p(**pt), bqa.BQA_OP_FWD) == 1 * 4 * 3 * 512 * 4
+    assert fwd(_p(**dict(pt, mode=bqa.BQA_THRIFT))) == bqa.BQA_E_UNSUPPORTED
+    assert fwd(_p(**dict(pt, Nk=500))) == bqa.BQA_E_UNSUPPORTED
+    assert fwd(_p(**pt), qm=None) == bqa.BQA_E_NULL
+    assert fwd(_p(**pt), qm=0x60008) == bqa.BQA_E_ALIGN
+    assert fwd(_p(**pt), wsb=1000) == bqa.BQA_E_WORKSPACE
+    # the plain forward does not take this mode
+    assert bqa.lib().bqa_attn_fwd(C.byref(_p(**pt)), C.byref(mq), C.byref(mk), C.byref(mv), None, None, None, None,
+                                  None, C.byref(x), None, None, None, 0x70000, 1 << 30, None) == bqa.BQA_E_UNSUPPORTED
+    assert _nodev(fwd(_p(**pt)))
+    assert _nodev(quant(_p(**pt), bqa.BQA_ROLE_Q, mq, means=0x50000))
+    assert _nodev(quant(_p(**pt), bqa.BQA_ROLE_K, mk))
+
+
+def test_probe_validation(L):
+    P = bqa.lib().bqa_debug_probe
+    assert P(9, 16, 10, None, 0x1000, 4096, None) == bqa.BQA_E_UNSUPPORTED
+    assert P(bqa.BQA_PROBE_MFMA_I8, 0, 10, None, 0x1000, 4096, None) == bqa.BQA_E_SHAPE
+    assert P(bqa.BQA_PROBE_MFMA_I8, 16, -1, None, 0x1000, 4096, None) == bqa.BQA_E_SHAPE
+    assert P(bqa.BQA_PROBE_MFMA_I8, 16, 10, None, None, 4096, None) == bqa.BQA_E_NULL
+    assert P(bqa.BQA_PROBE_MFMA_I8, 16, 10, None, 0x1002, 4096, None) == bqa.BQA_E_ALIGN
+    assert P(bqa.BQA_PROBE_EXP, 2048, 10, None, 0x1000, 4096, None) == bqa.BQA_E_SHAPE      # 4 bytes per workgroup
+    assert P(bqa.BQA_PROBE_COPY, 16, 0, None, 0x1000, 4096, None) == bqa.BQA_E_NULL
+    assert P(bqa.BQA_PROBE_COPY, 16, 0, 0x2008, 0x1000, 4096, None) == bqa.BQA_E_ALIGN
+    assert P(bqa.BQA_PROBE_COPY, 16, 0, 0x2000, 0x1000, 4100, None) == bqa.BQA_E_ALIGN
+    assert _nodev(P(bqa.BQA_PROBE_MFMA_F4, 16, 10, None, 0x1000, 4096, None))
+    assert _nodev(P(bqa.BQA_PROBE_COPY, 16, 0, 0x2000, 0x1000, 4096, None))
