@@ -88,6 +88,8 @@ def _declare(L):
         "orc_thrift_decode": (None, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d,
                                      i, i, vp, vp]),
         "orc_ptq_fwd": (None, [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, vp, vp]),
+        "orc_qk_norm": (None, [vp, C.c_int64, i, vp, vp]),
+        "orc_qk_norm_bwd": (None, [vp, vp, vp, C.c_int64, i, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -217,6 +219,28 @@ def smooth_q_blocks(Q: np.ndarray, blk: int = 128):
         qbar[:, I] = round_to((s / rows.shape[1]).astype(np.float32), "bf16")
     Qs = (Q - np.repeat(qbar, blk, axis=1)[:, :N]).astype(np.float32)
     return qbar, Qs
+
+
+def qk_norm(X: np.ndarray):
+    """QK-norm forward ("SageBwd" Methodology 4): X [..., d] -> (Y, r) with
+    r = fp32(1/sqrt(sum x^2)) per row and Y = bf16(fp32(x r))."""
+    X = _f32(X)
+    d = X.shape[-1]
+    rows = X.size // d
+    Y = np.empty_like(X)
+    r = np.empty(X.shape[:-1], np.float32)
+    lib().orc_qk_norm(_p(X), rows, d, _p(Y), _p(r))
+    return Y, r
+
+
+def qk_norm_bwd(X: np.ndarray, r: np.ndarray, G: np.ndarray) -> np.ndarray:
+    """Gradient with respect to the raw rows X of y = x / |x| given dL/dy = G."""
+    X = _f32(X)
+    d = X.shape[-1]
+    G = np.ascontiguousarray(G, dtype=np.float64)
+    dX = np.empty(X.shape, np.float64)
+    lib().orc_qk_norm_bwd(_p(X), _p(_f32(r)), _p(G), X.size // d, d, _p(dX))
+    return dX
 
 
 def smooth_k(K: np.ndarray, eps: float = 0.0):

@@ -1072,3 +1072,36 @@ void orc_ptq_fwd(const uint8_t* qc, const uint8_t* qs, const float* qbar, const 
     }
     free(bias);
 }
+
+/* ========================================================================
+ * QK-norm ([SB] Methodology 4 and Practical implications: every query and
+ * key row is scaled to unit L2 norm before the dot product)
+ * ====================================================================== */
+
+/* Forward, row by row: S = sum_c x_c^2 in fp64 (exact for bf16 rows),
+ * r = fp32(1 / sqrt(S)) from the fp64 value (r = 0 for a zero row), and the
+ * normalised row y_c = bf16(fp32(x_c r)), the bf16 output a model's QK-norm
+ * layer would hand to the attention.  r is kept for the backward. */
+void orc_qk_norm(const float* X, int64_t rows, int d, float* Y, float* r) {
+    for (int64_t i = 0; i < rows; ++i) {
+        const float* x = X + (size_t)i * d;
+        double S = 0.0;
+        for (int c = 0; c < d; ++c) S += (double)x[c] * (double)x[c];
+        float ri = S > 0.0 ? (float)(1.0 / sqrt(S)) : 0.0f;
+        r[i] = ri;
+        for (int c = 0; c < d; ++c) Y[(size_t)i * d + c] = (float)orc_bf16_value((double)(x[c] * ri));
+    }
+}
+
+/* Backward of y = x / |x| with the bf16 rounding of y passed straight
+ * through: with y = x r (unrounded), dx = r (g - y (y . g)), in fp64. */
+void orc_qk_norm_bwd(const float* X, const float* r, const double* G, int64_t rows, int d, double* dX) {
+    for (int64_t i = 0; i < rows; ++i) {
+        const float* x = X + (size_t)i * d;
+        const double* g = G + (size_t)i * d;
+        double ri = (double)r[i], t = 0.0;
+        for (int c = 0; c < d; ++c) t += (double)x[c] * ri * g[c];
+        for (int c = 0; c < d; ++c) dX[(size_t)i * d + c] = ri * (g[c] - (double)x[c] * ri * t);
+    }
+}
+

@@ -95,6 +95,8 @@ void orc_thrift_decode(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, 
 void orc_ptq_fwd(const uint8_t* qc, const uint8_t* qs, const float* qbar, const uint8_t* kc, const uint8_t* ks,
                  const uint8_t* vc_t, const uint8_t* vs_t, int Nq, int Nk, int d, int blk, int causal, double tau,
                  int qb0, int qb1, double* O, double* lse);
+void orc_qk_norm(const float* X, int64_t rows, int d, float* Y, float* r);
+void orc_qk_norm_bwd(const float* X, const float* r, const double* G, int64_t rows, int d, double* dX);
 
 #ifdef __cplusplus
 }
