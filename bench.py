@@ -9,6 +9,8 @@ Workloads (``--workload``, default c2):
       inputs: K-smoothing (eps 1e-3), INT8 forward, INT8 backward with the
       bf16 dP = dO V^T; `value` counts forward + backward (14 B H N^2 d / 2)
       and the roofline covers the backward call.
+  c3n the same step from raw (unnormalised) Q, K rows with QK-norm fused
+      into the INT8 quantiser and its backward into the dQ / dK epilogues.
   c4  Attn-QAT FP4 forward at B=1, H=32, N=16384, d=128, non-causal,
       Student-t inputs: MXFP4 Q, K, V, fused attention with MXFP4 P.V and
       the bf16 auxiliary output O'.
@@ -36,7 +38,7 @@ time, measured with HIP events on the stream it runs on, against the dense
 matrix-core peak of its operand types.  `cpu_baseline` times the CPU oracle
 on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--workload c2|c3|c4|c4t|c4i|c4p|c5|c5d] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--workload c2|c3|c3n|c4|c4t|c4i|c4p|c5|c5d] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -427,13 +429,17 @@ def _sagebwd_case(w, bqa, torch):
     p = sage_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.causal, bqa.BQA_SAGE_I8_I8PV, q_block=128,
                      smooth_k=True, smooth_eps=1e-3)
     path = SageTrainStep(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"), to_device(dO, "bf16"))
+    return dict(_sagebwd_roofline(w), path=path)
+
+
+def _sagebwd_roofline(w):
     n_pairs = w.B * w.Hq * w.Nq * (w.Nq + 1) / 2
     bwd_ops = 10.0 * w.d * n_pairs          # S recompute, dP, dV, dQ, dK
     ops = 14.0 * w.B * w.Hq * w.Nq * w.Nk * w.d / 2
     # backward roofline: 4 of the 5 products at the i8 rate, dP at the bf16 rate
     t_peak = 0.8 * bwd_ops / (PEAK_I8_TOPS * 1e12) + 0.2 * bwd_ops / (PEAK_BF16_TFLOPS * 1e12)
     return dict(
-        path=path, ops=ops, dtype="i8+bf16", timed="backward",
+        ops=ops, dtype="i8+bf16", timed="backward",
         workload="SageBwd training step (c3): B=1 H=16 N=8192 d=128 causal, QK-norm bf16 in, K-smoothing eps=1e-3, "
                  "INT8 Q/K/V/P forward; backward with INT8 dO/P/dS and bf16 dP; step = quantise + forward + backward",
         roofline={"bound": "mfma", "kernel": "attn_bwd (delta, dO quantiser, code transposes, sbwd_dkdv_kernel, "
@@ -442,6 +448,24 @@ def _sagebwd_case(w, bqa, torch):
                   "peak_note": "i8 peak for 4 of the 5 backward products, bf16 for dP = dO V^T",
                   "ops_per_launch": bwd_ops},
         traffic_key="sbwd_dkdv_kernel", cpu=cpu_baseline_sagebwd)
+
+
+def _sagebwd_qknorm_case(w, bqa, torch):
+    from bit_quantized_attention_amd.runner import SageQkNormTrainStep, sage_problem, to_device
+    import workloads as wl
+    Qr, Kr, V, dO = (wl.build(w, t) for t in ("qraw", "kraw", "v", "do"))
+    p = sage_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.causal, bqa.BQA_SAGE_I8_I8PV, q_block=128,
+                     smooth_k=True, smooth_eps=1e-3)
+    path = SageQkNormTrainStep(p, to_device(Qr, "bf16"), to_device(Kr, "bf16"), to_device(V, "bf16"),
+                               to_device(dO, "bf16"))
+    case = _sagebwd_roofline(w)
+    case.update(path=path, workload="SageBwd training step with QK-norm fused (c3n): B=1 H=16 N=8192 d=128 causal, "
+                                    "raw bf16 Q/K rows normalised inside the INT8 quantiser, K-smoothing eps=1e-3, "
+                                    "INT8 forward; backward with the QK-norm backward in the dQ/dK epilogues; step = "
+                                    "fused quantise + forward + backward")
+    case["roofline"] = dict(case["roofline"], kernel="attn_bwd_qknorm (delta, dO quantiser, code transposes, "
+                                                      "sbwd_dkdv_kernel, sbwd_dq_kernel with the norm epilogues)")
+    return case
 
 
 def cpu_baseline_qat_train(w, budget_s: float = 25.0):
@@ -535,26 +559,36 @@ def probe_main(torch, bqa):
     it_exp = 100000
     t = timed(lambda: bqa.bqa_debug_probe(bqa.BQA_PROBE_EXP, grid, it_exp, None, out, out.numel()))
     v = grid * 256 * it_exp * 8 / t / 1e12
-    # one transcendental per lane every 4 clocks on each SIMD (16 lanes / clock), 2.4 GHz
-    spec = n_cu * 4 * 16 * 2.4e9 / 1e12
+    # one v_exp_f32 per lane every 8 clocks on each SIMD (8 lanes / clock), 2.4 GHz
+    spec = n_cu * 4 * 8 * 2.4e9 / 1e12
     res["v_exp_f32"] = {"measured": round(v, 3), "peak": round(spec, 3), "unit": "T exp/s",
                         "frac": round(v / spec, 4), "time_ms": round(t * 1e3, 3),
-                        "peak_note": "16 lanes per clock per SIMD, 4 SIMDs per CU, 2.4 GHz (with one fp32 "
-                                     "subtraction per exponential in the loop)"}
+                        "peak_note": "8 lanes per clock per SIMD (a wavefront instruction every 8 clocks), "
+                                     "4 SIMDs per CU, 2.4 GHz"}
     nbytes = 1 << 30
     src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
-    t = timed(lambda: bqa.bqa_debug_probe(bqa.BQA_PROBE_COPY, 8 * n_cu, 0, src, dst, nbytes))
-    v = 2 * nbytes / t / 1e9
-    res["hbm_copy"] = {"measured": round(v, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(v / 8000.0, 4),
-                       "time_ms": round(t * 1e3, 3), "note": "1 GiB read + 1 GiB written per launch"}
+    for name, kind, g in (("hbm_copy", bqa.BQA_PROBE_COPY, 8 * n_cu), ("hbm_copy_wide", bqa.BQA_PROBE_COPY, 32 * n_cu)):
+        t = timed(lambda: bqa.bqa_debug_probe(kind, g, 0, src, dst, nbytes))
+        v = 2 * nbytes / t / 1e9
+        res[name] = {"measured": round(v, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(v / 8000.0, 4),
+                     "time_ms": round(t * 1e3, 3), "grid": g, "note": "1 GiB read + 1 GiB written per launch"}
     assert torch.equal(dst[:4096], src[:4096])
+    t = timed(lambda: dst.copy_(src))
+    v = 2 * nbytes / t / 1e9
+    res["hbm_copy_torch"] = {"measured": round(v, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(v / 8000.0, 4),
+                             "time_ms": round(t * 1e3, 3), "note": "torch copy_ of the same buffers"}
+    for name, g in (("hbm_read", 8 * n_cu), ("hbm_read_wide", 32 * n_cu)):
+        t = timed(lambda: bqa.bqa_debug_probe(bqa.BQA_PROBE_READ, g, 0, src, out, nbytes))
+        v = nbytes / t / 1e9
+        res[name] = {"measured": round(v, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(v / 8000.0, 4),
+                     "time_ms": round(t * 1e3, 3), "grid": g, "note": "1 GiB read per launch"}
     print(json.dumps({"probes": res, "compute_units": n_cu, "grid_matrix": grid, "iters_matrix": iters}), flush=True)
 
 
-CASES = {"c2": _sage_case, "c3": _sagebwd_case, "c4": _qat_case, "c4t": _qat_train_case, "c4i": _qat_infer_case,
+CASES = {"c2": _sage_case, "c3": _sagebwd_case, "c3n": _sagebwd_qknorm_case, "c4": _qat_case, "c4t": _qat_train_case, "c4i": _qat_infer_case,
          "c4p": _ptq_case, "c5": _thrift_case, "c5d": _decode_case}
-INPUTS_OF = {"c4t": "c4", "c4i": "c4", "c4p": "c4"}        # workloads that reuse another's inputs
+INPUTS_OF = {"c3n": "c3", "c4t": "c4", "c4i": "c4", "c4p": "c4"}        # workloads that reuse another's inputs
 
 
 def main():

@@ -33,8 +33,10 @@ BQA_OP_QUANTIZE_Q, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_V, BQA_OP_QUANTIZE_DO, BQA
 
 EXPORTS = ["bqa_abi_version", "bqa_status_string", "bqa_workspace_size", "bqa_quantize_blocks", "bqa_quantize_kv",
            "bqa_select_blocks", "bqa_attn_fwd", "bqa_attn_bwd", "bqa_debug_qk_scores", "bqa_attn_decode_static",
-           "bqa_debug_mx_dequant", "bqa_attn_fwd_ptq", "bqa_debug_probe"]
-BQA_PROBE_MFMA_I8, BQA_PROBE_MFMA_F8, BQA_PROBE_MFMA_F4, BQA_PROBE_MFMA_BF16, BQA_PROBE_EXP, BQA_PROBE_COPY = range(6)
+           "bqa_debug_mx_dequant", "bqa_attn_fwd_ptq", "bqa_debug_probe", "bqa_quantize_qknorm",
+           "bqa_attn_bwd_qknorm"]
+BQA_PROBE_MFMA_I8, BQA_PROBE_MFMA_F8, BQA_PROBE_MFMA_F4, BQA_PROBE_MFMA_BF16, BQA_PROBE_EXP, BQA_PROBE_COPY, \
+    BQA_PROBE_READ = range(7)
 
 
 class BqaError(RuntimeError):
@@ -101,6 +103,13 @@ def lib():
         L.bqa_attn_fwd_ptq.restype = C.c_int32
         L.bqa_attn_fwd_ptq.argtypes = [P(bqa_problem), P(bqa_qtensor), P(bqa_qtensor), P(bqa_qtensor), vp,
                                        P(bqa_tensor), vp, vp, C.c_size_t, vp]
+        L.bqa_quantize_qknorm.restype = C.c_int32
+        L.bqa_quantize_qknorm.argtypes = [P(bqa_problem), C.c_int32, P(bqa_tensor), P(bqa_qtensor), vp, vp, vp,
+                                          C.c_size_t, vp]
+        L.bqa_attn_bwd_qknorm.restype = C.c_int32
+        L.bqa_attn_bwd_qknorm.argtypes = [P(bqa_problem), P(bqa_qtensor), P(bqa_qtensor), P(bqa_tensor),
+                                          P(bqa_tensor), vp, P(bqa_tensor), P(bqa_tensor), P(bqa_tensor), vp, vp,
+                                          P(bqa_tensor), P(bqa_tensor), P(bqa_tensor), vp, C.c_size_t, vp]
         L.bqa_debug_probe.restype = C.c_int32
         L.bqa_debug_probe.argtypes = [C.c_int32, C.c_int32, C.c_int64, vp, vp, C.c_size_t, vp]
         L.bqa_debug_mx_dequant.restype = C.c_int32
@@ -280,6 +289,34 @@ def bqa_attn_decode_static(p, q=None, k=None, v=None, q_hi=None, k_hi=None, v_hi
                                      _stream(stream))
     if check:
         _check(s, "bqa_attn_decode_static")
+    return s
+
+
+def bqa_quantize_qknorm(p, role, x, out: bqa_qtensor, inv_norm=None, k_mean=None, workspace=None,
+                        workspace_bytes=None, stream=None, check=True) -> int:
+    xd = x if isinstance(x, bqa_tensor) else dense(x)
+    wb = workspace_bytes if workspace_bytes is not None else (workspace.numel() * workspace.element_size()
+                                                              if workspace is not None else 0)
+    s = lib().bqa_quantize_qknorm(C.byref(p), int(role), _ref(xd), C.byref(out), _ptr(inv_norm), _ptr(k_mean),
+                                  _ptr(workspace), wb, _stream(stream))
+    if check:
+        _check(s, "bqa_quantize_qknorm")
+    return s
+
+
+def bqa_attn_bwd_qknorm(p, q=None, k=None, v_hi=None, o_for_delta=None, lse=None, d_o=None, q_raw=None, k_raw=None,
+                        q_inv_norm=None, k_inv_norm=None, dq=None, dk=None, dv=None, workspace=None,
+                        workspace_bytes=None, stream=None, check=True) -> int:
+    def dd(t):
+        return t if (t is None or isinstance(t, bqa_tensor)) else dense(t)
+    wb = workspace_bytes if workspace_bytes is not None else (workspace.numel() * workspace.element_size()
+                                                              if workspace is not None else 0)
+    s = lib().bqa_attn_bwd_qknorm(C.byref(p), _ref(q), _ref(k), _ref(dd(v_hi)), _ref(dd(o_for_delta)), _ptr(lse),
+                                  _ref(dd(d_o)), _ref(dd(q_raw)), _ref(dd(k_raw)), _ptr(q_inv_norm),
+                                  _ptr(k_inv_norm), _ref(dd(dq)), _ref(dd(dk)), _ref(dd(dv)), _ptr(workspace), wb,
+                                  _stream(stream))
+    if check:
+        _check(s, "bqa_attn_bwd_qknorm")
     return s
 
 

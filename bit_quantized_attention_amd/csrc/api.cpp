@@ -125,6 +125,35 @@ bqa_status check_decode(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
     return BQA_OK;
 }
 
+// Validation and argument block of a SageBwd backward call.
+bqa_status check_sage_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k, const bqa_tensor* v_hi,
+                          const bqa_tensor* o_for_delta, const float* lse, const bqa_tensor* d_o, const bqa_tensor* dq,
+                          const bqa_tensor* dk, const bqa_tensor* dv, const void* ws, size_t ws_bytes,
+                          SageBwdArgs& a) {
+    if (p->d != 128 || p->Hq != p->Hkv || p->Nq != p->Nk || p->Nq % 128 != 0) return BQA_E_UNSUPPORTED;
+    if (p->q_block != 128 || p->k_block != 64) return BQA_E_UNSUPPORTED;
+    TRY(check_q(q, BQA_INT8, 0));
+    TRY(check_q(k, BQA_INT8, 0));
+    if (q->block != 128 || k->block != 64) return BQA_E_UNSUPPORTED;
+    TRY(check_dense(v_hi, false, true));
+    TRY(check_dense(o_for_delta, false, true));
+    TRY(check_dense(d_o, false, true));
+    TRY(check_dense(dq, false, true));
+    TRY(check_dense(dk, false, true));
+    TRY(check_dense(dv, false, true));
+    if (!lse) return BQA_E_NULL;
+    if (!ws || ws_bytes < ws_sage_bwd_bytes(p->B, p->Hq, p->Nq, p->d)) return BQA_E_WORKSPACE;
+    if (!aligned16(ws) || ((uintptr_t)lse & 15u)) return BQA_E_ALIGN;
+    a.qc = (const int8_t*)q->codes; a.qs = (const float*)q->scales;
+    a.kc = (const int8_t*)k->codes; a.ks = (const float*)k->scales;
+    a.v = as_dense(v_hi); a.d_o = as_dense(d_o); a.lse = lse;
+    a.dq = as_dense(dq); a.dk = as_dense(dk); a.dv = as_dense(dv);
+    a.B = p->B; a.H = p->Hq; a.N = p->Nq; a.causal = p->causal;
+    a.tau = tau_of(p);
+    a.c_log2 = a.tau * 1.4426950408889634f;
+    return BQA_OK;
+}
+
 // BQA_DEBUG=1: scan the call's floating-point inputs before it launches.
 DebugInput dbg16(const bqa_tensor* t, int B, int H, int N, int d) {
     if (!t) return DebugInput{nullptr, DebugInput::BF16, 0, 0, 0, 0, 0, 0, 0, 0};
@@ -454,6 +483,55 @@ bqa_status bqa_attn_fwd_ptq(const bqa_problem* p, const bqa_qtensor* q, const bq
     return launched(launch_ptq_fwd(a, q_means, ws, (hipStream_t)stream));
 }
 
+bqa_status bqa_quantize_qknorm(const bqa_problem* p, int32_t role, const bqa_tensor* x, bqa_qtensor* out,
+                               float* inv_norm, float* k_mean, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_problem(p));
+    if (!is_sage(p->mode) || p->d != 128) return BQA_E_UNSUPPORTED;
+    if (role != BQA_ROLE_Q && role != BQA_ROLE_K) return BQA_E_UNSUPPORTED;
+    if (!out || !inv_norm) return BQA_E_NULL;
+    const bool key = role == BQA_ROLE_K;
+    const int H = key ? p->Hkv : p->Hq, N = key ? p->Nk : p->Nq;
+    TRY(check_dense(x, true, true));
+    TRY(check_q(out, BQA_INT8, 0));
+    const int blk = out->block;
+    if ((blk != 64 && blk != 128) || N % blk != 0) return BQA_E_UNSUPPORTED;
+    if ((uintptr_t)inv_norm & 3u) return BQA_E_ALIGN;
+    const bool smooth = key && p->smooth_k;
+    if (smooth) {
+        if (!ws || ws_bytes < ws_kmean_bytes(p->B * H, N, p->d)) return BQA_E_WORKSPACE;
+        if (!std::isfinite(p->smooth_eps)) return BQA_E_SHAPE;
+    }
+    TRY(check_device());
+    TRY(debug_check(stream, {dbg16(x, p->B, H, N, p->d)}));
+    return launched(launch_quant_i8_qknorm(as_dense(x), x->dtype == BQA_FP16, p->B, H, N, p->d, blk, smooth,
+                                           (double)p->smooth_eps, smooth ? k_mean : nullptr, inv_norm, ws,
+                                           (int8_t*)out->codes, (float*)out->scales, (hipStream_t)stream));
+}
+
+bqa_status bqa_attn_bwd_qknorm(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
+                               const bqa_tensor* v_hi, const bqa_tensor* o_for_delta, const float* lse,
+                               const bqa_tensor* d_o, const bqa_tensor* q_raw, const bqa_tensor* k_raw,
+                               const float* q_inv_norm, const float* k_inv_norm, bqa_tensor* dq, bqa_tensor* dk,
+                               bqa_tensor* dv, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_problem(p));
+    if (!is_sage(p->mode)) return BQA_E_UNSUPPORTED;
+    SageBwdArgs a{};
+    TRY(check_sage_bwd(p, q, k, v_hi, o_for_delta, lse, d_o, dq, dk, dv, ws, ws_bytes, a));
+    TRY(check_dense(q_raw, false, true));
+    TRY(check_dense(k_raw, false, true));
+    if (!q_inv_norm || !k_inv_norm) return BQA_E_NULL;
+    if (((uintptr_t)q_inv_norm & 3u) || ((uintptr_t)k_inv_norm & 3u)) return BQA_E_ALIGN;
+    a.q_raw = as_dense(q_raw); a.k_raw = as_dense(k_raw);
+    a.q_rn = q_inv_norm; a.k_rn = k_inv_norm;
+    TRY(check_device());
+    const int64_t bhn = (int64_t)p->B * p->Hq * p->Nq;
+    TRY(debug_check(stream, {dbg16(v_hi, p->B, p->Hq, p->Nq, p->d), dbg16(o_for_delta, p->B, p->Hq, p->Nq, p->d),
+                             dbg16(d_o, p->B, p->Hq, p->Nq, p->d), dbg32(lse, bhn),
+                             dbg16(q_raw, p->B, p->Hq, p->Nq, p->d), dbg16(k_raw, p->B, p->Hq, p->Nq, p->d),
+                             dbg32(q_inv_norm, bhn), dbg32(k_inv_norm, bhn)}));
+    return launched(launch_sage_bwd(a, as_dense(o_for_delta), ws, (hipStream_t)stream));
+}
+
 bqa_status bqa_attn_decode_static(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
                                   const bqa_qtensor* v, const bqa_tensor* q_hi, const bqa_tensor* k_hi,
                                   const bqa_tensor* v_hi, const int32_t* sel_idx, const int32_t* sel_cnt,
@@ -478,29 +556,9 @@ bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
     (void)v;
     TRY(check_problem(p));
     hipStream_t st = (hipStream_t)stream;
-    if (p->mode == BQA_SAGE_I8_I8PV || p->mode == BQA_SAGE_I8_F8PV || p->mode == BQA_SAGE_I8_F16PV) {
-        if (p->d != 128 || p->Hq != p->Hkv || p->Nq != p->Nk || p->Nq % 128 != 0) return BQA_E_UNSUPPORTED;
-        if (p->q_block != 128 || p->k_block != 64) return BQA_E_UNSUPPORTED;
-        TRY(check_q(q, BQA_INT8, 0));
-        TRY(check_q(k, BQA_INT8, 0));
-        if (q->block != 128 || k->block != 64) return BQA_E_UNSUPPORTED;
-        TRY(check_dense(v_hi, false, true));
-        TRY(check_dense(o_for_delta, false, true));
-        TRY(check_dense(d_o, false, true));
-        TRY(check_dense(dq, false, true));
-        TRY(check_dense(dk, false, true));
-        TRY(check_dense(dv, false, true));
-        if (!lse) return BQA_E_NULL;
-        if (!ws || ws_bytes < ws_sage_bwd_bytes(p->B, p->Hq, p->Nq, p->d)) return BQA_E_WORKSPACE;
-        if (!aligned16(ws) || ((uintptr_t)lse & 15u)) return BQA_E_ALIGN;
+    if (is_sage(p->mode)) {
         SageBwdArgs a{};
-        a.qc = (const int8_t*)q->codes; a.qs = (const float*)q->scales;
-        a.kc = (const int8_t*)k->codes; a.ks = (const float*)k->scales;
-        a.v = as_dense(v_hi); a.d_o = as_dense(d_o); a.lse = lse;
-        a.dq = as_dense(dq); a.dk = as_dense(dk); a.dv = as_dense(dv);
-        a.B = p->B; a.H = p->Hq; a.N = p->Nq; a.causal = p->causal;
-        a.tau = tau_of(p);
-        a.c_log2 = a.tau * 1.4426950408889634f;
+        TRY(check_sage_bwd(p, q, k, v_hi, o_for_delta, lse, d_o, dq, dk, dv, ws, ws_bytes, a));
         TRY(check_device());
         const int64_t bhn = (int64_t)p->B * p->Hq * p->Nq;
         TRY(debug_check(stream, {dbg16(v_hi, p->B, p->Hq, p->Nq, p->d), dbg16(o_for_delta, p->B, p->Hq, p->Nq, p->d),
@@ -589,12 +647,15 @@ extern "C" bqa_status bqa_debug_mx_dequant(const void* codes, const void* scales
 
 extern "C" bqa_status bqa_debug_probe(int32_t kind, int32_t grid, int64_t iters, const void* src, void* dst,
                                       size_t bytes, void* stream) {
-    if (kind < BQA_PROBE_MFMA_I8 || kind > BQA_PROBE_COPY) return BQA_E_UNSUPPORTED;
+    if (kind < BQA_PROBE_MFMA_I8 || kind > BQA_PROBE_READ) return BQA_E_UNSUPPORTED;
     if (grid < 1 || grid > (1 << 20) || iters < 0 || iters > ((int64_t)1 << 30)) return BQA_E_SHAPE;
     if (!dst) return BQA_E_NULL;
     if (kind == BQA_PROBE_COPY) {
         if (!src) return BQA_E_NULL;
         if (!aligned16(src) || !aligned16(dst) || bytes % 16 != 0) return BQA_E_ALIGN;
+    } else if (kind == BQA_PROBE_READ) {
+        if (!src) return BQA_E_NULL;
+        if (!aligned16(src) || bytes % 16 != 0 || ((uintptr_t)dst & 3u)) return BQA_E_ALIGN;
     } else {
         if ((uintptr_t)dst & 3u) return BQA_E_ALIGN;
         if (bytes < (size_t)grid * 4) return BQA_E_SHAPE;

@@ -400,6 +400,35 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
         products(tv, tk);
         fold(tv, tk, sv_prev, sk_prev);
     }
+    if (a.k_rn) {
+        // QK-norm backward ("SageBwd", Methodology 4): dk = r (g - y (y . g))
+        // per key row, y = k_raw r; a row's channels span 32 lanes of 4 waves
+        __shared__ float red[4][TK];
+        const uint16_t* kr = (const uint16_t*)a.k_raw.p + b * a.k_raw.sB + hq * a.k_raw.sH;
+        float rr[16], y[16], t[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t kpos = (int64_t)J * TK + 32 * kh + 8 * (i >> 2) + 4 * h + (i & 3);
+            rr[i] = a.k_rn[(int64_t)bh * a.N + kpos];
+            y[i] = bf16_bits_to_f32(kr[kpos * a.k_raw.sN + crow]) * rr[i];
+            t[i] = y[i] * dk[i];
+        }
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) t[i] += __shfl_xor(t[i], off);
+        if (lq == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) red[qg][32 * kh + 8 * (i >> 2) + 4 * h + (i & 3)] = t[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int kl = 32 * kh + 8 * (i >> 2) + 4 * h + (i & 3);
+            const float T = (red[0][kl] + red[1][kl]) + (red[2][kl] + red[3][kl]);
+            dk[i] = rr[i] * (dk[i] - y[i] * T);
+        }
+    }
     uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sB + hq * a.dv.sH;
     uint16_t* dkp = (uint16_t*)a.dk.p + b * a.dk.sB + hq * a.dk.sH;
 #pragma unroll
@@ -563,6 +592,35 @@ __global__ __launch_bounds__(256, 2) void sbwd_dq_kernel(SageBwdArgs a) {
         barrier_only();
     }
     // dq[cb] reg i: query 32 w + 8 (i / 4) + 4 h + i % 4, channel 32 cb + lq
+    if (a.q_rn) {
+        // QK-norm backward: dq = r (g - y (y . g)), y = q_raw r; a row's
+        // channels span the 32 lanes of one half-wavefront (4 per lane)
+        const uint16_t* qr = (const uint16_t*)a.q_raw.p + b * a.q_raw.sB + hq * a.q_raw.sH;
+        float rr[16], t[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t row = (int64_t)I * TQ + 32 * w + 8 * (i >> 2) + 4 * h + (i & 3);
+            rr[i] = a.q_rn[(int64_t)bh * a.N + row];
+            float acc = 0.0f;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+                acc = __builtin_fmaf(bf16_bits_to_f32(qr[row * a.q_raw.sN + 32 * cb + lq]) * rr[i], dq[cb][i], acc);
+            t[i] = acc;
+        }
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) t[i] += __shfl_xor(t[i], off);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t row = (int64_t)I * TQ + 32 * w + 8 * (i >> 2) + 4 * h + (i & 3);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const float y = bf16_bits_to_f32(qr[row * a.q_raw.sN + 32 * cb + lq]) * rr[i];
+                dq[cb][i] = rr[i] * (dq[cb][i] - y * t[i]);
+            }
+        }
+    }
     uint16_t* dqp = (uint16_t*)a.dq.p + b * a.dq.sB + hq * a.dq.sH;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)

@@ -23,6 +23,9 @@ hipError_t launch_quant_kv(const Dense& k, const Dense& v, bool f16, int B, int 
                            hipStream_t st);
 hipError_t launch_quant_mx(const Dense& x, bool f16, int B, int H, int N, int d, int axis, uint8_t* codes,
                            uint8_t* scales, float* means, hipStream_t st);
+hipError_t launch_quant_i8_qknorm(const Dense& x, bool f16, int B, int H, int N, int d, int blk, bool smooth,
+                                  double eps, float* mu, float* inv_norm, void* ws, int8_t* codes, float* scales,
+                                  hipStream_t st);
 hipError_t launch_quant_mx_smooth(const Dense& x, bool f16, int B, int H, int N, int d, bool key, double eps,
                                   uint8_t* codes, uint8_t* scales, float* means, void* ws, hipStream_t st);
 
@@ -76,6 +79,10 @@ struct SageBwdArgs {
     Dense dq, dk, dv;                                    // outputs bf16
     int B, H, N, causal;
     float c_log2, tau;
+    // QK-norm backward in the dQ / dK epilogues (null: gradients of the
+    // normalised rows): raw Q, K [B,H,N,d] bf16 and their inverse norms [B,H,N]
+    Dense q_raw, k_raw;
+    const float* q_rn; const float* k_rn;
 };
 size_t ws_sage_bwd_bytes(int B, int H, int N, int d);
 hipError_t launch_sage_bwd(SageBwdArgs a, Dense o, void* ws, hipStream_t st);
@@ -154,7 +161,8 @@ bool debug_enabled();
 int debug_scan(hipStream_t st, const DebugInput* in, int n_in);   // 1 found, 0 clean, -1 HIP error
 
 // ---- rate probes (probe.hip); the kinds are the BQA_PROBE_* values of bqa.h
-enum { PROBE_MFMA_I8 = 0, PROBE_MFMA_F8 = 1, PROBE_MFMA_F4 = 2, PROBE_MFMA_BF16 = 3, PROBE_EXP = 4, PROBE_COPY = 5 };
+enum { PROBE_MFMA_I8 = 0, PROBE_MFMA_F8 = 1, PROBE_MFMA_F4 = 2, PROBE_MFMA_BF16 = 3, PROBE_EXP = 4, PROBE_COPY = 5,
+       PROBE_READ = 6 };
 hipError_t launch_probe(int kind, int grid, int64_t iters, const void* src, void* dst, size_t bytes, hipStream_t st);
 
 }  // namespace bqa

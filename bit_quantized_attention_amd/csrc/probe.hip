@@ -7,9 +7,11 @@
 //    independent accumulator chains (enough to cover the instruction's
 //    latency at four wavefronts per SIMD);
 //  * exp probe: every lane runs `iters` rounds of eight independent
-//    v_exp_f32, each followed by one subtraction that keeps the values in
-//    [-1, 1];
-//  * copy probe: a grid-stride 16-byte copy of `bytes` from src to dst.
+//    v_exp_f32 chains, x <- 2^-x (the negation is a source modifier, so the
+//    loop is exponentials only; the values stay in (1/4, 1));
+//  * copy probe: a grid-stride 16-byte copy of `bytes` from src to dst;
+//  * read probe: a grid-stride 16-byte read of `bytes` from src, folded into
+//    one word per workgroup.
 // Each workgroup writes one checksum word to dst (matrix and exp probes) so
 // that nothing is optimised away.
 #include "common.hpp"
@@ -77,10 +79,10 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int64_t iters, uint32_t
 __global__ __launch_bounds__(256) void exp_probe_kernel(int64_t iters, uint32_t* __restrict__ out) {
     float x[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = (float)((threadIdx.x + 37 * k) & 63) * (1.0f / 64.0f) - 0.5f;
+    for (int k = 0; k < 8; ++k) x[k] = (float)((threadIdx.x + 37 * k) & 63) * (1.0f / 64.0f) + 0.25f;
     for (int64_t it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = __builtin_amdgcn_exp2f(x[k]) - 1.5f;   // [-1, 1] -> [-1, 0.5]
+        for (int k = 0; k < 8; ++k) x[k] = __builtin_amdgcn_exp2f(-x[k]);
     }
     float s = 0.0f;
 #pragma unroll
@@ -103,6 +105,21 @@ __global__ __launch_bounds__(256) void copy_probe_kernel(const v4i* __restrict__
     for (; i < n16; i += stride) dst[i] = src[i];
 }
 
+__global__ __launch_bounds__(256) void read_probe_kernel(const v4i* __restrict__ src, int64_t n16,
+                                                         uint32_t* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    v4i acc = {0, 0, 0, 0};
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const v4i a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        acc ^= a ^ b ^ c ^ d;
+    }
+    for (; i < n16; i += stride) acc ^= src[i];
+    const float f = (float)((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) & 0xFFFF);
+    const float m = wave_max(f);
+    if (threadIdx.x == 0) out[blockIdx.x] = (uint32_t)m;
+}
+
 }  // namespace
 
 hipError_t launch_probe(int kind, int grid, int64_t iters, const void* src, void* dst, size_t bytes,
@@ -116,6 +133,9 @@ hipError_t launch_probe(int kind, int grid, int64_t iters, const void* src, void
         case PROBE_EXP: exp_probe_kernel<<<grid, 256, 0, st>>>(iters, out); break;
         case PROBE_COPY:
             copy_probe_kernel<<<grid, 256, 0, st>>>((const v4i*)src, (v4i*)dst, (int64_t)(bytes / 16));
+            break;
+        case PROBE_READ:
+            read_probe_kernel<<<grid, 256, 0, st>>>((const v4i*)src, (int64_t)(bytes / 16), out);
             break;
         default: return hipErrorInvalidValue;
     }

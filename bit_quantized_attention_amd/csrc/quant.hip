@@ -25,12 +25,30 @@
 
 namespace bqa {
 
+// QK-norm ("SageBwd", Methodology 4) of one 128-channel row whose 16 groups
+// of 8 channels sit in 16 consecutive lanes: S = sum of squares in fp64
+// (exact for bf16 rows, so the lane order does not matter), r =
+// fp32(1/sqrt(S)) (0 for a zero row), and the 8 values of this lane become
+// bf16(fp32(x r)).  Returns r.
+__device__ __forceinline__ float qk_norm8(float* v) {
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += (double)v[j] * (double)v[j];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off, 16);
+    const float r = s > 0.0 ? (float)(1.0 / __builtin_sqrt(s)) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = bf16_bits_to_f32(f32_to_bf16_bits(v[j] * r));
+    return r;
+}
+
 // ------------------------------------------------------------ column partials
 // grid (BH, chunks); 256 threads = 16 rows x 16 column groups of 8 channels.
 // Each chunk of tokens is reduced per channel into part[bh][chunk][c]: SUM
 // gives fp64 token sums (K smoothing), otherwise fp32 absolute maxima
-// (per-channel V scales).
-template <bool IS_F16, bool SUM>
+// (per-channel V scales).  NORM (with SUM, d = 128): the sums are of the
+// QK-normalised rows.
+template <bool IS_F16, bool SUM, bool NORM = false>
 __device__ __forceinline__ void col_partial_body(const Dense& x, int H, int N, int d, int rows_per_chunk,
                                                  void* __restrict__ part_out, int bh, int chunk, int nchunks) {
     using Acc = typename std::conditional<SUM, double, float>::type;
@@ -40,11 +58,14 @@ __device__ __forceinline__ void col_partial_body(const Dense& x, int H, int N, i
     Acc acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     auto take = [&](const v4i& raw) {
         const uint16_t* e = (const uint16_t*)&raw;
+        float f[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = load_half<IS_F16>(e + k);
+        if constexpr (NORM) qk_norm8(f);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const float f = load_half<IS_F16>(e + k);
-            if constexpr (SUM) acc[k] += (double)f;
-            else acc[k] = __builtin_fmaxf(acc[k], __builtin_fabsf(f));
+            if constexpr (SUM) acc[k] += (double)f[k];
+            else acc[k] = __builtin_fmaxf(acc[k], __builtin_fabsf(f[k]));
         }
     };
     const int t0 = chunk * rows_per_chunk, t1 = min(N, t0 + rows_per_chunk);
@@ -76,10 +97,10 @@ __device__ __forceinline__ void col_partial_body(const Dense& x, int H, int N, i
     }
 }
 
-template <bool IS_F16, bool SUM>
+template <bool IS_F16, bool SUM, bool NORM = false>
 __global__ __launch_bounds__(256) void col_partial_kernel(Dense x, int H, int N, int d, int rows_per_chunk,
                                                           void* __restrict__ part_out) {
-    col_partial_body<IS_F16, SUM>(x, H, N, d, rows_per_chunk, part_out, blockIdx.x, blockIdx.y, gridDim.y);
+    col_partial_body<IS_F16, SUM, NORM>(x, H, N, d, rows_per_chunk, part_out, blockIdx.x, blockIdx.y, gridDim.y);
 }
 
 // Per-chunk partials of one channel (stride d between chunks), combined in
@@ -119,12 +140,14 @@ struct PartLoad {
 // each thread owns NG groups of 8 consecutive elements (NG = blk d / 2048),
 // always at the same 8 channels.  With `part` the K-smoothing mean is
 // finalised here from the fp64 partial token sums, mu = fp32(S/N - eps), and
-// block 0 of each head writes it to `mu_out`.
-template <bool IS_F16, int NG>
+// block 0 of each head writes it to `mu_out`.  NORM (d = 128): every row is
+// QK-normalised first (qk_norm8) and its inverse norm written to inv_norm.
+template <bool IS_F16, int NG, bool NORM = false>
 __device__ __forceinline__ void tokblock_body(const Dense& x, int H, int N, int d, int blk,
                                               const double* __restrict__ part, int nchunks, double eps,
                                               float* __restrict__ mu_out, int8_t* __restrict__ codes,
-                                              float* __restrict__ scales, int block_id) {
+                                              float* __restrict__ scales, int block_id,
+                                              float* __restrict__ inv_norm = nullptr) {
     const int nb = N / blk;
     const int bh = block_id / nb, ib = block_id % nb;
     const int b = bh / H, h = bh % H;
@@ -163,11 +186,16 @@ __device__ __forceinline__ void tokblock_body(const Dense& x, int H, int N, int 
     for (int k = 0; k < NG; ++k) {
         const uint16_t* e = (const uint16_t*)&raw[k];
 #pragma unroll
+        for (int j = 0; j < 8; ++j) v[k][j] = load_half<IS_F16>(e + j);
+        if constexpr (NORM) {
+            const float r = qk_norm8(v[k]);
+            if (threadIdx.x % gpr == 0)
+                inv_norm[(int64_t)bh * N + (int64_t)ib * blk + (threadIdx.x + k * 256) / gpr] = r;
+        }
+#pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float f = load_half<IS_F16>(e + j);
-            if (has_mu) f = f - mu[j];
-            v[k][j] = f;
-            amax = __builtin_fmaxf(amax, __builtin_fabsf(f));
+            if (has_mu) v[k][j] = v[k][j] - mu[j];
+            amax = __builtin_fmaxf(amax, __builtin_fabsf(v[k][j]));
         }
     }
     amax = wave_max(amax);
@@ -189,13 +217,15 @@ __device__ __forceinline__ void tokblock_body(const Dense& x, int H, int N, int 
     }
 }
 
-template <bool IS_F16, int NG>
+template <bool IS_F16, int NG, bool NORM = false>
 __global__ __launch_bounds__(256) void quant_i8_tokblock_kernel(Dense x, int H, int N, int d, int blk,
                                                                  const double* __restrict__ part, int nchunks,
                                                                  double eps, float* __restrict__ mu_out,
                                                                  int8_t* __restrict__ codes,
-                                                                 float* __restrict__ scales) {
-    tokblock_body<IS_F16, NG>(x, H, N, d, blk, part, nchunks, eps, mu_out, codes, scales, blockIdx.x);
+                                                                 float* __restrict__ scales,
+                                                                 float* __restrict__ inv_norm = nullptr) {
+    tokblock_body<IS_F16, NG, NORM>(x, H, N, d, blk, part, nchunks, eps, mu_out, codes, scales, blockIdx.x,
+                                    inv_norm);
 }
 
 // ------------------------------------------------------------ per-channel V
@@ -774,6 +804,34 @@ hipError_t launch_quant_i8_tokblock(const Dense& x, bool f16, int B, int H, int 
     }
     return f16 ? launch_tokblock_t<true>(x, B, H, N, d, blk, part, nch, eps, mu, codes, scales, st)
                : launch_tokblock_t<false>(x, B, H, N, d, blk, part, nch, eps, mu, codes, scales, st);
+}
+
+// QK-norm fused into the INT8 token-block quantiser (d = 128): rows are
+// normalised, rounded to bf16 and quantised in one pass; with smoothing the
+// token sums of the normalised rows go to the workspace first.
+hipError_t launch_quant_i8_qknorm(const Dense& x, bool f16, int B, int H, int N, int d, int blk, bool smooth,
+                                  double eps, float* mu, float* inv_norm, void* ws, int8_t* codes, float* scales,
+                                  hipStream_t st) {
+    const int BH = B * H, nch = chunks_for(BH, N), rpc = (N + nch - 1) / nch;
+    double* part = nullptr;
+    if (smooth) {
+        part = (double*)ws;
+        if (f16) col_partial_kernel<true, true, true><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
+        else col_partial_kernel<false, true, true><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
+    }
+    const int grid = BH * (N / blk);
+#define BQA_QKN(F16, NG) \
+    quant_i8_tokblock_kernel<F16, NG, true><<<grid, 256, 0, st>>>(x, H, N, d, blk, part, nch, eps, mu, codes, scales, \
+                                                                   inv_norm)
+    if (blk == 64) {
+        if (f16) BQA_QKN(true, 4);
+        else BQA_QKN(false, 4);
+    } else {
+        if (f16) BQA_QKN(true, 8);
+        else BQA_QKN(false, 8);
+    }
+#undef BQA_QKN
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_chan(const Dense& x, bool f16, int B, int H, int N, int d, int fmt, uint8_t* codes_t,

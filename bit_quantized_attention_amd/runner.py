@@ -12,8 +12,8 @@ import torch
 from . import (BQA_FP8E4M3, BQA_INT8, BQA_MXFP4, BQA_OP_FWD, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_KV,
                BQA_OP_QUANTIZE_V, BQA_OP_BWD, BQA_PTQ_MXFP4, BQA_QAT_MXFP4, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V,
                BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV, BQA_SAGE_I8_I8PV, BQA_THRIFT, bqa_attn_bwd, bqa_attn_fwd,
-               bqa_attn_fwd_ptq, bqa_quantize_blocks, bqa_quantize_kv, bqa_select_blocks, bqa_workspace_size, dense,
-               max_sel, problem, qtensor)
+               bqa_attn_bwd_qknorm, bqa_attn_fwd_ptq, bqa_quantize_blocks, bqa_quantize_kv, bqa_quantize_qknorm,
+               bqa_select_blocks, bqa_workspace_size, dense, max_sel, problem, qtensor)
 
 
 def sage_problem(B, Hq, Hkv, Nq, Nk, d, causal, mode, q_block=128, k_block=64, smooth_k=True, smooth_eps=0.0,
@@ -111,6 +111,31 @@ class SageTrainStep(SagePath):
         self.forward()
         self.backward()
         return self.dq, self.dk, self.dv
+
+
+class SageQkNormTrainStep(SageTrainStep):
+    """The SageBwd training step of the recommended recipe with QK-norm fused
+    into it: q and k are the raw rows; the quantiser normalises them on the
+    way in (keeping each row's inverse norm) and the backward returns the
+    gradients of the raw rows."""
+
+    def __init__(self, p, q_raw, k_raw, v, d_o):
+        super().__init__(p, q_raw, k_raw, v, d_o)
+        self.fuse_q = False
+        dev = q_raw.device
+        self.q_rn = torch.empty((p.B, p.Hq, p.Nq), dtype=torch.float32, device=dev)
+        self.k_rn = torch.empty((p.B, p.Hkv, p.Nk), dtype=torch.float32, device=dev)
+
+    def quantize(self):
+        bqa_quantize_qknorm(self.p, BQA_ROLE_Q, self._qd, self.qq, inv_norm=self.q_rn)
+        bqa_quantize_qknorm(self.p, BQA_ROLE_K, self._kd, self.kq, inv_norm=self.k_rn, k_mean=self.mu,
+                            workspace=self.ws)
+        bqa_quantize_blocks(self.p, BQA_ROLE_V, self._vd, self.vq, workspace=self.ws)
+
+    def backward(self):
+        bqa_attn_bwd_qknorm(self.p, q=self.qq, k=self.kq, v_hi=self._vd, o_for_delta=self._od, lse=self.lse,
+                            d_o=self._dod, q_raw=self._qd, k_raw=self._kd, q_inv_norm=self.q_rn,
+                            k_inv_norm=self.k_rn, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws_bwd)
 
 
 def qat_problem(B, Hq, Hkv, Nq, Nk, d, sm_scale=0.0):

@@ -207,6 +207,24 @@ bqa_status bqa_quantize_kv(const bqa_problem* p, const bqa_tensor* k, const bqa_
                            bqa_qtensor* vq, float* k_mean, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * QK-norm fused into the INT8 quantisation ("SageBwd", Methodology 4 and the
+ * recommended SageBwd + QK-norm + K-smoothing recipe): the raw rows x of Q
+ * or K (bf16 or fp16, d = 128, a Sage mode) are scaled to unit L2 norm,
+ * y = bf16(fp32(x r)) with r = fp32(1/sqrt(S)) from the fp64 sum of squares
+ * S (r = 0 for a zero row), and y is quantised exactly as
+ * bqa_quantize_blocks quantises its input for the same role: INT8 token
+ * blocks of out->block (64 or 128) tokens; for K with p->smooth_k the
+ * smoothing mean is taken over the normalised rows (to k_mean when not
+ * NULL; workspace bqa_workspace_size(p, BQA_OP_QUANTIZE_K) bytes).  One pass
+ * over x replaces a normalisation pass and the quantiser's read of its
+ * output.  inv_norm (fp32 [B, H, N], required) receives r of every row, for
+ * bqa_attn_bwd_qknorm.
+ */
+bqa_status bqa_quantize_qknorm(const bqa_problem* p, int32_t role, const bqa_tensor* x, bqa_qtensor* out,
+                               float* inv_norm, float* k_mean, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * ThriftAttention block selection ("ThriftAttention", Method step 1): for
  * every (b, query head h, query block i) the importance of key block j is
  * qbar_i . kbar_j (kbar of KV head h / (Hq/Hkv)) over the valid key blocks
@@ -336,6 +354,24 @@ bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The SageBwd backward of bqa_attn_bwd (same arguments, requirements and
+ * workspace) for a forward whose Q and K came from bqa_quantize_qknorm: the
+ * QK-norm backward is applied in the dQ and dK epilogues, so dq and dk are
+ * the gradients with respect to the raw rows: dx = r (g - y (y . g)) with
+ * g the gradient with respect to the normalised row, y = x r (the bf16
+ * rounding of the forward passed straight through).  K-smoothing adds no
+ * term: its mean enters every score of a query row equally, and the key
+ * gradients it would add sum, over all keys, to zero in exact arithmetic
+ * (each query's dS row sums to zero).  q_raw, k_raw: the raw bf16 rows;
+ * q_inv_norm, k_inv_norm: the r that bqa_quantize_qknorm wrote.
+ */
+bqa_status bqa_attn_bwd_qknorm(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,
+                               const bqa_tensor* v_hi, const bqa_tensor* o_for_delta, const float* lse,
+                               const bqa_tensor* d_o, const bqa_tensor* q_raw, const bqa_tensor* k_raw,
+                               const float* q_inv_norm, const float* k_inv_norm, bqa_tensor* dq, bqa_tensor* dk,
+                               bqa_tensor* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Test hook: the raw Q K^T accumulator of one tile as the forward kernel's
  * matrix-instruction code computes it — int32 [32 x 32] for INT8 codes
  * (exact integer dot products) or fp32 [32 x 32] for MXFP4 codes (the
@@ -368,10 +404,12 @@ bqa_status bqa_debug_mx_dequant(const void* codes, const void* scales, int64_t n
  * checksum word per workgroup to dst (bytes >= 4 grid, 4-byte aligned; src
  * unused).  BQA_PROBE_COPY: copies `bytes` (a multiple of 16, both pointers
  * 16-byte aligned) from src to dst with 16-byte accesses; iters unused.
+ * BQA_PROBE_READ: reads `bytes` (a multiple of 16, src 16-byte aligned) with
+ * 16-byte accesses and writes one checksum word per workgroup to dst.
  */
 enum {
     BQA_PROBE_MFMA_I8 = 0, BQA_PROBE_MFMA_F8 = 1, BQA_PROBE_MFMA_F4 = 2, BQA_PROBE_MFMA_BF16 = 3,
-    BQA_PROBE_EXP = 4, BQA_PROBE_COPY = 5
+    BQA_PROBE_EXP = 4, BQA_PROBE_COPY = 5, BQA_PROBE_READ = 6
 };
 bqa_status bqa_debug_probe(int32_t kind, int32_t grid, int64_t iters, const void* src, void* dst, size_t bytes,
                            void* stream);

@@ -511,6 +511,9 @@ typedef struct {
     const double* delta;
     int N, d, causal, tq, tk, do_blk, quantize;
     double tau;
+    const int8_t* vc;     /* fully INT8 backward: V codes per v_blk tokens; NULL: dP from bf16 V */
+    const float* vs;
+    int v_blk;
 } sbwd_ctx;
 
 /* Round a tile to INT8 with one scale (its absmax) and return the
@@ -545,7 +548,16 @@ static void sbwd_tile(const sbwd_ctx* c, int I, int J, double* dQ /* tile rows, 
             s = (double)acc * (double)c->qs[i / tq] * (double)c->ks[j / tk] * c->tau;
             P[(size_t)a * tk + b] = exp(s - (double)c->lse[i]);
             double dp = 0.0;
-            for (int k = 0; k < d; ++k) dp += (double)c->dO[(size_t)i * d + k] * (double)c->V[(size_t)j * d + k];
+            if (c->vc) {
+                /* dP in INT8: the dO codes (per do_blk tokens) against the V
+                 * codes (per v_blk tokens), exact integer sum, then both scales */
+                int64_t di = 0;
+                for (int k = 0; k < d; ++k)
+                    di += (int64_t)c->doc[(size_t)i * d + k] * (int64_t)c->vc[(size_t)j * d + k];
+                dp = (double)di * (double)c->dos[i / c->do_blk] * (double)c->vs[j / c->v_blk];
+            } else {
+                for (int k = 0; k < d; ++k) dp += (double)c->dO[(size_t)i * d + k] * (double)c->V[(size_t)j * d + k];
+            }
             dS[(size_t)a * tk + b] = P[(size_t)a * tk + b] * (dp - c->delta[i]);
         }
     }
@@ -595,12 +607,15 @@ static void sbwd_tile(const sbwd_ctx* c, int I, int J, double* dQ /* tile rows, 
  * head (outputs hold only those rows).  Q codes are per 128-token block and
  * K codes per 64-token block (the forward's), dO is quantised here per
  * do_blk tokens.  With quantize == 0 every rounding is skipped (the codes
- * times their scales are then the operands). */
-void orc_sage_bwd(const int8_t* qc, const float* qs, const int8_t* kc, const float* ks,
-                  const float* V, const float* dO, const float* O, const float* lse,
-                  int N, int d, int causal, double tau, int tile_q, int tile_k, int do_blk,
-                  int quantize, int qt0, int qt1, int kt0, int kt1,
-                  double* dQ, double* dK, double* dV) {
+ * times their scales are then the operands).  With vc != NULL the fully
+ * INT8 variant that [SB] Limitations leaves open: dP = dO V^T from the INT8
+ * codes of dO and of V (vc, vs: V per v_blk tokens). */
+void orc_sage_bwd_v(const int8_t* qc, const float* qs, const int8_t* kc, const float* ks,
+                    const float* V, const float* dO, const float* O, const float* lse,
+                    int N, int d, int causal, double tau, int tile_q, int tile_k, int do_blk,
+                    int quantize, int qt0, int qt1, int kt0, int kt1,
+                    const int8_t* vc, const float* vs, int v_blk,
+                    double* dQ, double* dK, double* dV) {
     double* delta = (double*)malloc(sizeof(double) * (size_t)N);
     for (int i = 0; i < N; ++i) {
         double acc = 0.0;
@@ -610,7 +625,8 @@ void orc_sage_bwd(const int8_t* qc, const float* qs, const int8_t* kc, const flo
     int8_t* doc = (int8_t*)malloc((size_t)N * d);
     float* dos = (float*)malloc(sizeof(float) * (size_t)(N / do_blk));
     orc_quant_i8_tokblock(dO, NULL, 1, N, d, do_blk, doc, dos);
-    sbwd_ctx c = {qc, kc, qs, ks, V, dO, lse, doc, dos, delta, N, d, causal, tile_q, tile_k, do_blk, quantize, tau};
+    sbwd_ctx c = {qc, kc, qs, ks, V, dO, lse, doc, dos, delta, N, d, causal, tile_q, tile_k, do_blk, quantize, tau,
+                  vc, vs, v_blk};
     memset(dQ, 0, sizeof(double) * (size_t)(qt1 - qt0) * tile_q * d);
     memset(dK, 0, sizeof(double) * (size_t)(kt1 - kt0) * tile_k * d);
     memset(dV, 0, sizeof(double) * (size_t)(kt1 - kt0) * tile_k * d);
@@ -630,6 +646,15 @@ void orc_sage_bwd(const int8_t* qc, const float* qs, const int8_t* kc, const flo
     free(delta);
     free(doc);
     free(dos);
+}
+
+void orc_sage_bwd(const int8_t* qc, const float* qs, const int8_t* kc, const float* ks,
+                  const float* V, const float* dO, const float* O, const float* lse,
+                  int N, int d, int causal, double tau, int tile_q, int tile_k, int do_blk,
+                  int quantize, int qt0, int qt1, int kt0, int kt1,
+                  double* dQ, double* dK, double* dV) {
+    orc_sage_bwd_v(qc, qs, kc, ks, V, dO, O, lse, N, d, causal, tau, tile_q, tile_k, do_blk, quantize, qt0, qt1,
+                   kt0, kt1, NULL, NULL, 0, dQ, dK, dV);
 }
 
 /* ========================================================================

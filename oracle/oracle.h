@@ -64,6 +64,12 @@ void orc_sage_bwd(const int8_t* qc, const float* qs, const int8_t* kc, const flo
                   int N, int d, int causal, double tau, int tile_q, int tile_k, int do_blk,
                   int quantize, int qt0, int qt1, int kt0, int kt1,
                   double* dQ, double* dK, double* dV);
+void orc_sage_bwd_v(const int8_t* qc, const float* qs, const int8_t* kc, const float* ks,
+                    const float* V, const float* dO, const float* O, const float* lse,
+                    int N, int d, int causal, double tau, int tile_q, int tile_k, int do_blk,
+                    int quantize, int qt0, int qt1, int kt0, int kt1,
+                    const int8_t* vc, const float* vs, int v_blk,
+                    double* dQ, double* dK, double* dV);
 
 /* ---- Attn-QAT FP4 forward / backward ---- */
 int  orc_mx_scores(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,

@@ -304,5 +304,37 @@ def test_probe_validation(L):
     assert P(bqa.BQA_PROBE_COPY, 16, 0, None, 0x1000, 4096, None) == bqa.BQA_E_NULL
     assert P(bqa.BQA_PROBE_COPY, 16, 0, 0x2008, 0x1000, 4096, None) == bqa.BQA_E_ALIGN
     assert P(bqa.BQA_PROBE_COPY, 16, 0, 0x2000, 0x1000, 4100, None) == bqa.BQA_E_ALIGN
+    assert P(bqa.BQA_PROBE_READ, 16, 0, None, 0x1000, 4096, None) == bqa.BQA_E_NULL
+    assert P(bqa.BQA_PROBE_READ, 16, 0, 0x2000, 0x1002, 4096, None) == bqa.BQA_E_ALIGN
+    assert _nodev(P(bqa.BQA_PROBE_READ, 16, 0, 0x2000, 0x1000, 4096, None))
     assert _nodev(P(bqa.BQA_PROBE_MFMA_F4, 16, 10, None, 0x1000, 4096, None))
     assert _nodev(P(bqa.BQA_PROBE_COPY, 16, 0, 0x2000, 0x1000, 4096, None))
+
+
+def test_qknorm_validation(L):
+    x = _dense()
+    sage = dict(mode=bqa.BQA_SAGE_I8_I8PV, Nq=4096, Nk=4096, smooth_k=1, smooth_eps=1e-3)
+
+    def quant(p, role, out, rn=0x70000, ws=0x40000, wsb=1 << 30):
+        return bqa.lib().bqa_quantize_qknorm(C.byref(p), role, C.byref(x), C.byref(out), rn, None, ws, wsb, None)
+    assert quant(_p(**sage), bqa.BQA_ROLE_V, _q()) == bqa.BQA_E_UNSUPPORTED
+    assert quant(_p(**dict(sage, mode=bqa.BQA_QAT_MXFP4)), bqa.BQA_ROLE_Q, _q()) == bqa.BQA_E_UNSUPPORTED
+    assert quant(_p(**dict(sage, d=64)), bqa.BQA_ROLE_Q, _q()) == bqa.BQA_E_UNSUPPORTED
+    assert quant(_p(**sage), bqa.BQA_ROLE_Q, _q(), rn=None) == bqa.BQA_E_NULL
+    assert quant(_p(**sage), bqa.BQA_ROLE_Q, _q(), rn=0x70002) == bqa.BQA_E_ALIGN
+    assert quant(_p(**sage), bqa.BQA_ROLE_Q, _q(block=96)) == bqa.BQA_E_UNSUPPORTED
+    assert quant(_p(**sage), bqa.BQA_ROLE_K, _q(block=64), wsb=8) == bqa.BQA_E_WORKSPACE
+    assert _nodev(quant(_p(**sage), bqa.BQA_ROLE_Q, _q()))
+    assert _nodev(quant(_p(**sage), bqa.BQA_ROLE_K, _q(block=64)))
+    g = _dense()
+    q, k = _q(), _q(block=64)
+
+    def bwd(p, qraw=g, rq=0x71000, rk=0x72000):
+        return bqa.lib().bqa_attn_bwd_qknorm(C.byref(p), C.byref(q), C.byref(k), C.byref(g), C.byref(g), 0x50000,
+                                             C.byref(g), None if qraw is None else C.byref(qraw), C.byref(g), rq, rk,
+                                             C.byref(g), C.byref(g), C.byref(g), 0x40000, 1 << 34, None)
+    assert bwd(_p(**dict(sage, mode=bqa.BQA_QAT_MXFP4))) == bqa.BQA_E_UNSUPPORTED
+    assert bwd(_p(**sage), qraw=None) == bqa.BQA_E_NULL
+    assert bwd(_p(**sage), rk=None) == bqa.BQA_E_NULL
+    assert bwd(_p(**sage), rq=0x71001) == bqa.BQA_E_ALIGN
+    assert _nodev(bwd(_p(**sage)))

@@ -21,7 +21,8 @@ Recipes (distributions written N(mean, variance)):
   are multiplied by 20 (outlier channels); K gets a channel bias ~ N(0,4).
 * ``c3``  B=1 H=16 N=8192 (or 2048) d=128, bf16, causal.  Q, K, V ~ N(0,1);
   every row of Q and K is scaled to unit L2 norm (QK-norm) before rounding;
-  dO ~ N(0, 0.01).
+  dO ~ N(0, 0.01).  ``qraw`` / ``kraw`` are the same draws rounded to bf16
+  without the normalisation (inputs of the fused QK-norm quantiser).
 * ``c4``  B=1 H=32 N=16384 d=128, bf16, non-causal.  Q, K, V ~ Student-t
   with 3 degrees of freedom (heavy tails); dO ~ N(0, 0.01).
 * ``c5``  B=1 Hq=32 Hkv=8 N=131072 d=128, bf16, causal, GQA.  Per KV head a
@@ -123,7 +124,7 @@ def _basis(w: Workload, hkv: int) -> np.ndarray:
 
 def chunk(w: Workload, tensor: str, b: int, h: int) -> np.ndarray:
     """One [N, d] slice (fp32 values, exact in the workload dtype)."""
-    N = w.Nk if tensor in ("k", "v") else w.Nq
+    N = w.Nk if tensor in ("k", "v", "kraw") else w.Nq
     d = w.d
     if w.name == "c1" or w.name == "c2":
         tid = {"q": T_Q, "k": T_K, "v": T_V}[tensor]
@@ -136,11 +137,13 @@ def chunk(w: Workload, tensor: str, b: int, h: int) -> np.ndarray:
             x += bias[None, :]
         return round_to(x, w.dtype)
     if w.name == "c3":
+        raw = tensor in ("qraw", "kraw")        # the same draws before QK-norm
+        tensor = {"qraw": "q", "kraw": "k"}.get(tensor, tensor)
         tid = {"q": T_Q, "k": T_K, "v": T_V, "do": T_DO}[tensor]
         if tensor == "do":
             return round_to(_normal(_rng(w.cfg_id, tid, b, h), (N, d), 0.1), w.dtype)
         x = _normal(_rng(w.cfg_id, tid, b, h), (N, d))
-        if tensor in ("q", "k"):       # QK-norm of the model layer, applied to the inputs
+        if tensor in ("q", "k") and not raw:       # QK-norm of the model layer, applied to the inputs
             x64 = x.astype(np.float64)
             x64 /= np.sqrt(np.sum(x64 * x64, axis=1, keepdims=True))
             x = x64.astype(np.float32)
@@ -175,7 +178,7 @@ def chunk(w: Workload, tensor: str, b: int, h: int) -> np.ndarray:
 
 
 def heads_of(w: Workload, tensor: str) -> int:
-    return w.Hkv if tensor in ("k", "v") else w.Hq
+    return w.Hkv if tensor in ("k", "v", "kraw") else w.Hq
 
 
 def _chunk_job(args):
@@ -189,7 +192,7 @@ def build(w: Workload, tensor: str, workers: int = 0) -> np.ndarray:
     workers > 1 generates the (b, h) chunks in that many fresh interpreter
     processes (each chunk has its own seed, so the result is the same)."""
     H = heads_of(w, tensor)
-    N = w.Nk if tensor in ("k", "v") else w.Nq
+    N = w.Nk if tensor in ("k", "v", "kraw") else w.Nq
     out = np.empty((w.B, H, N, w.d), dtype=np.float32)
     jobs = [(w, tensor, b, h) for b in range(w.B) for h in range(H)]
     if workers > 1 and len(jobs) > 1:
