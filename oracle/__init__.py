@@ -75,6 +75,8 @@ def _declare(L):
         "orc_ref_bwd": (None, [vp, vp, vp, vp, i, i, i, i, d, vp, vp, vp]),
         "orc_sage_fwd": (None, [i, vp, vp, i, vp, vp, i, vp, vp, i, vp, vp, vp,
                                 i, i, i, i, d, i, i, i, vp, vp]),
+        "orc_sage_bwd_v": (None, [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, d, i, i, i, i,
+                                  i, i, i, i, vp, vp, i, vp, vp, vp]),
         "orc_sage_bwd": (None, [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, d, i, i, i, i,
                                 i, i, i, i, vp, vp, vp]),
         "orc_mx_scores": (i, [vp, vp, vp, vp, i, i, i, vp]),
@@ -299,15 +301,19 @@ def sage_fwd(*, qk_mode=QK_I8, qc=None, qs=None, q_blk=128, kc=None, ks=None, k_
 
 
 def sage_bwd(*, qc, qs, kc, ks, V, dO, O, lse, causal, tau, tile_q=128, tile_k=64, do_blk=128,
-             quantize=True, qtiles=None, ktiles=None):
+             quantize=True, qtiles=None, ktiles=None, vc=None, vs=None, v_blk=64):
+    """SageBwd backward of one head; with vc / vs (V's INT8 codes per v_blk
+    tokens) dP = dO V^T runs in INT8 as well (the fully INT8 variant)."""
     N, d = V.shape
     qt0, qt1 = (0, N // tile_q) if qtiles is None else qtiles
     kt0, kt1 = (0, N // tile_k) if ktiles is None else ktiles
     dQ = np.empty(((qt1 - qt0) * tile_q, d)); dK = np.empty(((kt1 - kt0) * tile_k, d))
     dV = np.empty_like(dK)
     a = [_c(qc, np.int8), _f32(qs), _c(kc, np.int8), _f32(ks), _f32(V), _f32(dO), _f32(O), _f32(lse)]
-    lib().orc_sage_bwd(*[_p(x) for x in a], N, d, int(causal), float(tau), tile_q, tile_k, do_blk,
-                       int(quantize), qt0, qt1, kt0, kt1, _p(dQ), _p(dK), _p(dV))
+    vcc = None if vc is None else _c(vc, np.int8)
+    vss = None if vs is None else _f32(vs)
+    lib().orc_sage_bwd_v(*[_p(x) for x in a], N, d, int(causal), float(tau), tile_q, tile_k, do_blk,
+                         int(quantize), qt0, qt1, kt0, kt1, _p(vcc), _p(vss), int(v_blk), _p(dQ), _p(dK), _p(dV))
     return dQ, dK, dV
 
 
