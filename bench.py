@@ -9,6 +9,7 @@ Workloads (``--workload``, default c2):
       inputs: K-smoothing (eps 1e-3), INT8 forward, INT8 backward with the
       bf16 dP = dO V^T; `value` counts forward + backward (14 B H N^2 d / 2)
       and the roofline covers the backward call.
+  c3i the same step with the fully INT8 backward (dP = dO V^T in INT8 too).
   c3n the same step from raw (unnormalised) Q, K rows with QK-norm fused
       into the INT8 quantiser and its backward into the dQ / dK epilogues.
   c4  Attn-QAT FP4 forward at B=1, H=32, N=16384, d=128, non-causal,
@@ -38,7 +39,7 @@ time, measured with HIP events on the stream it runs on, against the dense
 matrix-core peak of its operand types.  `cpu_baseline` times the CPU oracle
 on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--workload c2|c3|c3n|c4|c4t|c4i|c4p|c5|c5d] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--workload c2|c3|c3i|c3n|c4|c4t|c4i|c4p|c5|c5d] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -450,6 +451,28 @@ def _sagebwd_roofline(w):
         traffic_key="sbwd_dkdv_kernel", cpu=cpu_baseline_sagebwd)
 
 
+def _sagebwd_i8dp_case(w, bqa, torch):
+    from bit_quantized_attention_amd.runner import SageTrainStep, sage_problem, to_device
+    import workloads as wl
+    Q, K, V, dO = (wl.build(w, t) for t in ("q", "k", "v", "do"))
+    p = sage_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.causal, bqa.BQA_SAGE_I8_I8PV, q_block=128,
+                     smooth_k=True, smooth_eps=1e-3)
+    path = SageTrainStep(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"), to_device(dO, "bf16"),
+                         int8_dp=True)
+    case = _sagebwd_roofline(w)
+    n_pairs = w.B * w.Hq * w.Nq * (w.Nq + 1) / 2
+    bwd_ops = 10.0 * w.d * n_pairs
+    case.update(path=path, dtype="i8",
+                workload="fully INT8 SageBwd training step (c3i): B=1 H=16 N=8192 d=128 causal, QK-norm bf16 in, "
+                         "K-smoothing eps=1e-3, INT8 forward; backward with all five products in INT8 (dP = dO V^T "
+                         "from V's 64-token codes); step = quantise (V twice) + forward + backward")
+    case["roofline"] = dict(case["roofline"], kernel="attn_bwd with INT8 dP (delta and row-major dO codes, code "
+                                                     "transposes, sbwd_dkdv_kernel<I8DP>, sbwd_dq_kernel<I8DP>)",
+                            peak=PEAK_I8_TOPS, peak_note="i8 peak for all five backward products",
+                            ops_per_launch=bwd_ops)
+    return case
+
+
 def _sagebwd_qknorm_case(w, bqa, torch):
     from bit_quantized_attention_amd.runner import SageQkNormTrainStep, sage_problem, to_device
     import workloads as wl
@@ -586,9 +609,9 @@ def probe_main(torch, bqa):
     print(json.dumps({"probes": res, "compute_units": n_cu, "grid_matrix": grid, "iters_matrix": iters}), flush=True)
 
 
-CASES = {"c2": _sage_case, "c3": _sagebwd_case, "c3n": _sagebwd_qknorm_case, "c4": _qat_case, "c4t": _qat_train_case, "c4i": _qat_infer_case,
+CASES = {"c2": _sage_case, "c3": _sagebwd_case, "c3i": _sagebwd_i8dp_case, "c3n": _sagebwd_qknorm_case, "c4": _qat_case, "c4t": _qat_train_case, "c4i": _qat_infer_case,
          "c4p": _ptq_case, "c5": _thrift_case, "c5d": _decode_case}
-INPUTS_OF = {"c3n": "c3", "c4t": "c4", "c4i": "c4", "c4p": "c4"}        # workloads that reuse another's inputs
+INPUTS_OF = {"c3i": "c3", "c3n": "c3", "c4t": "c4", "c4i": "c4", "c4p": "c4"}        # workloads that reuse another's inputs
 
 
 def main():

@@ -263,7 +263,7 @@ bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_ten
         return launched(launch_quant_mx(as_dense(x), f16, p->B, H, N, d, axis, (uint8_t*)out->codes,
                                         (uint8_t*)out->scales, block_means, st));
     }
-    if (role == BQA_ROLE_V) {
+    if (role == BQA_ROLE_V && out->axis == 1) {
         if (out->fmt != BQA_INT8 && out->fmt != BQA_FP8E4M3) return BQA_E_UNSUPPORTED;
         TRY(check_q(out, out->fmt, 1));
         if (out->block != N || N % 64 != 0) return BQA_E_UNSUPPORTED;
@@ -274,7 +274,7 @@ bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_ten
         return launched(launch_quant_chan(as_dense(x), f16, p->B, H, N, d, out->fmt == BQA_INT8 ? 0 : 1,
                                           (uint8_t*)out->codes, (float*)out->scales, ws, st));
     }
-    // INT8 token blocks: Q, K, dO
+    // INT8 token blocks: Q, K, dO, and V for the fully INT8 backward
     TRY(check_q(out, BQA_INT8, 0));
     const int blk = out->block;
     if (blk != 64 && blk != 128) return BQA_E_UNSUPPORTED;
@@ -553,12 +553,18 @@ bqa_status bqa_attn_bwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
                         const bqa_tensor* v_hi, const bqa_tensor* o_for_delta, const float* lse,
                         const float* row_max, const bqa_tensor* d_o, bqa_tensor* dq, bqa_tensor* dk, bqa_tensor* dv, void* ws,
                         size_t ws_bytes, void* stream) {
-    (void)v;
     TRY(check_problem(p));
     hipStream_t st = (hipStream_t)stream;
     if (is_sage(p->mode)) {
         SageBwdArgs a{};
         TRY(check_sage_bwd(p, q, k, v_hi, o_for_delta, lse, d_o, dq, dk, dv, ws, ws_bytes, a));
+        if (v) {
+            // the fully INT8 variant: dP from V's INT8 codes per 64 tokens
+            TRY(check_q(v, BQA_INT8, 0));
+            if (v->block != 64) return BQA_E_UNSUPPORTED;
+            a.vc8 = (const int8_t*)v->codes;
+            a.vs8 = (const float*)v->scales;
+        }
         TRY(check_device());
         const int64_t bhn = (int64_t)p->B * p->Hq * p->Nq;
         TRY(debug_check(stream, {dbg16(v_hi, p->B, p->Hq, p->Nq, p->d), dbg16(o_for_delta, p->B, p->Hq, p->Nq, p->d),

@@ -8,7 +8,9 @@
 // dP = dO V^T stays in 16-bit (bf16 operands, fp32 accumulation).
 // dS = P o (dP - delta), delta = rowsum(dO o O) with the forward's O.  P and
 // dS are rounded to INT8 with one scale per 128 x 64 backward tile; dO is
-// INT8 per 128-token block.
+// INT8 per 128-token block.  The fully INT8 variant (I8DP, the open problem
+// of the page's Limitations) also runs dP on INT8 codes: the dO codes
+// against V's codes per 64 tokens, times both scales.
 //
 // Kernels:
 //   do_prep_kernel        delta per query row (fp32) and the channel-major
@@ -57,7 +59,8 @@ __device__ __forceinline__ v4i pack16(const float* x, float inv) {
 // tokens (the token-block quantiser's arithmetic), written channel-major only
 // ([BH][d][N], the layout the products read) through an LDS transpose.
 __global__ __launch_bounds__(256) void do_prep_kernel(Dense dO, Dense O, int H, int N, float* __restrict__ delta,
-                                                      float* __restrict__ dos, int8_t* __restrict__ doT) {
+                                                      float* __restrict__ dos, int8_t* __restrict__ doT,
+                                                      int8_t* __restrict__ doc) {
     const int nb = N / 128;
     const int bh = blockIdx.x / nb, ib = blockIdx.x % nb;
     const int b = bh / H, h = bh % H;
@@ -114,6 +117,23 @@ __global__ __launch_bounds__(256) void do_prep_kernel(Dense dO, Dense O, int H, 
             // one channel, four consecutive rows; |f| <= bm, so |f * inv| <= 127
             tT[8 * part + e][q + 16 * i] = (uint32_t)q8x4(f[0], f[1], f[2], f[3], inv);
         }
+    if (doc) {
+        // the same codes row-major (the INT8 dP reads dO by rows): 8 channels of one row per thread and row
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float f[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t w2 = (uint32_t)gv[i][u][e >> 1];
+                    f[e] = bf16_bits_to_f32((uint16_t)((e & 1) ? (w2 >> 16) : w2));
+                }
+                const int64_t row = (int64_t)bh * N + ib * 128 + 4 * q + u + 64 * i;
+                *(uint2*)(doc + row * D + 8 * part) = make_uint2((uint32_t)q8x4(f[0], f[1], f[2], f[3], inv),
+                                                                 (uint32_t)q8x4(f[4], f[5], f[6], f[7], inv));
+            }
+    }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -194,7 +214,10 @@ struct LdsKV {
 // One wavefront's share of the copies of a query tile, as per-lane offsets
 // from a tile base (the swizzles come from the source each lane names).
 struct KvPlan {
-    static constexpr int NA = 2 + 4 + 1;   // copies per wavefront of an A tile (a B tile: 2 + 2)
+    // copies per wavefront of an A tile (Q codes, dO, log-sum-exp / delta; a
+    // B tile: 2 + 2): dO as bf16 takes 4, as INT8 codes 2
+    template <bool I8DP>
+    static constexpr int na() { return I8DP ? 2 + 2 + 1 : 2 + 4 + 1; }
     uint32_t q[2], g[4], t[2];
     __device__ __forceinline__ KvPlan(int w, int l, int N, int64_t g_sN) {
 #pragma unroll
@@ -215,15 +238,23 @@ struct KvPlan {
     }
 };
 
+template <bool I8DP>
 __device__ __forceinline__ void kv_copy_a(const SageBwdArgs& a, const KvPlan& cp, int bh, int b, int hq, int I, LdsKV& L,
                                           int slot, int w, int l) {
     const int q0 = I * TQ;
     const int8_t* qbase = a.qc + ((int64_t)bh * a.N + q0) * D;
 #pragma unroll
     for (int u = 0; u < 2; ++u) lds_copy16(cp.q[u], qbase, lds_addr(L.q[slot] + 1024 * (2 * w + u)));
-    const uint16_t* gbase = (const uint16_t*)a.d_o.p + b * a.d_o.sB + hq * a.d_o.sH + (int64_t)q0 * a.d_o.sN;
+    if constexpr (I8DP) {
+        // dO codes in the layout of the Q codes (128 x 128 B, sigma reads)
+        const int8_t* cbase = a.doc + ((int64_t)bh * a.N + q0) * D;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) lds_copy16(cp.g[u], gbase, lds_addr(L.dob[slot] + 1024 * (4 * w + u)));
+        for (int u = 0; u < 2; ++u) lds_copy16(cp.q[u], cbase, lds_addr(L.dob[slot] + 1024 * (2 * w + u)));
+    } else {
+        const uint16_t* gbase = (const uint16_t*)a.d_o.p + b * a.d_o.sB + hq * a.d_o.sH + (int64_t)q0 * a.d_o.sN;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lds_copy16(cp.g[u], gbase, lds_addr(L.dob[slot] + 1024 * (4 * w + u)));
+    }
     // log-sum-exp and delta of the tile: 256-byte copies by wavefronts 0-3,
     // repeated by 4-7 (same bytes) so every wavefront counts the same copies
     const int v = w & 3;
@@ -241,6 +272,7 @@ __device__ __forceinline__ void kv_copy_b(const SageBwdArgs& a, const KvPlan& cp
     }
 }
 
+template <bool I8DP>
 __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
     __shared__ __attribute__((aligned(16))) LdsKV L;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
@@ -263,10 +295,19 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
     v4i kb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) kb[kk] = *(const v4i*)(a.kc + ((int64_t)bh * a.N + key) * D + 32 * kk + 16 * h);
-    v8bf vb[8];
-    const uint16_t* vrow = (const uint16_t*)a.v.p + b * a.v.sB + hq * a.v.sH + (int64_t)key * a.v.sN;
+    v8bf vb[I8DP ? 1 : 8];
+    v4i vcb[I8DP ? 4 : 1];
+    float vsc = 0.0f;
+    if constexpr (I8DP) {
+        // INT8 dP: this lane's key as V codes (B operand), the block's V scale
 #pragma unroll
-    for (int st = 0; st < 8; ++st) vb[st] = *(const v8bf*)(vrow + 16 * st + 8 * h);
+        for (int kk = 0; kk < 4; ++kk) vcb[kk] = *(const v4i*)(a.vc8 + ((int64_t)bh * a.N + key) * D + 32 * kk + 16 * h);
+        vsc = uniform_ptr(a.vs8)[(int64_t)bh * nkt + J];
+    } else {
+        const uint16_t* vrow = (const uint16_t*)a.v.p + b * a.v.sB + hq * a.v.sH + (int64_t)key * a.v.sN;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) vb[st] = *(const v8bf*)(vrow + 16 * st + 8 * h);
+    }
     __builtin_amdgcn_s_waitcnt(0);
 
     v16f dv = v16f{}, dk = v16f{};                   // keys 32 kh + 8 (i/4) + 4 h + i%4, channel 32 qg + lq
@@ -276,7 +317,7 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
     const int I0 = a.causal ? (J * TK) / TQ : 0;
     // query tiles in descending order: the key blocks of a head that run at
     // the same time read the same query tile, which then comes from L2
-    kv_copy_a(a, cp, bh, b, hq, nqt - 1, L, 0, w, l);
+    kv_copy_a<I8DP>(a, cp, bh, b, hq, nqt - 1, L, 0, w, l);
     BQA_WAIT_VM(0);
     barrier_only();
     // The products of tile I+1 run in step I, between its two barriers, under
@@ -307,7 +348,7 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
     for (int I = nqt - 1; I >= I0; --I) {
         const int s = (nqt - 1 - I) & 1;
         const bool more = I > I0, prev = I < nqt - 1;
-        if (more) kv_copy_a(a, cp, bh, b, hq, I - 1, L, s ^ 1, w, l);   // that slot's reads ended a step ago
+        if (more) kv_copy_a<I8DP>(a, cp, bh, b, hq, I - 1, L, s ^ 1, w, l);   // that slot's reads ended a step ago
         const float qsc = qs_u[I];
         const float sc = qsc * ks * c;
         // ---- scores: S (int32), dP (fp32) of 32 queries x 32 keys; reg i of half h = query 16h + i
@@ -319,10 +360,22 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
             sacc = mfma_i8_32x32x32(av, kb[kk], sacc);
         }
         v16f dp = v16f{};
+        if constexpr (I8DP) {
+            v16i dpi = v16i{};
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            const v8bf av = *(const v8bf*)(L.dob[s] + rq * 256 + 16 * ((2 * st + h) ^ fs256(rq)));
-            dp = mfma_bf16_32x32x16(av, vb[st], dp);
+            for (int kk = 0; kk < 4; ++kk) {
+                const v4i av = *(const v4i*)(L.dob[s] + rq * 128 + 16 * ((2 * kk + h) ^ fs128(rq)));
+                dpi = mfma_i8_32x32x32(av, vcb[kk], dpi);
+            }
+            const float dsc = dos_u[I] * vsc;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) dp[i] = (float)dpi[i] * dsc;
+        } else {
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+                const v8bf av = *(const v8bf*)(L.dob[s] + rq * 256 + 16 * ((2 * st + h) ^ fs256(rq)));
+                dp = mfma_bf16_32x32x16(av, vb[st], dp);
+            }
         }
         const int qb0 = 32 * qg + 16 * h;            // tile-local query of register 0
         float P[16], dS[16];
@@ -358,7 +411,7 @@ __global__ __launch_bounds__(512, 1) void sbwd_dkdv_kernel(SageBwdArgs a) {
             L.red[8 + w] = dmax;
         }
         // maxima written; B(I+1) landed (the copies of A(I-1) may stay in flight)
-        if (more) BQA_WAIT_VM(KvPlan::NA);
+        if (more) BQA_WAIT_VM(KvPlan::na<I8DP>());
         else BQA_WAIT_VM(0);
         barrier_only();
         // ---- products of tile I+1 (codes and B written / landed before the barrier)
@@ -477,20 +530,29 @@ struct QPlan {
     }
 };
 
+template <bool I8DP>
 __device__ __forceinline__ void q_copy(const SageBwdArgs& a, const QPlan& cp, int bh, int b, int hq, int J, LdsQ& L,
                                        int w) {
     const int k0 = J * TK;
     const int8_t* kbase = a.kc + ((int64_t)bh * a.N + k0) * D;
 #pragma unroll
     for (int u = 0; u < 2; ++u) lds_copy16(cp.k[u], kbase, lds_addr(L.k + 1024 * (2 * w + u)));
-    const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.sB + hq * a.v.sH + (int64_t)k0 * a.v.sN;
+    if constexpr (I8DP) {
+        // V codes in the layout of the K codes (64 x 128 B, sigma reads)
+        const int8_t* vbase = a.vc8 + ((int64_t)bh * a.N + k0) * D;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) lds_copy16(cp.v[u], vbase, lds_addr(L.vb + 1024 * (4 * w + u)));
+        for (int u = 0; u < 2; ++u) lds_copy16(cp.k[u], vbase, lds_addr(L.vb + 1024 * (2 * w + u)));
+    } else {
+        const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.sB + hq * a.v.sH + (int64_t)k0 * a.v.sN;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lds_copy16(cp.v[u], vbase, lds_addr(L.vb + 1024 * (4 * w + u)));
+    }
     const int8_t* tbase = a.kT + (int64_t)bh * D * a.N + k0;
 #pragma unroll
     for (int u = 0; u < 2; ++u) lds_copy16(cp.t[u], tbase, lds_addr(L.kT + 1024 * (2 * w + u)));
 }
 
+template <bool I8DP>
 __global__ __launch_bounds__(256, 2) void sbwd_dq_kernel(SageBwdArgs a) {
     __shared__ __attribute__((aligned(16))) LdsQ L[2];
     __shared__ float red[8];
@@ -512,10 +574,19 @@ __global__ __launch_bounds__(256, 2) void sbwd_dq_kernel(SageBwdArgs a) {
     v4i qb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qb[kk] = *(const v4i*)(a.qc + ((int64_t)bh * a.N + qrow) * D + 32 * kk + 16 * h);
-    v8bf gb[8];
-    const uint16_t* grow = (const uint16_t*)a.d_o.p + b * a.d_o.sB + hq * a.d_o.sH + (int64_t)qrow * a.d_o.sN;
+    v8bf gb[I8DP ? 1 : 8];
+    v4i gcb[I8DP ? 4 : 1];
+    float dsq = 0.0f;
+    if constexpr (I8DP) {
+        // INT8 dP: this lane's query as dO codes (B operand of dP^T = V dO^T)
 #pragma unroll
-    for (int st = 0; st < 8; ++st) gb[st] = *(const v8bf*)(grow + 16 * st + 8 * h);
+        for (int kk = 0; kk < 4; ++kk) gcb[kk] = *(const v4i*)(a.doc + ((int64_t)bh * a.N + qrow) * D + 32 * kk + 16 * h);
+        dsq = uniform_ptr(a.dos)[(int64_t)bh * nqt + I];
+    } else {
+        const uint16_t* grow = (const uint16_t*)a.d_o.p + b * a.d_o.sB + hq * a.d_o.sH + (int64_t)qrow * a.d_o.sN;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) gb[st] = *(const v8bf*)(grow + 16 * st + 8 * h);
+    }
     const float lse2 = a.lse[(int64_t)bh * a.N + qrow] * 1.4426950408889634f;
     const float dlt = a.delta[(int64_t)bh * a.N + qrow];
     __builtin_amdgcn_s_waitcnt(0);
@@ -525,13 +596,13 @@ __global__ __launch_bounds__(256, 2) void sbwd_dq_kernel(SageBwdArgs a) {
     for (int cb = 0; cb < 4; ++cb) dq[cb] = v16f{};
 
     const int nJ = a.causal ? (I * TQ + TQ - 1) / TK + 1 : nkt;
-    q_copy(a, cp, bh, b, hq, 0, L[0], w);
+    q_copy<I8DP>(a, cp, bh, b, hq, 0, L[0], w);
     BQA_WAIT_VM(0);
     barrier_only();
     for (int J = 0; J < nJ; ++J) {
         const int cur = J & 1;
         const bool more = J + 1 < nJ;
-        if (more) q_copy(a, cp, bh, b, hq, J + 1, L[cur ^ 1], w);   // that buffer's reads ended a step ago
+        if (more) q_copy<I8DP>(a, cp, bh, b, hq, J + 1, L[cur ^ 1], w);   // that buffer's reads ended a step ago
         const LdsQ& T = L[cur];
         const float ks = ks_u[J];
         const float sc = qsc * ks * c;
@@ -549,10 +620,22 @@ __global__ __launch_bounds__(256, 2) void sbwd_dq_kernel(SageBwdArgs a) {
                 sacc = mfma_i8_32x32x32(av, qb[kk], sacc);
             }
             v16f dp = v16f{};
+            if constexpr (I8DP) {
+                v16i dpi = v16i{};
 #pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                const v8bf av = *(const v8bf*)(T.vb + rk * 256 + 16 * ((2 * st + h) ^ fs256(rk)));
-                dp = mfma_bf16_32x32x16(av, gb[st], dp);
+                for (int kk = 0; kk < 4; ++kk) {
+                    const v4i av = *(const v4i*)(T.vb + rk * 128 + 16 * ((2 * kk + h) ^ fs128(rk)));
+                    dpi = mfma_i8_32x32x32(av, gcb[kk], dpi);
+                }
+                const float dsc = dsq * uniform_ptr(a.vs8)[(int64_t)bh * nkt + J];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dp[i] = (float)dpi[i] * dsc;
+            } else {
+#pragma unroll
+                for (int st = 0; st < 8; ++st) {
+                    const v8bf av = *(const v8bf*)(T.vb + rk * 256 + 16 * ((2 * st + h) ^ fs256(rk)));
+                    dp = mfma_bf16_32x32x16(av, gb[st], dp);
+                }
             }
             float p[16];
 #pragma unroll
@@ -637,7 +720,7 @@ size_t ws_sage_bwd_bytes(int B, int H, int N, int d) {
     const size_t bhn = (size_t)B * H * N;
     return bhn * 4                 // delta
            + (bhn / 128) * 4       // dO scales
-           + 3 * bhn * d           // channel-major dO, Q, K codes
+           + 4 * bhn * d           // channel-major dO, Q, K codes; row-major dO codes (INT8 dP)
            + 256;
 }
 
@@ -649,14 +732,21 @@ hipError_t launch_sage_bwd(SageBwdArgs a, Dense o, void* ws, hipStream_t st) {
     p = (uint8_t*)(((uintptr_t)p + 15) & ~(uintptr_t)15);
     int8_t* doT = (int8_t*)p;                 p += bhn * D;
     int8_t* qT = (int8_t*)p;                  p += bhn * D;
-    int8_t* kT = (int8_t*)p;
+    int8_t* kT = (int8_t*)p;                  p += bhn * D;
+    const bool i8dp = a.vc8 != nullptr;
     a.delta = delta; a.dos = dos; a.doT = doT; a.qT = qT; a.kT = kT;
+    a.doc = i8dp ? (int8_t*)p : nullptr;
 
-    do_prep_kernel<<<(unsigned)(bhn / 128), 256, 0, st>>>(a.d_o, o, a.H, a.N, delta, dos, doT);
+    do_prep_kernel<<<(unsigned)(bhn / 128), 256, 0, st>>>(a.d_o, o, a.H, a.N, delta, dos, doT, a.doc);
     const int tiles = (int)((int64_t)a.B * a.H * (a.N / 64));
     transpose2_i8_kernel<<<2 * tiles, 256, 0, st>>>(a.qc, a.kc, qT, kT, a.N, tiles);
-    sbwd_dkdv_kernel<<<a.B * a.H * (a.N / TK), 512, 0, st>>>(a);
-    sbwd_dq_kernel<<<a.B * a.H * (a.N / TQ), 256, 0, st>>>(a);
+    if (i8dp) {
+        sbwd_dkdv_kernel<true><<<a.B * a.H * (a.N / TK), 512, 0, st>>>(a);
+        sbwd_dq_kernel<true><<<a.B * a.H * (a.N / TQ), 256, 0, st>>>(a);
+    } else {
+        sbwd_dkdv_kernel<false><<<a.B * a.H * (a.N / TK), 512, 0, st>>>(a);
+        sbwd_dq_kernel<false><<<a.B * a.H * (a.N / TQ), 256, 0, st>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -83,6 +83,10 @@ struct SageBwdArgs {
     // normalised rows): raw Q, K [B,H,N,d] bf16 and their inverse norms [B,H,N]
     Dense q_raw, k_raw;
     const float* q_rn; const float* k_rn;
+    // fully INT8 variant (null: dP in bf16 from v): V's INT8 codes [B,H,N,d]
+    // and scales per 64 tokens; doc: workspace, row-major dO codes
+    const int8_t* vc8; const float* vs8;
+    int8_t* doc;
 };
 size_t ws_sage_bwd_bytes(int B, int H, int N, int d);
 hipError_t launch_sage_bwd(SageBwdArgs a, Dense o, void* ws, hipStream_t st);

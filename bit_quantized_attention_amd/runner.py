@@ -92,7 +92,7 @@ class SageTrainStep(SagePath):
     then the backward from dO (delta from the stored O, INT8 dO, four INT8
     products and the bf16 dP = dO V^T)."""
 
-    def __init__(self, p, q, k, v, d_o):
+    def __init__(self, p, q, k, v, d_o, int8_dp=False):
         super().__init__(p, q, k, v)
         dev = q.device
         self.d_o = d_o
@@ -101,9 +101,20 @@ class SageTrainStep(SagePath):
         self.dv = torch.empty_like(v)
         self.ws_bwd = torch.empty(max(bqa_workspace_size(p, BQA_OP_BWD), 16), dtype=torch.uint8, device=dev)
         self._dod = dense(d_o)
+        # the fully INT8 backward: V's INT8 codes per 64 tokens feed dP = dO V^T
+        self.vq8 = None
+        if int8_dp:
+            self.vc8 = torch.empty((p.B, p.Hkv, p.Nk, p.d), dtype=torch.int8, device=dev)
+            self.vs8 = torch.empty((p.B, p.Hkv, p.Nk // 64), dtype=torch.float32, device=dev)
+            self.vq8 = qtensor(BQA_INT8, 0, 64, self.vc8, self.vs8)
+
+    def quantize(self):
+        super().quantize()
+        if self.vq8 is not None:
+            bqa_quantize_blocks(self.p, BQA_ROLE_V, self._vd, self.vq8)
 
     def backward(self):
-        bqa_attn_bwd(self.p, q=self.qq, k=self.kq, v_hi=self._vd, o_for_delta=self._od, lse=self.lse,
+        bqa_attn_bwd(self.p, q=self.qq, k=self.kq, v=self.vq8, v_hi=self._vd, o_for_delta=self._od, lse=self.lse,
                      d_o=self._dod, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws_bwd)
 
     def step(self):

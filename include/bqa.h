@@ -154,7 +154,8 @@ size_t bqa_workspace_size(const bqa_problem* p, int32_t op);
  *  - Q, dO, INT8 axis 0: per token block of out->block tokens, scale =
  *    amax/127 and code = round-half-even(x * (127/amax)) clamped to +-127,
  *    both divisions correctly rounded in fp32 ("SageBwd", Methodology 1:
- *    per-block INT8).
+ *    per-block INT8).  V with INT8 axis 0 (block 64) is quantised the same
+ *    way, for the fully INT8 backward of bqa_attn_bwd.
  *  - K, INT8 axis 0 with p->smooth_k: K-smoothing ("SageBwd", Methodology 4
  *    and Results): mu = fp32(sum_t K / N - eps) per (b, h, channel), summed
  *    in fp64, written to k_mean [B, Hkv, d] when k_mean is not NULL; the codes
@@ -335,7 +336,12 @@ bqa_status bqa_attn_decode_static(const bqa_problem* p, const bqa_qtensor* q, co
  *    INT8 per 128 tokens; tiles of 128 queries x 64 keys; P and dS are
  *    INT8 with one scale per tile; dV = P^T dO, dQ = tau dS K and
  *    dK = tau dS^T Q run as INT8 products, dP = dO V^T in bf16 from v_hi
- *    (bf16).  Workspace: bqa_workspace_size(p, BQA_OP_BWD) bytes.
+ *    (bf16).  With v given (INT8 axis 0, block 64: V's token-block codes
+ *    from bqa_quantize_blocks) dP runs in INT8 as well, the dO codes against
+ *    the V codes times both scales: the fully INT8 backward the page's
+ *    Limitations leave open (v_hi is still validated and read for nothing
+ *    else; it may be the same V).  Otherwise v is unused.  Workspace:
+ *    bqa_workspace_size(p, BQA_OP_BWD) bytes.
  *  - BQA_QAT_MXFP4 ("Attn-QAT", §2 Principles 1 and 2): o_for_delta = O';
  *    d = 128, Hq == Hkv, Nq == Nk a multiple of 128, non-causal.  P is
  *    recomputed from the same FP4 scores; for dV it is rounded at the
