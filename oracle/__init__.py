@@ -91,6 +91,8 @@ def _declare(L):
                                      i, i, vp, vp]),
         "orc_ptq_fwd": (None, [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, vp, vp]),
         "orc_qk_norm": (None, [vp, C.c_int64, i, vp, vp]),
+        "orc_nvfp4_fake": (None, [vp, i, i, i, i, vp]),
+        "orc_thrift_fwd_nv": (None, [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, d, i, i, vp, vp]),
         "orc_qk_norm_bwd": (None, [vp, vp, vp, C.c_int64, i, vp]),
     }
     for name, (res, args) in sig.items():
@@ -403,3 +405,29 @@ def ptq_fwd(*, qc, qs, qbar, kc, ks, vc_t, vs_t, Nq, Nk, d, blk=128, causal=Fals
     lib().orc_ptq_fwd(_p(a[0]), _p(a[1]), _p(_f32(qbar)), *[_p(x) for x in b], Nq, Nk, d, blk, int(causal),
                       float(tau), qb0, qb1, _p(O), _p(lse))
     return O, lse
+
+
+def nvfp4_fake(X: np.ndarray, axis: int) -> np.ndarray:
+    """NVFP4 emulation ("ThriftAttention", Method step 2): X [BH, N, d] ->
+    the dequantised NVFP4 values (blocks of 16 along d for axis 0, along the
+    tokens of each channel for axis 1; E4M3 block scales; a power-of-two
+    tensor scale per slice)."""
+    X = _f32(X)
+    BH, N, d = X.shape
+    out = np.empty_like(X)
+    lib().orc_nvfp4_fake(_p(X), BH, N, d, int(axis), _p(out))
+    return out
+
+
+def thrift_fwd_nv(*, Qn, Kn, Vn, Qh, Kh, Vh, sel_idx, sel_cnt, Nq, Nk, d, blk=128, hp_tile=64, causal=True, tau,
+                  qblocks=None):
+    """Thrift prefill with the FP4 path in NVFP4 emulation (dequantised NVFP4
+    Qn, Kn, Vn; two-level NVFP4 P; tiles of hp_tile keys)."""
+    qb0, qb1 = (0, Nq // blk) if qblocks is None else qblocks
+    O = np.empty(((qb1 - qb0) * blk, d)); lse = np.empty((qb1 - qb0) * blk)
+    sel_idx = _c(sel_idx, np.int32)
+    lib().orc_thrift_fwd_nv(*[_p(_f32(x)) for x in (Qn, Kn, Vn, Qh, Kh, Vh)], _p(sel_idx),
+                            _p(_c(sel_cnt, np.int32)), sel_idx.shape[1], Nq, Nk, d, blk, hp_tile, int(causal),
+                            float(tau), qb0, qb1, _p(O), _p(lse))
+    return O, lse
+

@@ -906,6 +906,7 @@ typedef struct {
     int Nk, d, quantize;
     double tau;
     const double* bias;   /* FP4 path: added to key j's raw score (query smoothing); NULL: none */
+    const float *Qn, *Kn, *Vn;   /* NVFP4 emulation (path 2): the dequantised NVFP4 rows */
 } thrift_ctx;
 
 /* One key block (keys [j0, j0+n)) through one path, for query row i (row
@@ -915,10 +916,14 @@ typedef struct {
  * as (r/6) deq(P'), times the FP4 V.  path 1: bf16 — scores from the bf16
  * Q and K, bf16(P) times the bf16 V.  quantize == 0: both paths use the
  * bf16 operands and unrounded P. */
+static void nvfp4_p_tile(double* p, int n, double* out);
+
 static void thrift_block(const thrift_ctx* c, row_state* st, int i, int j0, int n, int path) {
     int d = c->d;
     double s[256], p[256];
     double tmax = -INFINITY;
+    const float* Qx = path == 2 ? c->Qn : c->Qh;
+    const float* Kx = path == 2 ? c->Kn : c->Kh;
     for (int u = 0; u < n; ++u) {
         int j = j0 + u;
         if (path == 0 && c->quantize) {
@@ -927,12 +932,22 @@ static void thrift_block(const thrift_ctx* c, row_state* st, int i, int j0, int 
             s[u] *= c->tau;
         } else {
             double acc = 0.0;
-            for (int k = 0; k < d; ++k) acc += (double)c->Qh[(size_t)i * d + k] * (double)c->Kh[(size_t)j * d + k];
+            for (int k = 0; k < d; ++k) acc += (double)Qx[(size_t)i * d + k] * (double)Kx[(size_t)j * d + k];
             s[u] = c->tau * acc;
         }
         if (s[u] > tmax) tmax = s[u];
     }
     row_update_max(st, tmax, d);
+    if (path == 2) {
+        /* NVFP4 emulation: P quantised in two levels to NVFP4, times the
+         * dequantised NVFP4 V */
+        double pq[256];
+        for (int u = 0; u < n; ++u) { p[u] = exp(s[u] - st->m); st->l += p[u]; }
+        nvfp4_p_tile(p, n, pq);
+        for (int u = 0; u < n; ++u)
+            for (int k = 0; k < d; ++k) st->acc[k] += pq[u] * (double)c->Vn[(size_t)(j0 + u) * d + k];
+        return;
+    }
     double r = 0.0;
     for (int u = 0; u < n; ++u) { p[u] = exp(s[u] - st->m); st->l += p[u]; if (p[u] > r) r = p[u]; }
     if (!c->quantize) {
@@ -973,7 +988,7 @@ void orc_thrift_fwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, con
                     const int32_t* sel_idx, const int32_t* sel_cnt, int max_sel,
                     int Nq, int Nk, int d, int blk, int hp_tile, int causal, double tau, int quantize,
                     int qb0, int qb1, double* O, double* lse) {
-    thrift_ctx c = {qc, qs, kc, ks, vc_t, vs_t, Qh, Kh, Vh, Nk, d, quantize, tau, NULL};
+    thrift_ctx c = {qc, qs, kc, ks, vc_t, vs_t, Qh, Kh, Vh, Nk, d, quantize, tau, NULL, NULL, NULL, NULL};
     int nkb = Nk / blk;
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int I = qb0; I < qb1; ++I)
@@ -1012,7 +1027,7 @@ void orc_thrift_decode(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, 
                        const float* q, const float* Kh, const float* Vh,
                        const int32_t* sel, int nsel, int Nk, int d, int blk, int hp_tile, double tau,
                        int num_splits, int quantize, double* o, double* lse) {
-    thrift_ctx c = {qc, qs, kc, ks, vc_t, vs_t, q, Kh, Vh, Nk, d, quantize, tau, NULL};
+    thrift_ctx c = {qc, qs, kc, ks, vc_t, vs_t, q, Kh, Vh, Nk, d, quantize, tau, NULL, NULL, NULL, NULL};
     int nb = Nk / blk;
     double* ms = (double*)malloc(sizeof(double) * (size_t)num_splits);
     double* ls = (double*)malloc(sizeof(double) * (size_t)num_splits);
@@ -1077,7 +1092,7 @@ void orc_ptq_fwd(const uint8_t* qc, const uint8_t* qs, const float* qbar, const 
             for (int c = 0; c < d; ++c) acc += (double)qbar[(size_t)I * d + c] * kmx(kc, ks, d, j, c);
             bias[j] = acc;
         }
-        thrift_ctx ctx = {qc, qs, kc, ks, vc_t, vs_t, NULL, NULL, NULL, Nk, d, 1, tau, bias};
+        thrift_ctx ctx = {qc, qs, kc, ks, vc_t, vs_t, NULL, NULL, NULL, Nk, d, 1, tau, bias, NULL, NULL, NULL};
         int rows = Nq - I * blk < blk ? Nq - I * blk : blk;
 #pragma omp parallel for schedule(dynamic)
         for (int a = 0; a < rows; ++a) {
@@ -1128,5 +1143,120 @@ void orc_qk_norm_bwd(const float* X, const float* r, const double* G, int64_t ro
         for (int c = 0; c < d; ++c) t += (double)x[c] * ri * g[c];
         for (int c = 0; c < d; ++c) dX[(size_t)i * d + c] = ri * (g[c] - (double)x[c] * ri * t);
     }
+}
+
+/* ========================================================================
+ * NVFP4 format emulation ([TA] Method step 2: the FP4 path uses NVFP4
+ * micro-scaling: e2m1 values in blocks of 16 with an E4M3 block scale)
+ * ====================================================================== */
+
+/* e4m3 value nearest to x (RNE, saturating at 448). */
+static double e4m3_value(double x) { return orc_round_grid(x, 3, -6, 448.0, 1); }
+/* e2m1 value nearest to x (RNE, saturating at 6). */
+static double e2m1_value(double x) { return orc_round_grid(x, 1, 0, 6.0, 1); }
+
+/* One block of 16 values with shared scale S (an fp32 value, the block
+ * scale times the tensor scale): x_q = e2m1(fp32(x / S)) S; S == 0 gives
+ * zeros. */
+static void nv_block(const float* x, int stride, int n, float S, float* out, int ostride) {
+    for (int u = 0; u < n; ++u) {
+        double v = 0.0;
+        if (S != 0.0f) v = e2m1_value((double)(x[(size_t)u * stride] / S)) * (double)S;
+        out[(size_t)u * ostride] = (float)v;
+    }
+}
+
+/* NVFP4 quantisation of one [N, d] slice, written back as the dequantised
+ * values (exact in fp32 and in bf16): blocks of 16 along d (axis 0: Q, K)
+ * or along the tokens of each channel (axis 1: V).  Reading of the
+ * two-level scale: the tensor scale g of the slice is the power of two at
+ * or above amax / (448 * 6) (1 for an all-zero slice), so that every block
+ * scale fits E4M3; a block's scale is e4m3(fp32(amax_b / fp32(6 g))) and
+ * its values e2m1(fp32(x / fp32(s_b g))) s_b g. */
+void orc_nvfp4_fake(const float* X, int BH, int N, int d, int axis, float* out) {
+    for (int bh = 0; bh < BH; ++bh) {
+        const float* x = X + (size_t)bh * N * d;
+        float* o = out + (size_t)bh * N * d;
+        float amax = 0.0f;
+        for (size_t t = 0; t < (size_t)N * d; ++t) if (fabsf(x[t]) > amax) amax = fabsf(x[t]);
+        float g = 1.0f;
+        if (amax > 0.0f) {
+            int E;
+            double q = (double)amax / 2688.0;
+            double f = frexp(q, &E);          /* q = f 2^E, f in [0.5, 1) */
+            g = (float)ldexp(1.0, f == 0.5 ? E - 1 : E);
+        }
+        float six_g = 6.0f * g;
+        int nb = axis == 0 ? d / 16 : N / 16;
+        int nrow = axis == 0 ? N : d;
+        for (int r = 0; r < nrow; ++r)
+            for (int b = 0; b < nb; ++b) {
+                const float* xb = axis == 0 ? x + (size_t)r * d + 16 * b : x + (size_t)16 * b * d + r;
+                float* ob = axis == 0 ? o + (size_t)r * d + 16 * b : o + (size_t)16 * b * d + r;
+                int stride = axis == 0 ? 1 : d;
+                float am = 0.0f;
+                for (int u = 0; u < 16; ++u) if (fabsf(xb[(size_t)u * stride]) > am) am = fabsf(xb[(size_t)u * stride]);
+                float sb = (float)e4m3_value((double)(am / six_g));
+                nv_block(xb, stride, 16, sb * g, ob, stride);
+            }
+    }
+}
+
+/* Two-level NVFP4 quantisation of one row's probabilities in a tile of n
+ * keys (n a multiple of 16): r = the tile's largest fp32(P); P' =
+ * fp32(fp32(P) fp32(2688 / r)) puts it at 448 * 6; blocks of 16 keys get the
+ * scale e4m3(fp32(amax / 6)) and values e2m1(fp32(P' / s_b)) s_b; the first
+ * level is undone as bf16(fp32(P^' fp32(r / 2688))), the operand of the
+ * bf16 P.V.  A tile whose P all underflow fp32 gives zeros. */
+static void nvfp4_p_tile(double* p, int n, double* out) {
+    float pf[256], pp[256];
+    float r = 0.0f;
+    for (int u = 0; u < n; ++u) { pf[u] = (float)p[u]; if (pf[u] > r) r = pf[u]; }
+    if (r == 0.0f) { for (int u = 0; u < n; ++u) out[u] = 0.0; return; }
+    float f_in = 2688.0f / r, f_out = r / 2688.0f;
+    for (int u = 0; u < n; ++u) pp[u] = pf[u] * f_in;
+    for (int b = 0; b < n; b += 16) {
+        float am = 0.0f;
+        for (int u = b; u < b + 16 && u < n; ++u) if (pp[u] > am) am = pp[u];
+        float sb = (float)e4m3_value((double)(am / 6.0f));
+        for (int u = b; u < b + 16 && u < n; ++u) {
+            double q = sb != 0.0f ? e2m1_value((double)(pp[u] / sb)) * (double)sb : 0.0;
+            out[u] = orc_bf16_value((double)((float)q * f_out));
+        }
+    }
+}
+
+/* Thrift prefill in NVFP4 emulation: as orc_thrift_fwd, except that the
+ * unselected blocks take path 2 (the dequantised NVFP4 Q, K, V of Qn, Kn,
+ * Vn, NVFP4 two-level P) in tiles of hp_tile keys. */
+void orc_thrift_fwd_nv(const float* Qn, const float* Kn, const float* Vn, const float* Qh, const float* Kh,
+                       const float* Vh, const int32_t* sel_idx, const int32_t* sel_cnt, int max_sel, int Nq, int Nk,
+                       int d, int blk, int hp_tile, int causal, double tau, int qb0, int qb1, double* O,
+                       double* lse) {
+    thrift_ctx c = {NULL, NULL, NULL, NULL, NULL, NULL, Qh, Kh, Vh, Nk, d, 1, tau, NULL, Qn, Kn, Vn};
+    int nkb = Nk / blk;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int I = qb0; I < qb1; ++I)
+        for (int a = 0; a < blk; ++a) {
+            int i = I * blk + a;
+            int last = last_key(i, Nq, Nk, causal);
+            const int32_t* sel = sel_idx + (size_t)I * max_sel;
+            int ns = sel_cnt[I];
+            row_state st = {-INFINITY, 0.0, (double*)calloc((size_t)d, sizeof(double)), NULL};
+            for (int pass = 0; pass < 2; ++pass)
+                for (int J = 0; J < nkb && J * blk <= last; ++J) {
+                    int picked = 0;
+                    for (int u = 0; u < ns; ++u) if (sel[u] == J) picked = 1;
+                    if (picked != pass) continue;
+                    for (int t0 = J * blk; t0 < (J + 1) * blk && t0 <= last; t0 += hp_tile) {
+                        int n = hp_tile;
+                        if (t0 + n - 1 > last) n = last - t0 + 1;
+                        thrift_block(&c, &st, i, t0, n, pass ? 1 : 2);
+                    }
+                }
+            for (int k = 0; k < d; ++k) O[((size_t)(I - qb0) * blk + a) * d + k] = st.acc[k] / st.l;
+            lse[(size_t)(I - qb0) * blk + a] = st.m + log(st.l);
+            free(st.acc);
+        }
 }
 

@@ -101,6 +101,11 @@ void orc_thrift_decode(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, 
 void orc_ptq_fwd(const uint8_t* qc, const uint8_t* qs, const float* qbar, const uint8_t* kc, const uint8_t* ks,
                  const uint8_t* vc_t, const uint8_t* vs_t, int Nq, int Nk, int d, int blk, int causal, double tau,
                  int qb0, int qb1, double* O, double* lse);
+void orc_nvfp4_fake(const float* X, int BH, int N, int d, int axis, float* out);
+void orc_thrift_fwd_nv(const float* Qn, const float* Kn, const float* Vn, const float* Qh, const float* Kh,
+                       const float* Vh, const int32_t* sel_idx, const int32_t* sel_cnt, int max_sel, int Nq, int Nk,
+                       int d, int blk, int hp_tile, int causal, double tau, int qb0, int qb1, double* O,
+                       double* lse);
 void orc_qk_norm(const float* X, int64_t rows, int d, float* Y, float* r);
 void orc_qk_norm_bwd(const float* X, const float* r, const double* G, int64_t rows, int d, double* dX);
 
