@@ -29,12 +29,12 @@ BQA_BF16, BQA_FP16, BQA_INT8, BQA_FP8E4M3, BQA_MXFP4 = range(5)
 BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV, BQA_SAGE_I8_I8PV, BQA_QAT_MXFP4, BQA_THRIFT, BQA_PTQ_MXFP4 = range(6)
 BQA_ROLE_Q, BQA_ROLE_K, BQA_ROLE_V, BQA_ROLE_DO = range(4)
 BQA_OP_QUANTIZE_Q, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_V, BQA_OP_QUANTIZE_DO, BQA_OP_SELECT, BQA_OP_FWD, \
-    BQA_OP_BWD, BQA_OP_QUANTIZE_KV = range(8)
+    BQA_OP_BWD, BQA_OP_QUANTIZE_KV, BQA_OP_QUANTIZE_NVFP4 = range(9)
 
 EXPORTS = ["bqa_abi_version", "bqa_status_string", "bqa_workspace_size", "bqa_quantize_blocks", "bqa_quantize_kv",
            "bqa_select_blocks", "bqa_attn_fwd", "bqa_attn_bwd", "bqa_debug_qk_scores", "bqa_attn_decode_static",
            "bqa_debug_mx_dequant", "bqa_attn_fwd_ptq", "bqa_debug_probe", "bqa_quantize_qknorm",
-           "bqa_attn_bwd_qknorm"]
+           "bqa_attn_bwd_qknorm", "bqa_quantize_nvfp4", "bqa_attn_fwd_thrift_nvfp4"]
 BQA_PROBE_MFMA_I8, BQA_PROBE_MFMA_F8, BQA_PROBE_MFMA_F4, BQA_PROBE_MFMA_BF16, BQA_PROBE_EXP, BQA_PROBE_COPY, \
     BQA_PROBE_READ = range(7)
 
@@ -110,6 +110,12 @@ def lib():
         L.bqa_attn_bwd_qknorm.argtypes = [P(bqa_problem), P(bqa_qtensor), P(bqa_qtensor), P(bqa_tensor),
                                           P(bqa_tensor), vp, P(bqa_tensor), P(bqa_tensor), P(bqa_tensor), vp, vp,
                                           P(bqa_tensor), P(bqa_tensor), P(bqa_tensor), vp, C.c_size_t, vp]
+        L.bqa_quantize_nvfp4.restype = C.c_int32
+        L.bqa_quantize_nvfp4.argtypes = [P(bqa_problem), C.c_int32, P(bqa_tensor), P(bqa_tensor), vp, C.c_size_t, vp]
+        L.bqa_attn_fwd_thrift_nvfp4.restype = C.c_int32
+        L.bqa_attn_fwd_thrift_nvfp4.argtypes = [P(bqa_problem), P(bqa_tensor), P(bqa_tensor), P(bqa_tensor),
+                                                P(bqa_tensor), P(bqa_tensor), P(bqa_tensor), vp, vp, P(bqa_tensor),
+                                                vp, vp]
         L.bqa_debug_probe.restype = C.c_int32
         L.bqa_debug_probe.argtypes = [C.c_int32, C.c_int32, C.c_int64, vp, vp, C.c_size_t, vp]
         L.bqa_debug_mx_dequant.restype = C.c_int32
@@ -317,6 +323,30 @@ def bqa_attn_bwd_qknorm(p, q=None, k=None, v_hi=None, o_for_delta=None, lse=None
                                   _stream(stream))
     if check:
         _check(s, "bqa_attn_bwd_qknorm")
+    return s
+
+
+def bqa_quantize_nvfp4(p, role, x, out, workspace=None, workspace_bytes=None, stream=None, check=True) -> int:
+    def dd(t):
+        return t if (t is None or isinstance(t, bqa_tensor)) else dense(t)
+    wb = workspace_bytes if workspace_bytes is not None else (workspace.numel() * workspace.element_size()
+                                                              if workspace is not None else 0)
+    s = lib().bqa_quantize_nvfp4(C.byref(p), int(role), _ref(dd(x)), _ref(dd(out)), _ptr(workspace), wb,
+                                 _stream(stream))
+    if check:
+        _check(s, "bqa_quantize_nvfp4")
+    return s
+
+
+def bqa_attn_fwd_thrift_nvfp4(p, q_nv=None, k_nv=None, v_nv=None, q_hi=None, k_hi=None, v_hi=None, sel_idx=None,
+                              sel_cnt=None, o=None, lse=None, stream=None, check=True) -> int:
+    def dd(t):
+        return t if (t is None or isinstance(t, bqa_tensor)) else dense(t)
+    s = lib().bqa_attn_fwd_thrift_nvfp4(C.byref(p), _ref(dd(q_nv)), _ref(dd(k_nv)), _ref(dd(v_nv)), _ref(dd(q_hi)),
+                                        _ref(dd(k_hi)), _ref(dd(v_hi)), _ptr(sel_idx), _ptr(sel_cnt), _ref(dd(o)),
+                                        _ptr(lse), _stream(stream))
+    if check:
+        _check(s, "bqa_attn_fwd_thrift_nvfp4")
     return s
 
 

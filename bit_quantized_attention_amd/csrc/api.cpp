@@ -214,6 +214,10 @@ size_t bqa_workspace_size(const bqa_problem* p, int32_t op) {
                 return ws_decode_bytes(p->B, p->Hq, p->Hkv, p->Nk, p->num_splits);
             if (p->mode == BQA_PTQ_MXFP4) return ws_ptq_fwd_bytes(p->B, p->Hq, p->Nq, p->Nk);
             return 0;
+        case BQA_OP_QUANTIZE_NVFP4: {
+            const size_t a = ws_nvfp4_bytes(p->B * p->Hq, p->Nq, p->d), b = ws_nvfp4_bytes(p->B * p->Hkv, p->Nk, p->d);
+            return a > b ? a : b;
+        }
         default:
             return 0;
     }
@@ -530,6 +534,55 @@ bqa_status bqa_attn_bwd_qknorm(const bqa_problem* p, const bqa_qtensor* q, const
                              dbg16(q_raw, p->B, p->Hq, p->Nq, p->d), dbg16(k_raw, p->B, p->Hq, p->Nq, p->d),
                              dbg32(q_inv_norm, bhn), dbg32(k_inv_norm, bhn)}));
     return launched(launch_sage_bwd(a, as_dense(o_for_delta), ws, (hipStream_t)stream));
+}
+
+bqa_status bqa_quantize_nvfp4(const bqa_problem* p, int32_t role, const bqa_tensor* x, bqa_tensor* out, void* ws,
+                              size_t ws_bytes, void* stream) {
+    TRY(check_problem(p));
+    if (p->d != 128) return BQA_E_UNSUPPORTED;
+    if (role != BQA_ROLE_Q && role != BQA_ROLE_K && role != BQA_ROLE_V) return BQA_E_UNSUPPORTED;
+    const bool kv = role != BQA_ROLE_Q;
+    const int H = kv ? p->Hkv : p->Hq, N = kv ? p->Nk : p->Nq;
+    TRY(check_dense(x, true, true));
+    TRY(check_dense(out, false, true));
+    if (role == BQA_ROLE_V && N % 32 != 0) return BQA_E_UNSUPPORTED;
+    if (!ws || ws_bytes < ws_nvfp4_bytes(p->B * H, N, p->d)) return BQA_E_WORKSPACE;
+    if (!aligned16(ws)) return BQA_E_ALIGN;
+    TRY(check_device());
+    TRY(debug_check(stream, {dbg16(x, p->B, H, N, p->d)}));
+    return launched(launch_nvfp4(as_dense(x), x->dtype == BQA_FP16, p->B, H, N, p->d, role == BQA_ROLE_V ? 1 : 0,
+                                 as_dense(out), ws, (hipStream_t)stream));
+}
+
+bqa_status bqa_attn_fwd_thrift_nvfp4(const bqa_problem* p, const bqa_tensor* q_nv, const bqa_tensor* k_nv,
+                                     const bqa_tensor* v_nv, const bqa_tensor* q_hi, const bqa_tensor* k_hi,
+                                     const bqa_tensor* v_hi, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                     bqa_tensor* o, float* lse, void* stream) {
+    TRY(check_problem(p));
+    if (p->mode != BQA_THRIFT || p->Nq < 2) return BQA_E_UNSUPPORTED;
+    if (p->d != 128 || p->sel_block != 128 || p->Nk % 128 != 0) return BQA_E_UNSUPPORTED;
+    if (p->causal && p->Nq % 128 != 0) return BQA_E_UNSUPPORTED;
+    TRY(check_dense(q_nv, false, true));
+    TRY(check_dense(k_nv, false, true));
+    TRY(check_dense(v_nv, false, true));
+    TRY(check_dense(q_hi, false, true));
+    TRY(check_dense(k_hi, false, true));
+    TRY(check_dense(v_hi, false, true));
+    TRY(check_dense(o, false, true));
+    if (!sel_idx || !sel_cnt) return BQA_E_NULL;
+    if (p->hp_budget_ppm < 0 || p->hp_budget_ppm > 1000000) return BQA_E_SHAPE;
+    ThriftFwdArgs a{};
+    a.q_nv = as_dense(q_nv); a.k_nv = as_dense(k_nv); a.v_nv = as_dense(v_nv);
+    a.q_hi = as_dense(q_hi); a.k_hi = as_dense(k_hi); a.v_hi = as_dense(v_hi);
+    a.sel_idx = sel_idx; a.sel_cnt = sel_cnt; a.max_sel = max_sel_of(p);
+    a.o = as_dense(o); a.lse = lse;
+    a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk; a.causal = p->causal;
+    a.c_log2 = tau_of(p) * 1.4426950408889634f;
+    TRY(check_device());
+    TRY(debug_check(stream, {dbg16(q_nv, p->B, p->Hq, p->Nq, p->d), dbg16(k_nv, p->B, p->Hkv, p->Nk, p->d),
+                             dbg16(v_nv, p->B, p->Hkv, p->Nk, p->d), dbg16(q_hi, p->B, p->Hq, p->Nq, p->d),
+                             dbg16(k_hi, p->B, p->Hkv, p->Nk, p->d), dbg16(v_hi, p->B, p->Hkv, p->Nk, p->d)}));
+    return launched(launch_thrift_nv(a, (hipStream_t)stream));
 }
 
 bqa_status bqa_attn_decode_static(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,

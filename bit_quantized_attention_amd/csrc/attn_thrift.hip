@@ -86,18 +86,22 @@ __device__ __forceinline__ void issue_f4(const ThriftFwdArgs& a, int bhk, int J,
 struct VStage {
     v4i v[4];
 };
-__device__ __forceinline__ void issue_bf(const ThriftFwdArgs& a, int b, int hk, int k0, LdsBf& L, int w, int l,
-                                         int tid, VStage& vs) {
-    const uint16_t* kb = (const uint16_t*)a.k_hi.p + b * a.k_hi.sB + hk * a.k_hi.sH + (int64_t)k0 * a.k_hi.sN;
+__device__ __forceinline__ void issue_bf(const Dense& kx, const Dense& vx, int b, int hk, int k0, LdsBf& L, int w,
+                                         int l, int tid, VStage& vs) {
+    const uint16_t* kb = (const uint16_t*)kx.p + b * kx.sB + hk * kx.sH + (int64_t)k0 * kx.sN;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int sgm = 4 * w + u, r = 4 * sgm + (l >> 4);
-        lds_copy16((uint32_t)(2 * (r * a.k_hi.sN + 8 * ((l & 15) ^ fk256(r)))), kb, lds_addr(L.k + 1024 * sgm));
+        lds_copy16((uint32_t)(2 * (r * kx.sN + 8 * ((l & 15) ^ fk256(r)))), kb, lds_addr(L.k + 1024 * sgm));
     }
-    const uint16_t* vb = (const uint16_t*)a.v_hi.p + b * a.v_hi.sB + hk * a.v_hi.sH;
+    const uint16_t* vb = (const uint16_t*)vx.p + b * vx.sB + hk * vx.sH;
     const int cg = tid & 15, kq = tid >> 4;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) vs.v[u] = *(const v4i*)(vb + (int64_t)(k0 + 4 * kq + u) * a.v_hi.sN + 8 * cg);
+    for (int u = 0; u < 4; ++u) vs.v[u] = *(const v4i*)(vb + (int64_t)(k0 + 4 * kq + u) * vx.sN + 8 * cg);
+}
+__device__ __forceinline__ void issue_bf(const ThriftFwdArgs& a, int b, int hk, int k0, LdsBf& L, int w, int l,
+                                         int tid, VStage& vs) {
+    issue_bf(a.k_hi, a.v_hi, b, hk, k0, L, w, l, tid, vs);
 }
 __device__ __forceinline__ void store_bf(const VStage& vs, LdsBf& L, int tid) {
     const int cg = tid & 15, kq = tid >> 4;
@@ -466,7 +470,195 @@ __global__ __launch_bounds__(256) void ptq_bias_kernel(const uint8_t* __restrict
     }
 }
 
+// Two-level NVFP4 quantisation of 16 probabilities (one e2m1 block) of a
+// row whose tile maximum r maps to 448 * 6 (f_in = 2688 / r): block scale
+// e4m3(fp32(amax / 6)), values e2m1(fp32(P' / s_b)) s_b, then back by
+// f_out = r / 2688 (the caller rounds the result to bf16 for P.V).
+__device__ __forceinline__ void nv_p16(v16f& p, float f_in, float f_out) {
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        p[i] = p[i] * f_in;
+        am = __builtin_fmaxf(am, p[i]);
+    }
+    const float sb = e4m3_round(am / 6.0f);
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+        if (sb != 0.0f) {
+            const v2f q = e2m1_round2(p[i] / sb, p[i + 1] / sb);
+            p[i] = (q[0] * sb) * f_out;
+            p[i + 1] = (q[1] * sb) * f_out;
+        } else {
+            p[i] = p[i + 1] = 0.0f;
+        }
+    }
+}
+
+// ThriftAttention prefill with the FP4 path in NVFP4 emulation ("Thrift-
+// Attention", Method step 2 names NVFP4): the scaled matrix instructions take
+// only power-of-two block scales, so the unselected blocks run the 16-bit
+// instructions on the dequantised NVFP4 Q, K, V (exact in bf16) with P
+// quantised in two levels to NVFP4 in registers (each lane's 16 keys of a
+// half-tile form one e2m1 block); the selected blocks follow through the
+// ordinary bf16 path.  Tiles of 64 keys, FlashAttention-2's online softmax.
+__global__ __launch_bounds__(256, 2) void thrift_nv_kernel(ThriftFwdArgs a) {
+    __shared__ __attribute__((aligned(16))) LdsBf lds[2];
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
+    const int nqt = (a.Nq + BM - 1) / BM;
+    const int grid = gridDim.x;
+    const int bid = (grid & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (grid >> 3) + (int)(blockIdx.x >> 3);
+    const int qt = nqt - 1 - bid % nqt;
+    const int bh = bid / nqt, b = bh / a.Hq, hq = bh % a.Hq;
+    const int hk = hq / (a.Hq / a.Hkv);
+    const int qrow = qt * BM + 32 * w + lq;
+    const bool row_ok = qrow < a.Nq;
+    const int krow = sigma(lq);
+    const int off = a.Nk - a.Nq;
+    const int qpos = off + qrow;
+    const int qpos_lo = off + qt * BM;
+    const int qpos_hi = off + (qt * BM + BM - 1 < a.Nq - 1 ? qt * BM + BM - 1 : a.Nq - 1);
+    const int nkb = a.Nk / KB;
+    const int nJ = a.causal ? (qpos_hi / KB + 1 < nkb ? qpos_hi / KB + 1 : nkb) : nkb;
+    const int32_t* sel = a.sel_idx + ((int64_t)bh * nqt + qt) * a.max_sel;
+    const int ns = a.sel_cnt[(int64_t)bh * nqt + qt];
+    const float c = a.c_log2;
+
+    v16f oacc[D / 32];
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = v16f{};
+    float m_run = -__builtin_inff(), l_run = 0.0f;
+
+    // items: halves of 64 keys, first those of the unselected valid blocks
+    // (phase 0, NVFP4), then those of the selected blocks (phase 1, bf16)
+    int sp = 0;
+    auto next_unsel = [&](int J) {
+        while (sp < ns && sel[sp] < J) ++sp;
+        while (J < nJ && sp < ns && sel[sp] == J) { ++J; ++sp; }
+        return J;
+    };
+    struct Item { int J, half, phase, si; };
+    auto after_phase0 = [&]() { return ns > 0 ? Item{sel[0], 0, 1, 0} : Item{-1, 0, 0, 0}; };
+    auto advance = [&](Item x) {
+        if (x.half == 0) return Item{x.J, 1, x.phase, x.si};
+        if (x.phase == 0) {
+            const int J = next_unsel(x.J + 1);
+            return J < nJ ? Item{J, 0, 0, 0} : after_phase0();
+        }
+        return x.si + 1 < ns ? Item{sel[x.si + 1], 0, 1, x.si + 1} : Item{-1, 0, 0, 0};
+    };
+    auto issue = [&](const Item& x, LdsBf& L, VStage& vs) {
+        const int k0 = x.J * KB + HB * x.half;
+        if (x.phase == 0) issue_bf(a.k_nv, a.v_nv, b, hk, k0, L, w, l, tid, vs);
+        else issue_bf(a.k_hi, a.v_hi, b, hk, k0, L, w, l, tid, vs);
+    };
+    Item cur;
+    {
+        const int J0 = next_unsel(0);
+        cur = J0 < nJ ? Item{J0, 0, 0, 0} : after_phase0();
+    }
+    if (cur.J >= 0) {
+        VStage vst;
+        issue(cur, lds[0], vst);
+        store_bf(vst, lds[0], tid);
+        BQA_WAIT_VM(0);
+        barrier_only();
+    }
+    int buf = 0;
+    const int qr = row_ok ? qrow : 0;
+    while (cur.J >= 0) {
+        const Item nx = advance(cur);
+        VStage vst;
+        if (nx.J >= 0) issue(nx, lds[buf ^ 1], vst);
+        const LdsBf& L = lds[buf];
+        const int k0 = cur.J * KB + HB * cur.half;
+        const Dense& qx = cur.phase == 0 ? a.q_nv : a.q_hi;
+        const uint16_t* qh = (const uint16_t*)qx.p + b * qx.sB + hq * qx.sH + (int64_t)qr * qx.sN;
+        v8bf qv[8];
+#pragma unroll
+        for (int st = 0; st < 8; ++st) qv[st] = *(const v8bf*)(qh + 16 * st + 8 * h);
+        v16f s0 = v16f{}, s1 = v16f{};
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const v8bf a0 = *(const v8bf*)(L.k + krow * 256 + 16 * ((2 * st + h) ^ fk256(krow)));
+            const v8bf a1 = *(const v8bf*)(L.k + (32 + krow) * 256 + 16 * ((2 * st + h) ^ fk256(32 + krow)));
+            s0 = mfma_bf16_32x32x16(a0, qv[st], s0);
+            s1 = mfma_bf16_32x32x16(a1, qv[st], s1);
+        }
+        if (a.causal && k0 + HB - 1 > qpos_lo) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (k0 + 16 * h + i > qpos) s0[i] = -__builtin_inff();
+                if (k0 + 32 + 16 * h + i > qpos) s1[i] = -__builtin_inff();
+            }
+        }
+        float m = __builtin_fmaxf(s0[0], s1[0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m = __builtin_fmaxf(__builtin_fmaxf(m, s0[i]), s1[i]);
+        follow_max(oacc, l_run, m_run, __builtin_fmaxf(m_run, __builtin_fmaxf(m, partner32f(m)) * c));
+        const float mu = m_run == -__builtin_inff() ? 0.0f : m_run;
+        float ps[2] = {0.0f, 0.0f};
+        float r = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -mu));
+            s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -mu));
+            ps[0] += s0[i];
+            ps[1] += s1[i];
+            r = __builtin_fmaxf(r, __builtin_fmaxf(s0[i], s1[i]));
+        }
+        l_run += ps[0] + ps[1];
+        if (cur.phase == 0) {
+            r = __builtin_fmaxf(r, partner32f(r));
+            if (r > 0.0f) {
+                const float f_in = 2688.0f / r, f_out = r / 2688.0f;
+                nv_p16(s0, f_in, f_out);
+                nv_p16(s1, f_in, f_out);
+            }
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            v8bf pbf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pbf[e] = (__bf16)(st < 2 ? s0[8 * (st % 2) + e] : s1[8 * (st % 2) + e]);
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb) {
+                const int rr = 32 * cb + lq;
+                const v8bf av = *(const v8bf*)(L.vt + rr * 128 + 16 * ((4 * (st / 2) + 2 * h + (st % 2)) ^ fv128(rr)));
+                oacc[cb] = mfma_bf16_32x32x16(av, pbf, oacc[cb]);
+            }
+        }
+        if (nx.J >= 0) store_bf(vst, lds[buf ^ 1], tid);
+        BQA_WAIT_VM(0);
+        barrier_only();
+        buf ^= 1;
+        cur = nx;
+    }
+
+    const float l_tot = l_run + partner32f(l_run);
+    if (!row_ok) return;
+    const float inv_l = 1.0f / l_tot;
+    uint16_t* orow = (uint16_t*)a.o.p + b * a.o.sB + hq * a.o.sH + (int64_t)qrow * a.o.sN;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int ch0 = 32 * cb + 8 * g + 4 * h;
+            uint16_t o4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o4[e] = f32_to_bf16_bits(oacc[cb][4 * g + e] * inv_l);
+            *(uint2*)(orow + ch0) =
+                make_uint2((uint32_t)o4[0] | ((uint32_t)o4[1] << 16), (uint32_t)o4[2] | ((uint32_t)o4[3] << 16));
+        }
+    }
+    if (a.lse && h == 0) a.lse[(int64_t)bh * a.Nq + qrow] = m_run * 0.6931471805599453f + __logf(l_tot);
+}
+
 }  // namespace
+
+hipError_t launch_thrift_nv(const ThriftFwdArgs& a, hipStream_t st) {
+    thrift_nv_kernel<<<a.B * a.Hq * ((a.Nq + BM - 1) / BM), 256, 0, st>>>(a);
+    return hipGetLastError();
+}
 
 hipError_t launch_thrift_fwd(const ThriftFwdArgs& a, hipStream_t st) {
     const int grid = a.B * a.Hq * ((a.Nq + BM - 1) / BM);

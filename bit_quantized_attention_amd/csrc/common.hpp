@@ -176,4 +176,28 @@ __device__ __forceinline__ float wave_max(float v) {
     return __builtin_fmaxf(v, partner32f(v));
 }
 
+// ------------------------------------------------------------------ NVFP4 emulation
+// Nearest e4m3 value of x >= 0 (the hardware's nearest-even conversion after
+// clamping to 448, i.e. saturating), back in fp32.
+__device__ __forceinline__ float e4m3_round(float x) {
+    const int b = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(x, -448.0f, 448.0f), 0.0f, 0, false);
+    return __builtin_amdgcn_cvt_f32_fp8(b, 0);
+}
+// Nearest e2m1 value of x and y (nearest-even, saturating at 6; the hardware
+// conversion with a unit scale), back in fp32.
+__device__ __forceinline__ v2f e2m1_round2(float x, float y) {
+    const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x, y, 1.0f, 0);
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+}
+// Power-of-two NVFP4 tensor scale: the smallest 2^k with 2688 2^k >= amax
+// (2688 = 448 * 6, the largest block scale times the largest e2m1 value);
+// 1 for amax == 0.  With amax = f 2^e, f in [0.5, 1): 2^(e - 12) when
+// f <= 2688 / 4096, else 2^(e - 11).
+__device__ __forceinline__ float nv_tensor_scale(float amax) {
+    if (!(amax > 0.0f)) return 1.0f;
+    int e;
+    const float f = __builtin_frexpf(amax, &e);
+    return __builtin_ldexpf(1.0f, e - 12 + (f > 0.65625f ? 1 : 0));
+}
+
 }  // namespace bqa

@@ -26,6 +26,9 @@ hipError_t launch_quant_mx(const Dense& x, bool f16, int B, int H, int N, int d,
 hipError_t launch_quant_i8_qknorm(const Dense& x, bool f16, int B, int H, int N, int d, int blk, bool smooth,
                                   double eps, float* mu, float* inv_norm, void* ws, int8_t* codes, float* scales,
                                   hipStream_t st);
+size_t ws_nvfp4_bytes(int BH, int N, int d);
+hipError_t launch_nvfp4(const Dense& x, bool f16, int B, int H, int N, int d, int axis, const Dense& out, void* ws,
+                        hipStream_t st);
 hipError_t launch_quant_mx_smooth(const Dense& x, bool f16, int B, int H, int N, int d, bool key, double eps,
                                   uint8_t* codes, uint8_t* scales, float* means, void* ws, hipStream_t st);
 
@@ -122,10 +125,13 @@ struct ThriftFwdArgs {
     int B, Hq, Hkv, Nq, Nk, causal;
     float c_log2;                                        // tau * log2(e)
     const float* sbias;                                  // post-training baseline: [B,Hq,nqb,Nk] score shifts
+    Dense q_nv, k_nv, v_nv;                              // NVFP4 emulation: dequantised NVFP4 Q, K, V (bf16)
 };
 hipError_t launch_thrift_fwd(const ThriftFwdArgs& a, hipStream_t st);
 // post-training FP4 baseline: score shifts from qbar [B,Hq,nqb,d] into ws, then the FP4 path
 size_t ws_ptq_fwd_bytes(int B, int Hq, int Nq, int Nk);
+// Thrift prefill with the FP4 path in NVFP4 emulation (bf16 instructions on q_nv, k_nv, v_nv)
+hipError_t launch_thrift_nv(const ThriftFwdArgs& a, hipStream_t st);
 hipError_t launch_ptq_fwd(ThriftFwdArgs a, const float* qbar, void* ws, hipStream_t st);
 
 // ---- ThriftAttention decode (attn_thrift.hip): one query per (batch, query head)

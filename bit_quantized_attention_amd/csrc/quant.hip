@@ -764,6 +764,91 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(Dense x, int H, int N, int
     }
 }
 
+// ------------------------------------------------------------ NVFP4 emulation
+// ("ThriftAttention", Method step 2: the FP4 path in NVFP4 micro-scaling.)
+// The slice's tensor scale g (nv_tensor_scale of its absmax, reduced here
+// from the per-channel chunk maxima `part`), then blocks of 16 values with
+// the scale s_b = e4m3(fp32(amax_b / fp32(6 g))) and values
+// e2m1(fp32(x / (s_b g))) s_b g, written back as bf16 (exact).  A block
+// whose scale underflows is zero.
+__device__ __forceinline__ float nv_slice_scale(const float* part, int nch, int d, int bh) {
+    __shared__ float red[256];
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < nch * d; i += 256) m = __builtin_fmaxf(m, part[(int64_t)bh * nch * d + i]);
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] = __builtin_fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
+        __syncthreads();
+    }
+    return nv_tensor_scale(red[0]);
+}
+__device__ __forceinline__ void nv_block16(float* v, float g) {
+    float am = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) am = __builtin_fmaxf(am, __builtin_fabsf(v[k]));
+    const float S = e4m3_round(am / (6.0f * g)) * g;
+#pragma unroll
+    for (int k = 0; k < 16; k += 2) {
+        if (S != 0.0f) {
+            const v2f q = e2m1_round2(v[k] / S, v[k + 1] / S);
+            v[k] = q[0] * S;
+            v[k + 1] = q[1] * S;
+        } else {
+            v[k] = v[k + 1] = 0.0f;
+        }
+    }
+}
+// axis 0 (Q, K): grid BH * ceil(N / 16); thread = (token, 16-channel block)
+template <bool IS_F16>
+__global__ __launch_bounds__(256) void nv_rows_kernel(Dense x, int H, int N, int d, const float* __restrict__ part,
+                                                      int nch, Dense out) {
+    const int nt = (N + 15) / 16;
+    const int bh = blockIdx.x / nt, tb = blockIdx.x % nt;
+    const int b = bh / H, h = bh % H;
+    const float g = nv_slice_scale(part, nch, d, bh);
+    const int nblk = d / 16, t = tb * 16 + (int)threadIdx.x / nblk, blk = (int)threadIdx.x % nblk;
+    if ((int)threadIdx.x >= 16 * nblk || t >= N) return;
+    const uint16_t* row = (const uint16_t*)x.p + b * x.sB + h * x.sH + (int64_t)t * x.sN + 16 * blk;
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const uint4 raw = *(const uint4*)(row + 8 * q);
+        const uint16_t* e = (const uint16_t*)&raw;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[8 * q + j] = load_half<IS_F16>(e + j);
+    }
+    nv_block16(v, g);
+    uint16_t* orow = (uint16_t*)out.p + b * out.sB + h * out.sH + (int64_t)t * out.sN + 16 * blk;
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = (uint32_t)f32_to_bf16_bits(v[2 * k]) | ((uint32_t)f32_to_bf16_bits(v[2 * k + 1]) << 16);
+    *(uint4*)orow = make_uint4(w[0], w[1], w[2], w[3]);
+    *(uint4*)(orow + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+}
+// axis 1 (V): grid BH * (N / 32); thread = (channel, 16-token block), lanes
+// on consecutive channels (each token row is read coalesced)
+template <bool IS_F16>
+__global__ __launch_bounds__(256) void nv_cols_kernel(Dense x, int H, int N, int d, const float* __restrict__ part,
+                                                      int nch, Dense out) {
+    const int nt = N / 32;
+    const int bh = blockIdx.x / nt, tb = blockIdx.x % nt;
+    const int b = bh / H, h = bh % H;
+    const float g = nv_slice_scale(part, nch, d, bh);
+    const int c = (int)threadIdx.x % d, grp = (int)threadIdx.x / d;
+    if (grp >= 256 / d || 32 * tb + 16 * grp >= N) return;
+    for (int t0 = 32 * tb + 16 * grp; t0 < 32 * tb + 32; t0 += 16 * (256 / d)) {
+        const uint16_t* col = (const uint16_t*)x.p + b * x.sB + h * x.sH + (int64_t)t0 * x.sN + c;
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = load_half<IS_F16>(col + (int64_t)k * x.sN);
+        nv_block16(v, g);
+        uint16_t* ocol = (uint16_t*)out.p + b * out.sB + h * out.sH + (int64_t)t0 * out.sN + c;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) ocol[(int64_t)k * out.sN] = f32_to_bf16_bits(v[k]);
+    }
+}
+
 // ------------------------------------------------------------ launchers
 static int chunks_for(int BH, int N) {
     // about one block per CU, at least 512 rows per chunk (measured: fewer,
@@ -990,6 +1075,28 @@ hipError_t launch_quant_mx(const Dense& x, bool f16, int B, int H, int N, int d,
     } else {
         if (f16) mx_cols_kernel<true><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales);
         else mx_cols_kernel<false><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales);
+    }
+    return hipGetLastError();
+}
+
+size_t ws_nvfp4_bytes(int BH, int N, int d) { return ws_chan_bytes(BH, N, d); }
+
+// NVFP4 emulation: per-channel chunk maxima of the slice into the workspace,
+// then the blocks of 16 along d (axis 0) or along the tokens (axis 1).
+hipError_t launch_nvfp4(const Dense& x, bool f16, int B, int H, int N, int d, int axis, const Dense& out, void* ws,
+                        hipStream_t st) {
+    const int BH = B * H, nch = chunks_for(BH, N), rpc = (N + nch - 1) / nch;
+    float* part = (float*)ws;
+    if (f16) col_partial_kernel<true, false><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
+    else col_partial_kernel<false, false><<<dim3(BH, nch), 256, 0, st>>>(x, H, N, d, rpc, part);
+    if (axis == 0) {
+        const int grid = BH * ((N + 15) / 16);
+        if (f16) nv_rows_kernel<true><<<grid, 256, 0, st>>>(x, H, N, d, part, nch, out);
+        else nv_rows_kernel<false><<<grid, 256, 0, st>>>(x, H, N, d, part, nch, out);
+    } else {
+        const int grid = BH * (N / 32);
+        if (f16) nv_cols_kernel<true><<<grid, 256, 0, st>>>(x, H, N, d, part, nch, out);
+        else nv_cols_kernel<false><<<grid, 256, 0, st>>>(x, H, N, d, part, nch, out);
     }
     return hipGetLastError();
 }

@@ -10,9 +10,9 @@ from __future__ import annotations
 import torch
 
 from . import (BQA_FP8E4M3, BQA_INT8, BQA_MXFP4, BQA_OP_FWD, BQA_OP_QUANTIZE_K, BQA_OP_QUANTIZE_KV,
-               BQA_OP_QUANTIZE_V, BQA_OP_BWD, BQA_PTQ_MXFP4, BQA_QAT_MXFP4, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V,
+               BQA_OP_QUANTIZE_NVFP4, BQA_OP_QUANTIZE_V, BQA_OP_BWD, BQA_PTQ_MXFP4, BQA_QAT_MXFP4, BQA_ROLE_K, BQA_ROLE_Q, BQA_ROLE_V,
                BQA_SAGE_I8_F16PV, BQA_SAGE_I8_F8PV, BQA_SAGE_I8_I8PV, BQA_THRIFT, bqa_attn_bwd, bqa_attn_fwd,
-               bqa_attn_bwd_qknorm, bqa_attn_fwd_ptq, bqa_quantize_blocks, bqa_quantize_kv, bqa_quantize_qknorm,
+               bqa_attn_bwd_qknorm, bqa_attn_fwd_ptq, bqa_attn_fwd_thrift_nvfp4, bqa_quantize_blocks, bqa_quantize_nvfp4, bqa_quantize_kv, bqa_quantize_qknorm,
                bqa_select_blocks, bqa_workspace_size, dense, max_sel, problem, qtensor)
 
 
@@ -324,6 +324,29 @@ class ThriftPath:
         self.select()
         self.forward()
         return self.o
+
+
+class ThriftNvPath(ThriftPath):
+    """ThriftAttention prefill with its FP4 path in NVFP4 emulation: the block
+    means and selection as in ThriftPath; Q, K, V fake-quantised to NVFP4
+    (dequantised bf16 values); the unselected pairs in bf16 instructions on
+    those with two-level NVFP4 P, the selected pairs on the bf16 inputs."""
+
+    def __init__(self, p, q, k, v):
+        super().__init__(p, q, k, v)
+        self.qn, self.kn, self.vn = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        self.ws_nv = torch.empty(max(bqa_workspace_size(p, BQA_OP_QUANTIZE_NVFP4), 16), dtype=torch.uint8,
+                                 device=q.device)
+
+    def quantize(self):
+        super().quantize()
+        for role, x, y in ((BQA_ROLE_Q, self._qd, self.qn), (BQA_ROLE_K, self._kd, self.kn),
+                           (BQA_ROLE_V, self._vd, self.vn)):
+            bqa_quantize_nvfp4(self.p, role, x, y, workspace=self.ws_nv)
+
+    def forward(self):
+        bqa_attn_fwd_thrift_nvfp4(self.p, q_nv=self.qn, k_nv=self.kn, v_nv=self.vn, q_hi=self._qd, k_hi=self._kd,
+                                  v_hi=self._vd, sel_idx=self.sel_idx, sel_cnt=self.sel_cnt, o=self._od, lse=self.lse)
 
 
 class ThriftDecodePath:

@@ -134,7 +134,7 @@ typedef struct bqa_qtensor {
 /* Operations, for bqa_workspace_size(). */
 enum {
     BQA_OP_QUANTIZE_Q = 0, BQA_OP_QUANTIZE_K = 1, BQA_OP_QUANTIZE_V = 2, BQA_OP_QUANTIZE_DO = 3,
-    BQA_OP_SELECT = 4, BQA_OP_FWD = 5, BQA_OP_BWD = 6, BQA_OP_QUANTIZE_KV = 7
+    BQA_OP_SELECT = 4, BQA_OP_FWD = 5, BQA_OP_BWD = 6, BQA_OP_QUANTIZE_KV = 7, BQA_OP_QUANTIZE_NVFP4 = 8
 };
 
 /* ABI version of the loaded library (BQA_ABI_VERSION it was built with). */
@@ -224,6 +224,37 @@ bqa_status bqa_quantize_kv(const bqa_problem* p, const bqa_tensor* k, const bqa_
 bqa_status bqa_quantize_qknorm(const bqa_problem* p, int32_t role, const bqa_tensor* x, bqa_qtensor* out,
                                float* inv_norm, float* k_mean, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * NVFP4 format emulation ("ThriftAttention", Method step 2: the FP4 path of
+ * the pages uses NVFP4 micro-scaling, e2m1 values in blocks of 16 with an
+ * E4M3 scale; gfx950's scaled matrix instructions take only power-of-two
+ * scales, so NVFP4 is emulated).  x (Q: [B, Hq, Nq, d]; K, V: [B, Hkv, Nk,
+ * d], bf16 or fp16, d = 128) is quantised to NVFP4 and the dequantised
+ * values, exact in bf16, are written to out (bf16, same shape): per (b, h)
+ * slice a tensor scale g, the power of two at or above amax / (448 * 6);
+ * blocks of 16 along d (Q, K) or along the tokens of each channel (V, Nk a
+ * multiple of 32) with the scale s_b = e4m3(fp32(amax_b / (6 g))) and
+ * values e2m1(fp32(x / (s_b g))) s_b g (nearest-even, saturating).
+ * Workspace: bqa_workspace_size(p, BQA_OP_QUANTIZE_NVFP4) bytes.
+ */
+bqa_status bqa_quantize_nvfp4(const bqa_problem* p, int32_t role, const bqa_tensor* x, bqa_tensor* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ThriftAttention prefill (as bqa_attn_fwd in BQA_THRIFT mode, Nq > 1) with
+ * its FP4 path in NVFP4 emulation: the unselected valid blocks run the bf16
+ * matrix instructions on q_nv, k_nv, v_nv (from bqa_quantize_nvfp4) with P
+ * quantised in two levels to NVFP4 (the row's largest P of the 64-key tile
+ * scaled to 448 * 6, E4M3 scales per 16 keys, e2m1 values, the first level
+ * undone into the bf16 operand); the selected blocks then run through the
+ * bf16 path on q_hi, k_hi, v_hi; all in tiles of 64 keys merged by one
+ * online softmax.  For measuring the pages' numerics, not their speed.
+ */
+bqa_status bqa_attn_fwd_thrift_nvfp4(const bqa_problem* p, const bqa_tensor* q_nv, const bqa_tensor* k_nv,
+                                     const bqa_tensor* v_nv, const bqa_tensor* q_hi, const bqa_tensor* k_hi,
+                                     const bqa_tensor* v_hi, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                     bqa_tensor* o, float* lse, void* stream);
 
 /*
  * ThriftAttention block selection ("ThriftAttention", Method step 1): for

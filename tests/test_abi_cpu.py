@@ -23,7 +23,7 @@ def L():
 def _declared():
     txt = open(os.path.join(ROOT, "include", "bqa.h")).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(bqa_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(bqa_[a-z_0-9]+)\s*\(", txt)))
 
 
 def test_exports_every_declared_symbol(L):
@@ -338,3 +338,27 @@ def test_qknorm_validation(L):
     assert bwd(_p(**sage), rk=None) == bqa.BQA_E_NULL
     assert bwd(_p(**sage), rq=0x71001) == bqa.BQA_E_ALIGN
     assert _nodev(bwd(_p(**sage)))
+
+
+def test_nvfp4_validation(L):
+    x = _dense()
+    th = dict(mode=bqa.BQA_THRIFT, B=1, Hq=4, Hkv=2, Nq=1024, Nk=1024, hp_budget_ppm=50_000, sel_block=128)
+
+    def quant(p, role, out=x, ws=0x40000, wsb=1 << 30):
+        return bqa.lib().bqa_quantize_nvfp4(C.byref(p), role, C.byref(x), None if out is None else C.byref(out),
+                                            ws, wsb, None)
+    assert quant(_p(**dict(th, d=64)), bqa.BQA_ROLE_Q) == bqa.BQA_E_UNSUPPORTED
+    assert quant(_p(**th), bqa.BQA_ROLE_DO) == bqa.BQA_E_UNSUPPORTED
+    assert quant(_p(**th), bqa.BQA_ROLE_Q, out=None) == bqa.BQA_E_NULL
+    assert quant(_p(**dict(th, Nk=1008, causal=0)), bqa.BQA_ROLE_V) == bqa.BQA_E_UNSUPPORTED
+    need = bqa.bqa_workspace_size(_p(**th), bqa.BQA_OP_QUANTIZE_NVFP4)
+    assert need > 0 and quant(_p(**th), bqa.BQA_ROLE_K, wsb=need - 1) == bqa.BQA_E_WORKSPACE
+    assert _nodev(quant(_p(**th), bqa.BQA_ROLE_V, wsb=need))
+
+    def fwd(p, idx=0x30000):
+        return bqa.lib().bqa_attn_fwd_thrift_nvfp4(C.byref(p), *[C.byref(x)] * 6, idx, 0x31000, C.byref(x), None,
+                                                   None)
+    assert fwd(_p(**dict(th, Nq=1, Nk=1024))) == bqa.BQA_E_UNSUPPORTED
+    assert fwd(_p(**dict(th, mode=bqa.BQA_QAT_MXFP4))) == bqa.BQA_E_UNSUPPORTED
+    assert fwd(_p(**th), idx=None) == bqa.BQA_E_NULL
+    assert _nodev(fwd(_p(**th)))

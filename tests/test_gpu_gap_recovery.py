@@ -40,7 +40,7 @@ def _rel_err(got, ref):
 
 @pytest.mark.slow
 def test_gap_recovery_c5_recipe():
-    from bit_quantized_attention_amd.runner import ThriftPath, thrift_problem, to_device
+    from bit_quantized_attention_amd.runner import ThriftNvPath, ThriftPath, thrift_problem, to_device
     w = wl.with_len(wl.WORKLOADS["c5"], 131072, hq=8, hkv=2)
     nw = wl.default_workers()
     Q, K, V = (wl.build(w, t, workers=nw) for t in ("q", "k", "v"))
@@ -54,9 +54,9 @@ def test_gap_recovery_c5_recipe():
         O, _ = orc.ref_fwd(Q[0, h, r0:r0 + 32], K[0, hk, :r0 + 32], V[0, hk, :r0 + 32], True, tau)
         exact[(h, r0)] = O
 
-    def run(ppm, force_fp4=False):
+    def run(ppm, force_fp4=False, nv=False):
         p = thrift_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, budget_ppm=ppm)
-        path = ThriftPath(p, qd, kd, vd)
+        path = (ThriftNvPath if nv else ThriftPath)(p, qd, kd, vd)
         path.quantize()
         path.select()
         if force_fp4:
@@ -69,17 +69,19 @@ def test_gap_recovery_c5_recipe():
         ref = np.concatenate([exact[s] for s in samples])
         return _rel_err(got, ref)
 
-    e_fp4 = run(0, force_fp4=True)
     e_bf16 = run(1_000_000)
-    e = {ppm: run(ppm) for ppm in BUDGETS}
-    rec = {ppm: (e_fp4 - e[ppm]) / (e_fp4 - e_bf16) for ppm in BUDGETS}
+    out = {}
+    for fmt, nv in (("mxfp4", False), ("nvfp4_emulated", True)):
+        e_fp4 = run(0, force_fp4=True, nv=nv)
+        e = {ppm: run(ppm, nv=nv) for ppm in BUDGETS}
+        rec = {ppm: (e_fp4 - e[ppm]) / (e_fp4 - e_bf16) for ppm in BUDGETS}
+        out[fmt] = {"rel_l2_error": {"fp4_only": e_fp4, "bf16_only": e_bf16,
+                                     **{f"budget_{ppm / 1e4:g}%": e[ppm] for ppm in BUDGETS}},
+                    "recovery": {f"budget_{ppm / 1e4:g}%": rec[ppm] for ppm in BUDGETS}}
+        assert e_bf16 < e_fp4
+        assert rec[BUDGETS[0]] > 0.0
+        for a, b in zip(BUDGETS, BUDGETS[1:]):
+            assert e[b] <= e[a] * 1.02, (fmt, a, b, e)
+        assert e[BUDGETS[-1]] < e_fp4 and e[BUDGETS[-1]] > e_bf16 * 0.98
     print(json.dumps({"gap_recovery": {"workload": "c5 recipe, Hq=8 Hkv=2 N=131072 causal, 192 sampled rows",
-                                       "rel_l2_error": {"fp4_only": e_fp4, "bf16_only": e_bf16,
-                                                        **{f"budget_{ppm / 1e4:g}%": e[ppm] for ppm in BUDGETS}},
-                                       "recovery": {f"budget_{ppm / 1e4:g}%": rec[ppm] for ppm in BUDGETS}}}),
-          flush=True)
-    assert e_bf16 < e_fp4
-    assert rec[BUDGETS[0]] > 0.0
-    for a, b in zip(BUDGETS, BUDGETS[1:]):
-        assert e[b] <= e[a] * 1.02, (a, b, e)
-    assert e[BUDGETS[-1]] < e_fp4 and e[BUDGETS[-1]] > e_bf16 * 0.98
+                                       **out}}), flush=True)
