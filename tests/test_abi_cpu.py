@@ -352,7 +352,7 @@ def test_nvfp4_validation(L):
     assert quant(_p(**th), bqa.BQA_ROLE_Q, out=None) == bqa.BQA_E_NULL
     assert quant(_p(**dict(th, Nk=1008, causal=0)), bqa.BQA_ROLE_V) == bqa.BQA_E_UNSUPPORTED
     need = bqa.bqa_workspace_size(_p(**th), bqa.BQA_OP_QUANTIZE_NVFP4)
-    assert need > 0 and quant(_p(**th), bqa.BQA_ROLE_K, wsb=need - 1) == bqa.BQA_E_WORKSPACE
+    assert need > 0 and quant(_p(**th), bqa.BQA_ROLE_Q, wsb=need - 1) == bqa.BQA_E_WORKSPACE
     assert _nodev(quant(_p(**th), bqa.BQA_ROLE_V, wsb=need))
 
     def fwd(p, idx=0x30000):
