@@ -204,3 +204,26 @@ def test_qat_score_jump_rescales():
     compare_outputs(path.o[0, 0].float().cpu().numpy(), ref, "bf16", what="O (score jump)")
     compare_outputs(path.oa[0, 0].float().cpu().numpy(), ref_aux, "bf16", what="O' (score jump)")
     assert np.abs(path.lse[0, 0].cpu().numpy() - lse).max() < 2e-3
+
+
+@pytest.mark.parametrize("k", [-17, 20])
+def test_qat_backward_tiny_and_huge_do(k):
+    """dO scaled by 2^k: values around 1e-7 (below fp16's normal range) and
+    around 1e5 (above fp16's largest value).  The gradients are linear in dO,
+    so 2^-k times the GPU's gradients must match the oracle's gradients for
+    the unscaled dO: the fp16 dV product must lose nothing to the scale."""
+    from bit_quantized_attention_amd.runner import QatTrainStep, qat_problem, to_device
+    w = wl.with_len(wl.WORKLOADS["c4"], 256, hq=2, hkv=2)
+    Q, K, V, dO = (wl.build(w, t) for t in ("q", "k", "v", "do"))
+    dOs = (dO * np.float32(2.0 ** k)).astype(np.float32)
+    assert (np.abs(dOs).max() > 65504.0) if k > 0 else (np.abs(dOs).max() < 6.1e-5)
+    p = qat_problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+    step = QatTrainStep(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"), to_device(dOs, "bf16"))
+    step.step()
+    torch.cuda.synchronize()
+    oc = _Oracle(Q, K, V)
+    g = [t.float().cpu().numpy() * 2.0 ** -k for t in (step.dq, step.dk, step.dv)]
+    for h in range(2):
+        ref = _qat_grads(oc, dO, h)
+        for name, gi, ri in zip(("dQ", "dK", "dV"), g, ref):
+            compare_outputs(gi[0, h], ri, "bf16", what=f"{name}[h={h}] (dO x 2^{k})")
