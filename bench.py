@@ -81,6 +81,24 @@ def _traffic_for(kernel: str):
     return e["bytes_per_launch"]
 
 
+PROBES_FILE = os.path.join(ROOT, "profiles", "probes.json")
+
+
+def _measured_peak(kinds):
+    """The rate probes' measured figure for a roofline peak (committed from a
+    `bench.py --probe` run): the matrix rates per operand type, weighted the
+    way the spec peak is, or the HBM read rate."""
+    try:
+        with open(PROBES_FILE) as f:
+            pr = json.load(f)["probes"]
+    except (OSError, ValueError, KeyError):
+        return None
+    try:
+        return {k: pr[k]["measured"] for k in kinds}
+    except KeyError:
+        return None
+
+
 def cpu_baseline(w, budget_s: float = 20.0):
     """The oracle (as it stands) on a bounded sample: full quantisation and
     forward of whole (b, h) heads, as many as fit the time budget."""
@@ -715,6 +733,11 @@ def main():
         rl["unit"] = "TFLOP/s"
     rl.update({"achieved": round(achieved, 1), "frac": round(achieved / rl["peak"], 4),
                "traffic": _traffic_for(case["traffic_key"]), "kernel_ms": round(kern_ms, 5)})
+    # the probes' sustained rates of the same units, beside the published peak
+    probes = {"hbm": ["hbm_read_wide"], "mfma": ["mfma_i8", "mfma_fp8", "mfma_mxfp4", "mfma_bf16"]}[rl["bound"]]
+    mp = _measured_peak(probes)
+    if mp is not None:
+        rl["probe_rates"] = mp
     line = {
         "metric": METRIC,
         "value": round(value, 2),

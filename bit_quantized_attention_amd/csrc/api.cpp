@@ -106,7 +106,7 @@ bqa_status check_decode(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
     if (p->num_splits < 0) return BQA_E_SHAPE;
     TRY(check_q(q, BQA_MXFP4, 0));
     TRY(check_q(k, BQA_MXFP4, 0));
-    TRY(check_q(v, BQA_MXFP4, 1));
+    TRY(check_q(v, BQA_MXFP4, v && v->axis == 2 ? 2 : 1));
     if (q->block != 32 || k->block != 32 || v->block != 32) return BQA_E_UNSUPPORTED;
     TRY(check_dense(q_hi, false, true));
     TRY(check_dense(k_hi, false, true));
@@ -114,6 +114,7 @@ bqa_status check_decode(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
     TRY(check_dense(o, false, true));
     if (!sel_idx || !sel_cnt) return BQA_E_NULL;
     if (p->hp_budget_ppm < 0 || p->hp_budget_ppm > 1000000) return BQA_E_SHAPE;
+    a.v_tiled = v->axis == 2;
     a.qc = (const uint8_t*)q->codes; a.qs = (const uint8_t*)q->scales;
     a.kc = (const uint8_t*)k->codes; a.ks = (const uint8_t*)k->scales;
     a.vc = (const uint8_t*)v->codes; a.vs = (const uint8_t*)v->scales;
@@ -236,10 +237,11 @@ bqa_status bqa_quantize_blocks(const bqa_problem* p, int32_t role, const bqa_ten
     if (out->fmt != BQA_MXFP4 && out->fmt != BQA_INT8 && out->fmt != BQA_FP8E4M3) return BQA_E_UNSUPPORTED;
     if (out->fmt == BQA_MXFP4) {
         if (role == BQA_ROLE_DO) return BQA_E_UNSUPPORTED;
-        const int axis = role == BQA_ROLE_V ? 1 : 0;
+        // V: along tokens (axis 1) or blocked by 128 tokens (axis 2)
+        const int axis = role == BQA_ROLE_V ? (out->axis == 2 ? 2 : 1) : 0;
         TRY(check_q(out, BQA_MXFP4, axis));
         if (out->block != 32) return BQA_E_UNSUPPORTED;
-        if (axis == 1 && N % 128 != 0) return BQA_E_UNSUPPORTED;
+        if (axis >= 1 && N % 128 != 0) return BQA_E_UNSUPPORTED;
         if (p->mode == BQA_PTQ_MXFP4 && role != BQA_ROLE_V) {
             // the post-training baseline: Q less its bf16 block means (written to
             // block_means, required), K less its token mean when p->smooth_k

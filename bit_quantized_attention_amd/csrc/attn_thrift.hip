@@ -709,22 +709,33 @@ struct LdsDec {
     };
 };
 
+// FP4 key block J: K codes and scales (token-major, contiguous) and V codes
+// and scales, either channel-major over the whole cache (a channel's 64
+// bytes of the block are half of a 128-byte line, its 4 scale bytes a
+// sliver of another) or blocked by 128 keys (the block's 8 KB of codes and
+// 512 bytes of scales contiguous, each line read whole once).
 __device__ __forceinline__ void dec_issue_f4(const ThriftDecArgs& a, int bhk, int J, LdsF4& L, int l) {
     const int t0 = J * KB;
     const uint8_t* kbase = a.kc + ((int64_t)bhk * a.Nk + t0) * (D / 2);
-    const uint8_t* vbase = a.vc + (int64_t)bhk * D * (a.Nk / 2) + t0 / 2;
+    const int nb = a.Nk / KB;
+    const uint8_t* vbase = a.v_tiled ? a.vc + ((int64_t)bhk * nb + J) * D * (KB / 2)
+                                     : a.vc + (int64_t)bhk * D * (a.Nk / 2) + t0 / 2;
+    const uint32_t vrow = a.v_tiled ? (uint32_t)(KB / 2) : (uint32_t)(a.Nk / 2);
 #pragma unroll
     for (int sgm = 0; sgm < 8; ++sgm) {
         const int r = 16 * sgm + (l >> 2);
         lds_copy16((uint32_t)(r * (D / 2) + 16 * ((l & 3) ^ fk64(r))), kbase, lds_addr(L.kc + 1024 * sgm));
-        lds_copy16((uint32_t)r * (uint32_t)(a.Nk / 2) + (uint32_t)(16 * ((l & 3) ^ fv64(r))), vbase,
-                   lds_addr(L.vc + 1024 * sgm));
+        lds_copy16((uint32_t)r * vrow + (uint32_t)(16 * ((l & 3) ^ fv64(r))), vbase, lds_addr(L.vc + 1024 * sgm));
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         lds_copy4((uint32_t)(4 * l), a.ks + ((int64_t)bhk * a.Nk + t0 + 64 * u) * (D / 32), lds_addr(L.ks + 256 * u));
-        lds_copy4((uint32_t)l * (uint32_t)(a.Nk / 32), a.vs + ((int64_t)bhk * D + 64 * u) * (a.Nk / 32) + t0 / 32,
-                  lds_addr(L.vs + 256 * u));
+        if (a.v_tiled)
+            lds_copy4((uint32_t)(4 * l), a.vs + (((int64_t)bhk * nb + J) * D + 64 * u) * (KB / 32),
+                      lds_addr(L.vs + 256 * u));
+        else
+            lds_copy4((uint32_t)l * (uint32_t)(a.Nk / 32), a.vs + ((int64_t)bhk * D + 64 * u) * (a.Nk / 32) + t0 / 32,
+                      lds_addr(L.vs + 256 * u));
     }
 }
 

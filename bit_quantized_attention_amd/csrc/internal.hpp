@@ -138,7 +138,8 @@ hipError_t launch_ptq_fwd(ThriftFwdArgs a, const float* qbar, void* ws, hipStrea
 struct ThriftDecArgs {
     const uint8_t* qc; const uint8_t* qs;                // MXFP4 q [B,Hq,1,d/2], E8M0 [B,Hq,1,d/32]
     const uint8_t* kc; const uint8_t* ks;                // MXFP4 K cache [B,Hkv,Nk,d/2], E8M0
-    const uint8_t* vc; const uint8_t* vs;                // MXFP4 V cache [B,Hkv,d,Nk/2], E8M0
+    const uint8_t* vc; const uint8_t* vs;                // MXFP4 V cache [B,Hkv,d,Nk/2], E8M0 [B,Hkv,d,Nk/32],
+    int v_tiled;                                         // or blocked by 128 keys: [B,Hkv,Nk/128,d,64], [..,d,4]
     Dense q_hi, k_hi, v_hi;                              // bf16 q [B,Hq,1,d]; caches [B,Hkv,Nk,d]
     const int32_t* sel_idx; const int32_t* sel_cnt;      // [B,Hq,1,max_sel], [B,Hq,1]
     int max_sel;

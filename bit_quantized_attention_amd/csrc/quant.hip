@@ -732,9 +732,12 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(Dense x, int H, int N, int
 
 // Columns (V): grid BH * (N / 128); the 128 x d tile is staged in LDS, then a
 // thread encodes (channel, 32-token group) items into channel-major codes.
+// With `tiled` the layout is blocked by 128 tokens (axis 2): codes
+// [BH][N/128][d][64 B], scales [BH][N/128][d][4], so one key block's V is
+// one contiguous 8.5 KB stretch.
 template <bool IS_F16>
 __global__ __launch_bounds__(256) void mx_cols_kernel(Dense x, int H, int N, int d, uint8_t* __restrict__ codes_t,
-                                                       uint8_t* __restrict__ scales_t) {
+                                                       uint8_t* __restrict__ scales_t, int tiled) {
     const int nt = N / 128;
     const int bh = blockIdx.x / nt, tb = blockIdx.x % nt;
     const int b = bh / H, h = bh % H;
@@ -759,8 +762,10 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(Dense x, int H, int N, int
         uint32_t packed[4];
         uint32_t s = mx_encode32(v, packed);
         const int64_t tok = (int64_t)tb * 128 + grp * 32;
-        *(uint4*)(codes_t + ((int64_t)bh * d + c) * (N / 2) + tok / 2) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        scales_t[((int64_t)bh * d + c) * (N / 32) + tok / 32] = (uint8_t)s;
+        const int64_t ci = tiled ? (((int64_t)bh * nt + tb) * d + c) * 64 + grp * 16 : ((int64_t)bh * d + c) * (N / 2) + tok / 2;
+        const int64_t si = tiled ? (((int64_t)bh * nt + tb) * d + c) * 4 + grp : ((int64_t)bh * d + c) * (N / 32) + tok / 32;
+        *(uint4*)(codes_t + ci) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        scales_t[si] = (uint8_t)s;
     }
 }
 
@@ -1073,8 +1078,8 @@ hipError_t launch_quant_mx(const Dense& x, bool f16, int B, int H, int N, int d,
         if (f16) mx_rows_kernel<true, MX_PLAIN><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales, means, nullptr, 0, 0.0);
         else mx_rows_kernel<false, MX_PLAIN><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales, means, nullptr, 0, 0.0);
     } else {
-        if (f16) mx_cols_kernel<true><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales);
-        else mx_cols_kernel<false><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales);
+        if (f16) mx_cols_kernel<true><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales, axis == 2);
+        else mx_cols_kernel<false><<<grid, 256, 0, st>>>(x, H, N, d, codes, scales, axis == 2);
     }
     return hipGetLastError();
 }

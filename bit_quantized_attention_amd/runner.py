@@ -354,7 +354,7 @@ class ThriftDecodePath:
     key means, next to the bf16 cache) is built once by `build_cache`; a
     step quantises the new query, selects each head's blocks and attends."""
 
-    def __init__(self, p, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    def __init__(self, p, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, v_tiled: bool = True):
         dev = q.device
         self.p = p
         B, Hq, Hkv, Nk, d = p.B, p.Hq, p.Hkv, p.Nk, p.d
@@ -364,15 +364,20 @@ class ThriftDecodePath:
         self.qs = torch.empty((B, Hq, 1, d // 32), dtype=u8, device=dev)
         self.kc = torch.empty((B, Hkv, Nk, d // 2), dtype=u8, device=dev)
         self.ks = torch.empty((B, Hkv, Nk, d // 32), dtype=u8, device=dev)
-        self.vc = torch.empty((B, Hkv, d, Nk // 2), dtype=u8, device=dev)
-        self.vs = torch.empty((B, Hkv, d, Nk // 32), dtype=u8, device=dev)
+        # V codes of the cache blocked by 128 keys (one block's codes contiguous), or channel-major
+        if v_tiled:
+            self.vc = torch.empty((B, Hkv, Nk // 128, d, 64), dtype=u8, device=dev)
+            self.vs = torch.empty((B, Hkv, Nk // 128, d, 4), dtype=u8, device=dev)
+        else:
+            self.vc = torch.empty((B, Hkv, d, Nk // 2), dtype=u8, device=dev)
+            self.vs = torch.empty((B, Hkv, d, Nk // 32), dtype=u8, device=dev)
         self.qm = torch.empty((B, Hq, 1, d), dtype=torch.float32, device=dev)
         self.km = torch.empty((B, Hkv, Nk // 128, d), dtype=torch.float32, device=dev)
         self.sel_idx = torch.empty((B, Hq, 1, max_sel(p)), dtype=torch.int32, device=dev)
         self.sel_cnt = torch.empty((B, Hq, 1), dtype=torch.int32, device=dev)
         self.qq = qtensor(BQA_MXFP4, 0, 32, self.qc, self.qs)
         self.kq = qtensor(BQA_MXFP4, 0, 32, self.kc, self.ks)
-        self.vq = qtensor(BQA_MXFP4, 1, 32, self.vc, self.vs)
+        self.vq = qtensor(BQA_MXFP4, 2 if v_tiled else 1, 32, self.vc, self.vs)
         self.o = torch.empty((B, Hq, 1, d), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=dev)
         self.ws = torch.empty(max(bqa_workspace_size(p, BQA_OP_FWD), 16), dtype=u8, device=dev)

@@ -121,6 +121,8 @@ typedef struct bqa_tensor {
  *       scales fp32 [B, H, d]                                  (axis 1)
  *   MXFP4 along d (Q, K):      codes u8 [B, H, N, d / 2], scales u8 [B, H, N, d / 32]  (axis 0)
  *   MXFP4 along tokens (V):    codes u8 [B, H, d, N / 2], scales u8 [B, H, d, N / 32]  (axis 1)
+ *   MXFP4 along tokens, blocked by 128 tokens (V of a decode cache):
+ *       codes u8 [B, H, N / 128, d, 64], scales u8 [B, H, N / 128, d, 4]      (axis 2)
  * E8M0 scale bytes hold e + 127 for the power of two 2^e.
  */
 typedef struct bqa_qtensor {
@@ -162,8 +164,8 @@ size_t bqa_workspace_size(const bqa_problem* p, int32_t op);
  *    are those of fp32(K - mu).
  *  - V, INT8 or FP8E4M3 axis 1: one scale per (b, h, channel) over all tokens,
  *    amax/127 or amax/448; e4m3 codes round to nearest even and saturate.
- *  - Q, K, MXFP4 axis 0; V, MXFP4 axis 1: OCP MX blocks of 32 along d (Q, K)
- *    or along tokens (V) ("Attn-QAT", §1 Problem: FP4 has 15 values;
+ *  - Q, K, MXFP4 axis 0; V, MXFP4 axis 1 or 2: OCP MX blocks of 32 along d
+ *    (Q, K) or along tokens (V) ("Attn-QAT", §1 Problem: FP4 has 15 values;
  *    "ThriftAttention", Method step 2: micro-scaled FP4): X = 2^e with
  *    e = floor(log2 amax) - 2 clamped to [-127, 127], codes e2m1(x / X),
  *    nearest-even, saturating at 6.  With block_means != NULL and role Q or K
@@ -308,7 +310,9 @@ bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const f
  *    then MXFP4 per 32 keys), then the selected blocks (sel_idx, sel_cnt from
  *    bqa_select_blocks) through the bf16 path (q_hi, k_hi, v_hi), all merged
  *    by one online softmax.  Nq == 1 is decode: the key range is cut into
- *    p->num_splits parts whose partial results are merged at the end.
+ *    p->num_splits parts whose partial results are merged at the end; its v
+ *    may also be blocked by 128 tokens (axis 2), which lets each key
+ *    block's V be read as one contiguous stretch.
  * row_max is used by BQA_QAT_MXFP4 only (NULL elsewhere).
  */
 bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qtensor* k,

@@ -173,7 +173,7 @@ def test_thrift_prefill_small(ppm):
         assert np.abs(L[0, iq] - lse).max() < 2e-3
 
 
-def _decode_run(w, ppm, splits):
+def _decode_run(w, ppm, splits, v_tiled=False):
     import bit_quantized_attention_amd as bqa
     from bit_quantized_attention_amd.runner import to_device
     q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
@@ -184,10 +184,15 @@ def _decode_run(w, ppm, splits):
     qt, kt, vt = to_device(q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
     qc = torch.empty((B, Hq, 1, d // 2), dtype=u8, device=dev); qs = torch.empty((B, Hq, 1, d // 32), dtype=u8, device=dev)
     kc = torch.empty((B, Hkv, Nk, d // 2), dtype=u8, device=dev); ks = torch.empty((B, Hkv, Nk, d // 32), dtype=u8, device=dev)
-    vc = torch.empty((B, Hkv, d, Nk // 2), dtype=u8, device=dev); vs = torch.empty((B, Hkv, d, Nk // 32), dtype=u8, device=dev)
+    if v_tiled:      # the decode cache's V blocked by 128 keys
+        vc = torch.empty((B, Hkv, Nk // 128, d, 64), dtype=u8, device=dev)
+        vs = torch.empty((B, Hkv, Nk // 128, d, 4), dtype=u8, device=dev)
+    else:
+        vc = torch.empty((B, Hkv, d, Nk // 2), dtype=u8, device=dev); vs = torch.empty((B, Hkv, d, Nk // 32), dtype=u8, device=dev)
     qm = torch.empty((B, Hq, 1, d), dtype=torch.float32, device=dev)
     km = torch.empty((B, Hkv, Nk // 128, d), dtype=torch.float32, device=dev)
-    qq, kq, vq = (bqa.qtensor(bqa.BQA_MXFP4, ax, 32, c, s) for ax, c, s in ((0, qc, qs), (0, kc, ks), (1, vc, vs)))
+    qq, kq, vq = (bqa.qtensor(bqa.BQA_MXFP4, ax, 32, c, s)
+                  for ax, c, s in ((0, qc, qs), (0, kc, ks), (2 if v_tiled else 1, vc, vs)))
     bqa.bqa_quantize_blocks(p, bqa.BQA_ROLE_Q, qt, qq, block_means=qm)
     bqa.bqa_quantize_blocks(p, bqa.BQA_ROLE_K, kt, kq, block_means=km)
     bqa.bqa_quantize_blocks(p, bqa.BQA_ROLE_V, vt, vq)
@@ -201,15 +206,23 @@ def _decode_run(w, ppm, splits):
     bqa.bqa_attn_fwd(p, q=qq, k=kq, v=vq, q_hi=qt, k_hi=kt, v_hi=vt, sel_idx=idx, sel_cnt=cnt, o=o, lse=lse,
                      workspace=ws)
     torch.cuda.synchronize()
+    if v_tiled:
+        # the blocked codes are the channel-major ones, key block by key block
+        rc, rs = orc.quant_mx_cols(V.reshape(-1, Nk, d))
+        g = vc.cpu().numpy().reshape(B * Hkv, Nk // 128, d, 64).transpose(0, 2, 1, 3).reshape(B * Hkv, d, Nk // 2)
+        gs = vs.cpu().numpy().reshape(B * Hkv, Nk // 128, d, 4).transpose(0, 2, 1, 3).reshape(B * Hkv, d, Nk // 32)
+        assert_same(g, rc, "blocked V codes")
+        assert_same(gs, rs, "blocked V scales")
     return p, (q, K, V), idx.cpu().numpy(), o.float().cpu().numpy(), lse.cpu().numpy()
 
 
-@pytest.mark.parametrize("ppm,splits", [(PPM_5, 1), (PPM_5, 3), (250_000, 0), (1_000_000, 2)])
-def test_thrift_decode_small(ppm, splits):
+@pytest.mark.parametrize("ppm,splits,v_tiled", [(PPM_5, 1, False), (PPM_5, 3, False), (250_000, 0, False),
+                                                (1_000_000, 2, False), (PPM_5, 3, True), (250_000, 0, True)])
+def test_thrift_decode_small(ppm, splits, v_tiled):
     """Decode recipe (batch 2, GQA 8/2) against a 4096-token cache: per split
     the FP4 blocks, then each head's selected blocks in bf16; partials merged."""
     w = wl.with_len(wl.WORKLOADS["c5d"], 4096, b=2, hq=8, hkv=2)
-    p, (q, K, V), idx, O, L = _decode_run(w, ppm, splits)
+    p, (q, K, V), idx, O, L = _decode_run(w, ppm, splits, v_tiled)
     import bit_quantized_attention_amd as bqa
     ms = bqa.max_sel(p)
     B, Hq, Hkv, d = w.B, w.Hq, w.Hkv, w.d
