@@ -115,6 +115,28 @@ def test_selection_decode():
     assert_same(idx, ridx, "selected blocks")
 
 
+@pytest.mark.parametrize("nkb,ppm", [(1500, PPM_5), (1500, 1_000_000), (3000, 250_000), (1024, 1_000_000),
+                                     (37, PPM_5), (1, PPM_5)])
+def test_selection_row_lengths(nkb, ppm):
+    """Rows of 1 to 3000 key blocks (the single-wavefront sort up to 1024,
+    the workgroup sort beyond, with its narrower LDS pieces past 2048), two
+    query blocks at the bottom-right end of the causal mask, exact ties."""
+    import bit_quantized_attention_amd as bqa
+    rng = np.random.default_rng(53 + nkb)
+    nqb = min(2, nkb)
+    qbar = _lowrank_means(rng, 1, 4, nqb, 128)
+    kbar = _lowrank_means(rng, 1, 2, nkb, 128)
+    if nkb > 8:
+        kbar[0, 0, 7] = kbar[0, 0, 3]
+        kbar[0, 1, nkb - 1] = kbar[0, 1, 0]
+    p = bqa.problem(B=1, Hq=4, Hkv=2, Nq=128 * nqb, Nk=128 * nkb, d=128, causal=1, mode=bqa.BQA_THRIFT,
+                    sel_block=128, hp_budget_ppm=ppm)
+    idx, cnt, ms = _select_gpu(p, qbar, kbar)
+    ridx, rcnt = _select_oracle(qbar, kbar, True, ppm, ms)
+    assert_same(cnt, rcnt, "selection counts")
+    assert_same(idx, ridx, "selected blocks")
+
+
 class _ThriftOracle:
     """The oracle's own quantisation, block means and selection of the
     generated inputs (nothing from the GPU)."""
