@@ -710,7 +710,8 @@ struct LdsDec {
 };
 
 // FP4 key block J: K codes and scales (token-major, contiguous) and V codes
-// and scales, either channel-major over the whole cache (a channel's 64
+// and scales (a decode step reads each byte of the cache once: the copies
+// are non-temporal), either channel-major over the whole cache (a channel's 64
 // bytes of the block are half of a 128-byte line, its 4 scale bytes a
 // sliver of another) or blocked by 128 keys (the block's 8 KB of codes and
 // 512 bytes of scales contiguous, each line read whole once).
@@ -724,17 +725,17 @@ __device__ __forceinline__ void dec_issue_f4(const ThriftDecArgs& a, int bhk, in
 #pragma unroll
     for (int sgm = 0; sgm < 8; ++sgm) {
         const int r = 16 * sgm + (l >> 2);
-        lds_copy16((uint32_t)(r * (D / 2) + 16 * ((l & 3) ^ fk64(r))), kbase, lds_addr(L.kc + 1024 * sgm));
-        lds_copy16((uint32_t)r * vrow + (uint32_t)(16 * ((l & 3) ^ fv64(r))), vbase, lds_addr(L.vc + 1024 * sgm));
+        lds_copy16_nt((uint32_t)(r * (D / 2) + 16 * ((l & 3) ^ fk64(r))), kbase, lds_addr(L.kc + 1024 * sgm));
+        lds_copy16_nt((uint32_t)r * vrow + (uint32_t)(16 * ((l & 3) ^ fv64(r))), vbase, lds_addr(L.vc + 1024 * sgm));
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        lds_copy4((uint32_t)(4 * l), a.ks + ((int64_t)bhk * a.Nk + t0 + 64 * u) * (D / 32), lds_addr(L.ks + 256 * u));
+        lds_copy4_nt((uint32_t)(4 * l), a.ks + ((int64_t)bhk * a.Nk + t0 + 64 * u) * (D / 32), lds_addr(L.ks + 256 * u));
         if (a.v_tiled)
-            lds_copy4((uint32_t)(4 * l), a.vs + (((int64_t)bhk * nb + J) * D + 64 * u) * (KB / 32),
+            lds_copy4_nt((uint32_t)(4 * l), a.vs + (((int64_t)bhk * nb + J) * D + 64 * u) * (KB / 32),
                       lds_addr(L.vs + 256 * u));
         else
-            lds_copy4((uint32_t)l * (uint32_t)(a.Nk / 32), a.vs + ((int64_t)bhk * D + 64 * u) * (a.Nk / 32) + t0 / 32,
+            lds_copy4_nt((uint32_t)l * (uint32_t)(a.Nk / 32), a.vs + ((int64_t)bhk * D + 64 * u) * (a.Nk / 32) + t0 / 32,
                       lds_addr(L.vs + 256 * u));
     }
 }
@@ -750,14 +751,14 @@ __device__ __forceinline__ void dec_issue_bf(const ThriftDecArgs& a, int b, int 
 #pragma unroll
     for (int sgm = 0; sgm < 8; ++sgm) {
         const int r = 4 * sgm + (l >> 4);
-        lds_copy16((uint32_t)(2 * (r * a.k_hi.sN + 8 * ((l & 15) ^ fk256(r)))), kb, lds_addr(L.b.k + 1024 * sgm));
+        lds_copy16_nt((uint32_t)(2 * (r * a.k_hi.sN + 8 * ((l & 15) ^ fk256(r)))), kb, lds_addr(L.b.k + 1024 * sgm));
     }
     const uint16_t* vb = (const uint16_t*)a.v_hi.p + b * a.v_hi.sB + hk * a.v_hi.sH;
     const int cg = l & 15, kq = l >> 4;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const int key = 16 * (u >> 2) + 4 * kq + (u & 3);
-        vq.v[u] = *(const v4i*)(vb + (int64_t)(k0 + key) * a.v_hi.sN + 8 * cg);
+        vq.v[u] = __builtin_nontemporal_load((const v4i*)(vb + (int64_t)(k0 + key) * a.v_hi.sN + 8 * cg));
     }
 }
 __device__ __forceinline__ void dec_store_bf(const VQuarter& vq, LdsDec& L, int l) {
