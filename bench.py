@@ -624,6 +624,37 @@ def probe_main(torch, bqa):
         v = nbytes / t / 1e9
         res[name] = {"measured": round(v, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(v / 8000.0, 4),
                      "time_ms": round(t * 1e3, 3), "grid": g, "note": "1 GiB read per launch"}
+    del src, dst
+    torch.cuda.empty_cache()
+    # 4 GiB, default and non-temporal policy (the decode kernel's copies are non-temporal)
+    big = 4 << 30
+    src = torch.ones(big, dtype=torch.uint8, device=dev)
+    for name, kind in (("hbm_read_4g", bqa.BQA_PROBE_READ), ("hbm_read_nt", bqa.BQA_PROBE_READ_NT)):
+        g = 8 * n_cu
+        t = timed(lambda: bqa.bqa_debug_probe(kind, g, 0, src, out, big))
+        v = big / t / 1e9
+        res[name] = {"measured": round(v, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(v / 8000.0, 4),
+                     "time_ms": round(t * 1e3, 3), "grid": g,
+                     "note": "4 GiB read per launch" + (", non-temporal cache policy" if "nt" in name else "")}
+    del src
+    torch.cuda.empty_cache()
+    # vector work under matrix work: time per round of each mix, 2 wavefronts per SIMD
+    g2, it2 = 2 * n_cu, 20000
+    iss = {}
+    for name, kind in (("mfma", bqa.BQA_PROBE_ISSUE_MFMA), ("fma", bqa.BQA_PROBE_ISSUE_FMA),
+                       ("mfma_fma", bqa.BQA_PROBE_ISSUE_MFMA_FMA), ("exp", bqa.BQA_PROBE_ISSUE_EXP),
+                       ("mfma_exp", bqa.BQA_PROBE_ISSUE_MFMA_EXP)):
+        t = timed(lambda: bqa.bqa_debug_probe(kind, g2, it2, None, out, out.numel()))
+        iss[name] = t / it2 / 2 * 1e9                   # ns of SIMD time per wavefront round
+    res["issue_overlap"] = {
+        "unit": "ns per wavefront round (SIMD time, 2 wavefronts per SIMD)",
+        "round": "8 i8 32x32x32 matrix instructions / 64 fp32 multiply-adds / 32 v_exp_f32, or the matrix "
+                 "instructions interleaved with either",
+        **{k: round(v, 2) for k, v in iss.items()},
+        "hidden_fma_share": round((iss["mfma"] + iss["fma"] - iss["mfma_fma"]) / min(iss["mfma"], iss["fma"]), 3),
+        "hidden_exp_share": round((iss["mfma"] + iss["exp"] - iss["mfma_exp"]) / min(iss["mfma"], iss["exp"]), 3),
+        "note": "hidden share = (separate sum - mixed) / the shorter part: 1 if the shorter part runs entirely "
+                "under the longer one, 0 if the two only add up"}
     print(json.dumps({"probes": res, "compute_units": n_cu, "grid_matrix": grid, "iters_matrix": iters}), flush=True)
 
 
@@ -734,7 +765,8 @@ def main():
     rl.update({"achieved": round(achieved, 1), "frac": round(achieved / rl["peak"], 4),
                "traffic": _traffic_for(case["traffic_key"]), "kernel_ms": round(kern_ms, 5)})
     # the probes' sustained rates of the same units, beside the published peak
-    probes = {"hbm": ["hbm_read_wide"], "mfma": ["mfma_i8", "mfma_fp8", "mfma_mxfp4", "mfma_bf16"]}[rl["bound"]]
+    probes = {"hbm": ["hbm_read_wide", "hbm_read_nt"],
+              "mfma": ["mfma_i8", "mfma_fp8", "mfma_mxfp4", "mfma_bf16"]}[rl["bound"]]
     mp = _measured_peak(probes)
     if mp is not None:
         rl["probe_rates"] = mp

@@ -36,7 +36,8 @@ EXPORTS = ["bqa_abi_version", "bqa_status_string", "bqa_workspace_size", "bqa_qu
            "bqa_debug_mx_dequant", "bqa_attn_fwd_ptq", "bqa_debug_probe", "bqa_quantize_qknorm",
            "bqa_attn_bwd_qknorm", "bqa_quantize_nvfp4", "bqa_attn_fwd_thrift_nvfp4"]
 BQA_PROBE_MFMA_I8, BQA_PROBE_MFMA_F8, BQA_PROBE_MFMA_F4, BQA_PROBE_MFMA_BF16, BQA_PROBE_EXP, BQA_PROBE_COPY, \
-    BQA_PROBE_READ = range(7)
+    BQA_PROBE_READ, BQA_PROBE_READ_NT, BQA_PROBE_ISSUE_MFMA, BQA_PROBE_ISSUE_FMA, BQA_PROBE_ISSUE_MFMA_FMA, \
+    BQA_PROBE_ISSUE_EXP, BQA_PROBE_ISSUE_MFMA_EXP = range(13)
 
 
 class BqaError(RuntimeError):

@@ -11,7 +11,15 @@
 //    loop is exponentials only; the values stay in (1/4, 1));
 //  * copy probe: a grid-stride 16-byte copy of `bytes` from src to dst;
 //  * read probe: a grid-stride 16-byte read of `bytes` from src, folded into
-//    one word per workgroup.
+//    one word per workgroup; the non-temporal read probe does the same with
+//    the non-temporal cache policy (the policy of the decode kernel's
+//    copies);
+//  * issue probes: per round, every wavefront issues 8 dense i8 32x32x32
+//    matrix instructions (four accumulator chains), 64 independent fp32
+//    fused multiply-adds, 32 independent v_exp_f32, or the matrix
+//    instructions interleaved with either (one matrix instruction, then 8
+//    multiply-adds or 4 exponentials): the mixed time against the sum of the
+//    separate ones says how much vector work runs under matrix work.
 // Each workgroup writes one checksum word to dst (matrix and exp probes) so
 // that nothing is optimised away.
 #include "common.hpp"
@@ -105,19 +113,77 @@ __global__ __launch_bounds__(256) void copy_probe_kernel(const v4i* __restrict__
     for (; i < n16; i += stride) dst[i] = src[i];
 }
 
+template <bool NT>
+__device__ __forceinline__ v4i probe_load(const v4i* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(256) void read_probe_kernel(const v4i* __restrict__ src, int64_t n16,
                                                          uint32_t* __restrict__ out) {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // each workgroup reads 32 KB contiguous per round (8 loads per thread)
+    const int64_t stride = (int64_t)gridDim.x * 256 * 8;
+    int64_t i = (int64_t)blockIdx.x * 256 * 8 + threadIdx.x;
     v4i acc = {0, 0, 0, 0};
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const v4i a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-        acc ^= a ^ b ^ c ^ d;
+    for (; i + 256 * 7 < n16; i += stride) {
+        v4i a[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] = probe_load<NT>(src + i + 256 * u);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= a[u];
     }
-    for (; i < n16; i += stride) acc ^= src[i];
+    for (int u = 0; u < 8; ++u)
+        if (i + 256 * u < n16) acc ^= probe_load<NT>(src + i + 256 * u);
     const float f = (float)((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) & 0xFFFF);
     const float m = wave_max(f);
     if (threadIdx.x == 0) out[blockIdx.x] = (uint32_t)m;
+}
+
+// Issue probes: MODE 0 matrix only, 1 multiply-adds only, 2 both, 3
+// exponentials only, 4 matrix and exponentials.
+template <int MODE>
+__global__ __launch_bounds__(256) void issue_probe_kernel(int64_t iters, uint32_t* __restrict__ out) {
+    const int l = threadIdx.x & 63;
+    const int seed = (int)(threadIdx.x * 2654435761u + blockIdx.x);
+    const v4i a4 = {seed & 0x07070707, (seed >> 1) & 0x07070707, 0x01020304, l};
+    v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    float x[16];
+    const float fa = 0.5f + (float)(l & 7) * (1.0f / 1024.0f);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = (float)((threadIdx.x + 37 * k) & 63) * (1.0f / 64.0f) + 0.25f;
+    constexpr bool MF = MODE == 0 || MODE == 2 || MODE == 4, FM = MODE == 1 || MODE == 2, EX = MODE == 3 || MODE == 4;
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            if constexpr (MF) {
+                if (g % 4 == 0) c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a4, a4, c0, 0, 0, 0);
+                if (g % 4 == 1) c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a4, a4, c1, 0, 0, 0);
+                if (g % 4 == 2) c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a4, a4, c2, 0, 0, 0);
+                if (g % 4 == 3) c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a4, a4, c3, 0, 0, 0);
+            }
+            if constexpr (FM) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) x[(8 * g + k) & 15] = __builtin_fmaf(x[(8 * g + k) & 15], fa, 0.25f);
+            }
+            if constexpr (EX) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) x[(4 * g + k) & 15] = __builtin_amdgcn_exp2f(-x[(4 * g + k) & 15]);
+            }
+            if constexpr (MF && (FM || EX)) {
+                __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x0002, FM ? 8 : 4, 0);
+            }
+        }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s += x[k];
+    uint32_t sum = __builtin_bit_cast(uint32_t, s);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += (uint32_t)(c0[i] ^ c1[i] ^ c2[i] ^ c3[i]);
+    sum = (uint32_t)wave_max((float)(sum & 0xFFFF));
+    if (threadIdx.x == 0) out[blockIdx.x] = sum;
 }
 
 }  // namespace
@@ -135,8 +201,16 @@ hipError_t launch_probe(int kind, int grid, int64_t iters, const void* src, void
             copy_probe_kernel<<<grid, 256, 0, st>>>((const v4i*)src, (v4i*)dst, (int64_t)(bytes / 16));
             break;
         case PROBE_READ:
-            read_probe_kernel<<<grid, 256, 0, st>>>((const v4i*)src, (int64_t)(bytes / 16), out);
+            read_probe_kernel<false><<<grid, 256, 0, st>>>((const v4i*)src, (int64_t)(bytes / 16), out);
             break;
+        case PROBE_READ_NT:
+            read_probe_kernel<true><<<grid, 256, 0, st>>>((const v4i*)src, (int64_t)(bytes / 16), out);
+            break;
+        case PROBE_ISSUE_MFMA: issue_probe_kernel<0><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_ISSUE_FMA: issue_probe_kernel<1><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_ISSUE_MFMA_FMA: issue_probe_kernel<2><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_ISSUE_EXP: issue_probe_kernel<3><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_ISSUE_MFMA_EXP: issue_probe_kernel<4><<<grid, 256, 0, st>>>(iters, out); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

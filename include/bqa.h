@@ -446,11 +446,20 @@ bqa_status bqa_debug_mx_dequant(const void* codes, const void* scales, int64_t n
  * unused).  BQA_PROBE_COPY: copies `bytes` (a multiple of 16, both pointers
  * 16-byte aligned) from src to dst with 16-byte accesses; iters unused.
  * BQA_PROBE_READ: reads `bytes` (a multiple of 16, src 16-byte aligned) with
- * 16-byte accesses and writes one checksum word per workgroup to dst.
+ * 16-byte accesses and writes one checksum word per workgroup to dst;
+ * BQA_PROBE_READ_NT the same with the non-temporal cache policy.  Issue
+ * probes (src unused, one checksum word per workgroup to dst, bytes >= 4
+ * grid): every wavefront runs iters rounds of 8 int8 32x32x32 matrix
+ * instructions (BQA_PROBE_ISSUE_MFMA), 64 fp32 fused multiply-adds
+ * (BQA_PROBE_ISSUE_FMA), 32 v_exp_f32 (BQA_PROBE_ISSUE_EXP), or the matrix
+ * instructions interleaved with the multiply-adds (BQA_PROBE_ISSUE_MFMA_FMA)
+ * or with the exponentials (BQA_PROBE_ISSUE_MFMA_EXP).
  */
 enum {
     BQA_PROBE_MFMA_I8 = 0, BQA_PROBE_MFMA_F8 = 1, BQA_PROBE_MFMA_F4 = 2, BQA_PROBE_MFMA_BF16 = 3,
-    BQA_PROBE_EXP = 4, BQA_PROBE_COPY = 5, BQA_PROBE_READ = 6
+    BQA_PROBE_EXP = 4, BQA_PROBE_COPY = 5, BQA_PROBE_READ = 6, BQA_PROBE_READ_NT = 7,
+    BQA_PROBE_ISSUE_MFMA = 8, BQA_PROBE_ISSUE_FMA = 9, BQA_PROBE_ISSUE_MFMA_FMA = 10, BQA_PROBE_ISSUE_EXP = 11,
+    BQA_PROBE_ISSUE_MFMA_EXP = 12
 };
 bqa_status bqa_debug_probe(int32_t kind, int32_t grid, int64_t iters, const void* src, void* dst, size_t bytes,
                            void* stream);
