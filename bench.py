@@ -466,7 +466,7 @@ def _sagebwd_roofline(w):
                   "peak": round(bwd_ops / t_peak / 1e12, 1),
                   "peak_note": "i8 peak for 4 of the 5 backward products, bf16 for dP = dO V^T",
                   "ops_per_launch": bwd_ops},
-        traffic_key="sbwd_dkdv_kernel", cpu=cpu_baseline_sagebwd)
+        traffic_key="sbwd_dkdv_kernel<false>", cpu=cpu_baseline_sagebwd)
 
 
 def _sagebwd_i8dp_case(w, bqa, torch):
@@ -488,6 +488,7 @@ def _sagebwd_i8dp_case(w, bqa, torch):
                                                      "transposes, sbwd_dkdv_kernel<I8DP>, sbwd_dq_kernel<I8DP>)",
                             peak=PEAK_I8_TOPS, peak_note="i8 peak for all five backward products",
                             ops_per_launch=bwd_ops)
+    case["traffic_key"] = "sbwd_dkdv_kernel<true>"
     return case
 
 
