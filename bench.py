@@ -656,6 +656,18 @@ def probe_main(torch, bqa):
         "hidden_exp_share": round((iss["mfma"] + iss["exp"] - iss["mfma_exp"]) / min(iss["mfma"], iss["exp"]), 3),
         "note": "hidden share = (separate sum - mixed) / the shorter part: 1 if the shorter part runs entirely "
                 "under the longer one, 0 if the two only add up"}
+    # issue cost of single vector instructions: ns of SIMD time per wavefront instruction
+    ops = {}
+    for name, kind in (("v_mul_f32", bqa.BQA_PROBE_OP_MUL), ("v_fma_f32", bqa.BQA_PROBE_OP_FMA),
+                       ("v_cvt_f32_i32", bqa.BQA_PROBE_OP_CVT_F32_I32), ("v_max3_f32", bqa.BQA_PROBE_OP_MAX3),
+                       ("v_cvt_pk_fp8_f32", bqa.BQA_PROBE_OP_CVT_PK_FP8),
+                       ("v_cvt_scalef32_pk_fp4_f32", bqa.BQA_PROBE_OP_CVT_PK_FP4),
+                       ("v_permlane32_swap", bqa.BQA_PROBE_OP_PERMLANE32)):
+        t = timed(lambda: bqa.bqa_debug_probe(kind, g2, 2000, None, out, out.numel()))
+        ops[name] = round(t / 2000 / 2 / 64 * 1e9, 3)
+    ops["v_exp_f32"] = round(iss["exp"] / 32, 3)
+    res["instruction_issue"] = {"unit": "ns of SIMD time per wavefront instruction (2 wavefronts per SIMD, 16 "
+                                        "independent chains per lane)", **ops}
     print(json.dumps({"probes": res, "compute_units": n_cu, "grid_matrix": grid, "iters_matrix": iters}), flush=True)
 
 

@@ -19,7 +19,10 @@
 //    fused multiply-adds, 32 independent v_exp_f32, or the matrix
 //    instructions interleaved with either (one matrix instruction, then 8
 //    multiply-adds or 4 exponentials): the mixed time against the sum of the
-//    separate ones says how much vector work runs under matrix work.
+//    separate ones says how much vector work runs under matrix work;
+//  * instruction probes: 64 instances per round of one vector instruction
+//    (fp32 multiply, multiply-add, int->float conversion, v_max3, fp8 pack,
+//    scaled fp4 pack, permlane32 swap) over 16 independent chains.
 // Each workgroup writes one checksum word to dst (matrix and exp probes) so
 // that nothing is optimised away.
 #include "common.hpp"
@@ -186,6 +189,43 @@ __global__ __launch_bounds__(256) void issue_probe_kernel(int64_t iters, uint32_
     if (threadIdx.x == 0) out[blockIdx.x] = sum;
 }
 
+// Single-instruction issue probes: every round, each lane runs 64 instances
+// of one vector instruction over 16 independent chains.
+template <int OP>
+__global__ __launch_bounds__(256) void op_probe_kernel(int64_t iters, uint32_t* __restrict__ out) {
+    const int l = threadIdx.x & 63;
+    float x[16];
+    uint32_t u[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        x[q] = (float)((threadIdx.x + 37 * q) & 63) * (1.0f / 64.0f) + 0.25f;
+        u[q] = threadIdx.x * 77u + (uint32_t)q;
+    }
+    const float fa = 0.5f + (float)(l & 7) * (1.0f / 1024.0f);
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int q = 0; q < 64; ++q) {
+            const int i = q & 15, j = (q + 5) & 15, k = (q + 9) & 15;
+            if constexpr (OP == 0) x[i] = x[i] * x[j];                                           // v_mul_f32
+            else if constexpr (OP == 1) x[i] = __builtin_fmaf(x[i], fa, x[j]);                   // v_fma_f32
+            else if constexpr (OP == 2) x[i] = (float)__builtin_bit_cast(int, x[i]);             // v_cvt_f32_i32
+            else if constexpr (OP == 3) x[i] = __builtin_fmaxf(__builtin_fmaxf(x[i], x[j]), x[k]);   // v_max3_f32
+            else if constexpr (OP == 4) u[i] = __builtin_amdgcn_cvt_pk_fp8_f32(x[i], x[j], u[i], false);
+            else if constexpr (OP == 5) u[i] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u[i], x[i], x[j], fa, 0);
+            else {                                                                              // v_permlane32_swap
+                const v2i r = __builtin_amdgcn_permlane32_swap((int)u[i], (int)u[j], false, false);
+                u[i] = (uint32_t)r[0];
+                u[j] = (uint32_t)r[1];
+            }
+        }
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) s += __builtin_bit_cast(uint32_t, x[q]) + u[q];
+    s = (uint32_t)wave_max((float)(s & 0xFFFF));
+    if (threadIdx.x == 0) out[blockIdx.x] = s;
+}
+
 }  // namespace
 
 hipError_t launch_probe(int kind, int grid, int64_t iters, const void* src, void* dst, size_t bytes,
@@ -211,6 +251,13 @@ hipError_t launch_probe(int kind, int grid, int64_t iters, const void* src, void
         case PROBE_ISSUE_MFMA_FMA: issue_probe_kernel<2><<<grid, 256, 0, st>>>(iters, out); break;
         case PROBE_ISSUE_EXP: issue_probe_kernel<3><<<grid, 256, 0, st>>>(iters, out); break;
         case PROBE_ISSUE_MFMA_EXP: issue_probe_kernel<4><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_OP_MUL: op_probe_kernel<0><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_OP_FMA: op_probe_kernel<1><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_OP_CVT_F32_I32: op_probe_kernel<2><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_OP_MAX3: op_probe_kernel<3><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_OP_CVT_PK_FP8: op_probe_kernel<4><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_OP_CVT_PK_FP4: op_probe_kernel<5><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_OP_PERMLANE32: op_probe_kernel<6><<<grid, 256, 0, st>>>(iters, out); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

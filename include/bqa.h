@@ -453,13 +453,21 @@ bqa_status bqa_debug_mx_dequant(const void* codes, const void* scales, int64_t n
  * instructions (BQA_PROBE_ISSUE_MFMA), 64 fp32 fused multiply-adds
  * (BQA_PROBE_ISSUE_FMA), 32 v_exp_f32 (BQA_PROBE_ISSUE_EXP), or the matrix
  * instructions interleaved with the multiply-adds (BQA_PROBE_ISSUE_MFMA_FMA)
- * or with the exponentials (BQA_PROBE_ISSUE_MFMA_EXP).
+ * or with the exponentials (BQA_PROBE_ISSUE_MFMA_EXP).  Instruction probes
+ * (same arguments): every lane runs iters rounds of 64 instances of one
+ * vector instruction over 16 independent chains: fp32 multiply
+ * (BQA_PROBE_OP_MUL), fused multiply-add (BQA_PROBE_OP_FMA), int->float
+ * conversion (BQA_PROBE_OP_CVT_F32_I32), v_max3_f32 (BQA_PROBE_OP_MAX3), the
+ * packed fp8 conversion (BQA_PROBE_OP_CVT_PK_FP8), the scaled packed fp4
+ * conversion (BQA_PROBE_OP_CVT_PK_FP4), v_permlane32_swap
+ * (BQA_PROBE_OP_PERMLANE32).
  */
 enum {
     BQA_PROBE_MFMA_I8 = 0, BQA_PROBE_MFMA_F8 = 1, BQA_PROBE_MFMA_F4 = 2, BQA_PROBE_MFMA_BF16 = 3,
     BQA_PROBE_EXP = 4, BQA_PROBE_COPY = 5, BQA_PROBE_READ = 6, BQA_PROBE_READ_NT = 7,
     BQA_PROBE_ISSUE_MFMA = 8, BQA_PROBE_ISSUE_FMA = 9, BQA_PROBE_ISSUE_MFMA_FMA = 10, BQA_PROBE_ISSUE_EXP = 11,
-    BQA_PROBE_ISSUE_MFMA_EXP = 12
+    BQA_PROBE_ISSUE_MFMA_EXP = 12, BQA_PROBE_OP_MUL = 13, BQA_PROBE_OP_FMA = 14, BQA_PROBE_OP_CVT_F32_I32 = 15,
+    BQA_PROBE_OP_MAX3 = 16, BQA_PROBE_OP_CVT_PK_FP8 = 17, BQA_PROBE_OP_CVT_PK_FP4 = 18, BQA_PROBE_OP_PERMLANE32 = 19
 };
 bqa_status bqa_debug_probe(int32_t kind, int32_t grid, int64_t iters, const void* src, void* dst, size_t bytes,
                            void* stream);
