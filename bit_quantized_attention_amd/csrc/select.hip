@@ -156,11 +156,11 @@ __device__ __forceinline__ void radix_topk(const double* sc, int L, int kk, int3
 
 __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                     int Hq, int Hkv, int nqb, int nkb, int d, int causal,
-                                                    int budget_ppm, int max_sel, int L,
+                                                    int budget_ppm, int max_sel, int L, int ring,
                                                     int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     double* sc = (double*)smem;                       // [L]: block j's score at j
-    uint8_t* kt = smem + sizeof(double) * L;          // L <= 1024: 3 x [NT][64 B] pieces of the key means; then 8 KB of histograms
+    uint8_t* kt = smem + sizeof(double) * L;          // ring: 3 x [NT][64 B] pieces of the key means; then 8 KB of histograms
     __shared__ float q[128];
 
     const int tid = threadIdx.x;
@@ -202,8 +202,9 @@ __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qb
     // running sum carries over the pieces of a chunk, so the channels are
     // still added in ascending order.
     for (int j = tid; j < L; j += NT) sc[j] = -__builtin_inf();
-    if (L > 1024) {
-        // long rows (up to 4096 blocks, rare): each thread reads its rows directly
+    if (!ring) {
+        // many workgroups (prefill) or long rows: each thread reads its rows
+        // directly, and the small LDS footprint lets 8 workgroups share a CU
         for (int j = tid; j < nv; j += NT) {
             const float* kr = kb + (int64_t)j * d;
             double a = 0.0;
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qb
             sc[j] = a;
         }
     }
-    const int npc = d / 16, nch = L <= 1024 ? (nv + NT - 1) / NT : 0, n_pieces = nch * npc;
+    const int npc = d / 16, nch = ring ? (nv + NT - 1) / NT : 0, n_pieces = nch * npc;
     const int wv = tid >> 6, ln = tid & 63;
     auto issue = [&](int pc) __attribute__((always_inline)) {
         const int r0 = pc / npc * NT, c0 = pc % npc * 16;
@@ -278,10 +279,16 @@ hipError_t launch_select(const float* qbar, const float* kbar, int B, int Hq, in
                          hipStream_t st) {
     const int L = select_sort_len(nkb);
     const size_t shm = (size_t)L * sizeof(double);
-    // pieces of the key means (L <= 1024) or, later, the 8 KB of histograms
-    const size_t lds = shm + (L <= 1024 ? 3 * NT * 64 : 8192);     // at most 56 KB
-    select_kernel<<<B * Hq * nqb, NT, lds, st>>>(qbar, kbar, Hq, Hkv, nqb, nkb, d, causal, budget_ppm, max_sel, L,
-                                                 sel_idx, sel_cnt);
+    // The LDS ring of key-mean pieces serves rows of up to 1024 blocks when
+    // the grid is small enough that the time of one workgroup is the time of
+    // the launch (decode: 512 workgroups); a large grid (prefill, one
+    // workgroup per query block) is throughput-bound and takes the direct
+    // row reads with a small LDS footprint.
+    const int grid = B * Hq * nqb;
+    const int ring = L <= 1024 && grid <= 4096;
+    const size_t lds = shm + (ring ? 3 * NT * 64 : 8192);     // at most 56 KB
+    select_kernel<<<grid, NT, lds, st>>>(qbar, kbar, Hq, Hkv, nqb, nkb, d, causal, budget_ppm, max_sel, L, ring,
+                                         sel_idx, sel_cnt);
     return hipGetLastError();
 }
 
