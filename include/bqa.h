@@ -446,8 +446,10 @@ bqa_status bqa_debug_mx_dequant(const void* codes, const void* scales, int64_t n
  * unused).  BQA_PROBE_COPY: copies `bytes` (a multiple of 16, both pointers
  * 16-byte aligned) from src to dst with 16-byte accesses; iters unused.
  * BQA_PROBE_READ: reads `bytes` (a multiple of 16, src 16-byte aligned) with
- * 16-byte accesses and writes one checksum word per workgroup to dst;
- * BQA_PROBE_READ_NT the same with the non-temporal cache policy.  Issue
+ * 16-byte accesses and writes one checksum word per workgroup to dst (dst
+ * 4-byte aligned and holding grid words, which the caller sizes: `bytes`
+ * describes src here); BQA_PROBE_READ_NT the same with the non-temporal
+ * cache policy.  Issue
  * probes (src unused, one checksum word per workgroup to dst, bytes >= 4
  * grid): every wavefront runs iters rounds of 8 int8 32x32x32 matrix
  * instructions (BQA_PROBE_ISSUE_MFMA), 64 fp32 fused multiply-adds
