@@ -300,7 +300,7 @@ def cpu_baseline_thrift(w, budget_s: float = 20.0):
     while qb > 0 and time.perf_counter() - t0 < budget_s:
         qb -= 1
         oracle.thrift_fwd(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0], Qh=Q, Kh=K, Vh=V,
-                          sel_idx=idx, sel_cnt=cnt, Nq=w.Nq, Nk=w.Nk, d=w.d, blk=128, hp_tile=64, causal=True,
+                          sel_idx=idx, sel_cnt=cnt, Nq=w.Nq, Nk=w.Nk, d=w.d, blk=128, hp_tile=32, causal=True,
                           tau=tau_for(w.d),
                           qblocks=(qb, qb + 1))
         pairs += sum(128 * qb + a + 1 for a in range(128))

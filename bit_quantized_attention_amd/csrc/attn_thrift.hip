@@ -9,10 +9,12 @@
 // Q, K, V), all merged by one online softmax.  The diagonal block is masked
 // in whichever path takes it.
 //
-// Layout: one workgroup of 4 wavefronts per 128 query rows (32 rows per
-// wavefront, S^T = K Q^T so each lane owns one query row); FP4 key blocks of
-// 128 keys, bf16 key blocks in two halves of 64 (each half is one tile of
-// the online softmax).  The softmax is FlashAttention-2's: P = exp(s - m)
+// Layout: one workgroup per 128 query rows, S^T = K Q^T so that each lane
+// owns one query row; FP4 key blocks of 128 keys.  The prefill kernel runs
+// 8 wavefronts of 16 rows and takes the selected blocks in quarters of 32
+// keys, each quarter one tile of the online softmax; the NVFP4 emulation
+// kernel runs 4 wavefronts of 32 rows with tiles of 64 keys.  The softmax
+// is FlashAttention-2's: P = exp(s - m)
 // against the running row maximum m, the sums so far scaled by
 // exp(m_old - m_new) when m moves.  The FP4 path's accumulator is kept in
 // units of the current block's r/6 and rescaled when the next block brings a
@@ -21,6 +23,7 @@
 // its share of O is below 2^-64 of the row's, and the unit change would leave
 // fp32's range.
 #include <mutex>
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -64,23 +67,6 @@ union LdsBuf {
     LdsF4Bias p;
 };
 
-// FP4 key block J: codes and scales of K and V^T, all by direct copies.
-__device__ __forceinline__ void issue_f4(const ThriftFwdArgs& a, int bhk, int J, LdsF4& L, int w, int l) {
-    const int t0 = J * KB;
-    const uint8_t* kbase = a.kc + ((int64_t)bhk * a.Nk + t0) * (D / 2);
-    const uint8_t* vbase = a.vc + (int64_t)bhk * D * (a.Nk / 2) + t0 / 2;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int sgm = 2 * w + u, r = 16 * sgm + (l >> 2);
-        lds_copy16((uint32_t)(r * (D / 2) + 16 * ((l & 3) ^ fk64(r))), kbase, lds_addr(L.kc + 1024 * sgm));
-        lds_copy16((uint32_t)r * (uint32_t)(a.Nk / 2) + (uint32_t)(16 * ((l & 3) ^ fv64(r))), vbase,
-                   lds_addr(L.vc + 1024 * sgm));
-    }
-    if (w < 2) lds_copy4((uint32_t)(4 * l), a.ks + ((int64_t)bhk * a.Nk + t0 + 64 * w) * (D / 32), lds_addr(L.ks + 256 * w));
-    else lds_copy4((uint32_t)l * (uint32_t)(a.Nk / 32), a.vs + ((int64_t)bhk * D + 64 * (w - 2)) * (a.Nk / 32) + t0 / 32,
-                   lds_addr(L.vs + 256 * (w - 2)));
-}
-
 // bf16 half block (keys k0 .. k0 + 63): K rows by direct copies; V comes back
 // in registers (4 keys x 8 channels per thread) for a transposed store.
 struct VStage {
@@ -98,10 +84,6 @@ __device__ __forceinline__ void issue_bf(const Dense& kx, const Dense& vx, int b
     const int cg = tid & 15, kq = tid >> 4;
 #pragma unroll
     for (int u = 0; u < 4; ++u) vs.v[u] = *(const v4i*)(vb + (int64_t)(k0 + 4 * kq + u) * vx.sN + 8 * cg);
-}
-__device__ __forceinline__ void issue_bf(const ThriftFwdArgs& a, int b, int hk, int k0, LdsBf& L, int w, int l,
-                                         int tid, VStage& vs) {
-    issue_bf(a.k_hi, a.v_hi, b, hk, k0, L, w, l, tid, vs);
 }
 __device__ __forceinline__ void store_bf(const VStage& vs, LdsBf& L, int tid) {
     const int cg = tid & 15, kq = tid >> 4;
@@ -132,13 +114,97 @@ __device__ __forceinline__ void follow_max(v16f* oacc, float& l_run, float& m_ru
 }
 constexpr float R_FLOOR = 0x1p-64f;   // two-level factors below this add nothing
 
+// ---------------------------------------------------------------------------
+// Prefill kernel.  Eight wavefronts per 128-row query block, 16 query rows
+// each, on the 16 x 16 matrix instructions: a wavefront's accumulators and
+// block scores fit in about 120 registers, so four wavefronts share a SIMD.
+// Scores are S^T = K Q^T, lane l owning query row l % 16.  FP4 blocks: the
+// rows of S MFMA b are the keys kappa(b, r) = 32 (r / 4) + 4 b + r % 4, so
+// lane l holds keys 32 (l / 16) .. + 31 in order, one whole MX block of P:
+// its codes are the lane's B operand of P.V as they stand and its scale
+// needs no other lane.  bf16 quarters (32 keys): S MFMA b (16 keys) takes
+// the keys 8 (r / 4) + 4 b + r % 4, so lane l holds keys 8 (l / 16) .. + 7,
+// its B operand of P.V.
+//
 // PTQ: the post-training FP4 baseline (query and key smoothing, two-level
 // P): no selected blocks, and key j's shift qbar . k^_j of the workgroup's
 // query block (a.sbias) is added to its raw scores.
+
+// LDS layout of the FP4 block: chunk-major.  A matrix instruction's operand
+// read gives each group of 16 lanes (l / 16 = g) the 16-byte chunk g of 16
+// rows; the rows' chunks g sit next to one another, so each group reads one
+// contiguous 256-byte span.  Measured on gfx950, such reads have no bank
+// conflicts, while four groups that read different chunks of the same
+// 64-byte rows take twice the cycles under each row swizzle tried, although
+// every group alone spreads over all banks.  K codes: chunk g (channels
+// 32 g .. + 31) of the key
+// at position p at kc + 2048 g + 16 p, with the keys in the order the S
+// instructions read them: position p = 16 b + 4 a + c holds key
+// 32 a + 4 b + c; K scales: the key at position p has its four bytes at word
+// p.  V^T codes: chunk g (keys 32 g .. + 31) of channel ch at
+// vc + 2048 g + 16 ch; V scales channel-major.
+__device__ __forceinline__ int key_at(int p) { return 32 * ((p >> 2) & 3) + 4 * (p >> 4) + (p & 3); }
+
+// FP4 key block J into L, one K copy and one V copy per wavefront of eight.
+__device__ __forceinline__ void issue_f4_16(const ThriftFwdArgs& a, int bhk, int J, LdsF4& L, int w, int l) {
+    const int t0 = J * KB;
+    const uint8_t* kbase = a.kc + ((int64_t)bhk * a.Nk + t0) * (D / 2);
+    const uint8_t* vbase = a.vc + (int64_t)bhk * D * (a.Nk / 2) + t0 / 2;
+    // wavefront w: chunk w / 2 of positions (K) and channels (V) 64 (w % 2) .. + 63
+    const int j = w >> 1, p = 64 * (w & 1) + l;
+    lds_copy16((uint32_t)(key_at(p) * (D / 2) + 16 * j), kbase, lds_addr(L.kc + 1024 * w));
+    lds_copy16((uint32_t)p * (uint32_t)(a.Nk / 2) + (uint32_t)(16 * j), vbase, lds_addr(L.vc + 1024 * w));
+    if (w < 2) lds_copy4((uint32_t)(4 * key_at(64 * w + l)), a.ks + ((int64_t)bhk * a.Nk + t0) * (D / 32), lds_addr(L.ks + 256 * w));
+    else if (w < 4)
+        lds_copy4((uint32_t)l * (uint32_t)(a.Nk / 32), a.vs + ((int64_t)bhk * D + 64 * (w - 2)) * (a.Nk / 32) + t0 / 32,
+                  lds_addr(L.vs + 256 * (w - 2)));
+}
+
+// bf16 quarter block (keys k0 .. k0 + 31), chunk-major as the FP4 block: K
+// chunk j (channels 8 j .. + 7) of the key at position p at k + 512 j + 16 p,
+// position p = 16 b + 4 a + c holding key 8 a + 4 b + c, by direct copies (one
+// per wavefront); V through registers (two keys x 4 channels per thread) for
+// a transposed store: chunk j (keys 8 j .. + 7) of channel ch at
+// vt + 2048 j + 16 ch.
+struct LdsBq {
+    uint8_t k[32 * D * 2];      // 32 keys x 256 B
+    uint8_t vt[D * 32 * 2];     // 128 channels x 64 B (32 keys)
+};
+struct VStageQ {
+    v2i v[2];
+};
+__device__ __forceinline__ void issue_bq(const ThriftFwdArgs& a, int b, int hk, int k0, LdsBq& L, int w, int l, int tid,
+                                         VStageQ& vs) {
+    const uint16_t* kb = (const uint16_t*)a.k_hi.p + b * a.k_hi.sB + hk * a.k_hi.sH + (int64_t)k0 * a.k_hi.sN;
+    const int j = 2 * w + (l >> 5), p = l & 31;
+    const int kk = 8 * ((p >> 2) & 3) + 4 * (p >> 4) + (p & 3);
+    lds_copy16((uint32_t)(2 * (kk * a.k_hi.sN + 8 * j)), kb, lds_addr(L.k + 1024 * w));
+    const uint16_t* vb = (const uint16_t*)a.v_hi.p + b * a.v_hi.sB + hk * a.v_hi.sH;
+    const int kp = tid & 15, cq = tid >> 4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) vs.v[u] = *(const v2i*)(vb + (int64_t)(k0 + 2 * kp + u) * a.v_hi.sN + 4 * cq);
+}
+__device__ __forceinline__ void store_bq(const VStageQ& vs, LdsBq& L, int tid) {
+    const int kp = tid & 15, cq = tid >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // channel 4 cq + e, keys 2 kp and 2 kp + 1
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t x = __builtin_amdgcn_perm((uint32_t)vs.v[1][e >> 1], (uint32_t)vs.v[0][e >> 1], sel);
+        const int r = 4 * cq + e;
+        *(uint32_t*)(L.vt + 2048 * (kp >> 2) + 16 * r + 4 * (kp & 3)) = x;
+    }
+}
+union LdsBuf16 {
+    LdsF4 f;
+    LdsBq b;
+    LdsF4Bias p;
+};
+
 template <bool PTQ>
-__global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
-    __shared__ __attribute__((aligned(16))) LdsBuf lds[2];
-    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, lq = l & 31;
+__global__ __launch_bounds__(512, 4) void thrift_fwd_kernel(ThriftFwdArgs a) {
+    __shared__ __attribute__((aligned(16))) LdsBuf16 lds[2];
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, q = l & 15;
     const int nqt = (a.Nq + BM - 1) / BM;
     const int grid = gridDim.x;
     // XCD-aware order: each XCD takes a contiguous range, heavy (late) query blocks first
@@ -146,40 +212,44 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
     const int qt = nqt - 1 - bid % nqt;
     const int bh = bid / nqt, b = bh / a.Hq, hq = bh % a.Hq;
     const int hk = hq / (a.Hq / a.Hkv), bhk = b * a.Hkv + hk;
-    const int qrow = qt * BM + 32 * w + lq;
+    const int qrow = qt * BM + 16 * w + q;
     const bool row_ok = qrow < a.Nq;
-    const int krow = sigma(lq);
     const int off = a.Nk - a.Nq;                       // bottom-right alignment of the causal mask
     const int qpos = off + qrow;
     const int qpos_lo = off + qt * BM;                 // smallest position in the workgroup
     const int qpos_hi = off + (qt * BM + BM - 1 < a.Nq - 1 ? qt * BM + BM - 1 : a.Nq - 1);
     const int nkb = a.Nk / KB;
     const int nJ = a.causal ? (qpos_hi / KB + 1 < nkb ? qpos_hi / KB + 1 : nkb) : nkb;
-    const int32_t* sel = PTQ ? nullptr : a.sel_idx + ((int64_t)bh * nqt + qt) * a.max_sel;
+    // the selection list through the scalar cache: its reads then wait on the
+    // scalar counter, not on the vector one that also counts the block copies
+    const __attribute__((address_space(4))) int32_t* sel =
+        PTQ ? nullptr : uniform_ptr(a.sel_idx + ((int64_t)bh * nqt + qt) * a.max_sel);
     const int ns = PTQ ? 0 : a.sel_cnt[(int64_t)bh * nqt + qt];
     const float* brow = PTQ ? a.sbias + ((int64_t)bh * nqt + qt) * a.Nk : nullptr;
-    // waves 2 and 3 copy the 128 shifts of key block J next to its codes
-    auto issue_bias = [&](int J, LdsBuf& L) {
-        if (PTQ && w >= 2) lds_copy4((uint32_t)(4 * l), brow + J * KB + 64 * (w - 2), lds_addr(L.p.bias + 64 * (w - 2)));
+    // waves 4 and 5 copy the 128 shifts of key block J next to its codes
+    auto issue_bias = [&](int J, LdsBuf16& L) {
+        if (PTQ && (w == 4 || w == 5))
+            lds_copy4((uint32_t)(4 * l), brow + J * KB + 64 * (w - 4), lds_addr(L.p.bias + 64 * (w - 4)));
     };
     const float c = a.c_log2;
 
-    // FP4 query codes: B operand of S^T (channels 64 kk + 32 h .. + 31)
-    v4i qb[2];
-    int qsb[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        qb[kk] = row_ok ? *(const v4i*)(a.qc + ((int64_t)bh * a.Nq + qrow) * (D / 2) + 32 * kk + 16 * h) : v4i{};
-        qsb[kk] = row_ok ? (int)a.qs[((int64_t)bh * a.Nq + qrow) * (D / 32) + 2 * kk + h] : 0;
-    }
-    __builtin_amdgcn_s_waitcnt(0);
+    // FP4 query codes: B operand of S^T (channels 32 g .. 32 g + 31)
+    const v4i qb = row_ok ? *(const v4i*)(a.qc + ((int64_t)bh * a.Nq + qrow) * (D / 2) + 16 * g) : v4i{};
+    const int qsb = row_ok ? (int)a.qs[((int64_t)bh * a.Nq + qrow) * (D / 32) + g] : 0;
 
-    v16f oacc[D / 32];
+    v4f oacc[D / 16];                  // O^T tile cb: channels 16 cb + 4 g + i of row q
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = v16f{};
+    for (int cb = 0; cb < D / 16; ++cb) oacc[cb] = v4f{};
     float m_run = -__builtin_inff();   // running maximum (log2 units); -inf before the first finite score
-    float l_run = 0.0f;                // this lane half's share of the row sum
+    float l_run = 0.0f;                // this lane's share of the row sum
     float gsc = 1.0f;                  // FP4 path: oacc holds O / gsc, gsc = r / 6 of the last block
+
+    // LDS byte offsets of this lane's operands (block-independent parts)
+    // (S MFMA b reads key 32 (q / 4) + 4 b + q % 4, at position 16 b + q)
+    const int koff = 2048 * g + 16 * q;      // + 256 b
+    const int ksoff = 4 * q + g;             // + 64 b
+    const int voff = 2048 * g + 16 * q;      // channel 16 cb + q: + 256 cb
+    const int vsoff = 4 * q + g;             // + 64 cb
 
     // ------------------------------------------------------------ FP4 path
     int sp = 0;
@@ -188,60 +258,42 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
         while (J < nJ && sp < ns && sel[sp] == J) { ++J; ++sp; }
         return J;
     };
-    int J = next_unsel(0);
-    if (J < nJ) {
-        issue_f4(a, bhk, J, lds[0].f, w, l);
-        issue_bias(J, lds[0]);
-        BQA_WAIT_VM(0);
-        barrier_only();
-    }
-    int buf = 0;
-    while (J < nJ) {
-        const int Jn = next_unsel(J + 1);
+    auto f4_step = [&](auto slot, int J, int Jn) __attribute__((always_inline)) {
+        constexpr int SB = decltype(slot)::value;
         if (Jn < nJ) {
-            issue_f4(a, bhk, Jn, lds[buf ^ 1].f, w, l);
-            issue_bias(Jn, lds[buf ^ 1]);
+            issue_f4_16(a, bhk, Jn, lds[SB ^ 1].f, w, l);
+            issue_bias(Jn, lds[SB ^ 1]);
         }
-        const LdsF4& L = lds[buf].f;
-        // scores: s[t] reg i of half h is key 32 t + 16 h + i of the block
-        v16f s[4];
+        const LdsF4& L = lds[SB].f;
+        // scores: s[b][i] is key 32 g + 4 b + i of the block
+        v4f s[8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            s[t] = v16f{};
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int r = 32 * t + krow;
-                const v4i av = *(const v4i*)(L.kc + r * 64 + 16 * ((2 * kk + h) ^ fk64(r)));
-                s[t] = mfma_f4_32x32x64(av, (int)L.ks[4 * r + 2 * kk + h], qb[kk], qsb[kk], s[t]);
-            }
+        for (int bb = 0; bb < 8; ++bb) {
+            const v4i av = *(const v4i*)(L.kc + koff + 256 * bb);
+            s[bb] = mfma_f4_16x16x128(av, (int)L.ks[ksoff + 64 * bb], qb, qsb, v4f{});
         }
         if constexpr (PTQ) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int bb = 0; bb < 8; ++bb) {
+                const v4f sh = *(const v4f*)(lds[SB].p.bias + 32 * g + 4 * bb);
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const v4f bb = *(const v4f*)(lds[buf].p.bias + 32 * t + 16 * h + 4 * q4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) s[t][4 * q4 + e] += bb[e];
-                }
+                for (int i = 0; i < 4; ++i) s[bb][i] += sh[i];
+            }
         }
         if (a.causal && J * KB + KB - 1 > qpos_lo) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int bb = 0; bb < 8; ++bb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (J * KB + 32 * t + 16 * h + i > qpos) s[t][i] = -__builtin_inff();
+                for (int i = 0; i < 4; ++i)
+                    if (J * KB + 32 * g + 4 * bb + i > qpos) s[bb][i] = -__builtin_inff();
         }
-        float bt[4];
+        // the lane's MX block maximum, then the row's over its four lanes
+        float gm = max3f(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            float m = __builtin_fmaxf(s[t][0], s[t][1]);
-#pragma unroll
-            for (int i = 2; i < 16; i += 2) m = __builtin_fmaxf(__builtin_fmaxf(m, s[t][i]), s[t][i + 1]);
-            bt[t] = __builtin_fmaxf(m, partner32f(m));
-        }
-        const float smax = __builtin_fmaxf(__builtin_fmaxf(bt[0], bt[1]), __builtin_fmaxf(bt[2], bt[3]));
-        const float m_new = __builtin_fmaxf(m_run, smax * c);
+        for (int k = 3; k < 31; k += 2) gm = max3f(gm, s[k >> 2][k & 3], s[(k + 1) >> 2][(k + 1) & 3]);
+        gm = max2f(gm, s[7][3]);
+        const float smax = quad_max16(gm);
+        const float m_new = max2f(m_run, smax * c);
         const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
         const float mu = m_new == -__builtin_inff() ? 0.0f : m_new;
         // two-level P: r = the row's largest P in the block, P' = P 6 / r =
@@ -253,161 +305,168 @@ __global__ __launch_bounds__(256, 2) void thrift_fwd_kernel(ThriftFwdArgs a) {
         const float bias2 = r > 0.0f ? 2.584962500721156f - smax * c : -__builtin_inff();   // log2(6) - smax c
         float ps[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            float q0 = 0.0f, q1 = 0.0f;
+        for (int bb = 0; bb < 8; ++bb)
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-                s[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c, bias2));
-                s[t][i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i + 1], c, bias2));
-                q0 += s[t][i];
-                q1 += s[t][i + 1];
+            for (int i = 0; i < 4; ++i) {
+                s[bb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][i], c, bias2));
+                ps[i] = bb == 0 ? s[bb][i] : ps[i] + s[bb][i];
             }
-            ps[t] = q0 + q1;
-        }
         l_run *= alpha;
         if (r > 0.0f) l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) * (r * (1.0f / 6.0f));
         m_run = m_new;
-        const float six_r = r > 0.0f ? 6.0f / r : 0.0f;
-        int e[4];
+        const float six_r = r > 0.0f ? 6.0f * __builtin_amdgcn_rcpf(r) : 0.0f;
+        const int e = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(gm, c, bias2)));
+        const float sc = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+        v4i pb;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) e[t] = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(bt[t], c, bias2)));
-        uint32_t pw[4][2];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const float sc = __builtin_bit_cast(float, (uint32_t)(e[t] + 127) << 23);
-#pragma unroll
-            for (int wd = 0; wd < 2; ++wd) {
-                uint32_t x = 0;
-                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 0], s[t][8 * wd + 1], sc, 0);
-                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 2], s[t][8 * wd + 3], sc, 1);
-                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 4], s[t][8 * wd + 5], sc, 2);
-                x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[t][8 * wd + 6], s[t][8 * wd + 7], sc, 3);
-                pw[t][wd] = x;
-            }
+        for (int wd = 0; wd < 4; ++wd) {
+            // the four conversions fill the word: its old value is moot
+            uint32_t x = __builtin_bit_cast(uint32_t, s[2 * wd][0]);
+            x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[2 * wd][0], s[2 * wd][1], sc, 0);
+            x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[2 * wd][2], s[2 * wd][3], sc, 1);
+            x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[2 * wd + 1][0], s[2 * wd + 1][1], sc, 2);
+            x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[2 * wd + 1][2], s[2 * wd + 1][3], sc, 3);
+            pb[wd] = (int)x;
         }
         // accumulator units: from the previous block's r/6 (at the old maximum)
-        // to this block's
-        // (when r = 0 the maximum did not move, alpha = 1)
+        // to this block's (when r = 0 the maximum did not move, alpha = 1)
         if (r > 0.0f) {
             const float ratio = gsc * six_r * alpha;
 #pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb)
+            for (int cb = 0; cb < D / 16; ++cb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[cb][i] *= ratio;
+                for (int i = 0; i < 4; ++i) oacc[cb][i] *= ratio;
             gsc = r * (1.0f / 6.0f);
         }
-        // P.V: K-step g covers keys 64 g .. 64 g + 63; half 0 takes MX block 2 g, half 1 block 2 g + 1
+        // P.V: the lane's P codes are its 32 keys; the scale is its MX block's
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const v2i r0 = __builtin_amdgcn_permlane32_swap((int)pw[2 * g][0], (int)pw[2 * g + 1][0], false, false);
-            const v2i r1 = __builtin_amdgcn_permlane32_swap((int)pw[2 * g][1], (int)pw[2 * g + 1][1], false, false);
-            const v4i pb = {r0[0], r1[0], r0[1], r1[1]};
-            const int psc = (h ? e[2 * g + 1] : e[2 * g]) + 127;
-#pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb) {
-                const int rr = 32 * cb + lq;
-                const v4i av = *(const v4i*)(L.vc + rr * 64 + 16 * ((2 * g + h) ^ fv64(rr)));
-                oacc[cb] = mfma_f4_32x32x64(av, (int)L.vs[4 * rr + 2 * g + h], pb, psc, oacc[cb]);
-            }
+        for (int cb = 0; cb < D / 16; ++cb) {
+            const v4i av = *(const v4i*)(L.vc + voff + 256 * cb);
+            oacc[cb] = mfma_f4_16x16x128(av, (int)L.vs[vsoff + 64 * cb], pb, e + 127, oacc[cb]);
         }
         BQA_WAIT_VM(0);
         barrier_only();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    int J = next_unsel(0);
+    if (J < nJ) {
+        issue_f4_16(a, bhk, J, lds[0].f, w, l);
+        issue_bias(J, lds[0]);
+        BQA_WAIT_VM(0);
+        barrier_only();
+    }
+    while (J < nJ) {
+        int Jn = next_unsel(J + 1);
+        f4_step(I0{}, J, Jn);
         J = Jn;
-        buf ^= 1;
+        if (J >= nJ) break;
+        Jn = next_unsel(J + 1);
+        f4_step(I1{}, J, Jn);
+        J = Jn;
     }
     // back to plain units
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
+    for (int cb = 0; cb < D / 16; ++cb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[cb][i] *= gsc;
+        for (int i = 0; i < 4; ++i) oacc[cb][i] *= gsc;
 
     // ------------------------------------------------------------ bf16 path
-    const int n_items = 2 * ns;
+    // selected blocks in quarters of 32 keys, each one tile of the online softmax
+    const int n_items = 4 * ns;
     if (n_items > 0) {
-        VStage vst;
-        issue_bf(a, b, hk, sel[0] * KB, lds[0].b, w, l, tid, vst);
-        store_bf(vst, lds[0].b, tid);
+        VStageQ vst;
+        issue_bq(a, b, hk, sel[0] * KB, lds[0].b, w, l, tid, vst);
+        store_bq(vst, lds[0].b, tid);
         BQA_WAIT_VM(0);
         barrier_only();
     }
-    buf = 0;
-    const uint16_t* qh = (const uint16_t*)a.q_hi.p + b * a.q_hi.sB + hq * a.q_hi.sH + (int64_t)(row_ok ? qrow : 0) * a.q_hi.sN;
-    for (int it = 0; it < n_items; ++it) {
-        const int k0 = sel[it >> 1] * KB + HB * (it & 1);
-        VStage vst;
-        if (it + 1 < n_items) issue_bf(a, b, hk, sel[(it + 1) >> 1] * KB + HB * ((it + 1) & 1), lds[buf ^ 1].b, w, l,
-                                       tid, vst);
-        const LdsBf& L = lds[buf].b;
-        // Q in bf16, only for the selected blocks: channels 16 s + 8 h .. + 7
-        v8bf qv[8];
+    // Q in bf16, only for the selected blocks: channels 32 k + 8 g .. + 7
+    v8bf qv[4];
+    if (n_items > 0) {
+        const uint16_t* qh = (const uint16_t*)a.q_hi.p + b * a.q_hi.sB + hq * a.q_hi.sH + (int64_t)(row_ok ? qrow : 0) * a.q_hi.sN;
 #pragma unroll
-        for (int st = 0; st < 8; ++st) qv[st] = *(const v8bf*)(qh + 16 * st + 8 * h);
-        v16f s0 = v16f{}, s1 = v16f{};
+        for (int k = 0; k < 4; ++k) qv[k] = *(const v8bf*)(qh + 32 * k + 8 * g);
+    }
+    // S MFMA bb of step k reads chunk 4 k + g of key 8 (q / 4) + 4 bb + q % 4
+    // (position 16 bb + q); P.V reads chunk g of channel 16 cb + q
+    const int kq = 512 * g + 16 * q;         // + 2048 k + 256 bb
+    const int vq = 2048 * g + 16 * q;        // + 256 cb
+    auto bf_step = [&](auto slot, int it) __attribute__((always_inline)) {
+        constexpr int SB = decltype(slot)::value;
+        const int k0 = sel[it >> 2] * KB + 32 * (it & 3);
+        VStageQ vst;
+        if (it + 1 < n_items)
+            issue_bq(a, b, hk, sel[(it + 1) >> 2] * KB + 32 * ((it + 1) & 3), lds[SB ^ 1].b, w, l, tid, vst);
+        const LdsBq& L = lds[SB].b;
+        v4f s[2] = {v4f{}, v4f{}};
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            const v8bf a0 = *(const v8bf*)(L.k + krow * 256 + 16 * ((2 * st + h) ^ fk256(krow)));
-            const v8bf a1 = *(const v8bf*)(L.k + (32 + krow) * 256 + 16 * ((2 * st + h) ^ fk256(32 + krow)));
-            s0 = mfma_bf16_32x32x16(a0, qv[st], s0);
-            s1 = mfma_bf16_32x32x16(a1, qv[st], s1);
-        }
-        if (a.causal && k0 + HB - 1 > qpos_lo) {
+        for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (k0 + 16 * h + i > qpos) s0[i] = -__builtin_inff();
-                if (k0 + 32 + 16 * h + i > qpos) s1[i] = -__builtin_inff();
+            for (int bb = 0; bb < 2; ++bb) {
+                const v8bf av = *(const v8bf*)(L.k + kq + 2048 * k + 256 * bb);
+                s[bb] = mfma_bf16_16x16x32(av, qv[k], s[bb]);
             }
-        }
-        float m = __builtin_fmaxf(s0[0], s1[0]);
+        // s[bb][i] is key k0 + 8 g + 4 bb + i
+        if (a.causal && k0 + 31 > qpos_lo) {
 #pragma unroll
-        for (int i = 1; i < 16; ++i) m = __builtin_fmaxf(__builtin_fmaxf(m, s0[i]), s1[i]);
-        follow_max(oacc, l_run, m_run, __builtin_fmaxf(m_run, __builtin_fmaxf(m, partner32f(m)) * c));
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (k0 + 8 * g + 4 * bb + i > qpos) s[bb][i] = -__builtin_inff();
+        }
+        float m = max3f(max3f(s[0][0], s[0][1], s[0][2]), s[0][3], s[1][0]);
+        m = max3f(m, s[1][1], max3f(s[1][2], s[1][3], m));
+        const float m_new = max2f(m_run, quad_max16(m) * c);
+        if (__any(m_new > m_run)) {
+            const float f = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            l_run *= f;
+#pragma unroll
+            for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) oacc[cb][i] *= f;
+        }
+        m_run = m_new;
         const float mu = m_run == -__builtin_inff() ? 0.0f : m_run;
-        float ps[2] = {0.0f, 0.0f};
+        float ps[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -mu));
-            s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -mu));
-            ps[0] += s0[i];
-            ps[1] += s1[i];
+        for (int i = 0; i < 4; ++i) {
+            s[0][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][i], c, -mu));
+            s[1][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1][i], c, -mu));
+            ps[i] = s[0][i] + s[1][i];
         }
-        l_run += ps[0] + ps[1];
-        // P.V in bf16: step st covers keys 32 (st / 2) + 16 h + 8 (st % 2) + e
+        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        // P.V in bf16: the lane's keys 8 g + j of the quarter
+        v8bf pbf;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            v8bf pbf;
+        for (int j = 0; j < 8; ++j) pbf[j] = (__bf16)s[j >> 2][j & 3];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pbf[e] = (__bf16)(st < 2 ? s0[8 * (st % 2) + e] : s1[8 * (st % 2) + e]);
-#pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb) {
-                const int rr = 32 * cb + lq;
-                const v8bf av = *(const v8bf*)(L.vt + rr * 128 + 16 * ((4 * (st / 2) + 2 * h + (st % 2)) ^ fv128(rr)));
-                oacc[cb] = mfma_bf16_32x32x16(av, pbf, oacc[cb]);
-            }
+        for (int cb = 0; cb < D / 16; ++cb) {
+            const v8bf av = *(const v8bf*)(L.vt + vq + 256 * cb);
+            oacc[cb] = mfma_bf16_16x16x32(av, pbf, oacc[cb]);
         }
-        if (it + 1 < n_items) store_bf(vst, lds[buf ^ 1].b, tid);
+        if (it + 1 < n_items) store_bq(vst, lds[SB ^ 1].b, tid);
         BQA_WAIT_VM(0);
         barrier_only();
-        buf ^= 1;
-        (void)k0;
+    };
+    for (int it = 0; it < n_items; it += 2) {
+        bf_step(I0{}, it);
+        bf_step(I1{}, it + 1);
     }
 
-    const float l_tot = l_run + partner32f(l_run);
+    const float l_tot = quad_sum16(l_run);
     if (!row_ok) return;
     const float inv_l = 1.0f / l_tot;
     uint16_t* orow = (uint16_t*)a.o.p + b * a.o.sB + hq * a.o.sH + (int64_t)qrow * a.o.sN;
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) {
+    for (int cb = 0; cb < D / 16; ++cb) {
+        uint16_t o4[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int ch0 = 32 * cb + 8 * g + 4 * h;
-            uint16_t o4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o4[e] = f32_to_bf16_bits(oacc[cb][4 * g + e] * inv_l);
-            *(uint2*)(orow + ch0) =
-                make_uint2((uint32_t)o4[0] | ((uint32_t)o4[1] << 16), (uint32_t)o4[2] | ((uint32_t)o4[3] << 16));
-        }
+        for (int i = 0; i < 4; ++i) o4[i] = f32_to_bf16_bits(oacc[cb][i] * inv_l);
+        *(uint2*)(orow + 16 * cb + 4 * g) =
+            make_uint2((uint32_t)o4[0] | ((uint32_t)o4[1] << 16), (uint32_t)o4[2] | ((uint32_t)o4[3] << 16));
     }
-    if (a.lse && h == 0) a.lse[(int64_t)bh * a.Nq + qrow] = m_run * 0.6931471805599453f + __logf(l_tot);
+    if (a.lse && g == 0) a.lse[(int64_t)bh * a.Nq + qrow] = m_run * 0.6931471805599453f + __logf(l_tot);
 }
 
 // Score shifts of the post-training baseline: bias[b, hq, I, j] =
@@ -662,7 +721,7 @@ hipError_t launch_thrift_nv(const ThriftFwdArgs& a, hipStream_t st) {
 
 hipError_t launch_thrift_fwd(const ThriftFwdArgs& a, hipStream_t st) {
     const int grid = a.B * a.Hq * ((a.Nq + BM - 1) / BM);
-    thrift_fwd_kernel<false><<<grid, 256, 0, st>>>(a);
+    thrift_fwd_kernel<false><<<grid, 512, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -675,7 +734,7 @@ hipError_t launch_ptq_fwd(ThriftFwdArgs a, const float* qbar, void* ws, hipStrea
     float* bias = (float*)ws;
     ptq_bias_kernel<<<a.B * a.Hq * (a.Nk / KB), 256, 0, st>>>(a.kc, a.ks, qbar, a.Hq, a.Hkv, nqb, a.Nk, bias);
     a.sbias = bias;
-    thrift_fwd_kernel<true><<<a.B * a.Hq * nqb, 256, 0, st>>>(a);
+    thrift_fwd_kernel<true><<<a.B * a.Hq * nqb, 512, 0, st>>>(a);
     return hipGetLastError();
 }
 

@@ -2,7 +2,7 @@
 //
 // Everything here is written for CDNA4 (gfx950) only: 64-lane wavefronts,
 // the gfx950 matrix instructions (i8 32x32x32, scaled f8f6f4 32x32x64 /
-// 16x16x128, bf16/f16 32x32x16) and permlane32_swap.
+// 16x16x128, bf16/f16 32x32x16, bf16 16x16x32) and the permlane swaps.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -109,6 +109,19 @@ __device__ __forceinline__ v16f mfma_f4_32x32x64(v4i a, int sa, v4i b, int sb, v
     v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
 }
+// The same at 16 x 16 x 128: lane l supplies row (A) or column (B) l % 16,
+// elements 32 (l / 16) .. + 31, with that block's scale byte; lane l of the
+// result holds column l % 16, rows 4 (l / 16) .. + 3.
+__device__ __forceinline__ v4f mfma_f4_16x16x128(v4i a, int sa, v4i b, int sb, v4f c) {
+    v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+    v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
+}
+// bf16 16 x 16 x 32: lane l supplies row (A) or column (B) l % 16, elements
+// 8 (l / 16) .. + 7; the result is laid out as above.
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(v8bf a, v8bf b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ v16f mfma_bf16_32x32x16(v8bf a, v8bf b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -170,6 +183,43 @@ __device__ __forceinline__ float partner16f(float x) {
     const int b = __builtin_bit_cast(int, x);
     v2i r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
     return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
+}
+// v_max3_f32 as written: __builtin_fmaxf on values the compiler cannot prove
+// canonical (matrix results) costs an extra v_max x, x per operand.  Only for
+// values that are never NaN.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+// Maximum (of values that are never NaN) and sum over the four lanes
+// l % 16 + 16 k of a wavefront (whole wavefront active): each swap hands
+// every lane its partner's value in one of the two registers, so the result
+// needs no select.
+__device__ __forceinline__ float quad_max16(float x) {
+    int b = __builtin_bit_cast(int, x);
+    v2i r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    const int r0 = r[0], r1 = r[1];
+    x = max2f(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+    b = __builtin_bit_cast(int, x);
+    r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    const int t0 = r[0], t1 = r[1];
+    return max2f(__builtin_bit_cast(float, t0), __builtin_bit_cast(float, t1));
+}
+__device__ __forceinline__ float quad_sum16(float x) {
+    int b = __builtin_bit_cast(int, x);
+    v2i r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    const int r0 = r[0], r1 = r[1];
+    x = __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+    b = __builtin_bit_cast(int, x);
+    r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    const int t0 = r[0], t1 = r[1];
+    return __builtin_bit_cast(float, t0) + __builtin_bit_cast(float, t1);
 }
 // x of another lane of the same row of 16 by a DPP pattern (whole wave active)
 template <int CTRL>

@@ -160,7 +160,7 @@ class _ThriftOracle:
         idx, cnt = self.sel[iq]
         return orc.thrift_fwd(qc=self.qc[iq], qs=self.qs[iq], kc=self.kc[ik], ks=self.ks[ik], vc_t=self.vc[ik],
                               vs_t=self.vs[ik], Qh=self.Q[iq], Kh=self.K[ik], Vh=self.V[ik], sel_idx=idx, sel_cnt=cnt,
-                              Nq=self.Nq, Nk=self.Nk, d=self.d, blk=128, hp_tile=64, causal=self.causal,
+                              Nq=self.Nq, Nk=self.Nk, d=self.d, blk=128, hp_tile=32, causal=self.causal,
                               tau=tau_for(self.d),
                               qblocks=qblocks)
 
@@ -292,7 +292,7 @@ def test_thrift_prefill_full_size_sampled():
         assert_same(path.sel_idx[0, h].cpu().numpy(), idx, f"selection of head {h}")
         for qb in (0, 517, 1023):
             ref, lse = orc.thrift_fwd(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0], Qh=Qh, Kh=Kh, Vh=Vh,
-                                      sel_idx=idx, sel_cnt=rc, Nq=w.Nq, Nk=w.Nk, d=w.d, blk=128, hp_tile=64,
+                                      sel_idx=idx, sel_cnt=rc, Nq=w.Nq, Nk=w.Nk, d=w.d, blk=128, hp_tile=32,
                                       causal=True,
                                       tau=tau_for(w.d), qblocks=(qb, qb + 1))
             compare_outputs(O[h, 128 * qb:128 * qb + 128], ref, "bf16", what=f"O[h={h}, query block {qb}]")
