@@ -656,6 +656,25 @@ def probe_main(torch, bqa):
         "hidden_exp_share": round((iss["mfma"] + iss["exp"] - iss["mfma_exp"]) / min(iss["mfma"], iss["exp"]), 3),
         "note": "hidden share = (separate sum - mixed) / the shorter part: 1 if the shorter part runs entirely "
                 "under the longer one, 0 if the two only add up"}
+    # vector work under vector work: the multiply-adds and exponentials of a round interleaved
+    t = timed(lambda: bqa.bqa_debug_probe(bqa.BQA_PROBE_ISSUE_EXP_FMA, g2, it2, None, out, out.numel()))
+    ef = t / it2 / 2 * 1e9
+    res["vector_overlap"] = {
+        "unit": "ns per wavefront round (SIMD time, 2 wavefronts per SIMD)",
+        "round": "64 fp32 multiply-adds and 32 v_exp_f32 on independent chains, interleaved",
+        "fma": round(iss["fma"], 2), "exp": round(iss["exp"], 2), "fma_exp": round(ef, 2),
+        "hidden_share": round((iss["fma"] + iss["exp"] - ef) / min(iss["fma"], iss["exp"]), 3)}
+    # LDS: 16-byte reads with every 16-lane group on its own span, or the four groups on one set of rows
+    lds = {}
+    for name, kind in (("spans", bqa.BQA_PROBE_LDS_SPANS), ("shared_rows", bqa.BQA_PROBE_LDS_SHARED_ROWS)):
+        t = timed(lambda: bqa.bqa_debug_probe(kind, g2, 20000, None, out, out.numel()))
+        lds[name] = round(t / 20000 / 8 / 2 * 1e9, 3)      # per wavefront read, 2 wavefronts per SIMD
+    res["lds_read_b128"] = {
+        "unit": "ns per wavefront 16-byte read (SIMD time, 2 wavefronts per SIMD, 8 reads per round)",
+        "layouts": "spans: lane 16 g + q reads entry q of group g's own 256-byte span; shared_rows: chunk "
+                   "g ^ (q / 4) of 64-byte row q (the four groups read different chunks of the same rows); "
+                   "every group of 16 lanes covers all 64 banks in both",
+        **lds, "ratio": round(lds["shared_rows"] / lds["spans"], 3)}
     # issue cost of single vector instructions: ns of SIMD time per wavefront instruction
     ops = {}
     for name, kind in (("v_mul_f32", bqa.BQA_PROBE_OP_MUL), ("v_fma_f32", bqa.BQA_PROBE_OP_FMA),

@@ -38,7 +38,8 @@ EXPORTS = ["bqa_abi_version", "bqa_status_string", "bqa_workspace_size", "bqa_qu
 BQA_PROBE_MFMA_I8, BQA_PROBE_MFMA_F8, BQA_PROBE_MFMA_F4, BQA_PROBE_MFMA_BF16, BQA_PROBE_EXP, BQA_PROBE_COPY, \
     BQA_PROBE_READ, BQA_PROBE_READ_NT, BQA_PROBE_ISSUE_MFMA, BQA_PROBE_ISSUE_FMA, BQA_PROBE_ISSUE_MFMA_FMA, \
     BQA_PROBE_ISSUE_EXP, BQA_PROBE_ISSUE_MFMA_EXP, BQA_PROBE_OP_MUL, BQA_PROBE_OP_FMA, BQA_PROBE_OP_CVT_F32_I32, \
-    BQA_PROBE_OP_MAX3, BQA_PROBE_OP_CVT_PK_FP8, BQA_PROBE_OP_CVT_PK_FP4, BQA_PROBE_OP_PERMLANE32 = range(20)
+    BQA_PROBE_OP_MAX3, BQA_PROBE_OP_CVT_PK_FP8, BQA_PROBE_OP_CVT_PK_FP4, BQA_PROBE_OP_PERMLANE32, \
+    BQA_PROBE_ISSUE_EXP_FMA, BQA_PROBE_LDS_SHARED_ROWS, BQA_PROBE_LDS_SPANS = range(23)
 
 
 class BqaError(RuntimeError):

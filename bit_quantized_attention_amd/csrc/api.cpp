@@ -708,7 +708,7 @@ extern "C" bqa_status bqa_debug_mx_dequant(const void* codes, const void* scales
 
 extern "C" bqa_status bqa_debug_probe(int32_t kind, int32_t grid, int64_t iters, const void* src, void* dst,
                                       size_t bytes, void* stream) {
-    if (kind < BQA_PROBE_MFMA_I8 || kind > BQA_PROBE_OP_PERMLANE32) return BQA_E_UNSUPPORTED;
+    if (kind < BQA_PROBE_MFMA_I8 || kind > BQA_PROBE_LDS_SPANS) return BQA_E_UNSUPPORTED;
     if (grid < 1 || grid > (1 << 20) || iters < 0 || iters > ((int64_t)1 << 30)) return BQA_E_SHAPE;
     if (!dst) return BQA_E_NULL;
     if (kind == BQA_PROBE_COPY) {

@@ -176,7 +176,7 @@ enum { PROBE_MFMA_I8 = 0, PROBE_MFMA_F8 = 1, PROBE_MFMA_F4 = 2, PROBE_MFMA_BF16 
        PROBE_READ = 6, PROBE_READ_NT = 7, PROBE_ISSUE_MFMA = 8, PROBE_ISSUE_FMA = 9, PROBE_ISSUE_MFMA_FMA = 10,
        PROBE_ISSUE_EXP = 11, PROBE_ISSUE_MFMA_EXP = 12, PROBE_OP_MUL = 13, PROBE_OP_FMA = 14,
        PROBE_OP_CVT_F32_I32 = 15, PROBE_OP_MAX3 = 16, PROBE_OP_CVT_PK_FP8 = 17, PROBE_OP_CVT_PK_FP4 = 18,
-       PROBE_OP_PERMLANE32 = 19 };
+       PROBE_OP_PERMLANE32 = 19, PROBE_ISSUE_EXP_FMA = 20, PROBE_LDS_SHARED_ROWS = 21, PROBE_LDS_SPANS = 22 };
 hipError_t launch_probe(int kind, int grid, int64_t iters, const void* src, void* dst, size_t bytes, hipStream_t st);
 
 }  // namespace bqa

@@ -18,8 +18,12 @@
 //    matrix instructions (four accumulator chains), 64 independent fp32
 //    fused multiply-adds, 32 independent v_exp_f32, or the matrix
 //    instructions interleaved with either (one matrix instruction, then 8
-//    multiply-adds or 4 exponentials): the mixed time against the sum of the
-//    separate ones says how much vector work runs under matrix work;
+//    multiply-adds or 4 exponentials), or the multiply-adds interleaved with
+//    the exponentials: the mixed time against the sum of the separate ones
+//    says how much of one kind of work runs under the other;
+//  * LDS read probes: 8 back-to-back 16-byte reads per round, with each
+//    group of 16 lanes on its own 256-byte span or the four groups on
+//    different chunks of the same 64-byte rows;
 //  * instruction probes: 64 instances per round of one vector instruction
 //    (fp32 multiply, multiply-add, int->float conversion, v_max3, fp8 pack,
 //    scaled fp4 pack, permlane32 swap) over 16 independent chains.
@@ -144,18 +148,23 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const v4i* __restrict__
 }
 
 // Issue probes: MODE 0 matrix only, 1 multiply-adds only, 2 both, 3
-// exponentials only, 4 matrix and exponentials.
+// exponentials only, 4 matrix and exponentials, 5 multiply-adds and
+// exponentials (the multiply-adds on chains of their own).
 template <int MODE>
 __global__ __launch_bounds__(256) void issue_probe_kernel(int64_t iters, uint32_t* __restrict__ out) {
     const int l = threadIdx.x & 63;
     const int seed = (int)(threadIdx.x * 2654435761u + blockIdx.x);
     const v4i a4 = {seed & 0x07070707, (seed >> 1) & 0x07070707, 0x01020304, l};
     v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
-    float x[16];
+    float x[16], y[16];
     const float fa = 0.5f + (float)(l & 7) * (1.0f / 1024.0f);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) x[k] = (float)((threadIdx.x + 37 * k) & 63) * (1.0f / 64.0f) + 0.25f;
-    constexpr bool MF = MODE == 0 || MODE == 2 || MODE == 4, FM = MODE == 1 || MODE == 2, EX = MODE == 3 || MODE == 4;
+    for (int k = 0; k < 16; ++k) {
+        x[k] = (float)((threadIdx.x + 37 * k) & 63) * (1.0f / 64.0f) + 0.25f;
+        y[k] = x[k] * 0.5f;
+    }
+    constexpr bool MF = MODE == 0 || MODE == 2 || MODE == 4, FM = MODE == 1 || MODE == 2 || MODE == 5,
+                   EX = MODE == 3 || MODE == 4 || MODE == 5;
     for (int64_t it = 0; it < iters; ++it) {
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
@@ -167,7 +176,7 @@ __global__ __launch_bounds__(256) void issue_probe_kernel(int64_t iters, uint32_
             }
             if constexpr (FM) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k) x[(8 * g + k) & 15] = __builtin_fmaf(x[(8 * g + k) & 15], fa, 0.25f);
+                for (int k = 0; k < 8; ++k) y[(8 * g + k) & 15] = __builtin_fmaf(y[(8 * g + k) & 15], fa, 0.25f);
             }
             if constexpr (EX) {
 #pragma unroll
@@ -181,12 +190,49 @@ __global__ __launch_bounds__(256) void issue_probe_kernel(int64_t iters, uint32_
     }
     float s = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) s += x[k];
+    for (int k = 0; k < 16; ++k) s += x[k] + y[k];
     uint32_t sum = __builtin_bit_cast(uint32_t, s);
 #pragma unroll
     for (int i = 0; i < 16; ++i) sum += (uint32_t)(c0[i] ^ c1[i] ^ c2[i] ^ c3[i]);
     sum = (uint32_t)wave_max((float)(sum & 0xFFFF));
     if (threadIdx.x == 0) out[blockIdx.x] = sum;
+}
+
+// LDS read probes: every wavefront runs iters rounds of 8 independent 16-byte
+// reads issued back to back (8 KB apart), then one wait.  Lane l = 16 g + q.
+// SPANS: group g reads entry q of its own contiguous 256-byte span
+// (2048 g + 16 q); SHARED_ROWS: group g reads chunk g ^ (q / 4) of the
+// 64-byte row q, so that the four groups read different chunks of the same
+// 16 rows.  In both, every group of 16 lanes covers all 64 banks once.
+template <bool SPANS>
+__global__ __launch_bounds__(256) void lds_probe_kernel(int64_t iters, uint32_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) v4i buf[4096];   // 64 KB
+    for (int i = threadIdx.x; i < 4096; i += 256) buf[i] = v4i{i, i + 1, i + 2, i + 3};
+    __syncthreads();
+    const int l = threadIdx.x & 63, g = l >> 4, q = l & 15;
+    const int off = SPANS ? 2048 * g + 16 * q : 64 * q + 16 * (g ^ ((q >> 2) & 3));   // below 8 KB
+    const uint32_t a = lds_addr(buf) + (uint32_t)off;
+    v4i acc = {0, 0, 0, 0};
+    for (int64_t it = 0; it < iters; ++it) {
+        v4i r0, r1, r2, r3, r4, r5, r6, r7;
+        asm volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %8 offset:8192\n\t"
+            "ds_read_b128 %2, %8 offset:16384\n\t"
+            "ds_read_b128 %3, %8 offset:24576\n\t"
+            "ds_read_b128 %4, %8 offset:32768\n\t"
+            "ds_read_b128 %5, %8 offset:40960\n\t"
+            "ds_read_b128 %6, %8 offset:49152\n\t"
+            "ds_read_b128 %7, %8 offset:57344\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+            : "v"(a)
+            : "memory");
+        acc ^= r0 ^ r1 ^ r2 ^ r3 ^ r4 ^ r5 ^ r6 ^ r7;
+    }
+    const uint32_t sum = (uint32_t)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+    const uint32_t m = (uint32_t)wave_max((float)(sum & 0xFFFF));
+    if (threadIdx.x == 0) out[blockIdx.x] = m;
 }
 
 // Single-instruction issue probes: every round, each lane runs 64 instances
@@ -258,6 +304,9 @@ hipError_t launch_probe(int kind, int grid, int64_t iters, const void* src, void
         case PROBE_OP_CVT_PK_FP8: op_probe_kernel<4><<<grid, 256, 0, st>>>(iters, out); break;
         case PROBE_OP_CVT_PK_FP4: op_probe_kernel<5><<<grid, 256, 0, st>>>(iters, out); break;
         case PROBE_OP_PERMLANE32: op_probe_kernel<6><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_ISSUE_EXP_FMA: issue_probe_kernel<5><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_LDS_SHARED_ROWS: lds_probe_kernel<false><<<grid, 256, 0, st>>>(iters, out); break;
+        case PROBE_LDS_SPANS: lds_probe_kernel<true><<<grid, 256, 0, st>>>(iters, out); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

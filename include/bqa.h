@@ -462,14 +462,21 @@ bqa_status bqa_debug_mx_dequant(const void* codes, const void* scales, int64_t n
  * conversion (BQA_PROBE_OP_CVT_F32_I32), v_max3_f32 (BQA_PROBE_OP_MAX3), the
  * packed fp8 conversion (BQA_PROBE_OP_CVT_PK_FP8), the scaled packed fp4
  * conversion (BQA_PROBE_OP_CVT_PK_FP4), v_permlane32_swap
- * (BQA_PROBE_OP_PERMLANE32).
+ * (BQA_PROBE_OP_PERMLANE32).  BQA_PROBE_ISSUE_EXP_FMA (same arguments): the
+ * 64 multiply-adds and the 32 v_exp_f32 of a round interleaved, on chains of
+ * their own.  LDS read probes (same arguments): every wavefront runs iters
+ * rounds of 8 back-to-back 16-byte LDS reads; lane 16 g + q reads entry q of
+ * its group's own 256-byte span (BQA_PROBE_LDS_SPANS) or chunk g ^ (q / 4) of
+ * the 64-byte row q, the four groups sharing the rows
+ * (BQA_PROBE_LDS_SHARED_ROWS).
  */
 enum {
     BQA_PROBE_MFMA_I8 = 0, BQA_PROBE_MFMA_F8 = 1, BQA_PROBE_MFMA_F4 = 2, BQA_PROBE_MFMA_BF16 = 3,
     BQA_PROBE_EXP = 4, BQA_PROBE_COPY = 5, BQA_PROBE_READ = 6, BQA_PROBE_READ_NT = 7,
     BQA_PROBE_ISSUE_MFMA = 8, BQA_PROBE_ISSUE_FMA = 9, BQA_PROBE_ISSUE_MFMA_FMA = 10, BQA_PROBE_ISSUE_EXP = 11,
     BQA_PROBE_ISSUE_MFMA_EXP = 12, BQA_PROBE_OP_MUL = 13, BQA_PROBE_OP_FMA = 14, BQA_PROBE_OP_CVT_F32_I32 = 15,
-    BQA_PROBE_OP_MAX3 = 16, BQA_PROBE_OP_CVT_PK_FP8 = 17, BQA_PROBE_OP_CVT_PK_FP4 = 18, BQA_PROBE_OP_PERMLANE32 = 19
+    BQA_PROBE_OP_MAX3 = 16, BQA_PROBE_OP_CVT_PK_FP8 = 17, BQA_PROBE_OP_CVT_PK_FP4 = 18, BQA_PROBE_OP_PERMLANE32 = 19,
+    BQA_PROBE_ISSUE_EXP_FMA = 20, BQA_PROBE_LDS_SHARED_ROWS = 21, BQA_PROBE_LDS_SPANS = 22
 };
 bqa_status bqa_debug_probe(int32_t kind, int32_t grid, int64_t iters, const void* src, void* dst, size_t bytes,
                            void* stream);

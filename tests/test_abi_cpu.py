@@ -295,7 +295,7 @@ def test_ptq_validation(L):
 
 def test_probe_validation(L):
     P = bqa.lib().bqa_debug_probe
-    assert P(20, 16, 10, None, 0x1000, 4096, None) == bqa.BQA_E_UNSUPPORTED
+    assert P(23, 16, 10, None, 0x1000, 4096, None) == bqa.BQA_E_UNSUPPORTED
     assert P(-1, 16, 10, None, 0x1000, 4096, None) == bqa.BQA_E_UNSUPPORTED
     assert P(bqa.BQA_PROBE_MFMA_I8, 0, 10, None, 0x1000, 4096, None) == bqa.BQA_E_SHAPE
     assert P(bqa.BQA_PROBE_MFMA_I8, 16, -1, None, 0x1000, 4096, None) == bqa.BQA_E_SHAPE
@@ -311,7 +311,7 @@ def test_probe_validation(L):
     assert P(bqa.BQA_PROBE_READ_NT, 16, 0, None, 0x1000, 4096, None) == bqa.BQA_E_NULL
     assert _nodev(P(bqa.BQA_PROBE_READ_NT, 16, 0, 0x2000, 0x1000, 4096, None))
     assert P(bqa.BQA_PROBE_ISSUE_MFMA_EXP, 2048, 10, None, 0x1000, 4096, None) == bqa.BQA_E_SHAPE
-    for kind in range(bqa.BQA_PROBE_ISSUE_MFMA, bqa.BQA_PROBE_OP_PERMLANE32 + 1):
+    for kind in range(bqa.BQA_PROBE_ISSUE_MFMA, bqa.BQA_PROBE_LDS_SPANS + 1):
         assert _nodev(P(kind, 16, 10, None, 0x1000, 4096, None))
     assert _nodev(P(bqa.BQA_PROBE_MFMA_F4, 16, 10, None, 0x1000, 4096, None))
     assert _nodev(P(bqa.BQA_PROBE_COPY, 16, 0, 0x2000, 0x1000, 4096, None))

@@ -69,7 +69,7 @@ def test_copy_probe(grid, n16):
 def test_compute_probes_write_every_word():
     import bit_quantized_attention_amd as bqa
     kinds = [bqa.BQA_PROBE_MFMA_I8, bqa.BQA_PROBE_MFMA_F8, bqa.BQA_PROBE_MFMA_F4, bqa.BQA_PROBE_MFMA_BF16,
-             bqa.BQA_PROBE_EXP] + list(range(bqa.BQA_PROBE_ISSUE_MFMA, bqa.BQA_PROBE_OP_PERMLANE32 + 1))
+             bqa.BQA_PROBE_EXP] + list(range(bqa.BQA_PROBE_ISSUE_MFMA, bqa.BQA_PROBE_LDS_SPANS + 1))
     grid = 9
     for kind in kinds:
         dst = torch.full((grid + 1,), -1, dtype=torch.int32, device="cuda")
