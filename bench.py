@@ -133,10 +133,11 @@ def cpu_baseline(w, budget_s: float = 20.0):
                       f"{dt:.1f} s"}
 
 
-def cpu_baseline_qat(w, budget_s: float = 20.0):
+def cpu_baseline_qat(w, budget_s: float = 20.0, kv_tile: int = 64):
     """The oracle on a bounded sample of the Attn-QAT forward: MXFP4
     quantisation of one whole head, then its forward (O and O') over chunks of
-    query rows until the time budget is spent."""
+    query rows until the time budget is spent; key tiles of kv_tile as the
+    kernel timed (64 for the forward with O', 128 without)."""
     import oracle
     import workloads as wl
     from tests.helpers import tau_for
@@ -150,7 +151,7 @@ def cpu_baseline_qat(w, budget_s: float = 20.0):
     rows, r0, chunk = 0, 0, 16
     while r0 < w.Nq and time.perf_counter() - t0 < budget_s:
         oracle.qat_fwd(qc=qc[0], qs=qs[0], kc=kc[0], ks=ks[0], vc_t=vc[0], vs_t=vs[0], Nq=w.Nq, Nk=w.Nk, d=w.d,
-                       tau=tau_for(w.d), kv_tile=64, rows=(r0, r0 + chunk))
+                       tau=tau_for(w.d), kv_tile=kv_tile, rows=(r0, r0 + chunk))
         rows += chunk
         r0 += chunk
     dt = time.perf_counter() - t0
@@ -191,12 +192,12 @@ def _qat_case(w, bqa, torch):
         path=path, ops=ops, dtype="mxfp4+bf16",
         workload="Attn-QAT FP4 forward (c4): B=1 H=32 N=16384 d=128 non-causal, Student-t bf16 in, MXFP4 Q/K/V/P, "
                  "bf16 auxiliary output O'; step = quantise Q,K,V + attention",
-        roofline={"bound": "mfma", "kernel": "attn_fwd QAT (vdeq_kernel + qat_fwd_kernel<aux>): MXFP4 QK^T and "
+        roofline={"bound": "mfma", "kernel": "attn_fwd QAT (vdeq_kernel + qat_aux_kernel): MXFP4 QK^T and "
                                              "P.V plus bf16 O'",
                   "peak": round((ops + aux) / t_peak / 1e12, 1), "peak_note": "fp4 and bf16 dense peaks "
                   "weighted by each product's share of the operations",
                   "ops_per_launch": ops + aux},
-        traffic_key="qat_fwd_kernel<aux>", cpu=cpu_baseline_qat)
+        traffic_key="qat_aux_kernel", cpu=cpu_baseline_qat)
 
 
 def cpu_baseline_ptq(w, budget_s: float = 20.0):
@@ -256,9 +257,9 @@ def _qat_infer_case(w, bqa, torch):
         path=path, ops=ops, dtype="mxfp4",
         workload="Attn-QAT FP4 inference forward (c4i): B=1 H=32 N=16384 d=128 non-causal, Student-t bf16 in, MXFP4 "
                  "Q/K/V/P, no auxiliary output; step = quantise Q,K,V + attention",
-        roofline={"bound": "mfma", "kernel": "attn_fwd QAT without O' (qat_fwd_kernel<false>): MXFP4 QK^T and P.V",
+        roofline={"bound": "mfma", "kernel": "attn_fwd QAT without O' (qat_fwd_kernel): MXFP4 QK^T and P.V",
                   "peak": PEAK_F4_TFLOPS, "ops_per_launch": ops},
-        traffic_key="qat_fwd_kernel<false>", cpu=cpu_baseline_qat)
+        traffic_key="qat_fwd_kernel", cpu=lambda w: cpu_baseline_qat(w, kv_tile=128))
 
 
 def _thrift_pairs(path, w):

@@ -356,7 +356,7 @@ bqa_status bqa_attn_fwd(const bqa_problem* p, const bqa_qtensor* q, const bqa_qt
                                     dbg16(v_hi, p->B, p->Hkv, p->Nk, p->d)});
     };
     if (p->mode == BQA_QAT_MXFP4) {
-        if (p->d != 128 || p->causal || p->Nk % 64 != 0) return BQA_E_UNSUPPORTED;
+        if (p->d != 128 || p->causal || p->Nk % 128 != 0) return BQA_E_UNSUPPORTED;
         TRY(check_q(q, BQA_MXFP4, 0));
         TRY(check_q(k, BQA_MXFP4, 0));
         TRY(check_q(v, BQA_MXFP4, 1));

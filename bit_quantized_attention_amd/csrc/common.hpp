@@ -184,19 +184,14 @@ __device__ __forceinline__ float partner16f(float x) {
     v2i r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
     return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
 }
-// v_max3_f32 as written: __builtin_fmaxf on values the compiler cannot prove
-// canonical (matrix results) costs an extra v_max x, x per operand.  Only for
-// values that are never NaN.
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-__device__ __forceinline__ float max2f(float a, float b) {
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
+// Maxima of values that are never NaN.  Written with the compiler's own
+// maximum (which the backend fuses into v_max3_f32), never as inline
+// assembly: the hardware does not interlock a vector read of a matrix
+// instruction's result, and the compiler inserts the wait states such a read
+// needs only for its own instructions.  The kernels that use them are built
+// with -fno-honor-nans, so no canonicalising v_max x, x precede them.
+__device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
+__device__ __forceinline__ float max2f(float a, float b) { return __builtin_fmaxf(a, b); }
 // Maximum (of values that are never NaN) and sum over the four lanes
 // l % 16 + 16 k of a wavefront (whole wavefront active): each swap hands
 // every lane its partner's value in one of the two registers, so the result

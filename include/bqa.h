@@ -296,7 +296,7 @@ bqa_status bqa_select_blocks(const bqa_problem* p, const float* q_means, const f
  *    NULL).
  *    Key tiles of k_block, ascending (causal: up to the row's diagonal).
  *  - BQA_QAT_MXFP4 ("Attn-QAT", §2): q, k MXFP4 along d, v MXFP4 along tokens;
- *    d = 128, non-causal, Nk a multiple of 64.  Key tiles of 64, ascending;
+ *    d = 128, non-causal, Nk a multiple of 128.  Key tiles of 128, ascending;
  *    P is made MXFP4 per 32 keys of the row for O (no smoothing or two-level
  *    step, §2 Implementation).  When o_aux is not NULL, O' = sum bf16(P) V / l
  *    is written too (Principle 2); this needs a workspace of

@@ -161,6 +161,8 @@ def test_fwd_validation(L):
     assert fwd(_p(), o=_dense(dtype=bqa.BQA_FP16)) == bqa.BQA_E_UNSUPPORTED
     assert fwd(_p(mode=bqa.BQA_SAGE_I8_F16PV), v=None) == bqa.BQA_E_NULL
     assert fwd(_p(mode=9)) == bqa.BQA_E_UNSUPPORTED
+    # Attn-QAT: key tiles of 128, so Nk a multiple of 128
+    assert fwd(_p(mode=bqa.BQA_QAT_MXFP4, causal=0, Nq=320, Nk=320)) == bqa.BQA_E_UNSUPPORTED
 
     def fwd_qhi(p, q=q, q_hi=_dense(ptr=0x60000)):
         return bqa.lib().bqa_attn_fwd(C.byref(p), None if q is None else C.byref(q), C.byref(k), C.byref(v),

@@ -40,10 +40,12 @@ class _Oracle:
         self.kc, self.ks = orc.quant_mx_rows(K.reshape(-1, self.Nk, self.d))
         self.vc, self.vs = orc.quant_mx_cols(V.reshape(-1, self.Nk, self.d))
 
-    def forward(self, b, h, rows=None, return_rowmax=False):
+    def forward(self, b, h, rows=None, return_rowmax=False, kv_tile=64):
+        """kv_tile: keys per online-softmax tile of the kernel compared against
+        (64 for the forward with O', 128 for the inference forward)."""
         iq, ik = b * self.Hq + h, b * self.Hkv + h // (self.Hq // self.Hkv)
         return orc.qat_fwd(qc=self.qc[iq], qs=self.qs[iq], kc=self.kc[ik], ks=self.ks[ik], vc_t=self.vc[ik],
-                           vs_t=self.vs[ik], Nq=self.Nq, Nk=self.Nk, d=self.d, tau=tau_for(self.d), kv_tile=64,
+                           vs_t=self.vs[ik], Nq=self.Nq, Nk=self.Nk, d=self.d, tau=tau_for(self.d), kv_tile=kv_tile,
                            rows=rows, return_rowmax=return_rowmax)
 
 
@@ -51,9 +53,10 @@ def _check(path, oc, heads, rows=None):
     O = path.o.float().cpu().numpy()
     Oa = path.oa.float().cpu().numpy() if path.oa is not None else None
     L = path.lse.cpu().numpy()
+    kv_tile = 64 if Oa is not None else 128
     for b, h in heads:
         r = rows or (0, oc.Nq)
-        ref, ref_aux, lse = oc.forward(b, h, rows=r)
+        ref, ref_aux, lse = oc.forward(b, h, rows=r, kv_tile=kv_tile)
         compare_outputs(O[b, h, r[0]:r[1]], ref, "bf16", what=f"O[b={b},h={h},rows={r}]")
         if Oa is not None:
             compare_outputs(Oa[b, h, r[0]:r[1]], ref_aux, "bf16", what=f"O'[b={b},h={h},rows={r}]")
@@ -65,11 +68,11 @@ def _fits_f32(x: float) -> bool:
 
 
 def test_mx_scores_tile():
-    """One 32 x 32 tile of raw MXFP4 scores from the forward's tile code.  The
-    tile code runs two scaled instructions of 64 channels each; where the
-    oracle's exact rational score and the first instruction's exact partial
-    sum are both fp32 values, the result is compared bit for bit; elsewhere
-    within the rounding of one fp32 addition of the two partials."""
+    """One 32 x 32 tile of raw MXFP4 scores from the forward's tile code (one
+    scaled 16x16x128 instruction per 16 keys over all 128 channels).  Where
+    the oracle's exact rational score and its 64-channel partial sum are both
+    fp32 values, the result is compared bit for bit; elsewhere within the
+    rounding of one fp32 addition of two 64-channel partials."""
     import bit_quantized_attention_amd as bqa
     w = wl.with_len(wl.WORKLOADS["c4"], 256, hq=2, hkv=2)
     p, path, (Q, K, V) = _run(w)
@@ -98,32 +101,38 @@ def test_mx_scores_tile():
     assert n_exact > 1000
 
 
-@pytest.mark.parametrize("Nq,Nk,hq,hkv", [(512, 512, 2, 2), (1000, 1024, 4, 2), (64, 384, 1, 1)])
-def test_qat_forward_small(Nq, Nk, hq, hkv):
+@pytest.mark.parametrize("aux", [True, False], ids=["with_aux", "inference"])
+@pytest.mark.parametrize("Nq,Nk,hq,hkv", [(512, 512, 2, 2), (1000, 1024, 4, 2), (64, 384, 1, 1), (200, 128, 2, 1)])
+def test_qat_forward_small(Nq, Nk, hq, hkv, aux):
     """c4 recipe at sizes spanning several tiles: ragged query count, grouped
-    heads, a single partial query tile."""
+    heads, a single partial query tile, a single key tile; the forward with O'
+    (tiles of 64 keys) and the inference forward (tiles of 128)."""
     w = wl.with_len(wl.WORKLOADS["c4"], Nk, hq=hq, hkv=hkv)
-    p, path, (Q, K, V) = _run(w, Nq=Nq)
+    p, path, (Q, K, V) = _run(w, Nq=Nq, aux=aux)
     oc = _Oracle(Q, K, V)
     assert_same(path.vc.cpu().numpy().reshape(oc.vc.shape), oc.vc, "V MX codes")
     _check(path, oc, [(0, h) for h in range(hq)])
 
 
-def test_qat_forward_without_aux_matches():
-    """Without O' the kernel takes its other variant; O must be bit-identical."""
+def test_qat_forward_variants_agree():
+    """The inference forward and the forward with O' visit the keys in tiles
+    of 128 and 64: their O differ by the MXFP4 rounding of P under different
+    running maxima only, and their log-sum-exps by fp32 rounding."""
     w = wl.with_len(wl.WORKLOADS["c4"], 1024, hq=2, hkv=2)
     _, with_aux, _ = _run(w)
     _, no_aux, _ = _run(w, aux=False)
-    assert torch.equal(with_aux.o, no_aux.o)
-    assert torch.equal(with_aux.lse, no_aux.lse)
+    a, b = with_aux.o.float().cpu().numpy(), no_aux.o.float().cpu().numpy()
+    assert np.abs(a - b).sum() / np.abs(a).sum() < 2e-2
+    assert torch.allclose(with_aux.lse, no_aux.lse, atol=2e-3, rtol=0)
 
 
 @pytest.mark.slow
-def test_qat_forward_full_size_sampled():
+@pytest.mark.parametrize("aux", [True, False], ids=["with_aux", "inference"])
+def test_qat_forward_full_size_sampled(aux):
     """Full c4 shape (B=1, H=32, N=16384, d=128, non-causal); the oracle checks
     sampled rows of sampled heads."""
     w = wl.WORKLOADS["c4"]
-    p, path, (Q, K, V) = _run(w)
+    p, path, (Q, K, V) = _run(w, aux=aux)
     oc = _Oracle(Q, K, V)
     for h in (0, 13, 31):
         for r0 in (0, 8191, 16384 - 16):
