@@ -62,7 +62,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def _traffic_for(kernel: str):
     """Measured HBM bytes per launch of `kernel` from the committed counter
-    summary, if it was taken on the current kernel source."""
+    summary, if it was taken on the current kernel source and build flags."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -77,6 +77,9 @@ def _traffic_for(kernel: str):
         if hashlib.sha256(open(src, "rb").read()).hexdigest() != e["source_sha256"]:
             return None
     except OSError:
+        return None
+    from bit_quantized_attention_amd.csrc import build as _build
+    if e.get("build_flags") != _build.EXTRA.get(os.path.basename(src), []):
         return None
     return e["bytes_per_launch"]
 

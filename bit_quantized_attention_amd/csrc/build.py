@@ -33,13 +33,16 @@ FLAGS = [
 # of those instructions costs two extra register-file moves.  The VGPR form
 # keeps them in VGPRs (214 registers, no spills; the prefill kernel of the
 # same file compiles to the same code either way).
-# The FP4 attention kernels (Thrift / post-training prefill and decode,
-# Attn-QAT forward) take row maxima of matrix results; their scores are finite
-# or -inf (masked) and never NaN, so with -fno-honor-nans the backend forms
-# v_max3_f32 directly instead of first canonicalising each matrix result with
-# a v_max x, x.
+# The attention kernels take row maxima of matrix results; their scores are
+# finite or -inf (masked) and never NaN for finite inputs (non-finite inputs
+# give unspecified results unless the BQA_DEBUG scan, built without this flag,
+# rejects them), so with -fno-honor-nans the backend forms v_max3_f32 directly
+# instead of first canonicalising each matrix result with a v_max x, x
+# (measured: c3 backward 1.083 -> 1.058 ms).
 EXTRA = {"attn_thrift.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
-         "attn_qat.hip": ["-fno-honor-nans"]}
+         "attn_qat.hip": ["-fno-honor-nans"],
+         "attn_sage_fwd.hip": ["-fno-honor-nans"],
+         "attn_sage_bwd.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:
