@@ -433,17 +433,12 @@ __global__ __launch_bounds__(512, 1) void qbwd_dkdv_kernel(QatBwdArgs a) {
                 dk = mfma_bf16_32x32x16(as, bq, dk);
             }
         }
-        // every wavefront is done with P^, dS and the columns: copy the next
-        // columns; the next rows must have landed
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        // every wavefront is done with P^, dS and the columns, and the next
+        // rows have landed: copy the next columns (they land during the next
+        // step's P and dS, which do not read them)
+        BQA_WAIT_VM(0);
         barrier_only();
-        if (more) {
-            cols_issue(a, cp, bh, I + 1, L, w);
-            BQA_WAIT_VM(KvqPlan::NC);
-        } else {
-            BQA_WAIT_VM(0);
-        }
-        barrier_only();
+        if (more) cols_issue(a, cp, bh, I + 1, L, w);
     }
     // dv reg i: key ko + 8 (i / 4) + 4 h + i % 4, channel co + lq; dO entered scaled by 2^k
     uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sB + hq * a.dv.sH;
