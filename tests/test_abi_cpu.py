@@ -183,6 +183,26 @@ def test_fwd_validation(L):
                    o=_dense(dtype=bqa.BQA_FP16)) == bqa.BQA_E_DEVICE
 
 
+def test_empty_and_inconsistent_shapes(L):
+    """Empty inputs (a zero batch, head count or length) and head counts that
+    do not group are refused before any device work, by every attention
+    entry point."""
+    g = _dense()
+    q, k = _q(), _q(block=64)
+    v = _q(fmt=bqa.BQA_FP8E4M3, axis=1, block=4096)
+
+    def fwd(p):
+        return bqa.lib().bqa_attn_fwd(C.byref(p), C.byref(q), C.byref(k), C.byref(v), None, None, None, None, None,
+                                      C.byref(g), None, None, None, None, 0, None)
+
+    def bwd(p):
+        return bqa.lib().bqa_attn_bwd(C.byref(p), C.byref(q), C.byref(k), None, C.byref(g), C.byref(g), 0x50000, None,
+                                      C.byref(g), C.byref(g), C.byref(g), C.byref(g), 0x40000, 1 << 34, None)
+    for bad in (dict(B=0), dict(Hq=0), dict(Hkv=0), dict(Nq=0), dict(Nk=0), dict(Nq=-128), dict(Hq=6, Hkv=4)):
+        assert fwd(_p(**bad)) == bqa.BQA_E_SHAPE, bad
+        assert bwd(_p(mode=bqa.BQA_SAGE_I8_I8PV, **dict(dict(Nq=4096, Nk=4096), **bad))) == bqa.BQA_E_SHAPE, bad
+
+
 def test_debug_scores_validation(L):
     q, k = _q(), _q(block=64)
     f = bqa.lib().bqa_debug_qk_scores
