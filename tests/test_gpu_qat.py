@@ -114,6 +114,36 @@ def test_qat_forward_small(Nq, Nk, hq, hkv, aux):
     _check(path, oc, [(0, h) for h in range(hq)])
 
 
+@pytest.mark.parametrize("aux", [True, False], ids=["with_aux", "inference"])
+def test_qat_forward_zero_blocks(aux):
+    """Degenerate MXFP4 blocks: a whole query tile of zero rows (E8M0 scale
+    byte 0, zero codes) scores exactly 0 against every key, so its rows have
+    row maximum 0 and identical outputs; a key tile of zero rows scores 0
+    against every query; a zero V channel gives exactly zero output.  O, O'
+    and the log-sum-exp against the oracle."""
+    from bit_quantized_attention_amd.runner import QatPath, qat_problem, to_device
+    w = wl.with_len(wl.WORKLOADS["c4"], 512, hq=1, hkv=1)
+    Q, K, V = wl.build(w, "q"), wl.build(w, "k"), wl.build(w, "v")
+    Q[0, 0, 128:256] = 0.0
+    K[0, 0, 256:384] = 0.0
+    V[0, 0, :, 5] = 0.0
+    p = qat_problem(1, 1, 1, 512, 512, w.d)
+    path = QatPath(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"), aux=aux)
+    path.step()
+    torch.cuda.synchronize()
+    oc = _Oracle(Q, K, V)
+    assert_same(path.qc.cpu().numpy().reshape(oc.qc.shape), oc.qc, "Q MX codes")
+    assert_same(path.qs.cpu().numpy().reshape(oc.qs.shape), oc.qs, "Q MX scales")
+    assert not path.qc[0, 0, 128:256].any() and not path.qs[0, 0, 128:256].any()
+    _check(path, oc, [(0, 0)])
+    assert torch.equal(path.row_max[0, 0, 128:256], torch.zeros(128, device="cuda"))
+    O = path.o[0, 0].float()
+    assert torch.equal(O[128:256], O[128:129].expand(128, -1))
+    assert not O[:, 5].any()
+    if aux:
+        assert not path.oa[0, 0, :, 5].float().any()
+
+
 def test_qat_forward_variants_agree():
     """The inference forward and the forward with O' visit the keys in tiles
     of 128 and 64: their O differ by the MXFP4 rounding of P under different
