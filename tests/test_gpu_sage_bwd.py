@@ -54,6 +54,29 @@ def test_sage_backward_small(N):
             compare_outputs(gi[0, h], ri, "bf16", what=f"{name}[h={h}]")
 
 
+def test_sage_backward_zero_do_tile():
+    """A query tile whose dO rows are all zero: its dO block quantises to
+    scale 0 and zero codes, its dS tiles have maximum 0 (the zero-scale path
+    of both product kernels: inverse scale 0, zero codes), so its dQ is
+    exactly zero and it adds nothing to dK and dV.  All three against the
+    oracle, which takes the same degenerate tiles."""
+    import bit_quantized_attention_amd as bqa
+    from bit_quantized_attention_amd.runner import SageTrainStep, sage_problem, to_device
+    w = wl.with_len(wl.WORKLOADS["c3"], 512, hq=1, hkv=1)
+    Q, K, V, dO = (wl.build(w, t) for t in ("q", "k", "v", "do"))
+    dO[0, 0, 128:256] = 0.0
+    p = sage_problem(1, 1, 1, 512, 512, w.d, True, bqa.BQA_SAGE_I8_I8PV, q_block=128, smooth_k=True, smooth_eps=1e-3)
+    step = SageTrainStep(p, to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"), to_device(dO, "bf16"))
+    step.step()
+    torch.cuda.synchronize()
+    assert not step.dq[0, 0, 128:256].any()
+    oc = SageOracle(Q, K, V, q_block=128, eps=1e-3, pv="i8")
+    ref = _oracle_grads(oc, Q, V, dO, 0, True)
+    assert not ref[0][128:256].any()
+    for name, gi, ri in zip(("dQ", "dK", "dV"), (step.dq, step.dk, step.dv), ref):
+        compare_outputs(gi[0, 0].float().cpu().numpy(), ri, "bf16", what=f"{name} (zero dO tile)")
+
+
 @pytest.mark.slow
 def test_sage_backward_full_size_sampled():
     """Full c3 shape (B=1, H=16, N=8192, causal): the GPU runs the whole
